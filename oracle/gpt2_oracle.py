@@ -1,0 +1,201 @@
+"""CPU float64 oracle of the GPT-2 decoder forward pass.
+
+TEST INFRASTRUCTURE ONLY. Only the test suite, the smoke check and the benchmark's CPU-baseline
+leg may import this module. The product path (the HIP library and its Python binding) never
+imports, calls or falls back to it, and this module imports nothing from the product path: it
+depends on numpy alone and receives its inputs as plain arrays.
+
+Every function is the plain definition of one step, written out in float64 with numpy (matmul
+is the only library primitive used as a step). Nothing is blocked, fused or reordered beyond
+what the definition states, so each function can be checked against the pages by eye.
+
+Pages cited (titles as they appear on the pages):
+  [手写] "从零手写GPT-2：PyTorch实现Transformer解码器核心模块"
+  [实战] "GPT2模型开发实战：从原理到部署全解析"
+  [解析] "GPT-2模型架构解析与实现指南"
+  [复现] "复现GPT-2 124M"
+  [指南] "从零实现 GPT-2：PyTorch 版大语言模型构建指南"
+
+Readings taken where the pages are silent or disagree (each one also recorded in the design
+notes): learned wpe table; GELU in its tanh form; biases present on all four block Linears and
+absent on lm_head; causal mask keeps the diagonal (key j visible to query i iff j <= i); scale
+1/sqrt(d_head) applied before the mask; biased variance with eps 1e-5 inside the square root;
+dropout is the identity (inference forward); q, k, v are the column blocks [0,d), [d,2d), [2d,3d)
+of the fused projection and head h owns columns h*dh .. (h+1)*dh-1 within each block.
+
+Parity pins: every function below is pinned by a CPU test against values the mathematics or
+the pages fix (closed forms, brute force on tiny inputs, library special cases, invariants).
+The whole-model logits at random init are "parity unpinned" beyond those component pins and the
+model-level invariants (shape, parameter count, causality, batch independence, all-ones MLP):
+the pages print no logits for any input.
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+F64 = np.float64
+
+
+def embed(wte: np.ndarray, wpe: np.ndarray, tokens: np.ndarray) -> np.ndarray:
+    """Token embedding plus learned position embedding.
+
+    x[b, t, :] = wte[tokens[b, t], :] + wpe[t, :] with positions counted from 0
+    ([手写] §4.1 forward, steps 1; [复现] §2.1 learned position table; [解析] §1.2).
+    Dropout after the sum is the identity in the inference forward.
+    """
+    tokens = np.asarray(tokens)
+    B, T = tokens.shape
+    wte = np.asarray(wte, dtype=F64)
+    wpe = np.asarray(wpe, dtype=F64)
+    return wte[tokens] + wpe[np.arange(T)][None, :, :]
+
+
+def layer_norm(x: np.ndarray, gamma: np.ndarray, beta: np.ndarray, eps: float = 1e-5) -> np.ndarray:
+    """LayerNorm over the last axis with the biased variance.
+
+    mean = E[x]; var = E[(x - mean)^2] (no Bessel correction); out = gamma * (x - mean) /
+    sqrt(var + eps) + beta ([复现] §2.1 LayerNorm class, unbiased=False; eps 1e-5 per [手写] §3.2
+    and §4.2).
+    """
+    x = np.asarray(x, dtype=F64)
+    mean = x.mean(axis=-1, keepdims=True)
+    var = ((x - mean) ** 2).mean(axis=-1, keepdims=True)
+    return np.asarray(gamma, F64) * (x - mean) / np.sqrt(var + eps) + np.asarray(beta, F64)
+
+
+def linear(x: np.ndarray, w: np.ndarray, b: np.ndarray | None) -> np.ndarray:
+    """nn.Linear semantics: y = x W^T + b with W stored [out, in] (all pages' code listings)."""
+    y = np.asarray(x, dtype=F64) @ np.asarray(w, dtype=F64).T
+    if b is not None:
+        y = y + np.asarray(b, dtype=F64)
+    return y
+
+
+def gelu_tanh(x: np.ndarray) -> np.ndarray:
+    """GELU, tanh form: 0.5 x (1 + tanh(sqrt(2/pi) (x + 0.044715 x^3))).
+
+    [复现] §2.4 names this form as the one original GPT-2 used; [手写] §3.4 prints the same
+    formula.
+    """
+    x = np.asarray(x, dtype=F64)
+    return 0.5 * x * (1.0 + np.tanh(math.sqrt(2.0 / math.pi) * (x + 0.044715 * x ** 3)))
+
+
+def gelu_erf(x: np.ndarray) -> np.ndarray:
+    """GELU, erf form 0.5 x (1 + erf(x / sqrt(2))) (the F.gelu default used by [解析] §2.2).
+
+    Kept only for the optional erf configuration; the default reading is the tanh form.
+    """
+    from math import erf
+    x = np.asarray(x, dtype=F64)
+    return 0.5 * x * (1.0 + np.vectorize(erf)(x / math.sqrt(2.0)))
+
+
+def softmax(s: np.ndarray, axis: int = -1) -> np.ndarray:
+    """Row softmax with the row maximum subtracted first (exact in float64; -inf gives 0)."""
+    s = np.asarray(s, dtype=F64)
+    m = np.max(s, axis=axis, keepdims=True)
+    e = np.exp(s - m)
+    return e / e.sum(axis=axis, keepdims=True)
+
+
+def causal_attention(q: np.ndarray, k: np.ndarray, v: np.ndarray) -> np.ndarray:
+    """Causal scaled dot-product attention per (batch, head); inputs [..., T, dh].
+
+    S = q k^T / sqrt(dh); S[i, j] = -inf for j > i (diagonal kept); P = softmax over keys;
+    out = P v ([复现] §2.1 CausalSelfAttention and §2.2; [解析] §2.1; [手写] §3.3: the mask goes
+    after the scores and before the softmax). The [T, T] score matrix is materialised on purpose.
+    """
+    q = np.asarray(q, dtype=F64)
+    k = np.asarray(k, dtype=F64)
+    v = np.asarray(v, dtype=F64)
+    T, dh = q.shape[-2], q.shape[-1]
+    s = (q @ np.swapaxes(k, -1, -2)) * (1.0 / math.sqrt(dh))
+    future = np.triu(np.ones((T, T), dtype=bool), k=1)
+    s = np.where(future, -np.inf, s)
+    return softmax(s, axis=-1) @ v
+
+
+def split_heads(qkv: np.ndarray, n_head: int):
+    """[B, T, 3d] -> q, k, v each [B, H, T, dh]: split by d, view (B, T, H, dh), swap T and H.
+
+    ([复现] §2.1 forward: split(n_embd) then view/transpose; [解析] §2.1 reshape(B, T, 3, H, dh).)
+    """
+    B, T, three_d = qkv.shape
+    d = three_d // 3
+    dh = d // n_head
+    q, k, v = qkv[..., 0:d], qkv[..., d:2 * d], qkv[..., 2 * d:3 * d]
+    return tuple(t.reshape(B, T, n_head, dh).transpose(0, 2, 1, 3) for t in (q, k, v))
+
+
+def merge_heads(o: np.ndarray) -> np.ndarray:
+    """[B, H, T, dh] -> [B, T, H*dh] (transpose back, then view)."""
+    B, H, T, dh = o.shape
+    return o.transpose(0, 2, 1, 3).reshape(B, T, H * dh)
+
+
+def attention_block(x: np.ndarray, p: dict, l: int, n_head: int) -> np.ndarray:
+    """Self-attention sub-layer of block l on its LayerNorm'd input: c_attn, heads, c_proj."""
+    pre = f"h.{l}.attn."
+    qkv = linear(x, p[pre + "c_attn.w"], p[pre + "c_attn.b"])
+    q, k, v = split_heads(qkv, n_head)
+    o = merge_heads(causal_attention(q, k, v))
+    return linear(o, p[pre + "c_proj.w"], p[pre + "c_proj.b"])
+
+
+def mlp_block(x: np.ndarray, p: dict, l: int, gelu=gelu_tanh) -> np.ndarray:
+    """MLP sub-layer: c_fc (d -> d_mlp), GELU, c_proj (d_mlp -> d) ([解析] §2.2; [复现] §2.4)."""
+    pre = f"h.{l}.mlp."
+    return linear(gelu(linear(x, p[pre + "c_fc.w"], p[pre + "c_fc.b"])),
+                  p[pre + "c_proj.w"], p[pre + "c_proj.b"])
+
+
+def block(x: np.ndarray, p: dict, l: int, n_head: int, eps: float = 1e-5, gelu=gelu_tanh) -> np.ndarray:
+    """Pre-LN block: x + attn(ln_1(x)), then + mlp(ln_2(x)) ([手写] §3.2; [复现] §2.3; [解析] §1.1)."""
+    pre = f"h.{l}."
+    x = x + attention_block(layer_norm(x, p[pre + "ln_1.w"], p[pre + "ln_1.b"], eps), p, l, n_head)
+    x = x + mlp_block(layer_norm(x, p[pre + "ln_2.w"], p[pre + "ln_2.b"], eps), p, l, gelu)
+    return x
+
+
+def residual(p: dict, tokens: np.ndarray, n_head: int, n_layers: int, eps: float = 1e-5,
+             gelu=gelu_tanh) -> np.ndarray:
+    """Residual stream [B, T, d] after the embedding and the first n_layers blocks."""
+    x = embed(p["wte"], p["wpe"], tokens)
+    for l in range(n_layers):
+        x = block(x, p, l, n_head, eps, gelu)
+    return x
+
+
+def final_hidden(p: dict, tokens: np.ndarray, n_head: int, n_layer: int, eps: float = 1e-5,
+                 gelu=gelu_tanh) -> np.ndarray:
+    """ln_f applied to the residual stream after all blocks ([手写] §4.1 forward, step 3)."""
+    x = residual(p, tokens, n_head, n_layer, eps, gelu)
+    return layer_norm(x, p["ln_f.w"], p["ln_f.b"], eps)
+
+
+def lm_head(h: np.ndarray, wte: np.ndarray) -> np.ndarray:
+    """Tied output projection, no bias: logits = h wte^T ([手写] §2.2 item 4 and §4.1)."""
+    return linear(h, wte, None)
+
+
+def forward(p: dict, tokens: np.ndarray, n_head: int, n_layer: int, eps: float = 1e-5,
+            gelu=gelu_tanh) -> np.ndarray:
+    """Whole forward: tokens [B, T] -> logits [B, T, n_vocab] in float64."""
+    return lm_head(final_hidden(p, tokens, n_head, n_layer, eps, gelu), p["wte"])
+
+
+def argmax_first(logits: np.ndarray) -> np.ndarray:
+    """Index of the largest entry along the last axis; the first such index on ties."""
+    return np.argmax(np.asarray(logits), axis=-1)
+
+
+def param_count(n_vocab: int, n_ctx: int, d: int, n_layer: int, d_mlp: int) -> int:
+    """Number of parameters with lm_head tied to wte (counted once).
+
+    wte + wpe + per block (ln_1, c_attn, attn.c_proj, ln_2, c_fc, mlp.c_proj) + ln_f.
+    """
+    per_block = (2 * d) + (3 * d * d + 3 * d) + (d * d + d) + (2 * d) + (d_mlp * d + d_mlp) + (d * d_mlp + d)
+    return n_vocab * d + n_ctx * d + n_layer * per_block + 2 * d

@@ -1,0 +1,408 @@
+"""Pins of the CPU fp64 oracle against what the pages and the mathematics fix.
+
+Each pin is a check function that takes the oracle function under test as an argument, so the
+same pins also run against deliberately broken copies of the oracle (planted mistakes: dropped
+term, wrong sign or index, transposed operand) and must catch every one of them.
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+import torch.nn.functional as F
+
+from oracle import gpt2_oracle as O
+from decoder_only_transformer_gpt2_amd import synth
+
+GOLDEN = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "page_facts.json")))
+
+
+def rng(seed=1234):
+    return np.random.Generator(np.random.PCG64(seed))
+
+
+# ----------------------------------------------------------------------------- LayerNorm pins
+def check_layer_norm(ln):
+    fails = []
+    # closed form: x = [1,2,3,4] has mean 2.5 and biased variance 1.25 (unbiased would be 5/3)
+    x = np.array([1.0, 2.0, 3.0, 4.0])
+    out = ln(x, np.ones(4), np.zeros(4), 1e-5)
+    want = np.array([-1.5, -0.5, 0.5, 1.5]) / math.sqrt(1.25 + 1e-5)
+    if not np.allclose(out, want, rtol=0, atol=1e-15):
+        fails.append("closed form [1,2,3,4]")
+    # invariants: (out - beta)/gamma has mean 0 and variance var/(var+eps) per row
+    r = rng(1)
+    x = r.standard_normal((5, 48)) * 3 + 1
+    g = 1 + 0.3 * r.standard_normal(48)
+    b = 0.5 * r.standard_normal(48)
+    out = ln(x, g, b, 1e-5)
+    z = (out - b) / g
+    var = x.var(axis=-1)
+    if not np.allclose(z.mean(-1), 0, atol=1e-13):
+        fails.append("mean invariant")
+    if not np.allclose(z.var(-1), var / (var + 1e-5), rtol=1e-12):
+        fails.append("variance invariant")
+    # library special case: torch's layer_norm (biased variance) in float64
+    ref = F.layer_norm(torch.from_numpy(x), (48,), torch.from_numpy(g), torch.from_numpy(b), 1e-5).numpy()
+    if not np.allclose(out, ref, rtol=1e-12, atol=1e-12):
+        fails.append("torch layer_norm fp64")
+    return fails
+
+
+def test_layer_norm_pins():
+    assert check_layer_norm(O.layer_norm) == []
+
+
+def test_layer_norm_eps_from_pages():
+    assert GOLDEN["layernorm_eps"]["value"] == 1e-5
+    # eps sits inside the square root: a constant row maps to beta exactly
+    out = O.layer_norm(np.full((3, 8), 7.0), np.full(8, 2.0), np.full(8, 0.25))
+    assert np.all(out == 0.25)
+
+
+# ---------------------------------------------------------------------------------- GELU pins
+def check_gelu(gelu):
+    fails = []
+    if gelu(np.array([0.0]))[0] != 0.0:
+        fails.append("gelu(0)")
+    big = gelu(np.array([12.0, -12.0]))
+    if abs(big[0] - 12.0) > 1e-12 or abs(big[1]) > 1e-12:
+        fails.append("asymptotes")
+    x = np.linspace(-6, 6, 2001)
+    ref = F.gelu(torch.from_numpy(x), approximate="tanh").numpy()
+    if not np.allclose(gelu(x), ref, rtol=1e-13, atol=1e-15):
+        fails.append("torch gelu tanh fp64")
+    return fails
+
+
+def test_gelu_pins():
+    assert check_gelu(O.gelu_tanh) == []
+
+
+def test_gelu_forms_differ_enough_to_matter():
+    # The two GELU forms the pages mention differ by ~4.7e-4 at most: a swap would be visible.
+    x = np.linspace(-6, 6, 20001)
+    d = np.abs(O.gelu_tanh(x) - O.gelu_erf(x))
+    assert 4.0e-4 < d.max() < 5.5e-4
+    ref = F.gelu(torch.from_numpy(x)).numpy()
+    assert np.allclose(O.gelu_erf(x), ref, rtol=1e-13, atol=1e-15)
+
+
+# -------------------------------------------------------------------------------- Linear pins
+def check_linear(linear):
+    fails = []
+    r = rng(2)
+    x = r.standard_normal((2, 3, 5))
+    w = r.standard_normal((4, 5))  # [out, in]
+    b = r.standard_normal(4)
+    y = linear(x, w, b)
+    loops = np.zeros((2, 3, 4))
+    for i in range(2):
+        for t in range(3):
+            for o in range(4):
+                s = b[o]
+                for k in range(5):
+                    s += x[i, t, k] * w[o, k]
+                loops[i, t, o] = s
+    if y.shape != (2, 3, 4) or not np.allclose(y, loops, rtol=1e-13, atol=1e-14):
+        fails.append("explicit loops")
+    ref = F.linear(torch.from_numpy(x), torch.from_numpy(w), torch.from_numpy(b)).numpy()
+    if not np.allclose(y, ref, rtol=1e-13, atol=1e-14):
+        fails.append("torch linear")
+    return fails
+
+
+def test_linear_pins():
+    assert check_linear(O.linear) == []
+
+
+# ----------------------------------------------------------------------------- Attention pins
+def brute_attention(q, k, v):
+    B, H, T, dh = q.shape
+    out = np.zeros_like(q)
+    for b in range(B):
+        for h in range(H):
+            for i in range(T):
+                s = [sum(q[b, h, i, c] * k[b, h, j, c] for c in range(dh)) / math.sqrt(dh) for j in range(i + 1)]
+                m = max(s)
+                e = [math.exp(x - m) for x in s]
+                z = sum(e)
+                for c in range(dh):
+                    out[b, h, i, c] = sum(e[j] / z * v[b, h, j, c] for j in range(i + 1))
+    return out
+
+
+def check_attention(attn):
+    fails = []
+    r = rng(3)
+    q, k, v = (r.standard_normal((1, 2, 5, 4)) for _ in range(3))
+    if not np.allclose(attn(q, k, v), brute_attention(q, k, v), rtol=0, atol=1e-12):
+        fails.append("brute force B=1 H=2 T=5 dh=4")
+    o = attn(q, k, v)
+    if not np.array_equal(o[:, :, 0, :], v[:, :, 0, :]):
+        fails.append("row 0 equals v0")
+    if not np.array_equal(attn(q[:, :, :1], k[:, :, :1], v[:, :, :1]), v[:, :, :1]):
+        fails.append("T=1")
+    # identical keys: every visible key scores the same, so row i is the mean of v0..vi
+    kk = np.repeat(k[:, :, :1], 5, axis=2)
+    pref = np.cumsum(v, axis=2) / np.arange(1, 6)[None, None, :, None]
+    if not np.allclose(attn(q, kk, v), pref, rtol=0, atol=1e-13):
+        fails.append("identical keys -> prefix mean")
+    # v = identity recovers the probability matrix: rows sum to 1, nothing above the diagonal
+    T = 6
+    qq, kq = r.standard_normal((1, 1, T, T)), r.standard_normal((1, 1, T, T))
+    P = attn(qq, kq, np.eye(T)[None, None])[0, 0]
+    if not np.allclose(P.sum(-1), 1.0, rtol=0, atol=1e-12):
+        fails.append("softmax rows sum to 1")
+    if np.any(np.triu(P, 1) != 0.0):
+        fails.append("causal zeros above the diagonal")
+    # library special case at the real head size: dh=64 (scale 1/8), T=33
+    q, k, v = (r.standard_normal((2, 3, 33, 64)) for _ in range(3))
+    ref = F.scaled_dot_product_attention(torch.from_numpy(q), torch.from_numpy(k), torch.from_numpy(v),
+                                         is_causal=True).numpy()
+    if not np.allclose(attn(q, k, v), ref, rtol=1e-12, atol=1e-12):
+        fails.append("torch sdpa causal fp64 dh=64")
+    return fails
+
+
+def test_attention_pins():
+    assert check_attention(O.causal_attention) == []
+
+
+def test_split_merge_heads_layout():
+    B, T, H, dh = 2, 3, 4, 5
+    d = H * dh
+    # entry value encodes (b, t, column): reading it back names the column a head element came from
+    qkv = np.zeros((B, T, 3 * d))
+    for b in range(B):
+        for t in range(T):
+            qkv[b, t] = 1e6 * b + 1e3 * t + np.arange(3 * d)
+    q, k, v = O.split_heads(qkv, H)
+    for which, arr in enumerate((q, k, v)):
+        assert arr.shape == (B, H, T, dh)
+        for b in range(B):
+            for h in range(H):
+                for t in range(T):
+                    for j in range(dh):
+                        assert arr[b, h, t, j] == 1e6 * b + 1e3 * t + which * d + h * dh + j
+    assert np.array_equal(O.merge_heads(q), qkv[..., :d])
+
+
+# ------------------------------------------------------------------------------ Embedding pins
+def check_embed(embed):
+    fails = []
+    r = rng(4)
+    wte = r.standard_normal((11, 3))
+    wpe = r.standard_normal((7, 3))
+    tok = np.array([[3, 10, 0], [5, 5, 1]])
+    x = embed(wte, wpe, tok)
+    for b in range(2):
+        for t in range(3):
+            if not np.array_equal(x[b, t], wte[tok[b, t]] + wpe[t]):
+                fails.append(f"gather ({b},{t})")
+    return fails
+
+
+def test_embed_pins():
+    assert check_embed(O.embed) == []
+
+
+# --------------------------------------------------------------------------- Model-level pins
+@pytest.fixture(scope="module")
+def small_f32():
+    return synth.make_weights(synth.GPT2_SMALL, bf16=False)
+
+
+def test_param_count_matches_pages():
+    s = synth.GPT2_SMALL
+    n = O.param_count(s.n_vocab, s.n_ctx, s.d_model, s.n_layer, s.d_mlp)
+    assert n == 124_439_808
+    # independent count: the sizes of the tensors the generator emits (lm_head tied, no tensor)
+    assert n == sum(int(np.prod(shape)) for _, shape, _ in synth.tensor_specs(s))
+    g = GOLDEN
+    assert abs(n - g["param_count_124m"]["value"]) / g["param_count_124m"]["value"] < g["param_count_124m"]["rel_tol"]
+    tied = s.n_vocab * s.d_model
+    assert abs(2 * tied - g["tied_matrix_counted_twice"]["value"]) / 77e6 < g["tied_matrix_counted_twice"]["rel_tol"]
+    assert abs(tied - g["tying_saves"]["value"]) / 38e6 < g["tying_saves"]["rel_tol"]
+    assert abs(2 * n - g["weights_fp16_bytes"]["value"]) / 250e6 < g["weights_fp16_bytes"]["rel_tol"]
+    assert abs(4 * n - g["weights_fp32_bytes"]["value"]) / 500e6 < g["weights_fp32_bytes"]["rel_tol"]
+    # the larger sizes the configurations use
+    assert O.param_count(50257, 1024, 1024, 24, 4096) == 354_823_168
+    assert O.param_count(50257, 1024, 1600, 48, 6400) == 1_557_611_200
+    cfg = g["config_124m"]["value"]
+    assert (s.n_vocab, s.n_ctx, s.d_model, s.n_head, s.n_layer) == (
+        cfg["n_vocab"], cfg["n_ctx"], cfg["d_model"], cfg["n_head"], cfg["n_layer"])
+
+
+def test_demo_output_shape(small_f32):
+    g = GOLDEN["demo_output_shape"]
+    tok = synth.make_tokens(g["input"]["B"], g["input"]["T"])
+    logits = O.forward(small_f32, tok, 12, 12)
+    assert list(logits.shape) == g["value"]
+    assert np.all(np.isfinite(logits))
+    # logits at this init are ~N(0, (0.02*sqrt(768))^2): a loose sanity bound
+    assert 0.3 < logits.std() < 0.9
+
+
+def test_causality_bit_identical(small_f32):
+    tok = synth.make_tokens(1, 9)
+    base = O.forward(small_f32, tok, 12, 12)
+    for t in (0, 3, 7):
+        tok2 = tok.copy()
+        tok2[0, t + 1:] = (tok2[0, t + 1:] + 12345) % 50257
+        other = O.forward(small_f32, tok2, 12, 12)
+        assert np.array_equal(base[:, :t + 1], other[:, :t + 1])
+        assert not np.allclose(base[:, t + 1:], other[:, t + 1:])
+
+
+def test_batch_independence(small_f32):
+    tok = synth.make_tokens(3, 5)
+    both = O.forward(small_f32, tok, 12, 12)
+    for b in range(3):
+        one = O.forward(small_f32, tok[b:b + 1], 12, 12)
+        assert np.allclose(both[b:b + 1], one, rtol=0, atol=1e-12)
+
+
+def test_mlp_all_ones_hand_value():
+    # 从零手写GPT-2 §3.4 describes checking the MLP with all-ones weights and an all-ones input
+    # against a hand calculation: pre-activation = d, gelu(d) = d (tanh saturates), out = d_mlp*d.
+    d, f = 768, 3072
+    p = {"h.0.mlp.c_fc.w": np.ones((f, d)), "h.0.mlp.c_fc.b": np.zeros(f),
+         "h.0.mlp.c_proj.w": np.ones((d, f)), "h.0.mlp.c_proj.b": np.zeros(d)}
+    out = O.mlp_block(np.ones((1, 1, d)), p, 0)
+    assert np.all(out == float(f * d))
+    # a negative input is (almost) cut off: gelu(-768) is 0 to float64 precision
+    out = O.mlp_block(-np.ones((1, 1, d)), p, 0)
+    assert np.all(np.abs(out) < 1e-300)
+
+
+@pytest.mark.slow
+def test_activation_sizes_b4_t1024(small_f32):
+    # 从零手写GPT-2 §2.3: at batch 4, seq 1024 in fp32 the embedding output is ~12MB, the QKV
+    # projection ~36MB, the attention output ~12MB and the MLP hidden ~48MB per block.
+    g = GOLDEN["activation_mib_b4_t1024_fp32"]
+    p = small_f32
+    tok = synth.make_tokens(4, 1024)
+    x = O.embed(p["wte"], p["wpe"], tok)
+    a = O.layer_norm(x, p["h.0.ln_1.w"], p["h.0.ln_1.b"])
+    qkv = O.linear(a, p["h.0.attn.c_attn.w"], p["h.0.attn.c_attn.b"])
+    o = O.merge_heads(O.causal_attention(*O.split_heads(qkv, 12)))
+    hid = O.linear(O.layer_norm(x, p["h.0.ln_2.w"], p["h.0.ln_2.b"]), p["h.0.mlp.c_fc.w"], p["h.0.mlp.c_fc.b"])
+    mib = lambda t: t.size * 4 / 2 ** 20
+    assert mib(x) == g["embedding_out"]
+    assert mib(qkv) == g["qkv"]
+    assert mib(o) == g["attn_out"]
+    assert mib(hid) == g["mlp_hidden"]
+    assert 12 * (mib(qkv) + mib(o) + mib(hid)) == g["twelve_blocks"]
+
+
+def test_logits_size_b1_t1024(small_f32):
+    # 复现GPT-2 124M §3.4: logits [1, 1024, 50257] take ~205MB in FP32 and ~103MB in FP16
+    g = GOLDEN["logits_bytes_b1_t1024"]
+    p = small_f32
+    tok = synth.make_tokens(1, 1024)
+    h = O.layer_norm(O.embed(p["wte"], p["wpe"], tok), p["ln_f.w"], p["ln_f.b"])
+    logits = O.lm_head(h, p["wte"])
+    assert list(logits.shape) == g["shape"]
+    assert abs(logits.size * 4 - g["fp32"]) / g["fp32"] < g["rel_tol"]
+    assert abs(logits.size * 2 - g["fp16"]) / g["fp16"] < g["rel_tol"]
+
+
+def test_argmax_first_index_on_ties():
+    a = np.array([[1.0, 3.0, 3.0, 2.0], [5.0, 5.0, 5.0, 5.0], [-1.0, -2.0, -0.5, -0.5]])
+    assert O.argmax_first(a).tolist() == [1, 0, 2]
+
+
+# --------------------------------------------------------------------- planted-mistake audit
+def _unbiased_ln(x, g, b, eps=1e-5):
+    x = np.asarray(x, float)
+    m = x.mean(-1, keepdims=True)
+    v = ((x - m) ** 2).sum(-1, keepdims=True) / (x.shape[-1] - 1)
+    return g * (x - m) / np.sqrt(v + eps) + b
+
+
+def _eps_outside_ln(x, g, b, eps=1e-5):
+    x = np.asarray(x, float)
+    m = x.mean(-1, keepdims=True)
+    v = ((x - m) ** 2).mean(-1, keepdims=True)
+    return g * (x - m) / (np.sqrt(v) + eps) + b
+
+
+def _no_beta_ln(x, g, b, eps=1e-5):
+    return O.layer_norm(x, g, np.zeros_like(np.asarray(b, float)), eps)
+
+
+def _cubic_sign_gelu(x):
+    x = np.asarray(x, float)
+    return 0.5 * x * (1.0 + np.tanh(math.sqrt(2 / math.pi) * (x - 0.044715 * x ** 3)))
+
+
+def _no_half_gelu(x):
+    x = np.asarray(x, float)
+    return x * (1.0 + np.tanh(math.sqrt(2 / math.pi) * (x + 0.044715 * x ** 3))) / 2.0001
+
+
+def _transposed_linear(x, w, b):
+    w = np.asarray(w, float)
+    return np.asarray(x, float) @ w.reshape(w.shape[1], w.shape[0]) + b
+
+
+def _no_bias_linear(x, w, b):
+    return O.linear(x, w, None)
+
+
+def _strict_mask_attn(q, k, v):
+    T, dh = q.shape[-2], q.shape[-1]
+    s = (q @ np.swapaxes(k, -1, -2)) / math.sqrt(dh)
+    s = np.where(np.triu(np.ones((T, T), bool), k=0), -np.inf, s)
+    with np.errstate(invalid="ignore"):
+        return O.softmax(s) @ v
+
+
+def _no_scale_attn(q, k, v):
+    T = q.shape[-2]
+    s = q @ np.swapaxes(k, -1, -2)
+    s = np.where(np.triu(np.ones((T, T), bool), k=1), -np.inf, s)
+    return O.softmax(s) @ v
+
+
+def _query_axis_softmax_attn(q, k, v):
+    T, dh = q.shape[-2], q.shape[-1]
+    s = (q @ np.swapaxes(k, -1, -2)) / math.sqrt(dh)
+    s = np.where(np.triu(np.ones((T, T), bool), k=1), -np.inf, s)
+    with np.errstate(invalid="ignore"):
+        return O.softmax(s, axis=-2) @ v
+
+
+def _mask_after_softmax_attn(q, k, v):
+    T, dh = q.shape[-2], q.shape[-1]
+    s = (q @ np.swapaxes(k, -1, -2)) / math.sqrt(dh)
+    P = O.softmax(s)
+    return np.where(np.triu(np.ones((T, T), bool), k=1), 0.0, P) @ v
+
+
+def _shifted_pos_embed(wte, wpe, tok):
+    T = tok.shape[1]
+    return np.asarray(wte, float)[tok] + np.asarray(wpe, float)[np.arange(1, T + 1) % wpe.shape[0]][None]
+
+
+def _missing_pos_embed(wte, wpe, tok):
+    return np.asarray(wte, float)[tok]
+
+
+@pytest.mark.parametrize("check,mutant", [
+    (check_layer_norm, _unbiased_ln), (check_layer_norm, _eps_outside_ln), (check_layer_norm, _no_beta_ln),
+    (check_gelu, _cubic_sign_gelu), (check_gelu, _no_half_gelu), (check_gelu, O.gelu_erf),
+    (check_linear, _transposed_linear), (check_linear, _no_bias_linear),
+    (check_attention, _strict_mask_attn), (check_attention, _no_scale_attn),
+    (check_attention, _query_axis_softmax_attn), (check_attention, _mask_after_softmax_attn),
+    (check_embed, _shifted_pos_embed), (check_embed, _missing_pos_embed),
+])
+def test_pins_catch_planted_mistakes(check, mutant):
+    try:
+        fails = check(mutant)
+    except Exception as e:  # a crash on the pin inputs also counts as caught
+        fails = [repr(e)]
+    assert fails, f"{mutant.__name__} slipped past {check.__name__}"
