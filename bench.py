@@ -1,0 +1,174 @@
+"""Forward-pass throughput of the HIP GPT-2 library on one MI355X.
+
+python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload small|medium|xl] [--no-cpu-baseline]
+
+One step = one gpt2_forward over a batch of synthetic token ids already resident in HBM:
+embedding, every block, ln_f, the tied lm_head (fp32 logits) and the fused argmax. Weights are the
+seeded synthetic init (no checkpoint exists). Prints one JSON line.
+
+The roofline object is for the lm_head GEMM, the largest single launch: its duration is taken
+from HIP events the library records on its own stream around that launch in every timed step.
+The CPU baseline times the fp64 oracle on a bounded sample (one full sequence) on the host.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+from decoder_only_transformer_gpt2_amd import synth  # noqa: E402
+
+METRIC = "forward tokens/s, GPT-2 small B=4 T=1024 bf16; % of MFMA peak"
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0
+
+WORKLOADS = {
+    "small": (synth.GPT2_SMALL, 4, 1024),
+    "medium": (synth.GPT2_MEDIUM, 8, 1024),
+    "xl": (synth.GPT2_XL, 4, 1024),
+}
+
+
+def forward_flops(s: synth.ModelShape, B: int, T: int) -> float:
+    """Algorithmic FLOPs: block GEMMs + causal half of attention + lm_head (no padded columns)."""
+    M = B * T
+    return 24.0 * M * s.n_layer * s.d_model ** 2 + 2.0 * B * s.n_layer * s.d_model * T * (T + 1) \
+        + 2.0 * M * s.d_model * s.n_vocab
+
+
+def traffic_record(kernel_src: str):
+    """HBM bytes per lm_head launch from the stored rocprofv3 counter summary, or None when the
+    summary is missing or was taken on a different version of the kernel source."""
+    path = os.path.join(ROOT, "profiles", "lm_head_traffic.txt")
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    for line in open(path):
+        if "=" in line and not line.startswith("#"):
+            k, v = line.split("=", 1)
+            kv[k.strip()] = v.strip()
+    sha = hashlib.sha256(open(kernel_src, "rb").read()).hexdigest()[:16]
+    if kv.get("kernel_source_sha") != sha or "traffic_bytes_per_launch" not in kv:
+        return None
+    return float(kv["traffic_bytes_per_launch"])
+
+
+def cpu_baseline(weights: dict, tokens: np.ndarray, s: synth.ModelShape):
+    """Oracle (fp64 numpy) forward of one full sequence of the workload on the host cores."""
+    from oracle import gpt2_oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max((p.get("num_threads", 1) for p in threadpool_info()), default=1)
+    except Exception:  # pragma: no cover
+        cores = os.cpu_count() or 1
+    sample = tokens[:1]
+    O.forward(weights, tokens[:1, :4], s.n_head, s.n_layer)  # warm-up on a tiny input
+    t0 = time.perf_counter()
+    O.forward(weights, sample, s.n_head, s.n_layer)
+    dt = time.perf_counter() - t0
+    return {"value": sample.size / dt, "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"one sequence (B=1, T={sample.shape[1]}) of the workload, full forward incl. logits, "
+                      f"fp64 numpy, {dt:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", choices=sorted(WORKLOADS), default="small")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--breakdown", action="store_true", help="also time every launch of one extra forward")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the forward is not sharded "
+              "across GPUs in this build", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from decoder_only_transformer_gpt2_amd import gpt2
+
+    shape, B, T = WORKLOADS[args.workload]
+    M = B * T
+    w = synth.make_weights(shape, bf16=True)
+    m = gpt2.GPT2(gpt2.ModelConfig(n_vocab=shape.n_vocab, n_ctx=shape.n_ctx, d_model=shape.d_model,
+                                   n_head=shape.n_head, n_layer=shape.n_layer, d_mlp=shape.d_mlp, dtype="bf16"))
+    m.load_numpy(w)
+    tok_np = synth.make_tokens(B, T, shape.n_vocab)
+    tokens = torch.from_numpy(tok_np).cuda()
+    logits = torch.empty((B, T, shape.n_vocab), dtype=torch.float32, device="cuda")
+    am = torch.empty((B, T), dtype=torch.int32, device="cuda")
+    ws = m.workspace(B, T)
+    kinds = m.launches(with_argmax=True)
+    lm_idx = kinds.index("lm_head")
+    stream = torch.cuda.current_stream()
+
+    def raw_event():
+        e = torch.cuda.Event(enable_timing=True)
+        e.record(stream)
+        return e
+
+    for _ in range(args.warmup):
+        m.forward(tokens, logits, am, ws)
+    ev = [(raw_event(), raw_event()) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        before = [None] * (lm_idx + 1)
+        after = [None] * (lm_idx + 1)
+        before[lm_idx] = ev[i][0].cuda_event
+        after[lm_idx] = ev[i][1].cuda_event
+        m.forward_timed(tokens, logits, am, before, after, ws)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    if m.check(B, T, ws) != gpt2.OK:
+        raise RuntimeError("token check failed")
+
+    ms = (t1 - t0) * 1e3 / args.steps
+    lm_ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+    lm_flops = 2.0 * M * shape.d_model * shape.n_vocab
+    achieved = lm_flops / (lm_ms * 1e-3) / 1e12
+    flops = forward_flops(shape, B, T)
+    traffic = traffic_record(os.path.join(ROOT, "decoder_only_transformer_gpt2_amd", "csrc", "gemm_bf16.hip"))
+
+    out = {
+        "metric": METRIC, "value": M / (ms * 1e-3), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic (seeded random-init weights and token ids)",
+        "config": {"workload": f"GPT-2 {args.workload} forward, bf16 operands / fp32 accumulation, fp32 logits",
+                   "batch": B, "seq_len": T, "d_model": shape.d_model, "n_layer": shape.n_layer,
+                   "n_head": shape.n_head, "n_vocab": shape.n_vocab, "parallelism": "none (1 GPU)"},
+        "forward_tflops": flops / (ms * 1e-3) / 1e12,
+        "forward_mfma_frac": flops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+        "roofline": {"kernel": "lm_head GEMM (tied wte, fp32 logits + argmax partials)", "bound": "mfma",
+                     "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": achieved / PEAK_BF16_TFLOPS, "traffic": traffic, "avg_launch_ms": lm_ms,
+                     "flops_per_launch": lm_flops},
+    }
+
+    if args.breakdown:
+        evs = [(raw_event(), raw_event()) for _ in kinds]
+        torch.cuda.synchronize()
+        m.forward_timed(tokens, logits, am, [a.cuda_event for a, _ in evs], [b.cuda_event for _, b in evs], ws)
+        torch.cuda.synchronize()
+        per = {}
+        for k, (a, b) in zip(kinds, evs):
+            per[k] = per.get(k, 0.0) + a.elapsed_time(b)
+        out["breakdown_ms"] = per
+
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(w, tok_np, shape)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

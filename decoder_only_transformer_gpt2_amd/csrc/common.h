@@ -1,0 +1,73 @@
+// Device helpers and kernel-launcher declarations shared by the library's translation units.
+// gfx950 (CDNA4) only: 64-wide wavefronts, bf16 MFMA, 160 KB LDS per CU.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+#define GPT2_WAVE 64
+
+// bf16 is stored as its raw 16-bit pattern (uint16_t) in every buffer.
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t u16) { return __uint_as_float(u16 << 16); }
+
+// fp32 -> bf16, round to nearest even (the hardware conversion on gfx950).
+__device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
+    __bf16 b = (__bf16)f;
+    return __builtin_bit_cast(uint16_t, b);
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    return (uint32_t)f32_to_bf16_bits(lo) | ((uint32_t)f32_to_bf16_bits(hi) << 16);
+}
+
+// GELU forms. tanh form: 0.5 x (1 + tanh(sqrt(2/pi) (x + 0.044715 x^3))); erf form: 0.5 x (1 + erf(x/sqrt 2)).
+__device__ __forceinline__ float gelu_tanh_f32(float x) {
+    const float k0 = 0.7978845608028654f;  // sqrt(2/pi)
+    return 0.5f * x * (1.0f + tanhf(k0 * (x + 0.044715f * x * x * x)));
+}
+__device__ __forceinline__ float gelu_erf_f32(float x) { return 0.5f * x * (1.0f + erff(x * 0.7071067811865476f)); }
+
+// (value, index) maximum with ties broken toward the smaller index.
+__device__ __forceinline__ void argmax_merge(float& v, int& i, float v2, int i2) {
+    if (v2 > v || (v2 == v && i2 < i)) { v = v2; i = i2; }
+}
+
+// ---------------------------------------------------------------------------------------------
+// Launchers (each returns the hipError_t of the launch). Pointers are device pointers.
+// ---------------------------------------------------------------------------------------------
+namespace gpt2k {
+
+enum Epi { EPI_BIAS = 0, EPI_BIAS_GELU = 1, EPI_BIAS_RESIDUAL = 2, EPI_LOGITS = 3 };
+
+// Tile width along N of each GEMM flavour: the argmax partial count per row is ceil(N / BN).
+constexpr int kGemmBf16BN = 128;
+constexpr int kGemmF32BN = 64;
+
+hipError_t embed(const int32_t* tok, const void* wte, const void* wpe, float* x, int M, int T, int d,
+                 int n_vocab, bool bf16, int32_t* flags, hipStream_t s);
+int embed_flag_count(int M);
+
+hipError_t layernorm(const float* x, const float* g, const float* b, void* y, int M, int n, float eps,
+                     bool out_bf16, hipStream_t s);
+
+hipError_t gemm_bf16(const uint16_t* A, const uint16_t* W, const float* bias, void* C, int M, int N, int K,
+                     long ldc, int epi, int gelu_erf, float* amax_v, int32_t* amax_i, hipStream_t s);
+hipError_t gemm_f32(const float* A, const float* W, const float* bias, void* C, int M, int N, int K, long ldc,
+                    int epi, int gelu_erf, float* amax_v, int32_t* amax_i, hipStream_t s);
+
+hipError_t argmax_reduce(const float* pv, const int32_t* pi, int M, int n_part, int32_t* out, hipStream_t s);
+
+hipError_t attention_bf16(const uint16_t* q, const int64_t* qs, const uint16_t* k, const int64_t* ks,
+                          const uint16_t* v, const int64_t* vs, uint16_t* o, const int64_t* os, int B, int H,
+                          int T, hipStream_t s);
+hipError_t attention_f32(const float* q, const int64_t* qs, const float* k, const int64_t* ks, const float* v,
+                         const int64_t* vs, float* o, const int64_t* os, int B, int H, int T, hipStream_t s);
+
+// dst[i] = i < n_src ? convert(src[i]) : 0 for i < n_dst (element types fp32 or bf16).
+hipError_t convert(const void* src, bool src_bf16, void* dst, bool dst_bf16, long n_src, long n_dst,
+                   hipStream_t s);
+
+}  // namespace gpt2k

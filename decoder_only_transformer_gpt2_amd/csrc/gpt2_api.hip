@@ -1,0 +1,419 @@
+// Host side of the C ABI declared in include/gpt2.h: configuration checks, packed weight layout,
+// workspace carving and the launch sequence of the forward pass. Every device buffer belongs to
+// the caller; nothing here allocates device memory.
+#include <cstring>
+#include <new>
+#include <vector>
+
+#include "../../include/gpt2.h"
+#include "common.h"
+
+namespace {
+
+constexpr size_t kAlign = 256;
+constexpr int kRowPad = 256;
+
+size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+int64_t round_up(int64_t v, int64_t a) { return (v + a - 1) / a * a; }
+
+struct TensorSlot {
+    int64_t rows, cols;  // source shape (cols = 0 for a vector)
+    int64_t rows_padded;  // matrices: rows rounded up to kRowPad
+    size_t offset;        // byte offset in the packed buffer
+    bool matrix;
+};
+
+// Per-layer tensor indices inside the fixed source order.
+enum LayerTensor {
+    LN1_W = 0, LN1_B, ATTN_W, ATTN_B, APROJ_W, APROJ_B, LN2_W, LN2_B, FC_W, FC_B, MPROJ_W, MPROJ_B, PER_LAYER
+};
+
+struct WorkspaceLayout {
+    size_t x, a, qkv, o, hid, amax_v, amax_i, flags, total;
+    int64_t Mp;
+    int n_part;
+};
+
+}  // namespace
+
+struct gpt2_model {
+    gpt2_config_t cfg;
+    std::vector<TensorSlot> slots;
+    size_t weight_bytes = 0;
+    void* weights = nullptr;  // borrowed device pointer, set by gpt2_load_weights
+    bool loaded = false;
+};
+
+namespace {
+
+bool is_bf16(const gpt2_model* m) { return m->cfg.dtype == GPT2_BF16; }
+size_t act_size(const gpt2_model* m) { return is_bf16(m) ? 2 : 4; }
+
+void build_layout(gpt2_model* m) {
+    const gpt2_config_t& c = m->cfg;
+    const int64_t d = c.d_model, f = c.d_mlp;
+    auto mat = [&](int64_t r, int64_t k) { m->slots.push_back({r, k, round_up(r, kRowPad), 0, true}); };
+    auto vec = [&](int64_t n) { m->slots.push_back({n, 0, n, 0, false}); };
+    mat(c.n_vocab, d);  // wte (also the lm_head operand)
+    mat(c.n_ctx, d);    // wpe
+    for (int l = 0; l < c.n_layer; ++l) {
+        vec(d); vec(d);
+        mat(3 * d, d); vec(3 * d);
+        mat(d, d); vec(d);
+        vec(d); vec(d);
+        mat(f, d); vec(f);
+        mat(d, f); vec(d);
+    }
+    vec(d); vec(d);  // ln_f
+    size_t off = 0;
+    for (auto& s : m->slots) {
+        s.offset = off;
+        const size_t bytes = s.matrix ? (size_t)s.rows_padded * s.cols * act_size(m) : (size_t)s.rows * 4;
+        off = align_up(off + bytes, kAlign);
+    }
+    m->weight_bytes = off;
+}
+
+const void* wptr(const gpt2_model* m, int idx) { return static_cast<const char*>(m->weights) + m->slots[idx].offset; }
+int layer_idx(int l, int t) { return 2 + l * PER_LAYER + t; }
+
+WorkspaceLayout ws_layout(const gpt2_model* m, int B, int T) {
+    const gpt2_config_t& c = m->cfg;
+    WorkspaceLayout w{};
+    const int64_t M = (int64_t)B * T;
+    w.Mp = round_up(M, kRowPad);
+    const size_t as = act_size(m);
+    const int bn = is_bf16(m) ? gpt2k::kGemmBf16BN : gpt2k::kGemmF32BN;
+    w.n_part = (c.n_vocab + bn - 1) / bn;
+    size_t off = 0;
+    auto take = [&](size_t bytes) { size_t o = off; off = align_up(off + bytes, kAlign); return o; };
+    w.x = take((size_t)w.Mp * c.d_model * 4);
+    w.a = take((size_t)w.Mp * c.d_model * as);
+    w.qkv = take((size_t)w.Mp * 3 * c.d_model * as);
+    w.o = take((size_t)w.Mp * c.d_model * as);
+    w.hid = take((size_t)w.Mp * c.d_mlp * as);
+    w.amax_v = take((size_t)M * w.n_part * 4);
+    w.amax_i = take((size_t)M * w.n_part * 4);
+    w.flags = take((size_t)gpt2k::embed_flag_count((int)M) * 4);
+    w.total = off;
+    return w;
+}
+
+#define GPT2_HIP(call)                              \
+    do {                                            \
+        if ((call) != hipSuccess) return GPT2_EHIP; \
+    } while (0)
+
+gpt2_status check_run_args(const gpt2_model* m, const int32_t* tokens, int B, int T, const void* out, const void* ws,
+                           size_t ws_bytes) {
+    if (!m || !tokens || !out || !ws) return GPT2_EINVAL;
+    if (!m->loaded) return GPT2_ESTATE;
+    if (B < 1 || T < 1 || T > m->cfg.n_ctx) return GPT2_ESHAPE;
+    if ((int64_t)B * T > (int64_t)1 << 24) return GPT2_ESHAPE;
+    if (reinterpret_cast<uintptr_t>(ws) % kAlign) return GPT2_EINVAL;
+    if (ws_bytes < ws_layout(m, B, T).total) return GPT2_EWORKSPACE;
+    return GPT2_OK;
+}
+
+// Linear dispatch on the compute dtype.
+hipError_t linear(const gpt2_model* m, const void* A, int widx, int bidx, void* C, int M, int N, int K, long ldc,
+                  int epi, float* av, int32_t* ai, hipStream_t s) {
+    const float* bias = bidx >= 0 ? static_cast<const float*>(wptr(m, bidx)) : nullptr;
+    const int ge = m->cfg.gelu == GPT2_GELU_ERF;
+    if (is_bf16(m))
+        return gpt2k::gemm_bf16(static_cast<const uint16_t*>(A), static_cast<const uint16_t*>(wptr(m, widx)), bias, C, M,
+                                N, K, ldc, epi, ge, av, ai, s);
+    return gpt2k::gemm_f32(static_cast<const float*>(A), static_cast<const float*>(wptr(m, widx)), bias, C, M, N, K, ldc,
+                           epi, ge, av, ai, s);
+}
+
+// Enqueues launches in order, optionally recording caller events around them, or (dry) only
+// counts them and reports their kinds.
+struct Sequencer {
+    hipStream_t s;
+    hipEvent_t* before = nullptr;
+    hipEvent_t* after = nullptr;
+    int n_slots = 0;
+    int32_t* kinds = nullptr;
+    int cap = 0;
+    bool dry = false;
+    int idx = 0;
+
+    template <class F>
+    hipError_t run(int kind, F&& launch) {
+        if (kinds && idx < cap) kinds[idx] = kind;
+        if (dry) {
+            ++idx;
+            return hipSuccess;
+        }
+        const bool slot = idx < n_slots;
+        if (slot && before && before[idx] && hipEventRecord(before[idx], s) != hipSuccess) return hipErrorUnknown;
+        hipError_t e = launch();
+        if (e == hipSuccess && slot && after && after[idx]) e = hipEventRecord(after[idx], s);
+        ++idx;
+        return e;
+    }
+};
+
+#define GPT2_RUN(kind, expr)                                                   \
+    do {                                                                       \
+        if (q.run(kind, [&]() { return (expr); }) != hipSuccess) return GPT2_EHIP; \
+    } while (0)
+
+// Embedding and the first n_layers blocks; leaves the residual stream in the workspace's x.
+gpt2_status enqueue_trunk(const gpt2_model* m, const int32_t* tokens, int B, int T, int n_layers, char* ws,
+                          const WorkspaceLayout& w, Sequencer& q) {
+    const gpt2_config_t& c = m->cfg;
+    const hipStream_t s = q.s;
+    const int M = B * T, d = c.d_model, f = c.d_mlp, H = c.n_head;
+    const bool bf = is_bf16(m);
+    float* x = reinterpret_cast<float*>(ws + w.x);
+    void* a = ws + w.a;
+    void* qkv = ws + w.qkv;
+    void* o = ws + w.o;
+    void* hid = ws + w.hid;
+    GPT2_RUN(GPT2_K_EMBED, gpt2k::embed(tokens, wptr(m, 0), wptr(m, 1), x, M, T, d, c.n_vocab, bf,
+                                        reinterpret_cast<int32_t*>(ws + w.flags), s));
+    // q, k, v views of qkv [B, T, 3, H, 64]: strides (batch, head, token) in elements
+    const int64_t qs[3] = {(int64_t)T * 3 * d, 64, 3 * d};
+    const int64_t os[3] = {(int64_t)T * d, 64, d};
+    const size_t as = act_size(m);
+    for (int l = 0; l < n_layers; ++l) {
+        auto L = [&](int t) { return layer_idx(l, t); };
+        auto vecp = [&](int t) { return static_cast<const float*>(wptr(m, L(t))); };
+        GPT2_RUN(GPT2_K_LN, gpt2k::layernorm(x, vecp(LN1_W), vecp(LN1_B), a, M, d, c.ln_eps, bf, s));
+        GPT2_RUN(GPT2_K_QKV, linear(m, a, L(ATTN_W), L(ATTN_B), qkv, M, 3 * d, d, 3 * d, gpt2k::EPI_BIAS, nullptr,
+                                    nullptr, s));
+        const char* qb = static_cast<const char*>(qkv);
+        if (bf)
+            GPT2_RUN(GPT2_K_ATTN, gpt2k::attention_bf16(reinterpret_cast<const uint16_t*>(qb), qs,
+                                                        reinterpret_cast<const uint16_t*>(qb + d * as), qs,
+                                                        reinterpret_cast<const uint16_t*>(qb + 2 * d * as), qs,
+                                                        static_cast<uint16_t*>(o), os, B, H, T, s));
+        else
+            GPT2_RUN(GPT2_K_ATTN, gpt2k::attention_f32(reinterpret_cast<const float*>(qb), qs,
+                                                       reinterpret_cast<const float*>(qb + d * as), qs,
+                                                       reinterpret_cast<const float*>(qb + 2 * d * as), qs,
+                                                       static_cast<float*>(o), os, B, H, T, s));
+        GPT2_RUN(GPT2_K_ATTN_PROJ, linear(m, o, L(APROJ_W), L(APROJ_B), x, M, d, d, d, gpt2k::EPI_BIAS_RESIDUAL,
+                                          nullptr, nullptr, s));
+        GPT2_RUN(GPT2_K_LN, gpt2k::layernorm(x, vecp(LN2_W), vecp(LN2_B), a, M, d, c.ln_eps, bf, s));
+        GPT2_RUN(GPT2_K_FC, linear(m, a, L(FC_W), L(FC_B), hid, M, f, d, f, gpt2k::EPI_BIAS_GELU, nullptr, nullptr, s));
+        GPT2_RUN(GPT2_K_MLP_PROJ, linear(m, hid, L(MPROJ_W), L(MPROJ_B), x, M, d, f, d, gpt2k::EPI_BIAS_RESIDUAL,
+                                         nullptr, nullptr, s));
+    }
+    return GPT2_OK;
+}
+
+// The whole forward: trunk, ln_f, tied lm_head (+ argmax partials), argmax reduction.
+gpt2_status enqueue_forward(const gpt2_model* m, const int32_t* tokens, int B, int T, float* logits, int32_t* argmax,
+                            char* ws, Sequencer& q) {
+    const gpt2_config_t& c = m->cfg;
+    const hipStream_t s = q.s;
+    const WorkspaceLayout w = ws_layout(m, B, T);
+    const int M = B * T;
+    gpt2_status st = enqueue_trunk(m, tokens, B, T, c.n_layer, ws, w, q);
+    if (st != GPT2_OK) return st;
+    const int ln_f = 2 + c.n_layer * PER_LAYER;
+    GPT2_RUN(GPT2_K_LN_F, gpt2k::layernorm(reinterpret_cast<float*>(ws + w.x), static_cast<const float*>(wptr(m, ln_f)),
+                                           static_cast<const float*>(wptr(m, ln_f + 1)), ws + w.a, M, c.d_model,
+                                           c.ln_eps, is_bf16(m), s));
+    float* av = argmax ? reinterpret_cast<float*>(ws + w.amax_v) : nullptr;
+    int32_t* ai = argmax ? reinterpret_cast<int32_t*>(ws + w.amax_i) : nullptr;
+    GPT2_RUN(GPT2_K_LM_HEAD,
+             linear(m, ws + w.a, 0, -1, logits, M, c.n_vocab, c.d_model, c.n_vocab, gpt2k::EPI_LOGITS, av, ai, s));
+    if (argmax) GPT2_RUN(GPT2_K_ARGMAX, gpt2k::argmax_reduce(av, ai, M, w.n_part, argmax, s));
+    return GPT2_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+gpt2_status gpt2_config(const gpt2_config_t* cfg, gpt2_model** out) {
+    if (!cfg || !out) return GPT2_EINVAL;
+    *out = nullptr;
+    const gpt2_config_t& c = *cfg;
+    if (c.dtype != GPT2_F32 && c.dtype != GPT2_BF16) return GPT2_EINVAL;
+    if (c.gelu != GPT2_GELU_TANH && c.gelu != GPT2_GELU_ERF) return GPT2_EINVAL;
+    if (!(c.ln_eps > 0.f)) return GPT2_EINVAL;
+    if (c.n_vocab < 1 || c.n_ctx < 1 || c.d_model < 1 || c.n_head < 1 || c.n_layer < 1 || c.d_mlp < 1)
+        return GPT2_ESHAPE;
+    if (c.d_model % c.n_head != 0 || c.d_model / c.n_head != 64) return GPT2_ESHAPE;
+    if (c.d_model % 64 != 0 || c.d_mlp % 64 != 0 || c.d_model > 4096 || c.n_ctx > 65536) return GPT2_ESHAPE;
+    gpt2_model* m = new (std::nothrow) gpt2_model();
+    if (!m) return GPT2_EINVAL;
+    m->cfg = c;
+    build_layout(m);
+    *out = m;
+    return GPT2_OK;
+}
+
+void gpt2_destroy(gpt2_model* m) { delete m; }
+
+int32_t gpt2_n_tensors(const gpt2_model* m) { return m ? (int32_t)m->slots.size() : 0; }
+
+gpt2_status gpt2_tensor_shape(const gpt2_model* m, int32_t i, int64_t* rows, int64_t* cols) {
+    if (!m || !rows || !cols) return GPT2_EINVAL;
+    if (i < 0 || i >= (int32_t)m->slots.size()) return GPT2_EINVAL;
+    *rows = m->slots[i].rows;
+    *cols = m->slots[i].cols;
+    return GPT2_OK;
+}
+
+size_t gpt2_weight_bytes(const gpt2_model* m) { return m ? m->weight_bytes : 0; }
+
+size_t gpt2_workspace_bytes(const gpt2_model* m, int32_t B, int32_t T) {
+    if (!m || B < 1 || T < 1 || T > m->cfg.n_ctx || (int64_t)B * T > (int64_t)1 << 24) return 0;
+    return ws_layout(m, B, T).total;
+}
+
+gpt2_status gpt2_load_weights(gpt2_model* m, const void* const* src, int32_t n_src, int32_t src_dtype, void* dst,
+                              size_t dst_bytes, hipStream_t stream) {
+    if (!m || !src || !dst) return GPT2_EINVAL;
+    if (n_src != (int32_t)m->slots.size()) return GPT2_EINVAL;
+    if (src_dtype != GPT2_F32 && src_dtype != GPT2_BF16) return GPT2_EINVAL;
+    if (reinterpret_cast<uintptr_t>(dst) % kAlign) return GPT2_EINVAL;
+    if (dst_bytes < m->weight_bytes) return GPT2_EWORKSPACE;
+    for (int i = 0; i < n_src; ++i)
+        if (!src[i]) return GPT2_EINVAL;
+    const bool sb = src_dtype == GPT2_BF16;
+    for (int i = 0; i < n_src; ++i) {
+        const TensorSlot& s = m->slots[i];
+        char* d = static_cast<char*>(dst) + s.offset;
+        if (s.matrix) {
+            const long n = (long)s.rows * s.cols, np = (long)s.rows_padded * s.cols;
+            GPT2_HIP(gpt2k::convert(src[i], sb, d, is_bf16(m), n, np, stream));
+        } else {
+            GPT2_HIP(gpt2k::convert(src[i], sb, d, false, s.rows, s.rows, stream));
+        }
+    }
+    m->weights = dst;
+    m->loaded = true;
+    return GPT2_OK;
+}
+
+gpt2_status gpt2_forward(const gpt2_model* m, const int32_t* tokens, int32_t B, int32_t T, float* logits,
+                         int32_t* argmax, void* ws_dev, size_t ws_bytes, hipStream_t s) {
+    const gpt2_status st = check_run_args(m, tokens, B, T, logits, ws_dev, ws_bytes);
+    if (st != GPT2_OK) return st;
+    Sequencer q{s};
+    return enqueue_forward(m, tokens, B, T, logits, argmax, static_cast<char*>(ws_dev), q);
+}
+
+gpt2_status gpt2_forward_timed(const gpt2_model* m, const int32_t* tokens, int32_t B, int32_t T, float* logits,
+                               int32_t* argmax, void* ws_dev, size_t ws_bytes, hipStream_t s, hipEvent_t* ev_before,
+                               hipEvent_t* ev_after, int32_t n_slots) {
+    const gpt2_status st = check_run_args(m, tokens, B, T, logits, ws_dev, ws_bytes);
+    if (st != GPT2_OK) return st;
+    if (n_slots < 0) return GPT2_EINVAL;
+    Sequencer q{s};
+    q.before = ev_before;
+    q.after = ev_after;
+    q.n_slots = n_slots;
+    return enqueue_forward(m, tokens, B, T, logits, argmax, static_cast<char*>(ws_dev), q);
+}
+
+int32_t gpt2_forward_launches(const gpt2_model* m, int32_t with_argmax, int32_t* kinds, int32_t cap) {
+    if (!m) return 0;
+    Sequencer q{nullptr};
+    q.dry = true;
+    q.kinds = kinds;
+    q.cap = kinds ? cap : 0;
+    // a dry run touches no memory: the pointers only need to be non-null where the path branches
+    int32_t dummy = 0;
+    if (enqueue_forward(m, &dummy, 1, 1, nullptr, with_argmax ? &dummy : nullptr, nullptr, q) != GPT2_OK) return 0;
+    return q.idx;
+}
+
+gpt2_status gpt2_forward_debug(const gpt2_model* m, const int32_t* tokens, int32_t B, int32_t T, int32_t n_layers,
+                               float* resid, void* ws_dev, size_t ws_bytes, hipStream_t s) {
+    gpt2_status st = check_run_args(m, tokens, B, T, resid, ws_dev, ws_bytes);
+    if (st != GPT2_OK) return st;
+    if (n_layers < 0 || n_layers > m->cfg.n_layer) return GPT2_EINVAL;
+    char* ws = static_cast<char*>(ws_dev);
+    const WorkspaceLayout w = ws_layout(m, B, T);
+    Sequencer q{s};
+    st = enqueue_trunk(m, tokens, B, T, n_layers, ws, w, q);
+    if (st != GPT2_OK) return st;
+    GPT2_HIP(hipMemcpyAsync(resid, ws + w.x, (size_t)B * T * m->cfg.d_model * 4, hipMemcpyDeviceToDevice, s));
+    return GPT2_OK;
+}
+
+gpt2_status gpt2_check(const gpt2_model* m, const void* ws_dev, int32_t B, int32_t T, hipStream_t s) {
+    if (!m || !ws_dev) return GPT2_EINVAL;
+    if (B < 1 || T < 1 || T > m->cfg.n_ctx) return GPT2_ESHAPE;
+    const WorkspaceLayout w = ws_layout(m, B, T);
+    const int n = gpt2k::embed_flag_count(B * T);
+    std::vector<int32_t> flags(n);
+    GPT2_HIP(hipStreamSynchronize(s));
+    GPT2_HIP(hipMemcpy(flags.data(), static_cast<const char*>(ws_dev) + w.flags, n * sizeof(int32_t),
+                       hipMemcpyDeviceToHost));
+    for (int i = 0; i < n; ++i)
+        if (flags[i]) return GPT2_ETOKEN;
+    return GPT2_OK;
+}
+
+gpt2_status gpt2_attention(const void* q, const int64_t* qs, const void* k, const int64_t* ks, const void* v,
+                           const int64_t* vs, void* o, const int64_t* os, int32_t B, int32_t H, int32_t T, int32_t dh,
+                           int32_t dtype, hipStream_t s) {
+    if (!q || !k || !v || !o || !qs || !ks || !vs || !os) return GPT2_EINVAL;
+    if (dtype != GPT2_F32 && dtype != GPT2_BF16) return GPT2_EINVAL;
+    if (dh != 64 || B < 1 || H < 1 || T < 1) return GPT2_ESHAPE;
+    if ((int64_t)B * H * ((T + 127) / 128) > 0x7fffffff) return GPT2_ESHAPE;
+    for (const int64_t* st : {qs, ks, vs, os})
+        for (int i = 0; i < 3; ++i)
+            if (st[i] < 0 || st[i] % 8) return GPT2_EINVAL;
+    for (const void* p : {q, k, v, static_cast<const void*>(o)})
+        if (reinterpret_cast<uintptr_t>(p) % 16) return GPT2_EINVAL;
+    if (dtype == GPT2_BF16)
+        GPT2_HIP(gpt2k::attention_bf16(static_cast<const uint16_t*>(q), qs, static_cast<const uint16_t*>(k), ks,
+                                       static_cast<const uint16_t*>(v), vs, static_cast<uint16_t*>(o), os, B, H, T, s));
+    else
+        GPT2_HIP(gpt2k::attention_f32(static_cast<const float*>(q), qs, static_cast<const float*>(k), ks,
+                                      static_cast<const float*>(v), vs, static_cast<float*>(o), os, B, H, T, s));
+    return GPT2_OK;
+}
+
+gpt2_status gpt2_layernorm(const float* x, const float* g, const float* b, void* y, int32_t M, int32_t n, float eps,
+                           int32_t out_dtype, hipStream_t s) {
+    if (!x || !g || !b || !y) return GPT2_EINVAL;
+    if (out_dtype != GPT2_F32 && out_dtype != GPT2_BF16) return GPT2_EINVAL;
+    if (M < 1 || n < 4 || n % 4 || n > 4096) return GPT2_ESHAPE;
+    if (!(eps > 0.f)) return GPT2_EINVAL;
+    GPT2_HIP(gpt2k::layernorm(x, g, b, y, M, n, eps, out_dtype == GPT2_BF16, s));
+    return GPT2_OK;
+}
+
+gpt2_status gpt2_linear(const void* A, const void* W, const float* bias, void* C, int32_t M, int32_t N, int32_t K,
+                        int64_t ldc, int32_t dtype, int32_t epi, int32_t gelu, hipStream_t s) {
+    if (!A || !W || !C) return GPT2_EINVAL;
+    if (dtype != GPT2_F32 && dtype != GPT2_BF16) return GPT2_EINVAL;
+    if (epi < GPT2_EPI_BIAS || epi > GPT2_EPI_LOGITS) return GPT2_EINVAL;
+    if (gelu != GPT2_GELU_TANH && gelu != GPT2_GELU_ERF) return GPT2_EINVAL;
+    if (epi != GPT2_EPI_LOGITS && !bias) return GPT2_EINVAL;
+    if (M < 1 || N < 1 || K < 64 || K % 64 || ldc < N) return GPT2_ESHAPE;
+    const int ge = gelu == GPT2_GELU_ERF;
+    if (dtype == GPT2_BF16)
+        GPT2_HIP(gpt2k::gemm_bf16(static_cast<const uint16_t*>(A), static_cast<const uint16_t*>(W), bias, C, M, N, K, ldc,
+                                  epi, ge, nullptr, nullptr, s));
+    else
+        GPT2_HIP(gpt2k::gemm_f32(static_cast<const float*>(A), static_cast<const float*>(W), bias, C, M, N, K, ldc, epi,
+                                 ge, nullptr, nullptr, s));
+    return GPT2_OK;
+}
+
+const char* gpt2_strerror(gpt2_status s) {
+    switch (s) {
+        case GPT2_OK: return "ok";
+        case GPT2_EINVAL: return "invalid argument";
+        case GPT2_ESHAPE: return "unsupported or inconsistent shape";
+        case GPT2_EWORKSPACE: return "buffer smaller than required";
+        case GPT2_ETOKEN: return "token id outside [0, n_vocab)";
+        case GPT2_EHIP: return "HIP runtime error";
+        case GPT2_ESTATE: return "call made in the wrong state";
+    }
+    return "unknown status";
+}
+
+}  // extern "C"

@@ -1,0 +1,195 @@
+// Row-wise HBM-bound kernels: embedding gather-add, LayerNorm, argmax reduction, weight packing.
+#include "common.h"
+
+namespace gpt2k {
+namespace {
+
+constexpr int kRowsPerBlock = 4;  // one wavefront per row, four wavefronts per workgroup
+
+// x[m, :] = wte[tok[m], :] + wpe[m mod T, :]  (token embedding plus learned position embedding,
+// positions from 0; "从零手写GPT-2" §4.1 forward step 1, "复现GPT-2 124M" §2.1).
+// Tables are bf16 or fp32; the sum is one fp32 add of the two exactly-upcast entries, so it equals
+// the correctly rounded fp32 value of the exact sum. An id outside [0, n_vocab) is clamped for the
+// read and recorded in flags[blockIdx.x] (every block writes its slot on every launch).
+template <bool BF16>
+__global__ __launch_bounds__(256) void embed_kernel(const int32_t* __restrict__ tok, const void* __restrict__ wte,
+                                                    const void* __restrict__ wpe, float* __restrict__ x, int M,
+                                                    int T, int d, int n_vocab, int32_t* __restrict__ flags) {
+    const int wave = threadIdx.x / GPT2_WAVE, lane = threadIdx.x % GPT2_WAVE;
+    const int row = blockIdx.x * kRowsPerBlock + wave;
+    int bad = 0;
+    if (row < M) {
+        int t = tok[row];
+        if (t < 0 || t >= n_vocab) {
+            bad = 1;
+            t = t < 0 ? 0 : n_vocab - 1;
+        }
+        const int pos = row % T;
+        float4* xr = reinterpret_cast<float4*>(x + (size_t)row * d);
+        const int nq = d / 4;
+        if (BF16) {
+            const uint2* er = reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(wte) + (size_t)t * d);
+            const uint2* pr = reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(wpe) + (size_t)pos * d);
+            for (int c = lane; c < nq; c += GPT2_WAVE) {
+                const uint2 e = er[c], p = pr[c];
+                float4 o;
+                o.x = bf16_bits_to_f32(e.x & 0xffffu) + bf16_bits_to_f32(p.x & 0xffffu);
+                o.y = bf16_bits_to_f32(e.x >> 16) + bf16_bits_to_f32(p.x >> 16);
+                o.z = bf16_bits_to_f32(e.y & 0xffffu) + bf16_bits_to_f32(p.y & 0xffffu);
+                o.w = bf16_bits_to_f32(e.y >> 16) + bf16_bits_to_f32(p.y >> 16);
+                xr[c] = o;
+            }
+        } else {
+            const float4* er = reinterpret_cast<const float4*>(static_cast<const float*>(wte) + (size_t)t * d);
+            const float4* pr = reinterpret_cast<const float4*>(static_cast<const float*>(wpe) + (size_t)pos * d);
+            for (int c = lane; c < nq; c += GPT2_WAVE) {
+                const float4 e = er[c], p = pr[c];
+                xr[c] = make_float4(e.x + p.x, e.y + p.y, e.z + p.z, e.w + p.w);
+            }
+        }
+    }
+    const int any_bad = __syncthreads_or(bad);
+    if (threadIdx.x == 0) flags[blockIdx.x] = any_bad;
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, GPT2_WAVE);
+    return v;
+}
+
+// LayerNorm with the biased variance ("复现GPT-2 124M" §2.1: unbiased=False; eps inside the square
+// root, "从零手写GPT-2" §3.2). One wavefront per row; the row stays in registers between the two
+// passes (mean, then the centred sum of squares), so x is read from memory once.
+template <int NV, bool OUT_BF16>
+__global__ __launch_bounds__(256) void layernorm_kernel(const float* __restrict__ x, const float* __restrict__ g,
+                                                        const float* __restrict__ b, void* __restrict__ y, int M,
+                                                        int n, float eps) {
+    const int wave = threadIdx.x / GPT2_WAVE, lane = threadIdx.x % GPT2_WAVE;
+    const int row = blockIdx.x * kRowsPerBlock + wave;
+    if (row >= M) return;
+    const int nq = n / 4;
+    const float4* xr = reinterpret_cast<const float4*>(x + (size_t)row * n);
+    float4 v[NV];
+    float s = 0.f;
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+        const int c = i * GPT2_WAVE + lane;
+        v[i] = c < nq ? xr[c] : make_float4(0.f, 0.f, 0.f, 0.f);
+        s += (v[i].x + v[i].y) + (v[i].z + v[i].w);
+    }
+    const float mean = wave_sum(s) / (float)n;
+    float q = 0.f;
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+        const int c = i * GPT2_WAVE + lane;
+        if (c < nq) {
+            const float a0 = v[i].x - mean, a1 = v[i].y - mean, a2 = v[i].z - mean, a3 = v[i].w - mean;
+            q += (a0 * a0 + a1 * a1) + (a2 * a2 + a3 * a3);
+        }
+    }
+    const float var = wave_sum(q) / (float)n;
+    const float rstd = 1.0f / sqrtf(var + eps);
+    const float4* g4 = reinterpret_cast<const float4*>(g);
+    const float4* b4 = reinterpret_cast<const float4*>(b);
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+        const int c = i * GPT2_WAVE + lane;
+        if (c < nq) {
+            const float4 gg = g4[c], bb = b4[c];
+            float4 o;
+            o.x = (v[i].x - mean) * rstd * gg.x + bb.x;
+            o.y = (v[i].y - mean) * rstd * gg.y + bb.y;
+            o.z = (v[i].z - mean) * rstd * gg.z + bb.z;
+            o.w = (v[i].w - mean) * rstd * gg.w + bb.w;
+            if (OUT_BF16) {
+                uint2 p;
+                p.x = pack_bf16x2(o.x, o.y);
+                p.y = pack_bf16x2(o.z, o.w);
+                reinterpret_cast<uint2*>(static_cast<uint16_t*>(y) + (size_t)row * n)[c] = p;
+            } else {
+                reinterpret_cast<float4*>(static_cast<float*>(y) + (size_t)row * n)[c] = o;
+            }
+        }
+    }
+}
+
+// Row argmax from per-tile partials (value, index) written by the logits GEMM epilogue.
+__global__ __launch_bounds__(256) void argmax_reduce_kernel(const float* __restrict__ pv, const int32_t* __restrict__ pi,
+                                                            int M, int n_part, int32_t* __restrict__ out) {
+    const int wave = threadIdx.x / GPT2_WAVE, lane = threadIdx.x % GPT2_WAVE;
+    const int row = blockIdx.x * kRowsPerBlock + wave;
+    if (row >= M) return;
+    float bv = -INFINITY;
+    int bi = 0x7fffffff;
+    for (int j = lane; j < n_part; j += GPT2_WAVE)
+        argmax_merge(bv, bi, pv[(size_t)row * n_part + j], pi[(size_t)row * n_part + j]);
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) {
+        const float v2 = __shfl_xor(bv, o, GPT2_WAVE);
+        const int i2 = __shfl_xor(bi, o, GPT2_WAVE);
+        argmax_merge(bv, bi, v2, i2);
+    }
+    if (lane == 0) out[row] = bi;
+}
+
+__global__ __launch_bounds__(256) void convert_kernel(const void* __restrict__ src, int src_bf16, void* __restrict__ dst,
+                                                      int dst_bf16, long n_src, long n_dst) {
+    for (long i = (long)blockIdx.x * blockDim.x + threadIdx.x; i < n_dst; i += (long)gridDim.x * blockDim.x) {
+        float v = 0.f;
+        if (i < n_src)
+            v = src_bf16 ? bf16_bits_to_f32(static_cast<const uint16_t*>(src)[i]) : static_cast<const float*>(src)[i];
+        if (dst_bf16)
+            static_cast<uint16_t*>(dst)[i] = f32_to_bf16_bits(v);
+        else
+            static_cast<float*>(dst)[i] = v;
+    }
+}
+
+template <int NV>
+hipError_t launch_ln(const float* x, const float* g, const float* b, void* y, int M, int n, float eps, bool out_bf16,
+                     hipStream_t s) {
+    dim3 grid((M + kRowsPerBlock - 1) / kRowsPerBlock), block(256);
+    if (out_bf16)
+        layernorm_kernel<NV, true><<<grid, block, 0, s>>>(x, g, b, y, M, n, eps);
+    else
+        layernorm_kernel<NV, false><<<grid, block, 0, s>>>(x, g, b, y, M, n, eps);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+int embed_flag_count(int M) { return (M + kRowsPerBlock - 1) / kRowsPerBlock; }
+
+hipError_t embed(const int32_t* tok, const void* wte, const void* wpe, float* x, int M, int T, int d, int n_vocab,
+                 bool bf16, int32_t* flags, hipStream_t s) {
+    dim3 grid(embed_flag_count(M)), block(256);
+    if (bf16)
+        embed_kernel<true><<<grid, block, 0, s>>>(tok, wte, wpe, x, M, T, d, n_vocab, flags);
+    else
+        embed_kernel<false><<<grid, block, 0, s>>>(tok, wte, wpe, x, M, T, d, n_vocab, flags);
+    return hipGetLastError();
+}
+
+hipError_t layernorm(const float* x, const float* g, const float* b, void* y, int M, int n, float eps, bool out_bf16,
+                     hipStream_t s) {
+    const int nq = n / 4;
+    if (nq <= 4 * GPT2_WAVE) return launch_ln<4>(x, g, b, y, M, n, eps, out_bf16, s);
+    if (nq <= 8 * GPT2_WAVE) return launch_ln<8>(x, g, b, y, M, n, eps, out_bf16, s);
+    return launch_ln<16>(x, g, b, y, M, n, eps, out_bf16, s);  // n <= 4096 (checked by the callers)
+}
+
+hipError_t argmax_reduce(const float* pv, const int32_t* pi, int M, int n_part, int32_t* out, hipStream_t s) {
+    argmax_reduce_kernel<<<dim3((M + kRowsPerBlock - 1) / kRowsPerBlock), dim3(256), 0, s>>>(pv, pi, M, n_part, out);
+    return hipGetLastError();
+}
+
+hipError_t convert(const void* src, bool src_bf16, void* dst, bool dst_bf16, long n_src, long n_dst, hipStream_t s) {
+    if (n_dst <= 0) return hipSuccess;
+    long blocks = (n_dst + 255) / 256;
+    if (blocks > 65536) blocks = 65536;
+    convert_kernel<<<dim3((unsigned)blocks), dim3(256), 0, s>>>(src, src_bf16, dst, dst_bf16, n_src, n_dst);
+    return hipGetLastError();
+}
+
+}  // namespace gpt2k

@@ -1,0 +1,343 @@
+"""GPU parity: the HIP path through the C ABI against the CPU fp64 oracle on the same seeded inputs.
+
+Tolerances (written here, derived in the design notes):
+  * embedding: bit-exact (one correctly rounded fp32 add on both sides);
+  * fp32 mode: per-row relative L2 error of the logits <= 1e-4;
+  * bf16 mode: max |logit error| <= 5e-2 and top-1 agreement with the oracle >= 99%;
+  * argmax: bit-exact against the first maximum of the GPU's own fp32 logits;
+  * single ops (LayerNorm, linear, attention): bounds from the roundings each op performs.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import gpt2_oracle as O
+from decoder_only_transformer_gpt2_amd import synth
+
+pytestmark = pytest.mark.gpu
+
+BF16_EPS = 2.0 ** -8  # bf16 unit roundoff is 2^-9; one ulp relative spacing is at most 2^-7
+
+
+@pytest.fixture(scope="session")
+def g():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU visible")
+    from decoder_only_transformer_gpt2_amd import gpt2
+    gpt2.lib()  # raises when the library has not been built
+    return gpt2
+
+
+def log(msg):
+    print(msg, flush=True)
+
+
+def model(g, shape, dtype, perturbed=False, gelu="tanh"):
+    w = synth.make_weights(shape, bf16=(dtype == "bf16"), perturbed=perturbed)
+    m = g.GPT2(g.ModelConfig(n_vocab=shape.n_vocab, n_ctx=shape.n_ctx, d_model=shape.d_model, n_head=shape.n_head,
+                             n_layer=shape.n_layer, d_mlp=shape.d_mlp, dtype=dtype, gelu=gelu))
+    m.load_numpy(w)
+    return m, w
+
+
+@pytest.fixture(scope="session")
+def small_f32(g):
+    return model(g, synth.GPT2_SMALL, "f32")
+
+
+@pytest.fixture(scope="session")
+def small_bf16(g):
+    return model(g, synth.GPT2_SMALL, "bf16")
+
+
+def dev_tokens(tok):
+    return torch.from_numpy(np.ascontiguousarray(tok, dtype=np.int32)).cuda()
+
+
+def row_rel_l2(gpu, ref):
+    gpu = gpu.reshape(-1, gpu.shape[-1]).astype(np.float64)
+    ref = ref.reshape(-1, ref.shape[-1])
+    return np.linalg.norm(gpu - ref, axis=1) / np.linalg.norm(ref, axis=1)
+
+
+def first_argmax(a):
+    return np.argmax(a, axis=-1)
+
+
+# ------------------------------------------------------------------------------------ embedding
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_embedding_bit_exact(g, small_f32, small_bf16, dtype):
+    m, w = small_f32 if dtype == "f32" else small_bf16
+    tok = synth.make_tokens(3, 77)
+    log(f"embedding {dtype} B=3 T=77")
+    x = m.forward_debug(dev_tokens(tok), 0).cpu().numpy()
+    ref = O.embed(w["wte"], w["wpe"], tok).astype(np.float32)
+    assert np.array_equal(x.view(np.uint32), ref.view(np.uint32))
+
+
+# ------------------------------------------------------------------------------------ LayerNorm
+@pytest.mark.parametrize("n", [768, 1024, 1600])
+@pytest.mark.parametrize("out", ["f32", "bf16"])
+def test_layernorm(g, n, out):
+    r = np.random.Generator(np.random.PCG64(11))
+    M = 37
+    x = (r.standard_normal((M, n)) * 2 + 0.5).astype(np.float32)
+    gam = (1 + 0.1 * r.standard_normal(n)).astype(np.float32)
+    bet = (0.02 * r.standard_normal(n)).astype(np.float32)
+    log(f"layernorm n={n} out={out}")
+    y = g.layernorm(torch.from_numpy(x).cuda(), torch.from_numpy(gam).cuda(), torch.from_numpy(bet).cuda(), 1e-5,
+                    torch.float32 if out == "f32" else torch.bfloat16)
+    y = y.float().cpu().numpy().astype(np.float64)
+    ref = O.layer_norm(x, gam, bet, 1e-5)
+    if out == "f32":
+        assert np.max(np.abs(y - ref)) < 2e-5
+    else:
+        # one rounding to bf16 of a value carrying fp32 error
+        assert np.all(np.abs(y - ref) <= BF16_EPS * np.abs(ref) / 2 + 1e-5)
+
+
+# ---------------------------------------------------------------------------------------- linear
+def _pad_rows(a, mult=256):
+    rows = -(-a.shape[0] // mult) * mult
+    out = np.zeros((rows,) + a.shape[1:], dtype=a.dtype)
+    out[:a.shape[0]] = a
+    return out
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("epi", [0, 1, 2, 3])
+@pytest.mark.parametrize("M,N,K", [(300, 200, 128), (256, 2304, 768), (77, 1000, 3072)])
+def test_linear(g, dtype, epi, M, N, K):
+    r = np.random.Generator(np.random.PCG64(100 + epi))
+    A = synth.round_bf16(r.standard_normal((M, K)).astype(np.float32))
+    W = synth.round_bf16((0.02 * r.standard_normal((N, K))).astype(np.float32))
+    b = (0.02 * r.standard_normal(N)).astype(np.float32)
+    C0 = r.standard_normal((M, N)).astype(np.float32)
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    Ad = torch.from_numpy(_pad_rows(A)).cuda().to(tdt)
+    Wd = torch.from_numpy(_pad_rows(W)).cuda().to(tdt)
+    bd = torch.from_numpy(b).cuda()
+    out_dt = torch.float32 if (epi >= 2 or dtype == "f32") else torch.bfloat16
+    C = torch.from_numpy(C0).cuda().to(out_dt) if epi == 2 else torch.empty((M, N), dtype=out_dt, device="cuda")
+    log(f"linear {dtype} epi={epi} M={M} N={N} K={K}")
+    g.linear(Ad, Wd, bd, C, M, N, K, epi)
+    got = C.float().cpu().numpy().astype(np.float64)
+    acc = O.linear(A, W, None if epi == 3 else b)
+    if epi == 1:
+        ref = O.gelu_tanh(acc)
+    elif epi == 2:
+        ref = C0 + acc
+    else:
+        ref = acc
+    # fp32 accumulation of exact bf16 products: error well under 1e-5 of the sum of |terms|
+    scale = O.linear(np.abs(A), np.abs(W), None) + 1.0
+    tol = 1e-5 * scale
+    if out_dt == torch.bfloat16:
+        tol = tol + BF16_EPS / 2 * np.abs(ref)
+    assert np.all(np.abs(got - ref) <= tol), float(np.max(np.abs(got - ref) - tol))
+
+
+def test_linear_gelu_erf_variant(g):
+    r = np.random.Generator(np.random.PCG64(7))
+    M, N, K = 128, 256, 64
+    A = synth.round_bf16(r.standard_normal((M, K)).astype(np.float32))
+    W = synth.round_bf16((0.3 * r.standard_normal((N, K))).astype(np.float32))
+    b = np.zeros(N, np.float32)
+    C = torch.empty((M, N), dtype=torch.float32, device="cuda")
+    g.linear(torch.from_numpy(_pad_rows(A)).cuda(), torch.from_numpy(_pad_rows(W)).cuda(), torch.from_numpy(b).cuda(),
+             C, M, N, K, 1, g.GELU_ERF)
+    ref = O.gelu_erf(O.linear(A, W, None))
+    assert np.max(np.abs(C.cpu().numpy() - ref)) < 1e-5
+    assert np.max(np.abs(C.cpu().numpy() - O.gelu_tanh(O.linear(A, W, None)))) > 1e-5
+
+
+# ------------------------------------------------------------------------------------- attention
+def attn_tolerance(q, k, v, ref, dtype):
+    if dtype == "f32":
+        return 2e-5 * (np.abs(ref) + 1)
+    # bf16: the probabilities and the output are rounded to bf16 once each
+    pv = O.causal_attention(q, k, np.abs(v))
+    return BF16_EPS * (np.abs(ref) + pv) + 1e-4
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("B,H,T", [(1, 1, 1), (2, 3, 64), (2, 3, 200), (1, 2, 1024)])
+def test_attention_small(g, dtype, B, H, T):
+    q, k, v = synth.make_qkv(B, H, T, 64, bf16=True)
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    qd, kd, vd = (torch.from_numpy(a).cuda().to(tdt) for a in (q, k, v))
+    log(f"attention {dtype} B={B} H={H} T={T}")
+    o = g.attention(qd, kd, vd).float().cpu().numpy()
+    ref = O.causal_attention(q, k, v)
+    tol = attn_tolerance(q, k, v, ref, dtype)
+    assert np.all(np.abs(o - ref) <= tol), float(np.max(np.abs(o - ref) - tol))
+
+
+def test_attention_strided_views(g):
+    """q, k, v read straight out of a fused [B, T, 3, H, 64] buffer, output into [B, T, H, 64]."""
+    B, T, H = 2, 130, 4
+    r = np.random.Generator(np.random.PCG64(5))
+    qkv = synth.round_bf16(r.standard_normal((B, T, 3, H, 64)).astype(np.float32))
+    d = torch.from_numpy(qkv).cuda().to(torch.bfloat16)
+    q, k, v = (d[:, :, i].transpose(1, 2) for i in range(3))
+    o_buf = torch.zeros((B, T, H, 64), dtype=torch.bfloat16, device="cuda")
+    g.attention(q, k, v, o_buf.transpose(1, 2))
+    got = o_buf.float().cpu().numpy().transpose(0, 2, 1, 3)
+    qn, kn, vn = (qkv[:, :, i].transpose(0, 2, 1, 3) for i in range(3))
+    ref = O.causal_attention(qn, kn, vn)
+    assert np.all(np.abs(got - ref) <= attn_tolerance(qn, kn, vn, ref, "bf16"))
+
+
+def test_attention_config2_sampled(g):
+    """B=8, H=12, T=1024, dh=64 (the isolated-attention workload); oracle on sampled heads."""
+    B, H, T = 8, 12, 1024
+    q, k, v = synth.make_qkv(B, H, T, 64, bf16=True)
+    qd, kd, vd = (torch.from_numpy(a).cuda().to(torch.bfloat16) for a in (q, k, v))
+    log("attention config2 B=8 H=12 T=1024")
+    o = g.attention(qd, kd, vd).float().cpu().numpy()
+    for b, h in [(0, 0), (3, 7), (7, 11), (5, 2)]:
+        ref = O.causal_attention(q[b, h], k[b, h], v[b, h])
+        tol = attn_tolerance(q[b, h], k[b, h], v[b, h], ref, "bf16")
+        assert np.all(np.abs(o[b, h] - ref) <= tol), (b, h)
+    # property at full size: row 0 of every head is v_0 (up to the bf16 rounding of the output)
+    assert np.allclose(o[:, :, 0], v[:, :, 0], rtol=BF16_EPS, atol=0)
+
+
+# ------------------------------------------------------------------------------- whole forward
+def test_forward_f32_demo_shape(g, small_f32):
+    m, w = small_f32
+    tok = synth.make_tokens(2, 4)
+    log("forward f32 B=2 T=4")
+    logits, am = m.forward(dev_tokens(tok))
+    assert tuple(logits.shape) == (2, 4, 50257)
+    assert m.check(2, 4) == g.OK
+    got = logits.cpu().numpy()
+    ref = O.forward(w, tok, 12, 12)
+    err = row_rel_l2(got, ref)
+    log(f"  max row rel L2 = {err.max():.3e}")
+    assert err.max() <= 1e-4
+    assert np.array_equal(am.cpu().numpy(), first_argmax(got))
+    assert np.array_equal(first_argmax(got), first_argmax(ref))
+
+
+@pytest.mark.parametrize("perturbed,B,T", [(False, 3, 77), (True, 2, 129)])
+def test_forward_f32_ragged(g, small_f32, perturbed, B, T):
+    m, w = small_f32 if not perturbed else model(g, synth.GPT2_SMALL, "f32", perturbed=True)
+    tok = synth.make_tokens(B, T)
+    log(f"forward f32 perturbed={perturbed} B={B} T={T}")
+    logits, am = m.forward(dev_tokens(tok))
+    got = logits.cpu().numpy()
+    ref = O.forward(w, tok, 12, 12)
+    err = row_rel_l2(got, ref)
+    log(f"  max row rel L2 = {err.max():.3e}")
+    assert err.max() <= 1e-4
+    assert np.array_equal(am.cpu().numpy(), first_argmax(got))
+
+
+def test_forward_f32_per_block(g, small_f32):
+    m, w = small_f32
+    tok = synth.make_tokens(2, 33)
+    for n in (1, 6, 12):
+        x = m.forward_debug(dev_tokens(tok), n).cpu().numpy()
+        ref = O.residual(w, tok, 12, n)
+        rel = np.linalg.norm(x - ref) / np.linalg.norm(ref)
+        log(f"  block {n}: rel L2 {rel:.3e}")
+        assert rel < 1e-5
+
+
+def bf16_report(got, ref, label):
+    err = np.abs(got.astype(np.float64) - ref)
+    top_g, top_o = first_argmax(got), first_argmax(ref)
+    agree = float(np.mean(top_g == top_o))
+    srt = np.sort(ref, axis=-1)
+    margin = srt[..., -1] - srt[..., -2]
+    flips = top_g != top_o
+    log(f"  {label}: max|err|={err.max():.4e} mean|err|={err.mean():.3e} top1={agree:.5f} "
+        f"flips={int(flips.sum())} (of which oracle margin < 2*max|err|: "
+        f"{int(np.sum(flips & (margin < 2 * err.max())))})")
+    return err.max(), agree
+
+
+def test_forward_bf16_config1(g, small_bf16):
+    """GPT-2 small, B=4, T=1024, bf16: the headline workload, oracle on every row."""
+    m, w = small_bf16
+    tok = synth.make_tokens(4, 1024)
+    log("forward bf16 B=4 T=1024")
+    logits, am = m.forward(dev_tokens(tok))
+    assert m.check(4, 1024) == g.OK
+    got = logits.cpu().numpy()
+    assert np.array_equal(am.cpu().numpy(), first_argmax(got))
+    worst, agree_all = 0.0, []
+    for b in range(4):
+        ref = O.forward(w, tok[b:b + 1], 12, 12)
+        e, a = bf16_report(got[b:b + 1], ref, f"row {b}")
+        worst = max(worst, e)
+        agree_all.append(a)
+    assert worst <= 5e-2
+    assert np.mean(agree_all) >= 0.99
+
+
+def test_forward_bf16_perturbed(g):
+    m, w = model(g, synth.GPT2_SMALL, "bf16", perturbed=True)
+    tok = synth.make_tokens(2, 200)
+    logits, am = m.forward(dev_tokens(tok))
+    got = logits.cpu().numpy()
+    ref = O.forward(w, tok, 12, 12)
+    e, a = bf16_report(got, ref, "perturbed B=2 T=200")
+    assert e <= 5e-2 and a >= 0.99
+    assert np.array_equal(am.cpu().numpy(), first_argmax(got))
+
+
+def test_bf16_causality_bit_identical(g, small_bf16):
+    m, _ = small_bf16
+    tok = synth.make_tokens(1, 300)
+    base = m.forward(dev_tokens(tok))[0].cpu().numpy()
+    for t in (0, 127, 128, 250):
+        tok2 = tok.copy()
+        tok2[0, t + 1:] = (tok2[0, t + 1:] + 777) % 50257
+        other = m.forward(dev_tokens(tok2))[0].cpu().numpy()
+        assert np.array_equal(base[:, :t + 1], other[:, :t + 1]), t
+        assert not np.array_equal(base[:, t + 1:], other[:, t + 1:])
+
+
+def test_bf16_batch_independence(g, small_bf16):
+    m, _ = small_bf16
+    tok = synth.make_tokens(3, 70)
+    both = m.forward(dev_tokens(tok))[0].cpu().numpy()
+    for b in range(3):
+        one = m.forward(dev_tokens(tok[b:b + 1]))[0].cpu().numpy()
+        assert np.array_equal(both[b:b + 1], one)
+
+
+@pytest.mark.parametrize("B,T", [(1, 1), (1, 2), (5, 3)])
+def test_bf16_tiny_shapes(g, small_bf16, B, T):
+    m, w = small_bf16
+    tok = synth.make_tokens(B, T)
+    got = m.forward(dev_tokens(tok))[0].cpu().numpy()
+    ref = O.forward(w, tok, 12, 12)
+    e, a = bf16_report(got, ref, f"B={B} T={T}")
+    assert e <= 5e-2
+
+
+# ---------------------------------------------------------------------------------- error paths
+def test_errors_reported(g, small_bf16):
+    m, _ = small_bf16
+    tok = dev_tokens(synth.make_tokens(1, 8))
+    with pytest.raises(g.GPT2Error) as e:
+        m.forward(dev_tokens(synth.make_tokens(1, 1025)))
+    assert e.value.status == g.ESHAPE
+    ws = m.workspace(1, 8)
+    with pytest.raises(g.GPT2Error) as e:
+        m.forward(tok, ws=ws[: ws.numel() // 2])
+    assert e.value.status == g.EWORKSPACE
+    bad = synth.make_tokens(1, 8)
+    bad[0, 5] = 50257
+    logits, _ = m.forward(dev_tokens(bad))
+    assert m.check(1, 8) == g.ETOKEN
+    bad[0, 5] = -3
+    m.forward(dev_tokens(bad))
+    assert m.check(1, 8) == g.ETOKEN
+    m.forward(tok)
+    assert m.check(1, 8) == g.OK
