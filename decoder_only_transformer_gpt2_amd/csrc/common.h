@@ -7,6 +7,9 @@
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
+// 16-byte register vector for global/LDS staging. A native vector (not the uint4 struct) so that a
+// load and its later store stay two separate instructions instead of being merged into one copy.
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
 #define GPT2_WAVE 64
 
@@ -42,8 +45,8 @@ namespace gpt2k {
 
 enum Epi { EPI_BIAS = 0, EPI_BIAS_GELU = 1, EPI_BIAS_RESIDUAL = 2, EPI_LOGITS = 3 };
 
-// Tile width along N of each GEMM flavour: the argmax partial count per row is ceil(N / BN).
-constexpr int kGemmBf16BN = 128;
+// Tile width along N the GEMMs use for a shape: the argmax partial count per row is ceil(N / BN).
+int gemm_bf16_tile_n(int M, int N, int K);
 constexpr int kGemmF32BN = 64;
 
 hipError_t embed(const int32_t* tok, const void* wte, const void* wpe, float* x, int M, int T, int d,
@@ -53,8 +56,10 @@ int embed_flag_count(int M);
 hipError_t layernorm(const float* x, const float* g, const float* b, void* y, int M, int n, float eps,
                      bool out_bf16, hipStream_t s);
 
+// A must have a_rows >= M readable rows and W w_rows >= N (rows past them are never read).
 hipError_t gemm_bf16(const uint16_t* A, const uint16_t* W, const float* bias, void* C, int M, int N, int K,
-                     long ldc, int epi, int gelu_erf, float* amax_v, int32_t* amax_i, hipStream_t s);
+                     long ldc, int epi, int gelu_erf, int a_rows, int w_rows, float* amax_v, int32_t* amax_i,
+                     hipStream_t s);
 hipError_t gemm_f32(const float* A, const float* W, const float* bias, void* C, int M, int N, int K, long ldc,
                     int epi, int gelu_erf, float* amax_v, int32_t* amax_i, hipStream_t s);
 

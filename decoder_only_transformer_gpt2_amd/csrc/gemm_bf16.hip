@@ -4,59 +4,115 @@
 // attn.c_proj, mlp.c_fc, mlp.c_proj and the tied lm_head ("复现GPT-2 124M" §2.1 and §2.4,
 // "从零手写GPT-2" §4.1).
 //
-// Tiling: a 256-thread workgroup (4 wavefronts as 2 x 2) owns a BM x BN tile of C and walks K in
-// steps of 64. Each step's A and W slabs are staged global -> registers -> LDS (double-buffered,
-// one barrier per step); 16-byte chunks are XOR-swizzled by row so the 16-byte fragment reads of
-// a wavefront spread over all LDS banks. Each wavefront computes (BM/2) x (BN/2) with
-// v_mfma_f32_16x16x32_bf16 and keeps the fp32 accumulators in registers to the epilogue.
+// Tiling: a workgroup of WGM x WGN wavefronts owns a BM x BN tile of C and walks K in steps of
+// BK. The A and W slabs of each step go straight from global memory into a ring of S LDS stages
+// (global_load_lds_dwordx4, no staging registers), issued S-1 steps ahead, so up to S-1 stages
+// are in flight while one is consumed: the loop is bound by how many bytes are in flight per CU,
+// and the DMA ring holds far more than register staging could. Each step waits for its own stage
+// with an explicit vmcnt, meets the other wavefronts at a barrier, refills the stage it freed and
+// runs its MFMAs (v_mfma_f32_16x16x32_bf16, fp32 accumulators kept in registers until the
+// epilogue). 16-byte chunks are XOR-swizzled by row in LDS (the permutation is applied on the
+// global side, since a DMA writes 64 consecutive 16-byte lane slots) so that the 16-byte
+// fragment reads of a wavefront spread over all banks.
+//
+// Tile shapes come from a per-shape table chosen so that the grid fills the 256 compute units
+// (8 XCDs x 32). Workgroup ids are remapped so that each XCD (which receives every 8th id) works
+// on one contiguous range of tiles, and tiles are rasterised in groups of GROUP_M row-tiles, so
+// the A rows and W rows a group shares stay in that XCD's L2.
+#include <cstdlib>
+
 #include "common.h"
 
 namespace gpt2k {
 namespace {
 
-constexpr int BK = 64;  // K per LDS stage (eight 16-byte chunks per row)
+constexpr int kXcds = 8;
 
-// LDS element offset of (row, 16-byte chunk) in a [rows][64] bf16 slab with the XOR swizzle.
-__device__ __forceinline__ int swz(int row, int chunk) { return row * BK + ((chunk ^ (row & 7)) << 3); }
+struct TileCoord {
+    int tm, tn;
+};
 
-template <int ROWS>
-__device__ __forceinline__ void load_slab(const uint16_t* __restrict__ g, int ld, int k0, uint4 (&r)[ROWS / 32]) {
-    const int t = threadIdx.x;
-#pragma unroll
-    for (int i = 0; i < ROWS / 32; ++i) {
-        const int row = t / 8 + 32 * i, chunk = t % 8;
-        r[i] = *reinterpret_cast<const uint4*>(g + (size_t)row * ld + k0 + chunk * 8);
+// Workgroup id -> (row-tile, column-tile): XCD-contiguous ranges, then grouped rasterisation.
+__device__ __forceinline__ TileCoord tile_of(int b, int nblk, int tiles_m, int group_m) {
+    const int xcd = b % kXcds, idx = b / kXcds, q = nblk / kXcds, r = nblk % kXcds;
+    int logical = (xcd < r ? xcd * (q + 1) : r * (q + 1) + (xcd - r) * q) + idx;
+#ifdef GPT2_GEMM_TUNE
+    if (group_m < 0) {  // tuning only: plain order, no XCD remap
+        logical = b;
+        group_m = -group_m;
     }
+#endif
+    const int tiles_n = nblk / tiles_m;
+    const int per_group = group_m * tiles_n;
+    const int grp = logical / per_group, in = logical % per_group;
+    const int first_m = grp * group_m;
+    const int gm = min(tiles_m - first_m, group_m);
+    return {first_m + in % gm, in / gm};
 }
 
-template <int ROWS>
-__device__ __forceinline__ void store_slab(uint16_t* s, const uint4 (&r)[ROWS / 32]) {
-    const int t = threadIdx.x;
-#pragma unroll
-    for (int i = 0; i < ROWS / 32; ++i) {
-        const int row = t / 8 + 32 * i, chunk = t % 8;
-        *reinterpret_cast<uint4*>(s + swz(row, chunk)) = r[i];
-    }
-}
+// Waitcnt immediate (gfx9 encoding): wait until at most vm vector-memory and lgkm LDS/scalar
+// operations of this wavefront are outstanding (expcnt not waited on).
+constexpr int waitcnt_imm(int vm, int lgkm) { return (vm & 0xF) | ((vm >> 4) << 14) | (7 << 4) | (lgkm << 8); }
 
-template <int BM, int BN, int EPI>
-__global__ __launch_bounds__(256) void gemm_bf16_kernel(const uint16_t* __restrict__ A, const uint16_t* __restrict__ W,
-                                                        const float* __restrict__ bias, void* __restrict__ Cv, int M,
-                                                        int N, int K, long ldc, int gelu_erf, int tiles_m,
-                                                        float* __restrict__ amax_v, int32_t* __restrict__ amax_i) {
-    constexpr int WM = BM / 2, WN = BN / 2, FM = WM / 16, FN = WN / 16;
-    __shared__ __attribute__((aligned(16))) uint16_t sA[2][BM * BK];
-    __shared__ __attribute__((aligned(16))) uint16_t sW[2][BN * BK];
+template <int BM, int BN, int BK, int S, int WGM, int WGN, int EPI>
+__global__ __launch_bounds__(64 * WGM * WGN) void gemm_bf16_kernel(
+    const uint16_t* __restrict__ A, const uint16_t* __restrict__ W, const float* __restrict__ bias,
+    void* __restrict__ Cv, int M, int N, int K, long ldc, int gelu_erf, int a_rows, int w_rows, int tiles_m,
+    int group_m, float* __restrict__ amax_v, int32_t* __restrict__ amax_i) {
+    constexpr int NT = 64 * WGM * WGN, NW = WGM * WGN;
+    constexpr int WM = BM / WGM, WN = BN / WGN, FM = WM / 16, FN = WN / 16;
+    constexpr int CPR = BK / 8;                  // 16-byte chunks per slab row
+    constexpr int RPI = 64 / CPR;                // slab rows one 64-lane DMA instruction fills
+    constexpr int STAGE = (BM + BN) * BK;        // bf16 elements per stage (A slab, then W slab)
+    constexpr int PW = (BM + BN) / RPI / NW;     // DMA instructions per wavefront per stage
+    static_assert(BK == 32 || BK == 64, "BK is 32 or 64");
+    static_assert(WM % 16 == 0 && WN % 16 == 0, "wave tile must be a multiple of 16");
+    static_assert(BM % RPI == 0 && BN % RPI == 0 && (BM + BN) % (RPI * NW) == 0, "DMA rows must divide evenly");
+    static_assert(S >= 2 && S <= 5 && (S - 1) * PW < 64, "ring depth");
+    static_assert(S * STAGE * 2 <= 160 * 1024, "LDS");
+    // One LDS object per stage: lets the compiler see which outstanding DMA an LDS read depends on.
+    __shared__ __attribute__((aligned(1024))) uint16_t lds0[STAGE];
+    __shared__ __attribute__((aligned(1024))) uint16_t lds1[STAGE];
+    __shared__ __attribute__((aligned(1024))) uint16_t lds2[S > 2 ? STAGE : 8];
+    __shared__ __attribute__((aligned(1024))) uint16_t lds3[S > 3 ? STAGE : 8];
+    __shared__ __attribute__((aligned(1024))) uint16_t lds4[S > 4 ? STAGE : 8];
+    auto slot = [&](int i) -> uint16_t* {
+        return i == 0 ? lds0 : i == 1 ? lds1 : i == 2 ? lds2 : i == 3 ? lds3 : lds4;
+    };
 
-    // consecutive workgroups share a W tile (walk down M first)
-    const int tm = blockIdx.x % tiles_m, tn = blockIdx.x / tiles_m;
-    const int m0 = tm * BM, n0 = tn * BN;
+    const TileCoord tc = tile_of(blockIdx.x, gridDim.x, tiles_m, group_m);
+    const int m0 = tc.tm * BM, n0 = tc.tn * BN;
     const int wave = threadIdx.x / GPT2_WAVE, lane = threadIdx.x % GPT2_WAVE;
-    const int wm = wave / 2, wn = wave % 2;
+    const int wm = wave / WGN, wn = wave % WGN;
     const int r16 = lane & 15, g4 = lane >> 4;
 
-    const uint16_t* Ab = A + (size_t)m0 * K;
-    const uint16_t* Wb = W + (size_t)n0 * K;
+    // Swizzled chunk position of (row, chunk) within a slab row.
+    auto swz_chunk = [](int row, int chunk) { return CPR == 8 ? (chunk ^ (row & 7)) : (chunk ^ ((row >> 1) & 3)); };
+
+    // DMA sources: instruction p of this wavefront fills slab rows [q*RPI, q*RPI+RPI) of the stage
+    // (q = wave*PW + p; A rows first, then W rows); lane L writes LDS slot L of that 1 KB block,
+    // i.e. row q*RPI + L/CPR, swizzled chunk L%CPR, so it fetches the chunk that belongs there.
+    const uint16_t* src[PW];
+    int lds_off[PW];
+#pragma unroll
+    for (int p = 0; p < PW; ++p) {
+        const int q = wave * PW + p;
+        const int srow = q * RPI + lane / CPR;  // row within the stage (A rows, then W rows)
+        const int sch = lane % CPR;
+        const bool is_a = srow < BM;
+        const int row = is_a ? srow : srow - BM;
+        const int chunk = swz_chunk(row, sch);
+        const int g = is_a ? min(m0 + row, a_rows - 1) : min(n0 + row, w_rows - 1);
+        src[p] = (is_a ? A : W) + (size_t)g * K + chunk * 8;
+        lds_off[p] = q * RPI * BK;  // element offset of the instruction's 1 KB block
+    }
+    auto issue = [&](int st, int k0) {
+        uint16_t* base = slot(st);
+#pragma unroll
+        for (int p = 0; p < PW; ++p)
+            __builtin_amdgcn_global_load_lds((const void*)(src[p] + k0),
+                                             (__attribute__((address_space(3))) void*)(base + lds_off[p]), 16, 0, 0);
+    };
 
     f32x4_t acc[FM][FN];
 #pragma unroll
@@ -64,148 +120,287 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(const uint16_t* __restri
 #pragma unroll
         for (int j = 0; j < FN; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-    uint4 ra[BM / 32], rw[BN / 32];
-    load_slab<BM>(Ab, K, 0, ra);
-    load_slab<BN>(Wb, K, 0, rw);
-    store_slab<BM>(sA[0], ra);
-    store_slab<BN>(sW[0], rw);
-    __syncthreads();
-
-    const int nk = K / BK;
-    for (int kt = 0; kt < nk; ++kt) {
-        const int cur = kt & 1;
-        if (kt + 1 < nk) {
-            load_slab<BM>(Ab, K, (kt + 1) * BK, ra);
-            load_slab<BN>(Wb, K, (kt + 1) * BK, rw);
-        }
+    auto compute = [&](int st) {
+        const uint16_t* sa = slot(st);
+        const uint16_t* sw = sa + BM * BK;
 #pragma unroll
-        for (int kk = 0; kk < 2; ++kk) {
+        for (int kk = 0; kk < BK / 32; ++kk) {
             bf16x8_t af[FM], wf[FN];
             const int chunk = kk * 4 + g4;
 #pragma unroll
-            for (int i = 0; i < FM; ++i)
-                af[i] = *reinterpret_cast<const bf16x8_t*>(&sA[cur][swz(wm * WM + i * 16 + r16, chunk)]);
+            for (int i = 0; i < FM; ++i) {
+                const int row = wm * WM + i * 16 + r16;
+                af[i] = *reinterpret_cast<const bf16x8_t*>(&sa[row * BK + swz_chunk(row, chunk) * 8]);
+            }
 #pragma unroll
-            for (int j = 0; j < FN; ++j)
-                wf[j] = *reinterpret_cast<const bf16x8_t*>(&sW[cur][swz(wn * WN + j * 16 + r16, chunk)]);
+            for (int j = 0; j < FN; ++j) {
+                const int row = wn * WN + j * 16 + r16;
+                wf[j] = *reinterpret_cast<const bf16x8_t*>(&sw[row * BK + swz_chunk(row, chunk) * 8]);
+            }
 #pragma unroll
             for (int i = 0; i < FM; ++i)
 #pragma unroll
                 for (int j = 0; j < FN; ++j)
                     acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], wf[j], acc[i][j], 0, 0, 0);
         }
-        if (kt + 1 < nk) {
-            store_slab<BM>(sA[cur ^ 1], ra);
-            store_slab<BN>(sW[cur ^ 1], rw);
+    };
+
+    // Step kt: wait until this wavefront's DMAs of stage kt have landed (at most `after` stages
+    // issued later may still be in flight) and its LDS reads of the previous step are done, meet
+    // the other wavefronts (their stage kt has landed too, and nobody still reads the slot of step
+    // kt-1), refill that slot with stage kt+S-1, then run stage kt.
+#define GPT2_WAIT_BARRIER(after)                                              \
+    do {                                                                      \
+        __builtin_amdgcn_s_waitcnt(waitcnt_imm((after) * PW, 0));             \
+        __builtin_amdgcn_s_barrier();                                         \
+    } while (0)
+
+    const int nk = K / BK;
+#pragma unroll
+    for (int st = 0; st < S - 1; ++st)
+        if (st < nk) issue(st, st * BK);
+
+    int kt = 0;
+    // steady state: every step issues a new stage, so S-2 later stages are always in flight
+    for (; kt + 2 * S - 2 < nk; kt += S) {
+#pragma unroll
+        for (int u = 0; u < S; ++u) {
+            GPT2_WAIT_BARRIER(S - 2);
+            issue((u + S - 1) % S, (kt + u + S - 1) * BK);
+            compute(u);
         }
-        __syncthreads();
     }
+    // tail: fewer stages left to issue; wait exactly for this step's stage
+    for (; kt < nk; ++kt) {
+        const int later = min(kt + S - 2, nk - 1) - kt;  // stages issued after kt
+        switch (later) {
+            case 0: GPT2_WAIT_BARRIER(0); break;
+            case 1: GPT2_WAIT_BARRIER(1); break;
+            case 2: GPT2_WAIT_BARRIER(2); break;
+            default: GPT2_WAIT_BARRIER(3); break;
+        }
+        if (kt + S - 1 < nk) issue((kt + S - 1) % S, (kt + S - 1) * BK);
+        compute(kt % S);
+    }
+#undef GPT2_WAIT_BARRIER
+    __syncthreads();  // the ring is idle from here: the epilogue reuses it
 
     // Epilogue. acc[i][j][e] holds C[row, col] with row = wm*WM + i*16 + 4*g4 + e and
-    // col = wn*WN + j*16 + r16 (the 16x16 MFMA accumulator layout).
-    if (EPI == EPI_LOGITS) {
-        float* C = static_cast<float*>(Cv);
-        __shared__ float red_v[2][BM];
-        __shared__ int red_i[2][BM];
+    // col = wn*WN + j*16 + r16 (the 16x16 MFMA accumulator layout: each lane holds four rows of
+    // one column). Stores straight from that layout would scatter 2- or 4-byte writes over four
+    // rows per instruction, so each wavefront stages one 16-row strip at a time in its own LDS
+    // scratch ([16][WN+4] fp32, padded against bank conflicts) and then writes whole row segments
+    // with consecutive lanes on consecutive columns.
+    constexpr int SP = WN + 4;
+    constexpr int SCR_BYTES = 16 * SP * 4;
+    constexpr int WAVES_PER_SLOT = (STAGE * 2) / SCR_BYTES;
+    static_assert(WAVES_PER_SLOT >= 1 && (NW + WAVES_PER_SLOT - 1) / WAVES_PER_SLOT <= S - 1,
+                  "epilogue scratch fits the ring, leaving the last stage for the argmax partials");
+    static_assert(WGN * BM * 8 <= STAGE * 2, "argmax partials fit one stage");
+    float* scr = reinterpret_cast<float*>(slot(wave / WAVES_PER_SLOT)) + (wave % WAVES_PER_SLOT) * (16 * SP);
+    float* red_v = reinterpret_cast<float*>(slot(S - 1));
+    int* red_i = reinterpret_cast<int*>(slot(S - 1)) + WGN * BM;
+
+    const int row0 = m0 + wm * WM, col0 = n0 + wn * WN;
+    float bcol[FN];  // bias of this lane's column in each 16-column block (0 past N)
 #pragma unroll
-        for (int i = 0; i < FM; ++i) {
+    for (int j = 0; j < FN; ++j) {
+        const int n = col0 + j * 16 + r16;
+        bcol[j] = (EPI != EPI_LOGITS && n < N) ? bias[n] : 0.f;
+    }
+
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+        // stage the strip (bias and GELU applied; the residual add happens at the store)
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                const int rl = wm * WM + i * 16 + 4 * g4 + e;
-                const int m = m0 + rl;
+                float v = acc[i][j][e] + bcol[j];
+                if (EPI == EPI_BIAS_GELU) v = gelu_erf ? gelu_erf_f32(v) : gelu_tanh_f32(v);
+                scr[(4 * g4 + e) * SP + j * 16 + r16] = v;
+            }
+        if (EPI == EPI_LOGITS && amax_v) {
+            // per-row (value, index) maximum over this wavefront's columns
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
                 float bv = -INFINITY;
                 int bi = 0x7fffffff;
 #pragma unroll
                 for (int j = 0; j < FN; ++j) {
-                    const int n = n0 + wn * WN + j * 16 + r16;
-                    const float v = acc[i][j][e];
-                    if (n < N) {
-                        if (m < M) C[(size_t)m * ldc + n] = v;
-                        argmax_merge(bv, bi, v, n);
-                    }
+                    const int n = col0 + j * 16 + r16;
+                    if (n < N) argmax_merge(bv, bi, acc[i][j][e], n);
                 }
-                if (amax_v) {
 #pragma unroll
-                    for (int o = 8; o >= 1; o >>= 1) {
-                        const float v2 = __shfl_xor(bv, o, GPT2_WAVE);
-                        const int i2 = __shfl_xor(bi, o, GPT2_WAVE);
-                        argmax_merge(bv, bi, v2, i2);
-                    }
-                    if (r16 == 0) {
-                        red_v[wn][rl] = bv;
-                        red_i[wn][rl] = bi;
-                    }
+                for (int o = 8; o >= 1; o >>= 1) {
+                    const float v2 = __shfl_xor(bv, o, GPT2_WAVE);
+                    const int i2 = __shfl_xor(bi, o, GPT2_WAVE);
+                    argmax_merge(bv, bi, v2, i2);
+                }
+                if (r16 == 0) {
+                    const int rl = wm * WM + i * 16 + 4 * g4 + e;
+                    red_v[wn * BM + rl] = bv;
+                    red_i[wn * BM + rl] = bi;
                 }
             }
         }
-        if (amax_v) {
-            __syncthreads();
-            const int tiles_n = (N + BN - 1) / BN;
-            for (int rl = threadIdx.x; rl < BM; rl += 256) {
-                const int m = m0 + rl;
-                if (m < M) {
-                    float bv = red_v[0][rl];
-                    int bi = red_i[0][rl];
-                    argmax_merge(bv, bi, red_v[1][rl], red_i[1][rl]);
-                    amax_v[(size_t)m * tiles_n + tn] = bv;
-                    amax_i[(size_t)m * tiles_n + tn] = bi;
+        // write the strip out (a wavefront's LDS operations complete in order: no barrier needed)
+        if (EPI == EPI_LOGITS) {
+            // fp32 rows of odd stride: one float per lane, consecutive lanes on consecutive columns
+            float* C = static_cast<float*>(Cv);
+#pragma unroll
+            for (int it = 0; it < (16 * WN + GPT2_WAVE - 1) / GPT2_WAVE; ++it) {
+                const int idx = it * GPT2_WAVE + lane;
+                if (16 * WN % GPT2_WAVE != 0 && idx >= 16 * WN) break;
+                const int r = idx / WN, c = idx % WN;
+                const int m = row0 + i * 16 + r, n = col0 + c;
+                if (m < M && n < N) C[(size_t)m * ldc + n] = scr[r * SP + c];
+            }
+        } else if (EPI == EPI_BIAS_RESIDUAL) {
+            // C += staged, four floats per lane
+            float* C = static_cast<float*>(Cv);
+#pragma unroll
+            for (int it = 0; it < (16 * (WN / 4) + GPT2_WAVE - 1) / GPT2_WAVE; ++it) {
+                const int idx = it * GPT2_WAVE + lane;
+                if (16 * (WN / 4) % GPT2_WAVE != 0 && idx >= 16 * (WN / 4)) break;
+                const int r = idx / (WN / 4), c = (idx % (WN / 4)) * 4;
+                const int m = row0 + i * 16 + r, n = col0 + c;
+                if (m >= M) continue;
+                const float* sv = &scr[r * SP + c];
+                float* cp = C + (size_t)m * ldc + n;
+                if (n + 4 <= N && (ldc & 3) == 0) {
+                    f32x4_t cv = *reinterpret_cast<const f32x4_t*>(cp);
+                    cv[0] += sv[0]; cv[1] += sv[1]; cv[2] += sv[2]; cv[3] += sv[3];
+                    *reinterpret_cast<f32x4_t*>(cp) = cv;
+                } else {
+                    for (int t = 0; t < 4 && n + t < N; ++t) cp[t] += sv[t];
+                }
+            }
+        } else {
+            // bf16 rows: eight values (16 bytes) per lane
+            uint16_t* C = static_cast<uint16_t*>(Cv);
+#pragma unroll
+            for (int it = 0; it < (16 * (WN / 8) + GPT2_WAVE - 1) / GPT2_WAVE; ++it) {
+                const int idx = it * GPT2_WAVE + lane;
+                if (16 * (WN / 8) % GPT2_WAVE != 0 && idx >= 16 * (WN / 8)) break;
+                const int r = idx / (WN / 8), c = (idx % (WN / 8)) * 8;
+                const int m = row0 + i * 16 + r, n = col0 + c;
+                if (m >= M) continue;
+                const float* sv = &scr[r * SP + c];
+                uint16_t* cp = C + (size_t)m * ldc + n;
+                if (n + 8 <= N && (ldc & 7) == 0) {
+                    u32x4_t pk;
+                    pk[0] = pack_bf16x2(sv[0], sv[1]);
+                    pk[1] = pack_bf16x2(sv[2], sv[3]);
+                    pk[2] = pack_bf16x2(sv[4], sv[5]);
+                    pk[3] = pack_bf16x2(sv[6], sv[7]);
+                    *reinterpret_cast<u32x4_t*>(cp) = pk;
+                } else {
+                    for (int t = 0; t < 8 && n + t < N; ++t) cp[t] = f32_to_bf16_bits(sv[t]);
                 }
             }
         }
-    } else {
+    }
+
+    if (EPI == EPI_LOGITS && amax_v) {
+        __syncthreads();
+        const int tiles_n = (N + BN - 1) / BN;
+        for (int rl = threadIdx.x; rl < BM; rl += NT) {
+            const int m = m0 + rl;
+            if (m < M) {
+                float bv = red_v[rl];
+                int bi = red_i[rl];
 #pragma unroll
-        for (int j = 0; j < FN; ++j) {
-            const int n = n0 + wn * WN + j * 16 + r16;
-            if (n >= N) continue;
-            const float bn = bias[n];
-#pragma unroll
-            for (int i = 0; i < FM; ++i) {
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int m = m0 + wm * WM + i * 16 + 4 * g4 + e;
-                    if (m >= M) continue;
-                    float v = acc[i][j][e] + bn;
-                    if (EPI == EPI_BIAS_RESIDUAL) {
-                        float* C = static_cast<float*>(Cv);
-                        C[(size_t)m * ldc + n] += v;
-                    } else {
-                        if (EPI == EPI_BIAS_GELU) v = gelu_erf ? gelu_erf_f32(v) : gelu_tanh_f32(v);
-                        static_cast<uint16_t*>(Cv)[(size_t)m * ldc + n] = f32_to_bf16_bits(v);
-                    }
-                }
+                for (int w = 1; w < WGN; ++w) argmax_merge(bv, bi, red_v[w * BM + rl], red_i[w * BM + rl]);
+                amax_v[(size_t)m * tiles_n + tc.tn] = bv;
+                amax_i[(size_t)m * tiles_n + tc.tn] = bi;
             }
         }
     }
 }
 
-template <int BM, int BN>
-hipError_t launch(const uint16_t* A, const uint16_t* W, const float* bias, void* C, int M, int N, int K, long ldc,
-                  int epi, int gelu_erf, float* av, int32_t* ai, hipStream_t s) {
-    const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
-    dim3 grid(tiles_m * tiles_n), block(256);
-    switch (epi) {
-        case EPI_BIAS:
-            gemm_bf16_kernel<BM, BN, EPI_BIAS><<<grid, block, 0, s>>>(A, W, bias, C, M, N, K, ldc, gelu_erf, tiles_m, av, ai);
-            break;
-        case EPI_BIAS_GELU:
-            gemm_bf16_kernel<BM, BN, EPI_BIAS_GELU><<<grid, block, 0, s>>>(A, W, bias, C, M, N, K, ldc, gelu_erf, tiles_m, av, ai);
-            break;
-        case EPI_BIAS_RESIDUAL:
-            gemm_bf16_kernel<BM, BN, EPI_BIAS_RESIDUAL><<<grid, block, 0, s>>>(A, W, bias, C, M, N, K, ldc, gelu_erf, tiles_m, av, ai);
-            break;
-        default:
-            gemm_bf16_kernel<BM, BN, EPI_LOGITS><<<grid, block, 0, s>>>(A, W, bias, C, M, N, K, ldc, gelu_erf, tiles_m, av, ai);
-            break;
+// ------------------------------------------------------------------------------ tile table
+struct TileCfg {
+    int bm, bn, bk, stages, wgm, wgn;
+};
+
+// Instantiated tile shapes.
+constexpr TileCfg kCfgs[] = {
+    {256, 256, 32, 4, 2, 4},  // 0: 8 waves, 128 KB ring
+    {256, 256, 64, 2, 2, 4},  // 1
+    {256, 192, 32, 4, 2, 2},  // 2: 4 waves
+    {128, 128, 32, 4, 2, 2},  // 3: 64 KB ring, 2 workgroups per CU
+    {128, 128, 64, 2, 2, 2},  // 4
+    {128, 64, 32, 4, 2, 2},   // 5: 48 KB ring, 3 per CU
+    {256, 128, 32, 4, 2, 4},  // 6
+    {128, 96, 64, 2, 2, 2},   // 7
+    {256, 256, 32, 5, 2, 4},  // 8: 160 KB ring
+    {192, 256, 32, 4, 2, 2},  // 9: 4 waves
+};
+[[maybe_unused]] constexpr int kNumCfgs = sizeof(kCfgs) / sizeof(kCfgs[0]);
+
+// Tile shape per GEMM shape, from measurements on MI355X at M = 4096 (bf16, K = 768 / 3072):
+// the 128 x 96 tile with a two-stage 64-wide ring (two workgroups per CU) is fastest for the block
+// projections (N = 768 .. 3072), and the 256 x 256 tile with a five-stage 32-wide ring for the
+// vocabulary projection, where there are enough tiles to fill every CU twelve times over.
+int choose_cfg(int M, int N, int K) {
+#ifdef GPT2_GEMM_TUNE
+    if (const char* e = getenv("GPT2_GEMM_CFG")) {
+        const int c = atoi(e);
+        if (c >= 0 && c < kNumCfgs) return c;
     }
+#endif
+    (void)K;
+    const long tiles256 = (long)((M + 255) / 256) * ((N + 255) / 256);
+    return tiles256 >= 4 * 256 ? 8 : 7;
+}
+
+template <int BM, int BN, int BK, int S, int WGM, int WGN>
+hipError_t launch_cfg(const uint16_t* A, const uint16_t* W, const float* bias, void* C, int M, int N, int K, long ldc,
+                      int epi, int gelu_erf, int a_rows, int w_rows, float* av, int32_t* ai, hipStream_t s) {
+    const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
+    int group_m = 4;
+#ifdef GPT2_GEMM_TUNE
+    if (const char* e = getenv("GPT2_GEMM_GROUP")) group_m = atoi(e);
+#endif
+    dim3 grid(tiles_m * tiles_n), block(64 * WGM * WGN);
+#define GPT2_LAUNCH(E)                                                                                      \
+    gemm_bf16_kernel<BM, BN, BK, S, WGM, WGN, E><<<grid, block, 0, s>>>(A, W, bias, C, M, N, K, ldc, gelu_erf, \
+                                                                      a_rows, w_rows, tiles_m, group_m, av, ai)
+    switch (epi) {
+        case EPI_BIAS: GPT2_LAUNCH(EPI_BIAS); break;
+        case EPI_BIAS_GELU: GPT2_LAUNCH(EPI_BIAS_GELU); break;
+        case EPI_BIAS_RESIDUAL: GPT2_LAUNCH(EPI_BIAS_RESIDUAL); break;
+        default: GPT2_LAUNCH(EPI_LOGITS); break;
+    }
+#undef GPT2_LAUNCH
     return hipGetLastError();
 }
 
 }  // namespace
 
+int gemm_bf16_tile_n(int M, int N, int K) { return kCfgs[choose_cfg(M, N, K)].bn; }
+
 hipError_t gemm_bf16(const uint16_t* A, const uint16_t* W, const float* bias, void* C, int M, int N, int K, long ldc,
-                     int epi, int gelu_erf, float* amax_v, int32_t* amax_i, hipStream_t s) {
-    static_assert(kGemmBf16BN == 128, "argmax partial count assumes BN = 128");
-    return launch<128, 128>(A, W, bias, C, M, N, K, ldc, epi, gelu_erf, amax_v, amax_i, s);
+                     int epi, int gelu_erf, int a_rows, int w_rows, float* amax_v, int32_t* amax_i, hipStream_t s) {
+    switch (choose_cfg(M, N, K)) {
+#define GPT2_CFG(i, bm, bn, bk, st, wgm, wgn)                                                                    \
+    case i:                                                                                                      \
+        return launch_cfg<bm, bn, bk, st, wgm, wgn>(A, W, bias, C, M, N, K, ldc, epi, gelu_erf, a_rows, w_rows, \
+                                                    amax_v, amax_i, s);
+        GPT2_CFG(0, 256, 256, 32, 4, 2, 4)
+        GPT2_CFG(1, 256, 256, 64, 2, 2, 4)
+        GPT2_CFG(2, 256, 192, 32, 4, 2, 2)
+        GPT2_CFG(3, 128, 128, 32, 4, 2, 2)
+        GPT2_CFG(4, 128, 128, 64, 2, 2, 2)
+        GPT2_CFG(5, 128, 64, 32, 4, 2, 2)
+        GPT2_CFG(6, 256, 128, 32, 4, 2, 4)
+        GPT2_CFG(7, 128, 96, 64, 2, 2, 2)
+        GPT2_CFG(8, 256, 256, 32, 5, 2, 4)
+        GPT2_CFG(9, 192, 256, 32, 4, 2, 2)
+#undef GPT2_CFG
+    }
+    return hipErrorInvalidValue;
 }
 
 }  // namespace gpt2k

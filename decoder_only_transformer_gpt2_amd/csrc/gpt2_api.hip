@@ -83,7 +83,7 @@ WorkspaceLayout ws_layout(const gpt2_model* m, int B, int T) {
     const int64_t M = (int64_t)B * T;
     w.Mp = round_up(M, kRowPad);
     const size_t as = act_size(m);
-    const int bn = is_bf16(m) ? gpt2k::kGemmBf16BN : gpt2k::kGemmF32BN;
+    const int bn = is_bf16(m) ? gpt2k::gemm_bf16_tile_n((int)M, c.n_vocab, c.d_model) : gpt2k::kGemmF32BN;
     w.n_part = (c.n_vocab + bn - 1) / bn;
     size_t off = 0;
     auto take = [&](size_t bytes) { size_t o = off; off = align_up(off + bytes, kAlign); return o; };
@@ -122,7 +122,8 @@ hipError_t linear(const gpt2_model* m, const void* A, int widx, int bidx, void* 
     const int ge = m->cfg.gelu == GPT2_GELU_ERF;
     if (is_bf16(m))
         return gpt2k::gemm_bf16(static_cast<const uint16_t*>(A), static_cast<const uint16_t*>(wptr(m, widx)), bias, C, M,
-                                N, K, ldc, epi, ge, av, ai, s);
+                                N, K, ldc, epi, ge, (int)round_up(M, kRowPad), (int)m->slots[widx].rows_padded, av, ai,
+                                s);
     return gpt2k::gemm_f32(static_cast<const float*>(A), static_cast<const float*>(wptr(m, widx)), bias, C, M, N, K, ldc,
                            epi, ge, av, ai, s);
 }
@@ -396,7 +397,7 @@ gpt2_status gpt2_linear(const void* A, const void* W, const float* bias, void* C
     const int ge = gelu == GPT2_GELU_ERF;
     if (dtype == GPT2_BF16)
         GPT2_HIP(gpt2k::gemm_bf16(static_cast<const uint16_t*>(A), static_cast<const uint16_t*>(W), bias, C, M, N, K, ldc,
-                                  epi, ge, nullptr, nullptr, s));
+                                  epi, ge, (int)round_up(M, kRowPad), (int)round_up(N, kRowPad), nullptr, nullptr, s));
     else
         GPT2_HIP(gpt2k::gemm_f32(static_cast<const float*>(A), static_cast<const float*>(W), bias, C, M, N, K, ldc, epi,
                                  ge, nullptr, nullptr, s));

@@ -18,7 +18,7 @@ from decoder_only_transformer_gpt2_amd import synth
 
 pytestmark = pytest.mark.gpu
 
-BF16_EPS = 2.0 ** -8  # bf16 unit roundoff is 2^-9; one ulp relative spacing is at most 2^-7
+BF16_U = 2.0 ** -8  # unit roundoff of bf16 (8 significant bits): |round(x) - x| <= 2^-8 |x|
 
 
 @pytest.fixture(scope="session")
@@ -95,7 +95,7 @@ def test_layernorm(g, n, out):
         assert np.max(np.abs(y - ref)) < 2e-5
     else:
         # one rounding to bf16 of a value carrying fp32 error
-        assert np.all(np.abs(y - ref) <= BF16_EPS * np.abs(ref) / 2 + 1e-5)
+        assert np.all(np.abs(y - ref) <= BF16_U * np.abs(ref) + 1e-5)
 
 
 # ---------------------------------------------------------------------------------------- linear
@@ -135,7 +135,7 @@ def test_linear(g, dtype, epi, M, N, K):
     scale = O.linear(np.abs(A), np.abs(W), None) + 1.0
     tol = 1e-5 * scale
     if out_dt == torch.bfloat16:
-        tol = tol + BF16_EPS / 2 * np.abs(ref)
+        tol = tol + BF16_U * np.abs(ref)
     assert np.all(np.abs(got - ref) <= tol), float(np.max(np.abs(got - ref) - tol))
 
 
@@ -159,7 +159,7 @@ def attn_tolerance(q, k, v, ref, dtype):
         return 2e-5 * (np.abs(ref) + 1)
     # bf16: the probabilities and the output are rounded to bf16 once each
     pv = O.causal_attention(q, k, np.abs(v))
-    return BF16_EPS * (np.abs(ref) + pv) + 1e-4
+    return BF16_U * (np.abs(ref) + pv) + 1e-4
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
@@ -202,7 +202,7 @@ def test_attention_config2_sampled(g):
         tol = attn_tolerance(q[b, h], k[b, h], v[b, h], ref, "bf16")
         assert np.all(np.abs(o[b, h] - ref) <= tol), (b, h)
     # property at full size: row 0 of every head is v_0 (up to the bf16 rounding of the output)
-    assert np.allclose(o[:, :, 0], v[:, :, 0], rtol=BF16_EPS, atol=0)
+    assert np.allclose(o[:, :, 0], v[:, :, 0], rtol=BF16_U, atol=0)
 
 
 # ------------------------------------------------------------------------------- whole forward
