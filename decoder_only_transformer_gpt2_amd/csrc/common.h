@@ -10,6 +10,7 @@ typedef float f32x4_t __attribute__((ext_vector_type(4)));
 // 16-byte register vector for global/LDS staging. A native vector (not the uint4 struct) so that a
 // load and its later store stay two separate instructions instead of being merged into one copy.
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 
 #define GPT2_WAVE 64
 
@@ -36,6 +37,21 @@ __device__ __forceinline__ float gelu_erf_f32(float x) { return 0.5f * x * (1.0f
 // (value, index) maximum with ties broken toward the smaller index.
 __device__ __forceinline__ void argmax_merge(float& v, int& i, float v2, int i2) {
     if (v2 > v || (v2 == v && i2 < i)) { v = v2; i = i2; }
+}
+
+// (value, index) maximum over each group of 16 consecutive lanes (a DPP row), left in every lane
+// of the group: rotations by 8, 4, 2, 1 within the row, on the vector ALU (no LDS permutes).
+template <int ROR>
+__device__ __forceinline__ void argmax_ror_step(float& v, int& i) {
+    const float v2 = __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x120 + ROR, 0xF, 0xF, false));
+    const int i2 = __builtin_amdgcn_update_dpp(0, i, 0x120 + ROR, 0xF, 0xF, false);
+    argmax_merge(v, i, v2, i2);
+}
+__device__ __forceinline__ void argmax_row16(float& v, int& i) {
+    argmax_ror_step<8>(v, i);
+    argmax_ror_step<4>(v, i);
+    argmax_ror_step<2>(v, i);
+    argmax_ror_step<1>(v, i);
 }
 
 // ---------------------------------------------------------------------------------------------

@@ -231,12 +231,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_bf16_kernel(
                     const int n = col0 + j * 16 + r16;
                     if (n < N) argmax_merge(bv, bi, acc[i][j][e], n);
                 }
-#pragma unroll
-                for (int o = 8; o >= 1; o >>= 1) {
-                    const float v2 = __shfl_xor(bv, o, GPT2_WAVE);
-                    const int i2 = __shfl_xor(bi, o, GPT2_WAVE);
-                    argmax_merge(bv, bi, v2, i2);
-                }
+                argmax_row16(bv, bi);
                 if (r16 == 0) {
                     const int rl = wm * WM + i * 16 + 4 * g4 + e;
                     red_v[wn * BM + rl] = bv;
@@ -254,7 +249,9 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_bf16_kernel(
                 if (16 * WN % GPT2_WAVE != 0 && idx >= 16 * WN) break;
                 const int r = idx / WN, c = idx % WN;
                 const int m = row0 + i * 16 + r, n = col0 + c;
-                if (m < M && n < N) C[(size_t)m * ldc + n] = scr[r * SP + c];
+                // streaming store: the logits are written once and not read back by this pass, so
+                // keep them from evicting the weights and activations from the caches
+                if (m < M && n < N) __builtin_nontemporal_store(scr[r * SP + c], &C[(size_t)m * ldc + n]);
             }
         } else if (EPI == EPI_BIAS_RESIDUAL) {
             // C += staged, four floats per lane
@@ -336,13 +333,20 @@ constexpr TileCfg kCfgs[] = {
     {128, 96, 64, 2, 2, 2},   // 7
     {256, 256, 32, 5, 2, 4},  // 8: 160 KB ring
     {192, 256, 32, 4, 2, 2},  // 9: 4 waves
+    {128, 96, 64, 3, 2, 2},   // 10
+    {128, 96, 64, 4, 2, 2},   // 11
+    {64, 96, 64, 4, 2, 2},    // 12
+    {128, 64, 64, 4, 2, 2},   // 13
+    {256, 256, 32, 4, 2, 2},  // 14: 4 waves, 128 x 128 each
+    {128, 128, 64, 4, 2, 2},  // 15
 };
 [[maybe_unused]] constexpr int kNumCfgs = sizeof(kCfgs) / sizeof(kCfgs[0]);
 
 // Tile shape per GEMM shape, from measurements on MI355X at M = 4096 (bf16, K = 768 / 3072):
-// the 128 x 96 tile with a two-stage 64-wide ring (two workgroups per CU) is fastest for the block
-// projections (N = 768 .. 3072), and the 256 x 256 tile with a five-stage 32-wide ring for the
-// vocabulary projection, where there are enough tiles to fill every CU twelve times over.
+// 64 x 96 tiles with a four-stage 64-wide ring for the narrow outputs (N = 768: 512 tiles, two
+// workgroups per CU, more bytes in flight), 128 x 96 with a two-stage ring for the wider block
+// projections (N = 2304, 3072), and 256 x 256 with a four-stage 32-wide ring for the vocabulary
+// projection, where there are enough tiles to fill every CU twelve times over.
 int choose_cfg(int M, int N, int K) {
 #ifdef GPT2_GEMM_TUNE
     if (const char* e = getenv("GPT2_GEMM_CFG")) {
@@ -352,7 +356,9 @@ int choose_cfg(int M, int N, int K) {
 #endif
     (void)K;
     const long tiles256 = (long)((M + 255) / 256) * ((N + 255) / 256);
-    return tiles256 >= 4 * 256 ? 8 : 7;
+    if (tiles256 >= 4 * 256) return 0;  // vocabulary projection
+    if (N <= 1024) return 12;           // narrow outputs: more, smaller tiles and a deeper ring
+    return 7;
 }
 
 template <int BM, int BN, int BK, int S, int WGM, int WGN>
@@ -398,6 +404,12 @@ hipError_t gemm_bf16(const uint16_t* A, const uint16_t* W, const float* bias, vo
         GPT2_CFG(7, 128, 96, 64, 2, 2, 2)
         GPT2_CFG(8, 256, 256, 32, 5, 2, 4)
         GPT2_CFG(9, 192, 256, 32, 4, 2, 2)
+        GPT2_CFG(10, 128, 96, 64, 3, 2, 2)
+        GPT2_CFG(11, 128, 96, 64, 4, 2, 2)
+        GPT2_CFG(12, 64, 96, 64, 4, 2, 2)
+        GPT2_CFG(13, 128, 64, 64, 4, 2, 2)
+        GPT2_CFG(14, 256, 256, 32, 4, 2, 2)
+        GPT2_CFG(15, 128, 128, 64, 4, 2, 2)
 #undef GPT2_CFG
     }
     return hipErrorInvalidValue;
