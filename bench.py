@@ -87,6 +87,9 @@ def main():
     ap.add_argument("--workload", choices=sorted(WORKLOADS), default="small")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--breakdown", action="store_true", help="also time every launch of one extra forward")
+    ap.add_argument("--copy-bytes", type=int, default=0,
+                    help="after the timed region, run a plain device-to-device copy of this many bytes three "
+                         "times (a known-size reference for hardware traffic counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the forward is not sharded "
@@ -154,6 +157,14 @@ def main():
                      "frac": achieved / PEAK_BF16_TFLOPS, "traffic": traffic, "avg_launch_ms": lm_ms,
                      "flops_per_launch": lm_flops},
     }
+
+    if args.copy_bytes > 0:
+        src = torch.empty(args.copy_bytes, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        out["copy_bytes"] = args.copy_bytes
 
     if args.breakdown:
         evs = [(raw_event(), raw_event()) for _ in kinds]
