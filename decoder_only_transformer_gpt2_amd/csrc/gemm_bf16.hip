@@ -32,16 +32,15 @@ struct TileCoord {
     int tm, tn;
 };
 
-// Workgroup id -> (row-tile, column-tile): XCD-contiguous ranges, then grouped rasterisation.
-__device__ __forceinline__ TileCoord tile_of(int b, int nblk, int tiles_m, int group_m) {
-    const int xcd = b % kXcds, idx = b / kXcds, q = nblk / kXcds, r = nblk % kXcds;
-    int logical = (xcd < r ? xcd * (q + 1) : r * (q + 1) + (xcd - r) * q) + idx;
-#ifdef GPT2_GEMM_TUNE
-    if (group_m < 0) {  // tuning only: plain order, no XCD remap
-        logical = b;
-        group_m = -group_m;
+// Workgroup id -> (row-tile, column-tile). Optionally remapped so that each XCD (which receives
+// every 8th id) works on one contiguous range of tiles; then rasterised in groups of group_m
+// row-tiles (column-major inside a group), so neighbouring ids share W rows.
+__device__ __forceinline__ TileCoord tile_of(int b, int nblk, int tiles_m, int group_m, bool xcd_remap) {
+    int logical = b;
+    if (xcd_remap) {
+        const int xcd = b % kXcds, idx = b / kXcds, q = nblk / kXcds, r = nblk % kXcds;
+        logical = (xcd < r ? xcd * (q + 1) : r * (q + 1) + (xcd - r) * q) + idx;
     }
-#endif
     const int tiles_n = nblk / tiles_m;
     const int per_group = group_m * tiles_n;
     const int grp = logical / per_group, in = logical % per_group;
@@ -80,7 +79,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_bf16_kernel(
         return i == 0 ? lds0 : i == 1 ? lds1 : i == 2 ? lds2 : i == 3 ? lds3 : lds4;
     };
 
-    const TileCoord tc = tile_of(blockIdx.x, gridDim.x, tiles_m, group_m);
+    const TileCoord tc = tile_of(blockIdx.x, gridDim.x, tiles_m, group_m < 0 ? -group_m : group_m, group_m > 0);
     const int m0 = tc.tm * BM, n0 = tc.tn * BN;
     const int wave = threadIdx.x / GPT2_WAVE, lane = threadIdx.x % GPT2_WAVE;
     const int wm = wave / WGN, wn = wave % WGN;
@@ -339,14 +338,19 @@ constexpr TileCfg kCfgs[] = {
     {128, 64, 64, 4, 2, 2},   // 13
     {256, 256, 32, 4, 2, 2},  // 14: 4 waves, 128 x 128 each
     {128, 128, 64, 4, 2, 2},  // 15
+    {256, 192, 64, 2, 2, 4},  // 16: 8 waves, 128 x 48 each
+    {128, 288, 64, 2, 2, 2},  // 17
+    {256, 128, 64, 2, 2, 4},  // 18
+    {192, 256, 64, 2, 2, 4},  // 19: 8 waves, 96 x 64 each
 };
 [[maybe_unused]] constexpr int kNumCfgs = sizeof(kCfgs) / sizeof(kCfgs[0]);
 
-// Tile shape per GEMM shape, from measurements on MI355X at M = 4096 (bf16, K = 768 / 3072):
-// 64 x 96 tiles with a four-stage 64-wide ring for the narrow outputs (N = 768: 512 tiles, two
-// workgroups per CU, more bytes in flight), 128 x 96 with a two-stage ring for the wider block
-// projections (N = 2304, 3072), and 256 x 256 with a four-stage 32-wide ring for the vocabulary
-// projection, where there are enough tiles to fill every CU twelve times over.
+// Tile shape per GEMM shape, from measurements on MI355X at M = 4096 (bf16, K = 768 / 3072).
+// The block projections are bound by their operand traffic through L2 (re-reads grow as tiles
+// shrink), so the largest tile that still gives every CU about one tile wins: 192 x 256 for
+// N = 2304 (198 tiles), 256 x 192 for N = 3072 (256 tiles). Narrow outputs (N <= 1024) prefer
+// 64 x 96 tiles with a four-stage ring (two workgroups per CU). The vocabulary projection, with
+// tiles for every CU twelve times over, uses 256 x 256 with a four-stage 32-wide ring.
 int choose_cfg(int M, int N, int K) {
 #ifdef GPT2_GEMM_TUNE
     if (const char* e = getenv("GPT2_GEMM_CFG")) {
@@ -355,17 +359,23 @@ int choose_cfg(int M, int N, int K) {
     }
 #endif
     (void)K;
-    const long tiles256 = (long)((M + 255) / 256) * ((N + 255) / 256);
-    if (tiles256 >= 4 * 256) return 0;  // vocabulary projection
-    if (N <= 1024) return 12;           // narrow outputs: more, smaller tiles and a deeper ring
-    return 7;
+    auto tiles = [&](int bm, int bn) { return (long)((M + bm - 1) / bm) * ((N + bn - 1) / bn); };
+    if (tiles(256, 256) >= 4 * 256) return 0;  // vocabulary projection
+    if (N <= 1024) return 12;
+    if (tiles(192, 256) <= 256) return 19;
+    return 16;
 }
 
 template <int BM, int BN, int BK, int S, int WGM, int WGN>
 hipError_t launch_cfg(const uint16_t* A, const uint16_t* W, const float* bias, void* C, int M, int N, int K, long ldc,
                       int epi, int gelu_erf, int a_rows, int w_rows, float* av, int32_t* ai, hipStream_t s) {
     const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
-    int group_m = 4;
+    // group_m > 0: XCD-contiguous remap + groups of group_m row-tiles; < 0: plain order, groups of
+    // -group_m. Measured with cold caches (as inside a forward): the vocabulary projection is fastest
+    // in plain order with pairs of row-tiles (the XCDs then fetch each wte tile at about the same
+    // time, so it is read from HBM once and served to the others from the memory-side cache);
+    // the block projections are insensitive to the order.
+    int group_m = tiles_n >= 64 ? -2 : 4;
 #ifdef GPT2_GEMM_TUNE
     if (const char* e = getenv("GPT2_GEMM_GROUP")) group_m = atoi(e);
 #endif
@@ -410,6 +420,10 @@ hipError_t gemm_bf16(const uint16_t* A, const uint16_t* W, const float* bias, vo
         GPT2_CFG(13, 128, 64, 64, 4, 2, 2)
         GPT2_CFG(14, 256, 256, 32, 4, 2, 2)
         GPT2_CFG(15, 128, 128, 64, 4, 2, 2)
+        GPT2_CFG(16, 256, 192, 64, 2, 2, 4)
+        GPT2_CFG(17, 128, 288, 64, 2, 2, 2)
+        GPT2_CFG(18, 256, 128, 64, 2, 2, 4)
+        GPT2_CFG(19, 192, 256, 64, 2, 2, 4)
 #undef GPT2_CFG
     }
     return hipErrorInvalidValue;
