@@ -34,24 +34,43 @@ __device__ __forceinline__ float gelu_tanh_f32(float x) {
 }
 __device__ __forceinline__ float gelu_erf_f32(float x) { return 0.5f * x * (1.0f + erff(x * 0.7071067811865476f)); }
 
-// (value, index) maximum with ties broken toward the smaller index.
+// (value, index) maximum with ties broken toward the smaller index (selects, no branches).
 __device__ __forceinline__ void argmax_merge(float& v, int& i, float v2, int i2) {
-    if (v2 > v || (v2 == v && i2 < i)) { v = v2; i = i2; }
+    const bool take = (v2 > v) | ((v2 == v) & (i2 < i));
+    v = take ? v2 : v;
+    i = take ? i2 : i;
 }
 
-// (value, index) maximum over each group of 16 consecutive lanes (a DPP row), left in every lane
-// of the group: rotations by 8, 4, 2, 1 within the row, on the vector ALU (no LDS permutes).
-template <int ROR>
-__device__ __forceinline__ void argmax_ror_step(float& v, int& i) {
-    const float v2 = __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x120 + ROR, 0xF, 0xF, false));
-    const int i2 = __builtin_amdgcn_update_dpp(0, i, 0x120 + ROR, 0xF, 0xF, false);
-    argmax_merge(v, i, v2, i2);
+// Order-preserving map of a float to an unsigned integer (negatives bit-inverted, non-negatives
+// with the sign bit set; -0 is first turned into +0 so that it ties with +0 as a float compare
+// does), and its inverse. Integer max/min then reduce across lanes in one DPP-fused instruction.
+__device__ __forceinline__ uint32_t f32_order_key(float v) {
+    const uint32_t u = __builtin_bit_cast(uint32_t, v + 0.0f);
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
-__device__ __forceinline__ void argmax_row16(float& v, int& i) {
-    argmax_ror_step<8>(v, i);
-    argmax_ror_step<4>(v, i);
-    argmax_ror_step<2>(v, i);
-    argmax_ror_step<1>(v, i);
+__device__ __forceinline__ float f32_from_order_key(uint32_t u) {
+    return __builtin_bit_cast(float, (u & 0x80000000u) ? (u & 0x7fffffffu) : ~u);
+}
+
+// Maximum / minimum over each group of 16 consecutive lanes (a DPP row), left in every lane of
+// the group: rotations by 8, 4, 2, 1 within the row, on the vector ALU (no LDS permutes).
+template <int ROR>
+__device__ __forceinline__ uint32_t row_ror(uint32_t x) {
+    return (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0x120 + ROR, 0xF, 0xF, false);
+}
+__device__ __forceinline__ uint32_t row16_max_u32(uint32_t x) {
+    x = max(x, row_ror<8>(x));
+    x = max(x, row_ror<4>(x));
+    x = max(x, row_ror<2>(x));
+    x = max(x, row_ror<1>(x));
+    return x;
+}
+__device__ __forceinline__ uint32_t row16_min_u32(uint32_t x) {
+    x = min(x, row_ror<8>(x));
+    x = min(x, row_ror<4>(x));
+    x = min(x, row_ror<2>(x));
+    x = min(x, row_ror<1>(x));
+    return x;
 }
 
 // ---------------------------------------------------------------------------------------------

@@ -56,7 +56,7 @@ constexpr int waitcnt_imm(int vm, int lgkm) { return (vm & 0xF) | ((vm >> 4) << 
 template <int BM, int BN, int BK, int S, int WGM, int WGN, int EPI>
 __global__ __launch_bounds__(64 * WGM * WGN) void gemm_bf16_kernel(
     const uint16_t* __restrict__ A, const uint16_t* __restrict__ W, const float* __restrict__ bias,
-    void* __restrict__ Cv, int M, int N, int K, long ldc, int gelu_erf, int a_rows, int w_rows, int tiles_m,
+    void* __restrict__ Cv, int M, int N, int K, int ldc, int gelu_erf, int a_rows, int w_rows, int tiles_m,
     int group_m, float* __restrict__ amax_v, int32_t* __restrict__ amax_i) {
     constexpr int NT = 64 * WGM * WGN, NW = WGM * WGN;
     constexpr int WM = BM / WGM, WN = BN / WGN, FM = WM / 16, FN = WN / 16;
@@ -197,16 +197,19 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_bf16_kernel(
                   "epilogue scratch fits the ring, leaving the last stage for the argmax partials");
     static_assert(WGN * BM * 8 <= STAGE * 2, "argmax partials fit one stage");
     float* scr = reinterpret_cast<float*>(slot(wave / WAVES_PER_SLOT)) + (wave % WAVES_PER_SLOT) * (16 * SP);
-    float* red_v = reinterpret_cast<float*>(slot(S - 1));
-    int* red_i = reinterpret_cast<int*>(slot(S - 1)) + WGN * BM;
+    uint32_t* red_v = reinterpret_cast<uint32_t*>(slot(S - 1));  // [WGN][BM] row maximum (order key)
+    uint32_t* red_i = red_v + WGN * BM;                            // [WGN][BM] its first column
 
     const int row0 = m0 + wm * WM, col0 = n0 + wn * WN;
     float bcol[FN];  // bias of this lane's column in each 16-column block (0 past N)
+    float cneg[FN];  // 0, or -inf past N (argmax only)
 #pragma unroll
     for (int j = 0; j < FN; ++j) {
         const int n = col0 + j * 16 + r16;
         bcol[j] = (EPI != EPI_LOGITS && n < N) ? bias[n] : 0.f;
+        cneg[j] = n < N ? 0.f : -INFINITY;
     }
+    const bool lane_has_col = col0 + r16 < N;
 
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
@@ -220,37 +223,47 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_bf16_kernel(
                 scr[(4 * g4 + e) * SP + j * 16 + r16] = v;
             }
         if (EPI == EPI_LOGITS && amax_v) {
-            // per-row (value, index) maximum over this wavefront's columns
+            // Per row: this lane's best of its FN columns (they rise with j, so a strict > keeps
+            // the first of equal values), then the row maximum over the 16 lanes, then the
+            // smallest column among the lanes that hold it. Columns past N count as -inf and
+            // lanes whose every column is past N offer no column.
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                float bv = -INFINITY;
-                int bi = 0x7fffffff;
+                float bv = acc[i][0][e] + cneg[0];
+                int bj = 0;
 #pragma unroll
-                for (int j = 0; j < FN; ++j) {
-                    const int n = col0 + j * 16 + r16;
-                    if (n < N) argmax_merge(bv, bi, acc[i][j][e], n);
+                for (int j = 1; j < FN; ++j) {
+                    const float x = acc[i][j][e] + cneg[j];
+                    const bool take = x > bv;
+                    bv = take ? x : bv;
+                    bj = take ? j : bj;
                 }
-                argmax_row16(bv, bi);
+                const uint32_t key = f32_order_key(bv);
+                const uint32_t kmax = row16_max_u32(key);
+                const uint32_t col = (key == kmax && lane_has_col) ? (uint32_t)(col0 + bj * 16 + r16) : 0xffffffffu;
+                const uint32_t cmin = row16_min_u32(col);
                 if (r16 == 0) {
-                    const int rl = wm * WM + i * 16 + 4 * g4 + e;
-                    red_v[wn * BM + rl] = bv;
-                    red_i[wn * BM + rl] = bi;
+                    const int rl = wn * BM + wm * WM + i * 16 + 4 * g4 + e;
+                    red_v[rl] = kmax;
+                    red_i[rl] = cmin;
                 }
             }
         }
         // write the strip out (a wavefront's LDS operations complete in order: no barrier needed)
         if (EPI == EPI_LOGITS) {
             // fp32 rows of odd stride: one float per lane, consecutive lanes on consecutive columns
-            float* C = static_cast<float*>(Cv);
+            // addresses from the strip's origin (wave-uniform) plus a 32-bit in-strip offset
+            const int rs = row0 + i * 16;
+            float* Cs = static_cast<float*>(Cv) + (size_t)rs * ldc + col0;
+            const int rows = M - rs, cols = N - col0;
 #pragma unroll
             for (int it = 0; it < (16 * WN + GPT2_WAVE - 1) / GPT2_WAVE; ++it) {
                 const int idx = it * GPT2_WAVE + lane;
                 if (16 * WN % GPT2_WAVE != 0 && idx >= 16 * WN) break;
                 const int r = idx / WN, c = idx % WN;
-                const int m = row0 + i * 16 + r, n = col0 + c;
                 // streaming store: the logits are written once and not read back by this pass, so
                 // keep them from evicting the weights and activations from the caches
-                if (m < M && n < N) __builtin_nontemporal_store(scr[r * SP + c], &C[(size_t)m * ldc + n]);
+                if (r < rows && c < cols) __builtin_nontemporal_store(scr[r * SP + c], Cs + r * ldc + c);
             }
         } else if (EPI == EPI_BIAS_RESIDUAL) {
             // C += staged, four floats per lane
@@ -304,12 +317,16 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_bf16_kernel(
         for (int rl = threadIdx.x; rl < BM; rl += NT) {
             const int m = m0 + rl;
             if (m < M) {
-                float bv = red_v[rl];
-                int bi = red_i[rl];
+                uint32_t kv = red_v[rl], ki = red_i[rl];
 #pragma unroll
-                for (int w = 1; w < WGN; ++w) argmax_merge(bv, bi, red_v[w * BM + rl], red_i[w * BM + rl]);
-                amax_v[(size_t)m * tiles_n + tc.tn] = bv;
-                amax_i[(size_t)m * tiles_n + tc.tn] = bi;
+                for (int w = 1; w < WGN; ++w) {
+                    const uint32_t v2 = red_v[w * BM + rl], i2 = red_i[w * BM + rl];
+                    const bool take = (v2 > kv) | ((v2 == kv) & (i2 < ki));
+                    kv = take ? v2 : kv;
+                    ki = take ? i2 : ki;
+                }
+                amax_v[(size_t)m * tiles_n + tc.tn] = f32_from_order_key(kv);
+                amax_i[(size_t)m * tiles_n + tc.tn] = (int32_t)ki;
             }
         }
     }
@@ -399,6 +416,7 @@ int gemm_bf16_tile_n(int M, int N, int K) { return kCfgs[choose_cfg(M, N, K)].bn
 
 hipError_t gemm_bf16(const uint16_t* A, const uint16_t* W, const float* bias, void* C, int M, int N, int K, long ldc,
                      int epi, int gelu_erf, int a_rows, int w_rows, float* amax_v, int32_t* amax_i, hipStream_t s) {
+    if (ldc < N || ldc > (1 << 26)) return hipErrorInvalidValue;  // in-strip offsets are 32-bit
     switch (choose_cfg(M, N, K)) {
 #define GPT2_CFG(i, bm, bn, bk, st, wgm, wgn)                                                                    \
     case i:                                                                                                      \
