@@ -32,6 +32,13 @@ __device__ __forceinline__ float gelu_tanh_f32(float x) {
     const float k0 = 0.7978845608028654f;  // sqrt(2/pi)
     return 0.5f * x * (1.0f + tanhf(k0 * (x + 0.044715f * x * x * x)));
 }
+// The tanh form through the identity 0.5 (1 + tanh(u)) = 1 / (1 + exp(-2u)), on the hardware
+// exp2 and reciprocal (about 1 ulp each); saturates correctly at both ends (exp -> 0 or inf).
+__device__ __forceinline__ float gelu_tanh_fast(float x) {
+    const float u = 0.7978845608028654f * fmaf(0.044715f * x, x * x, x);
+    const float e = __builtin_amdgcn_exp2f(-2.8853900817779268f * u);  // exp(-2u) = 2^(-2u log2(e))
+    return x * __builtin_amdgcn_rcpf(1.0f + e);
+}
 __device__ __forceinline__ float gelu_erf_f32(float x) { return 0.5f * x * (1.0f + erff(x * 0.7071067811865476f)); }
 
 // (value, index) maximum with ties broken toward the smaller index (selects, no branches).
@@ -52,25 +59,18 @@ __device__ __forceinline__ float f32_from_order_key(uint32_t u) {
     return __builtin_bit_cast(float, (u & 0x80000000u) ? (u & 0x7fffffffu) : ~u);
 }
 
-// Maximum / minimum over each group of 16 consecutive lanes (a DPP row), left in every lane of
-// the group: rotations by 8, 4, 2, 1 within the row, on the vector ALU (no LDS permutes).
-template <int ROR>
-__device__ __forceinline__ uint32_t row_ror(uint32_t x) {
-    return (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0x120 + ROR, 0xF, 0xF, false);
+// Maximum / minimum over each group of 4 consecutive lanes (quad permutes [1,0,3,2], [2,3,0,1]).
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_mov(uint32_t x) {
+    return (uint32_t)__builtin_amdgcn_mov_dpp((int)x, CTRL, 0xF, 0xF, false);
 }
-__device__ __forceinline__ uint32_t row16_max_u32(uint32_t x) {
-    x = max(x, row_ror<8>(x));
-    x = max(x, row_ror<4>(x));
-    x = max(x, row_ror<2>(x));
-    x = max(x, row_ror<1>(x));
-    return x;
+__device__ __forceinline__ uint32_t quad_max_u32(uint32_t x) {
+    x = max(x, dpp_mov<0xB1>(x));
+    return max(x, dpp_mov<0x4E>(x));
 }
-__device__ __forceinline__ uint32_t row16_min_u32(uint32_t x) {
-    x = min(x, row_ror<8>(x));
-    x = min(x, row_ror<4>(x));
-    x = min(x, row_ror<2>(x));
-    x = min(x, row_ror<1>(x));
-    return x;
+__device__ __forceinline__ uint32_t quad_min_u32(uint32_t x) {
+    x = min(x, dpp_mov<0xB1>(x));
+    return min(x, dpp_mov<0x4E>(x));
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -78,7 +78,7 @@ __device__ __forceinline__ uint32_t row16_min_u32(uint32_t x) {
 // ---------------------------------------------------------------------------------------------
 namespace gpt2k {
 
-enum Epi { EPI_BIAS = 0, EPI_BIAS_GELU = 1, EPI_BIAS_RESIDUAL = 2, EPI_LOGITS = 3 };
+enum Epi { EPI_BIAS = 0, EPI_BIAS_GELU = 1, EPI_BIAS_RESIDUAL = 2, EPI_LOGITS = 3, EPI_BIAS_GELU_ERF = 4 };  // 4: kernel-internal
 
 // Tile width along N the GEMMs use for a shape: the argmax partial count per row is ceil(N / BN).
 int gemm_bf16_tile_n(int M, int N, int K);

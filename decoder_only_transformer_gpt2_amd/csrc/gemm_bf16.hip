@@ -23,6 +23,8 @@
 
 #include "common.h"
 
+#include <type_traits>
+
 namespace gpt2k {
 namespace {
 
@@ -54,9 +56,13 @@ __device__ __forceinline__ TileCoord tile_of(int b, int nblk, int tiles_m, int g
 constexpr int waitcnt_imm(int vm, int lgkm) { return (vm & 0xF) | ((vm >> 4) << 14) | (7 << 4) | (lgkm << 8); }
 
 template <int BM, int BN, int BK, int S, int WGM, int WGN, int EPI>
-__global__ __launch_bounds__(64 * WGM * WGN) void gemm_bf16_kernel(
+// Two workgroups per CU (256 registers per lane) wherever the ring fits twice in LDS and the
+// wave tile is at most 128 x 64.
+__global__ __launch_bounds__(64 * WGM * WGN,
+                             (BM / WGM) * (BN / WGN) <= 128 * 64 && S * (BM + BN) * BK * 2 <= 80 * 1024 ? 2 : 1)
+void gemm_bf16_kernel(
     const uint16_t* __restrict__ A, const uint16_t* __restrict__ W, const float* __restrict__ bias,
-    void* __restrict__ Cv, int M, int N, int K, int ldc, int gelu_erf, int a_rows, int w_rows, int tiles_m,
+    void* __restrict__ Cv, int M, int N, int K, int ldc, int a_rows, int w_rows, int tiles_m,
     int group_m, float* __restrict__ amax_v, int32_t* __restrict__ amax_i) {
     constexpr int NT = 64 * WGM * WGN, NW = WGM * WGN;
     constexpr int WM = BM / WGM, WN = BN / WGN, FM = WM / 16, FN = WN / 16;
@@ -201,15 +207,109 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_bf16_kernel(
     uint32_t* red_i = red_v + WGN * BM;                            // [WGN][BM] its first column
 
     const int row0 = m0 + wm * WM, col0 = n0 + wn * WN;
+    // Interior tiles (the common case) take the store and argmax paths without bounds checks.
+    const bool interior = m0 + BM <= M && n0 + BN <= N;
     float bcol[FN];  // bias of this lane's column in each 16-column block (0 past N)
-    float cneg[FN];  // 0, or -inf past N (argmax only)
 #pragma unroll
     for (int j = 0; j < FN; ++j) {
         const int n = col0 + j * 16 + r16;
         bcol[j] = (EPI != EPI_LOGITS && n < N) ? bias[n] : 0.f;
-        cneg[j] = n < N ? 0.f : -INFINITY;
     }
-    const bool lane_has_col = col0 + r16 < N;
+
+    // One strip: 16 rows x WN columns staged in scr, then written out (a wavefront's LDS
+    // operations complete in order, so its own staged values are visible to its later reads).
+    auto strip_out = [&](int i, auto checked) {
+        constexpr bool CHK = decltype(checked)::value;
+        const int rs = row0 + i * 16;  // first row of the strip (wave-uniform)
+        const int rows = M - rs, cols = N - col0;
+        if (EPI == EPI_LOGITS) {
+            if (amax_v) {
+                // Row argmax over the staged strip: four lanes per row, each scanning WN/4
+                // consecutive columns (a strict > keeps the first of equal values), then the row
+                // maximum (as an order key) and the smallest column holding it over the four
+                // lanes. Columns past N count as -inf; a lane with no column offers none.
+                constexpr int CQ = WN / 4;
+                const int ar = lane >> 2, aq = lane & 3;
+                const float* sp = scr + ar * SP + aq * CQ;
+                const int lim = CHK ? cols - aq * CQ : CQ;  // valid columns of this lane's quarter
+                float bv = sp[0];
+                int bc = 0;
+#pragma unroll
+                for (int c = 1; c < CQ; ++c) {
+                    float x = sp[c];
+                    if (CHK) x = c < lim ? x : -INFINITY;
+                    const bool take = x > bv;
+                    bv = take ? x : bv;
+                    bc = take ? c : bc;
+                }
+                const uint32_t key = f32_order_key(bv);
+                const uint32_t kmax = quad_max_u32(key);
+                const bool has_col = !CHK || lim > 0;
+                const uint32_t col = (key == kmax && has_col) ? (uint32_t)(col0 + aq * CQ + bc) : 0xffffffffu;
+                const uint32_t cmin = quad_min_u32(col);
+                if (aq == 0) {
+                    const int rl = wn * BM + wm * WM + i * 16 + ar;
+                    red_v[rl] = kmax;
+                    red_i[rl] = cmin;
+                }
+            }
+            // fp32 rows of odd stride: one float per lane, consecutive lanes on consecutive
+            // columns, from the strip's origin plus a 32-bit in-strip offset. Streaming stores:
+            // the logits are written once and not read back by this pass, so they should not
+            // evict the weights and activations from the caches.
+            float* Cs = static_cast<float*>(Cv) + (size_t)rs * ldc + col0;
+#pragma unroll
+            for (int it = 0; it < (16 * WN + GPT2_WAVE - 1) / GPT2_WAVE; ++it) {
+                const int idx = it * GPT2_WAVE + lane;
+                if (16 * WN % GPT2_WAVE != 0 && idx >= 16 * WN) break;
+                const int r = idx / WN, c = idx % WN;
+                if (!CHK || (r < rows && c < cols)) __builtin_nontemporal_store(scr[r * SP + c], Cs + r * ldc + c);
+            }
+        } else if (EPI == EPI_BIAS_RESIDUAL) {
+            // C += staged, four floats per lane
+            float* Cs = static_cast<float*>(Cv) + (size_t)rs * ldc + col0;
+            const bool vec = (ldc & 3) == 0;
+#pragma unroll
+            for (int it = 0; it < (16 * (WN / 4) + GPT2_WAVE - 1) / GPT2_WAVE; ++it) {
+                const int idx = it * GPT2_WAVE + lane;
+                if (16 * (WN / 4) % GPT2_WAVE != 0 && idx >= 16 * (WN / 4)) break;
+                const int r = idx / (WN / 4), c = (idx % (WN / 4)) * 4;
+                if (CHK && r >= rows) continue;
+                const float* sv = &scr[r * SP + c];
+                float* cp = Cs + r * ldc + c;
+                if ((!CHK || c + 4 <= cols) && vec) {
+                    f32x4_t cv = *reinterpret_cast<const f32x4_t*>(cp);
+                    cv[0] += sv[0]; cv[1] += sv[1]; cv[2] += sv[2]; cv[3] += sv[3];
+                    *reinterpret_cast<f32x4_t*>(cp) = cv;
+                } else {
+                    for (int t = 0; t < 4 && c + t < cols; ++t) cp[t] += sv[t];
+                }
+            }
+        } else {
+            // bf16 rows: eight values (16 bytes) per lane
+            uint16_t* Cs = static_cast<uint16_t*>(Cv) + (size_t)rs * ldc + col0;
+            const bool vec = (ldc & 7) == 0;
+#pragma unroll
+            for (int it = 0; it < (16 * (WN / 8) + GPT2_WAVE - 1) / GPT2_WAVE; ++it) {
+                const int idx = it * GPT2_WAVE + lane;
+                if (16 * (WN / 8) % GPT2_WAVE != 0 && idx >= 16 * (WN / 8)) break;
+                const int r = idx / (WN / 8), c = (idx % (WN / 8)) * 8;
+                if (CHK && r >= rows) continue;
+                const float* sv = &scr[r * SP + c];
+                uint16_t* cp = Cs + r * ldc + c;
+                if ((!CHK || c + 8 <= cols) && vec) {
+                    u32x4_t pk;
+                    pk[0] = pack_bf16x2(sv[0], sv[1]);
+                    pk[1] = pack_bf16x2(sv[2], sv[3]);
+                    pk[2] = pack_bf16x2(sv[4], sv[5]);
+                    pk[3] = pack_bf16x2(sv[6], sv[7]);
+                    *reinterpret_cast<u32x4_t*>(cp) = pk;
+                } else {
+                    for (int t = 0; t < 8 && c + t < cols; ++t) cp[t] = f32_to_bf16_bits(sv[t]);
+                }
+            }
+        }
+    };
 
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
@@ -218,97 +318,16 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_bf16_kernel(
         for (int j = 0; j < FN; ++j)
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                float v = acc[i][j][e] + bcol[j];
-                if (EPI == EPI_BIAS_GELU) v = gelu_erf ? gelu_erf_f32(v) : gelu_tanh_f32(v);
+                float v = acc[i][j][e];
+                if (EPI != EPI_LOGITS) v += bcol[j];
+                if (EPI == EPI_BIAS_GELU) v = gelu_tanh_fast(v);
+                if (EPI == EPI_BIAS_GELU_ERF) v = gelu_erf_f32(v);
                 scr[(4 * g4 + e) * SP + j * 16 + r16] = v;
             }
-        if (EPI == EPI_LOGITS && amax_v) {
-            // Per row: this lane's best of its FN columns (they rise with j, so a strict > keeps
-            // the first of equal values), then the row maximum over the 16 lanes, then the
-            // smallest column among the lanes that hold it. Columns past N count as -inf and
-            // lanes whose every column is past N offer no column.
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                float bv = acc[i][0][e] + cneg[0];
-                int bj = 0;
-#pragma unroll
-                for (int j = 1; j < FN; ++j) {
-                    const float x = acc[i][j][e] + cneg[j];
-                    const bool take = x > bv;
-                    bv = take ? x : bv;
-                    bj = take ? j : bj;
-                }
-                const uint32_t key = f32_order_key(bv);
-                const uint32_t kmax = row16_max_u32(key);
-                const uint32_t col = (key == kmax && lane_has_col) ? (uint32_t)(col0 + bj * 16 + r16) : 0xffffffffu;
-                const uint32_t cmin = row16_min_u32(col);
-                if (r16 == 0) {
-                    const int rl = wn * BM + wm * WM + i * 16 + 4 * g4 + e;
-                    red_v[rl] = kmax;
-                    red_i[rl] = cmin;
-                }
-            }
-        }
-        // write the strip out (a wavefront's LDS operations complete in order: no barrier needed)
-        if (EPI == EPI_LOGITS) {
-            // fp32 rows of odd stride: one float per lane, consecutive lanes on consecutive columns
-            // addresses from the strip's origin (wave-uniform) plus a 32-bit in-strip offset
-            const int rs = row0 + i * 16;
-            float* Cs = static_cast<float*>(Cv) + (size_t)rs * ldc + col0;
-            const int rows = M - rs, cols = N - col0;
-#pragma unroll
-            for (int it = 0; it < (16 * WN + GPT2_WAVE - 1) / GPT2_WAVE; ++it) {
-                const int idx = it * GPT2_WAVE + lane;
-                if (16 * WN % GPT2_WAVE != 0 && idx >= 16 * WN) break;
-                const int r = idx / WN, c = idx % WN;
-                // streaming store: the logits are written once and not read back by this pass, so
-                // keep them from evicting the weights and activations from the caches
-                if (r < rows && c < cols) __builtin_nontemporal_store(scr[r * SP + c], Cs + r * ldc + c);
-            }
-        } else if (EPI == EPI_BIAS_RESIDUAL) {
-            // C += staged, four floats per lane
-            float* C = static_cast<float*>(Cv);
-#pragma unroll
-            for (int it = 0; it < (16 * (WN / 4) + GPT2_WAVE - 1) / GPT2_WAVE; ++it) {
-                const int idx = it * GPT2_WAVE + lane;
-                if (16 * (WN / 4) % GPT2_WAVE != 0 && idx >= 16 * (WN / 4)) break;
-                const int r = idx / (WN / 4), c = (idx % (WN / 4)) * 4;
-                const int m = row0 + i * 16 + r, n = col0 + c;
-                if (m >= M) continue;
-                const float* sv = &scr[r * SP + c];
-                float* cp = C + (size_t)m * ldc + n;
-                if (n + 4 <= N && (ldc & 3) == 0) {
-                    f32x4_t cv = *reinterpret_cast<const f32x4_t*>(cp);
-                    cv[0] += sv[0]; cv[1] += sv[1]; cv[2] += sv[2]; cv[3] += sv[3];
-                    *reinterpret_cast<f32x4_t*>(cp) = cv;
-                } else {
-                    for (int t = 0; t < 4 && n + t < N; ++t) cp[t] += sv[t];
-                }
-            }
-        } else {
-            // bf16 rows: eight values (16 bytes) per lane
-            uint16_t* C = static_cast<uint16_t*>(Cv);
-#pragma unroll
-            for (int it = 0; it < (16 * (WN / 8) + GPT2_WAVE - 1) / GPT2_WAVE; ++it) {
-                const int idx = it * GPT2_WAVE + lane;
-                if (16 * (WN / 8) % GPT2_WAVE != 0 && idx >= 16 * (WN / 8)) break;
-                const int r = idx / (WN / 8), c = (idx % (WN / 8)) * 8;
-                const int m = row0 + i * 16 + r, n = col0 + c;
-                if (m >= M) continue;
-                const float* sv = &scr[r * SP + c];
-                uint16_t* cp = C + (size_t)m * ldc + n;
-                if (n + 8 <= N && (ldc & 7) == 0) {
-                    u32x4_t pk;
-                    pk[0] = pack_bf16x2(sv[0], sv[1]);
-                    pk[1] = pack_bf16x2(sv[2], sv[3]);
-                    pk[2] = pack_bf16x2(sv[4], sv[5]);
-                    pk[3] = pack_bf16x2(sv[6], sv[7]);
-                    *reinterpret_cast<u32x4_t*>(cp) = pk;
-                } else {
-                    for (int t = 0; t < 8 && n + t < N; ++t) cp[t] = f32_to_bf16_bits(sv[t]);
-                }
-            }
-        }
+        if (interior)
+            strip_out(i, std::integral_constant<bool, false>{});
+        else
+            strip_out(i, std::integral_constant<bool, true>{});
     }
 
     if (EPI == EPI_LOGITS && amax_v) {
@@ -359,6 +378,8 @@ constexpr TileCfg kCfgs[] = {
     {128, 288, 64, 2, 2, 2},  // 17
     {256, 128, 64, 2, 2, 4},  // 18
     {192, 256, 64, 2, 2, 4},  // 19: 8 waves, 96 x 64 each
+    {256, 128, 32, 3, 2, 2},  // 20: 4 waves, 128 x 64 each, 72 KB ring: 2 workgroups per CU
+    {128, 256, 32, 3, 2, 2},  // 21: 4 waves, 64 x 128 each, 72 KB ring
 };
 [[maybe_unused]] constexpr int kNumCfgs = sizeof(kCfgs) / sizeof(kCfgs[0]);
 
@@ -367,7 +388,9 @@ constexpr TileCfg kCfgs[] = {
 // shrink), so the largest tile that still gives every CU about one tile wins: 192 x 256 for
 // N = 2304 (198 tiles), 256 x 192 for N = 3072 (256 tiles). Narrow outputs (N <= 1024) prefer
 // 64 x 96 tiles with a four-stage ring (two workgroups per CU). The vocabulary projection, with
-// tiles for every CU twelve times over, uses 256 x 256 with a four-stage 32-wide ring.
+// tiles for every CU many times over, uses 256 x 128 tiles of four waves with a three-stage
+// 32-wide ring, two workgroups per CU, so that one workgroup's epilogue (the fp32 logits
+// stores) overlaps the other's main loop.
 int choose_cfg(int M, int N, int K) {
 #ifdef GPT2_GEMM_TUNE
     if (const char* e = getenv("GPT2_GEMM_CFG")) {
@@ -377,7 +400,7 @@ int choose_cfg(int M, int N, int K) {
 #endif
     (void)K;
     auto tiles = [&](int bm, int bn) { return (long)((M + bm - 1) / bm) * ((N + bn - 1) / bn); };
-    if (tiles(256, 256) >= 4 * 256) return 0;  // vocabulary projection
+    if (tiles(256, 256) >= 4 * 256) return 20;  // vocabulary projection
     if (N <= 1024) return 12;
     if (tiles(192, 256) <= 256) return 19;
     return 16;
@@ -398,11 +421,16 @@ hipError_t launch_cfg(const uint16_t* A, const uint16_t* W, const float* bias, v
 #endif
     dim3 grid(tiles_m * tiles_n), block(64 * WGM * WGN);
 #define GPT2_LAUNCH(E)                                                                                      \
-    gemm_bf16_kernel<BM, BN, BK, S, WGM, WGN, E><<<grid, block, 0, s>>>(A, W, bias, C, M, N, K, ldc, gelu_erf, \
+    gemm_bf16_kernel<BM, BN, BK, S, WGM, WGN, E><<<grid, block, 0, s>>>(A, W, bias, C, M, N, K, ldc,           \
                                                                       a_rows, w_rows, tiles_m, group_m, av, ai)
     switch (epi) {
         case EPI_BIAS: GPT2_LAUNCH(EPI_BIAS); break;
-        case EPI_BIAS_GELU: GPT2_LAUNCH(EPI_BIAS_GELU); break;
+        case EPI_BIAS_GELU:
+            if (gelu_erf)
+                GPT2_LAUNCH(EPI_BIAS_GELU_ERF);
+            else
+                GPT2_LAUNCH(EPI_BIAS_GELU);
+            break;
         case EPI_BIAS_RESIDUAL: GPT2_LAUNCH(EPI_BIAS_RESIDUAL); break;
         default: GPT2_LAUNCH(EPI_LOGITS); break;
     }
@@ -422,6 +450,7 @@ hipError_t gemm_bf16(const uint16_t* A, const uint16_t* W, const float* bias, vo
     case i:                                                                                                      \
         return launch_cfg<bm, bn, bk, st, wgm, wgn>(A, W, bias, C, M, N, K, ldc, epi, gelu_erf, a_rows, w_rows, \
                                                     amax_v, amax_i, s);
+#ifdef GPT2_GEMM_TUNE
         GPT2_CFG(0, 256, 256, 32, 4, 2, 4)
         GPT2_CFG(1, 256, 256, 64, 2, 2, 4)
         GPT2_CFG(2, 256, 192, 32, 4, 2, 2)
@@ -442,6 +471,14 @@ hipError_t gemm_bf16(const uint16_t* A, const uint16_t* W, const float* bias, vo
         GPT2_CFG(17, 128, 288, 64, 2, 2, 2)
         GPT2_CFG(18, 256, 128, 64, 2, 2, 4)
         GPT2_CFG(19, 192, 256, 64, 2, 2, 4)
+        GPT2_CFG(20, 256, 128, 32, 3, 2, 2)
+        GPT2_CFG(21, 128, 256, 32, 3, 2, 2)
+#else
+        GPT2_CFG(12, 64, 96, 64, 4, 2, 2)
+        GPT2_CFG(16, 256, 192, 64, 2, 2, 4)
+        GPT2_CFG(19, 192, 256, 64, 2, 2, 4)
+        GPT2_CFG(20, 256, 128, 32, 3, 2, 2)
+#endif
 #undef GPT2_CFG
     }
     return hipErrorInvalidValue;
