@@ -69,20 +69,23 @@ void gemm_bf16_kernel(
     constexpr int CPR = BK / 8;                  // 16-byte chunks per slab row
     constexpr int RPI = 64 / CPR;                // slab rows one 64-lane DMA instruction fills
     constexpr int STAGE = (BM + BN) * BK;        // bf16 elements per stage (A slab, then W slab)
-    constexpr int PW = (BM + BN) / RPI / NW;     // DMA instructions per wavefront per stage
+    constexpr int NI = (BM + BN) / RPI;          // DMA instructions per stage
+    constexpr int PW = (NI + NW - 1) / NW;       // per wavefront (the last ones may repeat a load)
     static_assert(BK == 32 || BK == 64, "BK is 32 or 64");
     static_assert(WM % 16 == 0 && WN % 16 == 0, "wave tile must be a multiple of 16");
-    static_assert(BM % RPI == 0 && BN % RPI == 0 && (BM + BN) % (RPI * NW) == 0, "DMA rows must divide evenly");
-    static_assert(S >= 2 && S <= 5 && (S - 1) * PW < 64, "ring depth");
+    static_assert(BM % RPI == 0 && BN % RPI == 0, "a DMA instruction fills rows of one operand");
+    static_assert(S >= 2 && S <= 6 && (S - 1) * PW < 64, "ring depth");
     static_assert(S * STAGE * 2 <= 160 * 1024, "LDS");
     // One LDS object per stage: lets the compiler see which outstanding DMA an LDS read depends on.
     __shared__ __attribute__((aligned(1024))) uint16_t lds0[STAGE];
     __shared__ __attribute__((aligned(1024))) uint16_t lds1[STAGE];
-    __shared__ __attribute__((aligned(1024))) uint16_t lds2[S > 2 ? STAGE : 8];
-    __shared__ __attribute__((aligned(1024))) uint16_t lds3[S > 3 ? STAGE : 8];
-    __shared__ __attribute__((aligned(1024))) uint16_t lds4[S > 4 ? STAGE : 8];
+    // (stages past S get a 2-byte placeholder so that they take no LDS)
+    __shared__ __attribute__((aligned(S > 2 ? 1024 : 2))) uint16_t lds2[S > 2 ? STAGE : 1];
+    __shared__ __attribute__((aligned(S > 3 ? 1024 : 2))) uint16_t lds3[S > 3 ? STAGE : 1];
+    __shared__ __attribute__((aligned(S > 4 ? 1024 : 2))) uint16_t lds4[S > 4 ? STAGE : 1];
+    __shared__ __attribute__((aligned(S > 5 ? 1024 : 2))) uint16_t lds5[S > 5 ? STAGE : 1];
     auto slot = [&](int i) -> uint16_t* {
-        return i == 0 ? lds0 : i == 1 ? lds1 : i == 2 ? lds2 : i == 3 ? lds3 : lds4;
+        return i == 0 ? lds0 : i == 1 ? lds1 : i == 2 ? lds2 : i == 3 ? lds3 : i == 4 ? lds4 : lds5;
     };
 
     const TileCoord tc = tile_of(blockIdx.x, gridDim.x, tiles_m, group_m < 0 ? -group_m : group_m, group_m > 0);
@@ -101,7 +104,9 @@ void gemm_bf16_kernel(
     int lds_off[PW];
 #pragma unroll
     for (int p = 0; p < PW; ++p) {
-        const int q = wave * PW + p;
+        // past the stage's last instruction, repeat it: the same bytes to the same LDS block, so
+        // every wavefront issues PW loads per stage and the waits below stay exact
+        const int q = min(wave * PW + p, NI - 1);
         const int srow = q * RPI + lane / CPR;  // row within the stage (A rows, then W rows)
         const int sch = lane % CPR;
         const bool is_a = srow < BM;
@@ -182,7 +187,8 @@ void gemm_bf16_kernel(
             case 0: GPT2_WAIT_BARRIER(0); break;
             case 1: GPT2_WAIT_BARRIER(1); break;
             case 2: GPT2_WAIT_BARRIER(2); break;
-            default: GPT2_WAIT_BARRIER(3); break;
+            case 3: GPT2_WAIT_BARRIER(3); break;
+            default: GPT2_WAIT_BARRIER(4); break;
         }
         if (kt + S - 1 < nk) issue((kt + S - 1) % S, (kt + S - 1) * BK);
         compute(kt % S);
@@ -380,13 +386,19 @@ constexpr TileCfg kCfgs[] = {
     {192, 256, 64, 2, 2, 4},  // 19: 8 waves, 96 x 64 each
     {256, 128, 32, 3, 2, 2},  // 20: 4 waves, 128 x 64 each, 72 KB ring: 2 workgroups per CU
     {128, 256, 32, 3, 2, 2},  // 21: 4 waves, 64 x 128 each, 72 KB ring
+    {192, 256, 32, 5, 2, 4},  // 22: 8 waves, 140 KB ring
+    {256, 192, 32, 5, 2, 4},  // 23: 8 waves, 140 KB ring
+    {64, 96, 32, 6, 2, 2},    // 24: 4 waves, 60 KB ring
+    {128, 96, 32, 5, 2, 2},   // 25: 4 waves, 70 KB ring
+    {128, 128, 32, 5, 2, 2},  // 26: 4 waves, 80 KB ring
+    {256, 128, 32, 5, 2, 4},  // 27: 8 waves, 120 KB ring
 };
 [[maybe_unused]] constexpr int kNumCfgs = sizeof(kCfgs) / sizeof(kCfgs[0]);
 
 // Tile shape per GEMM shape, from measurements on MI355X at M = 4096 (bf16, K = 768 / 3072).
 // The block projections are bound by their operand traffic through L2 (re-reads grow as tiles
 // shrink), so the largest tile that still gives every CU about one tile wins: 192 x 256 for
-// N = 2304 (198 tiles), 256 x 192 for N = 3072 (256 tiles). Narrow outputs (N <= 1024) prefer
+// N = 2304 (198 tiles, a five-stage 32-wide ring), 256 x 192 for N = 3072 (256 tiles). Narrow outputs (N <= 1024) prefer
 // 64 x 96 tiles with a four-stage ring (two workgroups per CU). The vocabulary projection, with
 // tiles for every CU many times over, uses 256 x 128 tiles of four waves with a three-stage
 // 32-wide ring, two workgroups per CU, so that one workgroup's epilogue (the fp32 logits
@@ -402,7 +414,7 @@ int choose_cfg(int M, int N, int K) {
     auto tiles = [&](int bm, int bn) { return (long)((M + bm - 1) / bm) * ((N + bn - 1) / bn); };
     if (tiles(256, 256) >= 4 * 256) return 20;  // vocabulary projection
     if (N <= 1024) return 12;
-    if (tiles(192, 256) <= 256) return 19;
+    if (tiles(192, 256) <= 256) return 22;
     return 16;
 }
 
@@ -473,11 +485,17 @@ hipError_t gemm_bf16(const uint16_t* A, const uint16_t* W, const float* bias, vo
         GPT2_CFG(19, 192, 256, 64, 2, 2, 4)
         GPT2_CFG(20, 256, 128, 32, 3, 2, 2)
         GPT2_CFG(21, 128, 256, 32, 3, 2, 2)
+        GPT2_CFG(22, 192, 256, 32, 5, 2, 4)
+        GPT2_CFG(23, 256, 192, 32, 5, 2, 4)
+        GPT2_CFG(24, 64, 96, 32, 6, 2, 2)
+        GPT2_CFG(25, 128, 96, 32, 5, 2, 2)
+        GPT2_CFG(26, 128, 128, 32, 5, 2, 2)
+        GPT2_CFG(27, 256, 128, 32, 5, 2, 4)
 #else
         GPT2_CFG(12, 64, 96, 64, 4, 2, 2)
         GPT2_CFG(16, 256, 192, 64, 2, 2, 4)
-        GPT2_CFG(19, 192, 256, 64, 2, 2, 4)
         GPT2_CFG(20, 256, 128, 32, 3, 2, 2)
+        GPT2_CFG(22, 192, 256, 32, 5, 2, 4)
 #endif
 #undef GPT2_CFG
     }
