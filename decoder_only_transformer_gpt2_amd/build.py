@@ -23,6 +23,11 @@ FLAGS = [
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-I", os.path.join(ROOT, "include"),
 ]
+# Per-source additions. The attention kernel runs its softmax on the MFMA results, so its
+# accumulators are kept in ordinary VGPRs (MFMA in VGPR form) instead of being copied out of AGPRs.
+FILE_FLAGS = {
+    "attention.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
+}
 
 
 def _hipcc() -> str:
@@ -43,7 +48,7 @@ def build(verbose: bool = False) -> str:
 
     def compile_one(src: str) -> str:
         obj = os.path.join(obj_dir, os.path.basename(src)[:-4] + ".o")
-        cmd = [hipcc, *FLAGS, "-c", src, "-o", obj]
+        cmd = [hipcc, *FLAGS, *FILE_FLAGS.get(os.path.basename(src), []), "-c", src, "-o", obj]
         r = subprocess.run(cmd, capture_output=True, text=True)
         if r.returncode != 0:
             raise RuntimeError(f"hipcc failed on {src}:\n{r.stdout}\n{r.stderr}")

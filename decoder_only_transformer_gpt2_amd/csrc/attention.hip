@@ -10,10 +10,12 @@
 // hidden. Scores are computed transposed, S^T = K Q^T, with v_mfma_f32_16x16x32_bf16, so each
 // lane's accumulator column is one query: the softmax row statistics are per-lane values combined
 // over the four 16-lane groups, and the probabilities are already in the operand layout of the
-// second product O^T += V^T P^T. Online softmax in fp32 with exp2 (scale and log2 e folded into
-// one multiplier). Tiles wholly above a wavefront's diagonal are skipped; only tiles that cross it
-// are masked. Workgroups are issued longest-first (last query tiles first) to even out the causal
-// imbalance.
+// second product O^T += V^T P^T. Online softmax in fp32 on the raw scores: exp2(s*c - m*c) is one
+// FMA and one v_exp_f32 per score (c = scale * log2 e); the reference maximum moves only when a
+// query's maximum grows by more than 2^8, so the accumulators are rarely rescaled. The row sums
+// come from the matrix unit as ones x P^T, over the same bf16 probabilities that weight V. Tiles
+// wholly above a wavefront's diagonal are skipped; only tiles that cross it are masked (selects).
+// Workgroups are issued longest-first (last query tiles first) to even out the causal imbalance.
 #include "common.h"
 
 #ifndef GPT2_ATT_WAVES
@@ -45,7 +47,7 @@ __global__ __launch_bounds__(64 * WAVES) void attn_bf16_kernel(const uint16_t* _
     const int qt = nqt - 1 - blockIdx.x / (B * H);
     const int b = bh / H, h = bh % H;
     const int q0 = qt * QT;
-    const int t = threadIdx.x, wave = t / GPT2_WAVE, lane = t % GPT2_WAVE;
+    const int t = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(t / GPT2_WAVE), lane = t % GPT2_WAVE;
     const int r16 = lane & 15, g4 = lane >> 4;
     const int qw = q0 + 16 * wave;  // this wavefront's first query
     const int qi = qw + r16;        // this lane's query (accumulator column)
@@ -63,11 +65,13 @@ __global__ __launch_bounds__(64 * WAVES) void attn_bf16_kernel(const uint16_t* _
         qf[kk] = __builtin_bit_cast(bf16x8_t, u);
     }
 
+    const u32x4_t ones_u = {0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};  // bf16 1.0 x 8
+    const bf16x8_t ones = __builtin_bit_cast(bf16x8_t, ones_u);
     f32x4_t oacc[4];  // [d fragment]; rows d = df*16 + 4*g4 + e, column = query qi
 #pragma unroll
     for (int i = 0; i < 4; ++i) oacc[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    float mrow = -INFINITY;  // running max (log2 domain) of this lane's query
-    float lrow = 0.f;        // this lane's share of the running denominator
+    f32x4_t lacc = {0.f, 0.f, 0.f, 0.f};  // every row: the running denominator of the column's query
+    float mrow = -INFINITY;               // reference maximum of the raw scores of this lane's query
 
     // tile loader: thread t moves CPT 16-byte K chunks (key c/8, chunk c%8) and CPT 16-byte V
     // chunks (key c%64, d chunk c/64) of a tile, c = t + i*NT
@@ -116,40 +120,38 @@ __global__ __launch_bounds__(64 * WAVES) void attn_bf16_kernel(const uint16_t* _
                     s[mf] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[kk], s[mf], 0, 0, 0);
                 }
             }
-            const bool edge = (k0 + KT - 1 > qw) || (k0 + KT > T);
+            if (k0 + KT - 1 > qw || k0 + KT > T) {  // the tile crosses the diagonal or T
+#pragma unroll
+                for (int mf = 0; mf < 4; ++mf)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const int key = k0 + mf * 16 + 4 * g4 + e;
+                        s[mf][e] = (key <= qi && key < T) ? s[mf][e] : -INFINITY;
+                    }
+            }
             float mx = -INFINITY;
 #pragma unroll
-            for (int mf = 0; mf < 4; ++mf)
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    float v = s[mf][e] * scale_log2;
-                    if (edge) {
-                        const int key = k0 + mf * 16 + 4 * g4 + e;
-                        if (key > qi || key >= T) v = -INFINITY;
-                    }
-                    s[mf][e] = v;
-                    mx = fmaxf(mx, v);
-                }
+            for (int mf = 0; mf < 4; ++mf) mx = fmaxf(mx, fmaxf(fmaxf(s[mf][0], s[mf][1]), fmaxf(s[mf][2], s[mf][3])));
             mx = fmaxf(mx, __shfl_xor(mx, 16, GPT2_WAVE));
             mx = fmaxf(mx, __shfl_xor(mx, 32, GPT2_WAVE));
-            // a query with every key of the tile masked (only possible past the last query)
-            // keeps its state: exp2(-inf - m) = 0 for all its keys
-            const float mnew = fmaxf(mrow, mx);
-            const float msafe = mnew == -INFINITY ? 0.f : mnew;
-            const float alpha = __builtin_amdgcn_exp2f(mrow - msafe);
-            mrow = mnew;
-            float ls = 0.f;
+            // The reference maximum moves only when some query's tile maximum exceeds it by more
+            // than 8 in log2 units (the softmax does not depend on the constant subtracted, and
+            // unscaled probabilities up to 2^8 are exact enough in fp32 and bf16); then the whole
+            // wavefront rescales its accumulators, which is rare after the first tiles.
+            if (__builtin_amdgcn_ballot_w64((mx - mrow) * scale_log2 > 8.f)) {
+                const float mnew = fmaxf(mrow, mx);
+                // a query with every key so far masked (only past T) keeps a zero state
+                const float alpha = mnew == -INFINITY ? 1.f : __builtin_amdgcn_exp2f((mrow - mnew) * scale_log2);
+                mrow = mnew;
+#pragma unroll
+                for (int df = 0; df < 4; ++df) oacc[df] *= alpha;
+                lacc *= alpha;
+            }
+            const float mb = mrow == -INFINITY ? 0.f : mrow * scale_log2;
 #pragma unroll
             for (int mf = 0; mf < 4; ++mf)
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const float p = __builtin_amdgcn_exp2f(s[mf][e] - msafe);
-                    s[mf][e] = p;
-                    ls += p;
-                }
-            lrow = lrow * alpha + ls;
-#pragma unroll
-            for (int df = 0; df < 4; ++df) oacc[df] *= alpha;
+                for (int e = 0; e < 4; ++e) s[mf][e] = __builtin_amdgcn_exp2f(fmaf(s[mf][e], scale_log2, -mb));
 
             // O^T[d, query] += V^T[d, key] P^T[key, query], 32 keys per MFMA. Slot j of a lane
             // holds key 32*hh + 4*g4 + j (j < 4) or 32*hh + 16 + 4*g4 + (j - 4) on both operands.
@@ -161,6 +163,7 @@ __global__ __launch_bounds__(64 * WAVES) void attn_bf16_kernel(const uint16_t* _
                 pu[2] = pack_bf16x2(s[2 * hh + 1][0], s[2 * hh + 1][1]);
                 pu[3] = pack_bf16x2(s[2 * hh + 1][2], s[2 * hh + 1][3]);
                 const bf16x8_t pf = __builtin_bit_cast(bf16x8_t, pu);
+                lacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pf, lacc, 0, 0, 0);
 #pragma unroll
                 for (int df = 0; df < 4; ++df) {
                     const uint16_t* vrow = &sVt[buf][(df * 16 + r16) * VTS + 32 * hh + 4 * g4];
@@ -179,11 +182,8 @@ __global__ __launch_bounds__(64 * WAVES) void attn_bf16_kernel(const uint16_t* _
         __syncthreads();
     }
 
-    float l = lrow;
-    l += __shfl_xor(l, 16, GPT2_WAVE);
-    l += __shfl_xor(l, 32, GPT2_WAVE);
     if (qi < T) {
-        const float inv = 1.0f / l;
+        const float inv = 1.0f / lacc[0];
         uint16_t* Ob = O + b * osb + h * osh + qi * ost;
 #pragma unroll
         for (int df = 0; df < 4; ++df) {
