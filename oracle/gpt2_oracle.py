@@ -192,6 +192,39 @@ def argmax_first(logits: np.ndarray) -> np.ndarray:
     return np.argmax(np.asarray(logits), axis=-1)
 
 
+IGNORE_INDEX = -100  # the default ignore_index of the cross-entropy loss the pages use
+
+
+def log_sum_exp(logits: np.ndarray) -> np.ndarray:
+    """log(sum_v exp(logits[..., v])) along the last axis, with the row maximum subtracted first."""
+    z = np.asarray(logits, dtype=F64)
+    m = z.max(axis=-1, keepdims=True)
+    return (m + np.log(np.exp(z - m).sum(axis=-1, keepdims=True)))[..., 0]
+
+
+def shifted_nll(logits: np.ndarray, labels: np.ndarray) -> tuple[np.ndarray, np.ndarray]:
+    """Next-token negative log-likelihood as in [手写] §4.1: the logits of positions 0..T-2 are
+    scored against the labels of positions 1..T-1, nll = logsumexp(logits) - logits[label].
+
+    logits [B, T, V], labels int [B, T]. Returns (nll [B, T-1], counted [B, T-1] bool): positions
+    whose label is the ignore index are not counted and get nll 0."""
+    z = np.asarray(logits, dtype=F64)[:, :-1, :]
+    y = np.asarray(labels)[:, 1:]
+    counted = y != IGNORE_INDEX
+    safe = np.where(counted, y, 0)
+    picked = np.take_along_axis(z, safe[..., None], axis=-1)[..., 0]
+    nll = np.where(counted, log_sum_exp(z) - picked, 0.0)
+    return nll, counted
+
+
+def shifted_cross_entropy(logits: np.ndarray, labels: np.ndarray) -> float:
+    """Mean of shifted_nll over the counted positions ([手写] §4.1, mean reduction); NaN when no
+    position is counted (0 / 0)."""
+    nll, counted = shifted_nll(logits, labels)
+    n = int(counted.sum())
+    return float(nll.sum() / n) if n else float("nan")
+
+
 def param_count(n_vocab: int, n_ctx: int, d: int, n_layer: int, d_mlp: int) -> int:
     """Number of parameters with lm_head tied to wte (counted once).
 

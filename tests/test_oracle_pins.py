@@ -315,6 +315,64 @@ def test_argmax_first_index_on_ties():
     assert O.argmax_first(a).tolist() == [1, 0, 2]
 
 
+# ------------------------------------------------------------------ shifted cross-entropy pins
+def check_cross_entropy(xent):
+    """xent(logits [B,T,V], labels [B,T]) -> mean loss, as in [手写] §4.1 (shift by one, mean
+    reduction, default ignore index -100)."""
+    fails = []
+    # closed form: equal logits give log(V) whatever the labels
+    lab = np.array([[0, 3, 6, 1, 2], [5, 5, 0, 4, 6]])
+    if not math.isclose(xent(np.full((2, 5, 7), 3.0), lab), math.log(7), rel_tol=1e-14):
+        fails.append("uniform logits = log V")
+    # closed form that fixes the shift: position t puts 10 on the label of position t+1
+    B, T, V = 2, 6, 9
+    lab = (np.arange(B * T).reshape(B, T) * 5) % V
+    z = np.zeros((B, T, V))
+    for b in range(B):
+        for t in range(T - 1):
+            z[b, t, lab[b, t + 1]] = 10.0
+    want = math.log1p((V - 1) * math.exp(-10.0))
+    # (lse - 10 cancels: an absolute error of about one ulp of 10 is 5e-12 of the result)
+    if not math.isclose(xent(z, lab), want, rel_tol=1e-10):
+        fails.append("shifted one-hot closed form")
+    # library special case: torch cross_entropy in float64 (mean, ignore_index -100) on the
+    # explicitly shifted tensors, with and without ignored labels
+    r = rng(7)
+    z = r.standard_normal((3, 8, 11)) * 2
+    lab = r.integers(0, 11, (3, 8))
+    lab_ig = lab.copy()
+    lab_ig[0, 3] = lab_ig[2, 7] = lab_ig[1, 0] = -100  # [1, 0] is never a target (no shift onto it)
+    for labels in (lab, lab_ig):
+        ref = F.cross_entropy(torch.from_numpy(z[:, :-1].reshape(-1, 11)),
+                              torch.from_numpy(labels[:, 1:].reshape(-1)).long()).item()
+        if not math.isclose(xent(z, labels), ref, rel_tol=1e-12):
+            fails.append("torch cross_entropy fp64")
+    # invariant: a constant added to every logit of a row changes nothing, even a large one
+    if not math.isclose(xent(z + 1000.0, lab), xent(z, lab), rel_tol=1e-9):
+        fails.append("shift invariance at +1000")
+    # every label ignored: 0 / 0
+    with np.errstate(invalid="ignore"):
+        if not math.isnan(xent(z, np.full((3, 8), -100))):
+            fails.append("all ignored -> nan")
+    return fails
+
+
+def test_cross_entropy_pins():
+    assert check_cross_entropy(O.shifted_cross_entropy) == []
+
+
+def test_shifted_nll_per_position():
+    r = rng(8)
+    z = r.standard_normal((2, 5, 6))
+    lab = r.integers(0, 6, (2, 5))
+    nll, counted = O.shifted_nll(z, lab)
+    assert nll.shape == (2, 4) and counted.all()
+    for b in range(2):
+        for t in range(4):
+            row = z[b, t]
+            assert math.isclose(nll[b, t], math.log(np.exp(row).sum()) - row[lab[b, t + 1]], rel_tol=1e-12)
+
+
 # --------------------------------------------------------------------- planted-mistake audit
 def _unbiased_ln(x, g, b, eps=1e-5):
     x = np.asarray(x, float)
@@ -392,6 +450,50 @@ def _missing_pos_embed(wte, wpe, tok):
     return np.asarray(wte, float)[tok]
 
 
+def _unshifted_xent(z, lab):
+    z = np.asarray(z, float)
+    lab = np.asarray(lab)
+    ok = lab != -100
+    nll = O.log_sum_exp(z) - np.take_along_axis(z, np.where(ok, lab, 0)[..., None], -1)[..., 0]
+    return float(np.where(ok, nll, 0).sum() / ok.sum())
+
+
+def _reverse_shift_xent(z, lab):
+    return _unshifted_xent(np.asarray(z, float)[:, 1:], np.asarray(lab)[:, :-1])
+
+
+def _sum_xent(z, lab):
+    nll, counted = O.shifted_nll(z, lab)
+    return float(nll.sum())
+
+
+def _no_max_xent(z, lab):
+    z = np.asarray(z, float)[:, :-1]
+    y = np.asarray(lab)[:, 1:]
+    ok = y != -100
+    with np.errstate(over="ignore", invalid="ignore"):
+        lse = np.log(np.exp(z).sum(-1))
+    nll = lse - np.take_along_axis(z, np.where(ok, y, 0)[..., None], -1)[..., 0]
+    return float(np.where(ok, nll, 0).sum() / ok.sum()) if ok.any() else float("nan")
+
+
+def _ignored_counted_xent(z, lab):
+    nll, counted = O.shifted_nll(z, lab)
+    return float(nll.sum() / nll.size)
+
+
+def _time_axis_xent(z, lab):
+    # normalises over positions instead of the vocabulary
+    z = np.asarray(z, float)[:, :-1]
+    y = np.asarray(lab)[:, 1:]
+    ok = y != -100
+    m = z.max(axis=1, keepdims=True)
+    lse_t = (m + np.log(np.exp(z - m).sum(axis=1, keepdims=True)))
+    nll = (lse_t - z)
+    picked = np.take_along_axis(nll, np.where(ok, y, 0)[..., None], -1)[..., 0]
+    return float(np.where(ok, picked, 0).sum() / ok.sum()) if ok.any() else float("nan")
+
+
 @pytest.mark.parametrize("check,mutant", [
     (check_layer_norm, _unbiased_ln), (check_layer_norm, _eps_outside_ln), (check_layer_norm, _no_beta_ln),
     (check_gelu, _cubic_sign_gelu), (check_gelu, _no_half_gelu), (check_gelu, O.gelu_erf),
@@ -399,6 +501,9 @@ def _missing_pos_embed(wte, wpe, tok):
     (check_attention, _strict_mask_attn), (check_attention, _no_scale_attn),
     (check_attention, _query_axis_softmax_attn), (check_attention, _mask_after_softmax_attn),
     (check_embed, _shifted_pos_embed), (check_embed, _missing_pos_embed),
+    (check_cross_entropy, _unshifted_xent), (check_cross_entropy, _reverse_shift_xent),
+    (check_cross_entropy, _sum_xent), (check_cross_entropy, _no_max_xent),
+    (check_cross_entropy, _ignored_counted_xent), (check_cross_entropy, _time_axis_xent),
 ])
 def test_pins_catch_planted_mistakes(check, mutant):
     try:
