@@ -1,10 +1,12 @@
 """Forward-pass throughput of the HIP GPT-2 library on one MI355X.
 
-python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload small|medium|xl] [--no-cpu-baseline]
+python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload small|medium|xl] [--no-cpu-baseline] [--no-loss]
 
 One step = one gpt2_forward over a batch of synthetic token ids already resident in HBM:
 embedding, every block, ln_f, the tied lm_head (fp32 logits) and the fused argmax. Weights are the
-seeded synthetic init (no checkpoint exists). Prints one JSON line.
+seeded synthetic init (no checkpoint exists). Prints one JSON line. After the timed region it also
+times gpt2_forward_loss (the same forward with the shifted next-token cross-entropy fused into the
+vocabulary projection, logits not stored) and reports it under "forward_loss".
 
 The roofline object is for the lm_head GEMM, the largest single launch: its duration is taken
 from HIP events the library records on its own stream around that launch in every timed step.
@@ -86,6 +88,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", choices=sorted(WORKLOADS), default="small")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-loss", action="store_true", help="skip the fused forward+loss measurement")
     ap.add_argument("--breakdown", action="store_true", help="also time every launch of one extra forward")
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="after the timed region, run a plain device-to-device copy of this many bytes three "
@@ -157,6 +160,24 @@ def main():
                      "frac": achieved / PEAK_BF16_TFLOPS, "traffic": traffic, "avg_launch_ms": lm_ms,
                      "flops_per_launch": lm_flops},
     }
+
+    if not args.no_loss:
+        # The forward followed by the shifted cross-entropy, with the logits never stored (timed
+        # separately, after the headline region).
+        nll = torch.empty((B, T), dtype=torch.float32, device="cuda")
+        loss = torch.empty((1,), dtype=torch.float32, device="cuda")
+        for _ in range(3):
+            m.forward_loss(tokens, None, nll, loss, ws)
+        n_loss = max(5, args.steps // 5)
+        torch.cuda.synchronize()
+        t2 = time.perf_counter()
+        for _ in range(n_loss):
+            m.forward_loss(tokens, None, nll, loss, ws)
+        torch.cuda.synchronize()
+        lms = (time.perf_counter() - t2) * 1e3 / n_loss
+        out["forward_loss"] = {"ms_per_step": lms, "tokens_per_s": M / (lms * 1e-3), "steps": n_loss,
+                               "loss": float(loss.item()),
+                               "what": "forward + shifted next-token cross-entropy, logits not stored"}
 
     if args.copy_bytes > 0:
         src = torch.empty(args.copy_bytes, dtype=torch.uint8, device="cuda")

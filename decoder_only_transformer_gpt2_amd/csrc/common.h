@@ -73,12 +73,41 @@ __device__ __forceinline__ uint32_t quad_min_u32(uint32_t x) {
     return min(x, dpp_mov<0x4E>(x));
 }
 
+// Log-sum-exp partials in base 2: (m, s) stands for 2^m * s. Merging two keeps the larger maximum;
+// an empty partial has m = -inf and s = 0.
+__device__ __forceinline__ void lse_merge(float& m, float& s, float m2, float s2) {
+    const float mn = fmaxf(m, m2);
+    const float ms = mn == -INFINITY ? 0.f : mn;  // both empty: 0 * 2^-inf + 0 * 2^-inf = 0
+    s = s * __builtin_amdgcn_exp2f(m - ms) + s2 * __builtin_amdgcn_exp2f(m2 - ms);
+    m = mn;
+}
+// The same over each group of 4 consecutive lanes.
+__device__ __forceinline__ void lse_quad_merge(float& m, float& s) {
+    lse_merge(m, s, __builtin_bit_cast(float, dpp_mov<0xB1>(__builtin_bit_cast(uint32_t, m))),
+              __builtin_bit_cast(float, dpp_mov<0xB1>(__builtin_bit_cast(uint32_t, s))));
+    lse_merge(m, s, __builtin_bit_cast(float, dpp_mov<0x4E>(__builtin_bit_cast(uint32_t, m))),
+              __builtin_bit_cast(float, dpp_mov<0x4E>(__builtin_bit_cast(uint32_t, s))));
+}
+
 // ---------------------------------------------------------------------------------------------
 // Launchers (each returns the hipError_t of the launch). Pointers are device pointers.
 // ---------------------------------------------------------------------------------------------
 namespace gpt2k {
 
-enum Epi { EPI_BIAS = 0, EPI_BIAS_GELU = 1, EPI_BIAS_RESIDUAL = 2, EPI_LOGITS = 3, EPI_BIAS_GELU_ERF = 4 };  // 4: kernel-internal
+// 0-3 as in the C ABI; 4 and 5 are internal: the erf GELU and the log-sum-exp head (no logits).
+enum Epi { EPI_BIAS = 0, EPI_BIAS_GELU = 1, EPI_BIAS_RESIDUAL = 2, EPI_LOGITS = 3, EPI_BIAS_GELU_ERF = 4, EPI_LSE = 5 };
+
+// Per-row, per-column-tile outputs of the vocabulary projection's epilogue ([M, n_part] arrays).
+//   EPI_LOGITS: pv/pi = (max logit, first column holding it) when pv is set.
+//   EPI_LSE:    pv/ps = (max of y, sum of 2^(y - max)) over the tile with y = logit * log2(e), and
+//               tgt_logit[m] = logit of column tgt[m] from the tile holding it (tgt[m] < 0: none).
+struct HeadOut {
+    float* pv = nullptr;
+    float* ps = nullptr;
+    int32_t* pi = nullptr;
+    const int32_t* tgt = nullptr;
+    float* tgt_logit = nullptr;
+};
 
 // Tile width along N the GEMMs use for a shape: the argmax partial count per row is ceil(N / BN).
 int gemm_bf16_tile_n(int M, int N, int K);
@@ -93,12 +122,22 @@ hipError_t layernorm(const float* x, const float* g, const float* b, void* y, in
 
 // A must have a_rows >= M readable rows and W w_rows >= N (rows past them are never read).
 hipError_t gemm_bf16(const uint16_t* A, const uint16_t* W, const float* bias, void* C, int M, int N, int K,
-                     long ldc, int epi, int gelu_erf, int a_rows, int w_rows, float* amax_v, int32_t* amax_i,
-                     hipStream_t s);
+                     long ldc, int epi, int gelu_erf, int a_rows, int w_rows, const HeadOut& ho, hipStream_t s);
 hipError_t gemm_f32(const float* A, const float* W, const float* bias, void* C, int M, int N, int K, long ldc,
-                    int epi, int gelu_erf, float* amax_v, int32_t* amax_i, hipStream_t s);
+                    int epi, int gelu_erf, const HeadOut& ho, hipStream_t s);
 
 hipError_t argmax_reduce(const float* pv, const int32_t* pi, int M, int n_part, int32_t* out, hipStream_t s);
+
+// Shifted next-token targets: tgt[m] = labels[m + 1] for positions t = m % T < T - 1, -1 for the
+// last position of each sequence and for the ignore index; a label outside [0, V) that is not the
+// ignore index sets flags[0] = 1 and counts as ignored.
+hipError_t xent_targets(const int32_t* labels, int M, int T, int n_vocab, int32_t* tgt, int32_t* flags,
+                        hipStream_t s);
+// nll[m] = log-sum-exp of row m (from the EPI_LSE partials) - tgt_logit[m], or 0 where tgt[m] < 0.
+hipError_t xent_rows(const float* pm, const float* ps, const int32_t* tgt, const float* tgt_logit, int M,
+                     int n_part, float* nll, hipStream_t s);
+// loss[0] = sum of nll over rows with tgt >= 0 / their count (NaN when none), summed in a fixed order.
+hipError_t xent_mean(const float* nll, const int32_t* tgt, int M, float* loss, hipStream_t s);
 
 hipError_t attention_bf16(const uint16_t* q, const int64_t* qs, const uint16_t* k, const int64_t* ks,
                           const uint16_t* v, const int64_t* vs, uint16_t* o, const int64_t* os, int B, int H,

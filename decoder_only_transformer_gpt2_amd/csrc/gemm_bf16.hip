@@ -63,8 +63,9 @@ __global__ __launch_bounds__(64 * WGM * WGN,
 void gemm_bf16_kernel(
     const uint16_t* __restrict__ A, const uint16_t* __restrict__ W, const float* __restrict__ bias,
     void* __restrict__ Cv, int M, int N, int K, int ldc, int a_rows, int w_rows, int tiles_m,
-    int group_m, float* __restrict__ amax_v, int32_t* __restrict__ amax_i) {
+    int group_m, HeadOut ho) {
     constexpr int NT = 64 * WGM * WGN, NW = WGM * WGN;
+    constexpr bool HEAD = EPI == EPI_LOGITS || EPI == EPI_LSE;  // vocabulary projection: no bias
     constexpr int WM = BM / WGM, WN = BN / WGN, FM = WM / 16, FN = WN / 16;
     constexpr int CPR = BK / 8;                  // 16-byte chunks per slab row
     constexpr int RPI = 64 / CPR;                // slab rows one 64-lane DMA instruction fills
@@ -211,6 +212,8 @@ void gemm_bf16_kernel(
     float* scr = reinterpret_cast<float*>(slot(wave / WAVES_PER_SLOT)) + (wave % WAVES_PER_SLOT) * (16 * SP);
     uint32_t* red_v = reinterpret_cast<uint32_t*>(slot(S - 1));  // [WGN][BM] row maximum (order key)
     uint32_t* red_i = red_v + WGN * BM;                            // [WGN][BM] its first column
+    float* red_m = reinterpret_cast<float*>(red_v);                // (EPI_LSE) [WGN][BM] base-2 maximum
+    float* red_s = reinterpret_cast<float*>(red_i);                // (EPI_LSE) [WGN][BM] sum below it
 
     const int row0 = m0 + wm * WM, col0 = n0 + wn * WN;
     // Interior tiles (the common case) take the store and argmax paths without bounds checks.
@@ -219,7 +222,7 @@ void gemm_bf16_kernel(
 #pragma unroll
     for (int j = 0; j < FN; ++j) {
         const int n = col0 + j * 16 + r16;
-        bcol[j] = (EPI != EPI_LOGITS && n < N) ? bias[n] : 0.f;
+        bcol[j] = (!HEAD && n < N) ? bias[n] : 0.f;
     }
 
     // One strip: 16 rows x WN columns staged in scr, then written out (a wavefront's LDS
@@ -228,8 +231,41 @@ void gemm_bf16_kernel(
         constexpr bool CHK = decltype(checked)::value;
         const int rs = row0 + i * 16;  // first row of the strip (wave-uniform)
         const int rows = M - rs, cols = N - col0;
-        if (EPI == EPI_LOGITS) {
-            if (amax_v) {
+        if (EPI == EPI_LSE) {
+            // Per row over the staged strip, four lanes per row with WN/4 consecutive columns each:
+            // the maximum of y = logit * log2(e) and the sum of 2^(y - max), then both combined over
+            // the four lanes. Columns past N are left out. The lane whose columns hold the row's
+            // target keeps that logit. Nothing is stored to the logits.
+            constexpr int CQ = WN / 4;
+            constexpr float LOG2E = 1.4426950408889634f;
+            const int ar = lane >> 2, aq = lane & 3;
+            const float* sp = scr + ar * SP + aq * CQ;
+            const int lim = CHK ? cols - aq * CQ : CQ;
+            float y[CQ];
+            float mx = -INFINITY;
+#pragma unroll
+            for (int c = 0; c < CQ; ++c) {
+                y[c] = sp[c] * LOG2E;
+                if (CHK) y[c] = c < lim ? y[c] : -INFINITY;
+                mx = fmaxf(mx, y[c]);
+            }
+            const float ms = mx == -INFINITY ? 0.f : mx;
+            float sum = 0.f;
+#pragma unroll
+            for (int c = 0; c < CQ; ++c) sum += __builtin_amdgcn_exp2f(y[c] - ms);
+            lse_quad_merge(mx, sum);
+            const int row = rs + ar;
+            if (!CHK || row < M) {
+                const int tc = ho.tgt[row], c0 = col0 + aq * CQ;
+                if (tc >= c0 && tc < c0 + CQ && tc < N) ho.tgt_logit[row] = sp[tc - c0];
+            }
+            if (aq == 0) {
+                const int rl = wn * BM + wm * WM + i * 16 + ar;
+                red_m[rl] = mx;
+                red_s[rl] = sum;
+            }
+        } else if (EPI == EPI_LOGITS) {
+            if (ho.pv) {
                 // Row argmax over the staged strip: four lanes per row, each scanning WN/4
                 // consecutive columns (a strict > keeps the first of equal values), then the row
                 // maximum (as an order key) and the smallest column holding it over the four
@@ -325,7 +361,7 @@ void gemm_bf16_kernel(
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 float v = acc[i][j][e];
-                if (EPI != EPI_LOGITS) v += bcol[j];
+                if (!HEAD) v += bcol[j];
                 if (EPI == EPI_BIAS_GELU) v = gelu_tanh_fast(v);
                 if (EPI == EPI_BIAS_GELU_ERF) v = gelu_erf_f32(v);
                 scr[(4 * g4 + e) * SP + j * 16 + r16] = v;
@@ -336,7 +372,21 @@ void gemm_bf16_kernel(
             strip_out(i, std::integral_constant<bool, true>{});
     }
 
-    if (EPI == EPI_LOGITS && amax_v) {
+    if (EPI == EPI_LSE) {
+        __syncthreads();
+        const int tiles_n = (N + BN - 1) / BN;
+        for (int rl = threadIdx.x; rl < BM; rl += NT) {
+            const int m = m0 + rl;
+            if (m < M) {
+                float mx = red_m[rl], sum = red_s[rl];
+#pragma unroll
+                for (int w = 1; w < WGN; ++w) lse_merge(mx, sum, red_m[w * BM + rl], red_s[w * BM + rl]);
+                ho.pv[(size_t)m * tiles_n + tc.tn] = mx;
+                ho.ps[(size_t)m * tiles_n + tc.tn] = sum;
+            }
+        }
+    }
+    if (EPI == EPI_LOGITS && ho.pv) {
         __syncthreads();
         const int tiles_n = (N + BN - 1) / BN;
         for (int rl = threadIdx.x; rl < BM; rl += NT) {
@@ -350,8 +400,8 @@ void gemm_bf16_kernel(
                     kv = take ? v2 : kv;
                     ki = take ? i2 : ki;
                 }
-                amax_v[(size_t)m * tiles_n + tc.tn] = f32_from_order_key(kv);
-                amax_i[(size_t)m * tiles_n + tc.tn] = (int32_t)ki;
+                ho.pv[(size_t)m * tiles_n + tc.tn] = f32_from_order_key(kv);
+                ho.pi[(size_t)m * tiles_n + tc.tn] = (int32_t)ki;
             }
         }
     }
@@ -420,7 +470,7 @@ int choose_cfg(int M, int N, int K) {
 
 template <int BM, int BN, int BK, int S, int WGM, int WGN>
 hipError_t launch_cfg(const uint16_t* A, const uint16_t* W, const float* bias, void* C, int M, int N, int K, long ldc,
-                      int epi, int gelu_erf, int a_rows, int w_rows, float* av, int32_t* ai, hipStream_t s) {
+                      int epi, int gelu_erf, int a_rows, int w_rows, const HeadOut& ho, hipStream_t s) {
     const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
     // group_m > 0: XCD-contiguous remap + groups of group_m row-tiles; < 0: plain order, groups of
     // -group_m. Measured with cold caches (as inside a forward): the vocabulary projection is fastest
@@ -434,7 +484,7 @@ hipError_t launch_cfg(const uint16_t* A, const uint16_t* W, const float* bias, v
     dim3 grid(tiles_m * tiles_n), block(64 * WGM * WGN);
 #define GPT2_LAUNCH(E)                                                                                      \
     gemm_bf16_kernel<BM, BN, BK, S, WGM, WGN, E><<<grid, block, 0, s>>>(A, W, bias, C, M, N, K, ldc,           \
-                                                                      a_rows, w_rows, tiles_m, group_m, av, ai)
+                                                                      a_rows, w_rows, tiles_m, group_m, ho)
     switch (epi) {
         case EPI_BIAS: GPT2_LAUNCH(EPI_BIAS); break;
         case EPI_BIAS_GELU:
@@ -444,6 +494,7 @@ hipError_t launch_cfg(const uint16_t* A, const uint16_t* W, const float* bias, v
                 GPT2_LAUNCH(EPI_BIAS_GELU);
             break;
         case EPI_BIAS_RESIDUAL: GPT2_LAUNCH(EPI_BIAS_RESIDUAL); break;
+        case EPI_LSE: GPT2_LAUNCH(EPI_LSE); break;
         default: GPT2_LAUNCH(EPI_LOGITS); break;
     }
 #undef GPT2_LAUNCH
@@ -455,13 +506,13 @@ hipError_t launch_cfg(const uint16_t* A, const uint16_t* W, const float* bias, v
 int gemm_bf16_tile_n(int M, int N, int K) { return kCfgs[choose_cfg(M, N, K)].bn; }
 
 hipError_t gemm_bf16(const uint16_t* A, const uint16_t* W, const float* bias, void* C, int M, int N, int K, long ldc,
-                     int epi, int gelu_erf, int a_rows, int w_rows, float* amax_v, int32_t* amax_i, hipStream_t s) {
+                     int epi, int gelu_erf, int a_rows, int w_rows, const HeadOut& ho, hipStream_t s) {
     if (ldc < N || ldc > (1 << 26)) return hipErrorInvalidValue;  // in-strip offsets are 32-bit
     switch (choose_cfg(M, N, K)) {
 #define GPT2_CFG(i, bm, bn, bk, st, wgm, wgn)                                                                    \
     case i:                                                                                                      \
-        return launch_cfg<bm, bn, bk, st, wgm, wgn>(A, W, bias, C, M, N, K, ldc, epi, gelu_erf, a_rows, w_rows, \
-                                                    amax_v, amax_i, s);
+        return launch_cfg<bm, bn, bk, st, wgm, wgn>(A, W, bias, C, M, N, K, ldc, epi, gelu_erf, a_rows, w_rows, ho, \
+                                                    s);
 #ifdef GPT2_GEMM_TUNE
         GPT2_CFG(0, 256, 256, 32, 4, 2, 4)
         GPT2_CFG(1, 256, 256, 64, 2, 2, 4)

@@ -14,7 +14,7 @@ template <int EPI>
 __global__ __launch_bounds__(256) void gemm_f32_kernel(const float* __restrict__ A, const float* __restrict__ W,
                                                        const float* __restrict__ bias, void* __restrict__ Cv, int M,
                                                        int N, int K, long ldc, int gelu_erf, int tiles_m,
-                                                       float* __restrict__ amax_v, int32_t* __restrict__ amax_i) {
+                                                       HeadOut ho) {
     __shared__ __attribute__((aligned(16))) float sA[TK][TM + PAD];
     __shared__ __attribute__((aligned(16))) float sW[TK][TN + PAD];
     const int tm = blockIdx.x % tiles_m, tn = blockIdx.x / tiles_m;
@@ -42,7 +42,42 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(const float* __restrict__
         }
     }
 
-    if (EPI == EPI_LOGITS) {
+    if (EPI == EPI_LSE) {
+        // per row: (max of y = logit * log2 e, sum of 2^(y - max)) over this tile's columns, merged
+        // over the 16 consecutive lanes that hold the row; the lane holding the target keeps it
+        constexpr float LOG2E = 1.4426950408889634f;
+        const int tiles_n = (N + TN - 1) / TN;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int m = m0 + ty * 4 + i;
+            float mx = -INFINITY;
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                if (n0 + tx * 4 + j < N) mx = fmaxf(mx, acc[i][j] * LOG2E);
+            const float ms = mx == -INFINITY ? 0.f : mx;
+            float sum = 0.f;
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                if (n0 + tx * 4 + j < N) sum += exp2f(acc[i][j] * LOG2E - ms);
+#pragma unroll
+            for (int o = 8; o >= 1; o >>= 1) {
+                const float m2 = __shfl_xor(mx, o, GPT2_WAVE), s2 = __shfl_xor(sum, o, GPT2_WAVE);
+                const float mn = fmaxf(mx, m2), mz = mn == -INFINITY ? 0.f : mn;
+                sum = sum * exp2f(mx - mz) + s2 * exp2f(m2 - mz);
+                mx = mn;
+            }
+            if (m < M) {
+                const int tc = ho.tgt[m];
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    if (tc == n0 + tx * 4 + j && tc < N) ho.tgt_logit[m] = acc[i][j];
+                if (tx == 0) {
+                    ho.pv[(size_t)m * tiles_n + tn] = mx;
+                    ho.ps[(size_t)m * tiles_n + tn] = sum;
+                }
+            }
+        }
+    } else if (EPI == EPI_LOGITS) {
         float* C = static_cast<float*>(Cv);
         const int tiles_n = (N + TN - 1) / TN;
 #pragma unroll
@@ -58,7 +93,7 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(const float* __restrict__
                     argmax_merge(bv, bi, acc[i][j], n);
                 }
             }
-            if (amax_v) {
+            if (ho.pv) {
                 // the 16 threads of one row are 16 consecutive lanes of a wavefront
 #pragma unroll
                 for (int o = 8; o >= 1; o >>= 1) {
@@ -67,8 +102,8 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(const float* __restrict__
                     argmax_merge(bv, bi, v2, i2);
                 }
                 if (tx == 0 && m < M) {
-                    amax_v[(size_t)m * tiles_n + tn] = bv;
-                    amax_i[(size_t)m * tiles_n + tn] = bi;
+                    ho.pv[(size_t)m * tiles_n + tn] = bv;
+                    ho.pi[(size_t)m * tiles_n + tn] = bi;
                 }
             }
         }
@@ -97,24 +132,19 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(const float* __restrict__
 }  // namespace
 
 hipError_t gemm_f32(const float* A, const float* W, const float* bias, void* C, int M, int N, int K, long ldc, int epi,
-                    int gelu_erf, float* amax_v, int32_t* amax_i, hipStream_t s) {
-    static_assert(kGemmF32BN == TN, "argmax partial count assumes BN = 64");
+                    int gelu_erf, const HeadOut& ho, hipStream_t s) {
+    static_assert(kGemmF32BN == TN, "head partial count assumes BN = 64");
     const int tiles_m = (M + TM - 1) / TM, tiles_n = (N + TN - 1) / TN;
     dim3 grid(tiles_m * tiles_n), block(256);
+#define GPT2_LAUNCH(E) gemm_f32_kernel<E><<<grid, block, 0, s>>>(A, W, bias, C, M, N, K, ldc, gelu_erf, tiles_m, ho)
     switch (epi) {
-        case EPI_BIAS:
-            gemm_f32_kernel<EPI_BIAS><<<grid, block, 0, s>>>(A, W, bias, C, M, N, K, ldc, gelu_erf, tiles_m, amax_v, amax_i);
-            break;
-        case EPI_BIAS_GELU:
-            gemm_f32_kernel<EPI_BIAS_GELU><<<grid, block, 0, s>>>(A, W, bias, C, M, N, K, ldc, gelu_erf, tiles_m, amax_v, amax_i);
-            break;
-        case EPI_BIAS_RESIDUAL:
-            gemm_f32_kernel<EPI_BIAS_RESIDUAL><<<grid, block, 0, s>>>(A, W, bias, C, M, N, K, ldc, gelu_erf, tiles_m, amax_v, amax_i);
-            break;
-        default:
-            gemm_f32_kernel<EPI_LOGITS><<<grid, block, 0, s>>>(A, W, bias, C, M, N, K, ldc, gelu_erf, tiles_m, amax_v, amax_i);
-            break;
+        case EPI_BIAS: GPT2_LAUNCH(EPI_BIAS); break;
+        case EPI_BIAS_GELU: GPT2_LAUNCH(EPI_BIAS_GELU); break;
+        case EPI_BIAS_RESIDUAL: GPT2_LAUNCH(EPI_BIAS_RESIDUAL); break;
+        case EPI_LSE: GPT2_LAUNCH(EPI_LSE); break;
+        default: GPT2_LAUNCH(EPI_LOGITS); break;
     }
+#undef GPT2_LAUNCH
     return hipGetLastError();
 }
 

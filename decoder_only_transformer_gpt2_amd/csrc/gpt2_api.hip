@@ -29,7 +29,7 @@ enum LayerTensor {
 };
 
 struct WorkspaceLayout {
-    size_t x, a, qkv, o, hid, amax_v, amax_i, flags, total;
+    size_t x, a, qkv, o, hid, amax_v, amax_i, tgt, tgt_logit, flags, total;
     int64_t Mp;
     int n_part;
 };
@@ -92,8 +92,10 @@ WorkspaceLayout ws_layout(const gpt2_model* m, int B, int T) {
     w.qkv = take((size_t)w.Mp * 3 * c.d_model * as);
     w.o = take((size_t)w.Mp * c.d_model * as);
     w.hid = take((size_t)w.Mp * c.d_mlp * as);
-    w.amax_v = take((size_t)M * w.n_part * 4);
-    w.amax_i = take((size_t)M * w.n_part * 4);
+    w.amax_v = take((size_t)M * w.n_part * 4);  // head partials: argmax value / base-2 maximum
+    w.amax_i = take((size_t)M * w.n_part * 4);  // argmax index / sum below the maximum
+    w.tgt = take((size_t)M * 4);                // cross-entropy target column per row
+    w.tgt_logit = take((size_t)M * 4);          // and its logit
     w.flags = take((size_t)gpt2k::embed_flag_count((int)M) * 4);
     w.total = off;
     return w;
@@ -117,15 +119,15 @@ gpt2_status check_run_args(const gpt2_model* m, const int32_t* tokens, int B, in
 
 // Linear dispatch on the compute dtype.
 hipError_t linear(const gpt2_model* m, const void* A, int widx, int bidx, void* C, int M, int N, int K, long ldc,
-                  int epi, float* av, int32_t* ai, hipStream_t s) {
+                  int epi, const gpt2k::HeadOut& ho, hipStream_t s) {
     const float* bias = bidx >= 0 ? static_cast<const float*>(wptr(m, bidx)) : nullptr;
     const int ge = m->cfg.gelu == GPT2_GELU_ERF;
     if (is_bf16(m))
         return gpt2k::gemm_bf16(static_cast<const uint16_t*>(A), static_cast<const uint16_t*>(wptr(m, widx)), bias, C, M,
-                                N, K, ldc, epi, ge, (int)round_up(M, kRowPad), (int)m->slots[widx].rows_padded, av, ai,
+                                N, K, ldc, epi, ge, (int)round_up(M, kRowPad), (int)m->slots[widx].rows_padded, ho,
                                 s);
     return gpt2k::gemm_f32(static_cast<const float*>(A), static_cast<const float*>(wptr(m, widx)), bias, C, M, N, K, ldc,
-                           epi, ge, av, ai, s);
+                           epi, ge, ho, s);
 }
 
 // Enqueues launches in order, optionally recording caller events around them, or (dry) only
@@ -183,8 +185,7 @@ gpt2_status enqueue_trunk(const gpt2_model* m, const int32_t* tokens, int B, int
         auto L = [&](int t) { return layer_idx(l, t); };
         auto vecp = [&](int t) { return static_cast<const float*>(wptr(m, L(t))); };
         GPT2_RUN(GPT2_K_LN, gpt2k::layernorm(x, vecp(LN1_W), vecp(LN1_B), a, M, d, c.ln_eps, bf, s));
-        GPT2_RUN(GPT2_K_QKV, linear(m, a, L(ATTN_W), L(ATTN_B), qkv, M, 3 * d, d, 3 * d, gpt2k::EPI_BIAS, nullptr,
-                                    nullptr, s));
+        GPT2_RUN(GPT2_K_QKV, linear(m, a, L(ATTN_W), L(ATTN_B), qkv, M, 3 * d, d, 3 * d, gpt2k::EPI_BIAS, {}, s));
         const char* qb = static_cast<const char*>(qkv);
         if (bf)
             GPT2_RUN(GPT2_K_ATTN, gpt2k::attention_bf16(reinterpret_cast<const uint16_t*>(qb), qs,
@@ -197,11 +198,11 @@ gpt2_status enqueue_trunk(const gpt2_model* m, const int32_t* tokens, int B, int
                                                        reinterpret_cast<const float*>(qb + 2 * d * as), qs,
                                                        static_cast<float*>(o), os, B, H, T, s));
         GPT2_RUN(GPT2_K_ATTN_PROJ, linear(m, o, L(APROJ_W), L(APROJ_B), x, M, d, d, d, gpt2k::EPI_BIAS_RESIDUAL,
-                                          nullptr, nullptr, s));
+                                          {}, s));
         GPT2_RUN(GPT2_K_LN, gpt2k::layernorm(x, vecp(LN2_W), vecp(LN2_B), a, M, d, c.ln_eps, bf, s));
-        GPT2_RUN(GPT2_K_FC, linear(m, a, L(FC_W), L(FC_B), hid, M, f, d, f, gpt2k::EPI_BIAS_GELU, nullptr, nullptr, s));
+        GPT2_RUN(GPT2_K_FC, linear(m, a, L(FC_W), L(FC_B), hid, M, f, d, f, gpt2k::EPI_BIAS_GELU, {}, s));
         GPT2_RUN(GPT2_K_MLP_PROJ, linear(m, hid, L(MPROJ_W), L(MPROJ_B), x, M, d, f, d, gpt2k::EPI_BIAS_RESIDUAL,
-                                         nullptr, nullptr, s));
+                                         {}, s));
     }
     return GPT2_OK;
 }
@@ -219,11 +220,43 @@ gpt2_status enqueue_forward(const gpt2_model* m, const int32_t* tokens, int B, i
     GPT2_RUN(GPT2_K_LN_F, gpt2k::layernorm(reinterpret_cast<float*>(ws + w.x), static_cast<const float*>(wptr(m, ln_f)),
                                            static_cast<const float*>(wptr(m, ln_f + 1)), ws + w.a, M, c.d_model,
                                            c.ln_eps, is_bf16(m), s));
-    float* av = argmax ? reinterpret_cast<float*>(ws + w.amax_v) : nullptr;
-    int32_t* ai = argmax ? reinterpret_cast<int32_t*>(ws + w.amax_i) : nullptr;
+    gpt2k::HeadOut ho;
+    if (argmax) {
+        ho.pv = reinterpret_cast<float*>(ws + w.amax_v);
+        ho.pi = reinterpret_cast<int32_t*>(ws + w.amax_i);
+    }
     GPT2_RUN(GPT2_K_LM_HEAD,
-             linear(m, ws + w.a, 0, -1, logits, M, c.n_vocab, c.d_model, c.n_vocab, gpt2k::EPI_LOGITS, av, ai, s));
-    if (argmax) GPT2_RUN(GPT2_K_ARGMAX, gpt2k::argmax_reduce(av, ai, M, w.n_part, argmax, s));
+             linear(m, ws + w.a, 0, -1, logits, M, c.n_vocab, c.d_model, c.n_vocab, gpt2k::EPI_LOGITS, ho, s));
+    if (argmax) GPT2_RUN(GPT2_K_ARGMAX, gpt2k::argmax_reduce(ho.pv, ho.pi, M, w.n_part, argmax, s));
+    return GPT2_OK;
+}
+
+// The forward followed by the shifted cross-entropy ([手写] §4.1): trunk, ln_f, targets, the
+// vocabulary projection with the log-sum-exp epilogue (no logits stored), per-row losses, mean.
+gpt2_status enqueue_forward_loss(const gpt2_model* m, const int32_t* tokens, const int32_t* labels, int B, int T,
+                                 float* nll, float* loss, char* ws, Sequencer& q) {
+    const gpt2_config_t& c = m->cfg;
+    const hipStream_t s = q.s;
+    const WorkspaceLayout w = ws_layout(m, B, T);
+    const int M = B * T;
+    gpt2_status st = enqueue_trunk(m, tokens, B, T, c.n_layer, ws, w, q);
+    if (st != GPT2_OK) return st;
+    const int ln_f = 2 + c.n_layer * PER_LAYER;
+    GPT2_RUN(GPT2_K_LN_F, gpt2k::layernorm(reinterpret_cast<float*>(ws + w.x), static_cast<const float*>(wptr(m, ln_f)),
+                                           static_cast<const float*>(wptr(m, ln_f + 1)), ws + w.a, M, c.d_model,
+                                           c.ln_eps, is_bf16(m), s));
+    int32_t* tgt = reinterpret_cast<int32_t*>(ws + w.tgt);
+    GPT2_RUN(GPT2_K_XENT, gpt2k::xent_targets(labels ? labels : tokens, M, T, c.n_vocab, tgt,
+                                              reinterpret_cast<int32_t*>(ws + w.flags), s));
+    gpt2k::HeadOut ho;
+    ho.pv = reinterpret_cast<float*>(ws + w.amax_v);
+    ho.ps = reinterpret_cast<float*>(ws + w.amax_i);
+    ho.tgt = tgt;
+    ho.tgt_logit = reinterpret_cast<float*>(ws + w.tgt_logit);
+    GPT2_RUN(GPT2_K_LM_HEAD,
+             linear(m, ws + w.a, 0, -1, nullptr, M, c.n_vocab, c.d_model, c.n_vocab, gpt2k::EPI_LSE, ho, s));
+    GPT2_RUN(GPT2_K_XENT, gpt2k::xent_rows(ho.pv, ho.ps, tgt, ho.tgt_logit, M, w.n_part, nll, s));
+    GPT2_RUN(GPT2_K_XENT, gpt2k::xent_mean(nll, tgt, M, loss, s));
     return GPT2_OK;
 }
 
@@ -300,6 +333,16 @@ gpt2_status gpt2_forward(const gpt2_model* m, const int32_t* tokens, int32_t B, 
     if (st != GPT2_OK) return st;
     Sequencer q{s};
     return enqueue_forward(m, tokens, B, T, logits, argmax, static_cast<char*>(ws_dev), q);
+}
+
+gpt2_status gpt2_forward_loss(const gpt2_model* m, const int32_t* tokens, const int32_t* labels, int32_t B, int32_t T,
+                              float* nll, float* loss, void* ws_dev, size_t ws_bytes, hipStream_t s) {
+    gpt2_status st = check_run_args(m, tokens, B, T, nll, ws_dev, ws_bytes);
+    if (st != GPT2_OK) return st;
+    if (!loss) return GPT2_EINVAL;
+    if (T < 2) return GPT2_ESHAPE;
+    Sequencer q{s};
+    return enqueue_forward_loss(m, tokens, labels, B, T, nll, loss, static_cast<char*>(ws_dev), q);
 }
 
 gpt2_status gpt2_forward_timed(const gpt2_model* m, const int32_t* tokens, int32_t B, int32_t T, float* logits,
@@ -397,10 +440,10 @@ gpt2_status gpt2_linear(const void* A, const void* W, const float* bias, void* C
     const int ge = gelu == GPT2_GELU_ERF;
     if (dtype == GPT2_BF16)
         GPT2_HIP(gpt2k::gemm_bf16(static_cast<const uint16_t*>(A), static_cast<const uint16_t*>(W), bias, C, M, N, K, ldc,
-                                  epi, ge, (int)round_up(M, kRowPad), (int)round_up(N, kRowPad), nullptr, nullptr, s));
+                                  epi, ge, (int)round_up(M, kRowPad), (int)round_up(N, kRowPad), {}, s));
     else
         GPT2_HIP(gpt2k::gemm_f32(static_cast<const float*>(A), static_cast<const float*>(W), bias, C, M, N, K, ldc, epi,
-                                 ge, nullptr, nullptr, s));
+                                 ge, {}, s));
     return GPT2_OK;
 }
 
@@ -410,7 +453,7 @@ const char* gpt2_strerror(gpt2_status s) {
         case GPT2_EINVAL: return "invalid argument";
         case GPT2_ESHAPE: return "unsupported or inconsistent shape";
         case GPT2_EWORKSPACE: return "buffer smaller than required";
-        case GPT2_ETOKEN: return "token id outside [0, n_vocab)";
+        case GPT2_ETOKEN: return "token id (or label) outside [0, n_vocab)";
         case GPT2_EHIP: return "HIP runtime error";
         case GPT2_ESTATE: return "call made in the wrong state";
     }

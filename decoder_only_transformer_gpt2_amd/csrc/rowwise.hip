@@ -133,6 +133,80 @@ __global__ __launch_bounds__(256) void argmax_reduce_kernel(const float* __restr
     if (lane == 0) out[row] = bi;
 }
 
+// Shifted next-token targets ([手写] §4.1: logits of position t are scored against the label of
+// position t+1); the ignore index and the last position of each sequence give -1.
+constexpr int kIgnoreIndex = -100;
+
+__global__ __launch_bounds__(256) void xent_targets_kernel(const int32_t* __restrict__ labels, int M, int T,
+                                                           int n_vocab, int32_t* __restrict__ tgt,
+                                                           int32_t* __restrict__ flags) {
+    const int m = blockIdx.x * blockDim.x + threadIdx.x;
+    if (m >= M) return;
+    int t = -1;
+    if (m % T != T - 1) {
+        const int y = labels[m + 1];
+        if (y >= 0 && y < n_vocab)
+            t = y;
+        else if (y != kIgnoreIndex)
+            flags[0] = 1;  // reported by gpt2_check; the position is left out
+    }
+    tgt[m] = t;
+}
+
+// One wavefront per row: log-sum-exp from the per-tile base-2 partials, minus the target logit.
+__global__ __launch_bounds__(256) void xent_rows_kernel(const float* __restrict__ pm, const float* __restrict__ ps,
+                                                        const int32_t* __restrict__ tgt,
+                                                        const float* __restrict__ tgt_logit, int M, int n_part,
+                                                        float* __restrict__ nll) {
+    const int wave = threadIdx.x / GPT2_WAVE, lane = threadIdx.x % GPT2_WAVE;
+    const int row = blockIdx.x * kRowsPerBlock + wave;
+    if (row >= M) return;
+    float mx = -INFINITY, sum = 0.f;
+    for (int j = lane; j < n_part; j += GPT2_WAVE) {
+        const float m2 = pm[(size_t)row * n_part + j], s2 = ps[(size_t)row * n_part + j];
+        const float mn = fmaxf(mx, m2), mz = mn == -INFINITY ? 0.f : mn;
+        sum = sum * exp2f(mx - mz) + s2 * exp2f(m2 - mz);
+        mx = mn;
+    }
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) {
+        const float m2 = __shfl_xor(mx, o, GPT2_WAVE), s2 = __shfl_xor(sum, o, GPT2_WAVE);
+        const float mn = fmaxf(mx, m2), mz = mn == -INFINITY ? 0.f : mn;
+        sum = sum * exp2f(mx - mz) + s2 * exp2f(m2 - mz);
+        mx = mn;
+    }
+    if (lane == 0) {
+        const float ln2 = 0.6931471805599453f;
+        nll[row] = tgt[row] >= 0 ? (mx + log2f(sum)) * ln2 - tgt_logit[row] : 0.f;
+    }
+}
+
+// One workgroup: the mean over the counted rows, summed in a fixed order (strided per thread,
+// then a tree), so the result does not depend on scheduling.
+__global__ __launch_bounds__(1024) void xent_mean_kernel(const float* __restrict__ nll, const int32_t* __restrict__ tgt,
+                                                         int M, float* __restrict__ loss) {
+    __shared__ float ssum[1024];
+    __shared__ int scnt[1024];
+    float acc = 0.f;
+    int cnt = 0;
+    for (int m = threadIdx.x; m < M; m += 1024)
+        if (tgt[m] >= 0) {
+            acc += nll[m];
+            ++cnt;
+        }
+    ssum[threadIdx.x] = acc;
+    scnt[threadIdx.x] = cnt;
+    __syncthreads();
+    for (int w = 512; w >= 1; w >>= 1) {
+        if ((int)threadIdx.x < w) {
+            ssum[threadIdx.x] += ssum[threadIdx.x + w];
+            scnt[threadIdx.x] += scnt[threadIdx.x + w];
+        }
+        __syncthreads();
+    }
+    if (threadIdx.x == 0) loss[0] = ssum[0] / (float)scnt[0];  // 0 / 0 = NaN when nothing counts
+}
+
 __global__ __launch_bounds__(256) void convert_kernel(const void* __restrict__ src, int src_bf16, void* __restrict__ dst,
                                                       int dst_bf16, long n_src, long n_dst) {
     for (long i = (long)blockIdx.x * blockDim.x + threadIdx.x; i < n_dst; i += (long)gridDim.x * blockDim.x) {
@@ -181,6 +255,24 @@ hipError_t layernorm(const float* x, const float* g, const float* b, void* y, in
 
 hipError_t argmax_reduce(const float* pv, const int32_t* pi, int M, int n_part, int32_t* out, hipStream_t s) {
     argmax_reduce_kernel<<<dim3((M + kRowsPerBlock - 1) / kRowsPerBlock), dim3(256), 0, s>>>(pv, pi, M, n_part, out);
+    return hipGetLastError();
+}
+
+hipError_t xent_targets(const int32_t* labels, int M, int T, int n_vocab, int32_t* tgt, int32_t* flags,
+                        hipStream_t s) {
+    xent_targets_kernel<<<dim3((M + 255) / 256), dim3(256), 0, s>>>(labels, M, T, n_vocab, tgt, flags);
+    return hipGetLastError();
+}
+
+hipError_t xent_rows(const float* pm, const float* ps, const int32_t* tgt, const float* tgt_logit, int M, int n_part,
+                     float* nll, hipStream_t s) {
+    xent_rows_kernel<<<dim3((M + kRowsPerBlock - 1) / kRowsPerBlock), dim3(256), 0, s>>>(pm, ps, tgt, tgt_logit, M,
+                                                                                        n_part, nll);
+    return hipGetLastError();
+}
+
+hipError_t xent_mean(const float* nll, const int32_t* tgt, int M, float* loss, hipStream_t s) {
+    xent_mean_kernel<<<dim3(1), dim3(1024), 0, s>>>(nll, tgt, M, loss);
     return hipGetLastError();
 }
 

@@ -20,7 +20,7 @@ OK, EINVAL, ESHAPE, EWORKSPACE, ETOKEN, EHIP, ESTATE = range(7)
 F32, BF16 = 0, 1
 GELU_TANH, GELU_ERF = 0, 1
 EPI_BIAS, EPI_BIAS_GELU, EPI_BIAS_RESIDUAL, EPI_LOGITS = range(4)
-KERNEL_KINDS = ("embed", "ln", "qkv", "attn", "attn_proj", "fc", "mlp_proj", "ln_f", "lm_head", "argmax")
+KERNEL_KINDS = ("embed", "ln", "qkv", "attn", "attn_proj", "fc", "mlp_proj", "ln_f", "lm_head", "argmax", "xent")
 
 # Every function the header declares, with its ctypes signature (restype, argtypes).
 _P = ctypes.c_void_p
@@ -38,6 +38,7 @@ SIGNATURES = {
     "gpt2_workspace_bytes": (_SZ, [_P, _I32, _I32]),
     "gpt2_load_weights": (_I32, [_P, ctypes.POINTER(_P), _I32, _I32, _P, _SZ, _P]),
     "gpt2_forward": (_I32, [_P, _P, _I32, _I32, _P, _P, _P, _SZ, _P]),
+    "gpt2_forward_loss": (_I32, [_P, _P, _P, _I32, _I32, _P, _P, _P, _SZ, _P]),
     "gpt2_forward_debug": (_I32, [_P, _P, _I32, _I32, _I32, _P, _P, _SZ, _P]),
     "gpt2_check": (_I32, [_P, _P, _I32, _I32, _P]),
     "gpt2_forward_launches": (_I32, [_P, _I32, ctypes.POINTER(_I32), _I32]),
@@ -222,6 +223,26 @@ class GPT2:
         _check(lib().gpt2_forward(self._h, _ptr(tokens), B, T, _ptr(logits), _ptr(argmax), _ptr(ws), ws.numel(),
                                   _stream(stream)), "gpt2_forward")
         return logits, argmax
+
+    def forward_loss(self, tokens: torch.Tensor, labels: torch.Tensor | None = None, nll: torch.Tensor | None = None,
+                     loss: torch.Tensor | None = None, ws: torch.Tensor | None = None, stream=None):
+        """tokens int32 [B, T] (and labels int32 [B, T] or None = tokens) on the device ->
+        (nll fp32 [B, T], loss fp32 [1]): the shifted next-token cross-entropy, logits never stored."""
+        _require_cuda(tokens, labels)
+        for t in (tokens, labels):
+            if t is not None and (t.dtype != torch.int32 or t.dim() != 2 or not t.is_contiguous()):
+                raise ValueError("tokens and labels must be contiguous int32 [B, T] device tensors")
+        B, T = tokens.shape
+        if labels is not None and tuple(labels.shape) != (B, T):
+            raise ValueError("labels must have the shape of tokens")
+        if nll is None:
+            nll = torch.empty((B, T), dtype=torch.float32, device=self.device)
+        if loss is None:
+            loss = torch.empty((1,), dtype=torch.float32, device=self.device)
+        ws = self.workspace(B, T) if ws is None else ws
+        _check(lib().gpt2_forward_loss(self._h, _ptr(tokens), _ptr(labels), B, T, _ptr(nll), _ptr(loss), _ptr(ws),
+                                       ws.numel(), _stream(stream)), "gpt2_forward_loss")
+        return nll, loss
 
     def launches(self, with_argmax: bool = True) -> list[str]:
         """Kinds of the kernel launches one forward enqueues, in order."""

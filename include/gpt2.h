@@ -118,6 +118,25 @@ gpt2_status gpt2_forward(const gpt2_model* m, const int32_t* tokens_dev, int32_t
                          float* logits_dev, int32_t* argmax_dev, void* ws_dev, size_t ws_bytes,
                          hipStream_t stream);
 
+/* The forward pass followed by the shifted next-token cross-entropy of [手写] §4.1, without
+ * writing the logits: the vocabulary projection reduces each row to its log-sum-exp and the
+ * logit of its target inside the GEMM epilogue, so the [B, T, n_vocab] fp32 logits are never
+ * stored.
+ *   labels_dev  int32 [B, T] or NULL (NULL: the tokens themselves, the language-model case).
+ *               Position t of row b is scored against labels[b, t+1]; the last position of each
+ *               row has no target. A label of -100 (the loss's default ignore index) leaves its
+ *               position out; any other label outside [0, n_vocab) is left out too and reported
+ *               by gpt2_check as GPT2_ETOKEN.
+ *   nll_dev     fp32 [B, T]: nll[b, t] = logsumexp(logits[b, t, :]) - logits[b, t, labels[b, t+1]],
+ *               0 where the position has no counted target (t = T-1 or ignored).
+ *   loss_dev    fp32 [1]: the mean of nll over the counted positions (NaN when none counts),
+ *               summed in a fixed order (run to run identical).
+ *   ws_dev      as for gpt2_forward (the same gpt2_workspace_bytes).
+ * Requires 2 <= T <= n_ctx (GPT2_ESHAPE otherwise), 1 <= B and loaded weights. */
+gpt2_status gpt2_forward_loss(const gpt2_model* m, const int32_t* tokens_dev, const int32_t* labels_dev,
+                              int32_t B, int32_t T, float* nll_dev, float* loss_dev, void* ws_dev,
+                              size_t ws_bytes, hipStream_t stream);
+
 /* Residual stream after the embedding and the first n_layers blocks (0 = embedding only,
  * n_layer = all blocks, before ln_f), as fp32 [B, T, d] into resid_dev. Same workspace and
  * argument rules as gpt2_forward. Used for per-block alignment checks ([手写] §4.2). */
@@ -128,7 +147,7 @@ gpt2_status gpt2_forward_debug(const gpt2_model* m, const int32_t* tokens_dev, i
 /* Kinds of the kernel launches a forward enqueues, in order (gpt2_forward_launches). */
 typedef enum {
     GPT2_K_EMBED = 0, GPT2_K_LN = 1, GPT2_K_QKV = 2, GPT2_K_ATTN = 3, GPT2_K_ATTN_PROJ = 4, GPT2_K_FC = 5,
-    GPT2_K_MLP_PROJ = 6, GPT2_K_LN_F = 7, GPT2_K_LM_HEAD = 8, GPT2_K_ARGMAX = 9
+    GPT2_K_MLP_PROJ = 6, GPT2_K_LN_F = 7, GPT2_K_LM_HEAD = 8, GPT2_K_ARGMAX = 9, GPT2_K_XENT = 10
 } gpt2_kernel_kind;
 
 /* Number of kernel launches one gpt2_forward enqueues (with_argmax: argmax_dev != NULL); when
@@ -145,7 +164,8 @@ gpt2_status gpt2_forward_timed(const gpt2_model* m, const int32_t* tokens_dev, i
                                int32_t n_slots);
 
 /* Synchronise stream, then report GPT2_ETOKEN if the last forward that used ws_dev saw a token
- * id outside [0, n_vocab), else GPT2_OK. B and T must be those of that forward. */
+ * id (or, for gpt2_forward_loss, a label other than -100) outside [0, n_vocab), else GPT2_OK.
+ * B and T must be those of that forward. */
 gpt2_status gpt2_check(const gpt2_model* m, const void* ws_dev, int32_t B, int32_t T, hipStream_t stream);
 
 /* Causal multi-head attention on its own ([复现] §2.1-§2.2; [解析] §2.1):

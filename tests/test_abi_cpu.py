@@ -31,7 +31,8 @@ def declared_functions():
 def test_header_declares_expected_entry_points():
     names = declared_functions()
     for required in ("gpt2_config", "gpt2_load_weights", "gpt2_forward", "gpt2_attention", "gpt2_forward_debug",
-                     "gpt2_check", "gpt2_strerror", "gpt2_destroy", "gpt2_weight_bytes", "gpt2_workspace_bytes"):
+                     "gpt2_check", "gpt2_strerror", "gpt2_destroy", "gpt2_weight_bytes", "gpt2_workspace_bytes",
+                     "gpt2_forward_loss"):
         assert required in names
 
 
@@ -135,6 +136,9 @@ def test_host_validation_before_any_launch(g):
     # weights not loaded -> ESTATE; null pointers -> EINVAL
     assert L.gpt2_forward(h, fake, 1, 4, fake, None, ctypes.c_void_p(0x100000), 1 << 30, None) == g.ESTATE
     assert L.gpt2_forward(h, None, 1, 4, fake, None, fake, 1 << 30, None) == g.EINVAL
+    assert L.gpt2_forward_loss(h, fake, None, 1, 4, fake, fake, ctypes.c_void_p(0x100000), 1 << 30, None) == g.ESTATE
+    assert L.gpt2_forward_loss(h, None, None, 1, 4, fake, fake, fake, 1 << 30, None) == g.EINVAL
+    assert L.gpt2_forward_loss(h, fake, None, 1, 4, None, fake, fake, 1 << 30, None) == g.EINVAL
     assert L.gpt2_load_weights(h, None, 0, 0, fake, 0, None) == g.EINVAL
     srcs = (ctypes.c_void_p * 3)(fake, fake, fake)
     assert L.gpt2_load_weights(h, srcs, 3, 0, fake, 1 << 40, None) == g.EINVAL   # wrong count

@@ -365,6 +365,89 @@ def test_bf16_tiny_shapes(g, small_bf16, B, T):
 
 
 # ---------------------------------------------------------------------------------- error paths
+# ------------------------------------------------------------ fused lm_head + cross-entropy
+def host_nll(logits, labels):
+    """Shifted next-token nll from given logits, in float64 on the host (same definition as the
+    oracle's, applied to the GPU's own logits)."""
+    nll, counted = O.shifted_nll(logits, labels)
+    return nll, counted
+
+
+@pytest.mark.parametrize("B,T", [(2, 4), (2, 33), (1, 129)])
+def test_forward_loss_f32(g, small_f32, B, T):
+    m, w = small_f32
+    tok = synth.make_tokens(B, T)
+    nll, loss = m.forward_loss(dev_tokens(tok))
+    assert m.check(B, T) == g.OK
+    nll = nll.cpu().numpy()
+    ref, counted = O.shifted_nll(O.forward(w, tok, 12, 12), tok)
+    assert np.all(nll[:, T - 1] == 0)
+    err = np.abs(nll[:, :T - 1] - ref)
+    log(f"  f32 B={B} T={T}: max|nll err|={err.max():.3e} loss={loss.item():.6f} ref={ref.mean():.6f}")
+    assert np.all(err <= 1e-4 * (1 + np.abs(ref)))
+    assert abs(loss.item() - ref.mean()) <= 1e-4 * (1 + abs(ref.mean()))
+
+
+def test_forward_loss_bf16_config1(g, small_bf16):
+    """GPT-2 small, B=4, T=1024: the fused loss against (a) the same loss computed in float64
+    from this library's own fp32 logits, every position, and (b) the oracle on two rows."""
+    m, w = small_bf16
+    tok = synth.make_tokens(4, 1024)
+    nll, loss = m.forward_loss(dev_tokens(tok))
+    nll = nll.cpu().numpy()
+    loss = loss.item()
+    logits, _ = m.forward(dev_tokens(tok), argmax=False)
+    own, counted = host_nll(logits.cpu().numpy(), tok)
+    del logits
+    d_own = np.abs(nll[:, :-1] - own)
+    # (a) the same fp32 logits reduced in fp32 (exp2 / log2 on the hardware, 50257-term sums):
+    # a few 1e-5 absolute at most
+    log(f"  fused vs own logits: max|d|={d_own.max():.3e}, loss {loss:.6f} vs {own.mean():.6f}")
+    assert d_own.max() <= 5e-4
+    assert abs(loss - own.mean()) <= 5e-4
+    # (b) against the oracle: |d nll| <= |d lse| + |d logit| <= 2 max|logit error| <= 2 * 5e-2
+    for b in (0, 3):
+        ref, _ = O.shifted_nll(O.forward(w, tok[b:b + 1], 12, 12), tok[b:b + 1])
+        e = np.abs(nll[b, :-1] - ref[0]).max()
+        log(f"  row {b}: max|nll - oracle|={e:.3e}")
+        assert e <= 0.1
+    # the same inputs give the same bits (fixed-order reductions)
+    nll2, loss2 = m.forward_loss(dev_tokens(tok))
+    assert np.array_equal(nll2.cpu().numpy(), nll) and loss2.item() == loss
+
+
+def test_forward_loss_labels_ignore_and_invalid(g, small_bf16):
+    m, _ = small_bf16
+    B, T = 2, 77
+    tok = synth.make_tokens(B, T)
+    lab = synth.make_tokens(B, T, seed=5)
+    lab[0, 5] = lab[1, 40] = lab[1, 76] = -100
+    nll, loss = m.forward_loss(dev_tokens(tok), dev_tokens(lab))
+    assert m.check(B, T) == g.OK
+    logits, _ = m.forward(dev_tokens(tok), argmax=False)
+    own, counted = host_nll(logits.cpu().numpy(), lab)
+    nll = nll.cpu().numpy()
+    assert not counted[0, 4] and not counted[1, 39] and not counted[1, 75]
+    assert nll[0, 4] == 0 and nll[1, 39] == 0 and nll[1, 75] == 0 and np.all(nll[:, T - 1] == 0)
+    assert np.abs(nll[:, :-1] - own).max() <= 5e-4
+    assert abs(loss.item() - own[counted].mean()) <= 5e-4
+    # a label outside [0, V) other than -100: reported, and its position is left out
+    lab2 = lab.copy()
+    lab2[1, 10] = 50257
+    nll2, loss2 = m.forward_loss(dev_tokens(tok), dev_tokens(lab2))
+    assert m.check(B, T) == g.ETOKEN
+    assert nll2.cpu().numpy()[1, 9] == 0
+    counted2 = counted.copy()
+    counted2[1, 9] = False
+    assert abs(loss2.item() - own[counted2].mean()) <= 5e-4
+    # every label ignored: 0 / 0
+    _, loss3 = m.forward_loss(dev_tokens(tok), dev_tokens(np.full((B, T), -100)))
+    assert math.isnan(loss3.item())
+    # one position per row has no target: T = 1 is rejected
+    with pytest.raises(g.GPT2Error):
+        m.forward_loss(dev_tokens(tok[:, :1]))
+
+
 def test_errors_reported(g, small_bf16):
     m, _ = small_bf16
     tok = dev_tokens(synth.make_tokens(1, 8))
