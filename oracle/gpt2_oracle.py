@@ -225,6 +225,18 @@ def shifted_cross_entropy(logits: np.ndarray, labels: np.ndarray) -> float:
     return float(nll.sum() / n) if n else float("nan")
 
 
+def greedy_generate(p: dict, prompt: np.ndarray, n_new: int, n_head: int, n_layer: int, eps: float = 1e-5,
+                    gelu=gelu_tanh) -> np.ndarray:
+    """Greedy decoding as in [手写] §6.3: run the forward on the whole sequence so far, take the
+    first-index argmax of the last position's logits as the next token, append, repeat.
+    prompt int [B, T] -> int [B, T + n_new]. (No cache: each step recomputes every position.)"""
+    seq = np.asarray(prompt).copy()
+    for _ in range(n_new):
+        nxt = argmax_first(forward(p, seq, n_head, n_layer, eps, gelu)[:, -1])
+        seq = np.concatenate([seq, nxt[:, None].astype(seq.dtype)], axis=1)
+    return seq
+
+
 def param_count(n_vocab: int, n_ctx: int, d: int, n_layer: int, d_mlp: int) -> int:
     """Number of parameters with lm_head tied to wte (counted once).
 

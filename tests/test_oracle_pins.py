@@ -373,6 +373,50 @@ def test_shifted_nll_per_position():
             assert math.isclose(nll[b, t], math.log(np.exp(row).sum()) - row[lab[b, t + 1]], rel_tol=1e-12)
 
 
+# ------------------------------------------------------------------- greedy generation pins
+def copy_model(V=40, d=64, n_ctx=16):
+    """One block whose Linear weights and biases are all zero, so every block adds nothing and
+    logits = LN(wte[tok]) wte^T (wpe = 0). With unit-norm random rows of wte in 64 dimensions,
+    each token's own row is by far its best match: greedy decoding repeats the last token."""
+    r = rng(11)
+    wte = r.standard_normal((V, d))
+    wte /= np.linalg.norm(wte, axis=1, keepdims=True)
+    p = {"wte": wte, "wpe": np.zeros((n_ctx, d)), "ln_f.w": np.ones(d), "ln_f.b": np.zeros(d)}
+    z = lambda *sh: np.zeros(sh)
+    p.update({"h.0.ln_1.w": np.ones(d), "h.0.ln_1.b": z(d), "h.0.attn.c_attn.w": z(3 * d, d),
+              "h.0.attn.c_attn.b": z(3 * d), "h.0.attn.c_proj.w": z(d, d), "h.0.attn.c_proj.b": z(d),
+              "h.0.ln_2.w": np.ones(d), "h.0.ln_2.b": z(d), "h.0.mlp.c_fc.w": z(4 * d, d),
+              "h.0.mlp.c_fc.b": z(4 * d), "h.0.mlp.c_proj.w": z(d, 4 * d), "h.0.mlp.c_proj.b": z(d)})
+    return p
+
+
+def check_generate(gen):
+    """gen(p, prompt, n_new, n_head, n_layer) -> [B, T + n_new]."""
+    fails = []
+    p = copy_model()
+    prompt = np.array([[3, 17, 5], [8, 8, 30]])
+    out = gen(p, prompt, 4, 1, 1)
+    if not np.array_equal(out, np.array([[3, 17, 5, 5, 5, 5, 5], [8, 8, 30, 30, 30, 30, 30]])):
+        fails.append("copy model repeats the last token")
+    # invariants on a random model: no new tokens = the prompt; the first new token is the argmax
+    # of the forward's last row; n then m more tokens = n + m tokens
+    s = synth.ModelShape(n_vocab=50, n_ctx=16, d_model=64, n_head=1, n_layer=2, d_mlp=256)
+    w = synth.make_weights(s, bf16=False)
+    pr = synth.make_tokens(2, 3, n_vocab=50)
+    if not np.array_equal(gen(w, pr, 0, 1, 2), pr):
+        fails.append("n_new = 0")
+    g5 = gen(w, pr, 5, 1, 2)
+    if not np.array_equal(g5[:, 3], O.argmax_first(O.forward(w, pr, 1, 2)[:, -1])):
+        fails.append("first token = argmax of the last row")
+    if not np.array_equal(gen(w, gen(w, pr, 2, 1, 2), 3, 1, 2), g5):
+        fails.append("2 then 3 = 5")
+    return fails
+
+
+def test_greedy_generate_pins():
+    assert check_generate(O.greedy_generate) == []
+
+
 # --------------------------------------------------------------------- planted-mistake audit
 def _unbiased_ln(x, g, b, eps=1e-5):
     x = np.asarray(x, float)
@@ -494,6 +538,23 @@ def _time_axis_xent(z, lab):
     return float(np.where(ok, picked, 0).sum() / ok.sum()) if ok.any() else float("nan")
 
 
+def _second_last_generate(p, prompt, n_new, n_head, n_layer):
+    seq = np.asarray(prompt).copy()
+    for _ in range(n_new):
+        lg = O.forward(p, seq, n_head, n_layer)
+        nxt = O.argmax_first(lg[:, -2] if seq.shape[1] > 1 else lg[:, -1])
+        seq = np.concatenate([seq, nxt[:, None]], axis=1)
+    return seq
+
+
+def _argmin_generate(p, prompt, n_new, n_head, n_layer):
+    seq = np.asarray(prompt).copy()
+    for _ in range(n_new):
+        nxt = np.argmin(O.forward(p, seq, n_head, n_layer)[:, -1], axis=-1)
+        seq = np.concatenate([seq, nxt[:, None]], axis=1)
+    return seq
+
+
 @pytest.mark.parametrize("check,mutant", [
     (check_layer_norm, _unbiased_ln), (check_layer_norm, _eps_outside_ln), (check_layer_norm, _no_beta_ln),
     (check_gelu, _cubic_sign_gelu), (check_gelu, _no_half_gelu), (check_gelu, O.gelu_erf),
@@ -504,6 +565,7 @@ def _time_axis_xent(z, lab):
     (check_cross_entropy, _unshifted_xent), (check_cross_entropy, _reverse_shift_xent),
     (check_cross_entropy, _sum_xent), (check_cross_entropy, _no_max_xent),
     (check_cross_entropy, _ignored_counted_xent), (check_cross_entropy, _time_axis_xent),
+    (check_generate, _second_last_generate), (check_generate, _argmin_generate),
 ])
 def test_pins_catch_planted_mistakes(check, mutant):
     try:
