@@ -1,12 +1,13 @@
 """Forward-pass throughput of the HIP GPT-2 library on one MI355X.
 
-python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload small|medium|xl] [--no-cpu-baseline] [--no-loss]
+python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload small|medium|xl] [--no-cpu-baseline] [--no-loss] [--no-decode]
 
 One step = one gpt2_forward over a batch of synthetic token ids already resident in HBM:
 embedding, every block, ln_f, the tied lm_head (fp32 logits) and the fused argmax. Weights are the
 seeded synthetic init (no checkpoint exists). Prints one JSON line. After the timed region it also
 times gpt2_forward_loss (the same forward with the shifted next-token cross-entropy fused into the
-vocabulary projection, logits not stored) and reports it under "forward_loss".
+vocabulary projection, logits not stored) under "forward_loss", and cached greedy decode steps
+(gpt2_decode_step after a gpt2_prefill of half the context) under "decode".
 
 The roofline object is for the lm_head GEMM, the largest single launch: its duration is taken
 from HIP events the library records on its own stream around that launch in every timed step.
@@ -89,6 +90,7 @@ def main():
     ap.add_argument("--workload", choices=sorted(WORKLOADS), default="small")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-loss", action="store_true", help="skip the fused forward+loss measurement")
+    ap.add_argument("--no-decode", action="store_true", help="skip the cached decode measurement")
     ap.add_argument("--breakdown", action="store_true", help="also time every launch of one extra forward")
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="after the timed region, run a plain device-to-device copy of this many bytes three "
@@ -178,6 +180,33 @@ def main():
         out["forward_loss"] = {"ms_per_step": lms, "tokens_per_s": M / (lms * 1e-3), "steps": n_loss,
                                "loss": float(loss.item()),
                                "what": "forward + shifted next-token cross-entropy, logits not stored"}
+
+    if not args.no_decode:
+        # Cached greedy decoding at the same batch: prefill half the context, then timed steps.
+        # Each step reads every weight once plus the cache up to its position, so HBM bounds it.
+        T0, n_dec = T // 2, 64
+        cache = m.kv_cache(B)
+        nxt = torch.empty((B,), dtype=torch.int32, device="cuda")
+        cur = torch.empty((B,), dtype=torch.int32, device="cuda")
+        prompt = tokens[:, :T0].contiguous()
+        m.prefill(prompt, cache, logits=False, nxt=cur)
+        wsd = m.workspace(B, 1)
+        for i in range(4):  # warm-up steps (their cache rows are rewritten below)
+            m.decode_step(cur, T0 + i, cache, logits=False, nxt=nxt, ws=wsd)
+        torch.cuda.synchronize()
+        t3 = time.perf_counter()
+        for i in range(n_dec):
+            m.decode_step(cur, T0 + i, cache, logits=False, nxt=nxt, ws=wsd)
+            cur, nxt = nxt, cur
+        torch.cuda.synchronize()
+        dms = (time.perf_counter() - t3) * 1e3 / n_dec
+        wbytes = m.weight_bytes()
+        kv_row = 2 * shape.n_layer * B * shape.d_model * 2  # bytes of one cached position (K and V, bf16)
+        step_bytes = wbytes + kv_row * (T0 + n_dec / 2)
+        out["decode"] = {"ms_per_step": dms, "tokens_per_s": B / (dms * 1e-3), "batch": B, "prefill_len": T0,
+                         "steps": n_dec, "hbm_bytes_per_step": step_bytes,
+                         "hbm_frac": step_bytes / (dms * 1e-3) / 1e9 / PEAK_HBM_GBS,
+                         "what": "greedy cached decode step (next-token argmax), weights + cache read per step"}
 
     if args.copy_bytes > 0:
         src = torch.empty(args.copy_bytes, dtype=torch.uint8, device="cuda")

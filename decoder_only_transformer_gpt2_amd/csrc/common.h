@@ -113,7 +113,8 @@ struct HeadOut {
 int gemm_bf16_tile_n(int M, int N, int K);
 constexpr int kGemmF32BN = 64;
 
-hipError_t embed(const int32_t* tok, const void* wte, const void* wpe, float* x, int M, int T, int d,
+// x[m] = wte[tok[m]] + wpe[pos0 + m % T] (rows m of [B, T]).
+hipError_t embed(const int32_t* tok, const void* wte, const void* wpe, float* x, int M, int T, int pos0, int d,
                  int n_vocab, bool bf16, int32_t* flags, hipStream_t s);
 int embed_flag_count(int M);
 
@@ -125,6 +126,12 @@ hipError_t gemm_bf16(const uint16_t* A, const uint16_t* W, const float* bias, vo
                      long ldc, int epi, int gelu_erf, int a_rows, int w_rows, const HeadOut& ho, hipStream_t s);
 hipError_t gemm_f32(const float* A, const float* W, const float* bias, void* C, int M, int N, int K, long ldc,
                     int epi, int gelu_erf, const HeadOut& ho, hipStream_t s);
+// The same for M <= kSkinnyM rows (gemm_bf16 dispatches to it): 16 output columns per workgroup,
+// so the head partial count per row is ceil(N / 16). Needs a_rows >= 16 and w_rows >= N rounded
+// up to 16 readable rows.
+constexpr int kSkinnyM = 16;
+hipError_t gemm_bf16_skinny(const uint16_t* A, const uint16_t* W, const float* bias, void* C, int M, int N, int K,
+                            int ldc, int epi, int gelu_erf, int a_rows, int w_rows, const HeadOut& ho, hipStream_t s);
 
 hipError_t argmax_reduce(const float* pv, const int32_t* pi, int M, int n_part, int32_t* out, hipStream_t s);
 
@@ -144,6 +151,17 @@ hipError_t attention_bf16(const uint16_t* q, const int64_t* qs, const uint16_t* 
                           int T, hipStream_t s);
 hipError_t attention_f32(const float* q, const int64_t* qs, const float* k, const int64_t* ks, const float* v,
                          const int64_t* vs, float* o, const int64_t* os, int B, int H, int T, hipStream_t s);
+
+// Key/value cache of one layer: K and V each [B][H][n_ctx][64] in the compute dtype.
+// Copies k, v of the rows of qkv [B, T, 3, H, 64] to positions pos0 .. pos0 + T - 1.
+hipError_t kv_append(const void* qkv, int B, int T, int H, int pos0, void* kc, void* vc, int n_ctx, bool bf16,
+                     hipStream_t s);
+// One query per (b, h) (q of row b of qkv [B, 1, 3, H, 64]) against cached keys 0 .. n_keys - 1:
+// o[b, h*64 .. h*64+63] = sum_j softmax_j(q . k_j / 8) v_j, fp32 softmax, output in the dtype.
+hipError_t decode_attention(const void* qkv, const void* kc, const void* vc, void* o, int B, int H, int n_ctx,
+                            int n_keys, bool bf16, hipStream_t s);
+// dst[b] = src[b * T + T - 1] for rows of n fp32 values.
+hipError_t gather_last_rows(const float* src, float* dst, int B, int T, int n, hipStream_t s);
 
 // dst[i] = i < n_src ? convert(src[i]) : 0 for i < n_dst (element types fp32 or bf16).
 hipError_t convert(const void* src, bool src_bf16, void* dst, bool dst_bf16, long n_src, long n_dst,

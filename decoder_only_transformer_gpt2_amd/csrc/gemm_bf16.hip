@@ -300,6 +300,7 @@ void gemm_bf16_kernel(
             // the logits are written once and not read back by this pass, so they should not
             // evict the weights and activations from the caches.
             float* Cs = static_cast<float*>(Cv) + (size_t)rs * ldc + col0;
+            if (Cv)  // no logits buffer: argmax partials only
 #pragma unroll
             for (int it = 0; it < (16 * WN + GPT2_WAVE - 1) / GPT2_WAVE; ++it) {
                 const int idx = it * GPT2_WAVE + lane;
@@ -503,11 +504,13 @@ hipError_t launch_cfg(const uint16_t* A, const uint16_t* W, const float* bias, v
 
 }  // namespace
 
-int gemm_bf16_tile_n(int M, int N, int K) { return kCfgs[choose_cfg(M, N, K)].bn; }
+int gemm_bf16_tile_n(int M, int N, int K) { return M <= kSkinnyM ? 16 : kCfgs[choose_cfg(M, N, K)].bn; }
 
 hipError_t gemm_bf16(const uint16_t* A, const uint16_t* W, const float* bias, void* C, int M, int N, int K, long ldc,
                      int epi, int gelu_erf, int a_rows, int w_rows, const HeadOut& ho, hipStream_t s) {
     if (ldc < N || ldc > (1 << 26)) return hipErrorInvalidValue;  // in-strip offsets are 32-bit
+    if (M <= kSkinnyM)  // a few rows: a stream over W
+        return gemm_bf16_skinny(A, W, bias, C, M, N, K, (int)ldc, epi, gelu_erf, a_rows, w_rows, ho, s);
     switch (choose_cfg(M, N, K)) {
 #define GPT2_CFG(i, bm, bn, bk, st, wgm, wgn)                                                                    \
     case i:                                                                                                      \

@@ -89,7 +89,7 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(const float* __restrict__
             for (int j = 0; j < 4; ++j) {
                 const int n = n0 + tx * 4 + j;
                 if (n < N) {
-                    if (m < M) C[(size_t)m * ldc + n] = acc[i][j];
+                    if (m < M && C) C[(size_t)m * ldc + n] = acc[i][j];
                     argmax_merge(bv, bi, acc[i][j], n);
                 }
             }

@@ -1,6 +1,7 @@
 // Host side of the C ABI declared in include/gpt2.h: configuration checks, packed weight layout,
 // workspace carving and the launch sequence of the forward pass. Every device buffer belongs to
 // the caller; nothing here allocates device memory.
+#include <algorithm>
 #include <cstring>
 #include <new>
 #include <vector>
@@ -29,9 +30,17 @@ enum LayerTensor {
 };
 
 struct WorkspaceLayout {
-    size_t x, a, qkv, o, hid, amax_v, amax_i, tgt, tgt_logit, flags, total;
+    size_t x, a, qkv, o, hid, amax_v, amax_i, tgt, tgt_logit, xl, al, flags, total;
     int64_t Mp;
     int n_part;
+};
+
+// Key/value cache arguments of the trunk: append this call's keys and values at positions pos0 ..
+// pos0 + T - 1; with from_cache (one new position per sequence) the attention reads the cache.
+struct KVArgs {
+    char* cache = nullptr;
+    int pos0 = 0;
+    bool from_cache = false;
 };
 
 }  // namespace
@@ -83,8 +92,14 @@ WorkspaceLayout ws_layout(const gpt2_model* m, int B, int T) {
     const int64_t M = (int64_t)B * T;
     w.Mp = round_up(M, kRowPad);
     const size_t as = act_size(m);
-    const int bn = is_bf16(m) ? gpt2k::gemm_bf16_tile_n((int)M, c.n_vocab, c.d_model) : gpt2k::kGemmF32BN;
-    w.n_part = (c.n_vocab + bn - 1) / bn;
+    auto n_part = [&](int rows) {
+        const int bn = is_bf16(m) ? gpt2k::gemm_bf16_tile_n(rows, c.n_vocab, c.d_model) : gpt2k::kGemmF32BN;
+        return (c.n_vocab + bn - 1) / bn;
+    };
+    w.n_part = n_part((int)M);
+    // the head partials serve the M-row projection and the B-row next-token projection of cached
+    // decoding, whose tile width can differ
+    const size_t n_head_part = std::max((size_t)M * w.n_part, (size_t)B * n_part(B));
     size_t off = 0;
     auto take = [&](size_t bytes) { size_t o = off; off = align_up(off + bytes, kAlign); return o; };
     w.x = take((size_t)w.Mp * c.d_model * 4);
@@ -92,10 +107,14 @@ WorkspaceLayout ws_layout(const gpt2_model* m, int B, int T) {
     w.qkv = take((size_t)w.Mp * 3 * c.d_model * as);
     w.o = take((size_t)w.Mp * c.d_model * as);
     w.hid = take((size_t)w.Mp * c.d_mlp * as);
-    w.amax_v = take((size_t)M * w.n_part * 4);  // head partials: argmax value / base-2 maximum
-    w.amax_i = take((size_t)M * w.n_part * 4);  // argmax index / sum below the maximum
+    w.amax_v = take(n_head_part * 4);  // head partials: argmax value / base-2 maximum
+    w.amax_i = take(n_head_part * 4);  // argmax index / sum below the maximum
     w.tgt = take((size_t)M * 4);                // cross-entropy target column per row
     w.tgt_logit = take((size_t)M * 4);          // and its logit
+    // cached decoding: the B rows whose logits are wanted (fp32 residual, ln_f output)
+    const int64_t Bp = round_up(B, kRowPad);
+    w.xl = take((size_t)B * c.d_model * 4);
+    w.al = take((size_t)Bp * c.d_model * as);
     w.flags = take((size_t)gpt2k::embed_flag_count((int)M) * 4);
     w.total = off;
     return w;
@@ -164,8 +183,10 @@ struct Sequencer {
     } while (0)
 
 // Embedding and the first n_layers blocks; leaves the residual stream in the workspace's x.
+size_t kv_layer_elems(const gpt2_model* m, int B) { return (size_t)B * m->cfg.d_model * m->cfg.n_ctx; }
+
 gpt2_status enqueue_trunk(const gpt2_model* m, const int32_t* tokens, int B, int T, int n_layers, char* ws,
-                          const WorkspaceLayout& w, Sequencer& q) {
+                          const WorkspaceLayout& w, Sequencer& q, const KVArgs& kv = KVArgs()) {
     const gpt2_config_t& c = m->cfg;
     const hipStream_t s = q.s;
     const int M = B * T, d = c.d_model, f = c.d_mlp, H = c.n_head;
@@ -175,7 +196,7 @@ gpt2_status enqueue_trunk(const gpt2_model* m, const int32_t* tokens, int B, int
     void* qkv = ws + w.qkv;
     void* o = ws + w.o;
     void* hid = ws + w.hid;
-    GPT2_RUN(GPT2_K_EMBED, gpt2k::embed(tokens, wptr(m, 0), wptr(m, 1), x, M, T, d, c.n_vocab, bf,
+    GPT2_RUN(GPT2_K_EMBED, gpt2k::embed(tokens, wptr(m, 0), wptr(m, 1), x, M, T, kv.pos0, d, c.n_vocab, bf,
                                         reinterpret_cast<int32_t*>(ws + w.flags), s));
     // q, k, v views of qkv [B, T, 3, H, 64]: strides (batch, head, token) in elements
     const int64_t qs[3] = {(int64_t)T * 3 * d, 64, 3 * d};
@@ -187,7 +208,16 @@ gpt2_status enqueue_trunk(const gpt2_model* m, const int32_t* tokens, int B, int
         GPT2_RUN(GPT2_K_LN, gpt2k::layernorm(x, vecp(LN1_W), vecp(LN1_B), a, M, d, c.ln_eps, bf, s));
         GPT2_RUN(GPT2_K_QKV, linear(m, a, L(ATTN_W), L(ATTN_B), qkv, M, 3 * d, d, 3 * d, gpt2k::EPI_BIAS, {}, s));
         const char* qb = static_cast<const char*>(qkv);
-        if (bf)
+        char* kc = nullptr;
+        char* vc = nullptr;
+        if (kv.cache) {
+            kc = kv.cache + (size_t)2 * l * kv_layer_elems(m, B) * as;
+            vc = kc + kv_layer_elems(m, B) * as;
+            GPT2_RUN(GPT2_K_KV, gpt2k::kv_append(qkv, B, T, H, kv.pos0, kc, vc, c.n_ctx, bf, s));
+        }
+        if (kv.from_cache)
+            GPT2_RUN(GPT2_K_ATTN, gpt2k::decode_attention(qkv, kc, vc, o, B, H, c.n_ctx, kv.pos0 + 1, bf, s));
+        else if (bf)
             GPT2_RUN(GPT2_K_ATTN, gpt2k::attention_bf16(reinterpret_cast<const uint16_t*>(qb), qs,
                                                         reinterpret_cast<const uint16_t*>(qb + d * as), qs,
                                                         reinterpret_cast<const uint16_t*>(qb + 2 * d * as), qs,
@@ -257,6 +287,40 @@ gpt2_status enqueue_forward_loss(const gpt2_model* m, const int32_t* tokens, con
              linear(m, ws + w.a, 0, -1, nullptr, M, c.n_vocab, c.d_model, c.n_vocab, gpt2k::EPI_LSE, ho, s));
     GPT2_RUN(GPT2_K_XENT, gpt2k::xent_rows(ho.pv, ho.ps, tgt, ho.tgt_logit, M, w.n_part, nll, s));
     GPT2_RUN(GPT2_K_XENT, gpt2k::xent_mean(nll, tgt, M, loss, s));
+    return GPT2_OK;
+}
+
+// ln_f and the tied lm_head on B rows of the residual (fp32 [B, d] at xr): the next-token logits
+// (not stored when logits is NULL) and their argmax.
+gpt2_status enqueue_next_token(const gpt2_model* m, const float* xr, int B, float* logits, int32_t* next, char* ws,
+                               const WorkspaceLayout& w, Sequencer& q) {
+    const gpt2_config_t& c = m->cfg;
+    const hipStream_t s = q.s;
+    const int ln_f = 2 + c.n_layer * PER_LAYER;
+    GPT2_RUN(GPT2_K_LN_F, gpt2k::layernorm(xr, static_cast<const float*>(wptr(m, ln_f)),
+                                           static_cast<const float*>(wptr(m, ln_f + 1)), ws + w.al, B, c.d_model,
+                                           c.ln_eps, is_bf16(m), s));
+    gpt2k::HeadOut ho;
+    if (next) {
+        ho.pv = reinterpret_cast<float*>(ws + w.amax_v);
+        ho.pi = reinterpret_cast<int32_t*>(ws + w.amax_i);
+    }
+    GPT2_RUN(GPT2_K_LM_HEAD, linear(m, ws + w.al, 0, -1, logits, B, c.n_vocab, c.d_model, c.n_vocab,
+                                    gpt2k::EPI_LOGITS, ho, s));
+    if (next) {
+        // the partial count of a B-row projection (the tile width depends on the shape)
+        const int bn = is_bf16(m) ? gpt2k::gemm_bf16_tile_n(B, c.n_vocab, c.d_model) : gpt2k::kGemmF32BN;
+        GPT2_RUN(GPT2_K_ARGMAX, gpt2k::argmax_reduce(ho.pv, ho.pi, B, (c.n_vocab + bn - 1) / bn, next, s));
+    }
+    return GPT2_OK;
+}
+
+size_t kv_cache_bytes(const gpt2_model* m, int B) { return 2 * (size_t)m->cfg.n_layer * kv_layer_elems(m, B) * act_size(m); }
+
+gpt2_status check_cache(const gpt2_model* m, int B, const void* cache, size_t cache_bytes) {
+    if (!cache) return GPT2_EINVAL;
+    if (reinterpret_cast<uintptr_t>(cache) % kAlign) return GPT2_EINVAL;
+    if (cache_bytes < kv_cache_bytes(m, B)) return GPT2_EWORKSPACE;
     return GPT2_OK;
 }
 
@@ -343,6 +407,49 @@ gpt2_status gpt2_forward_loss(const gpt2_model* m, const int32_t* tokens, const 
     if (T < 2) return GPT2_ESHAPE;
     Sequencer q{s};
     return enqueue_forward_loss(m, tokens, labels, B, T, nll, loss, static_cast<char*>(ws_dev), q);
+}
+
+size_t gpt2_kv_cache_bytes(const gpt2_model* m, int32_t B) {
+    if (!m || B < 1 || (int64_t)B * m->cfg.n_ctx > (int64_t)1 << 30) return 0;
+    return kv_cache_bytes(m, B);
+}
+
+gpt2_status gpt2_prefill(const gpt2_model* m, const int32_t* tokens, int32_t B, int32_t T, void* cache,
+                         size_t cache_bytes, float* logits, int32_t* next, void* ws_dev, size_t ws_bytes, hipStream_t s) {
+    gpt2_status st = check_run_args(m, tokens, B, T, cache, ws_dev, ws_bytes);
+    if (st != GPT2_OK) return st;
+    if ((st = check_cache(m, B, cache, cache_bytes)) != GPT2_OK) return st;
+    char* ws = static_cast<char*>(ws_dev);
+    const WorkspaceLayout w = ws_layout(m, B, T);
+    Sequencer q{s};
+    KVArgs kv;
+    kv.cache = static_cast<char*>(cache);
+    st = enqueue_trunk(m, tokens, B, T, m->cfg.n_layer, ws, w, q, kv);
+    if (st != GPT2_OK) return st;
+    if (!logits && !next) return GPT2_OK;
+    float* xl = reinterpret_cast<float*>(ws + w.xl);
+    GPT2_RUN(GPT2_K_LN_F, gpt2k::gather_last_rows(reinterpret_cast<const float*>(ws + w.x), xl, B, T, m->cfg.d_model, s));
+    return enqueue_next_token(m, xl, B, logits, next, ws, w, q);
+}
+
+gpt2_status gpt2_decode_step(const gpt2_model* m, const int32_t* tokens, int32_t B, int32_t pos, void* cache,
+                             size_t cache_bytes, float* logits, int32_t* next, void* ws_dev, size_t ws_bytes,
+                             hipStream_t s) {
+    gpt2_status st = check_run_args(m, tokens, B, 1, cache, ws_dev, ws_bytes);
+    if (st != GPT2_OK) return st;
+    if ((st = check_cache(m, B, cache, cache_bytes)) != GPT2_OK) return st;
+    if (pos < 0 || pos >= m->cfg.n_ctx) return GPT2_ESHAPE;
+    char* ws = static_cast<char*>(ws_dev);
+    const WorkspaceLayout w = ws_layout(m, B, 1);
+    Sequencer q{s};
+    KVArgs kv;
+    kv.cache = static_cast<char*>(cache);
+    kv.pos0 = pos;
+    kv.from_cache = true;
+    st = enqueue_trunk(m, tokens, B, 1, m->cfg.n_layer, ws, w, q, kv);
+    if (st != GPT2_OK) return st;
+    if (!logits && !next) return GPT2_OK;
+    return enqueue_next_token(m, reinterpret_cast<const float*>(ws + w.x), B, logits, next, ws, w, q);
 }
 
 gpt2_status gpt2_forward_timed(const gpt2_model* m, const int32_t* tokens, int32_t B, int32_t T, float* logits,

@@ -14,7 +14,7 @@ constexpr int kRowsPerBlock = 4;  // one wavefront per row, four wavefronts per 
 template <bool BF16>
 __global__ __launch_bounds__(256) void embed_kernel(const int32_t* __restrict__ tok, const void* __restrict__ wte,
                                                     const void* __restrict__ wpe, float* __restrict__ x, int M,
-                                                    int T, int d, int n_vocab, int32_t* __restrict__ flags) {
+                                                    int T, int pos0, int d, int n_vocab, int32_t* __restrict__ flags) {
     const int wave = threadIdx.x / GPT2_WAVE, lane = threadIdx.x % GPT2_WAVE;
     const int row = blockIdx.x * kRowsPerBlock + wave;
     int bad = 0;
@@ -24,7 +24,7 @@ __global__ __launch_bounds__(256) void embed_kernel(const int32_t* __restrict__ 
             bad = 1;
             t = t < 0 ? 0 : n_vocab - 1;
         }
-        const int pos = row % T;
+        const int pos = pos0 + row % T;
         float4* xr = reinterpret_cast<float4*>(x + (size_t)row * d);
         const int nq = d / 4;
         if (BF16) {
@@ -207,6 +207,36 @@ __global__ __launch_bounds__(1024) void xent_mean_kernel(const float* __restrict
     if (threadIdx.x == 0) loss[0] = ssum[0] / (float)scnt[0];  // 0 / 0 = NaN when nothing counts
 }
 
+// The same with a whole workgroup per row, for long partial lists (the 16-column partials of the
+// few-row projection: 3142 per row for the GPT-2 vocabulary).
+__global__ __launch_bounds__(256) void argmax_reduce_wide_kernel(const float* __restrict__ pv,
+                                                                 const int32_t* __restrict__ pi, int n_part,
+                                                                 int32_t* __restrict__ out) {
+    __shared__ float sv[4];
+    __shared__ int si[4];
+    const int row = blockIdx.x, wave = threadIdx.x / GPT2_WAVE, lane = threadIdx.x % GPT2_WAVE;
+    float bv = -INFINITY;
+    int bi = 0x7fffffff;
+    for (int j = threadIdx.x; j < n_part; j += 256)
+        argmax_merge(bv, bi, pv[(size_t)row * n_part + j], pi[(size_t)row * n_part + j]);
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) {
+        const float v2 = __shfl_xor(bv, o, GPT2_WAVE);
+        const int i2 = __shfl_xor(bi, o, GPT2_WAVE);
+        argmax_merge(bv, bi, v2, i2);
+    }
+    if (lane == 0) {
+        sv[wave] = bv;
+        si[wave] = bi;
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+#pragma unroll
+        for (int w = 1; w < 4; ++w) argmax_merge(bv, bi, sv[w], si[w]);
+        out[row] = bi;
+    }
+}
+
 __global__ __launch_bounds__(256) void convert_kernel(const void* __restrict__ src, int src_bf16, void* __restrict__ dst,
                                                       int dst_bf16, long n_src, long n_dst) {
     for (long i = (long)blockIdx.x * blockDim.x + threadIdx.x; i < n_dst; i += (long)gridDim.x * blockDim.x) {
@@ -235,13 +265,13 @@ hipError_t launch_ln(const float* x, const float* g, const float* b, void* y, in
 
 int embed_flag_count(int M) { return (M + kRowsPerBlock - 1) / kRowsPerBlock; }
 
-hipError_t embed(const int32_t* tok, const void* wte, const void* wpe, float* x, int M, int T, int d, int n_vocab,
-                 bool bf16, int32_t* flags, hipStream_t s) {
+hipError_t embed(const int32_t* tok, const void* wte, const void* wpe, float* x, int M, int T, int pos0, int d,
+                 int n_vocab, bool bf16, int32_t* flags, hipStream_t s) {
     dim3 grid(embed_flag_count(M)), block(256);
     if (bf16)
-        embed_kernel<true><<<grid, block, 0, s>>>(tok, wte, wpe, x, M, T, d, n_vocab, flags);
+        embed_kernel<true><<<grid, block, 0, s>>>(tok, wte, wpe, x, M, T, pos0, d, n_vocab, flags);
     else
-        embed_kernel<false><<<grid, block, 0, s>>>(tok, wte, wpe, x, M, T, d, n_vocab, flags);
+        embed_kernel<false><<<grid, block, 0, s>>>(tok, wte, wpe, x, M, T, pos0, d, n_vocab, flags);
     return hipGetLastError();
 }
 
@@ -254,7 +284,10 @@ hipError_t layernorm(const float* x, const float* g, const float* b, void* y, in
 }
 
 hipError_t argmax_reduce(const float* pv, const int32_t* pi, int M, int n_part, int32_t* out, hipStream_t s) {
-    argmax_reduce_kernel<<<dim3((M + kRowsPerBlock - 1) / kRowsPerBlock), dim3(256), 0, s>>>(pv, pi, M, n_part, out);
+    if (n_part >= 1024)
+        argmax_reduce_wide_kernel<<<dim3(M), dim3(256), 0, s>>>(pv, pi, n_part, out);
+    else
+        argmax_reduce_kernel<<<dim3((M + kRowsPerBlock - 1) / kRowsPerBlock), dim3(256), 0, s>>>(pv, pi, M, n_part, out);
     return hipGetLastError();
 }
 

@@ -7,6 +7,7 @@ other implementation when it is missing.
 """
 from __future__ import annotations
 
+import contextlib
 import ctypes
 import os
 from dataclasses import dataclass
@@ -20,7 +21,8 @@ OK, EINVAL, ESHAPE, EWORKSPACE, ETOKEN, EHIP, ESTATE = range(7)
 F32, BF16 = 0, 1
 GELU_TANH, GELU_ERF = 0, 1
 EPI_BIAS, EPI_BIAS_GELU, EPI_BIAS_RESIDUAL, EPI_LOGITS = range(4)
-KERNEL_KINDS = ("embed", "ln", "qkv", "attn", "attn_proj", "fc", "mlp_proj", "ln_f", "lm_head", "argmax", "xent")
+KERNEL_KINDS = ("embed", "ln", "qkv", "attn", "attn_proj", "fc", "mlp_proj", "ln_f", "lm_head", "argmax", "xent",
+                "kv")
 
 # Every function the header declares, with its ctypes signature (restype, argtypes).
 _P = ctypes.c_void_p
@@ -39,6 +41,9 @@ SIGNATURES = {
     "gpt2_load_weights": (_I32, [_P, ctypes.POINTER(_P), _I32, _I32, _P, _SZ, _P]),
     "gpt2_forward": (_I32, [_P, _P, _I32, _I32, _P, _P, _P, _SZ, _P]),
     "gpt2_forward_loss": (_I32, [_P, _P, _P, _I32, _I32, _P, _P, _P, _SZ, _P]),
+    "gpt2_kv_cache_bytes": (_SZ, [_P, _I32]),
+    "gpt2_prefill": (_I32, [_P, _P, _I32, _I32, _P, _SZ, _P, _P, _P, _SZ, _P]),
+    "gpt2_decode_step": (_I32, [_P, _P, _I32, _I32, _P, _SZ, _P, _P, _P, _SZ, _P]),
     "gpt2_forward_debug": (_I32, [_P, _P, _I32, _I32, _I32, _P, _P, _SZ, _P]),
     "gpt2_check": (_I32, [_P, _P, _I32, _I32, _P]),
     "gpt2_forward_launches": (_I32, [_P, _I32, ctypes.POINTER(_I32), _I32]),
@@ -243,6 +248,72 @@ class GPT2:
         _check(lib().gpt2_forward_loss(self._h, _ptr(tokens), _ptr(labels), B, T, _ptr(nll), _ptr(loss), _ptr(ws),
                                        ws.numel(), _stream(stream)), "gpt2_forward_loss")
         return nll, loss
+
+    # -- cached decoding -------------------------------------------------------------------------
+    def kv_cache(self, B: int) -> torch.Tensor:
+        """A key/value cache for B sequences (uint8 device buffer, 256-byte aligned)."""
+        n = lib().gpt2_kv_cache_bytes(self._h, B)
+        if n == 0:
+            raise GPT2Error(ESHAPE, "gpt2_kv_cache_bytes")
+        return _aligned_empty(n, self.device)
+
+    def _next_outputs(self, B: int, logits, nxt):
+        if logits is True:
+            logits = torch.empty((B, self.cfg.n_vocab), dtype=torch.float32, device=self.device)
+        elif logits is False:
+            logits = None
+        if nxt is True:
+            nxt = torch.empty((B,), dtype=torch.int32, device=self.device)
+        elif nxt is False:
+            nxt = None
+        return logits, nxt
+
+    def prefill(self, tokens: torch.Tensor, cache: torch.Tensor, logits=False, nxt=True, ws=None, stream=None):
+        """Forward over the prompt tokens int32 [B, T], filling cache positions 0..T-1; returns the
+        last position's (logits [B, V] or None, greedy next token int32 [B] or None)."""
+        _require_cuda(tokens, cache)
+        if tokens.dtype != torch.int32 or tokens.dim() != 2 or not tokens.is_contiguous():
+            raise ValueError("tokens must be a contiguous int32 [B, T] device tensor")
+        B, T = tokens.shape
+        logits, nxt = self._next_outputs(B, logits, nxt)
+        ws = self.workspace(B, T) if ws is None else ws
+        _check(lib().gpt2_prefill(self._h, _ptr(tokens), B, T, _ptr(cache), cache.numel(), _ptr(logits), _ptr(nxt),
+                                  _ptr(ws), ws.numel(), _stream(stream)), "gpt2_prefill")
+        return logits, nxt
+
+    def decode_step(self, tokens: torch.Tensor, pos: int, cache: torch.Tensor, logits=False, nxt=True, ws=None,
+                    stream=None):
+        """One step: tokens int32 [B] at position pos (positions 0..pos-1 already cached)."""
+        _require_cuda(tokens, cache)
+        if tokens.dtype != torch.int32 or tokens.dim() != 1 or not tokens.is_contiguous():
+            raise ValueError("tokens must be a contiguous int32 [B] device tensor")
+        B = tokens.shape[0]
+        logits, nxt = self._next_outputs(B, logits, nxt)
+        ws = self.workspace(B, 1) if ws is None else ws
+        _check(lib().gpt2_decode_step(self._h, _ptr(tokens), B, pos, _ptr(cache), cache.numel(), _ptr(logits),
+                                      _ptr(nxt), _ptr(ws), ws.numel(), _stream(stream)), "gpt2_decode_step")
+        return logits, nxt
+
+    def generate(self, prompt: torch.Tensor, n_new: int, cache: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+        """Greedy decoding: int32 [B, T] prompt -> int32 [B, T + n_new] (prefill, then one cached
+        step per new token; every call is enqueued on the stream without a host synchronisation)."""
+        B, T = prompt.shape
+        if T + n_new > self.cfg.n_ctx:
+            raise ValueError("prompt plus new tokens exceed n_ctx")
+        cache = self.kv_cache(B) if cache is None else cache
+        with torch.cuda.stream(stream) if stream is not None else contextlib.nullcontext():
+            out = torch.empty((B, T + n_new), dtype=torch.int32, device=self.device)
+            out[:, :T] = prompt
+            if n_new == 0:
+                return out
+            toks = [torch.empty((B,), dtype=torch.int32, device=self.device) for _ in range(2)]
+            self.prefill(prompt, cache, logits=False, nxt=toks[0])
+            out[:, T] = toks[0]
+            for i in range(1, n_new):
+                cur, nxt = toks[(i - 1) % 2], toks[i % 2]
+                self.decode_step(cur, T + i - 1, cache, logits=False, nxt=nxt)
+                out[:, T + i] = nxt
+        return out
 
     def launches(self, with_argmax: bool = True) -> list[str]:
         """Kinds of the kernel launches one forward enqueues, in order."""

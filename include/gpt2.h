@@ -137,6 +137,33 @@ gpt2_status gpt2_forward_loss(const gpt2_model* m, const int32_t* tokens_dev, co
                               int32_t B, int32_t T, float* nll_dev, float* loss_dev, void* ws_dev,
                               size_t ws_bytes, hipStream_t stream);
 
+/* Cached incremental decoding ([手写] §6.3 greedy generation; [实战] §4.2): the keys and values of
+ * every layer are kept in a caller-owned cache so that each new token costs one position of the
+ * forward. Layout: for each layer l, K then V, each [B][n_head][n_ctx][64] in the compute dtype
+ * (bf16 or fp32). Positions are shared by the batch: every sequence has the same length.
+ * Bytes of the cache for B sequences (0 for invalid B). */
+size_t gpt2_kv_cache_bytes(const gpt2_model* m, int32_t B);
+
+/* Run the forward over the prompt tokens_dev int32 [B, T] (1 <= T <= n_ctx), writing the keys and
+ * values of positions 0 .. T-1 of every layer into cache_dev (cache_bytes >= gpt2_kv_cache_bytes,
+ * 256-byte aligned); positions >= T are untouched. Then, for the last position of each sequence:
+ *   logits_dev fp32 [B, n_vocab] or NULL: its logits (the same values gpt2_forward gives for row T-1);
+ *   next_dev   int32 [B] or NULL: their argmax, the first index on ties (the greedy next token).
+ * Workspace: gpt2_workspace_bytes(m, B, T). Asynchronous on stream. */
+gpt2_status gpt2_prefill(const gpt2_model* m, const int32_t* tokens_dev, int32_t B, int32_t T, void* cache_dev,
+                         size_t cache_bytes, float* logits_dev, int32_t* next_dev, void* ws_dev, size_t ws_bytes,
+                         hipStream_t stream);
+
+/* One decoding step: tokens_dev int32 [B] is the token at position pos (0 <= pos < n_ctx) of each
+ * sequence, whose positions 0 .. pos-1 are already in cache_dev (from gpt2_prefill and earlier
+ * steps with this cache). Appends the keys and values of position pos, attends over positions
+ * 0 .. pos, and writes the next-token logits_dev fp32 [B, n_vocab] and/or next_dev int32 [B] as
+ * gpt2_prefill does (by causality these are row pos of gpt2_forward over the whole sequence).
+ * Workspace: gpt2_workspace_bytes(m, B, 1). GPT2_ESHAPE for pos outside [0, n_ctx). */
+gpt2_status gpt2_decode_step(const gpt2_model* m, const int32_t* tokens_dev, int32_t B, int32_t pos,
+                             void* cache_dev, size_t cache_bytes, float* logits_dev, int32_t* next_dev,
+                             void* ws_dev, size_t ws_bytes, hipStream_t stream);
+
 /* Residual stream after the embedding and the first n_layers blocks (0 = embedding only,
  * n_layer = all blocks, before ln_f), as fp32 [B, T, d] into resid_dev. Same workspace and
  * argument rules as gpt2_forward. Used for per-block alignment checks ([手写] §4.2). */
@@ -147,7 +174,8 @@ gpt2_status gpt2_forward_debug(const gpt2_model* m, const int32_t* tokens_dev, i
 /* Kinds of the kernel launches a forward enqueues, in order (gpt2_forward_launches). */
 typedef enum {
     GPT2_K_EMBED = 0, GPT2_K_LN = 1, GPT2_K_QKV = 2, GPT2_K_ATTN = 3, GPT2_K_ATTN_PROJ = 4, GPT2_K_FC = 5,
-    GPT2_K_MLP_PROJ = 6, GPT2_K_LN_F = 7, GPT2_K_LM_HEAD = 8, GPT2_K_ARGMAX = 9, GPT2_K_XENT = 10
+    GPT2_K_MLP_PROJ = 6, GPT2_K_LN_F = 7, GPT2_K_LM_HEAD = 8, GPT2_K_ARGMAX = 9, GPT2_K_XENT = 10,
+    GPT2_K_KV = 11
 } gpt2_kernel_kind;
 
 /* Number of kernel launches one gpt2_forward enqueues (with_argmax: argmax_dev != NULL); when

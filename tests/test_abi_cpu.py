@@ -32,7 +32,7 @@ def test_header_declares_expected_entry_points():
     names = declared_functions()
     for required in ("gpt2_config", "gpt2_load_weights", "gpt2_forward", "gpt2_attention", "gpt2_forward_debug",
                      "gpt2_check", "gpt2_strerror", "gpt2_destroy", "gpt2_weight_bytes", "gpt2_workspace_bytes",
-                     "gpt2_forward_loss"):
+                     "gpt2_forward_loss", "gpt2_kv_cache_bytes", "gpt2_prefill", "gpt2_decode_step"):
         assert required in names
 
 
@@ -114,6 +114,18 @@ def test_weight_and_workspace_bytes(g):
     L.gpt2_destroy(h)
 
 
+def test_kv_cache_bytes(g):
+    st, h = make(g)
+    L = g.lib()
+    # per layer K and V, each [B][H][n_ctx][64] bf16
+    assert L.gpt2_kv_cache_bytes(h, 4) == 12 * 2 * 4 * 12 * 1024 * 64 * 2
+    assert L.gpt2_kv_cache_bytes(h, 0) == 0
+    L.gpt2_destroy(h)
+    st, h = make(g, dtype="f32")
+    assert L.gpt2_kv_cache_bytes(h, 1) == 12 * 2 * 12 * 1024 * 64 * 4
+    L.gpt2_destroy(h)
+
+
 def test_forward_launch_sequence(g):
     st, h = make(g)
     L = g.lib()
@@ -139,6 +151,11 @@ def test_host_validation_before_any_launch(g):
     assert L.gpt2_forward_loss(h, fake, None, 1, 4, fake, fake, ctypes.c_void_p(0x100000), 1 << 30, None) == g.ESTATE
     assert L.gpt2_forward_loss(h, None, None, 1, 4, fake, fake, fake, 1 << 30, None) == g.EINVAL
     assert L.gpt2_forward_loss(h, fake, None, 1, 4, None, fake, fake, 1 << 30, None) == g.EINVAL
+    big = ctypes.c_void_p(0x100000)
+    assert L.gpt2_prefill(h, fake, 1, 4, big, 1 << 40, None, fake, big, 1 << 30, None) == g.ESTATE
+    assert L.gpt2_decode_step(h, fake, 1, 3, big, 1 << 40, None, fake, big, 1 << 30, None) == g.ESTATE
+    assert L.gpt2_prefill(h, fake, 1, 4, None, 1 << 40, None, fake, big, 1 << 30, None) == g.EINVAL
+    assert L.gpt2_decode_step(h, None, 1, 3, big, 1 << 40, None, fake, big, 1 << 30, None) == g.EINVAL
     assert L.gpt2_load_weights(h, None, 0, 0, fake, 0, None) == g.EINVAL
     srcs = (ctypes.c_void_p * 3)(fake, fake, fake)
     assert L.gpt2_load_weights(h, srcs, 3, 0, fake, 1 << 40, None) == g.EINVAL   # wrong count

@@ -448,6 +448,118 @@ def test_forward_loss_labels_ignore_and_invalid(g, small_bf16):
         m.forward_loss(dev_tokens(tok[:, :1]))
 
 
+# ------------------------------------------------------------------ cached incremental decoding
+def test_prefill_matches_forward(g, small_bf16):
+    """The prefill's last-position logits are row T-1 of the full forward (same kernels up to the
+    ln_f of that row; the projection's K order is the same for every tile shape)."""
+    m, _ = small_bf16
+    tok = synth.make_tokens(2, 77)
+    cache = m.kv_cache(2)
+    lg, nxt = m.prefill(dev_tokens(tok), cache, logits=True, nxt=True)
+    full, _ = m.forward(dev_tokens(tok), argmax=False)
+    d = (lg - full[:, -1]).abs().max().item()
+    log(f"  prefill vs forward row T-1: max|d|={d:.3e}")
+    assert d <= 1e-5
+    assert torch.equal(nxt, lg.argmax(dim=-1).int())
+
+
+def _teacher_forced(m, tok, T0, cache):
+    """Prefill tok[:, :T0], then decode steps feeding tok[:, pos] for pos = T0 .. end; returns the
+    logits of every step [B, steps, V] (row pos of the forward over tok[:, :pos+1])."""
+    m.prefill(dev_tokens(tok[:, :T0]), cache, logits=False, nxt=False)
+    out = []
+    for pos in range(T0, tok.shape[1]):
+        lg, _ = m.decode_step(dev_tokens(tok[:, pos]).reshape(-1).contiguous(), pos, cache, logits=True, nxt=False)
+        out.append(lg.cpu().numpy())
+    return np.stack(out, axis=1)
+
+
+def test_decode_f32_vs_oracle(g, small_f32):
+    m, w = small_f32
+    tok = synth.make_tokens(2, 9)
+    got = _teacher_forced(m, tok, 5, m.kv_cache(2))
+    ref = O.forward(w, tok, 12, 12)[:, 5:9]  # step k is row 5 + k of the full forward
+    e = row_rel_l2(got, ref).max()
+    log(f"  decode f32: max row rel L2 = {e:.3e}")
+    assert e <= 1e-4
+
+
+def test_decode_bf16_vs_forward_and_oracle(g, small_bf16):
+    m, w = small_bf16
+    tok = synth.make_tokens(2, 48)
+    got = _teacher_forced(m, tok, 40, m.kv_cache(2))
+    full, _ = m.forward(dev_tokens(tok), argmax=False)
+    full = full[:, 40:].cpu().numpy()
+    d = np.abs(got - full).max()
+    log(f"  decode bf16 vs forward rows 40..47: max|d|={d:.3e}")
+    assert d <= 5e-2
+    ref = O.forward(w, tok[:1], 12, 12)[:, 40:]
+    e, a = bf16_report(got[:1], ref, "decode bf16 row 0")
+    assert e <= 5e-2
+
+
+def test_decode_multi_chunk_context(g):
+    """A context longer than one 1024-key chunk of the decode attention (n_ctx 2048, small model,
+    fp32), against the oracle."""
+    s = synth.ModelShape(n_vocab=1000, n_ctx=2048, d_model=128, n_head=2, n_layer=2, d_mlp=512)
+    m, w = model(g, s, "f32")
+    tok = synth.make_tokens(1, 1504, n_vocab=1000)
+    got = _teacher_forced(m, tok, 1500, m.kv_cache(1))
+    ref = O.forward(w, tok, 2, 2)[:, 1500:]
+    e = row_rel_l2(got, ref).max()
+    log(f"  decode at positions 1500..1503: max row rel L2 = {e:.3e}")
+    assert e <= 1e-4
+
+
+def test_generate_f32_matches_oracle(g, small_f32):
+    m, w = small_f32
+    prompt = synth.make_tokens(2, 4)
+    out = m.generate(dev_tokens(prompt), 6).cpu().numpy()
+    ref = O.greedy_generate(w, prompt, 6, 12, 12)
+    log(f"  generated {out.tolist()}")
+    assert np.array_equal(out, ref)
+
+
+def test_generate_bf16_picks_top(g, small_bf16):
+    """bf16 greedy decoding: each new token is a maximum of the full forward's logits for that
+    prefix up to the bf16 logit bound (decode and forward attention round differently)."""
+    m, _ = small_bf16
+    prompt = synth.make_tokens(3, 20)
+    out = m.generate(dev_tokens(prompt), 10).cpu().numpy()
+    for i in range(10):
+        lg, _ = m.forward(dev_tokens(out[:, :20 + i]), argmax=False)
+        lg = lg[:, -1].cpu().numpy().astype(np.float64)
+        pick = out[:, 20 + i]
+        gap = lg.max(axis=-1) - lg[np.arange(3), pick]
+        assert np.all(gap <= 2 * 5e-2), (i, gap)
+
+
+def test_prefill_short_prompt_wide_batch(g, small_bf16):
+    """B=16 sequences of 2 tokens: the next-token projection (16 rows) has more head partials per
+    row than the prompt's projection; the workspace holds both."""
+    m, _ = small_bf16
+    tok = synth.make_tokens(16, 2)
+    cache = m.kv_cache(16)
+    lg, nxt = m.prefill(dev_tokens(tok), cache, logits=True, nxt=True)
+    full, _ = m.forward(dev_tokens(tok), argmax=False)
+    assert (lg - full[:, -1]).abs().max().item() <= 1e-5
+    assert torch.equal(nxt, lg.argmax(dim=-1).int())
+    lg2, nxt2 = m.decode_step(nxt, 2, cache, logits=True, nxt=True)
+    assert torch.equal(nxt2, lg2.argmax(dim=-1).int())
+
+
+def test_decode_errors(g, small_bf16):
+    m, _ = small_bf16
+    cache = m.kv_cache(2)
+    t = dev_tokens(np.array([1, 2]))
+    with pytest.raises(g.GPT2Error):
+        m.decode_step(t, 1024, cache)          # pos >= n_ctx
+    with pytest.raises(g.GPT2Error):
+        m.decode_step(t, 3, cache[:1024])      # cache too small
+    with pytest.raises(g.GPT2Error):
+        m.prefill(dev_tokens(synth.make_tokens(2, 1025)), cache)  # T > n_ctx
+
+
 def test_errors_reported(g, small_bf16):
     m, _ = small_bf16
     tok = dev_tokens(synth.make_tokens(1, 8))
