@@ -73,6 +73,34 @@ __device__ __forceinline__ uint32_t quad_min_u32(uint32_t x) {
     return min(x, dpp_mov<0x4E>(x));
 }
 
+// Sum over the 64 lanes of a wavefront (butterfly, result in every lane).
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, GPT2_WAVE);
+    return v;
+}
+
+// LayerNorm statistics of one row of n fp32 values (n % 4 == 0, n <= 4096) by one wavefront, in the
+// order the LayerNorm kernel uses (so both give the same bits): float4 c = i*64 + lane, sums of
+// (x + y) + (z + w), mean first, then the centred sum of squares; rstd = 1 / sqrt(var + eps).
+__device__ __forceinline__ void row_ln_stats(const float* __restrict__ xr, int n, float eps, float& mean, float& rstd) {
+    const int lane = threadIdx.x % GPT2_WAVE, nq = n / 4;
+    const f32x4_t* x4 = reinterpret_cast<const f32x4_t*>(xr);
+    float s = 0.f;
+    for (int c = lane; c < nq; c += GPT2_WAVE) {
+        const f32x4_t v = x4[c];
+        s += (v[0] + v[1]) + (v[2] + v[3]);
+    }
+    mean = wave_sum(s) / (float)n;
+    float q = 0.f;
+    for (int c = lane; c < nq; c += GPT2_WAVE) {
+        const f32x4_t v = x4[c];
+        const float a0 = v[0] - mean, a1 = v[1] - mean, a2 = v[2] - mean, a3 = v[3] - mean;
+        q += (a0 * a0 + a1 * a1) + (a2 * a2 + a3 * a3);
+    }
+    rstd = 1.0f / sqrtf(wave_sum(q) / (float)n + eps);
+}
+
 // Log-sum-exp partials in base 2: (m, s) stands for 2^m * s. Merging two keeps the larger maximum;
 // an empty partial has m = -inf and s = 0.
 __device__ __forceinline__ void lse_merge(float& m, float& s, float m2, float s2) {
@@ -130,8 +158,25 @@ hipError_t gemm_f32(const float* A, const float* W, const float* bias, void* C, 
 // so the head partial count per row is ceil(N / 16). Needs a_rows >= 16 and w_rows >= N rounded
 // up to 16 readable rows.
 constexpr int kSkinnyM = 16;
+// Fusions of the few-row GEMM used by cached decoding:
+//   ln_x set: A is LayerNorm(ln_x rows; ln_g, ln_b, ln_eps) (fp32 [M, K] in; normalised and rounded
+//             to bf16 on the fly, the same bits the LayerNorm kernel writes); the A argument is unused;
+//   kc set:   (bias epilogue of the fused QKV projection, N = 3d) columns [d, 2d) and [2d, 3d) of row m
+//             are also written as K and V of sequence m, position kv_pos, into the layer's cache
+//             ([B][H][kv_n_ctx][64] bf16 each).
+struct SkinnyExtra {
+    const float* ln_x = nullptr;
+    const float* ln_g = nullptr;
+    const float* ln_b = nullptr;
+    float ln_eps = 0.f;
+    uint16_t* kc = nullptr;
+    uint16_t* vc = nullptr;
+    int kv_n_ctx = 0;
+    int kv_pos = 0;
+};
 hipError_t gemm_bf16_skinny(const uint16_t* A, const uint16_t* W, const float* bias, void* C, int M, int N, int K,
-                            int ldc, int epi, int gelu_erf, int a_rows, int w_rows, const HeadOut& ho, hipStream_t s);
+                            int ldc, int epi, int gelu_erf, int a_rows, int w_rows, const HeadOut& ho,
+                            const SkinnyExtra& ex, hipStream_t s);
 
 hipError_t argmax_reduce(const float* pv, const int32_t* pi, int M, int n_part, int32_t* out, hipStream_t s);
 

@@ -510,7 +510,7 @@ hipError_t gemm_bf16(const uint16_t* A, const uint16_t* W, const float* bias, vo
                      int epi, int gelu_erf, int a_rows, int w_rows, const HeadOut& ho, hipStream_t s) {
     if (ldc < N || ldc > (1 << 26)) return hipErrorInvalidValue;  // in-strip offsets are 32-bit
     if (M <= kSkinnyM)  // a few rows: a stream over W
-        return gemm_bf16_skinny(A, W, bias, C, M, N, K, (int)ldc, epi, gelu_erf, a_rows, w_rows, ho, s);
+        return gemm_bf16_skinny(A, W, bias, C, M, N, K, (int)ldc, epi, gelu_erf, a_rows, w_rows, ho, SkinnyExtra(), s);
     switch (choose_cfg(M, N, K)) {
 #define GPT2_CFG(i, bm, bn, bk, st, wgm, wgn)                                                                    \
     case i:                                                                                                      \

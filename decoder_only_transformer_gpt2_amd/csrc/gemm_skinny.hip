@@ -38,19 +38,53 @@ __device__ __forceinline__ float row16_sum(float x) {
     return x + __builtin_bit_cast(float, ror16<1>(__builtin_bit_cast(uint32_t, x)));
 }
 
-template <int EPI, int KW>  // KW wavefronts split K
+template <int EPI, int KW, bool LNA>  // KW wavefronts split K; LNA: A = LayerNorm(ex.ln_x)
 __global__ __launch_bounds__(64 * KW) void gemm_skinny_kernel(const uint16_t* __restrict__ A,
                                                               const uint16_t* __restrict__ W,
                                                               const float* __restrict__ bias, void* __restrict__ Cv,
-                                                              int M, int N, int K, int ldc, HeadOut ho) {
+                                                              int M, int N, int K, int ldc, HeadOut ho,
+                                                              SkinnyExtra ex) {
     __shared__ f32x4_t red[KW][64];
+    __shared__ float ln_mean[16], ln_rstd[16];
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / GPT2_WAVE), lane = threadIdx.x % GPT2_WAVE;
     const int r16 = lane & 15, g4 = lane >> 4;
     const int n0 = blockIdx.x * 16;
+    if (LNA) {
+        for (int m = wave; m < M; m += KW) {
+            float mean, rstd;
+            row_ln_stats(ex.ln_x + (size_t)m * K, K, ex.ln_eps, mean, rstd);
+            if (lane == 0) {
+                ln_mean[m] = mean;
+                ln_rstd[m] = rstd;
+            }
+        }
+        __syncthreads();
+    }
     // operand fragments: A row r16 (rows >= M are padding; they only reach outputs never stored),
     // W row n0 + r16, each lane 8 consecutive k at 8*g4 within a 32-wide slice
     const uint16_t* ap = A + (size_t)r16 * K + 8 * g4;
     const uint16_t* wp = W + (size_t)(n0 + r16) * K + 8 * g4;
+    const bool arow = r16 < M;
+    const float* xp = ex.ln_x + (size_t)r16 * K + 8 * g4;
+    const float a_mean = LNA && arow ? ln_mean[r16] : 0.f, a_rstd = LNA && arow ? ln_rstd[r16] : 0.f;
+    auto a_frag = [&](int c) -> bf16x8_t {
+        if (!LNA) return *reinterpret_cast<const bf16x8_t*>(ap + c * 32);
+        u32x4_t u = {0u, 0u, 0u, 0u};
+        if (arow) {
+            const int k = c * 32 + 8 * g4;
+            const f32x4_t x0 = *reinterpret_cast<const f32x4_t*>(xp + c * 32);
+            const f32x4_t x1 = *reinterpret_cast<const f32x4_t*>(xp + c * 32 + 4);
+            const f32x4_t g0 = *reinterpret_cast<const f32x4_t*>(ex.ln_g + k);
+            const f32x4_t g1 = *reinterpret_cast<const f32x4_t*>(ex.ln_g + k + 4);
+            const f32x4_t b0 = *reinterpret_cast<const f32x4_t*>(ex.ln_b + k);
+            const f32x4_t b1 = *reinterpret_cast<const f32x4_t*>(ex.ln_b + k + 4);
+            u[0] = pack_bf16x2((x0[0] - a_mean) * a_rstd * g0[0] + b0[0], (x0[1] - a_mean) * a_rstd * g0[1] + b0[1]);
+            u[1] = pack_bf16x2((x0[2] - a_mean) * a_rstd * g0[2] + b0[2], (x0[3] - a_mean) * a_rstd * g0[3] + b0[3]);
+            u[2] = pack_bf16x2((x1[0] - a_mean) * a_rstd * g1[0] + b1[0], (x1[1] - a_mean) * a_rstd * g1[1] + b1[1]);
+            u[3] = pack_bf16x2((x1[2] - a_mean) * a_rstd * g1[2] + b1[2], (x1[3] - a_mean) * a_rstd * g1[3] + b1[3]);
+        }
+        return __builtin_bit_cast(bf16x8_t, u);
+    };
     f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
     const int nch = K / 32;
     int c = wave;
@@ -59,14 +93,14 @@ __global__ __launch_bounds__(64 * KW) void gemm_skinny_kernel(const uint16_t* __
         bf16x8_t af[4], wf[4];
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
-            af[u] = *reinterpret_cast<const bf16x8_t*>(ap + (c + u * KW) * 32);
+            af[u] = a_frag(c + u * KW);
             wf[u] = *reinterpret_cast<const bf16x8_t*>(wp + (c + u * KW) * 32);
         }
 #pragma unroll
         for (int u = 0; u < 4; ++u) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[u], wf[u], acc, 0, 0, 0);
     }
     for (; c < nch; c += KW) {
-        const bf16x8_t af = *reinterpret_cast<const bf16x8_t*>(ap + c * 32);
+        const bf16x8_t af = a_frag(c);
         const bf16x8_t wf = *reinterpret_cast<const bf16x8_t*>(wp + c * 32);
         acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, wf, acc, 0, 0, 0);
     }
@@ -117,7 +151,18 @@ __global__ __launch_bounds__(64 * KW) void gemm_skinny_kernel(const uint16_t* __
                 if (ncol && ho.tgt[m] == n) ho.tgt_logit[m] = v;
             }
         } else {
-            if (ok) static_cast<uint16_t*>(Cv)[(size_t)m * ldc + n] = f32_to_bf16_bits(v);
+            if (ok) {
+                const uint16_t bits = f32_to_bf16_bits(v);
+                static_cast<uint16_t*>(Cv)[(size_t)m * ldc + n] = bits;
+                if (EPI == EPI_BIAS && ex.kc) {  // fused QKV: k and v of this position into the cache
+                    const int d = N / 3, H = d / 64;
+                    if (n >= d) {
+                        const int nn = n < 2 * d ? n - d : n - 2 * d;
+                        uint16_t* cache = n < 2 * d ? ex.kc : ex.vc;
+                        cache[(((size_t)m * H + nn / 64) * ex.kv_n_ctx + ex.kv_pos) * 64 + nn % 64] = bits;
+                    }
+                }
+            }
         }
     }
 }
@@ -125,17 +170,27 @@ __global__ __launch_bounds__(64 * KW) void gemm_skinny_kernel(const uint16_t* __
 }  // namespace
 
 hipError_t gemm_bf16_skinny(const uint16_t* A, const uint16_t* W, const float* bias, void* C, int M, int N, int K,
-                            int ldc, int epi, int gelu_erf, int a_rows, int w_rows, const HeadOut& ho, hipStream_t s) {
+                            int ldc, int epi, int gelu_erf, int a_rows, int w_rows, const HeadOut& ho,
+                            const SkinnyExtra& ex, hipStream_t s) {
     if (M < 1 || M > kSkinnyM || K % 32 || a_rows < 16 || w_rows < (N + 15) / 16 * 16) return hipErrorInvalidValue;
+    if (ex.ln_x && (K % 8 || K > 4096)) return hipErrorInvalidValue;
+    if (ex.kc && (epi != EPI_BIAS || N % 3 || (N / 3) % 64)) return hipErrorInvalidValue;
     // long K over few columns: sixteen wavefronts per workgroup keep enough of W in flight
-    const bool wide = K >= 2048;
+    const bool wide = K >= 2048, lna = ex.ln_x != nullptr;
     const dim3 grid((N + 15) / 16), block(wide ? 1024 : 256);
-#define GPT2_LAUNCH(E)                                                                            \
-    do {                                                                                          \
-        if (wide)                                                                                 \
-            gemm_skinny_kernel<E, 16><<<grid, block, 0, s>>>(A, W, bias, C, M, N, K, ldc, ho);   \
-        else                                                                                      \
-            gemm_skinny_kernel<E, 4><<<grid, block, 0, s>>>(A, W, bias, C, M, N, K, ldc, ho);    \
+#define GPT2_LAUNCH_KW(E, KWV)                                                                                  \
+    do {                                                                                                        \
+        if (lna)                                                                                                \
+            gemm_skinny_kernel<E, KWV, true><<<grid, block, 0, s>>>(A, W, bias, C, M, N, K, ldc, ho, ex);       \
+        else                                                                                                    \
+            gemm_skinny_kernel<E, KWV, false><<<grid, block, 0, s>>>(A, W, bias, C, M, N, K, ldc, ho, ex);      \
+    } while (0)
+#define GPT2_LAUNCH(E)            \
+    do {                          \
+        if (wide)                 \
+            GPT2_LAUNCH_KW(E, 16); \
+        else                      \
+            GPT2_LAUNCH_KW(E, 4);  \
     } while (0)
     switch (epi) {
         case EPI_BIAS: GPT2_LAUNCH(EPI_BIAS); break;
@@ -150,6 +205,7 @@ hipError_t gemm_bf16_skinny(const uint16_t* A, const uint16_t* W, const float* b
         default: GPT2_LAUNCH(EPI_LOGITS); break;
     }
 #undef GPT2_LAUNCH
+#undef GPT2_LAUNCH_KW
     return hipGetLastError();
 }
 

@@ -199,21 +199,43 @@ gpt2_status enqueue_trunk(const gpt2_model* m, const int32_t* tokens, int B, int
     GPT2_RUN(GPT2_K_EMBED, gpt2k::embed(tokens, wptr(m, 0), wptr(m, 1), x, M, T, kv.pos0, d, c.n_vocab, bf,
                                         reinterpret_cast<int32_t*>(ws + w.flags), s));
     // q, k, v views of qkv [B, T, 3, H, 64]: strides (batch, head, token) in elements
+    // cached decoding in bf16 with few rows: LayerNorms and the cache append fused into the
+    // projections (fewer, larger launches)
+    const bool fuse = kv.from_cache && bf && M <= gpt2k::kSkinnyM;
+    auto skinny = [&](int widx, int bidx, void* C, int N, int K, int epi, const gpt2k::SkinnyExtra& ex) {
+        return gpt2k::gemm_bf16_skinny(static_cast<const uint16_t*>(a), static_cast<const uint16_t*>(wptr(m, widx)),
+                                       static_cast<const float*>(wptr(m, bidx)), C, M, N, K, N, epi,
+                                       c.gelu == GPT2_GELU_ERF, (int)w.Mp, (int)m->slots[widx].rows_padded, {}, ex, s);
+    };
     const int64_t qs[3] = {(int64_t)T * 3 * d, 64, 3 * d};
     const int64_t os[3] = {(int64_t)T * d, 64, d};
     const size_t as = act_size(m);
     for (int l = 0; l < n_layers; ++l) {
         auto L = [&](int t) { return layer_idx(l, t); };
         auto vecp = [&](int t) { return static_cast<const float*>(wptr(m, L(t))); };
-        GPT2_RUN(GPT2_K_LN, gpt2k::layernorm(x, vecp(LN1_W), vecp(LN1_B), a, M, d, c.ln_eps, bf, s));
-        GPT2_RUN(GPT2_K_QKV, linear(m, a, L(ATTN_W), L(ATTN_B), qkv, M, 3 * d, d, 3 * d, gpt2k::EPI_BIAS, {}, s));
         const char* qb = static_cast<const char*>(qkv);
         char* kc = nullptr;
         char* vc = nullptr;
         if (kv.cache) {
             kc = kv.cache + (size_t)2 * l * kv_layer_elems(m, B) * as;
             vc = kc + kv_layer_elems(m, B) * as;
-            GPT2_RUN(GPT2_K_KV, gpt2k::kv_append(qkv, B, T, H, kv.pos0, kc, vc, c.n_ctx, bf, s));
+        }
+        if (fuse) {
+            // one launch: ln_1, the QKV projection, and this position's k and v into the cache
+            gpt2k::SkinnyExtra ex;
+            ex.ln_x = x;
+            ex.ln_g = vecp(LN1_W);
+            ex.ln_b = vecp(LN1_B);
+            ex.ln_eps = c.ln_eps;
+            ex.kc = reinterpret_cast<uint16_t*>(kc);
+            ex.vc = reinterpret_cast<uint16_t*>(vc);
+            ex.kv_n_ctx = c.n_ctx;
+            ex.kv_pos = kv.pos0;
+            GPT2_RUN(GPT2_K_QKV, skinny(L(ATTN_W), L(ATTN_B), qkv, 3 * d, d, gpt2k::EPI_BIAS, ex));
+        } else {
+            GPT2_RUN(GPT2_K_LN, gpt2k::layernorm(x, vecp(LN1_W), vecp(LN1_B), a, M, d, c.ln_eps, bf, s));
+            GPT2_RUN(GPT2_K_QKV, linear(m, a, L(ATTN_W), L(ATTN_B), qkv, M, 3 * d, d, 3 * d, gpt2k::EPI_BIAS, {}, s));
+            if (kv.cache) GPT2_RUN(GPT2_K_KV, gpt2k::kv_append(qkv, B, T, H, kv.pos0, kc, vc, c.n_ctx, bf, s));
         }
         if (kv.from_cache)
             GPT2_RUN(GPT2_K_ATTN, gpt2k::decode_attention(qkv, kc, vc, o, B, H, c.n_ctx, kv.pos0 + 1, bf, s));
@@ -229,8 +251,17 @@ gpt2_status enqueue_trunk(const gpt2_model* m, const int32_t* tokens, int B, int
                                                        static_cast<float*>(o), os, B, H, T, s));
         GPT2_RUN(GPT2_K_ATTN_PROJ, linear(m, o, L(APROJ_W), L(APROJ_B), x, M, d, d, d, gpt2k::EPI_BIAS_RESIDUAL,
                                           {}, s));
-        GPT2_RUN(GPT2_K_LN, gpt2k::layernorm(x, vecp(LN2_W), vecp(LN2_B), a, M, d, c.ln_eps, bf, s));
-        GPT2_RUN(GPT2_K_FC, linear(m, a, L(FC_W), L(FC_B), hid, M, f, d, f, gpt2k::EPI_BIAS_GELU, {}, s));
+        if (fuse) {  // ln_2 inside the c_fc projection
+            gpt2k::SkinnyExtra ex;
+            ex.ln_x = x;
+            ex.ln_g = vecp(LN2_W);
+            ex.ln_b = vecp(LN2_B);
+            ex.ln_eps = c.ln_eps;
+            GPT2_RUN(GPT2_K_FC, skinny(L(FC_W), L(FC_B), hid, f, d, gpt2k::EPI_BIAS_GELU, ex));
+        } else {
+            GPT2_RUN(GPT2_K_LN, gpt2k::layernorm(x, vecp(LN2_W), vecp(LN2_B), a, M, d, c.ln_eps, bf, s));
+            GPT2_RUN(GPT2_K_FC, linear(m, a, L(FC_W), L(FC_B), hid, M, f, d, f, gpt2k::EPI_BIAS_GELU, {}, s));
+        }
         GPT2_RUN(GPT2_K_MLP_PROJ, linear(m, hid, L(MPROJ_W), L(MPROJ_B), x, M, d, f, d, gpt2k::EPI_BIAS_RESIDUAL,
                                          {}, s));
     }
@@ -297,14 +328,16 @@ gpt2_status enqueue_next_token(const gpt2_model* m, const float* xr, int B, floa
     const gpt2_config_t& c = m->cfg;
     const hipStream_t s = q.s;
     const int ln_f = 2 + c.n_layer * PER_LAYER;
-    GPT2_RUN(GPT2_K_LN_F, gpt2k::layernorm(xr, static_cast<const float*>(wptr(m, ln_f)),
-                                           static_cast<const float*>(wptr(m, ln_f + 1)), ws + w.al, B, c.d_model,
-                                           c.ln_eps, is_bf16(m), s));
     gpt2k::HeadOut ho;
     if (next) {
         ho.pv = reinterpret_cast<float*>(ws + w.amax_v);
         ho.pi = reinterpret_cast<int32_t*>(ws + w.amax_i);
     }
+    // (a separate ln_f: fused into the projection, each of its ~3000 workgroups would redo the
+    // row statistics, which measured slower)
+    GPT2_RUN(GPT2_K_LN_F, gpt2k::layernorm(xr, static_cast<const float*>(wptr(m, ln_f)),
+                                           static_cast<const float*>(wptr(m, ln_f + 1)), ws + w.al, B, c.d_model,
+                                           c.ln_eps, is_bf16(m), s));
     GPT2_RUN(GPT2_K_LM_HEAD, linear(m, ws + w.al, 0, -1, logits, B, c.n_vocab, c.d_model, c.n_vocab,
                                     gpt2k::EPI_LOGITS, ho, s));
     if (next) {

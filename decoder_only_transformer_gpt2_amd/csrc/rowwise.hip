@@ -52,12 +52,6 @@ __global__ __launch_bounds__(256) void embed_kernel(const int32_t* __restrict__ 
     if (threadIdx.x == 0) flags[blockIdx.x] = any_bad;
 }
 
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, GPT2_WAVE);
-    return v;
-}
-
 // LayerNorm with the biased variance ("复现GPT-2 124M" §2.1: unbiased=False; eps inside the square
 // root, "从零手写GPT-2" §3.2). One wavefront per row; the row stays in registers between the two
 // passes (mean, then the centred sum of squares), so x is read from memory once.
