@@ -417,6 +417,59 @@ def test_greedy_generate_pins():
     assert check_generate(O.greedy_generate) == []
 
 
+# ----------------------------------------------------------------------------- sampling pins
+def check_sample(samp):
+    """samp(logits [B,V], u [B], history, temperature, top_k, top_p, repetition_penalty) -> int [B]."""
+    fails = []
+    L = np.log(np.array([[0.1, 0.2, 0.3, 0.4]]))
+    # inverse CDF by hand: cumulative 0.1, 0.3, 0.6, 1.0
+    got = [int(samp(L, np.array([u]), None, 1.0, 0, 1.0, 1.0)[0]) for u in (0.05, 0.15, 0.35, 0.65, 0.999)]
+    if got != [0, 1, 2, 3, 3]:
+        fails.append("inverse CDF")
+    # top-p by hand on probabilities 0.5, 0.3, 0.15, 0.05 (ascending cumulative 0.05, 0.2, 0.5, 1.0)
+    P = np.log(np.array([[0.5, 0.3, 0.15, 0.05]]))
+    # p = 0.7 keeps {0.5, 0.3} renormalised to 0.625 / 0.375
+    if [int(samp(P, np.array([u]), None, 1.0, 0, 0.7, 1.0)[0]) for u in (0.6, 0.7)] != [0, 1]:
+        fails.append("top-p 0.7")
+    # p = 0.5 keeps only 0.5 (the 0.3 token's cumulative mass is exactly 0.5, not above)
+    if int(samp(P, np.array([0.99]), None, 1.0, 0, 0.5, 1.0)[0]) != 0:
+        fails.append("top-p 0.5 boundary")
+    # top-k 2 keeps {0.5, 0.3}
+    if [int(samp(P, np.array([u]), None, 1.0, 2, 1.0, 1.0)[0]) for u in (0.6, 0.7)] != [0, 1]:
+        fails.append("top-k 2")
+    # temperature: a very large one flattens to uniform (token floor(u V) at bucket midpoints)
+    r = rng(21)
+    Z = r.standard_normal((1, 10))
+    if [int(samp(Z, np.array([(i + 0.5) / 10]), None, 1e9, 0, 1.0, 1.0)[0]) for i in range(10)] != list(range(10)):
+        fails.append("uniform at huge temperature")
+    # top-k 1 is greedy
+    Z = r.standard_normal((6, 300))
+    if not np.array_equal(samp(Z, r.random(6), None, 0.8, 1, 1.0, 1.0), O.argmax_first(Z)):
+        fails.append("top-k 1 = argmax")
+    # repetition penalty 2: 2.0 -> 1.0 (positive divided), -1 -> -2 (negative multiplied), once per id
+    Rl = np.array([[2.0, -1.0, 0.7]])
+    if int(samp(Rl, np.array([0.5]), np.array([[0, 0, 1]]), 1.0, 1, 1.0, 2.0)[0]) != 0:
+        fails.append("penalty once per id")
+    if int(samp(Rl, np.array([0.5]), np.array([[0]]), 1.0, 1, 1.0, 5.0)[0]) != 2:
+        fails.append("penalty divides a positive logit")
+    Rn = np.array([[-0.5, -1.0, -0.6]])
+    if int(samp(Rn, np.array([0.5]), np.array([[0]]), 1.0, 1, 1.0, 1.5)[0]) != 2:
+        fails.append("penalty multiplies a negative logit")
+    # the draw against an explicit multinomial: frequencies over a grid of u match softmax(z / T)
+    z = r.standard_normal((1, 12))
+    us = (np.arange(20000) + 0.5) / 20000
+    counts = np.bincount([int(samp(z, np.array([u]), None, 0.7, 0, 1.0, 1.0)[0]) for u in us], minlength=12)
+    q = np.exp(z[0] / 0.7 - (z[0] / 0.7).max())
+    q /= q.sum()
+    if np.abs(counts / len(us) - q).max() > 1e-3:
+        fails.append("frequencies = softmax(z / T)")
+    return fails
+
+
+def test_sample_pins():
+    assert check_sample(O.sample_next) == []
+
+
 # --------------------------------------------------------------------- planted-mistake audit
 def _unbiased_ln(x, g, b, eps=1e-5):
     x = np.asarray(x, float)
@@ -555,6 +608,33 @@ def _argmin_generate(p, prompt, n_new, n_head, n_layer):
     return seq
 
 
+def _double_penalty_sample(z, u, hist, T, k, p, pen):
+    z = np.array(z, float)
+    if hist is not None:
+        for b in range(z.shape[0]):
+            for i in np.asarray(hist[b]):
+                if i >= 0:
+                    z[b, i] = z[b, i] / pen if z[b, i] > 0 else z[b, i] * pen
+    return O.sample_next(z, u, None, T, k, p, 1.0)
+
+
+def _inverted_penalty_sample(z, u, hist, T, k, p, pen):
+    return O.sample_next(z, u, hist, T, k, p, 1.0 / pen if pen != 1.0 else 1.0)
+
+
+def _ge_top_p_sample(z, u, hist, T, k, p, pen):
+    # nudges the top-p cut so that a token whose cumulative mass equals 1 - p stays too
+    return O.sample_next(z, u, hist, T, k, p * (1 + 1e-9) if p < 1 else p, pen)
+
+
+def _top_k_plus_one_sample(z, u, hist, T, k, p, pen):
+    return O.sample_next(z, u, hist, T, k + 1 if k > 0 else 0, p, pen)
+
+
+def _no_temperature_sample(z, u, hist, T, k, p, pen):
+    return O.sample_next(z, u, hist, 1.0, k, p, pen)
+
+
 @pytest.mark.parametrize("check,mutant", [
     (check_layer_norm, _unbiased_ln), (check_layer_norm, _eps_outside_ln), (check_layer_norm, _no_beta_ln),
     (check_gelu, _cubic_sign_gelu), (check_gelu, _no_half_gelu), (check_gelu, O.gelu_erf),
@@ -566,6 +646,9 @@ def _argmin_generate(p, prompt, n_new, n_head, n_layer):
     (check_cross_entropy, _sum_xent), (check_cross_entropy, _no_max_xent),
     (check_cross_entropy, _ignored_counted_xent), (check_cross_entropy, _time_axis_xent),
     (check_generate, _second_last_generate), (check_generate, _argmin_generate),
+    (check_sample, _double_penalty_sample), (check_sample, _inverted_penalty_sample),
+    (check_sample, _ge_top_p_sample), (check_sample, _top_k_plus_one_sample),
+    (check_sample, _no_temperature_sample),
 ])
 def test_pins_catch_planted_mistakes(check, mutant):
     try:
