@@ -208,6 +208,14 @@ hipError_t decode_attention(const void* qkv, const void* kc, const void* vc, voi
 // dst[b] = src[b * T + T - 1] for rows of n fp32 values.
 hipError_t gather_last_rows(const float* src, float* dst, int B, int T, int n, hipStream_t s);
 
+// Sampled next token of each of B rows of fp32 logits (row stride ld, V <= sample_max_vocab()):
+// repetition penalty over hist[b, 0 .. n_hist) (row stride hist_ld, may be null), division by the
+// temperature, top-k (0 = off), top-p (1 = off), then the inverse-CDF draw at u[b]. n_kept may be null.
+hipError_t sample(const float* logits, long ld, int B, int V, const int32_t* hist, long hist_ld, int n_hist,
+                  float temperature, int top_k, float top_p, float penalty, const float* u, int32_t* out,
+                  int32_t* n_kept, hipStream_t s);
+int sample_max_vocab();
+
 // dst[i] = i < n_src ? convert(src[i]) : 0 for i < n_dst (element types fp32 or bf16).
 hipError_t convert(const void* src, bool src_bf16, void* dst, bool dst_bf16, long n_src, long n_dst,
                    hipStream_t s);

@@ -587,6 +587,20 @@ gpt2_status gpt2_linear(const void* A, const void* W, const float* bias, void* C
     return GPT2_OK;
 }
 
+gpt2_status gpt2_sample(const float* logits, int64_t ld, int32_t B, int32_t V, const int32_t* hist, int64_t hist_ld,
+                        int32_t n_hist, float temperature, int32_t top_k, float top_p, float penalty, const float* u,
+                        int32_t* out, int32_t* n_kept, hipStream_t s) {
+    if (!logits || !u || !out) return GPT2_EINVAL;
+    if (B < 1 || V < 1 || V > gpt2k::sample_max_vocab() || ld < V) return GPT2_ESHAPE;
+    if (n_hist < 0 || (n_hist > 0 && (!hist || hist_ld < n_hist))) return GPT2_EINVAL;
+    if (!(temperature > 0.f) || !(temperature < INFINITY)) return GPT2_EINVAL;
+    if (top_k < 0 || !(top_p > 0.f) || !(top_p <= 1.f)) return GPT2_EINVAL;
+    if (!(penalty > 0.f) || !(penalty < INFINITY)) return GPT2_EINVAL;
+    GPT2_HIP(gpt2k::sample(logits, ld, B, V, n_hist > 0 ? hist : nullptr, hist_ld, n_hist, temperature, top_k, top_p,
+                           penalty, u, out, n_kept, s));
+    return GPT2_OK;
+}
+
 const char* gpt2_strerror(gpt2_status s) {
     switch (s) {
         case GPT2_OK: return "ok";

@@ -51,6 +51,7 @@ SIGNATURES = {
     "gpt2_attention": (_I32, [_P, _I64P, _P, _I64P, _P, _I64P, _P, _I64P, _I32, _I32, _I32, _I32, _I32, _P]),
     "gpt2_layernorm": (_I32, [_P, _P, _P, _P, _I32, _I32, _F, _I32, _P]),
     "gpt2_linear": (_I32, [_P, _P, _P, _P, _I32, _I32, _I32, _I64, _I32, _I32, _I32, _P]),
+    "gpt2_sample": (_I32, [_P, _I64, _I32, _I32, _P, _I64, _I32, _F, _I32, _F, _F, _P, _P, _P, _P]),
     "gpt2_strerror": (ctypes.c_char_p, [_I32]),
 }
 
@@ -294,9 +295,15 @@ class GPT2:
                                       _ptr(nxt), _ptr(ws), ws.numel(), _stream(stream)), "gpt2_decode_step")
         return logits, nxt
 
-    def generate(self, prompt: torch.Tensor, n_new: int, cache: torch.Tensor | None = None, stream=None) -> torch.Tensor:
-        """Greedy decoding: int32 [B, T] prompt -> int32 [B, T + n_new] (prefill, then one cached
-        step per new token; every call is enqueued on the stream without a host synchronisation)."""
+    def generate(self, prompt: torch.Tensor, n_new: int, cache: torch.Tensor | None = None, stream=None,
+                 do_sample: bool = False, temperature: float = 1.0, top_k: int = 0, top_p: float = 1.0,
+                 repetition_penalty: float = 1.0, u: torch.Tensor | None = None,
+                 generator: torch.Generator | None = None) -> torch.Tensor:
+        """Decoding: int32 [B, T] prompt -> int32 [B, T + n_new] (prefill, then one cached step per new
+        token; every call is enqueued on the stream without a host synchronisation). Greedy unless
+        do_sample; sampling applies the repetition penalty over the whole sequence so far, the
+        temperature, top-k and top-p (gpt2_sample), drawing new token i of row b at the uniform
+        number u[i, b] (fp32 [n_new, B] on the device; drawn with torch.rand and generator if None)."""
         B, T = prompt.shape
         if T + n_new > self.cfg.n_ctx:
             raise ValueError("prompt plus new tokens exceed n_ctx")
@@ -306,13 +313,27 @@ class GPT2:
             out[:, :T] = prompt
             if n_new == 0:
                 return out
+            if do_sample and u is None:
+                u = torch.rand((n_new, B), generator=generator, dtype=torch.float32, device=self.device)
+            if do_sample and (u.shape != (n_new, B) or u.dtype != torch.float32 or u.device != out.device):
+                raise ValueError("u must be a float32 [n_new, B] tensor on the model's device")
+            u = u.contiguous() if do_sample else None
+            logits = torch.empty((B, self.cfg.n_vocab), dtype=torch.float32, device=self.device) if do_sample else None
             toks = [torch.empty((B,), dtype=torch.int32, device=self.device) for _ in range(2)]
-            self.prefill(prompt, cache, logits=False, nxt=toks[0])
-            out[:, T] = toks[0]
+
+            def pick(i, nxt):
+                if do_sample:
+                    sample(logits, u[i], history=out[:, :T + i], temperature=temperature, top_k=top_k, top_p=top_p,
+                           repetition_penalty=repetition_penalty, out=nxt)
+                out[:, T + i] = nxt
+
+            self.prefill(prompt, cache, logits=logits if do_sample else False, nxt=False if do_sample else toks[0])
+            pick(0, toks[0])
             for i in range(1, n_new):
                 cur, nxt = toks[(i - 1) % 2], toks[i % 2]
-                self.decode_step(cur, T + i - 1, cache, logits=False, nxt=nxt)
-                out[:, T + i] = nxt
+                self.decode_step(cur, T + i - 1, cache, logits=logits if do_sample else False,
+                                 nxt=False if do_sample else nxt)
+                pick(i, nxt)
         return out
 
     def launches(self, with_argmax: bool = True) -> list[str]:
@@ -349,6 +370,35 @@ class GPT2:
 
 
 # -- op-level entry points -----------------------------------------------------------------------
+def sample(logits: torch.Tensor, u: torch.Tensor, history: torch.Tensor | None = None, temperature: float = 1.0,
+           top_k: int = 0, top_p: float = 1.0, repetition_penalty: float = 1.0, out: torch.Tensor | None = None,
+           n_kept: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """Sampled next token per row of fp32 logits [B, V] (row stride logits.stride(0)) at the uniform
+    numbers u fp32 [B]; history int32 [B, n] (row stride history.stride(0)) feeds the repetition
+    penalty. Returns out int32 [B]; n_kept int32 [B], if given, receives the kept-set sizes."""
+    _require_cuda(logits, u)
+    if logits.dtype != torch.float32 or logits.dim() != 2 or logits.stride(1) != 1:
+        raise ValueError("logits must be a float32 [B, V] device tensor with unit column stride")
+    B, V = logits.shape
+    if u.dtype != torch.float32 or u.shape != (B,) or not u.is_contiguous():
+        raise ValueError("u must be a contiguous float32 [B] device tensor")
+    n_hist, hist_ld = 0, 0
+    if history is not None:
+        _require_cuda(history)
+        if history.dtype != torch.int32 or history.dim() != 2 or history.shape[0] != B or history.stride(1) != 1:
+            raise ValueError("history must be an int32 [B, n] device tensor with unit column stride")
+        n_hist, hist_ld = history.shape[1], history.stride(0)
+    out = torch.empty((B,), dtype=torch.int32, device=logits.device) if out is None else out
+    if out.dtype != torch.int32 or out.shape != (B,) or not out.is_contiguous():
+        raise ValueError("out must be a contiguous int32 [B] device tensor")
+    if n_kept is not None and (n_kept.dtype != torch.int32 or n_kept.shape != (B,) or not n_kept.is_contiguous()):
+        raise ValueError("n_kept must be a contiguous int32 [B] device tensor")
+    _check(lib().gpt2_sample(_ptr(logits), logits.stride(0), B, V, _ptr(history) if n_hist else None, hist_ld, n_hist,
+                             temperature, top_k, top_p, repetition_penalty, _ptr(u), _ptr(out), _ptr(n_kept),
+                             _stream(stream)), "gpt2_sample")
+    return out
+
+
 def attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor | None = None, stream=None):
     """Causal attention of [B, H, T, 64] views (bf16 or fp32); returns o (allocated if None)."""
     _require_cuda(q, k, v, o)

@@ -14,7 +14,7 @@ The "perturbed" variant additionally draws biases ~ N(0, 0.02), gamma ~ 1 + N(0,
 beta ~ N(0, 0.02) from its own stream, so that the bias and affine paths are exercised.
 
 Generator: numpy Generator(PCG64(seed)); seeds 0 (weights), 1 (tokens), 2 (attention Q/K/V),
-3 (perturbation extras). Tensors are drawn one after another in the fixed tensor order below as
+3 (perturbation extras), 4 (sampling inputs). Tensors are drawn one after another in the fixed tensor order below as
 float64 normals, rounded to float32 (round-to-nearest-even), and, for a bf16 model, rounded once
 more to bf16 (round-to-nearest-even) and kept as bf16-exact float32 values. The double rounding
 is deliberate and is the definition of the weights: both sides receive the same values.
@@ -29,6 +29,7 @@ SEED_WEIGHTS = 0
 SEED_TOKENS = 1
 SEED_ATTENTION = 2
 SEED_PERTURB = 3
+SEED_SAMPLING = 4
 
 
 @dataclasses.dataclass(frozen=True)
@@ -128,3 +129,20 @@ def make_qkv(B: int, H: int, T: int, dh: int, bf16: bool = True, seed: int = SEE
         a = rng.standard_normal((B, H, T, dh)).astype(np.float32)
         out.append(round_bf16(a) if bf16 else a)
     return tuple(out)
+
+
+def make_sampling_inputs(B: int, V: int, n_hist: int = 0, std: float = 2.0, n_peaked: int = 0,
+                         seed: int = SEED_SAMPLING):
+    """Inputs of the next-token sampler: logits float32 [B, V] ~ N(0, std^2), where the first
+    n_peaked rows also get 5 dominant tokens (+N(8, 1) on 5 distinct random ids, a peaked next-token
+    distribution); u float32 [B] uniform over [0, 1); history int32 [B, n_hist] uniform ids over
+    [0, V) (the tokens seen so far). Drawn in that order from one stream."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    logits = rng.standard_normal((B, V)) * std
+    for b in range(min(n_peaked, B)):
+        ids = rng.choice(V, size=min(5, V), replace=False)
+        logits[b, ids] += rng.normal(8.0, 1.0, size=ids.shape)
+    u = rng.random(B).astype(np.float32)
+    u = np.minimum(u, np.float32(1.0) - np.float32(2.0 ** -24))  # float32 rounding must not reach 1
+    hist = rng.integers(0, V, size=(B, n_hist)).astype(np.int32)
+    return logits.astype(np.float32), u, hist

@@ -232,6 +232,29 @@ gpt2_status gpt2_linear(const void* A_dev, const void* W_dev, const float* bias_
                         int32_t M, int32_t N, int32_t K, int64_t ldc, int32_t dtype, int32_t epilogue,
                         int32_t gelu, hipStream_t stream);
 
+/* Sampled next-token choice for B rows of fp32 logits, the sampling branch of generation: the
+ * repetition penalty, temperature, top-k and top-p knobs of [实战] §8.2, then a draw from
+ * softmax(z / temperature) restricted to the kept tokens ([解析] §4.1), taken by inverse CDF. Per row:
+ *   1. every distinct id of hist_dev[b, 0 .. n_hist) inside [0, V) has its logit divided by
+ *      repetition_penalty when positive and multiplied by it otherwise (ids outside are ignored);
+ *   2. z = logit / temperature (fp32);
+ *   3. top_k > 0 and < V: tokens whose z is below the k-th largest z are dropped (ties kept);
+ *   4. top_p < 1: with q the softmax of z over the tokens still kept, a token is dropped when the
+ *      q-mass of the kept tokens with a strictly larger z is p or more (the largest z always stays);
+ *   5. out_dev[b] = the first token in vocabulary order whose cumulative q over the kept tokens
+ *      exceeds u_dev[b] (u clamped into [0, 1)); n_kept_dev[b] (if not NULL) = how many were kept.
+ * Masses are summed in 2^-40 fixed point, so the result is independent of summation order.
+ *   logits_dev  fp32 [B, V], row stride ld >= V (elements); V <= 65536.
+ *   hist_dev    int32 [B, n_hist], row stride hist_ld >= n_hist; may be NULL when n_hist == 0.
+ *   u_dev       fp32 [B]: the caller's uniform random numbers (one per row).
+ * GPT2_EINVAL for temperature or repetition_penalty not finite and > 0, top_k < 0, top_p outside
+ * (0, 1] or a missing pointer; GPT2_ESHAPE for B < 1, V < 1, V > 65536 or ld < V. A row whose
+ * largest logit is not finite yields an unspecified token in [0, V). Needs no model handle. */
+gpt2_status gpt2_sample(const float* logits_dev, int64_t ld, int32_t B, int32_t V, const int32_t* hist_dev,
+                        int64_t hist_ld, int32_t n_hist, float temperature, int32_t top_k, float top_p,
+                        float repetition_penalty, const float* u_dev, int32_t* out_dev, int32_t* n_kept_dev,
+                        hipStream_t stream);
+
 /* Static text for a status code. */
 const char* gpt2_strerror(gpt2_status s);
 

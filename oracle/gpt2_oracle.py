@@ -237,53 +237,62 @@ def greedy_generate(p: dict, prompt: np.ndarray, n_new: int, n_head: int, n_laye
     return seq
 
 
-def sample_next(logits: np.ndarray, u: np.ndarray, history: np.ndarray | None = None, temperature: float = 1.0,
-                top_k: int = 0, top_p: float = 1.0, repetition_penalty: float = 1.0) -> np.ndarray:
-    """One sampled next token per row ([实战] §8.2: repetition penalty, temperature, top-k, top-p;
-    [解析] §4.1: softmax(logits / temperature), then a multinomial draw). logits [B, V]; u [B]
-    uniform numbers in [0, 1) supplied by the caller (the randomness of the draw); history int
-    [B, n] token ids seen so far (negative entries ignored) or None. Readings:
-      * penalty: each distinct id in the history has its logit divided by the penalty when it is
-        positive and multiplied by it otherwise (applied once per id);
+def sample_filter(logits: np.ndarray, history: np.ndarray | None = None, temperature: float = 1.0, top_k: int = 0,
+                  top_p: float = 1.0, repetition_penalty: float = 1.0):
+    """The logit processors of sampled decoding ([实战] §8.2: repetition penalty, temperature, top-k,
+    top-p), row by row. Returns (z, keep): z [B, V] the penalised logits divided by the temperature
+    and keep [B, V] the tokens that survive both cut-offs. Readings:
+      * penalty: each distinct id of the row's history inside [0, V) (others ignored) has its logit
+        divided by the penalty when it is positive and multiplied by it otherwise, once per id;
       * top_k = 0 or >= V keeps everything; otherwise every token whose value is at least the k-th
         largest value is kept (ties at the boundary stay);
       * top_p = 1 keeps everything; otherwise, with q the softmax over the tokens kept so far,
         token v stays when the mass of all kept tokens with value <= its own exceeds 1 - top_p
-        (ties together; the largest value always stays);
-      * the draw is the first token, in vocabulary order, whose cumulative probability over the
-        kept tokens exceeds u."""
+        (ties together; the largest value always stays)."""
     z = np.array(logits, dtype=F64)
     B, V = z.shape
-    out = np.empty(B, dtype=np.int64)
+    keep = np.ones((B, V), dtype=bool)
     for b in range(B):
-        zb = z[b].copy()
         if history is not None and repetition_penalty != 1.0:
-            ids = np.unique(np.asarray(history[b])[np.asarray(history[b]) >= 0])
-            v = zb[ids]
-            zb[ids] = np.where(v > 0, v / repetition_penalty, v * repetition_penalty)
-        zb = zb / temperature
-        keep = np.ones(V, dtype=bool)
+            h = np.asarray(history[b])
+            ids = np.unique(h[(h >= 0) & (h < V)])
+            v = z[b, ids]
+            z[b, ids] = np.where(v > 0, v / repetition_penalty, v * repetition_penalty)
+        z[b] = z[b] / temperature
         if 0 < top_k < V:
-            kth = np.sort(zb)[::-1][top_k - 1]
-            keep &= zb >= kth
+            kth = np.sort(z[b])[::-1][top_k - 1]
+            keep[b] &= z[b] >= kth
         if top_p < 1.0:
-            m = zb[keep].max()
-            q = np.where(keep, np.exp(zb - m), 0.0)
+            m = z[b][keep[b]].max()
+            q = np.where(keep[b], np.exp(z[b] - m), 0.0)
             q /= q.sum()
             # mass of the kept tokens whose value is <= each token's value
-            order = np.argsort(zb, kind="stable")
-            zs, qs = zb[order], q[order]
+            order = np.argsort(z[b], kind="stable")
+            zs, qs = z[b][order], q[order]
             cum = np.cumsum(qs)
             # ties: every member of a run of equal values gets the cumulative mass at the run's end
             last = np.searchsorted(zs, zs, side="right") - 1
             below = np.empty(V)
             below[order] = cum[last]
-            keep &= below > 1.0 - top_p
-        m = zb[keep].max()
-        q = np.where(keep, np.exp(zb - m), 0.0)
+            keep[b] &= below > 1.0 - top_p
+    return z, keep
+
+
+def sample_next(logits: np.ndarray, u: np.ndarray, history: np.ndarray | None = None, temperature: float = 1.0,
+                top_k: int = 0, top_p: float = 1.0, repetition_penalty: float = 1.0) -> np.ndarray:
+    """One sampled next token per row: the processors of sample_filter, then a multinomial draw
+    from the softmax of z over the kept tokens ([解析] §4.1: softmax(logits / temperature), then a
+    multinomial draw). logits [B, V]; u [B] uniform numbers in [0, 1) supplied by the caller (the
+    randomness of the draw); history int [B, n] token ids seen so far or None. The draw is the
+    first token, in vocabulary order, whose cumulative probability over the kept tokens exceeds u."""
+    z, keep = sample_filter(logits, history, temperature, top_k, top_p, repetition_penalty)
+    out = np.empty(z.shape[0], dtype=np.int64)
+    for b in range(z.shape[0]):
+        m = z[b][keep[b]].max()
+        q = np.where(keep[b], np.exp(z[b] - m), 0.0)
         c = np.cumsum(q) / q.sum()
         idx = int(np.searchsorted(c, u[b], side="right"))  # first index with c > u
-        out[b] = min(idx, int(np.nonzero(keep)[0][-1]))
+        out[b] = min(idx, int(np.nonzero(keep[b])[0][-1]))
     return out
 
 

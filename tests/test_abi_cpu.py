@@ -32,7 +32,7 @@ def test_header_declares_expected_entry_points():
     names = declared_functions()
     for required in ("gpt2_config", "gpt2_load_weights", "gpt2_forward", "gpt2_attention", "gpt2_forward_debug",
                      "gpt2_check", "gpt2_strerror", "gpt2_destroy", "gpt2_weight_bytes", "gpt2_workspace_bytes",
-                     "gpt2_forward_loss", "gpt2_kv_cache_bytes", "gpt2_prefill", "gpt2_decode_step"):
+                     "gpt2_forward_loss", "gpt2_kv_cache_bytes", "gpt2_prefill", "gpt2_decode_step", "gpt2_sample"):
         assert required in names
 
 
@@ -175,6 +175,23 @@ def test_host_validation_before_any_launch(g):
     assert L.gpt2_linear(fake, fake, fake, fake, 4, 8, 64, 4, 1, 0, 0, None) == g.ESHAPE    # ldc < N
     assert L.gpt2_linear(fake, fake, fake, fake, 4, 8, 64, 8, 1, 9, 0, None) == g.EINVAL    # epilogue
     assert L.gpt2_check(None, fake, 1, 1, None) == g.EINVAL
+    # sampler: argument checks (every case here is rejected on the host)
+    S = L.gpt2_sample
+    assert S(None, 8, 1, 8, None, 0, 0, 1.0, 0, 1.0, 1.0, fake, fake, None, None) == g.EINVAL   # no logits
+    assert S(fake, 8, 1, 8, None, 0, 0, 1.0, 0, 1.0, 1.0, None, fake, None, None) == g.EINVAL   # no u
+    assert S(fake, 8, 1, 8, None, 0, 0, 1.0, 0, 1.0, 1.0, fake, None, None, None) == g.EINVAL   # no out
+    assert S(fake, 8, 0, 8, None, 0, 0, 1.0, 0, 1.0, 1.0, fake, fake, None, None) == g.ESHAPE   # B = 0
+    assert S(fake, 4, 1, 8, None, 0, 0, 1.0, 0, 1.0, 1.0, fake, fake, None, None) == g.ESHAPE   # ld < V
+    assert S(fake, 70000, 1, 70000, None, 0, 0, 1.0, 0, 1.0, 1.0, fake, fake, None, None) == g.ESHAPE  # V too big
+    assert S(fake, 8, 1, 8, None, 4, 2, 1.0, 0, 1.0, 1.0, fake, fake, None, None) == g.EINVAL   # history missing
+    assert S(fake, 8, 1, 8, fake, 1, 2, 1.0, 0, 1.0, 1.0, fake, fake, None, None) == g.EINVAL   # hist_ld < n
+    assert S(fake, 8, 1, 8, None, 0, 0, 0.0, 0, 1.0, 1.0, fake, fake, None, None) == g.EINVAL   # temperature 0
+    assert S(fake, 8, 1, 8, None, 0, 0, float("inf"), 0, 1.0, 1.0, fake, fake, None, None) == g.EINVAL
+    assert S(fake, 8, 1, 8, None, 0, 0, 1.0, -1, 1.0, 1.0, fake, fake, None, None) == g.EINVAL  # top_k < 0
+    assert S(fake, 8, 1, 8, None, 0, 0, 1.0, 0, 0.0, 1.0, fake, fake, None, None) == g.EINVAL   # top_p 0
+    assert S(fake, 8, 1, 8, None, 0, 0, 1.0, 0, 1.5, 1.0, fake, fake, None, None) == g.EINVAL   # top_p > 1
+    assert S(fake, 8, 1, 8, None, 0, 0, 1.0, 0, float("nan"), 1.0, fake, fake, None, None) == g.EINVAL
+    assert S(fake, 8, 1, 8, None, 0, 0, 1.0, 0, 1.0, 0.0, fake, fake, None, None) == g.EINVAL   # penalty 0
     for s in range(7):
         assert L.gpt2_strerror(s)
     L.gpt2_destroy(h)

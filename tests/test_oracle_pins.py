@@ -470,6 +470,25 @@ def test_sample_pins():
     assert check_sample(O.sample_next) == []
 
 
+def test_sample_filter_kept_sets():
+    """Kept-set sizes the definitions fix directly."""
+    P = np.log(np.array([[0.5, 0.3, 0.15, 0.05]]))
+    count = lambda **kw: int(O.sample_filter(P, **kw)[1].sum())
+    assert count() == 4
+    assert count(top_k=2) == 2 and count(top_k=4) == 4 and count(top_k=9) == 4
+    assert count(top_p=0.7) == 2 and count(top_p=0.5) == 1 and count(top_p=0.51) == 2 and count(top_p=0.96) == 4
+    assert count(top_k=3, top_p=0.7) == 2
+    # ties at the top-k boundary are all kept; ties share the top-p decision
+    T = np.array([[1.0, 2.0, 2.0, 0.5]])
+    assert int(O.sample_filter(T, top_k=2)[1].sum()) == 2 and int(O.sample_filter(T, top_k=1)[1].sum()) == 2
+    # two tied tokens with 0.4 each plus 0.2: p = 0.5 keeps both tied ones (mass strictly above each is 0)
+    T2 = np.log(np.array([[0.4, 0.2, 0.4]]))
+    assert O.sample_filter(T2, top_p=0.5)[1].tolist() == [[True, False, True]]
+    # the penalty ignores ids outside [0, V) and negative ones
+    z, _ = O.sample_filter(np.array([[2.0, -1.0]]), history=np.array([[-1, 5, 1]]), repetition_penalty=2.0)
+    assert z.tolist() == [[2.0, -2.0]]
+
+
 # --------------------------------------------------------------------- planted-mistake audit
 def _unbiased_ln(x, g, b, eps=1e-5):
     x = np.asarray(x, float)
