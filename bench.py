@@ -7,7 +7,9 @@ embedding, every block, ln_f, the tied lm_head (fp32 logits) and the fused argma
 seeded synthetic init (no checkpoint exists). Prints one JSON line. After the timed region it also
 times gpt2_forward_loss (the same forward with the shifted next-token cross-entropy fused into the
 vocabulary projection, logits not stored) under "forward_loss", and cached greedy decode steps
-(gpt2_decode_step after a gpt2_prefill of half the context) under "decode".
+(gpt2_decode_step after a gpt2_prefill of half the context) under "decode", and the same steps with
+sampling (gpt2_sample at temperature 0.7, top-k 50, top-p 0.95, repetition penalty 1.2) under
+"decode_sampled".
 
 The roofline object is for the lm_head GEMM, the largest single launch: its duration is taken
 from HIP events the library records on its own stream around that launch in every timed step.
@@ -207,6 +209,46 @@ def main():
                          "steps": n_dec, "hbm_bytes_per_step": step_bytes,
                          "hbm_frac": step_bytes / (dms * 1e-3) / 1e9 / PEAK_HBM_GBS,
                          "what": "greedy cached decode step (next-token argmax), weights + cache read per step"}
+
+        # Sampled decoding with the knobs of the pages' generation example (temperature 0.7, top-k 50,
+        # top-p 0.95, repetition penalty 1.2 over the whole sequence so far): each step writes the
+        # next-token logits, gpt2_sample draws from them, and the token is appended to the sequence.
+        knobs = dict(temperature=0.7, top_k=50, top_p=0.95, repetition_penalty=1.2)
+        seq = torch.zeros((B, T0 + n_dec + 8), dtype=torch.int32, device="cuda")
+        seq[:, :T0] = prompt
+        lg = torch.empty((B, shape.n_vocab), dtype=torch.float32, device="cuda")
+        u = torch.rand((n_dec + 8, B), generator=torch.Generator(device="cuda").manual_seed(5), device="cuda")
+        sws = gpt2._aligned_empty(gpt2.sample_workspace_bytes(B, shape.n_vocab), "cuda")
+        m.prefill(prompt, cache, logits=lg, nxt=False)
+        gpt2.sample(lg, u[0], history=seq[:, :T0], out=cur, ws=sws, **knobs)
+
+        def sampled_step(i, cur, nxt):
+            m.decode_step(cur, T0 + i, cache, logits=lg, nxt=False, ws=wsd)
+            gpt2.sample(lg, u[i + 1], history=seq[:, :T0 + i + 1], out=nxt, ws=sws, **knobs)
+            seq[:, T0 + i + 1] = nxt
+
+        for i in range(4):
+            sampled_step(i, cur, nxt)
+        torch.cuda.synchronize()
+        t4 = time.perf_counter()
+        for i in range(n_dec):
+            sampled_step(i, cur, nxt)
+            cur, nxt = nxt, cur
+        torch.cuda.synchronize()
+        sms = (time.perf_counter() - t4) * 1e3 / n_dec
+        # the sampler alone, timed with events on the stream it runs on
+        n_s = 50
+        e0, e1 = raw_event(), raw_event()
+        e0.record()
+        for i in range(n_s):
+            gpt2.sample(lg, u[i % n_dec], history=seq[:, :T0 + n_dec], out=nxt, ws=sws, **knobs)
+        e1.record()
+        torch.cuda.synchronize()
+        out["decode_sampled"] = {"ms_per_step": sms, "tokens_per_s": B / (sms * 1e-3), "batch": B,
+                                 "prefill_len": T0, "steps": n_dec, "knobs": knobs,
+                                 "sample_call_us": e0.elapsed_time(e1) * 1e3 / n_s,
+                                 "what": "cached decode step + gpt2_sample + append to the sequence; sample_call_us is "
+                                         "one gpt2_sample call through the Python binding (host-bound at this batch)"}
 
     if args.copy_bytes > 0:
         src = torch.empty(args.copy_bytes, dtype=torch.uint8, device="cuda")

@@ -211,9 +211,12 @@ hipError_t gather_last_rows(const float* src, float* dst, int B, int T, int n, h
 // Sampled next token of each of B rows of fp32 logits (row stride ld, V <= sample_max_vocab()):
 // repetition penalty over hist[b, 0 .. n_hist) (row stride hist_ld, may be null), division by the
 // temperature, top-k (0 = off), top-p (1 = off), then the inverse-CDF draw at u[b]. n_kept may be null.
+// With a workspace of sample_workspace_bytes(B, V) bytes (256-byte aligned) the top-k case is spread
+// over many workgroups per row; ws = null keeps every row on one workgroup.
 hipError_t sample(const float* logits, long ld, int B, int V, const int32_t* hist, long hist_ld, int n_hist,
                   float temperature, int top_k, float top_p, float penalty, const float* u, int32_t* out,
-                  int32_t* n_kept, hipStream_t s);
+                  int32_t* n_kept, void* ws, size_t ws_bytes, hipStream_t s);
+size_t sample_workspace_bytes(int B, int V);
 int sample_max_vocab();
 
 // dst[i] = i < n_src ? convert(src[i]) : 0 for i < n_dst (element types fp32 or bf16).

@@ -587,17 +587,24 @@ gpt2_status gpt2_linear(const void* A, const void* W, const float* bias, void* C
     return GPT2_OK;
 }
 
+size_t gpt2_sample_workspace_bytes(int32_t B, int32_t V) {
+    if (B < 1 || V < 1 || V > gpt2k::sample_max_vocab()) return 0;
+    return gpt2k::sample_workspace_bytes(B, V);
+}
+
 gpt2_status gpt2_sample(const float* logits, int64_t ld, int32_t B, int32_t V, const int32_t* hist, int64_t hist_ld,
                         int32_t n_hist, float temperature, int32_t top_k, float top_p, float penalty, const float* u,
-                        int32_t* out, int32_t* n_kept, hipStream_t s) {
+                        int32_t* out, int32_t* n_kept, void* ws, size_t ws_bytes, hipStream_t s) {
     if (!logits || !u || !out) return GPT2_EINVAL;
     if (B < 1 || V < 1 || V > gpt2k::sample_max_vocab() || ld < V) return GPT2_ESHAPE;
     if (n_hist < 0 || (n_hist > 0 && (!hist || hist_ld < n_hist))) return GPT2_EINVAL;
     if (!(temperature > 0.f) || !(temperature < INFINITY)) return GPT2_EINVAL;
     if (top_k < 0 || !(top_p > 0.f) || !(top_p <= 1.f)) return GPT2_EINVAL;
     if (!(penalty > 0.f) || !(penalty < INFINITY)) return GPT2_EINVAL;
+    if (ws && (reinterpret_cast<uintptr_t>(ws) % 256)) return GPT2_EINVAL;
+    if (ws && ws_bytes < gpt2k::sample_workspace_bytes(B, V)) return GPT2_EWORKSPACE;
     GPT2_HIP(gpt2k::sample(logits, ld, B, V, n_hist > 0 ? hist : nullptr, hist_ld, n_hist, temperature, top_k, top_p,
-                           penalty, u, out, n_kept, s));
+                           penalty, u, out, n_kept, ws, ws_bytes, s));
     return GPT2_OK;
 }
 

@@ -51,7 +51,8 @@ SIGNATURES = {
     "gpt2_attention": (_I32, [_P, _I64P, _P, _I64P, _P, _I64P, _P, _I64P, _I32, _I32, _I32, _I32, _I32, _P]),
     "gpt2_layernorm": (_I32, [_P, _P, _P, _P, _I32, _I32, _F, _I32, _P]),
     "gpt2_linear": (_I32, [_P, _P, _P, _P, _I32, _I32, _I32, _I64, _I32, _I32, _I32, _P]),
-    "gpt2_sample": (_I32, [_P, _I64, _I32, _I32, _P, _I64, _I32, _F, _I32, _F, _F, _P, _P, _P, _P]),
+    "gpt2_sample": (_I32, [_P, _I64, _I32, _I32, _P, _I64, _I32, _F, _I32, _F, _F, _P, _P, _P, _P, _SZ, _P]),
+    "gpt2_sample_workspace_bytes": (_SZ, [_I32, _I32]),
     "gpt2_strerror": (ctypes.c_char_p, [_I32]),
 }
 
@@ -319,12 +320,13 @@ class GPT2:
                 raise ValueError("u must be a float32 [n_new, B] tensor on the model's device")
             u = u.contiguous() if do_sample else None
             logits = torch.empty((B, self.cfg.n_vocab), dtype=torch.float32, device=self.device) if do_sample else None
+            sws = _aligned_empty(sample_workspace_bytes(B, self.cfg.n_vocab), self.device) if do_sample else None
             toks = [torch.empty((B,), dtype=torch.int32, device=self.device) for _ in range(2)]
 
             def pick(i, nxt):
                 if do_sample:
                     sample(logits, u[i], history=out[:, :T + i], temperature=temperature, top_k=top_k, top_p=top_p,
-                           repetition_penalty=repetition_penalty, out=nxt)
+                           repetition_penalty=repetition_penalty, out=nxt, ws=sws)
                 out[:, T + i] = nxt
 
             self.prefill(prompt, cache, logits=logits if do_sample else False, nxt=False if do_sample else toks[0])
@@ -372,10 +374,12 @@ class GPT2:
 # -- op-level entry points -----------------------------------------------------------------------
 def sample(logits: torch.Tensor, u: torch.Tensor, history: torch.Tensor | None = None, temperature: float = 1.0,
            top_k: int = 0, top_p: float = 1.0, repetition_penalty: float = 1.0, out: torch.Tensor | None = None,
-           n_kept: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+           n_kept: torch.Tensor | None = None, ws: torch.Tensor | bool | None = True, stream=None) -> torch.Tensor:
     """Sampled next token per row of fp32 logits [B, V] (row stride logits.stride(0)) at the uniform
     numbers u fp32 [B]; history int32 [B, n] (row stride history.stride(0)) feeds the repetition
-    penalty. Returns out int32 [B]; n_kept int32 [B], if given, receives the kept-set sizes."""
+    penalty. Returns out int32 [B]; n_kept int32 [B], if given, receives the kept-set sizes. ws: a
+    workspace of sample_workspace_bytes(B, V) bytes, True to allocate one, or None / False for the
+    one-workgroup-per-row path."""
     _require_cuda(logits, u)
     if logits.dtype != torch.float32 or logits.dim() != 2 or logits.stride(1) != 1:
         raise ValueError("logits must be a float32 [B, V] device tensor with unit column stride")
@@ -393,10 +397,21 @@ def sample(logits: torch.Tensor, u: torch.Tensor, history: torch.Tensor | None =
         raise ValueError("out must be a contiguous int32 [B] device tensor")
     if n_kept is not None and (n_kept.dtype != torch.int32 or n_kept.shape != (B,) or not n_kept.is_contiguous()):
         raise ValueError("n_kept must be a contiguous int32 [B] device tensor")
+    if ws is True:
+        ws = _aligned_empty(sample_workspace_bytes(B, V), logits.device)
+    elif ws is False:
+        ws = None
+    if ws is not None:
+        _require_cuda(ws)
     _check(lib().gpt2_sample(_ptr(logits), logits.stride(0), B, V, _ptr(history) if n_hist else None, hist_ld, n_hist,
-                             temperature, top_k, top_p, repetition_penalty, _ptr(u), _ptr(out), _ptr(n_kept),
-                             _stream(stream)), "gpt2_sample")
+                             temperature, top_k, top_p, repetition_penalty, _ptr(u), _ptr(out), _ptr(n_kept), _ptr(ws),
+                             0 if ws is None else ws.numel() * ws.element_size(), _stream(stream)), "gpt2_sample")
     return out
+
+
+def sample_workspace_bytes(B: int, V: int) -> int:
+    """Bytes of the optional sampler workspace (0 for invalid B, V)."""
+    return lib().gpt2_sample_workspace_bytes(B, V)
 
 
 def attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor | None = None, stream=None):

@@ -237,23 +237,36 @@ gpt2_status gpt2_linear(const void* A_dev, const void* W_dev, const float* bias_
  * softmax(z / temperature) restricted to the kept tokens ([解析] §4.1), taken by inverse CDF. Per row:
  *   1. every distinct id of hist_dev[b, 0 .. n_hist) inside [0, V) has its logit divided by
  *      repetition_penalty when positive and multiplied by it otherwise (ids outside are ignored);
- *   2. z = logit / temperature (fp32);
+ *   2. z = x / temperature for the penalised logits x (dividing by a positive temperature keeps
+ *      their order, so steps 3 and 4 compare x, in fp32, and the softmax weights are
+ *      exp((x - max x) / temperature));
  *   3. top_k > 0 and < V: tokens whose z is below the k-th largest z are dropped (ties kept);
  *   4. top_p < 1: with q the softmax of z over the tokens still kept, a token is dropped when the
  *      q-mass of the kept tokens with a strictly larger z is p or more (the largest z always stays);
  *   5. out_dev[b] = the first token in vocabulary order whose cumulative q over the kept tokens
  *      exceeds u_dev[b] (u clamped into [0, 1)); n_kept_dev[b] (if not NULL) = how many were kept.
- * Masses are summed in 2^-40 fixed point, so the result is independent of summation order.
+ * Each weight is rounded to 2^-31 of the largest one and the weights are summed exactly in integer
+ * arithmetic, so the result does not depend on summation order (a token whose weight is below
+ * 2^-31 of the largest is never drawn).
  *   logits_dev  fp32 [B, V], row stride ld >= V (elements); V <= 65536.
  *   hist_dev    int32 [B, n_hist], row stride hist_ld >= n_hist; may be NULL when n_hist == 0.
  *   u_dev       fp32 [B]: the caller's uniform random numbers (one per row).
+ *   ws_dev      NULL, or a 256-byte aligned device workspace of ws_bytes >=
+ *               gpt2_sample_workspace_bytes(B, V) bytes used by this call alone until the stream
+ *               passes it: with it, top-k rows are screened by many workgroups per row before one
+ *               wave finishes them; without it each row runs on one workgroup. The result is the
+ *               same either way.
  * GPT2_EINVAL for temperature or repetition_penalty not finite and > 0, top_k < 0, top_p outside
- * (0, 1] or a missing pointer; GPT2_ESHAPE for B < 1, V < 1, V > 65536 or ld < V. A row whose
- * largest logit is not finite yields an unspecified token in [0, V). Needs no model handle. */
+ * (0, 1], a missing pointer or a misaligned workspace; GPT2_EWORKSPACE for a workspace below the
+ * required size; GPT2_ESHAPE for B < 1, V < 1, V > 65536 or ld < V. A row whose largest logit is
+ * not finite yields an unspecified token in [0, V). Needs no model handle. */
 gpt2_status gpt2_sample(const float* logits_dev, int64_t ld, int32_t B, int32_t V, const int32_t* hist_dev,
                         int64_t hist_ld, int32_t n_hist, float temperature, int32_t top_k, float top_p,
                         float repetition_penalty, const float* u_dev, int32_t* out_dev, int32_t* n_kept_dev,
-                        hipStream_t stream);
+                        void* ws_dev, size_t ws_bytes, hipStream_t stream);
+
+/* Bytes of the optional gpt2_sample workspace for B rows of V logits (0 for invalid B, V). */
+size_t gpt2_sample_workspace_bytes(int32_t B, int32_t V);
 
 /* Static text for a status code. */
 const char* gpt2_strerror(gpt2_status s);

@@ -177,21 +177,27 @@ def test_host_validation_before_any_launch(g):
     assert L.gpt2_check(None, fake, 1, 1, None) == g.EINVAL
     # sampler: argument checks (every case here is rejected on the host)
     S = L.gpt2_sample
-    assert S(None, 8, 1, 8, None, 0, 0, 1.0, 0, 1.0, 1.0, fake, fake, None, None) == g.EINVAL   # no logits
-    assert S(fake, 8, 1, 8, None, 0, 0, 1.0, 0, 1.0, 1.0, None, fake, None, None) == g.EINVAL   # no u
-    assert S(fake, 8, 1, 8, None, 0, 0, 1.0, 0, 1.0, 1.0, fake, None, None, None) == g.EINVAL   # no out
-    assert S(fake, 8, 0, 8, None, 0, 0, 1.0, 0, 1.0, 1.0, fake, fake, None, None) == g.ESHAPE   # B = 0
-    assert S(fake, 4, 1, 8, None, 0, 0, 1.0, 0, 1.0, 1.0, fake, fake, None, None) == g.ESHAPE   # ld < V
-    assert S(fake, 70000, 1, 70000, None, 0, 0, 1.0, 0, 1.0, 1.0, fake, fake, None, None) == g.ESHAPE  # V too big
-    assert S(fake, 8, 1, 8, None, 4, 2, 1.0, 0, 1.0, 1.0, fake, fake, None, None) == g.EINVAL   # history missing
-    assert S(fake, 8, 1, 8, fake, 1, 2, 1.0, 0, 1.0, 1.0, fake, fake, None, None) == g.EINVAL   # hist_ld < n
-    assert S(fake, 8, 1, 8, None, 0, 0, 0.0, 0, 1.0, 1.0, fake, fake, None, None) == g.EINVAL   # temperature 0
-    assert S(fake, 8, 1, 8, None, 0, 0, float("inf"), 0, 1.0, 1.0, fake, fake, None, None) == g.EINVAL
-    assert S(fake, 8, 1, 8, None, 0, 0, 1.0, -1, 1.0, 1.0, fake, fake, None, None) == g.EINVAL  # top_k < 0
-    assert S(fake, 8, 1, 8, None, 0, 0, 1.0, 0, 0.0, 1.0, fake, fake, None, None) == g.EINVAL   # top_p 0
-    assert S(fake, 8, 1, 8, None, 0, 0, 1.0, 0, 1.5, 1.0, fake, fake, None, None) == g.EINVAL   # top_p > 1
-    assert S(fake, 8, 1, 8, None, 0, 0, 1.0, 0, float("nan"), 1.0, fake, fake, None, None) == g.EINVAL
-    assert S(fake, 8, 1, 8, None, 0, 0, 1.0, 0, 1.0, 0.0, fake, fake, None, None) == g.EINVAL   # penalty 0
+    assert S(None, 8, 1, 8, None, 0, 0, 1.0, 0, 1.0, 1.0, fake, fake, None, None, 0, None) == g.EINVAL   # no logits
+    assert S(fake, 8, 1, 8, None, 0, 0, 1.0, 0, 1.0, 1.0, None, fake, None, None, 0, None) == g.EINVAL   # no u
+    assert S(fake, 8, 1, 8, None, 0, 0, 1.0, 0, 1.0, 1.0, fake, None, None, None, 0, None) == g.EINVAL   # no out
+    assert S(fake, 8, 0, 8, None, 0, 0, 1.0, 0, 1.0, 1.0, fake, fake, None, None, 0, None) == g.ESHAPE   # B = 0
+    assert S(fake, 4, 1, 8, None, 0, 0, 1.0, 0, 1.0, 1.0, fake, fake, None, None, 0, None) == g.ESHAPE   # ld < V
+    assert S(fake, 70000, 1, 70000, None, 0, 0, 1.0, 0, 1.0, 1.0, fake, fake, None, None, 0, None) == g.ESHAPE  # V too big
+    assert S(fake, 8, 1, 8, None, 4, 2, 1.0, 0, 1.0, 1.0, fake, fake, None, None, 0, None) == g.EINVAL   # history missing
+    assert S(fake, 8, 1, 8, fake, 1, 2, 1.0, 0, 1.0, 1.0, fake, fake, None, None, 0, None) == g.EINVAL   # hist_ld < n
+    assert S(fake, 8, 1, 8, None, 0, 0, 0.0, 0, 1.0, 1.0, fake, fake, None, None, 0, None) == g.EINVAL   # temperature 0
+    assert S(fake, 8, 1, 8, None, 0, 0, float("inf"), 0, 1.0, 1.0, fake, fake, None, None, 0, None) == g.EINVAL
+    assert S(fake, 8, 1, 8, None, 0, 0, 1.0, -1, 1.0, 1.0, fake, fake, None, None, 0, None) == g.EINVAL  # top_k < 0
+    assert S(fake, 8, 1, 8, None, 0, 0, 1.0, 0, 0.0, 1.0, fake, fake, None, None, 0, None) == g.EINVAL   # top_p 0
+    assert S(fake, 8, 1, 8, None, 0, 0, 1.0, 0, 1.5, 1.0, fake, fake, None, None, 0, None) == g.EINVAL   # top_p > 1
+    assert S(fake, 8, 1, 8, None, 0, 0, 1.0, 0, float("nan"), 1.0, fake, fake, None, None, 0, None) == g.EINVAL
+    assert S(fake, 8, 1, 8, None, 0, 0, 1.0, 0, 1.0, 0.0, fake, fake, None, None, 0, None) == g.EINVAL   # penalty 0
+    need = L.gpt2_sample_workspace_bytes(2, 50257)
+    assert need > 0 and L.gpt2_sample_workspace_bytes(0, 8) == 0 and L.gpt2_sample_workspace_bytes(1, 70000) == 0
+    big = ctypes.c_void_p(0x100000)
+    assert S(fake, 50257, 2, 50257, None, 0, 0, 1.0, 5, 1.0, 1.0, fake, fake, None, big, need - 1, None) == g.EWORKSPACE
+    assert S(fake, 50257, 2, 50257, None, 0, 0, 1.0, 5, 1.0, 1.0, fake, fake, None, ctypes.c_void_p(0x100010), need,
+             None) == g.EINVAL  # misaligned workspace
     for s in range(7):
         assert L.gpt2_strerror(s)
     L.gpt2_destroy(h)

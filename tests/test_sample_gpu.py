@@ -36,7 +36,7 @@ def log(msg):
     print(msg, flush=True)
 
 
-def run_gpu(g, logits, u, hist, T, k, p, pen, ld=None):
+def run_gpu(g, logits, u, hist, T, k, p, pen, ld=None, ws=True):
     B, V = logits.shape
     ld = V if ld is None else ld
     buf = torch.full((B, ld), float("nan"), dtype=torch.float32)
@@ -45,7 +45,7 @@ def run_gpu(g, logits, u, hist, T, k, p, pen, ld=None):
     h = torch.from_numpy(np.ascontiguousarray(hist)).cuda() if hist is not None and hist.shape[1] else None
     n_kept = torch.full((B,), -1, dtype=torch.int32, device="cuda")
     out = g.sample(lg, torch.from_numpy(u).cuda(), history=h, temperature=T, top_k=k, top_p=p,
-                   repetition_penalty=pen, n_kept=n_kept)
+                   repetition_penalty=pen, n_kept=n_kept, ws=ws)
     torch.cuda.synchronize()
     return out.cpu().numpy().astype(np.int64), n_kept.cpu().numpy().astype(np.int64)
 
@@ -54,6 +54,9 @@ def check_rows(g, logits, u, hist, T, k, p, pen, ld=None, min_exact=0.95):
     B, V = logits.shape
     log(f"  sample B={B} V={V} ld={ld} T={T} k={k} p={p} pen={pen}")
     tok, kept = run_gpu(g, logits, u, hist, T, k, p, pen, ld)
+    # the one-workgroup-per-row path (no workspace) gives the same tokens and kept-set sizes
+    tok1, kept1 = run_gpu(g, logits, u, hist, T, k, p, pen, ld, ws=None)
+    assert np.array_equal(tok, tok1) and np.array_equal(kept, kept1)
     assert np.all((tok >= 0) & (tok < V))
     exact = 0
     for b in range(B):
@@ -126,6 +129,20 @@ def test_sample_ties_exact(g):
         _, keep = O.sample_filter(logits[b:b + 1].astype(np.float64), top_k=10)
         assert kept[b] == keep.sum() and keep[0, tok[b]]
     check_rows(g, logits, u, None, T=1.0, k=10, p=1.0, pen=1.0)
+
+
+def test_sample_long_candidate_lists(g):
+    """Rows whose screened candidate list is long: a plateau of equal logits at the top (hundreds
+    or thousands of tokens tie above the bound) sends the row to the general path; both paths and
+    the oracle agree."""
+    rng = np.random.Generator(np.random.PCG64(14))
+    logits = (rng.standard_normal((6, 50257)) * 2.0).astype(np.float32)
+    for b, width in enumerate((300, 600, 2000, 5000, 20000, 50257)):
+        ids = rng.choice(50257, size=width, replace=False)
+        logits[b, ids] = 7.0
+    u = rng.random(6).astype(np.float32)
+    check_rows(g, logits, u, None, T=1.0, k=50, p=1.0, pen=1.0)
+    check_rows(g, logits, u, None, T=0.7, k=50, p=0.9, pen=1.0)
 
 
 def test_sample_masked_vocab(g):
