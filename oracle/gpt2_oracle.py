@@ -296,6 +296,143 @@ def sample_next(logits: np.ndarray, u: np.ndarray, history: np.ndarray | None = 
     return out
 
 
+# ------------------------------------------------------------------------------------ backward
+# Gradients of the mean shifted cross-entropy ([手写] §4 training loop: loss.backward()) with
+# respect to every weight. Each function is the chain rule of one forward step above, written out
+# by hand in float64; the tied matrix wte collects both the lm_head gradient and the embedding
+# gradient ([手写] §2.2: with weight tying the gradient of wte is the sum of the two).
+
+
+def layer_norm_backward(x: np.ndarray, gamma: np.ndarray, dy: np.ndarray, eps: float = 1e-5):
+    """Gradients of layer_norm (biased variance): with xhat = (x - mean) / sqrt(var + eps) and
+    g = dy * gamma, dx = (g - mean(g) - xhat * mean(g * xhat)) / sqrt(var + eps); dgamma and dbeta
+    are dy * xhat and dy summed over every leading axis. Returns (dx, dgamma, dbeta)."""
+    x = np.asarray(x, dtype=F64)
+    dy = np.asarray(dy, dtype=F64)
+    mean = x.mean(axis=-1, keepdims=True)
+    var = ((x - mean) ** 2).mean(axis=-1, keepdims=True)
+    rstd = 1.0 / np.sqrt(var + eps)
+    xhat = (x - mean) * rstd
+    g = dy * np.asarray(gamma, F64)
+    dx = rstd * (g - g.mean(axis=-1, keepdims=True) - xhat * (g * xhat).mean(axis=-1, keepdims=True))
+    d = x.shape[-1]
+    return dx, (dy * xhat).reshape(-1, d).sum(axis=0), dy.reshape(-1, d).sum(axis=0)
+
+
+def linear_backward(x: np.ndarray, w: np.ndarray, dy: np.ndarray):
+    """Gradients of y = x W^T + b: dx = dy W, dW = dy^T x (summed over every row), db = sum of dy.
+    Returns (dx, dW, db)."""
+    x = np.asarray(x, dtype=F64)
+    w = np.asarray(w, dtype=F64)
+    dy = np.asarray(dy, dtype=F64)
+    n_out, n_in = w.shape
+    return dy @ w, dy.reshape(-1, n_out).T @ x.reshape(-1, n_in), dy.reshape(-1, n_out).sum(axis=0)
+
+
+def gelu_tanh_backward(x: np.ndarray, dy: np.ndarray) -> np.ndarray:
+    """dy * gelu'(x) for the tanh form: with c = sqrt(2/pi), z = c (x + 0.044715 x^3), t = tanh z,
+    gelu'(x) = 0.5 (1 + t) + 0.5 x (1 - t^2) c (1 + 3 * 0.044715 x^2)."""
+    x = np.asarray(x, dtype=F64)
+    c = math.sqrt(2.0 / math.pi)
+    t = np.tanh(c * (x + 0.044715 * x ** 3))
+    return np.asarray(dy, F64) * (0.5 * (1.0 + t) + 0.5 * x * (1.0 - t * t) * c * (1.0 + 3.0 * 0.044715 * x * x))
+
+
+def causal_attention_backward(q: np.ndarray, k: np.ndarray, v: np.ndarray, do: np.ndarray):
+    """Gradients of causal_attention for the output gradient do (all [..., T, dh]): with P the
+    masked softmax of S = q k^T / sqrt(dh), dV = P^T dO, dP = dO V^T, dS = P * (dP - rowsum(P * dP)),
+    dQ = dS K / sqrt(dh), dK = dS^T Q / sqrt(dh) (the masked entries have P = 0 and pass nothing).
+    Returns (dq, dk, dv)."""
+    q = np.asarray(q, dtype=F64)
+    k = np.asarray(k, dtype=F64)
+    v = np.asarray(v, dtype=F64)
+    do = np.asarray(do, dtype=F64)
+    T, dh = q.shape[-2], q.shape[-1]
+    scale = 1.0 / math.sqrt(dh)
+    s = (q @ np.swapaxes(k, -1, -2)) * scale
+    s = np.where(np.triu(np.ones((T, T), dtype=bool), k=1), -np.inf, s)
+    prob = softmax(s, axis=-1)
+    dv = np.swapaxes(prob, -1, -2) @ do
+    dp = do @ np.swapaxes(v, -1, -2)
+    ds = prob * (dp - (prob * dp).sum(axis=-1, keepdims=True))
+    return (ds @ k) * scale, (np.swapaxes(ds, -1, -2) @ q) * scale, dv
+
+
+def shifted_cross_entropy_backward(logits: np.ndarray, labels: np.ndarray) -> np.ndarray:
+    """Gradient of shifted_cross_entropy with respect to logits [B, T, V]: for every counted
+    position (b, t < T-1), (softmax(logits[b, t]) - onehot(labels[b, t+1])) / n_counted; zero at
+    the last position of each row and at ignored positions."""
+    z = np.asarray(logits, dtype=F64)
+    grad = np.zeros_like(z)
+    _, counted = shifted_nll(z, labels)
+    n = int(counted.sum())
+    if n == 0:
+        return grad
+    y = np.asarray(labels)[:, 1:]
+    g = softmax(z[:, :-1, :], axis=-1)
+    b_idx, t_idx = np.nonzero(counted)
+    g[b_idx, t_idx, y[b_idx, t_idx]] -= 1.0
+    grad[:, :-1, :] = np.where(counted[..., None], g, 0.0) / n
+    return grad
+
+
+def loss_and_grads(p: dict, tokens: np.ndarray, labels: np.ndarray | None, n_head: int, n_layer: int,
+                   eps: float = 1e-5) -> tuple[float, dict]:
+    """Mean shifted cross-entropy of the forward (labels None: the tokens themselves) and its
+    gradient with respect to every weight of p (same keys). The forward is the one above, step by
+    step, keeping what the backward needs; the backward visits the steps in reverse."""
+    tokens = np.asarray(tokens)
+    labels = tokens if labels is None else np.asarray(labels)
+    B, T = tokens.shape
+    x = embed(p["wte"], p["wpe"], tokens)
+    saved = []
+    for l in range(n_layer):
+        pre = f"h.{l}."
+        a1 = layer_norm(x, p[pre + "ln_1.w"], p[pre + "ln_1.b"], eps)
+        qkv = linear(a1, p[pre + "attn.c_attn.w"], p[pre + "attn.c_attn.b"])
+        q, k, v = split_heads(qkv, n_head)
+        o = merge_heads(causal_attention(q, k, v))
+        x_mid = x + linear(o, p[pre + "attn.c_proj.w"], p[pre + "attn.c_proj.b"])
+        a2 = layer_norm(x_mid, p[pre + "ln_2.w"], p[pre + "ln_2.b"], eps)
+        u = linear(a2, p[pre + "mlp.c_fc.w"], p[pre + "mlp.c_fc.b"])
+        h = gelu_tanh(u)
+        x_out = x_mid + linear(h, p[pre + "mlp.c_proj.w"], p[pre + "mlp.c_proj.b"])
+        saved.append((x, a1, q, k, v, o, x_mid, a2, u, h))
+        x = x_out
+    xf = layer_norm(x, p["ln_f.w"], p["ln_f.b"], eps)
+    logits = lm_head(xf, p["wte"])
+    loss = shifted_cross_entropy(logits, labels)
+
+    g = {}
+    dlogits = shifted_cross_entropy_backward(logits, labels)
+    dxf, dwte_head, _ = linear_backward(xf, p["wte"], dlogits)
+    dx, g["ln_f.w"], g["ln_f.b"] = layer_norm_backward(x, p["ln_f.w"], dxf, eps)
+    for l in reversed(range(n_layer)):
+        pre = f"h.{l}."
+        x_in, a1, q, k, v, o, x_mid, a2, u, h = saved[l]
+        dh, g[pre + "mlp.c_proj.w"], g[pre + "mlp.c_proj.b"] = linear_backward(h, p[pre + "mlp.c_proj.w"], dx)
+        du = gelu_tanh_backward(u, dh)
+        da2, g[pre + "mlp.c_fc.w"], g[pre + "mlp.c_fc.b"] = linear_backward(a2, p[pre + "mlp.c_fc.w"], du)
+        dln2, g[pre + "ln_2.w"], g[pre + "ln_2.b"] = layer_norm_backward(x_mid, p[pre + "ln_2.w"], da2, eps)
+        dx_mid = dx + dln2
+        do, g[pre + "attn.c_proj.w"], g[pre + "attn.c_proj.b"] = linear_backward(o, p[pre + "attn.c_proj.w"], dx_mid)
+        dh_ = do.shape[-1] // n_head
+        do_heads = do.reshape(B, T, n_head, dh_).transpose(0, 2, 1, 3)  # the layout split_heads gives q
+        dq, dk, dv = causal_attention_backward(q, k, v, do_heads)
+        dqkv = np.concatenate([merge_heads(dq), merge_heads(dk), merge_heads(dv)], axis=-1)
+        da1, g[pre + "attn.c_attn.w"], g[pre + "attn.c_attn.b"] = linear_backward(a1, p[pre + "attn.c_attn.w"], dqkv)
+        dln1, g[pre + "ln_1.w"], g[pre + "ln_1.b"] = layer_norm_backward(x_in, p[pre + "ln_1.w"], da1, eps)
+        dx = dx_mid + dln1
+    # embedding: x[b, t] = wte[tokens[b, t]] + wpe[t]
+    dwte_embed = np.zeros_like(np.asarray(p["wte"], F64))
+    np.add.at(dwte_embed, tokens.reshape(-1), dx.reshape(-1, dx.shape[-1]))
+    g["wte"] = dwte_head + dwte_embed
+    dwpe = np.zeros_like(np.asarray(p["wpe"], F64))
+    dwpe[:T] = dx.sum(axis=0)
+    g["wpe"] = dwpe
+    return loss, g
+
+
 def param_count(n_vocab: int, n_ctx: int, d: int, n_layer: int, d_mlp: int) -> int:
     """Number of parameters with lm_head tied to wte (counted once).
 

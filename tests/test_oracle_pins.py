@@ -489,6 +489,176 @@ def test_sample_filter_kept_sets():
     assert z.tolist() == [[2.0, -2.0]]
 
 
+# ------------------------------------------------------------------------------ backward pins
+# The gradients are pinned against central finite differences of the forward functions (which are
+# pinned above), the check the pages use for hand-written backward code ([手写] §5.2: gradcheck in
+# float64 with eps 1e-6, atol 1e-4, rtol 1e-3); here the bar is much tighter.
+FD_H = 1e-6
+
+
+def fd(f, arr, idx):
+    """Central difference of the scalar f() with respect to arr[idx] (arr is perturbed in place)."""
+    old = arr[idx]
+    arr[idx] = old + FD_H
+    up = f()
+    arr[idx] = old - FD_H
+    dn = f()
+    arr[idx] = old
+    return (up - dn) / (2 * FD_H)
+
+
+def fd_all(f, arr):
+    out = np.zeros_like(arr)
+    for idx in np.ndindex(arr.shape):
+        out[idx] = fd(f, arr, idx)
+    return out
+
+
+def check_layer_norm_backward(lnb):
+    fails = []
+    r = rng(31)
+    x = r.standard_normal((3, 6))
+    gam = 1 + 0.3 * r.standard_normal(6)
+    bet = r.standard_normal(6)
+    R = r.standard_normal((3, 6))
+    f = lambda: float((R * O.layer_norm(x, gam, bet)).sum())
+    dx, dg, db = lnb(x, gam, R)
+    for name, got, arr in (("dx", dx, x), ("dgamma", dg, gam), ("dbeta", db, bet)):
+        if np.abs(got - fd_all(f, arr)).max() > 1e-7:
+            fails.append(name)
+    # the output does not change when a constant is added to a row: each row of dx sums to 0
+    if np.abs(dx.sum(axis=-1)).max() > 1e-12:
+        fails.append("row sums")
+    return fails
+
+
+def check_gelu_backward(gb):
+    fails = []
+    xs = np.linspace(-6, 6, 49)
+    num = np.array([(O.gelu_tanh(v + FD_H) - O.gelu_tanh(v - FD_H)) / (2 * FD_H) for v in xs])
+    if np.abs(gb(xs, np.ones_like(xs)) - num).max() > 1e-8:
+        fails.append("finite differences")
+    if gb(np.array([0.0]), np.array([1.0]))[0] != 0.5:
+        fails.append("gelu'(0) = 1/2")
+    if abs(gb(np.array([30.0]), np.array([1.0]))[0] - 1.0) > 1e-12 or abs(gb(np.array([-30.0]), np.array([1.0]))[0]) > 1e-12:
+        fails.append("saturation")
+    return fails
+
+
+def check_linear_backward(lb):
+    r = rng(32)
+    x = r.standard_normal((2, 3, 4))
+    w = r.standard_normal((5, 4))
+    b = r.standard_normal(5)
+    R = r.standard_normal((2, 3, 5))
+    f = lambda: float((R * O.linear(x, w, b)).sum())
+    dx, dw, db = lb(x, w, R)
+    fails = []
+    for name, got, arr in (("dx", dx, x), ("dw", dw, w), ("db", db, b)):
+        if np.abs(got - fd_all(f, arr)).max() > 1e-7:
+            fails.append(name)
+    return fails
+
+
+def check_attention_backward(ab):
+    fails = []
+    r = rng(33)
+    q, k, v = (r.standard_normal((1, 2, 4, 3)) for _ in range(3))
+    R = r.standard_normal((1, 2, 4, 3))
+    f = lambda: float((R * O.causal_attention(q, k, v)).sum())
+    dq, dk, dv = ab(q, k, v, R)
+    for name, got, arr in (("dq", dq, q), ("dk", dk, k), ("dv", dv, v)):
+        if np.abs(got - fd_all(f, arr)).max() > 1e-7:
+            fails.append(name)
+    # one position: out = v, so dv = dout exactly and q, k get nothing
+    q1, k1, v1, d1 = (r.standard_normal((1, 1, 1, 3)) for _ in range(4))
+    a, b_, c = ab(q1, k1, v1, d1)
+    if not (np.array_equal(c, d1) and not a.any() and not b_.any()):
+        fails.append("T = 1")
+    return fails
+
+
+def check_xent_backward(xb):
+    fails = []
+    r = rng(34)
+    z = r.standard_normal((2, 4, 5))
+    lab = r.integers(0, 5, size=(2, 4))
+    lab[1, 2] = O.IGNORE_INDEX
+    f = lambda: O.shifted_cross_entropy(z, lab)
+    g = xb(z, lab)
+    if np.abs(g - fd_all(f, z)).max() > 1e-8:
+        fails.append("finite differences")
+    if np.abs(g.sum(axis=-1)).max() > 1e-15:
+        fails.append("rows sum to 0")
+    if g[:, -1].any() or g[1, 1].any():
+        fails.append("last and ignored positions get nothing")
+    return fails
+
+
+def tiny_model(seed=35):
+    """A model small enough for finite differences on every tensor, with every bias, gain and
+    shift perturbed so that no gradient path is trivially zero."""
+    s = synth.ModelShape(n_vocab=13, n_ctx=6, d_model=8, n_head=2, n_layer=2, d_mlp=16)
+    r = rng(seed)
+    p = {}
+    for name, shape, kind in synth.tensor_specs(s):
+        base = 1.0 if kind == "gamma" else 0.0
+        p[name] = base + (0.5 if kind in ("emb", "w", "w_res") else 0.2) * r.standard_normal(shape)
+    return s, p
+
+
+def check_model_grads(lg):
+    s, p = tiny_model()
+    r = rng(36)
+    tok = r.integers(0, s.n_vocab, size=(2, 5))
+    lab = tok.copy()
+    lab[0, 3] = O.IGNORE_INDEX
+    loss, g = lg(p, tok, lab, s.n_head, s.n_layer)
+    f = lambda: O.shifted_cross_entropy(O.forward(p, tok, s.n_head, s.n_layer), lab)
+    fails = []
+    if abs(loss - f()) > 1e-12:
+        fails.append("loss")
+    for name in p:
+        arr = p[name]
+        if g[name].shape != arr.shape:
+            fails.append(name + " shape")
+            continue
+        flat = list(np.ndindex(arr.shape))
+        pick = [flat[i] for i in r.choice(len(flat), size=min(12, len(flat)), replace=False)]
+        if name == "wte":  # rows fed to the embedding and rows only the lm_head touches
+            pick += [(int(tok[0, 0]), 1), (int(np.setdiff1d(np.arange(s.n_vocab), tok)[0]), 2)]
+        for idx in pick:
+            num = fd(f, arr, idx)
+            if abs(g[name][idx] - num) > 1e-7 * (1 + abs(num)):
+                fails.append(f"{name}{idx}")
+                break
+    return fails
+
+
+def test_layer_norm_backward_pins():
+    assert check_layer_norm_backward(O.layer_norm_backward) == []
+
+
+def test_gelu_backward_pins():
+    assert check_gelu_backward(O.gelu_tanh_backward) == []
+
+
+def test_linear_backward_pins():
+    assert check_linear_backward(O.linear_backward) == []
+
+
+def test_attention_backward_pins():
+    assert check_attention_backward(O.causal_attention_backward) == []
+
+
+def test_cross_entropy_backward_pins():
+    assert check_xent_backward(O.shifted_cross_entropy_backward) == []
+
+
+def test_model_gradients_finite_differences():
+    assert check_model_grads(O.loss_and_grads) == []
+
+
 # --------------------------------------------------------------------- planted-mistake audit
 def _unbiased_ln(x, g, b, eps=1e-5):
     x = np.asarray(x, float)
@@ -654,6 +824,63 @@ def _no_temperature_sample(z, u, hist, T, k, p, pen):
     return O.sample_next(z, u, hist, 1.0, k, p, pen)
 
 
+def _no_xhat_term_lnb(x, g, dy, eps=1e-5):
+    x = np.asarray(x, float)
+    mean = x.mean(-1, keepdims=True)
+    rstd = 1 / np.sqrt(((x - mean) ** 2).mean(-1, keepdims=True) + eps)
+    xhat = (x - mean) * rstd
+    gg = dy * g
+    return rstd * (gg - gg.mean(-1, keepdims=True)), (dy * xhat).reshape(-1, x.shape[-1]).sum(0), \
+        dy.reshape(-1, x.shape[-1]).sum(0)
+
+
+def _first_term_gelu_back(x, dy):
+    t = np.tanh(np.sqrt(2 / np.pi) * (x + 0.044715 * x ** 3))
+    return dy * 0.5 * (1 + t)
+
+
+def _transposed_dw_linear_back(x, w, dy):
+    dx, dw, db = O.linear_backward(x, w, dy)
+    return dx, dw.T.reshape(dw.shape) if dw.shape[0] == dw.shape[1] else dw[::-1], db
+
+
+def _no_rowsum_attn_back(q, k, v, do):
+    T, dh = q.shape[-2], q.shape[-1]
+    s = (q @ np.swapaxes(k, -1, -2)) / np.sqrt(dh)
+    s = np.where(np.triu(np.ones((T, T), bool), 1), -np.inf, s)
+    pr = O.softmax(s)
+    dv = np.swapaxes(pr, -1, -2) @ do
+    ds = pr * (do @ np.swapaxes(v, -1, -2))
+    return ds @ k / np.sqrt(dh), np.swapaxes(ds, -1, -2) @ q / np.sqrt(dh), dv
+
+
+def _unnormalised_xent_back(z, lab):
+    _, counted = O.shifted_nll(z, lab)
+    return O.shifted_cross_entropy_backward(z, lab) * max(int(counted.sum()), 1)
+
+
+def _wte_head_only_grads(p, tok, lab, n_head, n_layer):
+    loss, g = O.loss_and_grads(p, tok, lab, n_head, n_layer)
+    xf = O.final_hidden(p, tok, n_head, n_layer)
+    dlog = O.shifted_cross_entropy_backward(O.lm_head(xf, p["wte"]), lab)
+    g["wte"] = O.linear_backward(xf, p["wte"], dlog)[1]
+    return loss, g
+
+
+def _wte_embedding_only_grads(p, tok, lab, n_head, n_layer):
+    loss, g = O.loss_and_grads(p, tok, lab, n_head, n_layer)
+    xf = O.final_hidden(p, tok, n_head, n_layer)
+    dlog = O.shifted_cross_entropy_backward(O.lm_head(xf, p["wte"]), lab)
+    g["wte"] = g["wte"] - O.linear_backward(xf, p["wte"], dlog)[1]
+    return loss, g
+
+
+def _wpe_all_rows_grads(p, tok, lab, n_head, n_layer):
+    loss, g = O.loss_and_grads(p, tok, lab, n_head, n_layer)
+    g["wpe"] = g["wpe"] + g["wpe"][:1]  # position 0's gradient leaks into every position
+    return loss, g
+
+
 @pytest.mark.parametrize("check,mutant", [
     (check_layer_norm, _unbiased_ln), (check_layer_norm, _eps_outside_ln), (check_layer_norm, _no_beta_ln),
     (check_gelu, _cubic_sign_gelu), (check_gelu, _no_half_gelu), (check_gelu, O.gelu_erf),
@@ -668,6 +895,10 @@ def _no_temperature_sample(z, u, hist, T, k, p, pen):
     (check_sample, _double_penalty_sample), (check_sample, _inverted_penalty_sample),
     (check_sample, _ge_top_p_sample), (check_sample, _top_k_plus_one_sample),
     (check_sample, _no_temperature_sample),
+    (check_layer_norm_backward, _no_xhat_term_lnb), (check_gelu_backward, _first_term_gelu_back),
+    (check_linear_backward, _transposed_dw_linear_back), (check_attention_backward, _no_rowsum_attn_back),
+    (check_xent_backward, _unnormalised_xent_back), (check_model_grads, _wte_head_only_grads),
+    (check_model_grads, _wte_embedding_only_grads), (check_model_grads, _wpe_all_rows_grads),
 ])
 def test_pins_catch_planted_mistakes(check, mutant):
     try:
