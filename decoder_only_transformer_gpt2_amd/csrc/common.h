@@ -219,6 +219,33 @@ hipError_t sample(const float* logits, long ld, int B, int V, const int32_t* his
 size_t sample_workspace_bytes(int B, int V);
 int sample_max_vocab();
 
+// Backward pass (train.hip).
+// dst[c * ldd + r] = src[r * lds + c] (r < R, c < C) and 0 for R <= r < Rp; fp32 or bf16 each side.
+hipError_t transpose(const void* src, bool src_bf16, long lds, int R, int C, void* dst, bool dst_bf16, long ldd, int Rp,
+                     hipStream_t s);
+// out[c] = sum over rows of src[r * ld + c] (deterministic order); part holds colsum_blocks(R) * C floats.
+int colsum_blocks(int R);
+hipError_t colsum(const float* src, long ld, int R, int C, float* part, float* out, hipStream_t s);
+// LayerNorm backward on rows of x with output gradient dy (fp32 [M, d]): dx += the input gradient,
+// dgamma / dbeta = column sums (pg, pb hold ln_backward_blocks(M) * d floats each).
+int ln_backward_blocks(int M);
+hipError_t ln_backward(const float* x, const float* gamma, const float* dy, float* dx, int M, int d, float eps, float* pg,
+                       float* pb, float* dgamma, float* dbeta, hipStream_t s);
+// h = gelu(u) in the compute dtype; g *= gelu'(u) in place (fp32).
+hipError_t gelu_forward(const float* u, void* h, long n, bool bf16, int erf_form, hipStream_t s);
+hipError_t gelu_backward(const float* u, float* g, long n, int erf_form, hipStream_t s);
+// From fp32 logits [M, V] (row stride ld) and targets: cnt[0] = counted rows, nll[m], and the loss
+// gradient [M, Vp] (compute dtype; zero past V and on rows without target).
+hipError_t xent_grad(const float* logits, long ld, int M, int V, int Vp, const int32_t* tgt, int32_t* cnt, float* nll,
+                     void* dlogits, bool bf16, hipStream_t s);
+// Causal attention backward on qkv [B, T, 3, H, 64] and o [B, T, H, 64] (compute dtype) with the
+// output gradient dout fp32 [B, T, H * 64]: dqkv fp32 [B, T, 3 * H * 64]; lse, dvec: [B * H * T] scratch.
+hipError_t attention_backward(const void* qkv, const void* o, const float* dout, float* dqkv, float* lse, float* dvec,
+                              int B, int H, int T, bool bf16, hipStream_t s);
+// gwpe[t] = sum_b dx[b, t] (0 for t >= T, all n_ctx rows written); gwte[tok[m]] += dx[m].
+hipError_t embed_backward(const int32_t* tok, const float* dx, int B, int T, int n_ctx, int d, int V, float* gwte,
+                          float* gwpe, hipStream_t s);
+
 // dst[i] = i < n_src ? convert(src[i]) : 0 for i < n_dst (element types fp32 or bf16).
 hipError_t convert(const void* src, bool src_bf16, void* dst, bool dst_bf16, long n_src, long n_dst,
                    hipStream_t s);

@@ -357,6 +357,227 @@ gpt2_status check_cache(const gpt2_model* m, int B, const void* cache, size_t ca
     return GPT2_OK;
 }
 
+// ------------------------------------------------------------------------------ training
+// Gradient buffer: the fp32 gradient of source tensor i (in the order of gpt2_tensor_shape) starts
+// at grad_offset(i) bytes, every tensor 256-byte aligned, rows unpadded.
+size_t grad_offset(const gpt2_model* m, int i) {
+    size_t off = 0;
+    for (int j = 0; j < i; ++j) {
+        const TensorSlot& t = m->slots[j];
+        off = align_up(off + (size_t)t.rows * (t.matrix ? t.cols : 1) * 4, kAlign);
+    }
+    return off;
+}
+
+// Training workspace: the forward workspace first (so gpt2_check finds its flags), then the saved
+// activations of every layer, the head, and the buffers of the backward.
+struct TrainLayout {
+    WorkspaceLayout fw;
+    size_t layer0, per_layer;
+    size_t l_xin, l_xmid, l_a1, l_qkv, l_o, l_a2, l_u, l_h;  // inside one layer's block
+    size_t xfin, xf, logits, dx, dbuf, dbuf2, dact, dT, xT, wT, wteT, dlog, dlogT, part, lnpg, lnpb, lse, dvec, nll, cnt;
+    size_t total;
+    int64_t M, Mp, Mk, Vp, Vr, wide, rows_w, rows_dT, rows_x;
+};
+
+TrainLayout train_layout(const gpt2_model* m, int B, int T) {
+    const gpt2_config_t& c = m->cfg;
+    TrainLayout L{};
+    L.fw = ws_layout(m, B, T);
+    const size_t as = act_size(m);
+    const int64_t d = c.d_model, f = c.d_mlp;
+    L.M = (int64_t)B * T;
+    L.Mp = round_up(L.M, kRowPad);     // rows of a GEMM A operand
+    L.Mk = round_up(L.M, 64);          // reduction length of the weight-gradient GEMMs
+    L.Vp = round_up(c.n_vocab, 64);    // reduction length of the lm_head input gradient
+    L.Vr = round_up(c.n_vocab, kRowPad);
+    L.wide = std::max(3 * d, f);
+    L.rows_w = round_up(std::max(d, f), kRowPad);
+    L.rows_dT = round_up(L.wide, kRowPad);
+    L.rows_x = round_up(std::max(d, f), kRowPad);
+    size_t off = L.fw.total;
+    auto take = [&](size_t bytes) { size_t o = off; off = align_up(off + bytes, kAlign); return o; };
+    size_t lo = 0;
+    auto ltake = [&](size_t bytes) { size_t o = lo; lo = align_up(lo + bytes, kAlign); return o; };
+    L.l_xin = ltake(L.M * d * 4);
+    L.l_xmid = ltake(L.M * d * 4);
+    L.l_a1 = ltake(L.Mp * d * as);
+    L.l_qkv = ltake(L.Mp * 3 * d * as);
+    L.l_o = ltake(L.Mp * d * as);
+    L.l_a2 = ltake(L.Mp * d * as);
+    L.l_u = ltake(L.M * f * 4);
+    L.l_h = ltake(L.Mp * f * as);
+    L.per_layer = lo;
+    L.layer0 = take(L.per_layer * c.n_layer);
+    L.xfin = take(L.M * d * 4);
+    L.xf = take(L.Mp * d * as);
+    L.logits = take((size_t)L.M * c.n_vocab * 4);
+    L.dx = take(L.M * d * 4);
+    L.dbuf = take(L.M * L.wide * 4);
+    L.dbuf2 = take(L.M * L.wide * 4);
+    L.dact = take(L.Mp * L.wide * as);
+    L.dT = take(L.rows_dT * L.Mk * as);
+    L.xT = take(L.rows_x * L.Mk * as);
+    L.wT = take(L.rows_w * L.wide * as);
+    L.wteT = take(round_up(d, kRowPad) * L.Vp * as);
+    L.dlog = take(L.Mp * L.Vp * as);
+    L.dlogT = take(L.Vr * L.Mk * as);
+    L.part = take((size_t)gpt2k::colsum_blocks((int)L.M) * L.wide * 4);
+    L.lnpg = take((size_t)gpt2k::ln_backward_blocks((int)L.M) * d * 4);
+    L.lnpb = take((size_t)gpt2k::ln_backward_blocks((int)L.M) * d * 4);
+    L.lse = take((size_t)B * c.n_head * T * 4);
+    L.dvec = take((size_t)B * c.n_head * T * 4);
+    L.nll = take(L.M * 4);
+    L.cnt = take(4);
+    L.total = off;
+    return L;
+}
+
+// Forward keeping what the backward needs, then the mean shifted cross-entropy and the loss
+// gradient with respect to the logits (the fused GELU epilogue is split: u = a W^T + b is kept in
+// fp32 and h = gelu(u) rounded to the compute dtype, the values the fused epilogue produces).
+gpt2_status enqueue_train_forward(const gpt2_model* m, const int32_t* tokens, const int32_t* labels, int B, int T,
+                                  float* loss, char* ws, const TrainLayout& L, hipStream_t s) {
+    const gpt2_config_t& c = m->cfg;
+    const bool bf = is_bf16(m);
+    const int M = B * T, d = c.d_model, f = c.d_mlp, H = c.n_head;
+    const size_t as = act_size(m);
+    const int64_t qs[3] = {(int64_t)T * 3 * d, 64, 3 * d};
+    const int64_t os[3] = {(int64_t)T * d, 64, d};
+    auto lay = [&](int l, size_t o) { return ws + L.layer0 + (size_t)l * L.per_layer + o; };
+    GPT2_HIP(gpt2k::embed(tokens, wptr(m, 0), wptr(m, 1), reinterpret_cast<float*>(lay(0, L.l_xin)), M, T, 0, d,
+                          c.n_vocab, bf, reinterpret_cast<int32_t*>(ws + L.fw.flags), s));
+    for (int l = 0; l < c.n_layer; ++l) {
+        auto I = [&](int t) { return layer_idx(l, t); };
+        auto vecp = [&](int t) { return static_cast<const float*>(wptr(m, I(t))); };
+        float* xin = reinterpret_cast<float*>(lay(l, L.l_xin));
+        float* xmid = reinterpret_cast<float*>(lay(l, L.l_xmid));
+        float* xout = l + 1 < c.n_layer ? reinterpret_cast<float*>(lay(l + 1, L.l_xin)) : reinterpret_cast<float*>(ws + L.xfin);
+        char* a1 = lay(l, L.l_a1);
+        char* qkv = lay(l, L.l_qkv);
+        char* o = lay(l, L.l_o);
+        char* a2 = lay(l, L.l_a2);
+        float* u = reinterpret_cast<float*>(lay(l, L.l_u));
+        char* h = lay(l, L.l_h);
+        GPT2_HIP(gpt2k::layernorm(xin, vecp(LN1_W), vecp(LN1_B), a1, M, d, c.ln_eps, bf, s));
+        GPT2_HIP(linear(m, a1, I(ATTN_W), I(ATTN_B), qkv, M, 3 * d, d, 3 * d, gpt2k::EPI_BIAS, {}, s));
+        if (bf)
+            GPT2_HIP(gpt2k::attention_bf16(reinterpret_cast<const uint16_t*>(qkv), qs,
+                                           reinterpret_cast<const uint16_t*>(qkv + d * as), qs,
+                                           reinterpret_cast<const uint16_t*>(qkv + 2 * d * as), qs,
+                                           reinterpret_cast<uint16_t*>(o), os, B, H, T, s));
+        else
+            GPT2_HIP(gpt2k::attention_f32(reinterpret_cast<const float*>(qkv), qs,
+                                          reinterpret_cast<const float*>(qkv + d * as), qs,
+                                          reinterpret_cast<const float*>(qkv + 2 * d * as), qs,
+                                          reinterpret_cast<float*>(o), os, B, H, T, s));
+        GPT2_HIP(hipMemcpyAsync(xmid, xin, (size_t)M * d * 4, hipMemcpyDeviceToDevice, s));
+        GPT2_HIP(linear(m, o, I(APROJ_W), I(APROJ_B), xmid, M, d, d, d, gpt2k::EPI_BIAS_RESIDUAL, {}, s));
+        GPT2_HIP(gpt2k::layernorm(xmid, vecp(LN2_W), vecp(LN2_B), a2, M, d, c.ln_eps, bf, s));
+        GPT2_HIP(hipMemsetAsync(u, 0, (size_t)M * f * 4, s));
+        GPT2_HIP(linear(m, a2, I(FC_W), I(FC_B), u, M, f, d, f, gpt2k::EPI_BIAS_RESIDUAL, {}, s));
+        GPT2_HIP(gpt2k::gelu_forward(u, h, (long)M * f, bf, c.gelu == GPT2_GELU_ERF, s));
+        GPT2_HIP(hipMemcpyAsync(xout, xmid, (size_t)M * d * 4, hipMemcpyDeviceToDevice, s));
+        GPT2_HIP(linear(m, h, I(MPROJ_W), I(MPROJ_B), xout, M, d, f, d, gpt2k::EPI_BIAS_RESIDUAL, {}, s));
+    }
+    const int ln_f = 2 + c.n_layer * PER_LAYER;
+    GPT2_HIP(gpt2k::layernorm(reinterpret_cast<float*>(ws + L.xfin), static_cast<const float*>(wptr(m, ln_f)),
+                              static_cast<const float*>(wptr(m, ln_f + 1)), ws + L.xf, M, d, c.ln_eps, bf, s));
+    float* logits = reinterpret_cast<float*>(ws + L.logits);
+    GPT2_HIP(linear(m, ws + L.xf, 0, -1, logits, M, c.n_vocab, d, c.n_vocab, gpt2k::EPI_LOGITS, {}, s));
+    int32_t* tgt = reinterpret_cast<int32_t*>(ws + L.fw.tgt);
+    GPT2_HIP(gpt2k::xent_targets(labels ? labels : tokens, M, T, c.n_vocab, tgt,
+                                 reinterpret_cast<int32_t*>(ws + L.fw.flags), s));
+    float* nll = reinterpret_cast<float*>(ws + L.nll);
+    GPT2_HIP(gpt2k::xent_grad(logits, c.n_vocab, M, c.n_vocab, (int)L.Vp, tgt, reinterpret_cast<int32_t*>(ws + L.cnt), nll,
+                              ws + L.dlog, bf, s));
+    GPT2_HIP(gpt2k::xent_mean(nll, tgt, M, loss, s));
+    return GPT2_OK;
+}
+
+// The backward pass: every gradient into grads (fp32, grad_offset layout), the layers in reverse.
+// Each weight gradient dW = dY^T X and input gradient dX = dY W is a GEMM C = A B^T on copies
+// transposed here (A and B both K-contiguous, K padded with zeros).
+gpt2_status enqueue_backward(const gpt2_model* m, const int32_t* tokens, int B, int T, float* grads, char* ws,
+                             const TrainLayout& L, hipStream_t s) {
+    const gpt2_config_t& c = m->cfg;
+    const bool bf = is_bf16(m);
+    const int M = B * T, d = c.d_model, f = c.d_mlp, H = c.n_head, V = c.n_vocab;
+    const int Mp = (int)L.Mp, Mk = (int)L.Mk, Vp = (int)L.Vp;
+    auto lay = [&](int l, size_t o) { return ws + L.layer0 + (size_t)l * L.per_layer + o; };
+    auto G = [&](int i) { return grads + grad_offset(m, i) / 4; };
+    auto pad = [&](int64_t r) { return (int)round_up(r, kRowPad); };
+    float* dx = reinterpret_cast<float*>(ws + L.dx);
+    float* dbuf = reinterpret_cast<float*>(ws + L.dbuf);
+    float* dbuf2 = reinterpret_cast<float*>(ws + L.dbuf2);
+    char* dact = ws + L.dact;
+    char* dT = ws + L.dT;
+    char* xT = ws + L.xT;
+    char* wT = ws + L.wT;
+    float* part = reinterpret_cast<float*>(ws + L.part);
+    float* lnpg = reinterpret_cast<float*>(ws + L.lnpg);
+    float* lnpb = reinterpret_cast<float*>(ws + L.lnpb);
+    // C[Mg, Ng] (fp32, row stride ldc) = A[Mg, Kg] B[Ng, Kg]^T in the compute dtype
+    auto gemm_nt = [&](const void* A, int a_rows, const void* Bm, int b_rows, float* C, int Mg, int Ng, int Kg,
+                       long ldc) {
+        if (bf)
+            return gpt2k::gemm_bf16(static_cast<const uint16_t*>(A), static_cast<const uint16_t*>(Bm), nullptr, C, Mg, Ng,
+                                    Kg, ldc, gpt2k::EPI_LOGITS, 0, a_rows, b_rows, {}, s);
+        return gpt2k::gemm_f32(static_cast<const float*>(A), static_cast<const float*>(Bm), nullptr, C, Mg, Ng, Kg, ldc,
+                               gpt2k::EPI_LOGITS, 0, {}, s);
+    };
+    // dst (compute dtype) [C rows, ldd] = transpose of src [R, C] (row stride lds), zero for R <= r < Rp
+    auto tr = [&](const void* src, bool src_act, long lds, int R, int Cc, void* dst, long ldd, int Rp) {
+        return gpt2k::transpose(src, src_act && bf, lds, R, Cc, dst, bf, ldd, Rp, s);
+    };
+    // row-major fp32 [M, C] -> compute dtype [Mp, C] (rows past M zero)
+    auto to_act = [&](const float* src, int Cc, void* dst) {
+        return gpt2k::convert(src, false, dst, bf, (long)M * Cc, (long)Mp * Cc, s);
+    };
+    // the weight gradient and the input gradient of y = x W^T + b for output gradient dy (fp32 [M, n_out])
+    auto linear_back = [&](const float* dy, int n_out, const void* x_act, int n_in, int widx, float* dx_out) -> hipError_t {
+        hipError_t e;
+        if ((e = gpt2k::colsum(dy, n_out, M, n_out, part, G(widx + 1), s)) != hipSuccess) return e;
+        if ((e = tr(dy, false, n_out, M, n_out, dT, Mk, Mk)) != hipSuccess) return e;
+        if ((e = tr(x_act, true, n_in, M, n_in, xT, Mk, Mk)) != hipSuccess) return e;
+        if ((e = gemm_nt(dT, pad(n_out), xT, pad(n_in), G(widx), n_out, n_in, Mk, n_in)) != hipSuccess) return e;
+        if ((e = to_act(dy, n_out, dact)) != hipSuccess) return e;
+        if ((e = tr(wptr(m, widx), true, n_in, n_out, n_in, wT, n_out, n_out)) != hipSuccess) return e;
+        return gemm_nt(dact, Mp, wT, pad(n_in), dx_out, M, n_in, n_out, n_in);
+    };
+    // lm_head: dxf = dlogits wte, dwte (head part) = dlogits^T xf
+    GPT2_HIP(tr(wptr(m, 0), true, d, V, d, ws + L.wteT, Vp, Vp));
+    GPT2_HIP(gemm_nt(ws + L.dlog, Mp, ws + L.wteT, pad(d), dbuf, M, d, Vp, d));
+    GPT2_HIP(tr(ws + L.dlog, true, Vp, M, Vp, ws + L.dlogT, Mk, Mk));
+    GPT2_HIP(tr(ws + L.xf, true, d, M, d, xT, Mk, Mk));
+    GPT2_HIP(gemm_nt(ws + L.dlogT, (int)L.Vr, xT, pad(d), G(0), V, d, Mk, d));
+    GPT2_HIP(hipMemsetAsync(dx, 0, (size_t)M * d * 4, s));
+    const int ln_f = 2 + c.n_layer * PER_LAYER;
+    GPT2_HIP(gpt2k::ln_backward(reinterpret_cast<float*>(ws + L.xfin), static_cast<const float*>(wptr(m, ln_f)), dbuf, dx,
+                                M, d, c.ln_eps, lnpg, lnpb, G(ln_f), G(ln_f + 1), s));
+    for (int l = c.n_layer - 1; l >= 0; --l) {
+        auto I = [&](int t) { return layer_idx(l, t); };
+        auto vecp = [&](int t) { return static_cast<const float*>(wptr(m, I(t))); };
+        // MLP projection, GELU, c_fc, ln_2
+        GPT2_HIP(linear_back(dx, d, lay(l, L.l_h), f, I(MPROJ_W), dbuf));
+        const float* u = reinterpret_cast<const float*>(lay(l, L.l_u));
+        GPT2_HIP(gpt2k::gelu_backward(u, dbuf, (long)M * f, c.gelu == GPT2_GELU_ERF, s));
+        GPT2_HIP(linear_back(dbuf, f, lay(l, L.l_a2), d, I(FC_W), dbuf2));
+        GPT2_HIP(gpt2k::ln_backward(reinterpret_cast<const float*>(lay(l, L.l_xmid)), vecp(LN2_W), dbuf2, dx, M, d,
+                                    c.ln_eps, lnpg, lnpb, G(I(LN2_W)), G(I(LN2_B)), s));
+        // attention projection, attention, c_attn, ln_1
+        GPT2_HIP(linear_back(dx, d, lay(l, L.l_o), d, I(APROJ_W), dbuf));
+        GPT2_HIP(gpt2k::attention_backward(lay(l, L.l_qkv), lay(l, L.l_o), dbuf, dbuf2,
+                                           reinterpret_cast<float*>(ws + L.lse), reinterpret_cast<float*>(ws + L.dvec), B,
+                                           H, T, bf, s));
+        GPT2_HIP(linear_back(dbuf2, 3 * d, lay(l, L.l_a1), d, I(ATTN_W), dbuf));
+        GPT2_HIP(gpt2k::ln_backward(reinterpret_cast<const float*>(lay(l, L.l_xin)), vecp(LN1_W), dbuf, dx, M, d,
+                                    c.ln_eps, lnpg, lnpb, G(I(LN1_W)), G(I(LN1_B)), s));
+    }
+    GPT2_HIP(gpt2k::embed_backward(tokens, dx, B, T, c.n_ctx, d, V, G(0), G(1), s));
+    return GPT2_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -606,6 +827,32 @@ gpt2_status gpt2_sample(const float* logits, int64_t ld, int32_t B, int32_t V, c
     GPT2_HIP(gpt2k::sample(logits, ld, B, V, n_hist > 0 ? hist : nullptr, hist_ld, n_hist, temperature, top_k, top_p,
                            penalty, u, out, n_kept, ws, ws_bytes, s));
     return GPT2_OK;
+}
+
+size_t gpt2_grad_bytes(const gpt2_model* m) { return m ? grad_offset(m, (int)m->slots.size()) : 0; }
+
+size_t gpt2_grad_offset(const gpt2_model* m, int32_t i) {
+    if (!m || i < 0 || i >= (int)m->slots.size()) return (size_t)-1;
+    return grad_offset(m, i);
+}
+
+size_t gpt2_train_workspace_bytes(const gpt2_model* m, int32_t B, int32_t T) {
+    if (!m || B < 1 || T < 2 || T > m->cfg.n_ctx) return 0;
+    return train_layout(m, B, T).total;
+}
+
+gpt2_status gpt2_backward(const gpt2_model* m, const int32_t* tokens, const int32_t* labels, int32_t B, int32_t T,
+                          float* grads, size_t grads_bytes, float* loss, void* ws, size_t ws_bytes, hipStream_t s) {
+    if (!m || !tokens || !grads || !loss || !ws) return GPT2_EINVAL;
+    if (!m->loaded) return GPT2_ESTATE;
+    if (B < 1 || T < 2 || T > m->cfg.n_ctx || (int64_t)B * T > (int64_t)1 << 20) return GPT2_ESHAPE;
+    if (reinterpret_cast<uintptr_t>(ws) % kAlign || reinterpret_cast<uintptr_t>(grads) % kAlign) return GPT2_EINVAL;
+    const TrainLayout L = train_layout(m, B, T);
+    if (ws_bytes < L.total || grads_bytes < grad_offset(m, (int)m->slots.size())) return GPT2_EWORKSPACE;
+    char* w = static_cast<char*>(ws);
+    gpt2_status st = enqueue_train_forward(m, tokens, labels, B, T, loss, w, L, s);
+    if (st != GPT2_OK) return st;
+    return enqueue_backward(m, tokens, B, T, grads, w, L, s);
 }
 
 const char* gpt2_strerror(gpt2_status s) {

@@ -1,0 +1,477 @@
+// Kernels of the backward pass of the shifted next-token cross-entropy ("从零手写GPT-2：PyTorch实现
+// Transformer解码器核心模块" §4: the loss and loss.backward(); §2.2: the tied wte receives both the
+// lm_head gradient and the embedding gradient). The matrix products of the backward are the
+// library's GEMM (C = A B^T, both operands K-contiguous) on transposed copies made here.
+#include "common.h"
+
+namespace gpt2k {
+namespace {
+
+template <bool BF>
+struct Act;
+template <>
+struct Act<true> {
+    using T = uint16_t;
+    static __device__ __forceinline__ float load(const T* p, long i) { return bf16_bits_to_f32(p[i]); }
+    static __device__ __forceinline__ void store(T* p, long i, float v) { p[i] = f32_to_bf16_bits(v); }
+};
+template <>
+struct Act<false> {
+    using T = float;
+    static __device__ __forceinline__ float load(const T* p, long i) { return p[i]; }
+    static __device__ __forceinline__ void store(T* p, long i, float v) { p[i] = v; }
+};
+
+// ------------------------------------------------------------------------------ transpose
+// dst[c * ldd + r] = src[r * lds + c] for r < R, c < C, and 0 for R <= r < Rp (64x64 tiles via LDS).
+template <bool SRC_BF, bool DST_BF>
+__global__ void __launch_bounds__(256) transpose_kernel(const void* __restrict__ src, long lds, int R, int C,
+                                                        void* __restrict__ dst, long ldd, int Rp) {
+    __shared__ float tile[64][65];
+    const int c0 = blockIdx.x * 64, r0 = blockIdx.y * 64, t = threadIdx.x;
+    const auto* s = static_cast<const typename Act<SRC_BF>::T*>(src);
+    auto* d = static_cast<typename Act<DST_BF>::T*>(dst);
+    for (int e = t; e < 64 * 64; e += 256) {
+        const int rr = e >> 6, cc = e & 63, r = r0 + rr, c = c0 + cc;
+        tile[rr][cc] = (r < R && c < C) ? Act<SRC_BF>::load(s, (long)r * lds + c) : 0.f;
+    }
+    __syncthreads();
+    for (int e = t; e < 64 * 64; e += 256) {
+        const int cc = e >> 6, rr = e & 63, r = r0 + rr, c = c0 + cc;
+        if (c < C && r < Rp) Act<DST_BF>::store(d, (long)c * ldd + r, tile[rr][cc]);
+    }
+}
+
+// ------------------------------------------------------------------------------ column sums
+// part[b][c] = sum of src[r][c] over rows r of block b (256 rows), in row order.
+__global__ void __launch_bounds__(256) colsum_partial_kernel(const float* __restrict__ src, long ld, int R, int C,
+                                                             float* __restrict__ part) {
+    const int c = blockIdx.x * 256 + threadIdx.x, b = blockIdx.y;
+    if (c >= C) return;
+    const int r1 = min(R, (b + 1) * 256);
+    float acc = 0.f;
+    for (int r = b * 256; r < r1; ++r) acc += src[(long)r * ld + c];
+    part[(long)b * C + c] = acc;
+}
+// out[c] = sum over b < nb of part[b][c], in block order.
+__global__ void __launch_bounds__(256) colsum_reduce_kernel(const float* __restrict__ part, int nb, int C,
+                                                            float* __restrict__ out) {
+    const int c = blockIdx.x * 256 + threadIdx.x;
+    if (c >= C) return;
+    float acc = 0.f;
+    for (int b = 0; b < nb; ++b) acc += part[(long)b * C + c];
+    out[c] = acc;
+}
+
+// ------------------------------------------------------------------------------ LayerNorm backward
+// One wavefront per block of kLnRows rows. For each row: xhat = (x - mean) * rstd, g = dy * gamma,
+// dx += rstd * (g - mean(g) - xhat * mean(g * xhat)); the block's sums of dy * xhat and dy per
+// column go to pg / pb [block][d] (each lane owns columns lane + 64 j, so the sums run in row order).
+constexpr int kLnRows = 16;
+__global__ void __launch_bounds__(64) ln_backward_kernel(const float* __restrict__ x, const float* __restrict__ gamma,
+                                                         const float* __restrict__ dy, float* __restrict__ dx, int M,
+                                                         int d, float eps, float* __restrict__ pg,
+                                                         float* __restrict__ pb) {
+    extern __shared__ float sacc[];  // [2][d]
+    const int lane = threadIdx.x, blk = blockIdx.x;
+    for (int c = lane; c < 2 * d; c += 64) sacc[c] = 0.f;
+    const float inv_d = 1.0f / (float)d;
+    for (int rr = 0; rr < kLnRows; ++rr) {
+        const int m = blk * kLnRows + rr;
+        if (m >= M) break;
+        const float* xr = x + (long)m * d;
+        const float* gr = dy + (long)m * d;
+        float s = 0.f;
+        for (int c = lane; c < d; c += 64) s += xr[c];
+        const float mean = wave_sum(s) * inv_d;
+        float q = 0.f;
+        for (int c = lane; c < d; c += 64) {
+            const float a = xr[c] - mean;
+            q += a * a;
+        }
+        const float rstd = 1.0f / sqrtf(wave_sum(q) * inv_d + eps);
+        float sg = 0.f, sgx = 0.f;
+        for (int c = lane; c < d; c += 64) {
+            const float xh = (xr[c] - mean) * rstd, g = gr[c] * gamma[c];
+            sg += g;
+            sgx += g * xh;
+        }
+        const float mg = wave_sum(sg) * inv_d, mgx = wave_sum(sgx) * inv_d;
+        for (int c = lane; c < d; c += 64) {
+            const float xh = (xr[c] - mean) * rstd, g = gr[c] * gamma[c];
+            dx[(long)m * d + c] += rstd * (g - mg - xh * mgx);
+            sacc[c] += gr[c] * xh;
+            sacc[d + c] += gr[c];
+        }
+    }
+    for (int c = lane; c < d; c += 64) {
+        pg[(long)blk * d + c] = sacc[c];
+        pb[(long)blk * d + c] = sacc[d + c];
+    }
+}
+
+// ------------------------------------------------------------------------------ GELU
+__device__ __forceinline__ float gelu_tanh_grad(float x) {
+    const float c = 0.7978845608028654f;  // sqrt(2/pi)
+    const float t = tanhf(c * (x + 0.044715f * x * x * x));
+    return 0.5f * (1.0f + t) + 0.5f * x * (1.0f - t * t) * c * (1.0f + 3.0f * 0.044715f * x * x);
+}
+__device__ __forceinline__ float gelu_erf_grad(float x) {
+    return 0.5f * (1.0f + erff(x * 0.7071067811865476f)) + x * 0.3989422804014327f * expf(-0.5f * x * x);
+}
+// h = gelu(u) in the compute dtype (the values the fused forward epilogue produces from the same u)
+template <bool BF>
+__global__ void gelu_forward_kernel(const float* __restrict__ u, void* __restrict__ h, long n, int erf_form) {
+    const long i = (long)blockIdx.x * 256 + threadIdx.x;
+    if (i >= n) return;
+    const float x = u[i];
+    Act<BF>::store(static_cast<typename Act<BF>::T*>(h), i, erf_form ? gelu_erf_f32(x) : gelu_tanh_fast(x));
+}
+// g = g * gelu'(u), in place
+__global__ void gelu_backward_kernel(const float* __restrict__ u, float* __restrict__ g, long n, int erf_form) {
+    const long i = (long)blockIdx.x * 256 + threadIdx.x;
+    if (i >= n) return;
+    g[i] *= erf_form ? gelu_erf_grad(u[i]) : gelu_tanh_grad(u[i]);
+}
+
+// ------------------------------------------------------------------------------ cross-entropy
+// cnt[0] = number of rows with tgt >= 0.
+__global__ void __launch_bounds__(256) count_targets_kernel(const int32_t* __restrict__ tgt, int M, int32_t* cnt) {
+    __shared__ int part[4];
+    int n = 0;
+    for (int m = threadIdx.x; m < M; m += 256) n += tgt[m] >= 0;
+    for (int o = 32; o; o >>= 1) n += __shfl_xor(n, o);
+    if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = n;
+    __syncthreads();
+    if (threadIdx.x == 0) cnt[0] = part[0] + part[1] + part[2] + part[3];
+}
+
+// One workgroup per row m of the fp32 logits: lse = log sum exp, nll[m] = lse - z[tgt] (0 when the
+// row has no target), and the loss gradient row (exp(z - lse) - [v = tgt]) / n_counted in the
+// compute dtype, zero for rows without target and for the padding columns V <= v < Vp.
+template <bool BF>
+__global__ void __launch_bounds__(256) xent_grad_kernel(const float* __restrict__ logits, long ld, int V, int Vp,
+                                                        const int32_t* __restrict__ tgt, const int32_t* __restrict__ cnt,
+                                                        float* __restrict__ nll, void* __restrict__ dlogits) {
+    __shared__ float sm[4], ss[4];
+    const int m = blockIdx.x, t = threadIdx.x;
+    const float* z = logits + (long)m * ld;
+    const int y = tgt[m];
+    auto* out = static_cast<typename Act<BF>::T*>(dlogits) + (long)m * Vp;
+    if (y < 0) {
+        for (int v = t; v < Vp; v += 256) Act<BF>::store(out, v, 0.f);
+        if (t == 0) nll[m] = 0.f;
+        return;
+    }
+    const float L2E = 1.4426950408889634f;
+    float mx = -INFINITY, s = 0.f;  // running maximum of z * log2(e) and sum of 2^(.. - max)
+    for (int v = t; v < V; v += 256) {
+        const float a = z[v] * L2E;
+        if (a > mx) {
+            s = s * __builtin_amdgcn_exp2f(mx - a) + 1.f;
+            mx = a;
+        } else {
+            s += __builtin_amdgcn_exp2f(a - mx);
+        }
+    }
+    lse_merge(mx, s, __shfl_xor(mx, 32), __shfl_xor(s, 32));
+    lse_merge(mx, s, __shfl_xor(mx, 16), __shfl_xor(s, 16));
+    lse_merge(mx, s, __shfl_xor(mx, 8), __shfl_xor(s, 8));
+    lse_merge(mx, s, __shfl_xor(mx, 4), __shfl_xor(s, 4));
+    lse_merge(mx, s, __shfl_xor(mx, 2), __shfl_xor(s, 2));
+    lse_merge(mx, s, __shfl_xor(mx, 1), __shfl_xor(s, 1));
+    if ((t & 63) == 0) {
+        sm[t >> 6] = mx;
+        ss[t >> 6] = s;
+    }
+    __syncthreads();
+    mx = sm[0];
+    s = ss[0];
+    for (int i = 1; i < 4; ++i) lse_merge(mx, s, sm[i], ss[i]);
+    const float lse2 = mx + __log2f(s);  // log2 of sum 2^(z log2 e)
+    if (t == 0) nll[m] = lse2 / L2E - z[y];
+    const float inv_n = 1.0f / (float)max(cnt[0], 1);
+    for (int v = t; v < Vp; v += 256) {
+        float g = 0.f;
+        if (v < V) g = (__builtin_amdgcn_exp2f(z[v] * L2E - lse2) - (v == y ? 1.f : 0.f)) * inv_n;
+        Act<BF>::store(out, v, g);
+    }
+}
+
+// ------------------------------------------------------------------------------ attention backward
+// Causal attention of head (b, h) on qkv [B, T, 3, H, 64] (compute dtype), output o [B, T, H, 64],
+// output gradient dout fp32 [B, T, H*64]. Two threads per row, each owning 32 of the 64 dimensions;
+// a dot product is two half sums joined by a lane swap. Softmax in base 2: p = 2^(s c2 - lse2)
+// with c2 = log2(e) / 8. Gradients (fp32) go to dqkv [B, T, 3 * H * 64].
+constexpr int AB_ROWS = 64, AB_T = 2 * AB_ROWS;
+
+__device__ __forceinline__ float swap_pair(float v) {
+    return __builtin_bit_cast(float, dpp_mov<0xB1>(__builtin_bit_cast(uint32_t, v)));
+}
+
+template <bool BF>
+__device__ __forceinline__ void load_half(const typename Act<BF>::T* p, float (&r)[32]) {
+#pragma unroll
+    for (int c = 0; c < 32; ++c) r[c] = Act<BF>::load(p, c);
+}
+
+// Pass over the keys j <= i of query i: lse2[i], D[i] = dout_i . o_i, dq_i.
+template <bool BF>
+__global__ void __launch_bounds__(AB_T) attn_bwd_q_kernel(const void* __restrict__ qkv_, const void* __restrict__ o_,
+                                                          const float* __restrict__ dout, float* __restrict__ dqkv,
+                                                          float* __restrict__ lse_out, float* __restrict__ d_out, int H,
+                                                          int T) {
+    using AT = typename Act<BF>::T;
+    __shared__ float sk[AB_ROWS][64];
+    __shared__ float sv[AB_ROWS][64];
+    const AT* qkv = static_cast<const AT*>(qkv_);
+    const AT* o = static_cast<const AT*>(o_);
+    const int bh = blockIdx.y, b = bh / H, h = bh % H, qb = blockIdx.x;
+    const int r = threadIdx.x >> 1, half = threadIdx.x & 1, i = qb * AB_ROWS + r;
+    const int d = H * 64;
+    const float c2 = 0.125f * 1.4426950408889634f;
+    const bool valid = i < T;
+    const long row = (long)b * T + (valid ? i : 0);
+    float q[32], g[32], dq[32];
+    load_half<BF>(qkv + row * 3 * d + h * 64 + half * 32, q);
+#pragma unroll
+    for (int c = 0; c < 32; ++c) g[c] = dout[row * d + h * 64 + half * 32 + c];
+    float dd = 0.f;
+    {
+        float oc[32];
+        load_half<BF>(o + row * d + h * 64 + half * 32, oc);
+#pragma unroll
+        for (int c = 0; c < 32; ++c) dd += g[c] * oc[c];
+    }
+    dd += swap_pair(dd);
+    const int last = min(T - 1, qb * AB_ROWS + AB_ROWS - 1);
+    const int n_tiles = last / AB_ROWS + 1;
+    // pass 1: the row's log-sum-exp (base 2)
+    float mx = -INFINITY, s = 0.f;
+    for (int kt = 0; kt < n_tiles; ++kt) {
+        __syncthreads();
+        for (int e = threadIdx.x; e < AB_ROWS * 64; e += AB_T) {
+            const int j = kt * AB_ROWS + (e >> 6), c = e & 63;
+            sk[e >> 6][c] = j < T ? Act<BF>::load(qkv, ((long)b * T + j) * 3 * d + d + h * 64 + c) : 0.f;
+        }
+        __syncthreads();
+        const int jn = min(AB_ROWS, i - kt * AB_ROWS + 1);  // keys j <= i in this tile
+        for (int jj = 0; jj < AB_ROWS; ++jj) {
+            float a = 0.f;
+#pragma unroll
+            for (int c = 0; c < 32; ++c) a += q[c] * sk[jj][half * 32 + c];
+            a = (a + swap_pair(a)) * c2;
+            if (jj < jn) {
+                if (a > mx) {
+                    s = s * __builtin_amdgcn_exp2f(mx - a) + 1.f;
+                    mx = a;
+                } else {
+                    s += __builtin_amdgcn_exp2f(a - mx);
+                }
+            }
+        }
+    }
+    const float lse2 = mx + __log2f(s);
+    // pass 2: dq = sum_j p_ij (dout_i . v_j - D_i) k_j / 8
+#pragma unroll
+    for (int c = 0; c < 32; ++c) dq[c] = 0.f;
+    for (int kt = 0; kt < n_tiles; ++kt) {
+        __syncthreads();
+        for (int e = threadIdx.x; e < AB_ROWS * 64; e += AB_T) {
+            const int j = kt * AB_ROWS + (e >> 6), c = e & 63;
+            const long base = ((long)b * T + j) * 3 * d + h * 64 + c;
+            sk[e >> 6][c] = j < T ? Act<BF>::load(qkv, base + d) : 0.f;
+            sv[e >> 6][c] = j < T ? Act<BF>::load(qkv, base + 2 * d) : 0.f;
+        }
+        __syncthreads();
+        const int jn = min(AB_ROWS, i - kt * AB_ROWS + 1);
+        for (int jj = 0; jj < AB_ROWS; ++jj) {
+            float a = 0.f, dp = 0.f;
+#pragma unroll
+            for (int c = 0; c < 32; ++c) {
+                a += q[c] * sk[jj][half * 32 + c];
+                dp += g[c] * sv[jj][half * 32 + c];
+            }
+            a = (a + swap_pair(a)) * c2;
+            dp += swap_pair(dp);
+            const float p = jj < jn ? __builtin_amdgcn_exp2f(a - lse2) : 0.f;
+            const float ds = p * (dp - dd);
+#pragma unroll
+            for (int c = 0; c < 32; ++c) dq[c] += ds * sk[jj][half * 32 + c];
+        }
+    }
+    if (valid) {
+#pragma unroll
+        for (int c = 0; c < 32; ++c) dqkv[row * 3 * d + h * 64 + half * 32 + c] = dq[c] * 0.125f;
+        if (half == 0) {
+            lse_out[(long)bh * T + i] = lse2;
+            d_out[(long)bh * T + i] = dd;
+        }
+    }
+}
+
+// Pass over the queries i >= j of key j: dk_j, dv_j.
+template <bool BF>
+__global__ void __launch_bounds__(AB_T) attn_bwd_kv_kernel(const void* __restrict__ qkv_, const float* __restrict__ dout,
+                                                           const float* __restrict__ lse, const float* __restrict__ dvec,
+                                                           float* __restrict__ dqkv, int H, int T) {
+    using AT = typename Act<BF>::T;
+    __shared__ float sq[AB_ROWS][64];
+    __shared__ float sg[AB_ROWS][64];
+    __shared__ float sl[AB_ROWS], sd[AB_ROWS];
+    const AT* qkv = static_cast<const AT*>(qkv_);
+    const int bh = blockIdx.y, b = bh / H, h = bh % H, kb = blockIdx.x;
+    const int r = threadIdx.x >> 1, half = threadIdx.x & 1, j = kb * AB_ROWS + r;
+    const int d = H * 64;
+    const float c2 = 0.125f * 1.4426950408889634f;
+    const bool valid = j < T;
+    const long row = (long)b * T + (valid ? j : 0);
+    float k[32], v[32], dk[32], dv[32];
+    load_half<BF>(qkv + row * 3 * d + d + h * 64 + half * 32, k);
+    load_half<BF>(qkv + row * 3 * d + 2 * d + h * 64 + half * 32, v);
+#pragma unroll
+    for (int c = 0; c < 32; ++c) dk[c] = dv[c] = 0.f;
+    const int n_tiles = (T + AB_ROWS - 1) / AB_ROWS;
+    for (int qt = kb; qt < n_tiles; ++qt) {
+        __syncthreads();
+        for (int e = threadIdx.x; e < AB_ROWS * 64; e += AB_T) {
+            const int i = qt * AB_ROWS + (e >> 6), c = e & 63;
+            const long ri = (long)b * T + i;
+            sq[e >> 6][c] = i < T ? Act<BF>::load(qkv, ri * 3 * d + h * 64 + c) : 0.f;
+            sg[e >> 6][c] = i < T ? dout[ri * d + h * 64 + c] : 0.f;
+        }
+        if (threadIdx.x < AB_ROWS) {
+            const int i = qt * AB_ROWS + threadIdx.x;
+            sl[threadIdx.x] = i < T ? lse[(long)bh * T + i] : 0.f;
+            sd[threadIdx.x] = i < T ? dvec[(long)bh * T + i] : 0.f;
+        }
+        __syncthreads();
+        for (int ii = 0; ii < AB_ROWS; ++ii) {
+            const int i = qt * AB_ROWS + ii;
+            float a = 0.f, dp = 0.f;
+#pragma unroll
+            for (int c = 0; c < 32; ++c) {
+                a += sq[ii][half * 32 + c] * k[c];
+                dp += sg[ii][half * 32 + c] * v[c];
+            }
+            a = (a + swap_pair(a)) * c2;
+            dp += swap_pair(dp);
+            const float p = (i >= j && i < T) ? __builtin_amdgcn_exp2f(a - sl[ii]) : 0.f;
+            const float ds = p * (dp - sd[ii]);
+#pragma unroll
+            for (int c = 0; c < 32; ++c) {
+                dv[c] += p * sg[ii][half * 32 + c];
+                dk[c] += ds * sq[ii][half * 32 + c];
+            }
+        }
+    }
+    if (valid) {
+#pragma unroll
+        for (int c = 0; c < 32; ++c) {
+            dqkv[row * 3 * d + d + h * 64 + half * 32 + c] = dk[c] * 0.125f;
+            dqkv[row * 3 * d + 2 * d + h * 64 + half * 32 + c] = dv[c];
+        }
+    }
+}
+
+// ------------------------------------------------------------------------------ embedding backward
+// gwpe[t] = sum over b of dx[b, t] for t < T, 0 for T <= t < n_ctx (batch order).
+__global__ void wpe_grad_kernel(const float* __restrict__ dx, int B, int T, int n_ctx, int d, float* __restrict__ gwpe) {
+    const long e = (long)blockIdx.x * 256 + threadIdx.x;
+    if (e >= (long)n_ctx * d) return;
+    const int t = (int)(e / d), c = (int)(e % d);
+    float acc = 0.f;
+    if (t < T)
+        for (int b = 0; b < B; ++b) acc += dx[((long)b * T + t) * d + c];
+    gwpe[e] = acc;
+}
+// gwte[tok[m]] += dx[m] (float atomics: tokens that repeat add in an unspecified order).
+__global__ void wte_grad_kernel(const int32_t* __restrict__ tok, const float* __restrict__ dx, int M, int d, int V,
+                                float* __restrict__ gwte) {
+    const long e = (long)blockIdx.x * 256 + threadIdx.x;
+    if (e >= (long)M * d) return;
+    const int m = (int)(e / d), c = (int)(e % d), id = tok[m];
+    if (id >= 0 && id < V) atomicAdd(gwte + (long)id * d + c, dx[e]);
+}
+
+}  // namespace
+
+hipError_t transpose(const void* src, bool src_bf16, long lds, int R, int C, void* dst, bool dst_bf16, long ldd, int Rp,
+                     hipStream_t s) {
+    const dim3 grid((C + 63) / 64, (Rp + 63) / 64), block(256);
+    if (src_bf16 && dst_bf16)
+        transpose_kernel<true, true><<<grid, block, 0, s>>>(src, lds, R, C, dst, ldd, Rp);
+    else if (src_bf16)
+        transpose_kernel<true, false><<<grid, block, 0, s>>>(src, lds, R, C, dst, ldd, Rp);
+    else if (dst_bf16)
+        transpose_kernel<false, true><<<grid, block, 0, s>>>(src, lds, R, C, dst, ldd, Rp);
+    else
+        transpose_kernel<false, false><<<grid, block, 0, s>>>(src, lds, R, C, dst, ldd, Rp);
+    return hipGetLastError();
+}
+
+int colsum_blocks(int R) { return (R + 255) / 256; }
+
+hipError_t colsum(const float* src, long ld, int R, int C, float* part, float* out, hipStream_t s) {
+    const int nb = colsum_blocks(R);
+    colsum_partial_kernel<<<dim3((C + 255) / 256, nb), dim3(256), 0, s>>>(src, ld, R, C, part);
+    colsum_reduce_kernel<<<dim3((C + 255) / 256), dim3(256), 0, s>>>(part, nb, C, out);
+    return hipGetLastError();
+}
+
+int ln_backward_blocks(int M) { return (M + kLnRows - 1) / kLnRows; }
+
+hipError_t ln_backward(const float* x, const float* gamma, const float* dy, float* dx, int M, int d, float eps, float* pg,
+                       float* pb, float* dgamma, float* dbeta, hipStream_t s) {
+    const int nb = ln_backward_blocks(M);
+    ln_backward_kernel<<<dim3(nb), dim3(64), 2 * d * sizeof(float), s>>>(x, gamma, dy, dx, M, d, eps, pg, pb);
+    colsum_reduce_kernel<<<dim3((d + 255) / 256), dim3(256), 0, s>>>(pg, nb, d, dgamma);
+    colsum_reduce_kernel<<<dim3((d + 255) / 256), dim3(256), 0, s>>>(pb, nb, d, dbeta);
+    return hipGetLastError();
+}
+
+hipError_t gelu_forward(const float* u, void* h, long n, bool bf16, int erf_form, hipStream_t s) {
+    const dim3 grid((unsigned)((n + 255) / 256)), block(256);
+    if (bf16)
+        gelu_forward_kernel<true><<<grid, block, 0, s>>>(u, h, n, erf_form);
+    else
+        gelu_forward_kernel<false><<<grid, block, 0, s>>>(u, h, n, erf_form);
+    return hipGetLastError();
+}
+
+hipError_t gelu_backward(const float* u, float* g, long n, int erf_form, hipStream_t s) {
+    gelu_backward_kernel<<<dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s>>>(u, g, n, erf_form);
+    return hipGetLastError();
+}
+
+hipError_t xent_grad(const float* logits, long ld, int M, int V, int Vp, const int32_t* tgt, int32_t* cnt, float* nll,
+                     void* dlogits, bool bf16, hipStream_t s) {
+    count_targets_kernel<<<dim3(1), dim3(256), 0, s>>>(tgt, M, cnt);
+    if (bf16)
+        xent_grad_kernel<true><<<dim3(M), dim3(256), 0, s>>>(logits, ld, V, Vp, tgt, cnt, nll, dlogits);
+    else
+        xent_grad_kernel<false><<<dim3(M), dim3(256), 0, s>>>(logits, ld, V, Vp, tgt, cnt, nll, dlogits);
+    return hipGetLastError();
+}
+
+hipError_t attention_backward(const void* qkv, const void* o, const float* dout, float* dqkv, float* lse, float* dvec,
+                              int B, int H, int T, bool bf16, hipStream_t s) {
+    const dim3 grid((T + AB_ROWS - 1) / AB_ROWS, B * H), block(AB_T);
+    if (bf16) {
+        attn_bwd_q_kernel<true><<<grid, block, 0, s>>>(qkv, o, dout, dqkv, lse, dvec, H, T);
+        attn_bwd_kv_kernel<true><<<grid, block, 0, s>>>(qkv, dout, lse, dvec, dqkv, H, T);
+    } else {
+        attn_bwd_q_kernel<false><<<grid, block, 0, s>>>(qkv, o, dout, dqkv, lse, dvec, H, T);
+        attn_bwd_kv_kernel<false><<<grid, block, 0, s>>>(qkv, dout, lse, dvec, dqkv, H, T);
+    }
+    return hipGetLastError();
+}
+
+hipError_t embed_backward(const int32_t* tok, const float* dx, int B, int T, int n_ctx, int d, int V, float* gwte,
+                          float* gwpe, hipStream_t s) {
+    wpe_grad_kernel<<<dim3((unsigned)(((long)n_ctx * d + 255) / 256)), dim3(256), 0, s>>>(dx, B, T, n_ctx, d, gwpe);
+    wte_grad_kernel<<<dim3((unsigned)(((long)B * T * d + 255) / 256)), dim3(256), 0, s>>>(tok, dx, B * T, d, V, gwte);
+    return hipGetLastError();
+}
+
+}  // namespace gpt2k

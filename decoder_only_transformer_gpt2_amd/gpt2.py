@@ -12,6 +12,7 @@ import ctypes
 import os
 from dataclasses import dataclass
 
+import numpy as np
 import torch
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -53,6 +54,10 @@ SIGNATURES = {
     "gpt2_linear": (_I32, [_P, _P, _P, _P, _I32, _I32, _I32, _I64, _I32, _I32, _I32, _P]),
     "gpt2_sample": (_I32, [_P, _I64, _I32, _I32, _P, _I64, _I32, _F, _I32, _F, _F, _P, _P, _P, _P, _SZ, _P]),
     "gpt2_sample_workspace_bytes": (_SZ, [_I32, _I32]),
+    "gpt2_grad_bytes": (_SZ, [_P]),
+    "gpt2_grad_offset": (_SZ, [_P, _I32]),
+    "gpt2_train_workspace_bytes": (_SZ, [_P, _I32, _I32]),
+    "gpt2_backward": (_I32, [_P, _P, _P, _I32, _I32, _P, _SZ, _P, _P, _SZ, _P]),
     "gpt2_strerror": (ctypes.c_char_p, [_I32]),
 }
 
@@ -337,6 +342,43 @@ class GPT2:
                                  nxt=False if do_sample else nxt)
                 pick(i, nxt)
         return out
+
+    def grad_buffer(self) -> torch.Tensor:
+        """A zeroed fp32 device buffer for the gradients (gpt2_grad_bytes, 256-byte aligned)."""
+        return _aligned_empty(lib().gpt2_grad_bytes(self._h), self.device).zero_()
+
+    def grad_views(self, buf: torch.Tensor, names: list[str] | None = None) -> list[torch.Tensor] | dict:
+        """fp32 views of each tensor's gradient inside buf, in source order (a dict when names are given)."""
+        views = []
+        for i in range(self.n_tensors()):
+            off = lib().gpt2_grad_offset(self._h, i)
+            shape = self.tensor_shape(i)
+            n = int(np.prod(shape))
+            views.append(buf[off:off + 4 * n].view(torch.float32).view(shape))
+        return dict(zip(names, views)) if names is not None else views
+
+    def train_workspace(self, B: int, T: int) -> torch.Tensor:
+        n = lib().gpt2_train_workspace_bytes(self._h, B, T)
+        if n == 0:
+            raise GPT2Error(ESHAPE, "gpt2_train_workspace_bytes")
+        return _aligned_empty(n, self.device)
+
+    def backward(self, tokens: torch.Tensor, labels: torch.Tensor | None = None, grads: torch.Tensor | None = None,
+                 loss: torch.Tensor | None = None, ws: torch.Tensor | None = None, stream=None):
+        """Loss and gradients of the mean shifted cross-entropy: returns (loss fp32 [1], grads buffer)."""
+        _require_cuda(tokens, labels, grads, loss, ws)
+        if tokens.dtype != torch.int32 or tokens.dim() != 2 or not tokens.is_contiguous():
+            raise ValueError("tokens must be a contiguous int32 [B, T] device tensor")
+        B, T = tokens.shape
+        if labels is not None and (labels.shape != tokens.shape or labels.dtype != torch.int32 or
+                                   not labels.is_contiguous()):
+            raise ValueError("labels must be a contiguous int32 tensor shaped like tokens")
+        grads = self.grad_buffer() if grads is None else grads
+        loss = torch.empty((1,), dtype=torch.float32, device=self.device) if loss is None else loss
+        ws = self.train_workspace(B, T) if ws is None else ws
+        _check(lib().gpt2_backward(self._h, _ptr(tokens), _ptr(labels), B, T, _ptr(grads), grads.numel(), _ptr(loss),
+                                   _ptr(ws), ws.numel(), _stream(stream)), "gpt2_backward")
+        return loss, grads
 
     def launches(self, with_argmax: bool = True) -> list[str]:
         """Kinds of the kernel launches one forward enqueues, in order."""

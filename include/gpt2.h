@@ -268,6 +268,29 @@ gpt2_status gpt2_sample(const float* logits_dev, int64_t ld, int32_t B, int32_t 
 /* Bytes of the optional gpt2_sample workspace for B rows of V logits (0 for invalid B, V). */
 size_t gpt2_sample_workspace_bytes(int32_t B, int32_t V);
 
+/* Training gradients ([手写] §4 training loop: the loss and loss.backward(); §2.2: with the lm_head
+ * tied to wte, the gradient of wte is the lm_head's gradient plus the embedding's).
+ * gpt2_backward runs the forward keeping its activations, the mean shifted next-token
+ * cross-entropy of gpt2_forward_loss (same labels rules, -100 ignored), and the backward pass,
+ * writing loss_dev fp32 [1] and the fp32 gradient of every source tensor of gpt2_tensor_shape:
+ * tensor i's gradient starts at byte gpt2_grad_offset(m, i) of grads_dev, in its source shape (rows
+ * unpadded, row-major), and every element of every gradient is written (rows of wpe past T get 0).
+ *   grads_dev   256-byte aligned, at least gpt2_grad_bytes(m) bytes.
+ *   ws_dev      256-byte aligned, at least gpt2_train_workspace_bytes(m, B, T) bytes (the saved
+ *               activations of every layer and the backward's buffers; gpt2_check(m, ws_dev, B, T)
+ *               reports out-of-range token ids or labels afterwards).
+ * Products run in the compute dtype (bf16 operands with fp32 accumulation, or fp32); gradients,
+ * the residual stream and every reduction are fp32. The embedding part of the wte gradient is
+ * added with floating-point atomics, so rows of tokens that repeat may differ in the last bits from
+ * run to run; every other gradient is computed in a fixed order.
+ * Requires 2 <= T <= n_ctx, 1 <= B, B * T <= 2^20 and loaded weights. */
+size_t gpt2_grad_bytes(const gpt2_model* m);
+size_t gpt2_grad_offset(const gpt2_model* m, int32_t i); /* (size_t)-1 for an invalid i */
+size_t gpt2_train_workspace_bytes(const gpt2_model* m, int32_t B, int32_t T); /* 0 for invalid B, T */
+gpt2_status gpt2_backward(const gpt2_model* m, const int32_t* tokens_dev, const int32_t* labels_dev, int32_t B,
+                          int32_t T, float* grads_dev, size_t grads_bytes, float* loss_dev, void* ws_dev,
+                          size_t ws_bytes, hipStream_t stream);
+
 /* Static text for a status code. */
 const char* gpt2_strerror(gpt2_status s);
 

@@ -32,7 +32,8 @@ def test_header_declares_expected_entry_points():
     names = declared_functions()
     for required in ("gpt2_config", "gpt2_load_weights", "gpt2_forward", "gpt2_attention", "gpt2_forward_debug",
                      "gpt2_check", "gpt2_strerror", "gpt2_destroy", "gpt2_weight_bytes", "gpt2_workspace_bytes",
-                     "gpt2_forward_loss", "gpt2_kv_cache_bytes", "gpt2_prefill", "gpt2_decode_step", "gpt2_sample"):
+                     "gpt2_forward_loss", "gpt2_kv_cache_bytes", "gpt2_prefill", "gpt2_decode_step", "gpt2_sample",
+                     "gpt2_backward", "gpt2_grad_bytes", "gpt2_grad_offset", "gpt2_train_workspace_bytes"):
         assert required in names
 
 
@@ -123,6 +124,33 @@ def test_kv_cache_bytes(g):
     L.gpt2_destroy(h)
     st, h = make(g, dtype="f32")
     assert L.gpt2_kv_cache_bytes(h, 1) == 12 * 2 * 12 * 1024 * 64 * 4
+    L.gpt2_destroy(h)
+
+
+def test_grad_layout_and_train_workspace(g):
+    st, h = make(g)
+    L = g.lib()
+    n = L.gpt2_n_tensors(h)
+    off = [L.gpt2_grad_offset(h, i) for i in range(n)]
+    assert off[0] == 0 and all(o % 256 == 0 for o in off)
+    total = 0
+    for i in range(n):
+        r, c = ctypes.c_int64(), ctypes.c_int64()
+        assert L.gpt2_tensor_shape(h, i, ctypes.byref(r), ctypes.byref(c)) == 0
+        numel = r.value * (c.value or 1)
+        assert off[i] == total
+        total = (total + 4 * numel + 255) // 256 * 256
+    assert L.gpt2_grad_bytes(h) == total
+    assert L.gpt2_grad_offset(h, n) == 2 ** 64 - 1 and L.gpt2_grad_offset(h, -1) == 2 ** 64 - 1
+    assert L.gpt2_train_workspace_bytes(h, 4, 1) == 0 and L.gpt2_train_workspace_bytes(h, 0, 8) == 0
+    assert L.gpt2_train_workspace_bytes(h, 4, 1025) == 0
+    # the training workspace holds at least the forward workspace, the logits and every layer's activations
+    need = L.gpt2_train_workspace_bytes(h, 4, 1024)
+    assert need > L.gpt2_workspace_bytes(h, 4, 1024) + 4 * 1024 * 50257 * 4 + 12 * 4 * 1024 * 768 * 4 * 2
+    fake = ctypes.c_void_p(0x100000)
+    assert L.gpt2_backward(h, fake, None, 4, 8, fake, 1 << 40, fake, fake, 1 << 40, None) == g.ESTATE
+    assert L.gpt2_backward(h, None, None, 4, 8, fake, 1 << 40, fake, fake, 1 << 40, None) == g.EINVAL
+    assert L.gpt2_backward(None, fake, None, 4, 8, fake, 1 << 40, fake, fake, 1 << 40, None) == g.EINVAL
     L.gpt2_destroy(h)
 
 
