@@ -1,6 +1,6 @@
 """Forward-pass throughput of the HIP GPT-2 library on one MI355X.
 
-python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload small|medium|xl] [--no-cpu-baseline] [--no-loss] [--no-decode]
+python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload small|medium|xl] [--no-cpu-baseline] [--no-loss] [--no-decode] [--no-train]
 
 One step = one gpt2_forward over a batch of synthetic token ids already resident in HBM:
 embedding, every block, ln_f, the tied lm_head (fp32 logits) and the fused argmax. Weights are the
@@ -9,7 +9,8 @@ times gpt2_forward_loss (the same forward with the shifted next-token cross-entr
 vocabulary projection, logits not stored) under "forward_loss", and cached greedy decode steps
 (gpt2_decode_step after a gpt2_prefill of half the context) under "decode", and the same steps with
 sampling (gpt2_sample at temperature 0.7, top-k 50, top-p 0.95, repetition penalty 1.2) under
-"decode_sampled".
+"decode_sampled", and the training gradients (gpt2_backward: forward keeping activations, the loss,
+the backward pass) under "train".
 
 The roofline object is for the lm_head GEMM, the largest single launch: its duration is taken
 from HIP events the library records on its own stream around that launch in every timed step.
@@ -47,6 +48,15 @@ def forward_flops(s: synth.ModelShape, B: int, T: int) -> float:
     M = B * T
     return 24.0 * M * s.n_layer * s.d_model ** 2 + 2.0 * B * s.n_layer * s.d_model * T * (T + 1) \
         + 2.0 * M * s.d_model * s.n_vocab
+
+
+def train_flops(s: synth.ModelShape, B: int, T: int) -> float:
+    """Algorithmic FLOPs of forward + backward: each GEMM once forward and twice backward (input and
+    weight gradients), the causal attention products once forward and twice backward."""
+    M = B * T
+    gemm = 24.0 * M * s.n_layer * s.d_model ** 2 + 2.0 * M * s.d_model * s.n_vocab
+    attn = 2.0 * B * s.n_layer * s.d_model * T * (T + 1)
+    return 3.0 * gemm + 3.0 * attn
 
 
 def traffic_record(kernel_src: str):
@@ -93,6 +103,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-loss", action="store_true", help="skip the fused forward+loss measurement")
     ap.add_argument("--no-decode", action="store_true", help="skip the cached decode measurement")
+    ap.add_argument("--no-train", action="store_true", help="skip the forward+backward (gradients) measurement")
     ap.add_argument("--breakdown", action="store_true", help="also time every launch of one extra forward")
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="after the timed region, run a plain device-to-device copy of this many bytes three "
@@ -249,6 +260,29 @@ def main():
                                  "sample_call_us": e0.elapsed_time(e1) * 1e3 / n_s,
                                  "what": "cached decode step + gpt2_sample + append to the sequence; sample_call_us is "
                                          "one gpt2_sample call through the Python binding (host-bound at this batch)"}
+
+    if not args.no_train:
+        # Training gradients at the same shape: gpt2_backward = forward keeping activations, the
+        # shifted cross-entropy, and the backward pass writing fp32 gradients of every weight.
+        tws = m.train_workspace(B, T)
+        gbuf = m.grad_buffer()
+        tloss = torch.empty((1,), dtype=torch.float32, device="cuda")
+        n_train = 5
+        for _ in range(2):
+            m.backward(tokens, grads=gbuf, loss=tloss, ws=tws)
+        torch.cuda.synchronize()
+        t5 = time.perf_counter()
+        for _ in range(n_train):
+            m.backward(tokens, grads=gbuf, loss=tloss, ws=tws)
+        torch.cuda.synchronize()
+        tms = (time.perf_counter() - t5) * 1e3 / n_train
+        tfl = train_flops(shape, B, T)
+        out["train"] = {"ms_per_step": tms, "tokens_per_s": M / (tms * 1e-3), "steps": n_train,
+                        "tflops": tfl / (tms * 1e-3) / 1e12, "mfma_frac": tfl / (tms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+                        "loss": float(tloss.item()), "workspace_gb": tws.numel() / 1e9,
+                        "what": "forward keeping activations + shifted cross-entropy + backward (fp32 gradients "
+                                "of every weight, tied wte summed); no optimizer step"}
+        del tws, gbuf
 
     if args.copy_bytes > 0:
         src = torch.empty(args.copy_bytes, dtype=torch.uint8, device="cuda")

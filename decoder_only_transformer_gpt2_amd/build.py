@@ -23,10 +23,12 @@ FLAGS = [
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-I", os.path.join(ROOT, "include"),
 ]
-# Per-source additions. The attention kernel runs its softmax on the MFMA results, so its
-# accumulators are kept in ordinary VGPRs (MFMA in VGPR form) instead of being copied out of AGPRs.
+# Per-source additions. The attention kernels (forward and backward) run their softmax on the MFMA
+# results, so their accumulators are kept in ordinary VGPRs (MFMA in VGPR form) instead of being
+# copied out of AGPRs.
 FILE_FLAGS = {
     "attention.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
+    "attention_bwd.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
 }
 
 

@@ -1,0 +1,313 @@
+// Causal attention backward on the matrix cores (bf16 operands, fp32 accumulation).
+//   P = softmax_j(q_i . k_j / 8) over j <= i, o_i = sum_j P_ij v_j (the forward, "复现GPT-2 124M"
+//   §2.1-§2.2); given dO: dV = P^T dO, dP = dO V^T, dS = P * (dP - D) with D_i = dO_i . o_i,
+//   dQ = dS K / 8, dK = dS^T Q / 8.
+// Two kernels, each exact in its own accumulation order (no atomics):
+//   attn_bwd_dq_mfma: a workgroup owns 64 queries of one (b, h), a wavefront 16 of them. Pass 1
+//     over the key tiles finds each query's log-sum-exp (base 2); pass 2 forms S^T = K Q^T,
+//     P^T, dP^T = V dO^T and dS^T, and accumulates dQ^T += K^T dS^T. It also writes lse and D.
+//   attn_bwd_dkv_mfma: a workgroup owns 64 keys, a wavefront 16 of them; over the query tiles on
+//     and after the diagonal it forms S = Q K^T, P, dP = dO V^T, dS and accumulates
+//     dV^T += dO^T P and dK^T += Q^T dS.
+// With v_mfma_f32_16x16x32_bf16 a lane's accumulator holds one column (lane % 16) and rows
+// 4 (lane / 16) + e; the four accumulators of a 64-row product therefore give every lane the 8
+// values of its column at rows {32 h + 4 g + j, 32 h + 16 + 4 g + j} (j < 4), which is directly
+// the B operand of the next product over those 32 rows; the A operand is read from a transposed
+// LDS tile with the same row order.
+#include "common.h"
+
+namespace gpt2k {
+namespace {
+
+constexpr int BT = 64;        // rows (queries or keys) per tile
+constexpr int DHB = 64;       // head size
+constexpr int TSB = BT + 8;   // row stride of a transposed [d][row] tile (spreads rows over banks)
+
+__device__ __forceinline__ int swz(int row, int chunk) { return row * DHB + ((chunk ^ (row & 7)) << 3); }
+
+// Stage 64 rows x 64 dims of a bf16 matrix (row r at src + r * ld, rows >= n zero) into LDS as a
+// swizzled [row][d] tile and, when tr is set, also as a transposed [d][row] tile.
+__device__ __forceinline__ void stage_bf16(const uint16_t* __restrict__ src, long ld, int n, uint16_t* tile,
+                                           uint16_t* tr) {
+    for (int c = threadIdx.x; c < BT * 8; c += 256) {
+        const int r = c >> 3, ch = c & 7;
+        u32x4_t u = {0u, 0u, 0u, 0u};
+        if (r < n) u = *reinterpret_cast<const u32x4_t*>(src + (long)r * ld + ch * 8);
+        *reinterpret_cast<u32x4_t*>(&tile[swz(r, ch)]) = u;
+        if (tr) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                tr[(ch * 8 + 2 * j) * TSB + r] = (uint16_t)(u[j] & 0xffffu);
+                tr[(ch * 8 + 2 * j + 1) * TSB + r] = (uint16_t)(u[j] >> 16);
+            }
+        }
+    }
+}
+// The same for fp32 rows, rounded to bf16.
+__device__ __forceinline__ void stage_f32(const float* __restrict__ src, long ld, int n, uint16_t* tile, uint16_t* tr) {
+    for (int c = threadIdx.x; c < BT * 8; c += 256) {
+        const int r = c >> 3, ch = c & 7;
+        u32x4_t u = {0u, 0u, 0u, 0u};
+        if (r < n) {
+            const f32x4_t a = *reinterpret_cast<const f32x4_t*>(src + (long)r * ld + ch * 8);
+            const f32x4_t b = *reinterpret_cast<const f32x4_t*>(src + (long)r * ld + ch * 8 + 4);
+            u = u32x4_t{pack_bf16x2(a[0], a[1]), pack_bf16x2(a[2], a[3]), pack_bf16x2(b[0], b[1]), pack_bf16x2(b[2], b[3])};
+        }
+        *reinterpret_cast<u32x4_t*>(&tile[swz(r, ch)]) = u;
+        if (tr) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                tr[(ch * 8 + 2 * j) * TSB + r] = (uint16_t)(u[j] & 0xffffu);
+                tr[(ch * 8 + 2 * j + 1) * TSB + r] = (uint16_t)(u[j] >> 16);
+            }
+        }
+    }
+}
+
+// A operand from a swizzled [row][d] tile: row, dims kk * 32 + 8 g .. + 7
+__device__ __forceinline__ bf16x8_t a_rows(const uint16_t* tile, int row, int kk, int g) {
+    return *reinterpret_cast<const bf16x8_t*>(&tile[swz(row, kk * 4 + g)]);
+}
+// A operand from a transposed [d][row] tile: row d, k-slots = rows {32 h + 4 g + j, 32 h + 16 + 4 g + j}
+__device__ __forceinline__ bf16x8_t a_trans(const uint16_t* tr, int d, int h, int g) {
+    const uint16_t* p = &tr[d * TSB + 32 * h + 4 * g];
+    const u32x2_t lo = *reinterpret_cast<const u32x2_t*>(p);
+    const u32x2_t hi = *reinterpret_cast<const u32x2_t*>(p + 16);
+    return __builtin_bit_cast(bf16x8_t, u32x4_t{lo[0], lo[1], hi[0], hi[1]});
+}
+// B operand over 32 rows from two accumulators (rows 4 g + e of fragments 2 h and 2 h + 1)
+__device__ __forceinline__ bf16x8_t b_pack(const f32x4_t& x0, const f32x4_t& x1) {
+    return __builtin_bit_cast(bf16x8_t, u32x4_t{pack_bf16x2(x0[0], x0[1]), pack_bf16x2(x0[2], x0[3]),
+                                                 pack_bf16x2(x1[0], x1[1]), pack_bf16x2(x1[2], x1[3])});
+}
+// This lane's 16 dims (kk * 32 + 8 g .. + 7, kk < 2) of a bf16 row as two B operands.
+__device__ __forceinline__ void row_operand(const uint16_t* row, int g, bf16x8_t (&f)[2], bool valid) {
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+        u32x4_t u = {0u, 0u, 0u, 0u};
+        if (valid) u = *reinterpret_cast<const u32x4_t*>(row + kk * 32 + g * 8);
+        f[kk] = __builtin_bit_cast(bf16x8_t, u);
+    }
+}
+
+constexpr float kC2 = 0.125f * 1.4426950408889634f;  // (1 / sqrt(64)) * log2(e)
+
+__global__ __launch_bounds__(256) void attn_bwd_dq_mfma(const uint16_t* __restrict__ qkv, const uint16_t* __restrict__ o,
+                                                        const float* __restrict__ dout, float* __restrict__ dqkv,
+                                                        float* __restrict__ lse_out, float* __restrict__ d_out, int B,
+                                                        int H, int T) {
+    __shared__ __attribute__((aligned(16))) uint16_t sK[BT * DHB];
+    __shared__ __attribute__((aligned(16))) uint16_t sV[BT * DHB];
+    __shared__ __attribute__((aligned(16))) uint16_t sKt[DHB * TSB];
+    const int nqb = (T + BT - 1) / BT;
+    const int bh = blockIdx.x % (B * H), qb = nqb - 1 - blockIdx.x / (B * H);  // longest first
+    const int b = bh / H, h = bh % H, d = H * DHB;
+    const int t = threadIdx.x, w = t >> 6, lane = t & 63, r16 = lane & 15, g4 = lane >> 4;
+    const int qi = qb * BT + 16 * w + r16;  // this lane's query (accumulator column)
+    const bool qv = qi < T;
+    const long qrow = (long)b * T + (qv ? qi : 0);
+    const uint16_t* base = qkv + (long)b * T * 3 * d + h * DHB;  // q of row r at base + r * 3d
+
+    bf16x8_t qf[2], gf[2];
+    row_operand(qkv + qrow * 3 * d + h * DHB, g4, qf, qv);
+    // dO row (fp32) as bf16 operands, and D = dO . o over this lane's 16 dims, then over the row
+    float dd = 0.f;
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+        const float* gr = dout + qrow * d + h * DHB + kk * 32 + g4 * 8;
+        const uint16_t* orow = o + qrow * d + h * DHB + kk * 32 + g4 * 8;
+        f32x4_t a = {0.f, 0.f, 0.f, 0.f}, c = {0.f, 0.f, 0.f, 0.f};
+        u32x4_t ou = {0u, 0u, 0u, 0u};
+        if (qv) {
+            a = *reinterpret_cast<const f32x4_t*>(gr);
+            c = *reinterpret_cast<const f32x4_t*>(gr + 4);
+            ou = *reinterpret_cast<const u32x4_t*>(orow);
+        }
+        gf[kk] = __builtin_bit_cast(bf16x8_t, u32x4_t{pack_bf16x2(a[0], a[1]), pack_bf16x2(a[2], a[3]),
+                                                       pack_bf16x2(c[0], c[1]), pack_bf16x2(c[2], c[3])});
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const float lo = bf16_bits_to_f32(ou[j] & 0xffffu), hi = bf16_bits_to_f32(ou[j] >> 16);
+            dd += (j < 2 ? a[2 * j] : c[2 * j - 4]) * lo + (j < 2 ? a[2 * j + 1] : c[2 * j - 3]) * hi;
+        }
+    }
+    dd += __shfl_xor(dd, 16);
+    dd += __shfl_xor(dd, 32);
+
+    const int n_kt = qb + 1;  // key tiles up to the diagonal
+    // pass 1: log-sum-exp of this lane's query (base 2, scores times c2)
+    float mx = -INFINITY, sm = 0.f;
+    for (int kt = 0; kt < n_kt; ++kt) {
+        const int k0 = kt * BT;
+        __syncthreads();
+        stage_bf16(base + d + (long)k0 * 3 * d, 3 * d, min(BT, T - k0), sK, nullptr);
+        __syncthreads();
+        if (k0 > qb * BT + 16 * w + 15) continue;  // wave-uniform: every key of the tile is after every query
+        f32x4_t s[4];
+#pragma unroll
+        for (int mf = 0; mf < 4; ++mf) {
+            s[mf] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int kk = 0; kk < 2; ++kk)
+                s[mf] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a_rows(sK, mf * 16 + r16, kk, g4), qf[kk], s[mf], 0, 0, 0);
+        }
+#pragma unroll
+        for (int mf = 0; mf < 4; ++mf)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int key = k0 + mf * 16 + 4 * g4 + e;
+                if (key <= qi && key < T) {
+                    const float a = s[mf][e] * kC2;
+                    if (a > mx) {
+                        sm = sm * __builtin_amdgcn_exp2f(mx - a) + 1.f;
+                        mx = a;
+                    } else {
+                        sm += __builtin_amdgcn_exp2f(a - mx);
+                    }
+                }
+            }
+    }
+    lse_merge(mx, sm, __shfl_xor(mx, 16), __shfl_xor(sm, 16));
+    lse_merge(mx, sm, __shfl_xor(mx, 32), __shfl_xor(sm, 32));
+    const float lse2 = mx + __log2f(sm);
+
+    // pass 2: dQ^T += K^T dS^T over the key tiles
+    f32x4_t dq[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) dq[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int kt = 0; kt < n_kt; ++kt) {
+        const int k0 = kt * BT, nk = min(BT, T - k0);
+        __syncthreads();
+        stage_bf16(base + d + (long)k0 * 3 * d, 3 * d, nk, sK, sKt);
+        stage_bf16(base + 2 * d + (long)k0 * 3 * d, 3 * d, nk, sV, nullptr);
+        __syncthreads();
+        if (k0 > qb * BT + 16 * w + 15) continue;
+        f32x4_t s[4], dp[4];
+#pragma unroll
+        for (int mf = 0; mf < 4; ++mf) {
+            s[mf] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+            dp[mf] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int kk = 0; kk < 2; ++kk) {
+                s[mf] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a_rows(sK, mf * 16 + r16, kk, g4), qf[kk], s[mf], 0, 0, 0);
+                dp[mf] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a_rows(sV, mf * 16 + r16, kk, g4), gf[kk], dp[mf], 0, 0, 0);
+            }
+        }
+        // dS^T = P^T * (dP^T - D), P^T = 2^(s c2 - lse2) on visible keys
+#pragma unroll
+        for (int mf = 0; mf < 4; ++mf)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int key = k0 + mf * 16 + 4 * g4 + e;
+                const float p = (key <= qi && key < T) ? __builtin_amdgcn_exp2f(fmaf(s[mf][e], kC2, -lse2)) : 0.f;
+                s[mf][e] = p * (dp[mf][e] - dd);
+            }
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+            const bf16x8_t dsf = b_pack(s[2 * hh], s[2 * hh + 1]);
+#pragma unroll
+            for (int df = 0; df < 4; ++df)
+                dq[df] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a_trans(sKt, df * 16 + r16, hh, g4), dsf, dq[df], 0, 0, 0);
+        }
+    }
+    if (qv) {
+        float* out = dqkv + qrow * 3 * d + h * DHB;
+#pragma unroll
+        for (int df = 0; df < 4; ++df)
+            *reinterpret_cast<f32x4_t*>(out + df * 16 + 4 * g4) = dq[df] * 0.125f;
+        if (g4 == 0) {
+            lse_out[(long)bh * T + qi] = lse2;
+            d_out[(long)bh * T + qi] = dd;
+        }
+    }
+}
+
+__global__ __launch_bounds__(256) void attn_bwd_dkv_mfma(const uint16_t* __restrict__ qkv, const float* __restrict__ dout,
+                                                         const float* __restrict__ lse, const float* __restrict__ dvec,
+                                                         float* __restrict__ dqkv, int B, int H, int T) {
+    __shared__ __attribute__((aligned(16))) uint16_t sQ[BT * DHB];
+    __shared__ __attribute__((aligned(16))) uint16_t sQt[DHB * TSB];
+    __shared__ __attribute__((aligned(16))) uint16_t sG[BT * DHB];
+    __shared__ __attribute__((aligned(16))) uint16_t sGt[DHB * TSB];
+    __shared__ float sL[BT], sD[BT];
+    const int nkb = (T + BT - 1) / BT;
+    const int bh = blockIdx.x % (B * H), kb = blockIdx.x / (B * H);  // most query tiles first
+    const int b = bh / H, h = bh % H, d = H * DHB;
+    const int t = threadIdx.x, w = t >> 6, lane = t & 63, r16 = lane & 15, g4 = lane >> 4;
+    const int kj = kb * BT + 16 * w + r16;  // this lane's key (accumulator column)
+    const bool kv = kj < T;
+    const long krow = (long)b * T + (kv ? kj : 0);
+    const uint16_t* base = qkv + (long)b * T * 3 * d + h * DHB;
+    const float* gbase = dout + (long)b * T * d + h * DHB;
+
+    bf16x8_t kf[2], vf[2];
+    row_operand(qkv + krow * 3 * d + d + h * DHB, g4, kf, kv);
+    row_operand(qkv + krow * 3 * d + 2 * d + h * DHB, g4, vf, kv);
+    f32x4_t dk[4], dv[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) dk[i] = dv[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+    for (int qt = kb; qt < nkb; ++qt) {
+        const int q0 = qt * BT, nq = min(BT, T - q0);
+        __syncthreads();
+        stage_bf16(base + (long)q0 * 3 * d, 3 * d, nq, sQ, sQt);
+        stage_f32(gbase + (long)q0 * d, d, nq, sG, sGt);
+        if (t < BT) {
+            sL[t] = t < nq ? lse[(long)bh * T + q0 + t] : 0.f;
+            sD[t] = t < nq ? dvec[(long)bh * T + q0 + t] : 0.f;
+        }
+        __syncthreads();
+        if (q0 + BT - 1 < kb * BT + 16 * w) continue;  // wave-uniform: every query of the tile is before every key
+        f32x4_t s[4], dp[4];
+#pragma unroll
+        for (int mf = 0; mf < 4; ++mf) {
+            s[mf] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+            dp[mf] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int kk = 0; kk < 2; ++kk) {
+                s[mf] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a_rows(sQ, mf * 16 + r16, kk, g4), kf[kk], s[mf], 0, 0, 0);
+                dp[mf] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a_rows(sG, mf * 16 + r16, kk, g4), vf[kk], dp[mf], 0, 0, 0);
+            }
+        }
+        // P[q, key] and dS = P * (dP - D[q]) for visible (query, key) pairs
+#pragma unroll
+        for (int mf = 0; mf < 4; ++mf)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int qr = mf * 16 + 4 * g4 + e, q = q0 + qr;
+                const float p = (q >= kj && q < T && kv) ? __builtin_amdgcn_exp2f(fmaf(s[mf][e], kC2, -sL[qr])) : 0.f;
+                s[mf][e] = p;
+                dp[mf][e] = p * (dp[mf][e] - sD[qr]);
+            }
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+            const bf16x8_t pf = b_pack(s[2 * hh], s[2 * hh + 1]);
+            const bf16x8_t dsf = b_pack(dp[2 * hh], dp[2 * hh + 1]);
+#pragma unroll
+            for (int df = 0; df < 4; ++df) {
+                dv[df] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a_trans(sGt, df * 16 + r16, hh, g4), pf, dv[df], 0, 0, 0);
+                dk[df] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a_trans(sQt, df * 16 + r16, hh, g4), dsf, dk[df], 0, 0, 0);
+            }
+        }
+    }
+    if (kv) {
+        float* out = dqkv + krow * 3 * d + h * DHB;
+#pragma unroll
+        for (int df = 0; df < 4; ++df) {
+            *reinterpret_cast<f32x4_t*>(out + d + df * 16 + 4 * g4) = dk[df] * 0.125f;
+            *reinterpret_cast<f32x4_t*>(out + 2 * d + df * 16 + 4 * g4) = dv[df];
+        }
+    }
+}
+
+}  // namespace
+
+hipError_t attention_backward_bf16(const uint16_t* qkv, const uint16_t* o, const float* dout, float* dqkv, float* lse,
+                                   float* dvec, int B, int H, int T, hipStream_t s) {
+    const dim3 grid((unsigned)(((T + BT - 1) / BT) * B * H)), block(256);
+    attn_bwd_dq_mfma<<<grid, block, 0, s>>>(qkv, o, dout, dqkv, lse, dvec, B, H, T);
+    attn_bwd_dkv_mfma<<<grid, block, 0, s>>>(qkv, dout, lse, dvec, dqkv, B, H, T);
+    return hipGetLastError();
+}
+
+}  // namespace gpt2k

@@ -227,7 +227,7 @@ hipError_t transpose(const void* src, bool src_bf16, long lds, int R, int C, voi
 int colsum_blocks(int R);
 hipError_t colsum(const float* src, long ld, int R, int C, float* part, float* out, hipStream_t s);
 // LayerNorm backward on rows of x with output gradient dy (fp32 [M, d]): dx += the input gradient,
-// dgamma / dbeta = column sums (pg, pb hold ln_backward_blocks(M) * d floats each).
+// dgamma / dbeta = column sums (pg, pb hold ln_backward_blocks(M) * d floats each: partial rows).
 int ln_backward_blocks(int M);
 hipError_t ln_backward(const float* x, const float* gamma, const float* dy, float* dx, int M, int d, float eps, float* pg,
                        float* pb, float* dgamma, float* dbeta, hipStream_t s);
@@ -242,6 +242,8 @@ hipError_t xent_grad(const float* logits, long ld, int M, int V, int Vp, const i
 // output gradient dout fp32 [B, T, H * 64]: dqkv fp32 [B, T, 3 * H * 64]; lse, dvec: [B * H * T] scratch.
 hipError_t attention_backward(const void* qkv, const void* o, const float* dout, float* dqkv, float* lse, float* dvec,
                               int B, int H, int T, bool bf16, hipStream_t s);
+hipError_t attention_backward_bf16(const uint16_t* qkv, const uint16_t* o, const float* dout, float* dqkv, float* lse,
+                                   float* dvec, int B, int H, int T, hipStream_t s);
 // gwpe[t] = sum_b dx[b, t] (0 for t >= T, all n_ctx rows written); gwte[tok[m]] += dx[m].
 hipError_t embed_backward(const int32_t* tok, const float* dx, int B, int T, int n_ctx, int d, int V, float* gwte,
                           float* gwpe, hipStream_t s);

@@ -43,70 +43,134 @@ __global__ void __launch_bounds__(256) transpose_kernel(const void* __restrict__
 }
 
 // ------------------------------------------------------------------------------ column sums
-// part[b][c] = sum of src[r][c] over rows r of block b (256 rows), in row order.
+// part[b][c] = sum of src[r][c] over the 256 rows r of block b: four row groups of 64 rows per
+// column (eight loads in flight per thread), combined in group order.
+constexpr int kColRows = 256;
 __global__ void __launch_bounds__(256) colsum_partial_kernel(const float* __restrict__ src, long ld, int R, int C,
                                                              float* __restrict__ part) {
-    const int c = blockIdx.x * 256 + threadIdx.x, b = blockIdx.y;
-    if (c >= C) return;
-    const int r1 = min(R, (b + 1) * 256);
-    float acc = 0.f;
-    for (int r = b * 256; r < r1; ++r) acc += src[(long)r * ld + c];
-    part[(long)b * C + c] = acc;
+    __shared__ float acc4[4][64];
+    const int cl = threadIdx.x & 63, grp = threadIdx.x >> 6, c = blockIdx.x * 64 + cl, b = blockIdx.y;
+    const int r0 = b * kColRows + grp * 64, r1 = min(R, r0 + 64);
+    float a[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    if (c < C) {
+        int r = r0;
+        for (; r + 8 <= r1; r += 8) {
+#pragma unroll
+            for (int u = 0; u < 8; ++u) a[u] += src[(long)(r + u) * ld + c];
+        }
+        for (; r < r1; ++r) a[0] += src[(long)r * ld + c];
+    }
+    acc4[grp][cl] = ((a[0] + a[1]) + (a[2] + a[3])) + ((a[4] + a[5]) + (a[6] + a[7]));
+    __syncthreads();
+    if (grp == 0 && c < C) part[(long)b * C + c] = ((acc4[0][cl] + acc4[1][cl]) + acc4[2][cl]) + acc4[3][cl];
 }
-// out[c] = sum over b < nb of part[b][c], in block order.
+// out[c] = sum over b < nb of part[b][c] (eight partial sums per thread, fixed order).
 __global__ void __launch_bounds__(256) colsum_reduce_kernel(const float* __restrict__ part, int nb, int C,
                                                             float* __restrict__ out) {
     const int c = blockIdx.x * 256 + threadIdx.x;
     if (c >= C) return;
-    float acc = 0.f;
-    for (int b = 0; b < nb; ++b) acc += part[(long)b * C + c];
-    out[c] = acc;
+    float a[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    int b = 0;
+    for (; b + 8 <= nb; b += 8) {
+#pragma unroll
+        for (int u = 0; u < 8; ++u) a[u] += part[(long)(b + u) * C + c];
+    }
+    for (; b < nb; ++b) a[0] += part[(long)b * C + c];
+    out[c] = ((a[0] + a[1]) + (a[2] + a[3])) + ((a[4] + a[5]) + (a[6] + a[7]));
 }
 
 // ------------------------------------------------------------------------------ LayerNorm backward
-// One wavefront per block of kLnRows rows. For each row: xhat = (x - mean) * rstd, g = dy * gamma,
-// dx += rstd * (g - mean(g) - xhat * mean(g * xhat)); the block's sums of dy * xhat and dy per
-// column go to pg / pb [block][d] (each lane owns columns lane + 64 j, so the sums run in row order).
-constexpr int kLnRows = 16;
-__global__ void __launch_bounds__(64) ln_backward_kernel(const float* __restrict__ x, const float* __restrict__ gamma,
-                                                         const float* __restrict__ dy, float* __restrict__ dx, int M,
-                                                         int d, float eps, float* __restrict__ pg,
-                                                         float* __restrict__ pb) {
-    extern __shared__ float sacc[];  // [2][d]
-    const int lane = threadIdx.x, blk = blockIdx.x;
-    for (int c = lane; c < 2 * d; c += 64) sacc[c] = 0.f;
+// Four wavefronts per block of kLnRows rows, one row at a time per wavefront. For each row:
+// xhat = (x - mean) * rstd, g = dy * gamma, dx += rstd * (g - mean(g) - xhat * mean(g * xhat)). Each
+// wavefront sums dy * xhat and dy per column over its rows (lane l owns columns l + 64 j) and writes
+// them as partial row (block * kLnWaves + wave) of pg / pb [partials][d].
+constexpr int kLnRows = 16, kLnWaves = 4;
+
+// CPL > 0: the row and the column sums held in registers (d = 64 * CPL); CPL = 0: any d (multiple
+// of 64), the row re-read and the sums kept in the wave's own partial rows.
+template <int CPL>
+__global__ void __launch_bounds__(64 * kLnWaves) ln_backward_kernel(const float* __restrict__ x,
+                                                                    const float* __restrict__ gamma,
+                                                                    const float* __restrict__ dy, float* __restrict__ dx,
+                                                                    int M, int d, float eps, float* __restrict__ pg,
+                                                                    float* __restrict__ pb) {
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, blk = blockIdx.x;
+    float* og = pg + (long)(blk * kLnWaves + w) * d;
+    float* ob = pb + (long)(blk * kLnWaves + w) * d;
     const float inv_d = 1.0f / (float)d;
-    for (int rr = 0; rr < kLnRows; ++rr) {
+    float ag[CPL > 0 ? CPL : 1], ab[CPL > 0 ? CPL : 1];
+    if constexpr (CPL > 0) {
+#pragma unroll
+        for (int j = 0; j < CPL; ++j) ag[j] = ab[j] = 0.f;
+    } else {
+        for (int c = lane; c < d; c += 64) og[c] = ob[c] = 0.f;
+    }
+    for (int rr = w; rr < kLnRows; rr += kLnWaves) {
         const int m = blk * kLnRows + rr;
         if (m >= M) break;
         const float* xr = x + (long)m * d;
         const float* gr = dy + (long)m * d;
-        float s = 0.f;
-        for (int c = lane; c < d; c += 64) s += xr[c];
-        const float mean = wave_sum(s) * inv_d;
-        float q = 0.f;
-        for (int c = lane; c < d; c += 64) {
-            const float a = xr[c] - mean;
-            q += a * a;
-        }
-        const float rstd = 1.0f / sqrtf(wave_sum(q) * inv_d + eps);
-        float sg = 0.f, sgx = 0.f;
-        for (int c = lane; c < d; c += 64) {
-            const float xh = (xr[c] - mean) * rstd, g = gr[c] * gamma[c];
-            sg += g;
-            sgx += g * xh;
-        }
-        const float mg = wave_sum(sg) * inv_d, mgx = wave_sum(sgx) * inv_d;
-        for (int c = lane; c < d; c += 64) {
-            const float xh = (xr[c] - mean) * rstd, g = gr[c] * gamma[c];
-            dx[(long)m * d + c] += rstd * (g - mg - xh * mgx);
-            sacc[c] += gr[c] * xh;
-            sacc[d + c] += gr[c];
+        float* dr = dx + (long)m * d;
+        if constexpr (CPL > 0) {
+            float xv[CPL], gv[CPL];
+#pragma unroll
+            for (int j = 0; j < CPL; ++j) {
+                xv[j] = xr[lane + 64 * j];
+                gv[j] = gr[lane + 64 * j];
+            }
+            float s = 0.f;
+#pragma unroll
+            for (int j = 0; j < CPL; ++j) s += xv[j];
+            const float mean = wave_sum(s) * inv_d;
+            float q = 0.f;
+#pragma unroll
+            for (int j = 0; j < CPL; ++j) q += (xv[j] - mean) * (xv[j] - mean);
+            const float rstd = 1.0f / sqrtf(wave_sum(q) * inv_d + eps);
+            float sg = 0.f, sgx = 0.f;
+#pragma unroll
+            for (int j = 0; j < CPL; ++j) {
+                xv[j] = (xv[j] - mean) * rstd;
+                const float g = gv[j] * gamma[lane + 64 * j];
+                sg += g;
+                sgx += g * xv[j];
+            }
+            const float mg = wave_sum(sg) * inv_d, mgx = wave_sum(sgx) * inv_d;
+#pragma unroll
+            for (int j = 0; j < CPL; ++j) {
+                const int c = lane + 64 * j;
+                const float g = gv[j] * gamma[c];
+                dr[c] += rstd * (g - mg - xv[j] * mgx);
+                ag[j] += gv[j] * xv[j];
+                ab[j] += gv[j];
+            }
+        } else {
+            float s = 0.f;
+            for (int c = lane; c < d; c += 64) s += xr[c];
+            const float mean = wave_sum(s) * inv_d;
+            float q = 0.f;
+            for (int c = lane; c < d; c += 64) q += (xr[c] - mean) * (xr[c] - mean);
+            const float rstd = 1.0f / sqrtf(wave_sum(q) * inv_d + eps);
+            float sg = 0.f, sgx = 0.f;
+            for (int c = lane; c < d; c += 64) {
+                const float xh = (xr[c] - mean) * rstd, g = gr[c] * gamma[c];
+                sg += g;
+                sgx += g * xh;
+            }
+            const float mg = wave_sum(sg) * inv_d, mgx = wave_sum(sgx) * inv_d;
+            for (int c = lane; c < d; c += 64) {
+                const float xh = (xr[c] - mean) * rstd, g = gr[c] * gamma[c];
+                dr[c] += rstd * (g - mg - xh * mgx);
+                og[c] += gr[c] * xh;
+                ob[c] += gr[c];
+            }
         }
     }
-    for (int c = lane; c < d; c += 64) {
-        pg[(long)blk * d + c] = sacc[c];
-        pb[(long)blk * d + c] = sacc[d + c];
+    if constexpr (CPL > 0) {
+#pragma unroll
+        for (int j = 0; j < CPL; ++j) {
+            og[lane + 64 * j] = ag[j];
+            ob[lane + 64 * j] = ab[j];
+        }
     }
 }
 
@@ -199,6 +263,7 @@ __global__ void __launch_bounds__(256) xent_grad_kernel(const float* __restrict_
 }
 
 // ------------------------------------------------------------------------------ attention backward
+// fp32 compute mode (the bf16 mode uses the matrix-core kernels of attention_bwd.hip).
 // Causal attention of head (b, h) on qkv [B, T, 3, H, 64] (compute dtype), output o [B, T, H, 64],
 // output gradient dout fp32 [B, T, H*64]. Two threads per row, each owning 32 of the 64 dimensions;
 // a dot product is two half sums joined by a lane swap. Softmax in base 2: p = 2^(s c2 - lse2)
@@ -410,23 +475,29 @@ hipError_t transpose(const void* src, bool src_bf16, long lds, int R, int C, voi
     return hipGetLastError();
 }
 
-int colsum_blocks(int R) { return (R + 255) / 256; }
+int colsum_blocks(int R) { return (R + kColRows - 1) / kColRows; }
 
 hipError_t colsum(const float* src, long ld, int R, int C, float* part, float* out, hipStream_t s) {
     const int nb = colsum_blocks(R);
-    colsum_partial_kernel<<<dim3((C + 255) / 256, nb), dim3(256), 0, s>>>(src, ld, R, C, part);
+    colsum_partial_kernel<<<dim3((C + 63) / 64, nb), dim3(256), 0, s>>>(src, ld, R, C, part);
     colsum_reduce_kernel<<<dim3((C + 255) / 256), dim3(256), 0, s>>>(part, nb, C, out);
     return hipGetLastError();
 }
 
-int ln_backward_blocks(int M) { return (M + kLnRows - 1) / kLnRows; }
+int ln_backward_blocks(int M) { return (M + kLnRows - 1) / kLnRows * kLnWaves; }
 
 hipError_t ln_backward(const float* x, const float* gamma, const float* dy, float* dx, int M, int d, float eps, float* pg,
                        float* pb, float* dgamma, float* dbeta, hipStream_t s) {
-    const int nb = ln_backward_blocks(M);
-    ln_backward_kernel<<<dim3(nb), dim3(64), 2 * d * sizeof(float), s>>>(x, gamma, dy, dx, M, d, eps, pg, pb);
-    colsum_reduce_kernel<<<dim3((d + 255) / 256), dim3(256), 0, s>>>(pg, nb, d, dgamma);
-    colsum_reduce_kernel<<<dim3((d + 255) / 256), dim3(256), 0, s>>>(pb, nb, d, dbeta);
+    const int nb = (M + kLnRows - 1) / kLnRows, np = ln_backward_blocks(M);
+    const dim3 grid(nb), block(64 * kLnWaves);
+    switch (d) {
+        case 768: ln_backward_kernel<12><<<grid, block, 0, s>>>(x, gamma, dy, dx, M, d, eps, pg, pb); break;
+        case 1024: ln_backward_kernel<16><<<grid, block, 0, s>>>(x, gamma, dy, dx, M, d, eps, pg, pb); break;
+        case 1600: ln_backward_kernel<25><<<grid, block, 0, s>>>(x, gamma, dy, dx, M, d, eps, pg, pb); break;
+        default: ln_backward_kernel<0><<<grid, block, 0, s>>>(x, gamma, dy, dx, M, d, eps, pg, pb); break;
+    }
+    colsum_reduce_kernel<<<dim3((d + 255) / 256), dim3(256), 0, s>>>(pg, np, d, dgamma);
+    colsum_reduce_kernel<<<dim3((d + 255) / 256), dim3(256), 0, s>>>(pb, np, d, dbeta);
     return hipGetLastError();
 }
 
@@ -456,14 +527,12 @@ hipError_t xent_grad(const float* logits, long ld, int M, int V, int Vp, const i
 
 hipError_t attention_backward(const void* qkv, const void* o, const float* dout, float* dqkv, float* lse, float* dvec,
                               int B, int H, int T, bool bf16, hipStream_t s) {
+    if (bf16)  // matrix-core kernels
+        return attention_backward_bf16(static_cast<const uint16_t*>(qkv), static_cast<const uint16_t*>(o), dout, dqkv,
+                                       lse, dvec, B, H, T, s);
     const dim3 grid((T + AB_ROWS - 1) / AB_ROWS, B * H), block(AB_T);
-    if (bf16) {
-        attn_bwd_q_kernel<true><<<grid, block, 0, s>>>(qkv, o, dout, dqkv, lse, dvec, H, T);
-        attn_bwd_kv_kernel<true><<<grid, block, 0, s>>>(qkv, dout, lse, dvec, dqkv, H, T);
-    } else {
-        attn_bwd_q_kernel<false><<<grid, block, 0, s>>>(qkv, o, dout, dqkv, lse, dvec, H, T);
-        attn_bwd_kv_kernel<false><<<grid, block, 0, s>>>(qkv, dout, lse, dvec, dqkv, H, T);
-    }
+    attn_bwd_q_kernel<false><<<grid, block, 0, s>>>(qkv, o, dout, dqkv, lse, dvec, H, T);
+    attn_bwd_kv_kernel<false><<<grid, block, 0, s>>>(qkv, dout, lse, dvec, dqkv, H, T);
     return hipGetLastError();
 }
 
