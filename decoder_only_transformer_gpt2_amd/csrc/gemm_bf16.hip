@@ -465,6 +465,7 @@ int choose_cfg(int M, int N, int K) {
     auto tiles = [&](int bm, int bn) { return (long)((M + bm - 1) / bm) * ((N + bn - 1) / bn); };
     if (tiles(256, 256) >= 4 * 256) return 20;  // vocabulary projection
     if (N <= 1024) return 12;
+    if (tiles(192, 256) < 128) return 12;  // few rows (weight gradients, short prompts): fill the CUs
     if (tiles(192, 256) <= 256) return 22;
     return 16;
 }

@@ -64,19 +64,25 @@ __global__ void __launch_bounds__(256) colsum_partial_kernel(const float* __rest
     __syncthreads();
     if (grp == 0 && c < C) part[(long)b * C + c] = ((acc4[0][cl] + acc4[1][cl]) + acc4[2][cl]) + acc4[3][cl];
 }
-// out[c] = sum over b < nb of part[b][c] (eight partial sums per thread, fixed order).
+// out[c] = sum over b < nb of part[b][c]: four groups of partial rows per column (eight loads in
+// flight per thread), combined in group order.
 __global__ void __launch_bounds__(256) colsum_reduce_kernel(const float* __restrict__ part, int nb, int C,
                                                             float* __restrict__ out) {
-    const int c = blockIdx.x * 256 + threadIdx.x;
-    if (c >= C) return;
+    __shared__ float acc4[4][64];
+    const int cl = threadIdx.x & 63, grp = threadIdx.x >> 6, c = blockIdx.x * 64 + cl;
+    const int per = (nb + 3) / 4, b0 = grp * per, b1 = min(nb, b0 + per);
     float a[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    int b = 0;
-    for (; b + 8 <= nb; b += 8) {
+    if (c < C) {
+        int b = b0;
+        for (; b + 8 <= b1; b += 8) {
 #pragma unroll
-        for (int u = 0; u < 8; ++u) a[u] += part[(long)(b + u) * C + c];
+            for (int u = 0; u < 8; ++u) a[u] += part[(long)(b + u) * C + c];
+        }
+        for (; b < b1; ++b) a[0] += part[(long)b * C + c];
     }
-    for (; b < nb; ++b) a[0] += part[(long)b * C + c];
-    out[c] = ((a[0] + a[1]) + (a[2] + a[3])) + ((a[4] + a[5]) + (a[6] + a[7]));
+    acc4[grp][cl] = ((a[0] + a[1]) + (a[2] + a[3])) + ((a[4] + a[5]) + (a[6] + a[7]));
+    __syncthreads();
+    if (grp == 0 && c < C) out[c] = ((acc4[0][cl] + acc4[1][cl]) + acc4[2][cl]) + acc4[3][cl];
 }
 
 // ------------------------------------------------------------------------------ LayerNorm backward
@@ -480,7 +486,7 @@ int colsum_blocks(int R) { return (R + kColRows - 1) / kColRows; }
 hipError_t colsum(const float* src, long ld, int R, int C, float* part, float* out, hipStream_t s) {
     const int nb = colsum_blocks(R);
     colsum_partial_kernel<<<dim3((C + 63) / 64, nb), dim3(256), 0, s>>>(src, ld, R, C, part);
-    colsum_reduce_kernel<<<dim3((C + 255) / 256), dim3(256), 0, s>>>(part, nb, C, out);
+    colsum_reduce_kernel<<<dim3((C + 63) / 64), dim3(256), 0, s>>>(part, nb, C, out);
     return hipGetLastError();
 }
 
@@ -496,8 +502,8 @@ hipError_t ln_backward(const float* x, const float* gamma, const float* dy, floa
         case 1600: ln_backward_kernel<25><<<grid, block, 0, s>>>(x, gamma, dy, dx, M, d, eps, pg, pb); break;
         default: ln_backward_kernel<0><<<grid, block, 0, s>>>(x, gamma, dy, dx, M, d, eps, pg, pb); break;
     }
-    colsum_reduce_kernel<<<dim3((d + 255) / 256), dim3(256), 0, s>>>(pg, np, d, dgamma);
-    colsum_reduce_kernel<<<dim3((d + 255) / 256), dim3(256), 0, s>>>(pb, np, d, dbeta);
+    colsum_reduce_kernel<<<dim3((d + 63) / 64), dim3(256), 0, s>>>(pg, np, d, dgamma);
+    colsum_reduce_kernel<<<dim3((d + 63) / 64), dim3(256), 0, s>>>(pb, np, d, dbeta);
     return hipGetLastError();
 }
 
