@@ -101,6 +101,32 @@ __device__ __forceinline__ void row_ln_stats(const float* __restrict__ xr, int n
     rstd = 1.0f / sqrtf(wave_sum(q) / (float)n + eps);
 }
 
+// row_ln_stats with the row read once into registers (n <= 4096): the same order, the same bits.
+__device__ __forceinline__ void row_ln_stats_reg(const float* __restrict__ xr, int n, float eps, float& mean,
+                                                 float& rstd) {
+    const int lane = threadIdx.x % GPT2_WAVE, nq = n / 4;
+    const f32x4_t* x4 = reinterpret_cast<const f32x4_t*>(xr);
+    f32x4_t v[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        const int c = lane + GPT2_WAVE * i;
+        v[i] = c < nq ? x4[c] : f32x4_t{0.f, 0.f, 0.f, 0.f};
+    }
+    float s = 0.f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+        if (lane + GPT2_WAVE * i < nq) s += (v[i][0] + v[i][1]) + (v[i][2] + v[i][3]);
+    mean = wave_sum(s) / (float)n;
+    float q = 0.f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+        if (lane + GPT2_WAVE * i < nq) {
+            const float a0 = v[i][0] - mean, a1 = v[i][1] - mean, a2 = v[i][2] - mean, a3 = v[i][3] - mean;
+            q += (a0 * a0 + a1 * a1) + (a2 * a2 + a3 * a3);
+        }
+    rstd = 1.0f / sqrtf(wave_sum(q) / (float)n + eps);
+}
+
 // Log-sum-exp partials in base 2: (m, s) stands for 2^m * s. Merging two keeps the larger maximum;
 // an empty partial has m = -inf and s = 0.
 __device__ __forceinline__ void lse_merge(float& m, float& s, float m2, float s2) {

@@ -49,24 +49,13 @@ __global__ __launch_bounds__(64 * KW) void gemm_skinny_kernel(const uint16_t* __
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / GPT2_WAVE), lane = threadIdx.x % GPT2_WAVE;
     const int r16 = lane & 15, g4 = lane >> 4;
     const int n0 = blockIdx.x * 16;
-    if (LNA) {
-        for (int m = wave; m < M; m += KW) {
-            float mean, rstd;
-            row_ln_stats(ex.ln_x + (size_t)m * K, K, ex.ln_eps, mean, rstd);
-            if (lane == 0) {
-                ln_mean[m] = mean;
-                ln_rstd[m] = rstd;
-            }
-        }
-        __syncthreads();
-    }
     // operand fragments: A row r16 (rows >= M are padding; they only reach outputs never stored),
     // W row n0 + r16, each lane 8 consecutive k at 8*g4 within a 32-wide slice
     const uint16_t* ap = A + (size_t)r16 * K + 8 * g4;
     const uint16_t* wp = W + (size_t)(n0 + r16) * K + 8 * g4;
     const bool arow = r16 < M;
     const float* xp = ex.ln_x + (size_t)r16 * K + 8 * g4;
-    const float a_mean = LNA && arow ? ln_mean[r16] : 0.f, a_rstd = LNA && arow ? ln_rstd[r16] : 0.f;
+    float a_mean = 0.f, a_rstd = 0.f;  // row r16's statistics, set once they are computed
     auto a_frag = [&](int c) -> bf16x8_t {
         if (!LNA) return *reinterpret_cast<const bf16x8_t*>(ap + c * 32);
         u32x4_t u = {0u, 0u, 0u, 0u};
@@ -87,22 +76,45 @@ __global__ __launch_bounds__(64 * KW) void gemm_skinny_kernel(const uint16_t* __
     };
     f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
     const int nch = K / 32;
-    int c = wave;
-    // four slices per round: their loads are all in flight before the first MFMA waits
-    for (; c + 3 * KW < nch; c += 4 * KW) {
-        bf16x8_t af[4], wf[4];
+    // rounds of up to eight slices: every load of a round is in flight before the first MFMA waits
+    // (a wavefront has six slices in the decoding shapes, so its W stream is one round trip). The
+    // first round's W loads are issued before the LayerNorm statistics, so they overlap.
+    bf16x8_t wf[8];
+    {
+        const int ns = min(8, (nch - wave + KW - 1) / KW);
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            af[u] = a_frag(c + u * KW);
-            wf[u] = *reinterpret_cast<const bf16x8_t*>(wp + (c + u * KW) * 32);
+        for (int u = 0; u < 8; ++u)
+            if (u < ns) wf[u] = *reinterpret_cast<const bf16x8_t*>(wp + (wave + u * KW) * 32);
+    }
+    if (LNA) {
+        for (int m = wave; m < M; m += KW) {
+            float mean, rstd;
+            row_ln_stats_reg(ex.ln_x + (size_t)m * K, K, ex.ln_eps, mean, rstd);
+            if (lane == 0) {
+                ln_mean[m] = mean;
+                ln_rstd[m] = rstd;
+            }
+        }
+        __syncthreads();
+        if (arow) {
+            a_mean = ln_mean[r16];
+            a_rstd = ln_rstd[r16];
+        }
+    }
+    for (int c = wave; c < nch; c += 8 * KW) {
+        const int ns = min(8, (nch - c + KW - 1) / KW);  // wave-uniform
+        bf16x8_t af[8];
+        if (c != wave) {
+#pragma unroll
+            for (int u = 0; u < 8; ++u)
+                if (u < ns) wf[u] = *reinterpret_cast<const bf16x8_t*>(wp + (c + u * KW) * 32);
         }
 #pragma unroll
-        for (int u = 0; u < 4; ++u) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[u], wf[u], acc, 0, 0, 0);
-    }
-    for (; c < nch; c += KW) {
-        const bf16x8_t af = a_frag(c);
-        const bf16x8_t wf = *reinterpret_cast<const bf16x8_t*>(wp + c * 32);
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, wf, acc, 0, 0, 0);
+        for (int u = 0; u < 8; ++u)
+            if (u < ns) af[u] = a_frag(c + u * KW);
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+            if (u < ns) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[u], wf[u], acc, 0, 0, 0);
     }
     red[wave][lane] = acc;
     __syncthreads();
