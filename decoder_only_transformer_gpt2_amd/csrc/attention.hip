@@ -41,7 +41,8 @@ __global__ __launch_bounds__(64 * WAVES * G) void attn_bf16_kernel(const uint16_
                                                                int64_t ksh, int64_t kst,
                                                                const uint16_t* __restrict__ V, int64_t vsb,
                                                                int64_t vsh, int64_t vst, uint16_t* __restrict__ O,
-                                                               int64_t osb, int64_t osh, int64_t ost, int B, int H,
+                                                               int64_t osb, int64_t osh, int64_t ost, int64_t osx,
+                                                               int B, int H,
                                                                int T, float scale_log2) {
     constexpr int QT = 16 * WAVES, NG = 64 * WAVES, CPT = KT * 8 / NG;  // 16-byte chunks per thread per tile
     // sK / sVt: [buffer][group]; after the loop the same bytes hold the partial results of group 1
@@ -228,7 +229,8 @@ __global__ __launch_bounds__(64 * WAVES * G) void attn_bf16_kernel(const uint16_
             uint2 u;
             u.x = pack_bf16x2(oacc[df][0] * inv, oacc[df][1] * inv);
             u.y = pack_bf16x2(oacc[df][2] * inv, oacc[df][3] * inv);
-            *reinterpret_cast<uint2*>(Ob + df * 16 + 4 * g4) = u;
+            // head dims df*16 + 4*g4 .. +3 lie in half df/2 of the head (32 dims each, osx apart)
+            *reinterpret_cast<uint2*>(Ob + (df >> 1) * osx + (df & 1) * 16 + 4 * g4) = u;
         }
     }
 }
@@ -293,7 +295,8 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(const float* __restrict__ 
 }  // namespace
 
 hipError_t attention_bf16(const uint16_t* q, const int64_t* qs, const uint16_t* k, const int64_t* ks, const uint16_t* v,
-                          const int64_t* vs, uint16_t* o, const int64_t* os, int B, int H, int T, hipStream_t s) {
+                          const int64_t* vs, uint16_t* o, const int64_t* os, int B, int H, int T, hipStream_t s,
+                          int64_t os_half) {
     const float scale_log2 = 0.125f * 1.4426950408889634f;  // (1/sqrt(64)) * log2(e)
     constexpr int WAVES = GPT2_ATT_WAVES;
     const int nqt = (T + 16 * WAVES - 1) / (16 * WAVES);
@@ -304,7 +307,7 @@ hipError_t attention_bf16(const uint16_t* q, const int64_t* qs, const uint16_t* 
 #define GPT2_ATT_LAUNCH(G)                                                                                         \
     attn_bf16_kernel<WAVES, G><<<grid, dim3(64 * WAVES * G), 0, s>>>(q, qs[0], qs[1], qs[2], k, ks[0], ks[1], ks[2], \
                                                                      v, vs[0], vs[1], vs[2], o, os[0], os[1], os[2],  \
-                                                                     B, H, T, scale_log2)
+                                                                     os_half, B, H, T, scale_log2)
     if (nqt * B * H <= 512)
         GPT2_ATT_LAUNCH(2);
     else

@@ -172,12 +172,22 @@ hipError_t embed(const int32_t* tok, const void* wte, const void* wpe, float* x,
                  int n_vocab, bool bf16, int32_t* flags, hipStream_t s);
 int embed_flag_count(int M);
 
+// k-blocked layout of a bf16 matrix with `rows` rows and K columns (K a multiple of 32): the
+// 32-column blocks one after another, each holding all rows, [K/32][rows][32]. Element (r, k) sits
+// at (k / 32 * rows + r) * 32 + k % 32, so the 32-column slab of any range of rows is one
+// contiguous run of memory, which the GEMM's DMA reads at full cache-line width.
+
+// kb_rows > 0 (bf16 only): y is written k-blocked with that many rows per block (>= M).
 hipError_t layernorm(const float* x, const float* g, const float* b, void* y, int M, int n, float eps,
-                     bool out_bf16, hipStream_t s);
+                     bool out_bf16, hipStream_t s, int kb_rows = 0);
 
 // A must have a_rows >= M readable rows and W w_rows >= N (rows past them are never read).
+// kb: A and W are k-blocked with a_rows and w_rows rows per block (M > kSkinnyM only).
+// c_kb_rows > 0: the bf16 output (bias or GELU epilogues) is written k-blocked with that many rows
+// per block (>= M; N a multiple of 32; M > kSkinnyM only).
 hipError_t gemm_bf16(const uint16_t* A, const uint16_t* W, const float* bias, void* C, int M, int N, int K,
-                     long ldc, int epi, int gelu_erf, int a_rows, int w_rows, const HeadOut& ho, hipStream_t s);
+                     long ldc, int epi, int gelu_erf, int a_rows, int w_rows, const HeadOut& ho, hipStream_t s,
+                     bool kb = false, int c_kb_rows = 0);
 hipError_t gemm_f32(const float* A, const float* W, const float* bias, void* C, int M, int N, int K, long ldc,
                     int epi, int gelu_erf, const HeadOut& ho, hipStream_t s);
 // The same for M <= kSkinnyM rows (gemm_bf16 dispatches to it): 16 output columns per workgroup,
@@ -217,9 +227,11 @@ hipError_t xent_rows(const float* pm, const float* ps, const int32_t* tgt, const
 // loss[0] = sum of nll over rows with tgt >= 0 / their count (NaN when none), summed in a fixed order.
 hipError_t xent_mean(const float* nll, const int32_t* tgt, int M, float* loss, hipStream_t s);
 
+// o element (b, h, t, e) at o + b*os[0] + h*os[1] + t*os[2] + (e / 32) * os_half + e % 32 (os_half = 32
+// for a plain row; the k-blocked layout of [B*T, H*64] has os = {T*32, 2*rows*32, 32}, os_half = rows*32).
 hipError_t attention_bf16(const uint16_t* q, const int64_t* qs, const uint16_t* k, const int64_t* ks,
                           const uint16_t* v, const int64_t* vs, uint16_t* o, const int64_t* os, int B, int H,
-                          int T, hipStream_t s);
+                          int T, hipStream_t s, int64_t os_half = 32);
 hipError_t attention_f32(const float* q, const int64_t* qs, const float* k, const int64_t* ks, const float* v,
                          const int64_t* vs, float* o, const int64_t* os, int B, int H, int T, hipStream_t s);
 
@@ -277,5 +289,7 @@ hipError_t embed_backward(const int32_t* tok, const float* dx, int B, int T, int
 // dst[i] = i < n_src ? convert(src[i]) : 0 for i < n_dst (element types fp32 or bf16).
 hipError_t convert(const void* src, bool src_bf16, void* dst, bool dst_bf16, long n_src, long n_dst,
                    hipStream_t s);
+// dst = the k-blocked copy of the row-major bf16 matrix src [rows][K] (K a multiple of 32).
+hipError_t kblock_bf16(const uint16_t* src, uint16_t* dst, long rows, int K, hipStream_t s);
 
 }  // namespace gpt2k

@@ -55,7 +55,7 @@ __device__ __forceinline__ TileCoord tile_of(int b, int nblk, int tiles_m, int g
 // operations of this wavefront are outstanding (expcnt not waited on).
 constexpr int waitcnt_imm(int vm, int lgkm) { return (vm & 0xF) | ((vm >> 4) << 14) | (7 << 4) | (lgkm << 8); }
 
-template <int BM, int BN, int BK, int S, int WGM, int WGN, int EPI>
+template <int BM, int BN, int BK, int S, int WGM, int WGN, int EPI, bool KB>
 // Two workgroups per CU (256 registers per lane) wherever the ring fits twice in LDS and the
 // wave tile is at most 128 x 64.
 __global__ __launch_bounds__(64 * WGM * WGN,
@@ -63,7 +63,7 @@ __global__ __launch_bounds__(64 * WGM * WGN,
 void gemm_bf16_kernel(
     const uint16_t* __restrict__ A, const uint16_t* __restrict__ W, const float* __restrict__ bias,
     void* __restrict__ Cv, int M, int N, int K, int ldc, int a_rows, int w_rows, int tiles_m,
-    int group_m, HeadOut ho) {
+    int group_m, int c_kb, HeadOut ho) {
     constexpr int NT = 64 * WGM * WGN, NW = WGM * WGN;
     constexpr bool HEAD = EPI == EPI_LOGITS || EPI == EPI_LSE;  // vocabulary projection: no bias
     constexpr int WM = BM / WGM, WN = BN / WGN, FM = WM / 16, FN = WN / 16;
@@ -103,6 +103,7 @@ void gemm_bf16_kernel(
     // i.e. row q*RPI + L/CPR, swizzled chunk L%CPR, so it fetches the chunk that belongs there.
     const uint16_t* src[PW];
     int lds_off[PW];
+    [[maybe_unused]] int kstep[PW];
 #pragma unroll
     for (int p = 0; p < PW; ++p) {
         // past the stage's last instruction, repeat it: the same bytes to the same LDS block, so
@@ -114,14 +115,22 @@ void gemm_bf16_kernel(
         const int row = is_a ? srow : srow - BM;
         const int chunk = swz_chunk(row, sch);
         const int g = is_a ? min(m0 + row, a_rows - 1) : min(n0 + row, w_rows - 1);
-        src[p] = (is_a ? A : W) + (size_t)g * K + chunk * 8;
+        if (KB) {
+            // k-blocked operands ([K/32][rows][32]): chunk c of row g at k0 = 0 sits in block c/4
+            const int rows = is_a ? a_rows : w_rows;
+            src[p] = (is_a ? A : W) + ((size_t)(chunk >> 2) * rows + g) * 32 + (chunk & 3) * 8;
+            kstep[p] = rows;
+        } else {
+            src[p] = (is_a ? A : W) + (size_t)g * K + chunk * 8;
+        }
         lds_off[p] = q * RPI * BK;  // element offset of the instruction's 1 KB block
     }
     auto issue = [&](int st, int k0) {
         uint16_t* base = slot(st);
 #pragma unroll
         for (int p = 0; p < PW; ++p)
-            __builtin_amdgcn_global_load_lds((const void*)(src[p] + k0),
+            // k-blocked: block k0/32 starts k0/32 * rows * 32 = k0 * rows elements further on
+            __builtin_amdgcn_global_load_lds((const void*)(src[p] + (KB ? (size_t)k0 * kstep[p] : (size_t)k0)),
                                              (__attribute__((address_space(3))) void*)(base + lds_off[p]), 16, 0, 0);
     };
 
@@ -329,9 +338,10 @@ void gemm_bf16_kernel(
                 }
             }
         } else {
-            // bf16 rows: eight values (16 bytes) per lane
+            // bf16 rows: eight values (16 bytes) per lane (eight columns never straddle a 32-column
+            // block of the k-blocked layout)
             uint16_t* Cs = static_cast<uint16_t*>(Cv) + (size_t)rs * ldc + col0;
-            const bool vec = (ldc & 7) == 0;
+            const bool vec = c_kb || (ldc & 7) == 0;
 #pragma unroll
             for (int it = 0; it < (16 * (WN / 8) + GPT2_WAVE - 1) / GPT2_WAVE; ++it) {
                 const int idx = it * GPT2_WAVE + lane;
@@ -340,6 +350,10 @@ void gemm_bf16_kernel(
                 if (CHK && r >= rows) continue;
                 const float* sv = &scr[r * SP + c];
                 uint16_t* cp = Cs + r * ldc + c;
+                if (c_kb) {
+                    const int col = col0 + c;
+                    cp = static_cast<uint16_t*>(Cv) + ((size_t)(col >> 5) * c_kb + rs + r) * 32 + (col & 31);
+                }
                 if ((!CHK || c + 8 <= cols) && vec) {
                     u32x4_t pk;
                     pk[0] = pack_bf16x2(sv[0], sv[1]);
@@ -454,7 +468,7 @@ constexpr TileCfg kCfgs[] = {
 // tiles for every CU many times over, uses 256 x 128 tiles of four waves with a three-stage
 // 32-wide ring, two workgroups per CU, so that one workgroup's epilogue (the fp32 logits
 // stores) overlaps the other's main loop.
-int choose_cfg(int M, int N, int K) {
+int choose_cfg(int M, int N, int K, bool kb) {
 #ifdef GPT2_GEMM_TUNE
     if (const char* e = getenv("GPT2_GEMM_CFG")) {
         const int c = atoi(e);
@@ -467,12 +481,14 @@ int choose_cfg(int M, int N, int K) {
     if (N <= 1024) return 12;
     if (tiles(192, 256) < 128) return 12;  // few rows (weight gradients, short prompts): fill the CUs
     if (tiles(192, 256) <= 256) return 22;
+    // k-blocked operands stream at full cache-line width, which favours the deeper 32-wide ring
+    if (kb && tiles(256, 192) <= 256) return 23;
     return 16;
 }
 
-template <int BM, int BN, int BK, int S, int WGM, int WGN>
+template <int BM, int BN, int BK, int S, int WGM, int WGN, bool KB>
 hipError_t launch_cfg(const uint16_t* A, const uint16_t* W, const float* bias, void* C, int M, int N, int K, long ldc,
-                      int epi, int gelu_erf, int a_rows, int w_rows, const HeadOut& ho, hipStream_t s) {
+                      int epi, int gelu_erf, int a_rows, int w_rows, int c_kb, const HeadOut& ho, hipStream_t s) {
     const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
     // group_m > 0: XCD-contiguous remap + groups of group_m row-tiles; < 0: plain order, groups of
     // -group_m. Measured with cold caches (as inside a forward): the vocabulary projection is fastest
@@ -485,8 +501,8 @@ hipError_t launch_cfg(const uint16_t* A, const uint16_t* W, const float* bias, v
 #endif
     dim3 grid(tiles_m * tiles_n), block(64 * WGM * WGN);
 #define GPT2_LAUNCH(E)                                                                                      \
-    gemm_bf16_kernel<BM, BN, BK, S, WGM, WGN, E><<<grid, block, 0, s>>>(A, W, bias, C, M, N, K, ldc,           \
-                                                                      a_rows, w_rows, tiles_m, group_m, ho)
+    gemm_bf16_kernel<BM, BN, BK, S, WGM, WGN, E, KB><<<grid, block, 0, s>>>(A, W, bias, C, M, N, K, ldc,           \
+                                                                      a_rows, w_rows, tiles_m, group_m, c_kb, ho)
     switch (epi) {
         case EPI_BIAS: GPT2_LAUNCH(EPI_BIAS); break;
         case EPI_BIAS_GELU:
@@ -505,18 +521,27 @@ hipError_t launch_cfg(const uint16_t* A, const uint16_t* W, const float* bias, v
 
 }  // namespace
 
-int gemm_bf16_tile_n(int M, int N, int K) { return M <= kSkinnyM ? 16 : kCfgs[choose_cfg(M, N, K)].bn; }
+// (the vocabulary projection takes the same tile in either operand layout)
+int gemm_bf16_tile_n(int M, int N, int K) { return M <= kSkinnyM ? 16 : kCfgs[choose_cfg(M, N, K, false)].bn; }
 
 hipError_t gemm_bf16(const uint16_t* A, const uint16_t* W, const float* bias, void* C, int M, int N, int K, long ldc,
-                     int epi, int gelu_erf, int a_rows, int w_rows, const HeadOut& ho, hipStream_t s) {
+                     int epi, int gelu_erf, int a_rows, int w_rows, const HeadOut& ho, hipStream_t s, bool kb,
+                     int c_kb_rows) {
     if (ldc < N || ldc > (1 << 26)) return hipErrorInvalidValue;  // in-strip offsets are 32-bit
-    if (M <= kSkinnyM)  // a few rows: a stream over W
+    if (M <= kSkinnyM) {  // a few rows: a stream over W (row-major operands and output only)
+        if (kb || c_kb_rows) return hipErrorInvalidValue;
         return gemm_bf16_skinny(A, W, bias, C, M, N, K, (int)ldc, epi, gelu_erf, a_rows, w_rows, ho, SkinnyExtra(), s);
-    switch (choose_cfg(M, N, K)) {
+    }
+    if (c_kb_rows && (epi == EPI_BIAS_RESIDUAL || epi == EPI_LOGITS || epi == EPI_LSE || c_kb_rows < M || N % 32))
+        return hipErrorInvalidValue;  // k-blocked output: bf16 epilogues only
+    if (kb && K % 32) return hipErrorInvalidValue;
+    switch (choose_cfg(M, N, K, kb)) {
 #define GPT2_CFG(i, bm, bn, bk, st, wgm, wgn)                                                                    \
     case i:                                                                                                      \
-        return launch_cfg<bm, bn, bk, st, wgm, wgn>(A, W, bias, C, M, N, K, ldc, epi, gelu_erf, a_rows, w_rows, ho, \
-                                                    s);
+        return kb ? launch_cfg<bm, bn, bk, st, wgm, wgn, true>(A, W, bias, C, M, N, K, ldc, epi, gelu_erf, a_rows,  \
+                                                               w_rows, c_kb_rows, ho, s)                         \
+                  : launch_cfg<bm, bn, bk, st, wgm, wgn, false>(A, W, bias, C, M, N, K, ldc, epi, gelu_erf, a_rows, \
+                                                                w_rows, c_kb_rows, ho, s);
 #ifdef GPT2_GEMM_TUNE
         GPT2_CFG(0, 256, 256, 32, 4, 2, 4)
         GPT2_CFG(1, 256, 256, 64, 2, 2, 4)
@@ -551,6 +576,7 @@ hipError_t gemm_bf16(const uint16_t* A, const uint16_t* W, const float* bias, vo
         GPT2_CFG(16, 256, 192, 64, 2, 2, 4)
         GPT2_CFG(20, 256, 128, 32, 3, 2, 2)
         GPT2_CFG(22, 192, 256, 32, 5, 2, 4)
+        GPT2_CFG(23, 256, 192, 32, 5, 2, 4)
 #endif
 #undef GPT2_CFG
     }

@@ -48,6 +48,9 @@ struct KVArgs {
 struct gpt2_model {
     gpt2_config_t cfg;
     std::vector<TensorSlot> slots;
+    // bf16: byte offset of the k-blocked copy of each GEMM weight (wte and the four projections of
+    // every layer), read by the tiled GEMMs of the forward; 0 for other tensors
+    std::vector<size_t> kb_offset;
     size_t weight_bytes = 0;
     void* weights = nullptr;  // borrowed device pointer, set by gpt2_load_weights
     bool loaded = false;
@@ -80,10 +83,23 @@ void build_layout(gpt2_model* m) {
         const size_t bytes = s.matrix ? (size_t)s.rows_padded * s.cols * act_size(m) : (size_t)s.rows * 4;
         off = align_up(off + bytes, kAlign);
     }
+    m->kb_offset.assign(m->slots.size(), 0);
+    if (c.dtype == GPT2_BF16) {
+        auto kb = [&](int i) {
+            m->kb_offset[i] = off;
+            off = align_up(off + (size_t)m->slots[i].rows_padded * m->slots[i].cols * 2, kAlign);
+        };
+        kb(0);  // wte as the lm_head operand
+        for (int l = 0; l < c.n_layer; ++l)
+            for (int t : {ATTN_W, APROJ_W, FC_W, MPROJ_W}) kb(2 + l * PER_LAYER + t);
+    }
     m->weight_bytes = off;
 }
 
 const void* wptr(const gpt2_model* m, int idx) { return static_cast<const char*>(m->weights) + m->slots[idx].offset; }
+const void* wptr_kb(const gpt2_model* m, int idx) {
+    return static_cast<const char*>(m->weights) + m->kb_offset[idx];
+}
 int layer_idx(int l, int t) { return 2 + l * PER_LAYER + t; }
 
 WorkspaceLayout ws_layout(const gpt2_model* m, int B, int T) {
@@ -136,15 +152,18 @@ gpt2_status check_run_args(const gpt2_model* m, const int32_t* tokens, int B, in
     return GPT2_OK;
 }
 
-// Linear dispatch on the compute dtype.
+// Linear dispatch on the compute dtype. kb (bf16, tiled GEMM): A is k-blocked with M rounded up to
+// kRowPad rows per block and the weight's k-blocked copy is read; c_kb: the bf16 output is written
+// k-blocked the same way.
 hipError_t linear(const gpt2_model* m, const void* A, int widx, int bidx, void* C, int M, int N, int K, long ldc,
-                  int epi, const gpt2k::HeadOut& ho, hipStream_t s) {
+                  int epi, const gpt2k::HeadOut& ho, hipStream_t s, bool kb = false, bool c_kb = false) {
     const float* bias = bidx >= 0 ? static_cast<const float*>(wptr(m, bidx)) : nullptr;
     const int ge = m->cfg.gelu == GPT2_GELU_ERF;
     if (is_bf16(m))
-        return gpt2k::gemm_bf16(static_cast<const uint16_t*>(A), static_cast<const uint16_t*>(wptr(m, widx)), bias, C, M,
-                                N, K, ldc, epi, ge, (int)round_up(M, kRowPad), (int)m->slots[widx].rows_padded, ho,
-                                s);
+        return gpt2k::gemm_bf16(static_cast<const uint16_t*>(A),
+                                static_cast<const uint16_t*>(kb ? wptr_kb(m, widx) : wptr(m, widx)), bias, C, M, N, K,
+                                ldc, epi, ge, (int)round_up(M, kRowPad), (int)m->slots[widx].rows_padded, ho, s, kb,
+                                c_kb ? (int)round_up(M, kRowPad) : 0);
     return gpt2k::gemm_f32(static_cast<const float*>(A), static_cast<const float*>(wptr(m, widx)), bias, C, M, N, K, ldc,
                            epi, ge, ho, s);
 }
@@ -208,7 +227,12 @@ gpt2_status enqueue_trunk(const gpt2_model* m, const int32_t* tokens, int B, int
                                        c.gelu == GPT2_GELU_ERF, (int)w.Mp, (int)m->slots[widx].rows_padded, {}, ex, s);
     };
     const int64_t qs[3] = {(int64_t)T * 3 * d, 64, 3 * d};
-    const int64_t os[3] = {(int64_t)T * d, 64, d};
+    // bf16 with tiled GEMMs: the operands the GEMMs read (the LayerNorm outputs, the attention
+    // output and the GELU output) are written k-blocked, Mp rows per 32-column block
+    const bool kbl = bf && M > gpt2k::kSkinnyM && !kv.from_cache;
+    const int Mp = kbl ? (int)w.Mp : 0;
+    const int64_t os[3] = {kbl ? (int64_t)T * 32 : (int64_t)T * d, kbl ? (int64_t)2 * Mp * 32 : 64, kbl ? 32 : d};
+    const int64_t os_half = kbl ? (int64_t)Mp * 32 : 32;
     const size_t as = act_size(m);
     for (int l = 0; l < n_layers; ++l) {
         auto L = [&](int t) { return layer_idx(l, t); };
@@ -233,8 +257,9 @@ gpt2_status enqueue_trunk(const gpt2_model* m, const int32_t* tokens, int B, int
             ex.kv_pos = kv.pos0;
             GPT2_RUN(GPT2_K_QKV, skinny(L(ATTN_W), L(ATTN_B), qkv, 3 * d, d, gpt2k::EPI_BIAS, ex));
         } else {
-            GPT2_RUN(GPT2_K_LN, gpt2k::layernorm(x, vecp(LN1_W), vecp(LN1_B), a, M, d, c.ln_eps, bf, s));
-            GPT2_RUN(GPT2_K_QKV, linear(m, a, L(ATTN_W), L(ATTN_B), qkv, M, 3 * d, d, 3 * d, gpt2k::EPI_BIAS, {}, s));
+            GPT2_RUN(GPT2_K_LN, gpt2k::layernorm(x, vecp(LN1_W), vecp(LN1_B), a, M, d, c.ln_eps, bf, s, Mp));
+            GPT2_RUN(GPT2_K_QKV,
+                     linear(m, a, L(ATTN_W), L(ATTN_B), qkv, M, 3 * d, d, 3 * d, gpt2k::EPI_BIAS, {}, s, kbl));
             if (kv.cache) GPT2_RUN(GPT2_K_KV, gpt2k::kv_append(qkv, B, T, H, kv.pos0, kc, vc, c.n_ctx, bf, s));
         }
         if (kv.from_cache)
@@ -243,14 +268,14 @@ gpt2_status enqueue_trunk(const gpt2_model* m, const int32_t* tokens, int B, int
             GPT2_RUN(GPT2_K_ATTN, gpt2k::attention_bf16(reinterpret_cast<const uint16_t*>(qb), qs,
                                                         reinterpret_cast<const uint16_t*>(qb + d * as), qs,
                                                         reinterpret_cast<const uint16_t*>(qb + 2 * d * as), qs,
-                                                        static_cast<uint16_t*>(o), os, B, H, T, s));
+                                                        static_cast<uint16_t*>(o), os, B, H, T, s, os_half));
         else
             GPT2_RUN(GPT2_K_ATTN, gpt2k::attention_f32(reinterpret_cast<const float*>(qb), qs,
                                                        reinterpret_cast<const float*>(qb + d * as), qs,
                                                        reinterpret_cast<const float*>(qb + 2 * d * as), qs,
                                                        static_cast<float*>(o), os, B, H, T, s));
         GPT2_RUN(GPT2_K_ATTN_PROJ, linear(m, o, L(APROJ_W), L(APROJ_B), x, M, d, d, d, gpt2k::EPI_BIAS_RESIDUAL,
-                                          {}, s));
+                                          {}, s, kbl));
         if (fuse) {  // ln_2 inside the c_fc projection
             gpt2k::SkinnyExtra ex;
             ex.ln_x = x;
@@ -259,11 +284,12 @@ gpt2_status enqueue_trunk(const gpt2_model* m, const int32_t* tokens, int B, int
             ex.ln_eps = c.ln_eps;
             GPT2_RUN(GPT2_K_FC, skinny(L(FC_W), L(FC_B), hid, f, d, gpt2k::EPI_BIAS_GELU, ex));
         } else {
-            GPT2_RUN(GPT2_K_LN, gpt2k::layernorm(x, vecp(LN2_W), vecp(LN2_B), a, M, d, c.ln_eps, bf, s));
-            GPT2_RUN(GPT2_K_FC, linear(m, a, L(FC_W), L(FC_B), hid, M, f, d, f, gpt2k::EPI_BIAS_GELU, {}, s));
+            GPT2_RUN(GPT2_K_LN, gpt2k::layernorm(x, vecp(LN2_W), vecp(LN2_B), a, M, d, c.ln_eps, bf, s, Mp));
+            GPT2_RUN(GPT2_K_FC,
+                     linear(m, a, L(FC_W), L(FC_B), hid, M, f, d, f, gpt2k::EPI_BIAS_GELU, {}, s, kbl, kbl));
         }
         GPT2_RUN(GPT2_K_MLP_PROJ, linear(m, hid, L(MPROJ_W), L(MPROJ_B), x, M, d, f, d, gpt2k::EPI_BIAS_RESIDUAL,
-                                         {}, s));
+                                         {}, s, kbl));
     }
     return GPT2_OK;
 }
@@ -278,16 +304,17 @@ gpt2_status enqueue_forward(const gpt2_model* m, const int32_t* tokens, int B, i
     gpt2_status st = enqueue_trunk(m, tokens, B, T, c.n_layer, ws, w, q);
     if (st != GPT2_OK) return st;
     const int ln_f = 2 + c.n_layer * PER_LAYER;
+    const bool kbl = is_bf16(m) && M > gpt2k::kSkinnyM;  // the head reads a k-blocked ln_f output
     GPT2_RUN(GPT2_K_LN_F, gpt2k::layernorm(reinterpret_cast<float*>(ws + w.x), static_cast<const float*>(wptr(m, ln_f)),
                                            static_cast<const float*>(wptr(m, ln_f + 1)), ws + w.a, M, c.d_model,
-                                           c.ln_eps, is_bf16(m), s));
+                                           c.ln_eps, is_bf16(m), s, kbl ? (int)w.Mp : 0));
     gpt2k::HeadOut ho;
     if (argmax) {
         ho.pv = reinterpret_cast<float*>(ws + w.amax_v);
         ho.pi = reinterpret_cast<int32_t*>(ws + w.amax_i);
     }
     GPT2_RUN(GPT2_K_LM_HEAD,
-             linear(m, ws + w.a, 0, -1, logits, M, c.n_vocab, c.d_model, c.n_vocab, gpt2k::EPI_LOGITS, ho, s));
+             linear(m, ws + w.a, 0, -1, logits, M, c.n_vocab, c.d_model, c.n_vocab, gpt2k::EPI_LOGITS, ho, s, kbl));
     if (argmax) GPT2_RUN(GPT2_K_ARGMAX, gpt2k::argmax_reduce(ho.pv, ho.pi, M, w.n_part, argmax, s));
     return GPT2_OK;
 }
@@ -303,9 +330,10 @@ gpt2_status enqueue_forward_loss(const gpt2_model* m, const int32_t* tokens, con
     gpt2_status st = enqueue_trunk(m, tokens, B, T, c.n_layer, ws, w, q);
     if (st != GPT2_OK) return st;
     const int ln_f = 2 + c.n_layer * PER_LAYER;
+    const bool kbl = is_bf16(m) && M > gpt2k::kSkinnyM;
     GPT2_RUN(GPT2_K_LN_F, gpt2k::layernorm(reinterpret_cast<float*>(ws + w.x), static_cast<const float*>(wptr(m, ln_f)),
                                            static_cast<const float*>(wptr(m, ln_f + 1)), ws + w.a, M, c.d_model,
-                                           c.ln_eps, is_bf16(m), s));
+                                           c.ln_eps, is_bf16(m), s, kbl ? (int)w.Mp : 0));
     int32_t* tgt = reinterpret_cast<int32_t*>(ws + w.tgt);
     GPT2_RUN(GPT2_K_XENT, gpt2k::xent_targets(labels ? labels : tokens, M, T, c.n_vocab, tgt,
                                               reinterpret_cast<int32_t*>(ws + w.flags), s));
@@ -315,7 +343,7 @@ gpt2_status enqueue_forward_loss(const gpt2_model* m, const int32_t* tokens, con
     ho.tgt = tgt;
     ho.tgt_logit = reinterpret_cast<float*>(ws + w.tgt_logit);
     GPT2_RUN(GPT2_K_LM_HEAD,
-             linear(m, ws + w.a, 0, -1, nullptr, M, c.n_vocab, c.d_model, c.n_vocab, gpt2k::EPI_LSE, ho, s));
+             linear(m, ws + w.a, 0, -1, nullptr, M, c.n_vocab, c.d_model, c.n_vocab, gpt2k::EPI_LSE, ho, s, kbl));
     GPT2_RUN(GPT2_K_XENT, gpt2k::xent_rows(ho.pv, ho.ps, tgt, ho.tgt_logit, M, w.n_part, nll, s));
     GPT2_RUN(GPT2_K_XENT, gpt2k::xent_mean(nll, tgt, M, loss, s));
     return GPT2_OK;
@@ -636,6 +664,10 @@ gpt2_status gpt2_load_weights(gpt2_model* m, const void* const* src, int32_t n_s
         if (s.matrix) {
             const long n = (long)s.rows * s.cols, np = (long)s.rows_padded * s.cols;
             GPT2_HIP(gpt2k::convert(src[i], sb, d, is_bf16(m), n, np, stream));
+            if (m->kb_offset[i])
+                GPT2_HIP(gpt2k::kblock_bf16(reinterpret_cast<const uint16_t*>(d),
+                                            reinterpret_cast<uint16_t*>(static_cast<char*>(dst) + m->kb_offset[i]),
+                                            s.rows_padded, (int)s.cols, stream));
         } else {
             GPT2_HIP(gpt2k::convert(src[i], sb, d, false, s.rows, s.rows, stream));
         }

@@ -58,7 +58,7 @@ __global__ __launch_bounds__(256) void embed_kernel(const int32_t* __restrict__ 
 template <int NV, bool OUT_BF16>
 __global__ __launch_bounds__(256) void layernorm_kernel(const float* __restrict__ x, const float* __restrict__ g,
                                                         const float* __restrict__ b, void* __restrict__ y, int M,
-                                                        int n, float eps) {
+                                                        int n, float eps, int kb_rows) {
     const int wave = threadIdx.x / GPT2_WAVE, lane = threadIdx.x % GPT2_WAVE;
     const int row = blockIdx.x * kRowsPerBlock + wave;
     if (row >= M) return;
@@ -100,7 +100,11 @@ __global__ __launch_bounds__(256) void layernorm_kernel(const float* __restrict_
                 uint2 p;
                 p.x = pack_bf16x2(o.x, o.y);
                 p.y = pack_bf16x2(o.z, o.w);
-                reinterpret_cast<uint2*>(static_cast<uint16_t*>(y) + (size_t)row * n)[c] = p;
+                if (kb_rows)  // k-blocked: columns 4c..4c+3 share one 32-column block
+                    *reinterpret_cast<uint2*>(static_cast<uint16_t*>(y) +
+                                              ((size_t)(c >> 3) * kb_rows + row) * 32 + (c & 7) * 4) = p;
+                else
+                    reinterpret_cast<uint2*>(static_cast<uint16_t*>(y) + (size_t)row * n)[c] = p;
             } else {
                 reinterpret_cast<float4*>(static_cast<float*>(y) + (size_t)row * n)[c] = o;
             }
@@ -244,14 +248,27 @@ __global__ __launch_bounds__(256) void convert_kernel(const void* __restrict__ s
     }
 }
 
+// One 16-byte chunk (8 columns) per thread: chunk j of row r goes to block j/4 of the k-blocked copy.
+__global__ __launch_bounds__(256) void kblock_kernel(const uint16_t* __restrict__ src, uint16_t* __restrict__ dst,
+                                                     long rows, int K) {
+    const int cpr = K / 8;  // chunks per row
+    const long n = rows * cpr;
+    for (long i = (long)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (long)gridDim.x * blockDim.x) {
+        const long r = i / cpr;
+        const int j = (int)(i % cpr);
+        const u32x4_t v = *reinterpret_cast<const u32x4_t*>(src + r * K + j * 8);
+        *reinterpret_cast<u32x4_t*>(dst + ((long)(j >> 2) * rows + r) * 32 + (j & 3) * 8) = v;
+    }
+}
+
 template <int NV>
 hipError_t launch_ln(const float* x, const float* g, const float* b, void* y, int M, int n, float eps, bool out_bf16,
-                     hipStream_t s) {
+                     int kb_rows, hipStream_t s) {
     dim3 grid((M + kRowsPerBlock - 1) / kRowsPerBlock), block(256);
     if (out_bf16)
-        layernorm_kernel<NV, true><<<grid, block, 0, s>>>(x, g, b, y, M, n, eps);
+        layernorm_kernel<NV, true><<<grid, block, 0, s>>>(x, g, b, y, M, n, eps, kb_rows);
     else
-        layernorm_kernel<NV, false><<<grid, block, 0, s>>>(x, g, b, y, M, n, eps);
+        layernorm_kernel<NV, false><<<grid, block, 0, s>>>(x, g, b, y, M, n, eps, 0);
     return hipGetLastError();
 }
 
@@ -270,11 +287,12 @@ hipError_t embed(const int32_t* tok, const void* wte, const void* wpe, float* x,
 }
 
 hipError_t layernorm(const float* x, const float* g, const float* b, void* y, int M, int n, float eps, bool out_bf16,
-                     hipStream_t s) {
+                     hipStream_t s, int kb_rows) {
+    if (kb_rows && (!out_bf16 || kb_rows < M || n % 32)) return hipErrorInvalidValue;
     const int nq = n / 4;
-    if (nq <= 4 * GPT2_WAVE) return launch_ln<4>(x, g, b, y, M, n, eps, out_bf16, s);
-    if (nq <= 8 * GPT2_WAVE) return launch_ln<8>(x, g, b, y, M, n, eps, out_bf16, s);
-    return launch_ln<16>(x, g, b, y, M, n, eps, out_bf16, s);  // n <= 4096 (checked by the callers)
+    if (nq <= 4 * GPT2_WAVE) return launch_ln<4>(x, g, b, y, M, n, eps, out_bf16, kb_rows, s);
+    if (nq <= 8 * GPT2_WAVE) return launch_ln<8>(x, g, b, y, M, n, eps, out_bf16, kb_rows, s);
+    return launch_ln<16>(x, g, b, y, M, n, eps, out_bf16, kb_rows, s);  // n <= 4096 (checked by the callers)
 }
 
 hipError_t argmax_reduce(const float* pv, const int32_t* pi, int M, int n_part, int32_t* out, hipStream_t s) {
@@ -300,6 +318,14 @@ hipError_t xent_rows(const float* pm, const float* ps, const int32_t* tgt, const
 
 hipError_t xent_mean(const float* nll, const int32_t* tgt, int M, float* loss, hipStream_t s) {
     xent_mean_kernel<<<dim3(1), dim3(1024), 0, s>>>(nll, tgt, M, loss);
+    return hipGetLastError();
+}
+
+hipError_t kblock_bf16(const uint16_t* src, uint16_t* dst, long rows, int K, hipStream_t s) {
+    if (K % 32 || rows <= 0) return hipErrorInvalidValue;
+    long blocks = (rows * (K / 8) + 255) / 256;
+    if (blocks > 65536) blocks = 65536;
+    kblock_kernel<<<dim3((unsigned)blocks), dim3(256), 0, s>>>(src, dst, rows, K);
     return hipGetLastError();
 }
 

@@ -90,7 +90,10 @@ gpt2_status gpt2_tensor_shape(const gpt2_model* m, int32_t i, int64_t* rows, int
 
 /* Bytes of the packed device weight buffer gpt2_load_weights fills. Matrices are stored in the
  * compute dtype with their row count padded to a multiple of 256 (padding rows are zero);
- * vectors are fp32; every tensor starts on a 256-byte boundary. */
+ * vectors are fp32; every tensor starts on a 256-byte boundary. A bf16 model also holds, after the
+ * source tensors, a k-blocked copy of wte and of the four projection matrices of every layer
+ * ([cols/32][rows padded][32]: 32-column blocks of all rows one after another), which the tiled
+ * projections of the forward read so that every slab of a K step is contiguous. */
 size_t gpt2_weight_bytes(const gpt2_model* m);
 
 /* Bytes of device workspace one forward of shape [B, T] needs (0 for invalid B, T). */

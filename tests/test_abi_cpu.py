@@ -106,6 +106,8 @@ def test_weight_and_workspace_bytes(g):
     want += 12 * (4 * al(d * 4) + al(3 * d * d * 2) + al(3 * d * 4) + al(d * d * 2) + al(d * 4)
                   + al(f * d * 2) + al(f * 4) + al(d * f * 2) + al(d * 4))
     want += 2 * al(d * 4)
+    # bf16: k-blocked copies of wte and the four projection matrices of every layer
+    want += al(pad(V) * d * 2) + 12 * (al(3 * d * d * 2) + al(d * d * 2) + al(f * d * 2) + al(d * f * 2))
     assert wb == want
     assert L.gpt2_workspace_bytes(h, 4, 1024) > 4 * 1024 * d * 4
     assert L.gpt2_workspace_bytes(h, 4, 1025) == 0     # T > n_ctx
