@@ -58,7 +58,7 @@ __global__ __launch_bounds__(256) void embed_kernel(const int32_t* __restrict__ 
 template <int NV, bool OUT_BF16>
 __global__ __launch_bounds__(256) void layernorm_kernel(const float* __restrict__ x, const float* __restrict__ g,
                                                         const float* __restrict__ b, void* __restrict__ y, int M,
-                                                        int n, float eps, int kb_rows) {
+                                                        int n, float eps) {
     const int wave = threadIdx.x / GPT2_WAVE, lane = threadIdx.x % GPT2_WAVE;
     const int row = blockIdx.x * kRowsPerBlock + wave;
     if (row >= M) return;
@@ -100,11 +100,7 @@ __global__ __launch_bounds__(256) void layernorm_kernel(const float* __restrict_
                 uint2 p;
                 p.x = pack_bf16x2(o.x, o.y);
                 p.y = pack_bf16x2(o.z, o.w);
-                if (kb_rows)  // k-blocked: columns 4c..4c+3 share one 32-column block
-                    *reinterpret_cast<uint2*>(static_cast<uint16_t*>(y) +
-                                              ((size_t)(c >> 3) * kb_rows + row) * 32 + (c & 7) * 4) = p;
-                else
-                    reinterpret_cast<uint2*>(static_cast<uint16_t*>(y) + (size_t)row * n)[c] = p;
+                reinterpret_cast<uint2*>(static_cast<uint16_t*>(y) + (size_t)row * n)[c] = p;
             } else {
                 reinterpret_cast<float4*>(static_cast<float*>(y) + (size_t)row * n)[c] = o;
             }
@@ -248,6 +244,73 @@ __global__ __launch_bounds__(256) void convert_kernel(const void* __restrict__ s
     }
 }
 
+// LayerNorm with a k-blocked bf16 output: WAVES*RPW rows per workgroup (RPW per wavefront, all
+// their loads in flight together), normalised into LDS (rows padded by 16 bytes against bank
+// conflicts), then written block by block: the rows' 32-column slab of a block is one contiguous
+// run of WAVES*RPW*64 bytes, 16 bytes per lane. The statistics and rounding are those of
+// layernorm_kernel, so the values are bit-identical to its row-major output.
+template <int NV, int RPW, int WAVES>
+__global__ __launch_bounds__(64 * WAVES) void layernorm_kb_kernel(const float* __restrict__ x, const float* __restrict__ g,
+                                                           const float* __restrict__ b, uint16_t* __restrict__ y,
+                                                           int M, int n, float eps, int kb_rows) {
+    extern __shared__ __attribute__((aligned(16))) uint16_t sy[];  // [WAVES*RPW][n + 8]
+    constexpr int R = WAVES * RPW;
+    const int wave = threadIdx.x / GPT2_WAVE, lane = threadIdx.x % GPT2_WAVE;
+    const int r0 = blockIdx.x * R, nq = n / 4, sp = n + 8;
+    float4 v[RPW][NV];
+#pragma unroll
+    for (int r = 0; r < RPW; ++r) {
+        const int row = r0 + wave * RPW + r;
+        const float4* xr = reinterpret_cast<const float4*>(x + (size_t)min(row, M - 1) * n);
+#pragma unroll
+        for (int i = 0; i < NV; ++i) {
+            const int c = i * GPT2_WAVE + lane;
+            v[r][i] = c < nq ? xr[c] : make_float4(0.f, 0.f, 0.f, 0.f);
+        }
+    }
+    const float4* g4 = reinterpret_cast<const float4*>(g);
+    const float4* b4 = reinterpret_cast<const float4*>(b);
+#pragma unroll
+    for (int r = 0; r < RPW; ++r) {
+        float s = 0.f;
+#pragma unroll
+        for (int i = 0; i < NV; ++i) s += (v[r][i].x + v[r][i].y) + (v[r][i].z + v[r][i].w);
+        const float mean = wave_sum(s) / (float)n;
+        float q = 0.f;
+#pragma unroll
+        for (int i = 0; i < NV; ++i) {
+            const int c = i * GPT2_WAVE + lane;
+            if (c < nq) {
+                const float a0 = v[r][i].x - mean, a1 = v[r][i].y - mean, a2 = v[r][i].z - mean, a3 = v[r][i].w - mean;
+                q += (a0 * a0 + a1 * a1) + (a2 * a2 + a3 * a3);
+            }
+        }
+        const float var = wave_sum(q) / (float)n;
+        const float rstd = 1.0f / sqrtf(var + eps);
+        uint16_t* srow = sy + (wave * RPW + r) * sp;
+#pragma unroll
+        for (int i = 0; i < NV; ++i) {
+            const int c = i * GPT2_WAVE + lane;
+            if (c < nq) {
+                const float4 gg = g4[c], bb = b4[c];
+                uint2 p;
+                p.x = pack_bf16x2((v[r][i].x - mean) * rstd * gg.x + bb.x, (v[r][i].y - mean) * rstd * gg.y + bb.y);
+                p.y = pack_bf16x2((v[r][i].z - mean) * rstd * gg.z + bb.z, (v[r][i].w - mean) * rstd * gg.w + bb.w);
+                *reinterpret_cast<uint2*>(srow + 4 * c) = p;
+            }
+        }
+    }
+    __syncthreads();
+    const int n_chunks = (n / 32) * R * 4;  // 16-byte chunks: per block, R rows of four
+    for (int ci = threadIdx.x; ci < n_chunks; ci += blockDim.x) {
+        const int blk = ci / (R * 4), rr = (ci / 4) % R, part = ci % 4;
+        const int row = r0 + rr;
+        if (row < M)
+            *reinterpret_cast<u32x4_t*>(y + ((size_t)blk * kb_rows + row) * 32 + part * 8) =
+                *reinterpret_cast<const u32x4_t*>(sy + rr * sp + blk * 32 + part * 8);
+    }
+}
+
 // One 16-byte chunk (8 columns) per thread: chunk j of row r goes to block j/4 of the k-blocked copy.
 __global__ __launch_bounds__(256) void kblock_kernel(const uint16_t* __restrict__ src, uint16_t* __restrict__ dst,
                                                      long rows, int K) {
@@ -264,11 +327,19 @@ __global__ __launch_bounds__(256) void kblock_kernel(const uint16_t* __restrict_
 template <int NV>
 hipError_t launch_ln(const float* x, const float* g, const float* b, void* y, int M, int n, float eps, bool out_bf16,
                      int kb_rows, hipStream_t s) {
+    if (kb_rows) {
+        const size_t row_bytes = (size_t)(n + 8) * 2;
+        // four rows per workgroup (measured at B*T = 4096, d = 768: 16 rows per workgroup leave too
+        // few workgroups to hide the load latency; eight gain nothing)
+        layernorm_kb_kernel<NV, 1, 4><<<dim3((M + 3) / 4), dim3(256), 4 * row_bytes, s>>>(
+            x, g, b, static_cast<uint16_t*>(y), M, n, eps, kb_rows);
+        return hipGetLastError();
+    }
     dim3 grid((M + kRowsPerBlock - 1) / kRowsPerBlock), block(256);
     if (out_bf16)
-        layernorm_kernel<NV, true><<<grid, block, 0, s>>>(x, g, b, y, M, n, eps, kb_rows);
+        layernorm_kernel<NV, true><<<grid, block, 0, s>>>(x, g, b, y, M, n, eps);
     else
-        layernorm_kernel<NV, false><<<grid, block, 0, s>>>(x, g, b, y, M, n, eps, 0);
+        layernorm_kernel<NV, false><<<grid, block, 0, s>>>(x, g, b, y, M, n, eps);
     return hipGetLastError();
 }
 
