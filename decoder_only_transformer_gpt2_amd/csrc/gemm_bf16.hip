@@ -16,9 +16,15 @@
 // fragment reads of a wavefront spread over all banks.
 //
 // Tile shapes come from a per-shape table chosen so that the grid fills the 256 compute units
-// (8 XCDs x 32). Workgroup ids are remapped so that each XCD (which receives every 8th id) works
-// on one contiguous range of tiles, and tiles are rasterised in groups of GROUP_M row-tiles, so
-// the A rows and W rows a group shares stay in that XCD's L2.
+// (8 XCDs x 32). The block projections remap workgroup ids so that each XCD (which receives every
+// 8th id) works on one contiguous range of tiles, rasterised in groups of row-tiles, so the A rows
+// and W rows a group shares stay in that XCD's L2; the vocabulary projection interleaves the XCDs
+// instead (see tile_of).
+//
+// Operands are row-major ([rows][K]) or k-blocked ([K/32][rows][32]); with the k-blocked layout the
+// slab of a 32-wide K step is one contiguous run per operand, so each DMA instruction reads whole
+// 128-byte lines (row-major slabs are 64-byte pieces of lines, and the DMA rate follows the number
+// of lines an instruction touches: measured ~59 against ~115 GB/s per CU).
 #include <cstdlib>
 
 #include "common.h"
@@ -34,10 +40,29 @@ struct TileCoord {
     int tm, tn;
 };
 
-// Workgroup id -> (row-tile, column-tile). Optionally remapped so that each XCD (which receives
-// every 8th id) works on one contiguous range of tiles; then rasterised in groups of group_m
-// row-tiles (column-major inside a group), so neighbouring ids share W rows.
+// Workgroup id -> (row-tile, column-tile). group_m >= 1000: XCD-interleaved groups (below);
+// otherwise optionally remapped so that each XCD (which receives every 8th id) works on one
+// contiguous range of tiles, then rasterised in groups of group_m row-tiles (column-major inside a
+// group), so neighbouring ids share W rows.
 __device__ __forceinline__ TileCoord tile_of(int b, int nblk, int tiles_m, int group_m, bool xcd_remap) {
+    if (group_m >= 1000) {
+        // XCD-interleaved groups of g row-tiles: inside a group, column tiles go by octets and ids
+        // b, b+8, b+16, ... (one XCD, one L2) take the same column tile in consecutive row-tiles,
+        // while the eight XCDs work on eight neighbouring column tiles
+        const int g = group_m - 1000;
+        const int tiles_n = nblk / tiles_m;
+        const int per_group = g * tiles_n;
+        const int grp = b / per_group, lb = b % per_group;
+        const int first_m = grp * g;
+        const int gm = min(tiles_m - first_m, g);
+        const int full = tiles_n / 8;
+        if (lb < full * 8 * gm) {
+            const int oct = lb / (8 * gm), w = lb % (8 * gm);
+            return {first_m + w / 8, oct * 8 + w % 8};
+        }
+        const int rem = tiles_n - full * 8, w = lb - full * 8 * gm;
+        return {first_m + w / rem, full * 8 + w % rem};
+    }
     int logical = b;
     if (xcd_remap) {
         const int xcd = b % kXcds, idx = b / kXcds, q = nblk / kXcds, r = nblk % kXcds;
@@ -463,11 +488,11 @@ constexpr TileCfg kCfgs[] = {
 // Tile shape per GEMM shape, from measurements on MI355X at M = 4096 (bf16, K = 768 / 3072).
 // The block projections are bound by their operand traffic through L2 (re-reads grow as tiles
 // shrink), so the largest tile that still gives every CU about one tile wins: 192 x 256 for
-// N = 2304 (198 tiles, a five-stage 32-wide ring), 256 x 192 for N = 3072 (256 tiles). Narrow outputs (N <= 1024) prefer
-// 64 x 96 tiles with a four-stage ring (two workgroups per CU). The vocabulary projection, with
-// tiles for every CU many times over, uses 256 x 128 tiles of four waves with a three-stage
-// 32-wide ring, two workgroups per CU, so that one workgroup's epilogue (the fp32 logits
-// stores) overlaps the other's main loop.
+// N = 2304 (198 tiles, a five-stage 32-wide ring), 256 x 192 for N = 3072 (256 tiles; with
+// k-blocked operands the five-stage 32-wide ring, else the two-stage 64-wide one). Narrow outputs
+// (N <= 1024) prefer 64 x 96 tiles with a four-stage ring (two workgroups per CU). The vocabulary
+// projection, with tiles for every CU many times over, uses 256 x 256 tiles of eight waves
+// (measured in the forward: 420 us against 460 us for 256 x 128 tiles of four waves).
 int choose_cfg(int M, int N, int K, bool kb) {
 #ifdef GPT2_GEMM_TUNE
     if (const char* e = getenv("GPT2_GEMM_CFG")) {
@@ -477,7 +502,11 @@ int choose_cfg(int M, int N, int K, bool kb) {
 #endif
     (void)K;
     auto tiles = [&](int bm, int bn) { return (long)((M + bm - 1) / bm) * ((N + bn - 1) / bn); };
-    if (tiles(256, 256) >= 4 * 256) return 20;  // vocabulary projection
+#ifdef GPT2_GEMM_TUNE
+    if (tiles(256, 256) >= 4 * 256)
+        if (const char* e = getenv("GPT2_HEAD_CFG")) return atoi(e);
+#endif
+    if (tiles(256, 256) >= 4 * 256) return 0;  // vocabulary projection
     if (N <= 1024) return 12;
     if (tiles(192, 256) < 128) return 12;  // few rows (weight gradients, short prompts): fill the CUs
     if (tiles(192, 256) <= 256) return 22;
@@ -490,14 +519,18 @@ template <int BM, int BN, int BK, int S, int WGM, int WGN, bool KB>
 hipError_t launch_cfg(const uint16_t* A, const uint16_t* W, const float* bias, void* C, int M, int N, int K, long ldc,
                       int epi, int gelu_erf, int a_rows, int w_rows, int c_kb, const HeadOut& ho, hipStream_t s) {
     const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
-    // group_m > 0: XCD-contiguous remap + groups of group_m row-tiles; < 0: plain order, groups of
-    // -group_m. Measured with cold caches (as inside a forward): the vocabulary projection is fastest
-    // in plain order with pairs of row-tiles (the XCDs then fetch each wte tile at about the same
-    // time, so it is read from HBM once and served to the others from the memory-side cache);
-    // the block projections are insensitive to the order.
-    int group_m = tiles_n >= 64 ? -2 : 4;
+    // group_m in [1, 1000): XCD-contiguous remap + groups of group_m row-tiles; < 0: plain order,
+    // groups of -group_m; >= 1000: XCD-interleaved groups of group_m - 1000 row-tiles. Measured in
+    // the forward (cold caches for the wte operand): the vocabulary projection is fastest with
+    // XCD-interleaved pairs of row-tiles (420 us; plain pairs 442 us; XCD-contiguous ranges 520 us
+    // and more): each wte tile is then read once per row pair into one XCD's L2 instead of into
+    // two, while the eight XCDs sweep neighbouring columns together, so the logits are written in
+    // long runs. The block projections are insensitive to the order.
+    int group_m = tiles_n >= 64 ? 1002 : 4;
 #ifdef GPT2_GEMM_TUNE
     if (const char* e = getenv("GPT2_GEMM_GROUP")) group_m = atoi(e);
+    if (tiles_n >= 64)
+        if (const char* e = getenv("GPT2_HEAD_GROUP")) group_m = atoi(e);
 #endif
     dim3 grid(tiles_m * tiles_n), block(64 * WGM * WGN);
 #define GPT2_LAUNCH(E)                                                                                      \
@@ -572,9 +605,9 @@ hipError_t gemm_bf16(const uint16_t* A, const uint16_t* W, const float* bias, vo
         GPT2_CFG(26, 128, 128, 32, 5, 2, 2)
         GPT2_CFG(27, 256, 128, 32, 5, 2, 4)
 #else
+        GPT2_CFG(0, 256, 256, 32, 4, 2, 4)
         GPT2_CFG(12, 64, 96, 64, 4, 2, 2)
         GPT2_CFG(16, 256, 192, 64, 2, 2, 4)
-        GPT2_CFG(20, 256, 128, 32, 3, 2, 2)
         GPT2_CFG(22, 192, 256, 32, 5, 2, 4)
         GPT2_CFG(23, 256, 192, 32, 5, 2, 4)
 #endif
