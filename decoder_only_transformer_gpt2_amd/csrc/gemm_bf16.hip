@@ -507,6 +507,9 @@ int choose_cfg(int M, int N, int K, bool kb) {
         if (const char* e = getenv("GPT2_HEAD_CFG")) return atoi(e);
 #endif
     if (tiles(256, 256) >= 4 * 256) return 0;  // vocabulary projection
+    // narrow outputs of very many rows (the wte weight gradient, M = n_vocab): large tiles, since
+    // the grid fills the CUs twice over anyway and each tile re-reads less through L2
+    if (N <= 1024 && tiles(256, 192) >= 512) return 16;
     if (N <= 1024) return 12;
     if (tiles(192, 256) < 128) return 12;  // few rows (weight gradients, short prompts): fill the CUs
     if (tiles(192, 256) <= 256) return 22;

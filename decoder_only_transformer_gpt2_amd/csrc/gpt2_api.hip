@@ -439,7 +439,7 @@ TrainLayout train_layout(const gpt2_model* m, int B, int T) {
     L.layer0 = take(L.per_layer * c.n_layer);
     L.xfin = take(L.M * d * 4);
     L.xf = take(L.Mp * d * as);
-    L.logits = take((size_t)L.M * c.n_vocab * 4);
+    L.logits = take((size_t)L.M * L.Vp * 4);  // row stride Vp: rows 256-byte aligned for the loss gradient
     L.dx = take(L.M * d * 4);
     L.dbuf = take(L.M * L.wide * 4);
     L.dbuf2 = take(L.M * L.wide * 4);
@@ -512,12 +512,12 @@ gpt2_status enqueue_train_forward(const gpt2_model* m, const int32_t* tokens, co
     GPT2_HIP(gpt2k::layernorm(reinterpret_cast<float*>(ws + L.xfin), static_cast<const float*>(wptr(m, ln_f)),
                               static_cast<const float*>(wptr(m, ln_f + 1)), ws + L.xf, M, d, c.ln_eps, bf, s));
     float* logits = reinterpret_cast<float*>(ws + L.logits);
-    GPT2_HIP(linear(m, ws + L.xf, 0, -1, logits, M, c.n_vocab, d, c.n_vocab, gpt2k::EPI_LOGITS, {}, s));
+    GPT2_HIP(linear(m, ws + L.xf, 0, -1, logits, M, c.n_vocab, d, L.Vp, gpt2k::EPI_LOGITS, {}, s));
     int32_t* tgt = reinterpret_cast<int32_t*>(ws + L.fw.tgt);
     GPT2_HIP(gpt2k::xent_targets(labels ? labels : tokens, M, T, c.n_vocab, tgt,
                                  reinterpret_cast<int32_t*>(ws + L.fw.flags), s));
     float* nll = reinterpret_cast<float*>(ws + L.nll);
-    GPT2_HIP(gpt2k::xent_grad(logits, c.n_vocab, M, c.n_vocab, (int)L.Vp, tgt, reinterpret_cast<int32_t*>(ws + L.cnt), nll,
+    GPT2_HIP(gpt2k::xent_grad(logits, L.Vp, M, c.n_vocab, (int)L.Vp, tgt, reinterpret_cast<int32_t*>(ws + L.cnt), nll,
                               ws + L.dlog, bf, s));
     GPT2_HIP(gpt2k::xent_mean(nll, tgt, M, loss, s));
     return GPT2_OK;

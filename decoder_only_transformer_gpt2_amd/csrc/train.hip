@@ -268,6 +268,103 @@ __global__ void __launch_bounds__(256) xent_grad_kernel(const float* __restrict_
     }
 }
 
+// The same with the row held in registers: 512 threads per row, NF float4 per thread (row stride
+// ld a multiple of 4, columns V <= v of the row masked by index), so the logits are read once. The
+// row maximum and the sum of 2^((z - max) log2 e) are reduced over the wavefront and then over the
+// eight wavefronts in a fixed order.
+constexpr int XG_T = 512;
+
+__device__ __forceinline__ float wave_max_xor(float v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+    return v;
+}
+__device__ __forceinline__ float wave_sum_xor(float v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+    return v;
+}
+
+template <bool BF, int NF>
+__global__ void __launch_bounds__(XG_T) xent_grad_reg_kernel(const float* __restrict__ logits, long ld, int V, int Vp,
+                                                            const int32_t* __restrict__ tgt,
+                                                            const int32_t* __restrict__ cnt, float* __restrict__ nll,
+                                                            void* __restrict__ dlogits) {
+    __shared__ float red[2][XG_T / 64];
+    const int m = blockIdx.x, t = threadIdx.x, wave = t >> 6;
+    const float* z = logits + (long)m * ld;
+    const int y = tgt[m];
+    auto* out = static_cast<typename Act<BF>::T*>(dlogits) + (long)m * Vp;
+    const int nq = Vp / 4;
+    auto store4 = [&](int f, float g0, float g1, float g2, float g3) {
+        if constexpr (BF) {
+            uint2 p;
+            p.x = pack_bf16x2(g0, g1);
+            p.y = pack_bf16x2(g2, g3);
+            *reinterpret_cast<uint2*>(out + 4 * (long)f) = p;
+        } else {
+            *reinterpret_cast<float4*>(out + 4 * (long)f) = make_float4(g0, g1, g2, g3);
+        }
+    };
+    if (y < 0) {
+        for (int f = t; f < nq; f += XG_T) store4(f, 0.f, 0.f, 0.f, 0.f);
+        if (t == 0) nll[m] = 0.f;
+        return;
+    }
+    float4 zr[NF];
+    float mx = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < NF; ++i) {
+        const int f = t + i * XG_T;
+        float4 v = make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY);
+        if (f < nq) {
+            v = *reinterpret_cast<const float4*>(z + 4 * (long)f);
+            const int c = 4 * f;
+            if (c + 0 >= V) v.x = -INFINITY;
+            if (c + 1 >= V) v.y = -INFINITY;
+            if (c + 2 >= V) v.z = -INFINITY;
+            if (c + 3 >= V) v.w = -INFINITY;
+        }
+        zr[i] = v;
+        mx = fmaxf(mx, fmaxf(fmaxf(v.x, v.y), fmaxf(v.z, v.w)));
+    }
+    mx = wave_max_xor(mx);
+    if ((t & 63) == 0) red[0][wave] = mx;
+    __syncthreads();
+    mx = red[0][0];
+#pragma unroll
+    for (int w = 1; w < XG_T / 64; ++w) mx = fmaxf(mx, red[0][w]);
+    const float L2E = 1.4426950408889634f;
+    const float mb = mx * L2E;
+    float s = 0.f;
+#pragma unroll
+    for (int i = 0; i < NF; ++i) {  // masked columns: exp2(-inf) = 0
+        s += __builtin_amdgcn_exp2f(fmaf(zr[i].x, L2E, -mb)) + __builtin_amdgcn_exp2f(fmaf(zr[i].y, L2E, -mb));
+        s += __builtin_amdgcn_exp2f(fmaf(zr[i].z, L2E, -mb)) + __builtin_amdgcn_exp2f(fmaf(zr[i].w, L2E, -mb));
+    }
+    s = wave_sum_xor(s);
+    if ((t & 63) == 0) red[1][wave] = s;
+    __syncthreads();
+    s = red[1][0];
+#pragma unroll
+    for (int w = 1; w < XG_T / 64; ++w) s += red[1][w];
+    const float lse2 = mb + __log2f(s);  // log2 of sum 2^(z log2 e)
+    if (t == 0) nll[m] = lse2 / L2E - z[y];
+    const float inv_n = 1.0f / (float)max(cnt[0], 1);
+#pragma unroll
+    for (int i = 0; i < NF; ++i) {
+        const int f = t + i * XG_T;
+        if (f < nq) {
+            const int c = 4 * f;
+            auto g = [&](float zz, int v) {
+                return (__builtin_amdgcn_exp2f(fmaf(zz, L2E, -lse2)) - (v == y ? 1.f : 0.f)) * inv_n;
+            };
+            store4(f, c + 0 < V ? g(zr[i].x, c + 0) : 0.f, c + 1 < V ? g(zr[i].y, c + 1) : 0.f,
+                   c + 2 < V ? g(zr[i].z, c + 2) : 0.f, c + 3 < V ? g(zr[i].w, c + 3) : 0.f);
+        }
+    }
+}
+
 // ------------------------------------------------------------------------------ attention backward
 // fp32 compute mode (the bf16 mode uses the matrix-core kernels of attention_bwd.hip).
 // Causal attention of head (b, h) on qkv [B, T, 3, H, 64] (compute dtype), output o [B, T, H, 64],
@@ -524,6 +621,25 @@ hipError_t gelu_backward(const float* u, float* g, long n, int erf_form, hipStre
 hipError_t xent_grad(const float* logits, long ld, int M, int V, int Vp, const int32_t* tgt, int32_t* cnt, float* nll,
                      void* dlogits, bool bf16, hipStream_t s) {
     count_targets_kernel<<<dim3(1), dim3(256), 0, s>>>(tgt, M, cnt);
+    // the row in registers when it fits (the row stride and Vp multiples of 4), else two passes
+    const int nf = (Vp / 4 + XG_T - 1) / XG_T;
+    if (ld % 4 == 0 && Vp % 4 == 0 && nf <= 32) {
+#define GPT2_XG(NF)                                                                                          \
+    do {                                                                                                     \
+        if (bf16)                                                                                            \
+            xent_grad_reg_kernel<true, NF><<<dim3(M), dim3(XG_T), 0, s>>>(logits, ld, V, Vp, tgt, cnt, nll, dlogits); \
+        else                                                                                                 \
+            xent_grad_reg_kernel<false, NF><<<dim3(M), dim3(XG_T), 0, s>>>(logits, ld, V, Vp, tgt, cnt, nll,        \
+                                                                           dlogits);                         \
+        return hipGetLastError();                                                                            \
+    } while (0)
+        if (nf <= 1) GPT2_XG(1);
+        if (nf <= 4) GPT2_XG(4);
+        if (nf <= 12) GPT2_XG(12);
+        if (nf <= 25) GPT2_XG(25);
+        GPT2_XG(32);
+#undef GPT2_XG
+    }
     if (bf16)
         xent_grad_kernel<true><<<dim3(M), dim3(256), 0, s>>>(logits, ld, V, Vp, tgt, cnt, nll, dlogits);
     else
