@@ -25,6 +25,7 @@
 // slab of a 32-wide K step is one contiguous run per operand, so each DMA instruction reads whole
 // 128-byte lines (row-major slabs are 64-byte pieces of lines, and the DMA rate follows the number
 // of lines an instruction touches: measured ~59 against ~115 GB/s per CU).
+#include <cstdio>
 #include <cstdlib>
 
 #include "common.h"
@@ -595,9 +596,11 @@ constexpr TileCfg kCfgs[] = {
 // shrink), so the largest tile that still gives every CU about one tile wins: 192 x 256 for
 // N = 2304 (198 tiles, a five-stage 32-wide ring), 256 x 192 for N = 3072 (256 tiles; with
 // k-blocked operands the five-stage 32-wide ring, else the two-stage 64-wide one). Narrow outputs
-// (N <= 1024) prefer 64 x 96 tiles with a four-stage ring (two workgroups per CU). The vocabulary
-// projection, with tiles for every CU many times over, uses 256 x 256 tiles of eight waves
-// (measured in the forward: 420 us against 460 us for 256 x 128 tiles of four waves).
+// (N <= 1024) prefer 64 x 96 tiles with a four-stage ring (two workgroups per CU), or 128 x 96 with
+// a four-stage 64-wide ring for K >= 2048 (mlp.c_proj: 394 against 420 us per forward). The
+// vocabulary projection, with tiles for every CU many times over, uses 256 x 256 tiles of eight
+// waves with a five-stage ring (in the forward: 395-405 us; four stages 405-415 us; 256 x 128
+// tiles of four waves, two per CU, 460 us before the K loops were unrolled).
 int choose_cfg(int M, int N, int K, bool kb) {
 #ifdef GPT2_GEMM_TUNE
     if (const char* e = getenv("GPT2_GEMM_CFG")) {
@@ -605,16 +608,23 @@ int choose_cfg(int M, int N, int K, bool kb) {
         if (c >= 0 && c < kNumCfgs) return c;
     }
 #endif
-    (void)K;
     auto tiles = [&](int bm, int bn) { return (long)((M + bm - 1) / bm) * ((N + bn - 1) / bn); };
 #ifdef GPT2_GEMM_TUNE
     if (tiles(256, 256) >= 4 * 256)
         if (const char* e = getenv("GPT2_HEAD_CFG")) return atoi(e);
+    {
+        char name[32];
+        snprintf(name, sizeof name, "GPT2_CFG_N%d", N);
+        if (const char* e = getenv(name)) return atoi(e);
+    }
 #endif
-    if (tiles(256, 256) >= 4 * 256) return 0;  // vocabulary projection
+    if (tiles(256, 256) >= 4 * 256) return 8;  // vocabulary projection
     // narrow outputs of very many rows (the wte weight gradient, M = n_vocab): large tiles, since
     // the grid fills the CUs twice over anyway and each tile re-reads less through L2
     if (N <= 1024 && tiles(256, 192) >= 512) return 16;
+    // narrow outputs with a long reduction (mlp.c_proj, K = 4d) on k-blocked operands: 128 x 96
+    // tiles (one wave of 256 workgroups) re-read less than 64 x 96 ones
+    if (N <= 1024 && kb && K >= 2048 && tiles(128, 96) >= 192) return 11;
     if (N <= 1024) return 12;
     if (tiles(192, 256) < 128) return 12;  // few rows (weight gradients, short prompts): fill the CUs
     if (tiles(192, 256) <= 256) return 22;
@@ -723,35 +733,24 @@ hipError_t gemm_bf16(const uint16_t* A, const uint16_t* W, const float* bias, vo
                                                                        a_rows, w_rows, c_kb_rows, ho, s);
 #ifdef GPT2_GEMM_TUNE
         GPT2_CFG(0, 256, 256, 32, 4, 2, 4)
-        GPT2_CFG(1, 256, 256, 64, 2, 2, 4)
         GPT2_CFG(2, 256, 192, 32, 4, 2, 2)
-        GPT2_CFG(3, 128, 128, 32, 4, 2, 2)
-        GPT2_CFG(4, 128, 128, 64, 2, 2, 2)
         GPT2_CFG(5, 128, 64, 32, 4, 2, 2)
         GPT2_CFG(6, 256, 128, 32, 4, 2, 4)
-        GPT2_CFG(7, 128, 96, 64, 2, 2, 2)
         GPT2_CFG(8, 256, 256, 32, 5, 2, 4)
         GPT2_CFG(9, 192, 256, 32, 4, 2, 2)
         GPT2_CFG(10, 128, 96, 64, 3, 2, 2)
         GPT2_CFG(11, 128, 96, 64, 4, 2, 2)
         GPT2_CFG(12, 64, 96, 64, 4, 2, 2)
-        GPT2_CFG(13, 128, 64, 64, 4, 2, 2)
-        GPT2_CFG(14, 256, 256, 32, 4, 2, 2)
-        GPT2_CFG(15, 128, 128, 64, 4, 2, 2)
         GPT2_CFG(16, 256, 192, 64, 2, 2, 4)
-        GPT2_CFG(17, 128, 288, 64, 2, 2, 2)
-        GPT2_CFG(18, 256, 128, 64, 2, 2, 4)
         GPT2_CFG(19, 192, 256, 64, 2, 2, 4)
-        GPT2_CFG(20, 256, 128, 32, 3, 2, 2)
-        GPT2_CFG(21, 128, 256, 32, 3, 2, 2)
         GPT2_CFG(22, 192, 256, 32, 5, 2, 4)
         GPT2_CFG(23, 256, 192, 32, 5, 2, 4)
         GPT2_CFG(24, 64, 96, 32, 6, 2, 2)
         GPT2_CFG(25, 128, 96, 32, 5, 2, 2)
-        GPT2_CFG(26, 128, 128, 32, 5, 2, 2)
         GPT2_CFG(27, 256, 128, 32, 5, 2, 4)
 #else
-        GPT2_CFG(0, 256, 256, 32, 4, 2, 4)
+        GPT2_CFG(8, 256, 256, 32, 5, 2, 4)
+        GPT2_CFG(11, 128, 96, 64, 4, 2, 2)
         GPT2_CFG(12, 64, 96, 64, 4, 2, 2)
         GPT2_CFG(16, 256, 192, 64, 2, 2, 4)
         GPT2_CFG(22, 192, 256, 32, 5, 2, 4)
