@@ -89,7 +89,7 @@ __device__ __forceinline__ void static_for(F&& f) {
     }
 }
 
-template <int BM, int BN, int BK, int S, int WGM, int WGN, int EPI, bool KB, bool BD, int NKT>
+template <int BM, int BN, int BK, int S, int WGM, int WGN, int EPI, bool KB, int NKT>
 // NKT > 0: the K loop has exactly NKT steps and is unrolled completely (straight-line code with
 // compile-time ring slots and waits; a loop header makes the compiler drain every outstanding
 // DMA before the first LDS read of each iteration, since it cannot tell which stage that read
@@ -97,9 +97,7 @@ template <int BM, int BN, int BK, int S, int WGM, int WGN, int EPI, bool KB, boo
 // Two workgroups per CU (256 registers per lane) wherever the ring fits twice in LDS and the
 // wave tile is at most 128 x 64.
 __global__ __launch_bounds__(64 * WGM * WGN,
-                             (BM / WGM) * (BN / WGN) <= 128 * 64 && S * (BD ? BM : BM + BN) * BK * 2 <= 80 * 1024
-                                 ? 2
-                                 : 1)
+                             (BM / WGM) * (BN / WGN) <= 128 * 64 && S * (BM + BN) * BK * 2 <= 80 * 1024 ? 2 : 1)
 void gemm_bf16_kernel(
     const uint16_t* __restrict__ A, const uint16_t* __restrict__ W, const float* __restrict__ bias,
     void* __restrict__ Cv, int M, int N, int K, int ldc, int a_rows, int w_rows, int tiles_m,
@@ -109,18 +107,13 @@ void gemm_bf16_kernel(
     constexpr int WM = BM / WGM, WN = BN / WGN, FM = WM / 16, FN = WN / 16;
     constexpr int CPR = BK / 8;                  // 16-byte chunks per slab row
     constexpr int RPI = 64 / CPR;                // slab rows one 64-lane DMA instruction fills
-    // BD (k-blocked operands only): the W fragments go straight from global memory into registers
-    // (one 16-byte load per lane is one MFMA operand: 16 rows x 32 k of the k-blocked W are one
-    // contiguous 1 KB run), so the LDS ring holds only the A slabs
-    static_assert(!BD || KB, "direct W fragments need the k-blocked layout");
-    constexpr int STAGE = (BD ? BM : BM + BN) * BK;  // bf16 elements per stage (A slab, then W slab)
-    constexpr int NI = (BD ? BM : BM + BN) / RPI;    // DMA instructions per stage
-    constexpr int NB = BD ? FN * (BK / 32) : 0;      // direct W loads per stage per wavefront
+    constexpr int STAGE = (BM + BN) * BK;        // bf16 elements per stage (A slab, then W slab)
+    constexpr int NI = (BM + BN) / RPI;          // DMA instructions per stage
     constexpr int PW = (NI + NW - 1) / NW;       // per wavefront (the last ones may repeat a load)
     static_assert(BK == 32 || BK == 64, "BK is 32 or 64");
     static_assert(WM % 16 == 0 && WN % 16 == 0, "wave tile must be a multiple of 16");
     static_assert(BM % RPI == 0 && BN % RPI == 0, "a DMA instruction fills rows of one operand");
-    static_assert(S >= 2 && S <= 6 && (S - 1) * (PW + NB) < 64, "ring depth");
+    static_assert(S >= 2 && S <= 6 && (S - 1) * PW < 64, "ring depth");
     static_assert(S * STAGE * 2 <= 160 * 1024, "LDS");
     // One LDS object per stage: lets the compiler see which outstanding DMA an LDS read depends on.
     __shared__ __attribute__((aligned(1024))) uint16_t lds0[STAGE];
@@ -221,79 +214,7 @@ void gemm_bf16_kernel(
     } while (0)
 
     const int nk = K / BK;
-    if constexpr (BD) {
-        // this wavefront's W fragment rows (block 0; k0 adds k0 * w_rows elements)
-        const uint16_t* wb[FN];
-#pragma unroll
-        for (int j = 0; j < FN; ++j)
-            wb[j] = W + (size_t)min(n0 + wn * WN + j * 16 + r16, w_rows - 1) * 32 + g4 * 8;
-        u32x4_t bq[S][NB > 0 ? NB : 1];
-        auto issue_bd = [&](auto stc, int k0) {
-            constexpr int st = decltype(stc)::value;
-            issue(st, k0);
-#pragma unroll
-            for (int j = 0; j < FN; ++j)
-#pragma unroll
-                for (int kk = 0; kk < BK / 32; ++kk)
-                    bq[st][j * (BK / 32) + kk] =
-                        *reinterpret_cast<const u32x4_t*>(wb[j] + (size_t)(k0 + 32 * kk) * w_rows);
-        };
-        auto compute_bd = [&](auto stc) {
-            constexpr int st = decltype(stc)::value;
-            const uint16_t* sa = slot(st);
-#pragma unroll
-            for (int kk = 0; kk < BK / 32; ++kk) {
-                bf16x8_t af[FM];
-                const int chunk = kk * 4 + g4;
-#pragma unroll
-                for (int i = 0; i < FM; ++i) {
-                    const int row = wm * WM + i * 16 + r16;
-                    af[i] = *reinterpret_cast<const bf16x8_t*>(&sa[row * BK + swz_chunk(row, chunk) * 8]);
-                }
-#pragma unroll
-                for (int i = 0; i < FM; ++i)
-#pragma unroll
-                    for (int j = 0; j < FN; ++j)
-                        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                            af[i], __builtin_bit_cast(bf16x8_t, bq[st][j * (BK / 32) + kk]), acc[i][j], 0, 0, 0);
-            }
-        };
-#define GPT2_BD_WAIT(after)                                                        \
-    do {                                                                           \
-        __builtin_amdgcn_s_waitcnt(waitcnt_imm((after) * (PW + NB), 0));           \
-        __builtin_amdgcn_s_barrier();                                              \
-    } while (0)
-        static_for<0, S - 1>([&](auto st) {
-            if (decltype(st)::value < nk) issue_bd(st, decltype(st)::value * BK);
-        });
-        int kt = 0;  // stays a multiple of S, so stage kt + u sits in slot u
-        for (; kt + 2 * S - 2 < nk; kt += S) {
-            static_for<0, S>([&](auto u) {
-                constexpr int U = decltype(u)::value;
-                GPT2_BD_WAIT(S - 2);
-                issue_bd(std::integral_constant<int, (U + S - 1) % S>{}, (kt + U + S - 1) * BK);
-                compute_bd(u);
-            });
-        }
-        for (; kt < nk; kt += S) {
-            static_for<0, S>([&](auto u) {
-                constexpr int U = decltype(u)::value;
-                const int k = kt + U;
-                if (k < nk) {
-                    switch (min(k + S - 2, nk - 1) - k) {  // stages issued after k
-                        case 0: GPT2_BD_WAIT(0); break;
-                        case 1: GPT2_BD_WAIT(1); break;
-                        case 2: GPT2_BD_WAIT(2); break;
-                        case 3: GPT2_BD_WAIT(3); break;
-                        default: GPT2_BD_WAIT(4); break;
-                    }
-                    if (k + S - 1 < nk) issue_bd(std::integral_constant<int, (U + S - 1) % S>{}, (k + S - 1) * BK);
-                    compute_bd(u);
-                }
-            });
-        }
-#undef GPT2_BD_WAIT
-    } else if constexpr (NKT > 0) {
+    if constexpr (NKT > 0) {
         static_for<0, S - 1>([&](auto st) {
             if constexpr (decltype(st)::value < NKT) issue(decltype(st)::value, decltype(st)::value * BK);
         });
@@ -633,30 +554,22 @@ int choose_cfg(int M, int N, int K, bool kb) {
     return 16;
 }
 
-template <int BM, int BN, int BK, int S, int WGM, int WGN, bool KB, bool BD, int NKT = 0>
+template <int BM, int BN, int BK, int S, int WGM, int WGN, bool KB, int NKT = 0>
 hipError_t launch_cfg(const uint16_t* A, const uint16_t* W, const float* bias, void* C, int M, int N, int K, long ldc,
                       int epi, int gelu_erf, int a_rows, int w_rows, int c_kb, const HeadOut& ho, hipStream_t s) {
-    // direct W fragments shrink the ring to the A slabs; where the epilogue's staging no longer
-    // fits it (the same bounds the kernel asserts), the tile keeps W in LDS
-    constexpr int STG = (BD ? BM : BM + BN) * BK, SCR = 16 * (BN / WGN + 4) * 4, WPS = STG * 2 / SCR;
-    constexpr bool fits = WPS >= 1 && (WGM * WGN + WPS - 1) / WPS <= S - 1 && WGN * BM * 8 <= STG * 2;
-    if constexpr (BD && !fits)
-        return launch_cfg<BM, BN, BK, S, WGM, WGN, KB, false, NKT>(A, W, bias, C, M, N, K, ldc, epi, gelu_erf, a_rows,
-                                                                   w_rows, c_kb, ho, s);
-    else {
     // the K loops of the forward's projections (K = 768 and 3072, k-blocked) run fully unrolled
     if constexpr (KB && NKT == 0) {
         const int nk = K / BK;
         if constexpr (BK == 32) {
             if (nk == 24)
-                return launch_cfg<BM, BN, BK, S, WGM, WGN, KB, BD, 24>(A, W, bias, C, M, N, K, ldc, epi, gelu_erf,
+                return launch_cfg<BM, BN, BK, S, WGM, WGN, KB, 24>(A, W, bias, C, M, N, K, ldc, epi, gelu_erf,
                                                                        a_rows, w_rows, c_kb, ho, s);
         } else {
             if (nk == 12)
-                return launch_cfg<BM, BN, BK, S, WGM, WGN, KB, BD, 12>(A, W, bias, C, M, N, K, ldc, epi, gelu_erf,
+                return launch_cfg<BM, BN, BK, S, WGM, WGN, KB, 12>(A, W, bias, C, M, N, K, ldc, epi, gelu_erf,
                                                                        a_rows, w_rows, c_kb, ho, s);
             if (nk == 48)
-                return launch_cfg<BM, BN, BK, S, WGM, WGN, KB, BD, 48>(A, W, bias, C, M, N, K, ldc, epi, gelu_erf,
+                return launch_cfg<BM, BN, BK, S, WGM, WGN, KB, 48>(A, W, bias, C, M, N, K, ldc, epi, gelu_erf,
                                                                        a_rows, w_rows, c_kb, ho, s);
         }
     }
@@ -676,7 +589,7 @@ hipError_t launch_cfg(const uint16_t* A, const uint16_t* W, const float* bias, v
 #endif
     dim3 grid(tiles_m * tiles_n), block(64 * WGM * WGN);
 #define GPT2_LAUNCH(E)                                                                                      \
-    gemm_bf16_kernel<BM, BN, BK, S, WGM, WGN, E, KB, BD, NKT><<<grid, block, 0, s>>>(A, W, bias, C, M, N, K, ldc,           \
+    gemm_bf16_kernel<BM, BN, BK, S, WGM, WGN, E, KB, NKT><<<grid, block, 0, s>>>(A, W, bias, C, M, N, K, ldc,           \
                                                                       a_rows, w_rows, tiles_m, group_m, c_kb, ho)
     switch (epi) {
         case EPI_BIAS: GPT2_LAUNCH(EPI_BIAS); break;
@@ -692,7 +605,6 @@ hipError_t launch_cfg(const uint16_t* A, const uint16_t* W, const float* bias, v
     }
 #undef GPT2_LAUNCH
     return hipGetLastError();
-    }
 }
 
 }  // namespace
@@ -711,43 +623,21 @@ hipError_t gemm_bf16(const uint16_t* A, const uint16_t* W, const float* bias, vo
     if (c_kb_rows && (epi == EPI_BIAS_RESIDUAL || epi == EPI_LOGITS || epi == EPI_LSE || c_kb_rows < M || N % 32))
         return hipErrorInvalidValue;  // k-blocked output: bf16 epilogues only
     if (kb && K % 32) return hipErrorInvalidValue;
-#ifdef GPT2_GEMM_TUNE
-    bool bd = false;
-    if (const char* e = getenv("GPT2_GEMM_BD")) bd = atoi(e) != 0;
-#endif
     switch (choose_cfg(M, N, K, kb)) {
-#ifdef GPT2_GEMM_TUNE
-#define GPT2_CFG_BD(bm, bn, bk, st, wgm, wgn)                                                                   \
-    if (kb && bd)                                                                                               \
-        return launch_cfg<bm, bn, bk, st, wgm, wgn, true, true>(A, W, bias, C, M, N, K, ldc, epi, gelu_erf, a_rows, \
-                                                                w_rows, c_kb_rows, ho, s);
-#else
-#define GPT2_CFG_BD(bm, bn, bk, st, wgm, wgn)
-#endif
 #define GPT2_CFG(i, bm, bn, bk, st, wgm, wgn)                                                                    \
     case i:                                                                                                      \
-        GPT2_CFG_BD(bm, bn, bk, st, wgm, wgn)                                                                    \
-        return kb ? launch_cfg<bm, bn, bk, st, wgm, wgn, true, false>(A, W, bias, C, M, N, K, ldc, epi, gelu_erf,   \
-                                                                      a_rows, w_rows, c_kb_rows, ho, s)         \
-                  : launch_cfg<bm, bn, bk, st, wgm, wgn, false, false>(A, W, bias, C, M, N, K, ldc, epi, gelu_erf,  \
-                                                                       a_rows, w_rows, c_kb_rows, ho, s);
+        return kb ? launch_cfg<bm, bn, bk, st, wgm, wgn, true>(A, W, bias, C, M, N, K, ldc, epi, gelu_erf, a_rows,  \
+                                                               w_rows, c_kb_rows, ho, s)                         \
+                  : launch_cfg<bm, bn, bk, st, wgm, wgn, false>(A, W, bias, C, M, N, K, ldc, epi, gelu_erf, a_rows, \
+                                                                w_rows, c_kb_rows, ho, s);
 #ifdef GPT2_GEMM_TUNE
         GPT2_CFG(0, 256, 256, 32, 4, 2, 4)
-        GPT2_CFG(2, 256, 192, 32, 4, 2, 2)
-        GPT2_CFG(5, 128, 64, 32, 4, 2, 2)
-        GPT2_CFG(6, 256, 128, 32, 4, 2, 4)
         GPT2_CFG(8, 256, 256, 32, 5, 2, 4)
-        GPT2_CFG(9, 192, 256, 32, 4, 2, 2)
-        GPT2_CFG(10, 128, 96, 64, 3, 2, 2)
         GPT2_CFG(11, 128, 96, 64, 4, 2, 2)
         GPT2_CFG(12, 64, 96, 64, 4, 2, 2)
         GPT2_CFG(16, 256, 192, 64, 2, 2, 4)
-        GPT2_CFG(19, 192, 256, 64, 2, 2, 4)
         GPT2_CFG(22, 192, 256, 32, 5, 2, 4)
         GPT2_CFG(23, 256, 192, 32, 5, 2, 4)
-        GPT2_CFG(24, 64, 96, 32, 6, 2, 2)
-        GPT2_CFG(25, 128, 96, 32, 5, 2, 2)
-        GPT2_CFG(27, 256, 128, 32, 5, 2, 4)
 #else
         GPT2_CFG(8, 256, 256, 32, 5, 2, 4)
         GPT2_CFG(11, 128, 96, 64, 4, 2, 2)
@@ -757,7 +647,6 @@ hipError_t gemm_bf16(const uint16_t* A, const uint16_t* W, const float* bias, vo
         GPT2_CFG(23, 256, 192, 32, 5, 2, 4)
 #endif
 #undef GPT2_CFG
-#undef GPT2_CFG_BD
     }
     return hipErrorInvalidValue;
 }
