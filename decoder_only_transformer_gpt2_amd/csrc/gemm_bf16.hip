@@ -91,9 +91,9 @@ __device__ __forceinline__ void static_for(F&& f) {
 
 template <int BM, int BN, int BK, int S, int WGM, int WGN, int EPI, bool KB, int NKT>
 // NKT > 0: the K loop has exactly NKT steps and is unrolled completely (straight-line code with
-// compile-time ring slots and waits; a loop header makes the compiler drain every outstanding
-// DMA before the first LDS read of each iteration, since it cannot tell which stage that read
-// depends on across the back edge).
+// compile-time ring slots and waits): at a loop header the compiler drains every outstanding DMA
+// before the first LDS read of the iteration (vmcnt(0) once per ring turn), since it cannot tell
+// across the back edge which stage that read depends on.
 // Two workgroups per CU (256 registers per lane) wherever the ring fits twice in LDS and the
 // wave tile is at most 128 x 64.
 __global__ __launch_bounds__(64 * WGM * WGN,
@@ -554,25 +554,36 @@ int choose_cfg(int M, int N, int K, bool kb) {
     return 16;
 }
 
-template <int BM, int BN, int BK, int S, int WGM, int WGN, bool KB, int NKT = 0>
-hipError_t launch_cfg(const uint16_t* A, const uint16_t* W, const float* bias, void* C, int M, int N, int K, long ldc,
-                      int epi, int gelu_erf, int a_rows, int w_rows, int c_kb, const HeadOut& ho, hipStream_t s) {
-    // the K loops of the forward's projections (K = 768 and 3072, k-blocked) run fully unrolled
-    if constexpr (KB && NKT == 0) {
-        const int nk = K / BK;
+// One epilogue's launch, with the K loop fully unrolled for the step counts that occur: the
+// forward's k-blocked projections (K = 768 and 3072) and the plain fp32 products of the backward
+// (K = 768, 2304, 3072 and B*T = 4096 at the benchmark shape).
+template <int BM, int BN, int BK, int S, int WGM, int WGN, int EPI, bool KB>
+void launch_epi(dim3 grid, dim3 block, hipStream_t s, const uint16_t* A, const uint16_t* W, const float* bias,
+                void* C, int M, int N, int K, int ldc, int a_rows, int w_rows, int tiles_m, int group_m, int c_kb,
+                const HeadOut& ho) {
+#define GPT2_LAUNCH_NK(NK)                                                                                       \
+    gemm_bf16_kernel<BM, BN, BK, S, WGM, WGN, EPI, KB, NK><<<grid, block, 0, s>>>(A, W, bias, C, M, N, K, ldc, a_rows, \
+                                                                                  w_rows, tiles_m, group_m, c_kb, ho)
+    const int nk = K / BK;
+    if constexpr (KB || EPI == EPI_LOGITS) {
         if constexpr (BK == 32) {
-            if (nk == 24)
-                return launch_cfg<BM, BN, BK, S, WGM, WGN, KB, 24>(A, W, bias, C, M, N, K, ldc, epi, gelu_erf,
-                                                                       a_rows, w_rows, c_kb, ho, s);
+            if (nk == 24) return (void)GPT2_LAUNCH_NK(24);
         } else {
-            if (nk == 12)
-                return launch_cfg<BM, BN, BK, S, WGM, WGN, KB, 12>(A, W, bias, C, M, N, K, ldc, epi, gelu_erf,
-                                                                       a_rows, w_rows, c_kb, ho, s);
-            if (nk == 48)
-                return launch_cfg<BM, BN, BK, S, WGM, WGN, KB, 48>(A, W, bias, C, M, N, K, ldc, epi, gelu_erf,
-                                                                       a_rows, w_rows, c_kb, ho, s);
+            if (nk == 12) return (void)GPT2_LAUNCH_NK(12);
+            if (nk == 48) return (void)GPT2_LAUNCH_NK(48);
+            if constexpr (!KB) {
+                if (nk == 36) return (void)GPT2_LAUNCH_NK(36);
+                if (nk == 64) return (void)GPT2_LAUNCH_NK(64);
+            }
         }
     }
+    GPT2_LAUNCH_NK(0);
+#undef GPT2_LAUNCH_NK
+}
+
+template <int BM, int BN, int BK, int S, int WGM, int WGN, bool KB>
+hipError_t launch_cfg(const uint16_t* A, const uint16_t* W, const float* bias, void* C, int M, int N, int K, long ldc,
+                      int epi, int gelu_erf, int a_rows, int w_rows, int c_kb, const HeadOut& ho, hipStream_t s) {
     const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
     // group_m in [1, 1000): XCD-contiguous remap + groups of group_m row-tiles; < 0: plain order,
     // groups of -group_m; >= 1000: XCD-interleaved groups of group_m - 1000 row-tiles. Measured in
@@ -588,9 +599,9 @@ hipError_t launch_cfg(const uint16_t* A, const uint16_t* W, const float* bias, v
         if (const char* e = getenv("GPT2_HEAD_GROUP")) group_m = atoi(e);
 #endif
     dim3 grid(tiles_m * tiles_n), block(64 * WGM * WGN);
-#define GPT2_LAUNCH(E)                                                                                      \
-    gemm_bf16_kernel<BM, BN, BK, S, WGM, WGN, E, KB, NKT><<<grid, block, 0, s>>>(A, W, bias, C, M, N, K, ldc,           \
-                                                                      a_rows, w_rows, tiles_m, group_m, c_kb, ho)
+#define GPT2_LAUNCH(E)                                                                                         \
+    launch_epi<BM, BN, BK, S, WGM, WGN, E, KB>(grid, block, s, A, W, bias, C, M, N, K, (int)ldc, a_rows, w_rows, \
+                                               tiles_m, group_m, c_kb, ho)
     switch (epi) {
         case EPI_BIAS: GPT2_LAUNCH(EPI_BIAS); break;
         case EPI_BIAS_GELU:
