@@ -59,9 +59,21 @@ def train_flops(s: synth.ModelShape, B: int, T: int) -> float:
     return 3.0 * gemm + 3.0 * attn
 
 
-def traffic_record(kernel_src: str):
+GEMM_SOURCES = ("gemm_bf16_impl.h", "gemm_bf16.hip")  # the kernel and its launch / tile choice
+
+
+def gemm_source_sha() -> str:
+    """sha256 (first 16 hex digits) of the GEMM kernel sources, in GEMM_SOURCES order."""
+    h = hashlib.sha256()
+    for name in GEMM_SOURCES:
+        with open(os.path.join(ROOT, "decoder_only_transformer_gpt2_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_record():
     """HBM bytes per lm_head launch from the stored rocprofv3 counter summary, or None when the
-    summary is missing or was taken on a different version of the kernel source."""
+    summary is missing or was taken on a different version of the GEMM sources."""
     path = os.path.join(ROOT, "profiles", "lm_head_traffic.txt")
     if not os.path.exists(path):
         return None
@@ -70,8 +82,7 @@ def traffic_record(kernel_src: str):
         if "=" in line and not line.startswith("#"):
             k, v = line.split("=", 1)
             kv[k.strip()] = v.strip()
-    sha = hashlib.sha256(open(kernel_src, "rb").read()).hexdigest()[:16]
-    if kv.get("kernel_source_sha") != sha or "traffic_bytes_per_launch" not in kv:
+    if kv.get("kernel_source_sha") != gemm_source_sha() or "traffic_bytes_per_launch" not in kv:
         return None
     return float(kv["traffic_bytes_per_launch"])
 
@@ -159,7 +170,7 @@ def main():
     lm_flops = 2.0 * M * shape.d_model * shape.n_vocab
     achieved = lm_flops / (lm_ms * 1e-3) / 1e12
     flops = forward_flops(shape, B, T)
-    traffic = traffic_record(os.path.join(ROOT, "decoder_only_transformer_gpt2_amd", "csrc", "gemm_bf16.hip"))
+    traffic = traffic_record()
 
     out = {
         "metric": METRIC, "value": M / (ms * 1e-3), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
