@@ -139,6 +139,24 @@ def test_linear(g, dtype, epi, M, N, K):
     assert np.all(np.abs(got - ref) <= tol), float(np.max(np.abs(got - ref) - tol))
 
 
+@pytest.mark.parametrize("M,N,K", [(256, 768, 2304), (128, 768, 4096), (4096, 2304, 768)])
+def test_linear_unrolled_k(g, M, N, K):
+    """Plain fp32 products (epilogue 3, no bias) whose K loop is fully unrolled: 36 and 64 steps of
+    64 on 64 x 96 tiles (the backward's input and weight gradients), and 24 steps of 32 on the
+    five-stage 192 x 256 tiles."""
+    r = np.random.Generator(np.random.PCG64(K))
+    A = synth.round_bf16(r.standard_normal((M, K)).astype(np.float32))
+    W = synth.round_bf16((0.02 * r.standard_normal((N, K))).astype(np.float32))
+    C = torch.empty((M, N), dtype=torch.float32, device="cuda")
+    log(f"linear bf16 epi=3 M={M} N={N} K={K}")
+    g.linear(torch.from_numpy(_pad_rows(A)).cuda().to(torch.bfloat16),
+             torch.from_numpy(_pad_rows(W)).cuda().to(torch.bfloat16), None, C, M, N, K, 3)
+    got = C.cpu().numpy().astype(np.float64)
+    ref = O.linear(A, W, None)
+    tol = 1e-5 * (O.linear(np.abs(A), np.abs(W), None) + 1.0)
+    assert np.all(np.abs(got - ref) <= tol), float(np.max(np.abs(got - ref) - tol))
+
+
 def test_linear_gelu_erf_variant(g):
     r = np.random.Generator(np.random.PCG64(7))
     M, N, K = 128, 256, 64
@@ -498,16 +516,17 @@ def test_decode_bf16_vs_forward_and_oracle(g, small_bf16):
     assert e <= 5e-2
 
 
-def test_decode_multi_chunk_context(g):
-    """A context longer than one 1024-key chunk of the decode attention (n_ctx 2048, small model,
-    fp32), against the oracle."""
-    s = synth.ModelShape(n_vocab=1000, n_ctx=2048, d_model=128, n_head=2, n_layer=2, d_mlp=512)
+@pytest.mark.parametrize("n_ctx,pos", [(2048, 1500), (4096, 3000)])
+def test_decode_multi_chunk_context(g, n_ctx, pos):
+    """Contexts longer than one 1024-key chunk of the decode attention (small model, fp32), against
+    the oracle: 1501 keys (two chunks, the second partial) and 3001 keys (three chunks)."""
+    s = synth.ModelShape(n_vocab=1000, n_ctx=n_ctx, d_model=128, n_head=2, n_layer=2, d_mlp=512)
     m, w = model(g, s, "f32")
-    tok = synth.make_tokens(1, 1504, n_vocab=1000)
-    got = _teacher_forced(m, tok, 1500, m.kv_cache(1))
-    ref = O.forward(w, tok, 2, 2)[:, 1500:]
+    tok = synth.make_tokens(1, pos + 4, n_vocab=1000)
+    got = _teacher_forced(m, tok, pos, m.kv_cache(1))
+    ref = O.forward(w, tok, 2, 2)[:, pos:]
     e = row_rel_l2(got, ref).max()
-    log(f"  decode at positions 1500..1503: max row rel L2 = {e:.3e}")
+    log(f"  decode at positions {pos}..{pos + 3}: max row rel L2 = {e:.3e}")
     assert e <= 1e-4
 
 
