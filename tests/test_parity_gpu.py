@@ -108,7 +108,10 @@ def _pad_rows(a, mult=256):
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 @pytest.mark.parametrize("epi", [0, 1, 2, 3])
-@pytest.mark.parametrize("M,N,K", [(300, 200, 128), (256, 2304, 768), (77, 1000, 3072)])
+@pytest.mark.parametrize("M,N,K", [(300, 200, 128), (256, 2304, 768), (77, 1000, 3072),
+                                   # few rows (bf16: the W-streaming kernel, 16 columns per
+                                   # workgroup, a ragged last one at N = 1000; K split 16 / 4 ways)
+                                   (4, 768, 3072), (16, 1000, 768), (1, 2304, 768)])
 def test_linear(g, dtype, epi, M, N, K):
     r = np.random.Generator(np.random.PCG64(100 + epi))
     A = synth.round_bf16(r.standard_normal((M, K)).astype(np.float32))
