@@ -25,9 +25,10 @@ FLAGS = [
 ]
 # Per-source additions. The attention kernels (forward and backward) run their softmax on the MFMA
 # results, so their accumulators are kept in ordinary VGPRs (MFMA in VGPR form) instead of being
-# copied out of AGPRs.
+# copied out of AGPRs. The forward attention is also built without NaN semantics: its scores are
+# finite or -inf, and IEEE fmaxf would otherwise re-canonicalise every MFMA result before each max.
 FILE_FLAGS = {
-    "attention.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
+    "attention.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1", "-fno-honor-nans"],
     "attention_bwd.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
 }
 

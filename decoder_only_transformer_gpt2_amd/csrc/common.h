@@ -23,8 +23,12 @@ __device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
     return __builtin_bit_cast(uint16_t, b);
 }
 
+// Two floats to two bf16 (round to nearest even) in one word, lo in the low half: one
+// v_cvt_pk_bf16_f32 (the same rounding as f32_to_bf16_bits).
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-    return (uint32_t)f32_to_bf16_bits(lo) | ((uint32_t)f32_to_bf16_bits(hi) << 16);
+    typedef float f32x2_v __attribute__((ext_vector_type(2)));
+    typedef __bf16 bf16x2_v __attribute__((ext_vector_type(2)));
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_v{lo, hi}, bf16x2_v));
 }
 
 // GELU forms. tanh form: 0.5 x (1 + tanh(sqrt(2/pi) (x + 0.044715 x^3))); erf form: 0.5 x (1 + erf(x/sqrt 2)).

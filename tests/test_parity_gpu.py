@@ -184,7 +184,7 @@ def attn_tolerance(q, k, v, ref, dtype):
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
-@pytest.mark.parametrize("B,H,T", [(1, 1, 1), (2, 3, 64), (2, 3, 200), (1, 2, 1024)])
+@pytest.mark.parametrize("B,H,T", [(1, 1, 1), (2, 1, 33), (2, 3, 64), (1, 2, 96), (2, 3, 200), (1, 2, 1024)])
 def test_attention_small(g, dtype, B, H, T):
     q, k, v = synth.make_qkv(B, H, T, 64, bf16=True)
     tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
