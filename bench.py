@@ -59,7 +59,7 @@ def train_flops(s: synth.ModelShape, B: int, T: int) -> float:
     return 3.0 * gemm + 3.0 * attn
 
 
-GEMM_SOURCES = ("gemm_bf16_impl.h", "gemm_bf16.hip")  # the kernel and its launch / tile choice
+GEMM_SOURCES = ("gemm_bf16_impl.h", "gemm_bf16.hip", "common.h")  # the kernel, its launch / tile choice, helpers
 
 
 def gemm_source_sha() -> str:
