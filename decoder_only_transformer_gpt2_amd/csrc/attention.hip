@@ -31,16 +31,13 @@ constexpr int KT = 64;        // keys per LDS tile
 constexpr int DH = 64;        // head size
 constexpr int VTS = KT + 4;   // row stride (elements) of the transposed V tile: 34 words, so the
                               // 8-byte fragment reads of 16 rows fall on distinct banks
-// Maximum over the four lanes L, L^16, L^32, L^48 (the four 16-lane rows), with the gfx950 row
-// swaps: permlane16_swap exchanges rows 1 <-> 0 and 3 <-> 2 between its two results, permlane32_swap
-// the two wavefront halves, so each lane sees its own value and its partner's.
+// Maximum over the four lanes L, L^16, L^32, L^48 (the four 16-lane rows). Only the rare
+// rescale path needs it. (The gfx950 row-swap builtins would avoid the LDS crossbar, but this
+// toolchain miscompiles them when both operands are the same value.)
 __device__ __forceinline__ float max_over_rows(float m) {
-    const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(m), __float_as_uint(m), false, false);
-    m = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
-    const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(m), __float_as_uint(m), false, false);
-    return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+    m = fmaxf(m, __shfl_xor(m, 16, GPT2_WAVE));
+    return fmaxf(m, __shfl_xor(m, 32, GPT2_WAVE));
 }
-
 
 // K tile element offset of (key, 16-byte chunk): chunks are permuted within a key row by
 // (key & 7) ^ ((key >> 3) & 1), which spreads the 16-byte reads of 16 consecutive keys over all

@@ -13,9 +13,12 @@ namespace {
 // k-blocked operands the five-stage 32-wide ring, else the two-stage 64-wide one). Narrow outputs
 // (N <= 1024) prefer 64 x 96 tiles with a four-stage ring (two workgroups per CU), or 128 x 96 with
 // a four-stage 64-wide ring for K >= 2048 (mlp.c_proj: 394 against 420 us per forward). The
-// vocabulary projection, with tiles for every CU many times over, uses 256 x 256 tiles of eight
-// waves with a five-stage ring (in the forward: 395-405 us; four stages 405-415 us; 256 x 128
-// tiles of four waves, two per CU, 460 us before the K loops were unrolled).
+// vocabulary projection, with tiles for every CU many times over, spends about 40% of its time in
+// the epilogue (staging, argmax partials, 824 MB of fp32 logits), which overlaps nothing when one
+// workgroup fills a CU; it uses 128 x 256 tiles of four waves with a three-stage ring, two
+// workgroups per CU, so that one's epilogue runs beside the other's K loop (in the forward: 364-366
+// us; 256 x 256 tiles of eight waves with a five-stage ring, one per CU, 404-418 us; 256 x 128
+// tiles two per CU 409 us).
 int choose_cfg(int M, int N, int K, bool kb) {
 #ifdef GPT2_GEMM_TUNE
     if (const char* e = getenv("GPT2_GEMM_CFG")) {
@@ -33,7 +36,7 @@ int choose_cfg(int M, int N, int K, bool kb) {
         if (const char* e = getenv(name)) return atoi(e);
     }
 #endif
-    if (tiles(256, 256) >= 4 * 256) return 8;  // vocabulary projection
+    if (tiles(256, 256) >= 4 * 256) return 21;  // vocabulary projection
     // narrow outputs of very many rows (the wte weight gradient, M = n_vocab): large tiles, since
     // the grid fills the CUs twice over anyway and each tile re-reads less through L2
     if (N <= 1024 && tiles(256, 192) >= 512) return 16;
@@ -67,20 +70,22 @@ hipError_t gemm_bf16(const uint16_t* A, const uint16_t* W, const float* bias, vo
     switch (choose_cfg(M, N, K, kb)) {
 #define GPT2_CFG(i) \
     case i: return gemm_bf16_cfg_##i(A, W, bias, C, M, N, K, ldc, epi, gelu_erf, a_rows, w_rows, c_kb_rows, ho, s, kb);
-        GPT2_CFG(8)
         GPT2_CFG(11)
         GPT2_CFG(12)
         GPT2_CFG(16)
         GPT2_CFG(22)
         GPT2_CFG(23)
+        GPT2_CFG(21)
 #ifdef GPT2_GEMM_TUNE
         GPT2_CFG(0)
+        GPT2_CFG(8)
         GPT2_CFG(2)
         GPT2_CFG(5)
         GPT2_CFG(6)
         GPT2_CFG(9)
         GPT2_CFG(10)
         GPT2_CFG(19)
+        GPT2_CFG(20)
         GPT2_CFG(24)
         GPT2_CFG(25)
         GPT2_CFG(27)

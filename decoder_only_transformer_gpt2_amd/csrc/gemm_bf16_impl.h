@@ -503,7 +503,7 @@ constexpr TileCfg kCfgs[] = {
     {256, 128, 64, 2, 2, 4},  // 18
     {192, 256, 64, 2, 2, 4},  // 19: 8 waves, 96 x 64 each
     {256, 128, 32, 3, 2, 2},  // 20: 4 waves, 128 x 64 each, 72 KB ring: 2 workgroups per CU
-    {128, 256, 32, 3, 2, 2},  // 21: 4 waves, 64 x 128 each, 72 KB ring
+    {128, 256, 32, 3, 2, 2},  // 21: 4 waves, 64 x 128 each, 72 KB ring: 2 workgroups per CU
     {192, 256, 32, 5, 2, 4},  // 22: 8 waves, 140 KB ring
     {256, 192, 32, 5, 2, 4},  // 23: 8 waves, 140 KB ring
     {64, 96, 32, 6, 2, 2},    // 24: 4 waves, 60 KB ring
@@ -546,12 +546,13 @@ hipError_t launch_cfg(const uint16_t* A, const uint16_t* W, const float* bias, v
     const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
     // group_m in [1, 1000): XCD-contiguous remap + groups of group_m row-tiles; < 0: plain order,
     // groups of -group_m; >= 1000: XCD-interleaved groups of group_m - 1000 row-tiles. Measured in
-    // the forward (cold caches for the wte operand): the vocabulary projection is fastest with
-    // XCD-interleaved pairs of row-tiles (420 us; plain pairs 442 us; XCD-contiguous ranges 520 us
-    // and more): each wte tile is then read once per row pair into one XCD's L2 instead of into
-    // two, while the eight XCDs sweep neighbouring columns together, so the logits are written in
-    // long runs. The block projections are insensitive to the order.
-    int group_m = tiles_n >= 64 ? 1002 : 4;
+    // the forward (cold caches for the wte operand), vocabulary projection on 128 x 256 tiles:
+    // XCD-interleaved groups of 3-6 row-tiles 364-366 us, of 2 392 us, of 8 383 us, of 1 519 us;
+    // XCD-contiguous ranges 457 us and more, plain pairs 506 us. With interleaved groups each wte
+    // tile is read into one XCD's L2 per group of row-tiles instead of into several, while the eight
+    // XCDs sweep neighbouring columns together, so the logits are written in long runs. The block
+    // projections are insensitive to the order.
+    int group_m = tiles_n >= 64 ? 1004 : 4;
 #ifdef GPT2_GEMM_TUNE
     if (const char* e = getenv("GPT2_GEMM_GROUP")) group_m = atoi(e);
     if (tiles_n >= 64)
@@ -597,20 +598,22 @@ hipError_t launch_cfg(const uint16_t* A, const uint16_t* W, const float* bias, v
                                                                                 ho, s);                         \
     }
 // the configurations the library dispatches to (the tuning builds add the others of kCfgs)
-GPT2_GEMM_DECLARE_CFG(8)
 GPT2_GEMM_DECLARE_CFG(11)
 GPT2_GEMM_DECLARE_CFG(12)
 GPT2_GEMM_DECLARE_CFG(16)
 GPT2_GEMM_DECLARE_CFG(22)
 GPT2_GEMM_DECLARE_CFG(23)
+GPT2_GEMM_DECLARE_CFG(21)
 #ifdef GPT2_GEMM_TUNE
 GPT2_GEMM_DECLARE_CFG(0)
+GPT2_GEMM_DECLARE_CFG(8)
 GPT2_GEMM_DECLARE_CFG(2)
 GPT2_GEMM_DECLARE_CFG(5)
 GPT2_GEMM_DECLARE_CFG(6)
 GPT2_GEMM_DECLARE_CFG(9)
 GPT2_GEMM_DECLARE_CFG(10)
 GPT2_GEMM_DECLARE_CFG(19)
+GPT2_GEMM_DECLARE_CFG(20)
 GPT2_GEMM_DECLARE_CFG(24)
 GPT2_GEMM_DECLARE_CFG(25)
 GPT2_GEMM_DECLARE_CFG(27)
