@@ -14,6 +14,9 @@ the backward pass) under "train".
 
 The roofline object is for the lm_head GEMM, the largest single launch: its duration is taken
 from HIP events the library records on its own stream around that launch in every timed step.
+"kernels" gives the same for every launch kind of the forward (mean duration per launch from
+events around each launch of five extra forwards, algorithmic work, roofline fraction, share of
+the forward's kernel time).
 The CPU baseline times the fp64 oracle on a bounded sample (one full sequence) on the host.
 """
 from __future__ import annotations
@@ -57,6 +60,30 @@ def train_flops(s: synth.ModelShape, B: int, T: int) -> float:
     gemm = 24.0 * M * s.n_layer * s.d_model ** 2 + 2.0 * M * s.d_model * s.n_vocab
     attn = 2.0 * B * s.n_layer * s.d_model * T * (T + 1)
     return 3.0 * gemm + 3.0 * attn
+
+
+def kernel_work(kind: str, s: synth.ModelShape, B: int, T: int):
+    """(bound, algorithmic work per launch) of one launch kind of the forward: FLOPs for the matrix
+    products (attention: its causal half, diagonal included), HBM bytes for the row-wise kernels
+    (each operand read once, each result written once)."""
+    M, d, V = B * T, s.d_model, s.n_vocab
+    if kind == "qkv":
+        return "mfma", 2.0 * M * 3 * d * d
+    if kind == "attn_proj":
+        return "mfma", 2.0 * M * d * d
+    if kind in ("fc", "mlp_proj"):
+        return "mfma", 2.0 * M * s.d_mlp * d
+    if kind == "attn":
+        return "mfma", 2.0 * B * d * T * (T + 1)
+    if kind == "lm_head":
+        return "mfma", 2.0 * M * d * V
+    if kind in ("ln", "ln_f"):  # fp32 rows in, bf16 rows out, gamma and beta
+        return "hbm", M * d * 4.0 + M * d * 2.0 + 2 * d * 4.0
+    if kind == "embed":  # token ids, wte and wpe rows (bf16), fp32 residual out
+        return "hbm", M * 4.0 + M * d * 2.0 + T * d * 2.0 + M * d * 4.0
+    if kind == "argmax":  # (value, column) partials per 256-column tile, int32 result
+        return "hbm", M * ((V + 255) // 256) * 8.0 + M * 4.0
+    return None, None
 
 
 GEMM_SOURCES = ("gemm_bf16_impl.h", "gemm_bf16.hip", "common.h")  # the kernel, its launch / tile choice, helpers
@@ -115,7 +142,6 @@ def main():
     ap.add_argument("--no-loss", action="store_true", help="skip the fused forward+loss measurement")
     ap.add_argument("--no-decode", action="store_true", help="skip the cached decode measurement")
     ap.add_argument("--no-train", action="store_true", help="skip the forward+backward (gradients) measurement")
-    ap.add_argument("--breakdown", action="store_true", help="also time every launch of one extra forward")
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="after the timed region, run a plain device-to-device copy of this many bytes three "
                          "times (a known-size reference for hardware traffic counters)")
@@ -303,15 +329,34 @@ def main():
         torch.cuda.synchronize()
         out["copy_bytes"] = args.copy_bytes
 
-    if args.breakdown:
+    # Every launch kind of the forward, timed with HIP events around each launch of a few extra
+    # forwards (after the timed region): mean duration, algorithmic work and its roofline.
+    reps = 5
+    tot = {}
+    for _ in range(reps):
         evs = [(raw_event(), raw_event()) for _ in kinds]
         torch.cuda.synchronize()
         m.forward_timed(tokens, logits, am, [a.cuda_event for a, _ in evs], [b.cuda_event for _, b in evs], ws)
         torch.cuda.synchronize()
-        per = {}
         for k, (a, b) in zip(kinds, evs):
-            per[k] = per.get(k, 0.0) + a.elapsed_time(b)
-        out["breakdown_ms"] = per
+            tot[k] = tot.get(k, 0.0) + a.elapsed_time(b)
+    all_ms = sum(tot.values()) / reps
+    kernels = {}
+    for k in dict.fromkeys(kinds):
+        n = kinds.count(k)
+        us = tot[k] / reps / n * 1e3
+        bound, work = kernel_work(k, shape, B, T)
+        e = {"launches": n, "avg_us": us, "share": tot[k] / reps / all_ms}
+        if bound == "mfma":
+            e.update(bound="mfma", unit="TFLOP/s", work_per_launch=work, achieved=work / (us * 1e-6) / 1e12,
+                     peak=PEAK_BF16_TFLOPS)
+        elif bound == "hbm":
+            e.update(bound="hbm", unit="GB/s", work_per_launch=work, achieved=work / (us * 1e-6) / 1e9,
+                     peak=PEAK_HBM_GBS)
+        if bound:
+            e["frac"] = e["achieved"] / e["peak"]
+        kernels[k] = e
+    out["kernels"] = kernels
 
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, tok_np, shape)
