@@ -1,6 +1,6 @@
 """Forward-pass throughput of the HIP GPT-2 library on one MI355X.
 
-python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload small|medium|xl] [--no-cpu-baseline] [--no-loss] [--no-decode] [--no-train]
+python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload small|medium|xl] [--no-cpu-baseline] [--no-loss] [--no-decode] [--no-train] [--no-kernels]
 
 One step = one gpt2_forward over a batch of synthetic token ids already resident in HBM:
 embedding, every block, ln_f, the tied lm_head (fp32 logits) and the fused argmax. Weights are the
@@ -142,6 +142,7 @@ def main():
     ap.add_argument("--no-loss", action="store_true", help="skip the fused forward+loss measurement")
     ap.add_argument("--no-decode", action="store_true", help="skip the cached decode measurement")
     ap.add_argument("--no-train", action="store_true", help="skip the forward+backward (gradients) measurement")
+    ap.add_argument("--no-kernels", action="store_true", help="skip the per-kernel breakdown (five extra forwards)")
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="after the timed region, run a plain device-to-device copy of this many bytes three "
                          "times (a known-size reference for hardware traffic counters)")
@@ -331,7 +332,7 @@ def main():
 
     # Every launch kind of the forward, timed with HIP events around each launch of a few extra
     # forwards (after the timed region): mean duration, algorithmic work and its roofline.
-    reps = 5
+    reps = 0 if args.no_kernels else 5
     tot = {}
     for _ in range(reps):
         evs = [(raw_event(), raw_event()) for _ in kinds]
@@ -340,9 +341,9 @@ def main():
         torch.cuda.synchronize()
         for k, (a, b) in zip(kinds, evs):
             tot[k] = tot.get(k, 0.0) + a.elapsed_time(b)
-    all_ms = sum(tot.values()) / reps
     kernels = {}
-    for k in dict.fromkeys(kinds):
+    all_ms = sum(tot.values()) / reps if reps else 0.0
+    for k in dict.fromkeys(kinds) if reps else []:
         n = kinds.count(k)
         us = tot[k] / reps / n * 1e3
         bound, work = kernel_work(k, shape, B, T)
@@ -356,7 +357,8 @@ def main():
         if bound:
             e["frac"] = e["achieved"] / e["peak"]
         kernels[k] = e
-    out["kernels"] = kernels
+    if reps:
+        out["kernels"] = kernels
 
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, tok_np, shape)

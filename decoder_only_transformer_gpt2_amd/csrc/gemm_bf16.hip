@@ -11,8 +11,11 @@ namespace {
 // shrink), so the largest tile that still gives every CU about one tile wins: 192 x 256 for
 // N = 2304 (198 tiles, a five-stage 32-wide ring), 256 x 192 for N = 3072 (256 tiles; with
 // k-blocked operands the five-stage 32-wide ring, else the two-stage 64-wide one). Narrow outputs
-// (N <= 1024) prefer 64 x 96 tiles with a four-stage ring (two workgroups per CU), or 128 x 96 with
-// a four-stage 64-wide ring for K >= 2048 (mlp.c_proj: 394 against 420 us per forward). The
+// (N <= 1024) on k-blocked operands take 128 x 96 tiles of eight wavefronts (4 x 2, 32 x 48 each)
+// with a four-stage 64-wide ring: two wavefronts per SIMD hide the LDS and barrier latency that a
+// single one leaves exposed (per forward, mlp.c_proj 392 -> 376 us and attn.c_proj 192 -> 176 us
+// against 128 x 96 tiles of four wavefronts and 64 x 96 tiles two per CU); row-major narrow
+// products (the backward) keep 64 x 96 tiles with a four-stage ring, two workgroups per CU. The
 // vocabulary projection, with tiles for every CU many times over, spends about 40% of its time in
 // the epilogue (staging, argmax partials, 824 MB of fp32 logits), which overlaps nothing when one
 // workgroup fills a CU; it uses 128 x 256 tiles of four waves with a three-stage ring, two
@@ -40,9 +43,9 @@ int choose_cfg(int M, int N, int K, bool kb) {
     // narrow outputs of very many rows (the wte weight gradient, M = n_vocab): large tiles, since
     // the grid fills the CUs twice over anyway and each tile re-reads less through L2
     if (N <= 1024 && tiles(256, 192) >= 512) return 16;
-    // narrow outputs with a long reduction (mlp.c_proj, K = 4d) on k-blocked operands: 128 x 96
-    // tiles (one wave of 256 workgroups) re-read less than 64 x 96 ones
-    if (N <= 1024 && kb && K >= 2048 && tiles(128, 96) >= 192) return 11;
+    // narrow outputs on k-blocked operands (attn.c_proj, mlp.c_proj): 128 x 96 tiles of eight
+    // wavefronts (two per SIMD, 32 x 48 each), one wave of 256 workgroups
+    if (N <= 1024 && kb && tiles(128, 96) >= 192) return 28;
     if (N <= 1024) return 12;
     if (tiles(192, 256) < 128) return 12;  // few rows (weight gradients, short prompts): fill the CUs
     if (tiles(192, 256) <= 256) return 22;
@@ -70,13 +73,14 @@ hipError_t gemm_bf16(const uint16_t* A, const uint16_t* W, const float* bias, vo
     switch (choose_cfg(M, N, K, kb)) {
 #define GPT2_CFG(i) \
     case i: return gemm_bf16_cfg_##i(A, W, bias, C, M, N, K, ldc, epi, gelu_erf, a_rows, w_rows, c_kb_rows, ho, s, kb);
-        GPT2_CFG(11)
         GPT2_CFG(12)
         GPT2_CFG(16)
         GPT2_CFG(22)
         GPT2_CFG(23)
         GPT2_CFG(21)
+        GPT2_CFG(28)
 #ifdef GPT2_GEMM_TUNE
+        GPT2_CFG(11)
         GPT2_CFG(0)
         GPT2_CFG(8)
         GPT2_CFG(2)
@@ -89,6 +93,7 @@ hipError_t gemm_bf16(const uint16_t* A, const uint16_t* W, const float* bias, vo
         GPT2_CFG(24)
         GPT2_CFG(25)
         GPT2_CFG(27)
+        GPT2_CFG(29)
 #endif
 #undef GPT2_CFG
     }

@@ -510,6 +510,8 @@ constexpr TileCfg kCfgs[] = {
     {128, 96, 32, 5, 2, 2},   // 25: 4 waves, 70 KB ring
     {128, 128, 32, 5, 2, 2},  // 26: 4 waves, 80 KB ring
     {256, 128, 32, 5, 2, 4},  // 27: 8 waves, 120 KB ring
+    {128, 96, 64, 4, 4, 2},   // 28: 8 waves (4 x 2), 32 x 48 each, 112 KB ring
+    {64, 192, 64, 4, 2, 4},   // 29: 8 waves, 32 x 48 each, 128 KB ring
 };
 [[maybe_unused]] constexpr int kNumCfgs = sizeof(kCfgs) / sizeof(kCfgs[0]);
 
@@ -598,13 +600,14 @@ hipError_t launch_cfg(const uint16_t* A, const uint16_t* W, const float* bias, v
                                                                                 ho, s);                         \
     }
 // the configurations the library dispatches to (the tuning builds add the others of kCfgs)
-GPT2_GEMM_DECLARE_CFG(11)
 GPT2_GEMM_DECLARE_CFG(12)
 GPT2_GEMM_DECLARE_CFG(16)
 GPT2_GEMM_DECLARE_CFG(22)
 GPT2_GEMM_DECLARE_CFG(23)
 GPT2_GEMM_DECLARE_CFG(21)
+GPT2_GEMM_DECLARE_CFG(28)
 #ifdef GPT2_GEMM_TUNE
+GPT2_GEMM_DECLARE_CFG(11)
 GPT2_GEMM_DECLARE_CFG(0)
 GPT2_GEMM_DECLARE_CFG(8)
 GPT2_GEMM_DECLARE_CFG(2)
@@ -617,6 +620,7 @@ GPT2_GEMM_DECLARE_CFG(20)
 GPT2_GEMM_DECLARE_CFG(24)
 GPT2_GEMM_DECLARE_CFG(25)
 GPT2_GEMM_DECLARE_CFG(27)
+GPT2_GEMM_DECLARE_CFG(29)
 #endif
 
 }  // namespace gpt2k
