@@ -94,6 +94,8 @@ hipError_t gemm_bf16(const uint16_t* A, const uint16_t* W, const float* bias, vo
         GPT2_CFG(25)
         GPT2_CFG(27)
         GPT2_CFG(29)
+        GPT2_CFG(30)
+        GPT2_CFG(31)
 #endif
 #undef GPT2_CFG
     }

@@ -512,6 +512,8 @@ constexpr TileCfg kCfgs[] = {
     {256, 128, 32, 5, 2, 4},  // 27: 8 waves, 120 KB ring
     {128, 96, 64, 4, 4, 2},   // 28: 8 waves (4 x 2), 32 x 48 each, 112 KB ring
     {64, 192, 64, 4, 2, 4},   // 29: 8 waves, 32 x 48 each, 128 KB ring
+    {256, 192, 32, 5, 4, 4},  // 30: 16 waves, 64 x 48 each, 140 KB ring
+    {192, 256, 32, 5, 4, 4},  // 31: 16 waves, 48 x 64 each, 140 KB ring
 };
 [[maybe_unused]] constexpr int kNumCfgs = sizeof(kCfgs) / sizeof(kCfgs[0]);
 
@@ -621,6 +623,8 @@ GPT2_GEMM_DECLARE_CFG(24)
 GPT2_GEMM_DECLARE_CFG(25)
 GPT2_GEMM_DECLARE_CFG(27)
 GPT2_GEMM_DECLARE_CFG(29)
+GPT2_GEMM_DECLARE_CFG(30)
+GPT2_GEMM_DECLARE_CFG(31)
 #endif
 
 }  // namespace gpt2k
