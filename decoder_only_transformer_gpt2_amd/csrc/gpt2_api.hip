@@ -51,6 +51,7 @@ struct gpt2_model {
     // bf16: byte offset of the k-blocked copy of each GEMM weight (wte and the four projections of
     // every layer), read by the tiled GEMMs of the forward; 0 for other tensors
     std::vector<size_t> kb_offset;
+    std::vector<size_t> t_offset;  // transposed copy per matrix (0: none), for the backward
     size_t weight_bytes = 0;
     void* weights = nullptr;  // borrowed device pointer, set by gpt2_load_weights
     bool loaded = false;
@@ -93,13 +94,31 @@ void build_layout(gpt2_model* m) {
         for (int l = 0; l < c.n_layer; ++l)
             for (int t : {ATTN_W, APROJ_W, FC_W, MPROJ_W}) kb(2 + l * PER_LAYER + t);
     }
+    // bf16: transposed copies for the backward's input-gradient products (dX = dY W reads W^T
+    // [in][out] as its K-contiguous operand), packed once at load instead of on every backward:
+    // rows padded to 256 (zero), wte^T with its columns padded to a multiple of 64 (zero).
+    m->t_offset.assign(m->slots.size(), 0);
+    if (c.dtype == GPT2_BF16) {
+        auto tcopy = [&](int i, int64_t ld) {
+            m->t_offset[i] = off;
+            off = align_up(off + (size_t)round_up(m->slots[i].cols, kRowPad) * ld * 2, kAlign);
+        };
+        tcopy(0, round_up(c.n_vocab, 64));
+        for (int l = 0; l < c.n_layer; ++l)
+            for (int t : {ATTN_W, APROJ_W, FC_W, MPROJ_W}) tcopy(2 + l * PER_LAYER + t, m->slots[2 + l * PER_LAYER + t].rows);
+    }
     m->weight_bytes = off;
 }
+
+// Row stride (elements) of the transposed copy of matrix idx: its source row count, padded to a
+// multiple of 64 for wte (the reduction length of the lm_head input gradient).
+int64_t t_ld(const gpt2_model* m, int idx) { return idx == 0 ? round_up(m->cfg.n_vocab, 64) : m->slots[idx].rows; }
 
 const void* wptr(const gpt2_model* m, int idx) { return static_cast<const char*>(m->weights) + m->slots[idx].offset; }
 const void* wptr_kb(const gpt2_model* m, int idx) {
     return static_cast<const char*>(m->weights) + m->kb_offset[idx];
 }
+const void* wptr_t(const gpt2_model* m, int idx) { return static_cast<const char*>(m->weights) + m->t_offset[idx]; }
 int layer_idx(int l, int t) { return 2 + l * PER_LAYER + t; }
 
 WorkspaceLayout ws_layout(const gpt2_model* m, int B, int T) {
@@ -446,8 +465,10 @@ TrainLayout train_layout(const gpt2_model* m, int B, int T) {
     L.dact = take(L.Mp * L.wide * as);
     L.dT = take(L.rows_dT * L.Mk * as);
     L.xT = take(L.rows_x * L.Mk * as);
-    L.wT = take(L.rows_w * L.wide * as);
-    L.wteT = take(round_up(d, kRowPad) * L.Vp * as);
+    // transposed weights: packed with the weights in bf16 mode, transposed per backward in fp32 mode
+    const bool wt_packed = is_bf16(m);
+    L.wT = take(wt_packed ? 0 : L.rows_w * L.wide * as);
+    L.wteT = take(wt_packed ? 0 : round_up(d, kRowPad) * L.Vp * as);
     L.dlog = take(L.Mp * L.Vp * as);
     L.dlogT = take(L.Vr * L.Mk * as);
     L.part = take((size_t)gpt2k::colsum_blocks((int)L.M) * L.wide * 4);
@@ -570,12 +591,20 @@ gpt2_status enqueue_backward(const gpt2_model* m, const int32_t* tokens, int B, 
         if ((e = tr(x_act, true, n_in, M, n_in, xT, Mk, Mk)) != hipSuccess) return e;
         if ((e = gemm_nt(dT, pad(n_out), xT, pad(n_in), G(widx), n_out, n_in, Mk, n_in)) != hipSuccess) return e;
         if ((e = to_act(dy, n_out, dact)) != hipSuccess) return e;
-        if ((e = tr(wptr(m, widx), true, n_in, n_out, n_in, wT, n_out, n_out)) != hipSuccess) return e;
-        return gemm_nt(dact, Mp, wT, pad(n_in), dx_out, M, n_in, n_out, n_in);
+        const void* wt = wT;  // W^T: packed at load (bf16), else transposed here
+        if (m->t_offset[widx])
+            wt = wptr_t(m, widx);
+        else if ((e = tr(wptr(m, widx), true, n_in, n_out, n_in, wT, n_out, n_out)) != hipSuccess)
+            return e;
+        return gemm_nt(dact, Mp, wt, pad(n_in), dx_out, M, n_in, n_out, n_in);
     };
     // lm_head: dxf = dlogits wte, dwte (head part) = dlogits^T xf
-    GPT2_HIP(tr(wptr(m, 0), true, d, V, d, ws + L.wteT, Vp, Vp));
-    GPT2_HIP(gemm_nt(ws + L.dlog, Mp, ws + L.wteT, pad(d), dbuf, M, d, Vp, d));
+    const void* wteT = ws + L.wteT;
+    if (m->t_offset[0])
+        wteT = wptr_t(m, 0);
+    else
+        GPT2_HIP(tr(wptr(m, 0), true, d, V, d, ws + L.wteT, Vp, Vp));
+    GPT2_HIP(gemm_nt(ws + L.dlog, Mp, wteT, pad(d), dbuf, M, d, Vp, d));
     GPT2_HIP(tr(ws + L.dlog, true, Vp, M, Vp, ws + L.dlogT, Mk, Mk));
     GPT2_HIP(tr(ws + L.xf, true, d, M, d, xT, Mk, Mk));
     GPT2_HIP(gemm_nt(ws + L.dlogT, (int)L.Vr, xT, pad(d), G(0), V, d, Mk, d));
@@ -668,6 +697,12 @@ gpt2_status gpt2_load_weights(gpt2_model* m, const void* const* src, int32_t n_s
                 GPT2_HIP(gpt2k::kblock_bf16(reinterpret_cast<const uint16_t*>(d),
                                             reinterpret_cast<uint16_t*>(static_cast<char*>(dst) + m->kb_offset[i]),
                                             s.rows_padded, (int)s.cols, stream));
+            if (m->t_offset[i]) {
+                char* t = static_cast<char*>(dst) + m->t_offset[i];
+                const int64_t ld = t_ld(m, i);
+                GPT2_HIP(hipMemsetAsync(t, 0, (size_t)round_up(s.cols, kRowPad) * ld * 2, stream));
+                GPT2_HIP(gpt2k::transpose(d, true, s.cols, (int)s.rows, (int)s.cols, t, true, ld, (int)ld, stream));
+            }
         } else {
             GPT2_HIP(gpt2k::convert(src[i], sb, d, false, s.rows, s.rows, stream));
         }

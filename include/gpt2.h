@@ -93,7 +93,9 @@ gpt2_status gpt2_tensor_shape(const gpt2_model* m, int32_t i, int64_t* rows, int
  * vectors are fp32; every tensor starts on a 256-byte boundary. A bf16 model also holds, after the
  * source tensors, a k-blocked copy of wte and of the four projection matrices of every layer
  * ([cols/32][rows padded][32]: 32-column blocks of all rows one after another), which the tiled
- * projections of the forward read so that every slab of a K step is contiguous. */
+ * projections of the forward read so that every slab of a K step is contiguous, and a transposed
+ * copy of the same five matrices ([cols padded to 256][rows]; wte^T [d padded][n_vocab rounded up
+ * to 64], zero padding) that gpt2_backward reads for the input gradients. */
 size_t gpt2_weight_bytes(const gpt2_model* m);
 
 /* Bytes of device workspace one forward of shape [B, T] needs (0 for invalid B, T). */

@@ -108,6 +108,10 @@ def test_weight_and_workspace_bytes(g):
     want += 2 * al(d * 4)
     # bf16: k-blocked copies of wte and the four projection matrices of every layer
     want += al(pad(V) * d * 2) + 12 * (al(3 * d * d * 2) + al(d * d * 2) + al(f * d * 2) + al(d * f * 2))
+    # bf16: transposed copies of the same matrices for the backward ([in padded to 256][out]; wte^T
+    # [d padded][V rounded up to 64])
+    want += al(pad(d) * (-(-V // 64) * 64) * 2)
+    want += 12 * (al(pad(d) * 3 * d * 2) + al(pad(d) * d * 2) + al(pad(d) * f * 2) + al(pad(f) * d * 2))
     assert wb == want
     assert L.gpt2_workspace_bytes(h, 4, 1024) > 4 * 1024 * d * 4
     assert L.gpt2_workspace_bytes(h, 4, 1025) == 0     # T > n_ctx
