@@ -518,8 +518,9 @@ constexpr TileCfg kCfgs[] = {
 [[maybe_unused]] constexpr int kNumCfgs = sizeof(kCfgs) / sizeof(kCfgs[0]);
 
 // One epilogue's launch, with the K loop fully unrolled for the step counts that occur: the
-// forward's k-blocked projections (K = 768 and 3072) and the plain fp32 products of the backward
-// (K = 768, 2304, 3072 and B*T = 4096 at the benchmark shape).
+// forward's k-blocked projections (K = 768 and 3072; for GPT-2 medium and XL the vocabulary
+// projection and the residual projections, K = d and 4d for d = 1024 and 1600) and the plain fp32
+// products of the backward (K = 768, 2304, 3072 and B*T = 4096 at the benchmark shape).
 template <int BM, int BN, int BK, int S, int WGM, int WGN, int EPI, bool KB>
 void launch_epi(dim3 grid, dim3 block, hipStream_t s, const uint16_t* A, const uint16_t* W, const float* bias,
                 void* C, int M, int N, int K, int ldc, int a_rows, int w_rows, int tiles_m, int group_m, int c_kb,
@@ -528,12 +529,25 @@ void launch_epi(dim3 grid, dim3 block, hipStream_t s, const uint16_t* A, const u
     gemm_bf16_kernel<BM, BN, BK, S, WGM, WGN, EPI, KB, NK><<<grid, block, 0, s>>>(A, W, bias, C, M, N, K, ldc, a_rows, \
                                                                                   w_rows, tiles_m, group_m, c_kb, ho)
     const int nk = K / BK;
+    constexpr bool HEAD = EPI == EPI_LOGITS || EPI == EPI_LSE;
     if constexpr (KB || EPI == EPI_LOGITS) {
         if constexpr (BK == 32) {
             if (nk == 24) return (void)GPT2_LAUNCH_NK(24);
+            // the vocabulary projection of GPT-2 medium and XL (K = d = 1024, 1600)
+            if constexpr (HEAD) {
+                if (nk == 32) return (void)GPT2_LAUNCH_NK(32);
+                if (nk == 50) return (void)GPT2_LAUNCH_NK(50);
+            }
         } else {
             if (nk == 12) return (void)GPT2_LAUNCH_NK(12);
             if (nk == 48) return (void)GPT2_LAUNCH_NK(48);
+            // the residual projections of GPT-2 medium and XL (K = d and 4d)
+            if constexpr (KB && EPI == EPI_BIAS_RESIDUAL) {
+                if (nk == 16) return (void)GPT2_LAUNCH_NK(16);
+                if (nk == 64) return (void)GPT2_LAUNCH_NK(64);
+                if (nk == 25) return (void)GPT2_LAUNCH_NK(25);
+                if (nk == 100) return (void)GPT2_LAUNCH_NK(100);
+            }
             if constexpr (!KB) {
                 if (nk == 36) return (void)GPT2_LAUNCH_NK(36);
                 if (nk == 64) return (void)GPT2_LAUNCH_NK(64);
