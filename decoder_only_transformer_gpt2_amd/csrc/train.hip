@@ -110,13 +110,15 @@ __global__ void __launch_bounds__(256) colsum_partial_kernel(const float* __rest
     __syncthreads();
     if (grp == 0 && c < C) part[(long)b * C + c] = ((acc4[0][cl] + acc4[1][cl]) + acc4[2][cl]) + acc4[3][cl];
 }
-// out[c] = sum over b < nb of part[b][c]: four groups of partial rows per column (eight loads in
-// flight per thread), combined in group order.
+// out[c] = sum over b < nb of part[b][c]: a workgroup owns 16 columns and splits the partial rows
+// into 16 groups (eight loads in flight per thread), combined in group order, so short column
+// ranges (d = 768) still spread over 48 workgroups.
+constexpr int kRedCols = 16, kRedGroups = 16;
 __global__ void __launch_bounds__(256) colsum_reduce_kernel(const float* __restrict__ part, int nb, int C,
                                                             float* __restrict__ out) {
-    __shared__ float acc4[4][64];
-    const int cl = threadIdx.x & 63, grp = threadIdx.x >> 6, c = blockIdx.x * 64 + cl;
-    const int per = (nb + 3) / 4, b0 = grp * per, b1 = min(nb, b0 + per);
+    __shared__ float accg[kRedGroups][kRedCols];
+    const int cl = threadIdx.x % kRedCols, grp = threadIdx.x / kRedCols, c = blockIdx.x * kRedCols + cl;
+    const int per = (nb + kRedGroups - 1) / kRedGroups, b0 = grp * per, b1 = min(nb, b0 + per);
     float a[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
     if (c < C) {
         int b = b0;
@@ -126,9 +128,14 @@ __global__ void __launch_bounds__(256) colsum_reduce_kernel(const float* __restr
         }
         for (; b < b1; ++b) a[0] += part[(long)b * C + c];
     }
-    acc4[grp][cl] = ((a[0] + a[1]) + (a[2] + a[3])) + ((a[4] + a[5]) + (a[6] + a[7]));
+    accg[grp][cl] = ((a[0] + a[1]) + (a[2] + a[3])) + ((a[4] + a[5]) + (a[6] + a[7]));
     __syncthreads();
-    if (grp == 0 && c < C) out[c] = ((acc4[0][cl] + acc4[1][cl]) + acc4[2][cl]) + acc4[3][cl];
+    if (grp == 0 && c < C) {
+        float sum = 0.f;
+#pragma unroll
+        for (int g = 0; g < kRedGroups; ++g) sum += accg[g][cl];
+        out[c] = sum;
+    }
 }
 
 // ------------------------------------------------------------------------------ LayerNorm backward
@@ -634,7 +641,7 @@ int colsum_blocks(int R) { return (R + kColRows - 1) / kColRows; }
 hipError_t colsum(const float* src, long ld, int R, int C, float* part, float* out, hipStream_t s) {
     const int nb = colsum_blocks(R);
     colsum_partial_kernel<<<dim3((C + 63) / 64, nb), dim3(256), 0, s>>>(src, ld, R, C, part);
-    colsum_reduce_kernel<<<dim3((C + 63) / 64), dim3(256), 0, s>>>(part, nb, C, out);
+    colsum_reduce_kernel<<<dim3((C + kRedCols - 1) / kRedCols), dim3(256), 0, s>>>(part, nb, C, out);
     return hipGetLastError();
 }
 
@@ -650,8 +657,8 @@ hipError_t ln_backward(const float* x, const float* gamma, const float* dy, floa
         case 1600: ln_backward_kernel<25><<<grid, block, 0, s>>>(x, gamma, dy, dx, M, d, eps, pg, pb); break;
         default: ln_backward_kernel<0><<<grid, block, 0, s>>>(x, gamma, dy, dx, M, d, eps, pg, pb); break;
     }
-    colsum_reduce_kernel<<<dim3((d + 63) / 64), dim3(256), 0, s>>>(pg, np, d, dgamma);
-    colsum_reduce_kernel<<<dim3((d + 63) / 64), dim3(256), 0, s>>>(pb, np, d, dbeta);
+    colsum_reduce_kernel<<<dim3((d + kRedCols - 1) / kRedCols), dim3(256), 0, s>>>(pg, np, d, dgamma);
+    colsum_reduce_kernel<<<dim3((d + kRedCols - 1) / kRedCols), dim3(256), 0, s>>>(pb, np, d, dbeta);
     return hipGetLastError();
 }
 
