@@ -244,6 +244,23 @@ __global__ __launch_bounds__(256) void convert_kernel(const void* __restrict__ s
     }
 }
 
+// fp32 -> bf16, eight values per thread (two 16-byte reads, one 16-byte write), zero from n_src8 on;
+// the same rounding as convert_kernel.
+__global__ __launch_bounds__(256) void convert_f32_bf16_x8_kernel(const float4* __restrict__ src,
+                                                                 u32x4_t* __restrict__ dst, long n_src8, long n_dst8) {
+    for (long i = (long)blockIdx.x * blockDim.x + threadIdx.x; i < n_dst8; i += (long)gridDim.x * blockDim.x) {
+        u32x4_t o = {0u, 0u, 0u, 0u};
+        if (i < n_src8) {
+            const float4 a = src[2 * i], b = src[2 * i + 1];
+            o[0] = pack_bf16x2(a.x, a.y);
+            o[1] = pack_bf16x2(a.z, a.w);
+            o[2] = pack_bf16x2(b.x, b.y);
+            o[3] = pack_bf16x2(b.z, b.w);
+        }
+        dst[i] = o;
+    }
+}
+
 // LayerNorm with a k-blocked bf16 output: WAVES*RPW rows per workgroup (RPW per wavefront, all
 // their loads in flight together), normalised into LDS (rows padded by 16 bytes against bank
 // conflicts), then written block by block: the rows' 32-column slab of a block is one contiguous
@@ -402,6 +419,14 @@ hipError_t kblock_bf16(const uint16_t* src, uint16_t* dst, long rows, int K, hip
 
 hipError_t convert(const void* src, bool src_bf16, void* dst, bool dst_bf16, long n_src, long n_dst, hipStream_t s) {
     if (n_dst <= 0) return hipSuccess;
+    if (!src_bf16 && dst_bf16 && n_src % 8 == 0 && n_dst % 8 == 0 && reinterpret_cast<uintptr_t>(src) % 16 == 0 &&
+        reinterpret_cast<uintptr_t>(dst) % 16 == 0) {
+        long blocks = (n_dst / 8 + 255) / 256;
+        if (blocks > 65536) blocks = 65536;
+        convert_f32_bf16_x8_kernel<<<dim3((unsigned)blocks), dim3(256), 0, s>>>(
+            static_cast<const float4*>(src), static_cast<u32x4_t*>(dst), n_src / 8, n_dst / 8);
+        return hipGetLastError();
+    }
     long blocks = (n_dst + 255) / 256;
     if (blocks > 65536) blocks = 65536;
     convert_kernel<<<dim3((unsigned)blocks), dim3(256), 0, s>>>(src, src_bf16, dst, dst_bf16, n_src, n_dst);

@@ -256,6 +256,36 @@ __global__ void gelu_backward_kernel(const float* __restrict__ u, float* __restr
     if (i >= n) return;
     g[i] *= erf_form ? gelu_erf_grad(u[i]) : gelu_tanh_grad(u[i]);
 }
+// The same four values per thread (16-byte accesses), n4 = n / 4.
+__global__ void gelu_backward_x4_kernel(const float4* __restrict__ u, float4* __restrict__ g, long n4, int erf_form) {
+    const long i = (long)blockIdx.x * 256 + threadIdx.x;
+    if (i >= n4) return;
+    const float4 x = u[i];
+    float4 y = g[i];
+    if (erf_form) {
+        y.x *= gelu_erf_grad(x.x); y.y *= gelu_erf_grad(x.y); y.z *= gelu_erf_grad(x.z); y.w *= gelu_erf_grad(x.w);
+    } else {
+        y.x *= gelu_tanh_grad(x.x); y.y *= gelu_tanh_grad(x.y); y.z *= gelu_tanh_grad(x.z); y.w *= gelu_tanh_grad(x.w);
+    }
+    g[i] = y;
+}
+// gelu_forward_kernel with four values per thread (16-byte reads), n4 = n / 4.
+template <bool BF>
+__global__ void gelu_forward_x4_kernel(const float4* __restrict__ u, void* __restrict__ h, long n4, int erf_form) {
+    const long i = (long)blockIdx.x * 256 + threadIdx.x;
+    if (i >= n4) return;
+    const float4 x = u[i];
+    float4 y;
+    if (erf_form) {
+        y.x = gelu_erf_f32(x.x); y.y = gelu_erf_f32(x.y); y.z = gelu_erf_f32(x.z); y.w = gelu_erf_f32(x.w);
+    } else {
+        y.x = gelu_tanh_fast(x.x); y.y = gelu_tanh_fast(x.y); y.z = gelu_tanh_fast(x.z); y.w = gelu_tanh_fast(x.w);
+    }
+    if constexpr (BF)
+        static_cast<uint2*>(h)[i] = make_uint2(pack_bf16x2(y.x, y.y), pack_bf16x2(y.z, y.w));
+    else
+        static_cast<float4*>(h)[i] = y;
+}
 
 // ------------------------------------------------------------------------------ cross-entropy
 // cnt[0] = number of rows with tgt >= 0.
@@ -663,6 +693,14 @@ hipError_t ln_backward(const float* x, const float* gamma, const float* dy, floa
 }
 
 hipError_t gelu_forward(const float* u, void* h, long n, bool bf16, int erf_form, hipStream_t s) {
+    if (n % 4 == 0 && reinterpret_cast<uintptr_t>(u) % 16 == 0 && reinterpret_cast<uintptr_t>(h) % 16 == 0) {
+        const dim3 grid4((unsigned)((n / 4 + 255) / 256)), block4(256);
+        if (bf16)
+            gelu_forward_x4_kernel<true><<<grid4, block4, 0, s>>>(reinterpret_cast<const float4*>(u), h, n / 4, erf_form);
+        else
+            gelu_forward_x4_kernel<false><<<grid4, block4, 0, s>>>(reinterpret_cast<const float4*>(u), h, n / 4, erf_form);
+        return hipGetLastError();
+    }
     const dim3 grid((unsigned)((n + 255) / 256)), block(256);
     if (bf16)
         gelu_forward_kernel<true><<<grid, block, 0, s>>>(u, h, n, erf_form);
@@ -672,6 +710,11 @@ hipError_t gelu_forward(const float* u, void* h, long n, bool bf16, int erf_form
 }
 
 hipError_t gelu_backward(const float* u, float* g, long n, int erf_form, hipStream_t s) {
+    if (n % 4 == 0 && reinterpret_cast<uintptr_t>(u) % 16 == 0 && reinterpret_cast<uintptr_t>(g) % 16 == 0) {
+        gelu_backward_x4_kernel<<<dim3((unsigned)((n / 4 + 255) / 256)), dim3(256), 0, s>>>(
+            reinterpret_cast<const float4*>(u), reinterpret_cast<float4*>(g), n / 4, erf_form);
+        return hipGetLastError();
+    }
     gelu_backward_kernel<<<dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s>>>(u, g, n, erf_form);
     return hipGetLastError();
 }
