@@ -42,13 +42,14 @@ __global__ void __launch_bounds__(256) transpose_kernel(const void* __restrict__
     }
 }
 
-// bf16 -> bf16 with 16-byte accesses on both sides (row strides and pointers 16-byte aligned): a
-// thread moves two 8-column pieces of source rows into the tile and two 8-row pieces of
-// destination rows out of it; element by element only where a piece crosses R, C or Rp. The
+// bf16 or fp32 -> bf16 with 16-byte accesses on both sides (row strides and pointers 16-byte
+// aligned): a thread moves two 8-column pieces of source rows into the tile and two 8-row pieces
+// of destination rows out of it; element by element only where a piece crosses R, C or Rp. The
 // 65-float tile rows keep both the row writes and the column reads of a wavefront on distinct
-// banks. The values are the same bits as transpose_kernel's.
-__global__ void __launch_bounds__(256) transpose_bf16_vec_kernel(const uint16_t* __restrict__ src, long lds, int R, int C,
-                                                                 uint16_t* __restrict__ dst, long ldd, int Rp) {
+// banks. The values are the same bits as transpose_kernel's (fp32 sources round to nearest even).
+template <bool SRC_BF>
+__global__ void __launch_bounds__(256) transpose_vec_kernel(const void* __restrict__ srcv, long lds, int R, int C,
+                                                            uint16_t* __restrict__ dst, long ldd, int Rp) {
     __shared__ float tile[64][65];
     const int c0 = blockIdx.x * 64, r0 = blockIdx.y * 64, t = threadIdx.x;
 #pragma unroll
@@ -56,16 +57,24 @@ __global__ void __launch_bounds__(256) transpose_bf16_vec_kernel(const uint16_t*
         const int e = t + i * 256, rr = e >> 3, ck = (e & 7) * 8, r = r0 + rr, c = c0 + ck;
         float v[8];
         if (r < R && c + 8 <= C) {
-            const u32x4_t u = *reinterpret_cast<const u32x4_t*>(src + (long)r * lds + c);
+            if constexpr (SRC_BF) {
+                const u32x4_t u = *reinterpret_cast<const u32x4_t*>(static_cast<const uint16_t*>(srcv) + (long)r * lds + c);
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                v[2 * j] = __uint_as_float(u[j] << 16);
-                v[2 * j + 1] = __uint_as_float(u[j] & 0xffff0000u);
+                for (int j = 0; j < 4; ++j) {
+                    v[2 * j] = __uint_as_float(u[j] << 16);
+                    v[2 * j + 1] = __uint_as_float(u[j] & 0xffff0000u);
+                }
+            } else {
+                const float4* p = reinterpret_cast<const float4*>(static_cast<const float*>(srcv) + (long)r * lds + c);
+                const float4 a = p[0], b = p[1];
+                v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w; v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
             }
         } else {
 #pragma unroll
             for (int j = 0; j < 8; ++j)
-                v[j] = (r < R && c + j < C) ? __uint_as_float((uint32_t)src[(long)r * lds + c + j] << 16) : 0.f;
+                v[j] = (r < R && c + j < C) ? Act<SRC_BF>::load(static_cast<const typename Act<SRC_BF>::T*>(srcv),
+                                                                (long)r * lds + c + j)
+                                            : 0.f;
         }
 #pragma unroll
         for (int j = 0; j < 8; ++j) tile[rr][ck + j] = v[j];
@@ -79,11 +88,10 @@ __global__ void __launch_bounds__(256) transpose_bf16_vec_kernel(const uint16_t*
         if (r + 8 <= Rp) {
             u32x4_t u;
 #pragma unroll
-            for (int j = 0; j < 4; ++j)
-                u[j] = (__float_as_uint(tile[rk + 2 * j][cc]) >> 16) | (__float_as_uint(tile[rk + 2 * j + 1][cc]) & 0xffff0000u);
+            for (int j = 0; j < 4; ++j) u[j] = pack_bf16x2(tile[rk + 2 * j][cc], tile[rk + 2 * j + 1][cc]);
             *reinterpret_cast<u32x4_t*>(dp) = u;
         } else {
-            for (int j = 0; j < 8 && r + j < Rp; ++j) dp[j] = (uint16_t)(__float_as_uint(tile[rk + j][cc]) >> 16);
+            for (int j = 0; j < 8 && r + j < Rp; ++j) dp[j] = f32_to_bf16_bits(tile[rk + j][cc]);
         }
     }
 }
@@ -653,8 +661,9 @@ hipError_t transpose(const void* src, bool src_bf16, long lds, int R, int C, voi
     const bool vec = lds % 8 == 0 && ldd % 8 == 0 && reinterpret_cast<uintptr_t>(src) % 16 == 0 &&
                      reinterpret_cast<uintptr_t>(dst) % 16 == 0;
     if (src_bf16 && dst_bf16 && vec)
-        transpose_bf16_vec_kernel<<<grid, block, 0, s>>>(static_cast<const uint16_t*>(src), lds, R, C,
-                                                         static_cast<uint16_t*>(dst), ldd, Rp);
+        transpose_vec_kernel<true><<<grid, block, 0, s>>>(src, lds, R, C, static_cast<uint16_t*>(dst), ldd, Rp);
+    else if (dst_bf16 && vec)
+        transpose_vec_kernel<false><<<grid, block, 0, s>>>(src, lds, R, C, static_cast<uint16_t*>(dst), ldd, Rp);
     else if (src_bf16 && dst_bf16)
         transpose_kernel<true, true><<<grid, block, 0, s>>>(src, lds, R, C, dst, ldd, Rp);
     else if (src_bf16)
