@@ -172,6 +172,19 @@ __global__ void __launch_bounds__(64 * kLnWaves) ln_backward_kernel(const float*
     } else {
         for (int c = lane; c < d; c += 64) og[c] = ob[c] = 0.f;
     }
+    // CPL > 0: the next row's x, dy and dx are loaded while this row is processed
+    [[maybe_unused]] float xv[CPL > 0 ? CPL : 1], gv[CPL > 0 ? CPL : 1], dv[CPL > 0 ? CPL : 1];
+    auto load_row = [&](int m, float* xa, float* ga, float* da) {
+#pragma unroll
+        for (int j = 0; j < (CPL > 0 ? CPL : 1); ++j) {
+            xa[j] = x[(long)m * d + lane + 64 * j];
+            ga[j] = dy[(long)m * d + lane + 64 * j];
+            da[j] = dx[(long)m * d + lane + 64 * j];
+        }
+    };
+    if constexpr (CPL > 0)
+        if (blk * kLnRows + w < M) load_row(blk * kLnRows + w, xv, gv, dv);
+#pragma unroll
     for (int rr = w; rr < kLnRows; rr += kLnWaves) {
         const int m = blk * kLnRows + rr;
         if (m >= M) break;
@@ -179,12 +192,9 @@ __global__ void __launch_bounds__(64 * kLnWaves) ln_backward_kernel(const float*
         const float* gr = dy + (long)m * d;
         float* dr = dx + (long)m * d;
         if constexpr (CPL > 0) {
-            float xv[CPL], gv[CPL];
-#pragma unroll
-            for (int j = 0; j < CPL; ++j) {
-                xv[j] = xr[lane + 64 * j];
-                gv[j] = gr[lane + 64 * j];
-            }
+            float xn[CPL], gn[CPL], dn[CPL];
+            const bool has_next = rr + kLnWaves < kLnRows && m + kLnWaves < M;
+            if (has_next) load_row(m + kLnWaves, xn, gn, dn);
             float s = 0.f;
 #pragma unroll
             for (int j = 0; j < CPL; ++j) s += xv[j];
@@ -206,9 +216,17 @@ __global__ void __launch_bounds__(64 * kLnWaves) ln_backward_kernel(const float*
             for (int j = 0; j < CPL; ++j) {
                 const int c = lane + 64 * j;
                 const float g = gv[j] * gamma[c];
-                dr[c] += rstd * (g - mg - xv[j] * mgx);
+                dr[c] = dv[j] + rstd * (g - mg - xv[j] * mgx);
                 ag[j] += gv[j] * xv[j];
                 ab[j] += gv[j];
+            }
+            if (has_next) {
+#pragma unroll
+                for (int j = 0; j < CPL; ++j) {
+                    xv[j] = xn[j];
+                    gv[j] = gn[j];
+                    dv[j] = dn[j];
+                }
             }
         } else {
             float s = 0.f;
