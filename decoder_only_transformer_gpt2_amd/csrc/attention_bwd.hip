@@ -64,6 +64,57 @@ __device__ __forceinline__ void stage_f32(const float* __restrict__ src, long ld
     }
 }
 
+// The same staging split in two, so that the next tile's global loads are in flight while the
+// current tile is computed: fetch_* loads this thread's two 16-byte chunks (rows >= n zero; fp32
+// rows kept as loaded), put_* rounds and writes them like stage_bf16 / stage_f32.
+struct Bf16Chunks {
+    u32x4_t u[2];
+};
+struct F32Chunks {
+    f32x4_t a[2], b[2];
+};
+__device__ __forceinline__ void fetch_bf16(const uint16_t* __restrict__ src, long ld, int n, Bf16Chunks& f) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const int c = threadIdx.x + 256 * i, r = c >> 3, ch = c & 7;
+        f.u[i] = u32x4_t{0u, 0u, 0u, 0u};
+        if (r < n) f.u[i] = *reinterpret_cast<const u32x4_t*>(src + (long)r * ld + ch * 8);
+    }
+}
+__device__ __forceinline__ void fetch_f32(const float* __restrict__ src, long ld, int n, F32Chunks& f) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const int c = threadIdx.x + 256 * i, r = c >> 3, ch = c & 7;
+        f.a[i] = f.b[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        if (r < n) {
+            f.a[i] = *reinterpret_cast<const f32x4_t*>(src + (long)r * ld + ch * 8);
+            f.b[i] = *reinterpret_cast<const f32x4_t*>(src + (long)r * ld + ch * 8 + 4);
+        }
+    }
+}
+__device__ __forceinline__ void put_chunk(const u32x4_t& u, int c, uint16_t* tile, uint16_t* tr) {
+    const int r = c >> 3, ch = c & 7;
+    *reinterpret_cast<u32x4_t*>(&tile[swz(r, ch)]) = u;
+    if (tr) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            tr[(ch * 8 + 2 * j) * TSB + r] = (uint16_t)(u[j] & 0xffffu);
+            tr[(ch * 8 + 2 * j + 1) * TSB + r] = (uint16_t)(u[j] >> 16);
+        }
+    }
+}
+__device__ __forceinline__ void put_bf16(const Bf16Chunks& f, uint16_t* tile, uint16_t* tr) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) put_chunk(f.u[i], threadIdx.x + 256 * i, tile, tr);
+}
+__device__ __forceinline__ void put_f32(const F32Chunks& f, uint16_t* tile, uint16_t* tr) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+        put_chunk(u32x4_t{pack_bf16x2(f.a[i][0], f.a[i][1]), pack_bf16x2(f.a[i][2], f.a[i][3]),
+                          pack_bf16x2(f.b[i][0], f.b[i][1]), pack_bf16x2(f.b[i][2], f.b[i][3])},
+                  threadIdx.x + 256 * i, tile, tr);
+}
+
 // A operand from a swizzled [row][d] tile: row, dims kk * 32 + 8 g .. + 7
 __device__ __forceinline__ bf16x8_t a_rows(const uint16_t* tile, int row, int kk, int g) {
     return *reinterpret_cast<const bf16x8_t*>(&tile[swz(row, kk * 4 + g)]);
@@ -175,11 +226,19 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_mfma(const uint16_t* __restri
     f32x4_t dq[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) dq[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    Bf16Chunks fk, fv;  // key tile kt + 1 in flight while tile kt is computed
+    fetch_bf16(base + d, 3 * d, min(BT, T), fk);
+    fetch_bf16(base + 2 * d, 3 * d, min(BT, T), fv);
     for (int kt = 0; kt < n_kt; ++kt) {
-        const int k0 = kt * BT, nk = min(BT, T - k0);
+        const int k0 = kt * BT;
         __syncthreads();
-        stage_bf16(base + d + (long)k0 * 3 * d, 3 * d, nk, sK, sKt);
-        stage_bf16(base + 2 * d + (long)k0 * 3 * d, 3 * d, nk, sV, nullptr);
+        put_bf16(fk, sK, sKt);
+        put_bf16(fv, sV, nullptr);
+        if (kt + 1 < n_kt) {
+            const int k1 = k0 + BT, nk1 = min(BT, T - k1);
+            fetch_bf16(base + d + (long)k1 * 3 * d, 3 * d, nk1, fk);
+            fetch_bf16(base + 2 * d + (long)k1 * 3 * d, 3 * d, nk1, fv);
+        }
         __syncthreads();
         if (k0 > qb * BT + 16 * w + 15) continue;
         f32x4_t s[4], dp[4];
@@ -247,15 +306,30 @@ __global__ __launch_bounds__(256) void attn_bwd_dkv_mfma(const uint16_t* __restr
 #pragma unroll
     for (int i = 0; i < 4; ++i) dk[i] = dv[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
+    // query tile qt + 1 (q, dO, lse, D) in flight while tile qt is computed
+    Bf16Chunks fq;
+    F32Chunks fg;
+    float fl = 0.f, fd = 0.f;
+    auto fetch_q = [&](int q0) {
+        const int nq = min(BT, T - q0);
+        fetch_bf16(base + (long)q0 * 3 * d, 3 * d, nq, fq);
+        fetch_f32(gbase + (long)q0 * d, d, nq, fg);
+        if (t < BT) {
+            fl = t < nq ? lse[(long)bh * T + q0 + t] : 0.f;
+            fd = t < nq ? dvec[(long)bh * T + q0 + t] : 0.f;
+        }
+    };
+    fetch_q(kb * BT);
     for (int qt = kb; qt < nkb; ++qt) {
         const int q0 = qt * BT, nq = min(BT, T - q0);
         __syncthreads();
-        stage_bf16(base + (long)q0 * 3 * d, 3 * d, nq, sQ, sQt);
-        stage_f32(gbase + (long)q0 * d, d, nq, sG, sGt);
+        put_bf16(fq, sQ, sQt);
+        put_f32(fg, sG, sGt);
         if (t < BT) {
-            sL[t] = t < nq ? lse[(long)bh * T + q0 + t] : 0.f;
-            sD[t] = t < nq ? dvec[(long)bh * T + q0 + t] : 0.f;
+            sL[t] = fl;
+            sD[t] = fd;
         }
+        if (qt + 1 < nkb) fetch_q(q0 + BT);
         __syncthreads();
         if (q0 + BT - 1 < kb * BT + 16 * w) continue;  // wave-uniform: every query of the tile is before every key
         f32x4_t s[4], dp[4];
