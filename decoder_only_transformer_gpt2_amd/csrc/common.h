@@ -267,6 +267,11 @@ hipError_t transpose(const void* src, bool src_bf16, long lds, int R, int C, voi
                      hipStream_t s);
 // out[c] = sum over rows of src[r * ld + c] (deterministic order); part holds colsum_blocks(R) * C floats.
 int colsum_blocks(int R);
+// transpose (fp32 src -> bf16 dst, as transpose) and out[c] = sum over rows of src[r][c], in one pass
+// over src when strides and pointers allow 16-byte accesses; part holds ceil(Rp / 64) * C floats
+// (and colsum_blocks(R) * C for the fallback).
+hipError_t transpose_colsum(const float* src, long lds, int R, int C, uint16_t* dst, long ldd, int Rp, float* part,
+                            float* out, hipStream_t s);
 hipError_t colsum(const float* src, long ld, int R, int C, float* part, float* out, hipStream_t s);
 // LayerNorm backward on rows of x with output gradient dy (fp32 [M, d]): dx += the input gradient,
 // dgamma / dbeta = column sums (pg, pb hold ln_backward_blocks(M) * d floats each: partial rows).

@@ -471,7 +471,7 @@ TrainLayout train_layout(const gpt2_model* m, int B, int T) {
     L.wteT = take(wt_packed ? 0 : round_up(d, kRowPad) * L.Vp * as);
     L.dlog = take(L.Mp * L.Vp * as);
     L.dlogT = take(L.Vr * L.Mk * as);
-    L.part = take((size_t)gpt2k::colsum_blocks((int)L.M) * L.wide * 4);
+    L.part = take((size_t)std::max<int64_t>(gpt2k::colsum_blocks((int)L.M), (L.Mk + 63) / 64) * L.wide * 4);
     L.lnpg = take((size_t)gpt2k::ln_backward_blocks((int)L.M) * d * 4);
     L.lnpb = take((size_t)gpt2k::ln_backward_blocks((int)L.M) * d * 4);
     L.lse = take((size_t)B * c.n_head * T * 4);
@@ -586,8 +586,14 @@ gpt2_status enqueue_backward(const gpt2_model* m, const int32_t* tokens, int B, 
     // the weight gradient and the input gradient of y = x W^T + b for output gradient dy (fp32 [M, n_out])
     auto linear_back = [&](const float* dy, int n_out, const void* x_act, int n_in, int widx, float* dx_out) -> hipError_t {
         hipError_t e;
-        if ((e = gpt2k::colsum(dy, n_out, M, n_out, part, G(widx + 1), s)) != hipSuccess) return e;
-        if ((e = tr(dy, false, n_out, M, n_out, dT, Mk, Mk)) != hipSuccess) return e;
+        if (bf) {  // bias gradient (column sums of dy) from the same pass as the transpose of dy
+            if ((e = gpt2k::transpose_colsum(dy, n_out, M, n_out, reinterpret_cast<uint16_t*>(dT), Mk, Mk, part,
+                                             G(widx + 1), s)) != hipSuccess)
+                return e;
+        } else {
+            if ((e = gpt2k::colsum(dy, n_out, M, n_out, part, G(widx + 1), s)) != hipSuccess) return e;
+            if ((e = tr(dy, false, n_out, M, n_out, dT, Mk, Mk)) != hipSuccess) return e;
+        }
         if ((e = tr(x_act, true, n_in, M, n_in, xT, Mk, Mk)) != hipSuccess) return e;
         if ((e = gemm_nt(dT, pad(n_out), xT, pad(n_in), G(widx), n_out, n_in, Mk, n_in)) != hipSuccess) return e;
         if ((e = to_act(dy, n_out, dact)) != hipSuccess) return e;

@@ -47,10 +47,14 @@ __global__ void __launch_bounds__(256) transpose_kernel(const void* __restrict__
 // of destination rows out of it; element by element only where a piece crosses R, C or Rp. The
 // 65-float tile rows keep both the row writes and the column reads of a wavefront on distinct
 // banks. The values are the same bits as transpose_kernel's (fp32 sources round to nearest even).
+// With colpart set (fp32 sources), the workgroup also writes the sums of its tile's columns over its
+// 64 rows to colpart[blockIdx.y][c] (four 16-row quarters added in order).
 template <bool SRC_BF>
 __global__ void __launch_bounds__(256) transpose_vec_kernel(const void* __restrict__ srcv, long lds, int R, int C,
-                                                            uint16_t* __restrict__ dst, long ldd, int Rp) {
+                                                            uint16_t* __restrict__ dst, long ldd, int Rp,
+                                                            float* __restrict__ colpart) {
     __shared__ float tile[64][65];
+    __shared__ float qsum[4][64];
     const int c0 = blockIdx.x * 64, r0 = blockIdx.y * 64, t = threadIdx.x;
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
@@ -80,6 +84,16 @@ __global__ void __launch_bounds__(256) transpose_vec_kernel(const void* __restri
         for (int j = 0; j < 8; ++j) tile[rr][ck + j] = v[j];
     }
     __syncthreads();
+    if (colpart) {
+        const int cc = t & 63, q = t >> 6;
+        float a = 0.f;
+#pragma unroll
+        for (int j = 0; j < 16; ++j) a += tile[q * 16 + j][cc];
+        qsum[q][cc] = a;
+        __syncthreads();
+        if (q == 0 && c0 + cc < C)
+            colpart[(long)blockIdx.y * C + c0 + cc] = ((qsum[0][cc] + qsum[1][cc]) + qsum[2][cc]) + qsum[3][cc];
+    }
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
         const int e = t + i * 256, cc = e >> 3, rk = (e & 7) * 8, c = c0 + cc, r = r0 + rk;
@@ -679,9 +693,9 @@ hipError_t transpose(const void* src, bool src_bf16, long lds, int R, int C, voi
     const bool vec = lds % 8 == 0 && ldd % 8 == 0 && reinterpret_cast<uintptr_t>(src) % 16 == 0 &&
                      reinterpret_cast<uintptr_t>(dst) % 16 == 0;
     if (src_bf16 && dst_bf16 && vec)
-        transpose_vec_kernel<true><<<grid, block, 0, s>>>(src, lds, R, C, static_cast<uint16_t*>(dst), ldd, Rp);
+        transpose_vec_kernel<true><<<grid, block, 0, s>>>(src, lds, R, C, static_cast<uint16_t*>(dst), ldd, Rp, nullptr);
     else if (dst_bf16 && vec)
-        transpose_vec_kernel<false><<<grid, block, 0, s>>>(src, lds, R, C, static_cast<uint16_t*>(dst), ldd, Rp);
+        transpose_vec_kernel<false><<<grid, block, 0, s>>>(src, lds, R, C, static_cast<uint16_t*>(dst), ldd, Rp, nullptr);
     else if (src_bf16 && dst_bf16)
         transpose_kernel<true, true><<<grid, block, 0, s>>>(src, lds, R, C, dst, ldd, Rp);
     else if (src_bf16)
@@ -694,6 +708,20 @@ hipError_t transpose(const void* src, bool src_bf16, long lds, int R, int C, voi
 }
 
 int colsum_blocks(int R) { return (R + kColRows - 1) / kColRows; }
+
+hipError_t transpose_colsum(const float* src, long lds, int R, int C, uint16_t* dst, long ldd, int Rp, float* part,
+                            float* out, hipStream_t s) {
+    const bool vec = lds % 8 == 0 && ldd % 8 == 0 && reinterpret_cast<uintptr_t>(src) % 16 == 0 &&
+                     reinterpret_cast<uintptr_t>(dst) % 16 == 0 && Rp >= R;
+    if (!vec) {
+        const hipError_t e = colsum(src, lds, R, C, part, out, s);
+        return e != hipSuccess ? e : transpose(src, false, lds, R, C, dst, true, ldd, Rp, s);
+    }
+    const int nb = (Rp + 63) / 64;
+    transpose_vec_kernel<false><<<dim3((C + 63) / 64, nb), dim3(256), 0, s>>>(src, lds, R, C, dst, ldd, Rp, part);
+    colsum_reduce_kernel<<<dim3((C + kRedCols - 1) / kRedCols), dim3(256), 0, s>>>(part, nb, C, out);
+    return hipGetLastError();
+}
 
 hipError_t colsum(const float* src, long ld, int R, int C, float* part, float* out, hipStream_t s) {
     const int nb = colsum_blocks(R);
