@@ -294,21 +294,22 @@ void gemm_bf16_kernel(
         const int rs = row0 + i * 16;  // first row of the strip (wave-uniform)
         const int rows = M - rs, cols = N - col0;
         if (EPI == EPI_LSE) {
-            // Per row over the staged strip, four lanes per row with WN/4 consecutive columns each:
+            // Per row over the staged strip, four lanes per row, lane q taking columns 4c + q (so
+            // that the 64 lanes' reads fall on distinct banks: SP is 4 more than a multiple of 16):
             // the maximum of y = logit * log2(e) and the sum of 2^(y - max), then both combined over
             // the four lanes. Columns past N are left out. The lane whose columns hold the row's
             // target keeps that logit. Nothing is stored to the logits.
             constexpr int CQ = WN / 4;
             constexpr float LOG2E = 1.4426950408889634f;
             const int ar = lane >> 2, aq = lane & 3;
-            const float* sp = scr + ar * SP + aq * CQ;
-            const int lim = CHK ? cols - aq * CQ : CQ;
+            const float* sp = scr + ar * SP + aq;
+            const int lim = CHK ? cols - aq : WN;  // column 4c + aq is valid when 4c < lim
             float y[CQ];
             float mx = -INFINITY;
 #pragma unroll
             for (int c = 0; c < CQ; ++c) {
-                y[c] = sp[c] * LOG2E;
-                if (CHK) y[c] = c < lim ? y[c] : -INFINITY;
+                y[c] = sp[4 * c] * LOG2E;
+                if (CHK) y[c] = 4 * c < lim ? y[c] : -INFINITY;
                 mx = fmaxf(mx, y[c]);
             }
             const float ms = mx == -INFINITY ? 0.f : mx;
@@ -318,8 +319,8 @@ void gemm_bf16_kernel(
             lse_quad_merge(mx, sum);
             const int row = rs + ar;
             if (!CHK || row < M) {
-                const int tc = ho.tgt[row], c0 = col0 + aq * CQ;
-                if (tc >= c0 && tc < c0 + CQ && tc < N) ho.tgt_logit[row] = sp[tc - c0];
+                const int tc = ho.tgt[row], rel = tc - col0;
+                if (rel >= 0 && rel < WN && (rel & 3) == aq && tc < N) ho.tgt_logit[row] = sp[rel - aq];
             }
             if (aq == 0) {
                 const int rl = wn * BM + wm * WM + i * 16 + ar;
@@ -328,20 +329,21 @@ void gemm_bf16_kernel(
             }
         } else if (EPI == EPI_LOGITS) {
             if (ho.pv) {
-                // Row argmax over the staged strip: four lanes per row, each scanning WN/4
-                // consecutive columns (a strict > keeps the first of equal values), then the row
-                // maximum (as an order key) and the smallest column holding it over the four
-                // lanes. Columns past N count as -inf; a lane with no column offers none.
+                // Row argmax over the staged strip: four lanes per row, lane q scanning columns
+                // 4c + q in increasing order (a strict > keeps the first of equal values; the
+                // interleave keeps the 64 lanes' reads on distinct banks), then the row maximum (as
+                // an order key) and the smallest column holding it over the four lanes. Columns
+                // past N count as -inf; a lane with no column offers none.
                 constexpr int CQ = WN / 4;
                 const int ar = lane >> 2, aq = lane & 3;
-                const float* sp = scr + ar * SP + aq * CQ;
-                const int lim = CHK ? cols - aq * CQ : CQ;  // valid columns of this lane's quarter
+                const float* sp = scr + ar * SP + aq;
+                const int lim = CHK ? cols - aq : WN;  // column 4c + aq is valid when 4c < lim
                 float bv = sp[0];
                 int bc = 0;
 #pragma unroll
                 for (int c = 1; c < CQ; ++c) {
-                    float x = sp[c];
-                    if (CHK) x = c < lim ? x : -INFINITY;
+                    float x = sp[4 * c];
+                    if (CHK) x = 4 * c < lim ? x : -INFINITY;
                     const bool take = x > bv;
                     bv = take ? x : bv;
                     bc = take ? c : bc;
@@ -349,7 +351,7 @@ void gemm_bf16_kernel(
                 const uint32_t key = f32_order_key(bv);
                 const uint32_t kmax = quad_max_u32(key);
                 const bool has_col = !CHK || lim > 0;
-                const uint32_t col = (key == kmax && has_col) ? (uint32_t)(col0 + aq * CQ + bc) : 0xffffffffu;
+                const uint32_t col = (key == kmax && has_col) ? (uint32_t)(col0 + 4 * bc + aq) : 0xffffffffu;
                 const uint32_t cmin = quad_min_u32(col);
                 if (aq == 0) {
                     const int rl = wn * BM + wm * WM + i * 16 + ar;
