@@ -136,44 +136,65 @@ def merge_heads(o: np.ndarray) -> np.ndarray:
     return o.transpose(0, 2, 1, 3).reshape(B, T, H * dh)
 
 
-def attention_block(x: np.ndarray, p: dict, l: int, n_head: int) -> np.ndarray:
-    """Self-attention sub-layer of block l on its LayerNorm'd input: c_attn, heads, c_proj."""
+def exact(a: np.ndarray) -> np.ndarray:
+    """Activations kept exact (float64): the default storage of every intermediate."""
+    return a
+
+
+def round_bf16(a: np.ndarray) -> np.ndarray:
+    """Each value rounded to the nearest bfloat16 (8 significant bits, ties to even), as float64.
+
+    bfloat16 keeps fp32's exponent range and 8 significant bits, so a value x = m * 2^e with
+    m in [0.5, 1) lies on the grid of spacing 2^(e - 8); np.round rounds halves to even. Used only
+    for forward_bf16_activations (values here are far from the subnormal and overflow ranges)."""
+    a = np.asarray(a, dtype=F64)
+    _, e = np.frexp(a)
+    step = np.ldexp(1.0, e - 8)
+    return np.round(a / step) * step
+
+
+def attention_block(x: np.ndarray, p: dict, l: int, n_head: int, act=exact) -> np.ndarray:
+    """Self-attention sub-layer of block l on its LayerNorm'd input: c_attn, heads, c_proj.
+    act stores the fused projection's output and the merged head outputs (identity by default)."""
     pre = f"h.{l}.attn."
-    qkv = linear(x, p[pre + "c_attn.w"], p[pre + "c_attn.b"])
+    qkv = act(linear(x, p[pre + "c_attn.w"], p[pre + "c_attn.b"]))
     q, k, v = split_heads(qkv, n_head)
-    o = merge_heads(causal_attention(q, k, v))
+    o = act(merge_heads(causal_attention(q, k, v)))
     return linear(o, p[pre + "c_proj.w"], p[pre + "c_proj.b"])
 
 
-def mlp_block(x: np.ndarray, p: dict, l: int, gelu=gelu_tanh) -> np.ndarray:
-    """MLP sub-layer: c_fc (d -> d_mlp), GELU, c_proj (d_mlp -> d) ([解析] §2.2; [复现] §2.4)."""
+def mlp_block(x: np.ndarray, p: dict, l: int, gelu=gelu_tanh, act=exact) -> np.ndarray:
+    """MLP sub-layer: c_fc (d -> d_mlp), GELU, c_proj (d_mlp -> d) ([解析] §2.2; [复现] §2.4).
+    act stores the GELU output (identity by default)."""
     pre = f"h.{l}.mlp."
-    return linear(gelu(linear(x, p[pre + "c_fc.w"], p[pre + "c_fc.b"])),
+    return linear(act(gelu(linear(x, p[pre + "c_fc.w"], p[pre + "c_fc.b"]))),
                   p[pre + "c_proj.w"], p[pre + "c_proj.b"])
 
 
-def block(x: np.ndarray, p: dict, l: int, n_head: int, eps: float = 1e-5, gelu=gelu_tanh) -> np.ndarray:
-    """Pre-LN block: x + attn(ln_1(x)), then + mlp(ln_2(x)) ([手写] §3.2; [复现] §2.3; [解析] §1.1)."""
+def block(x: np.ndarray, p: dict, l: int, n_head: int, eps: float = 1e-5, gelu=gelu_tanh, act=exact) -> np.ndarray:
+    """Pre-LN block: x + attn(ln_1(x)), then + mlp(ln_2(x)) ([手写] §3.2; [实战] §10 and [解析] §1.1
+    Block listings; [复现] §2.3). act stores the two LayerNorm outputs (identity by default); the
+    residual stream x itself is never passed through it."""
     pre = f"h.{l}."
-    x = x + attention_block(layer_norm(x, p[pre + "ln_1.w"], p[pre + "ln_1.b"], eps), p, l, n_head)
-    x = x + mlp_block(layer_norm(x, p[pre + "ln_2.w"], p[pre + "ln_2.b"], eps), p, l, gelu)
+    x = x + attention_block(act(layer_norm(x, p[pre + "ln_1.w"], p[pre + "ln_1.b"], eps)), p, l, n_head, act)
+    x = x + mlp_block(act(layer_norm(x, p[pre + "ln_2.w"], p[pre + "ln_2.b"], eps)), p, l, gelu, act)
     return x
 
 
 def residual(p: dict, tokens: np.ndarray, n_head: int, n_layers: int, eps: float = 1e-5,
-             gelu=gelu_tanh) -> np.ndarray:
+             gelu=gelu_tanh, act=exact) -> np.ndarray:
     """Residual stream [B, T, d] after the embedding and the first n_layers blocks."""
     x = embed(p["wte"], p["wpe"], tokens)
     for l in range(n_layers):
-        x = block(x, p, l, n_head, eps, gelu)
+        x = block(x, p, l, n_head, eps, gelu, act)
     return x
 
 
 def final_hidden(p: dict, tokens: np.ndarray, n_head: int, n_layer: int, eps: float = 1e-5,
-                 gelu=gelu_tanh) -> np.ndarray:
+                 gelu=gelu_tanh, act=exact) -> np.ndarray:
     """ln_f applied to the residual stream after all blocks ([手写] §4.1 forward, step 3)."""
-    x = residual(p, tokens, n_head, n_layer, eps, gelu)
-    return layer_norm(x, p["ln_f.w"], p["ln_f.b"], eps)
+    x = residual(p, tokens, n_head, n_layer, eps, gelu, act)
+    return act(layer_norm(x, p["ln_f.w"], p["ln_f.b"], eps))
 
 
 def lm_head(h: np.ndarray, wte: np.ndarray) -> np.ndarray:
@@ -182,9 +203,21 @@ def lm_head(h: np.ndarray, wte: np.ndarray) -> np.ndarray:
 
 
 def forward(p: dict, tokens: np.ndarray, n_head: int, n_layer: int, eps: float = 1e-5,
-            gelu=gelu_tanh) -> np.ndarray:
-    """Whole forward: tokens [B, T] -> logits [B, T, n_vocab] in float64."""
-    return lm_head(final_hidden(p, tokens, n_head, n_layer, eps, gelu), p["wte"])
+            gelu=gelu_tanh, act=exact) -> np.ndarray:
+    """Whole forward: tokens [B, T] -> logits [B, T, n_vocab] in float64 (every activation exact)."""
+    return lm_head(final_hidden(p, tokens, n_head, n_layer, eps, gelu, act), p["wte"])
+
+
+def forward_bf16_activations(p: dict, tokens: np.ndarray, n_head: int, n_layer: int, eps: float = 1e-5,
+                             gelu=gelu_tanh) -> np.ndarray:
+    """The forward of a model whose activations are stored in bf16 (the bf16 configuration:
+    bf16 weights and activations, fp32 accumulation): the same float64 arithmetic, with the
+    activations that configuration stores rounded to bf16 where they are produced -- the LayerNorm
+    outputs (ln_1, ln_2, ln_f), the fused q/k/v projection, the merged attention output and the
+    GELU output. The residual stream, every statistic and every sum stay exact, and the logits are
+    not rounded. Used where a floating-point result decides an integer (the top-1 token), so that
+    the decision is taken in the precision the configuration computes in."""
+    return forward(p, tokens, n_head, n_layer, eps, gelu, act=round_bf16)
 
 
 def argmax_first(logits: np.ndarray) -> np.ndarray:

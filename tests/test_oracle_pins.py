@@ -278,6 +278,213 @@ def test_mlp_all_ones_hand_value():
     assert np.all(np.abs(out) < 1e-300)
 
 
+# ------------------------------------------------------------- block composition (Pre-LN) pins
+def _hand_ln(x, g, b, eps=1e-5):
+    """LayerNorm of one short row written out with math (the [1,2,3,4] closed form generalised)."""
+    n = len(x)
+    mu = sum(x) / n
+    var = sum((v - mu) ** 2 for v in x) / n
+    return [gi * (v - mu) / math.sqrt(var + eps) + bi for v, gi, bi in zip(x, g, b)]
+
+
+def _hand_gelu(v):
+    return 0.5 * v * (1.0 + math.tanh(math.sqrt(2.0 / math.pi) * (v + 0.044715 * v ** 3)))
+
+
+def _tiny_block_model(d=4, f=16, V=3):
+    """One block, d=4, one head of size 4, every tensor zero except what a case sets; token 0's
+    embedding is [1, 2, 3, 4] and position 0's is zero, so x0 = [1, 2, 3, 4]."""
+    s = synth.ModelShape(n_vocab=V, n_ctx=2, d_model=d, n_head=1, n_layer=1, d_mlp=f)
+    p = {name: np.zeros(shape) for name, shape, _ in synth.tensor_specs(s)}
+    p["wte"][0] = [1.0, 2.0, 3.0, 4.0]
+    p["wte"][1] = [0.5, -1.0, 0.25, 2.0]
+    p["wte"][2] = [-3.0, 0.0, 1.0, -0.5]
+    for k in ("h.0.ln_1.w", "h.0.ln_2.w", "ln_f.w"):
+        p[k] = np.ones(d)
+    return s, p
+
+
+def check_block_composition(res):
+    """res(p, tokens, n_head, n_layers) -> residual stream after n_layers blocks.
+
+    The Pre-LN block of [手写] §3.2 and the Block listings of [实战] §10 and [解析] §1.1:
+    x <- x + attn(ln_1(x)), then x <- x + mlp(ln_2(x)). Three one-block cases whose outputs are
+    worked by hand from x0 = [1, 2, 3, 4] (one position, so attention returns v itself):
+      A. every Linear weight zero, biases and LayerNorm gains non-trivial: the sub-layers return
+         their output biases, so x1 = x0 + b_o + b_p exactly (a Post-LN block would normalise it);
+      B. the v block of c_attn and attn.c_proj are identities: x1 = x0 + ln_1(x0) + b_v + b_o
+         (the attention sees the normalised input, the residual adds to the raw one);
+      C. c_fc's first four rows and mlp.c_proj's first four columns are identities:
+         x1 = y + gelu(ln_2(y) + b_fc[:4]) + b_p with y = x0 + b_o.
+    """
+    fails = []
+    tok = np.array([[0]])
+    x0 = [1.0, 2.0, 3.0, 4.0]
+    # A
+    s, p = _tiny_block_model()
+    p["h.0.ln_1.w"][:] = [2.0, 0.5, -1.0, 3.0]
+    p["h.0.ln_1.b"][:] = [0.3, -0.2, 0.1, 0.0]
+    p["h.0.ln_2.w"][:] = [1.5, 1.5, 0.5, 0.5]
+    p["h.0.ln_2.b"][:] = [0.0, 0.4, 0.0, -0.4]
+    p["h.0.attn.c_attn.b"][:] = np.linspace(-1, 1, 12)
+    p["h.0.attn.c_proj.b"][:] = [0.25, -0.5, 0.75, 1.0]
+    p["h.0.mlp.c_fc.b"][:] = np.linspace(-2, 2, 16)
+    p["h.0.mlp.c_proj.b"][:] = [1.0, 0.0, -1.0, 0.5]
+    want = [x0[i] + p["h.0.attn.c_proj.b"][i] + p["h.0.mlp.c_proj.b"][i] for i in range(4)]
+    got = np.asarray(res(p, tok, 1, 1))[0, 0]
+    if not np.allclose(got, want, rtol=0, atol=1e-12):
+        fails.append("A: zero weights")
+    # B
+    s, p = _tiny_block_model()
+    g1, b1 = [2.0, 1.0, 0.5, 1.0], [0.5, 0.0, -0.5, 0.25]
+    p["h.0.ln_1.w"][:] = g1
+    p["h.0.ln_1.b"][:] = b1
+    p["h.0.attn.c_attn.w"][8:12] = np.eye(4)
+    bv = [0.1, 0.2, 0.3, 0.4]
+    p["h.0.attn.c_attn.b"][8:12] = bv
+    p["h.0.attn.c_proj.w"][:] = np.eye(4)
+    bo = [-0.5, 0.5, 0.0, 1.0]
+    p["h.0.attn.c_proj.b"][:] = bo
+    ln1 = _hand_ln(x0, g1, b1)
+    want = [x0[i] + ln1[i] + bv[i] + bo[i] for i in range(4)]
+    got = np.asarray(res(p, tok, 1, 1))[0, 0]
+    if not np.allclose(got, want, rtol=0, atol=1e-12):
+        fails.append("B: attention on ln_1(x)")
+    # C
+    s, p = _tiny_block_model()
+    bo = [1.0, -1.0, 0.5, 2.0]  # not a constant shift, which LayerNorm would not see
+    p["h.0.attn.c_proj.b"][:] = bo
+    g2, b2 = [0.5, 2.0, 1.0, 1.5], [0.0, 0.1, -0.1, 0.2]
+    p["h.0.ln_2.w"][:] = g2
+    p["h.0.ln_2.b"][:] = b2
+    p["h.0.mlp.c_fc.w"][:4] = np.eye(4)
+    bfc = [0.5, -0.5, 0.25, 0.0]
+    p["h.0.mlp.c_fc.b"][:4] = bfc
+    p["h.0.mlp.c_proj.w"][:, :4] = np.eye(4)
+    bp = [0.0, 0.3, 0.0, -0.3]
+    p["h.0.mlp.c_proj.b"][:] = bp
+    y = [x0[i] + bo[i] for i in range(4)]
+    ln2 = _hand_ln(y, g2, b2)
+    want = [y[i] + _hand_gelu(ln2[i] + bfc[i]) + bp[i] for i in range(4)]
+    got = np.asarray(res(p, tok, 1, 1))[0, 0]
+    if not np.allclose(got, want, rtol=0, atol=1e-12):
+        fails.append("C: MLP on ln_2(x)")
+    return fails
+
+
+def check_head_composition(fwd):
+    """fwd(p, tokens, n_head, n_layer) -> logits. ln_f sits between the last block and the tied
+    head ([手写] §4.1 forward: blocks, ln_f, lm_head = wte): with a block that adds nothing
+    (all zero), logits[v] = ln_f(x0) . wte[v], worked by hand."""
+    s, p = _tiny_block_model()
+    gf, bf = [1.0, 2.0, 0.5, 1.0], [0.1, 0.0, -0.1, 0.3]
+    p["ln_f.w"][:] = gf
+    p["ln_f.b"][:] = bf
+    xf = _hand_ln([1.0, 2.0, 3.0, 4.0], gf, bf)
+    want = [sum(xf[i] * p["wte"][v][i] for i in range(4)) for v in range(3)]
+    got = np.asarray(fwd(p, np.array([[0]]), 1, 1))[0, 0]
+    return [] if np.allclose(got, want, rtol=0, atol=1e-12) else ["ln_f before the tied head"]
+
+
+def test_block_composition_pins():
+    assert check_block_composition(O.residual) == []
+
+
+def test_head_composition_pins():
+    assert check_head_composition(O.forward) == []
+
+
+def test_training_forward_composition_agrees():
+    """The backward's own forward coding (loss_and_grads) composes the blocks the same way: its
+    loss equals the shifted cross-entropy of forward()'s logits on case B of the block pins."""
+    s, p = _tiny_block_model()
+    p["h.0.attn.c_attn.w"][8:12] = np.eye(4)
+    p["h.0.attn.c_proj.w"][:] = np.eye(4)
+    p["h.0.ln_1.w"][:] = [2.0, 1.0, 0.5, 1.0]
+    tok = np.array([[0, 1, 2]])
+    p["wpe"] = np.zeros((3, 4))
+    loss, _ = O.loss_and_grads(p, tok, None, 1, 1)
+    assert abs(loss - O.shifted_cross_entropy(O.forward(p, tok, 1, 1), tok)) < 1e-12
+
+
+# --------------------------------------------------- bf16 activation storage (top-1 decisions)
+def check_round_bf16(rnd):
+    """rnd(float64 array) -> nearest bf16 values (8 significant bits, ties to even)."""
+    fails = []
+    u = 2.0 ** -8
+    hand = {1.0: 1.0, 1.0 + u: 1.0,                      # a tie: the even neighbour (1.0)
+            1.0 + 3 * u: 1.0 + 4 * u,                    # a tie: the even neighbour is the upper one
+            1.0 + u + 2.0 ** -20: 1.0 + 2 * u,           # just above the tie
+            -(1.0 + 3 * u): -(1.0 + 4 * u), 0.0: 0.0, 3.0: 3.0,
+            0.1: 0.10009765625, 300.7: 300.0, 2.0 ** -30 * 1.00390625: 2.0 ** -30}
+    for x, want in hand.items():
+        got = float(np.asarray(rnd(np.array([x])))[0])
+        if got != want:
+            fails.append(f"{x!r} -> {got!r}, want {want!r}")
+    # fp32 inputs against torch's float32 -> bfloat16 conversion (round to nearest even)
+    x = (rng(77).standard_normal(4096) * np.exp(rng(78).uniform(-20, 20, 4096))).astype(np.float32)
+    want = torch.from_numpy(x).to(torch.bfloat16).to(torch.float64).numpy()
+    if not np.array_equal(np.asarray(rnd(x.astype(np.float64))), want):
+        fails.append("torch bfloat16 conversion")
+    return fails
+
+
+def test_round_bf16_pins():
+    assert check_round_bf16(O.round_bf16) == []
+
+
+def _torch_bf16(v):
+    return torch.tensor(np.asarray(v, dtype=np.float32)).to(torch.bfloat16).to(torch.float64).numpy()
+
+
+def check_bf16_activation_residual(res):
+    """res(p, tokens, n_head, n_layers) -> residual stream of the bf16-activation forward.
+
+    A. zero weights, output biases not on the bf16 grid: the residual stream is not rounded, so
+       x1 = x0 + b_o + b_p exactly;
+    B. a mixing v block (each v is half the sum of two LayerNorm outputs), c_proj the identity:
+       x1 = x0 + R(W_v R(ln_1(x0))) + b_o, R the bf16 rounding (worked with torch's conversion;
+       the case is chosen so that leaving out the inner rounding changes the result)."""
+    fails = []
+    tok = np.array([[0]])
+    x0 = np.array([1.0, 2.0, 3.0, 4.0])
+    s, p = _tiny_block_model()
+    p["h.0.attn.c_proj.b"][:] = [1e-3, -2e-3, 3e-3, 0.0]
+    p["h.0.mlp.c_proj.b"][:] = [1e-4, 0.0, 0.0, 7e-4]
+    want = x0 + p["h.0.attn.c_proj.b"] + p["h.0.mlp.c_proj.b"]
+    if not np.array_equal(np.asarray(res(p, tok, 1, 1))[0, 0], want):
+        fails.append("A: residual stream rounded")
+    s, p = _tiny_block_model()
+    g1 = np.array([1.1, 0.9, 1.3, 0.7])
+    p["h.0.ln_1.w"][:] = g1
+    wv = 0.5 * np.array([[1, 1, 0, 0], [0, 1, 1, 0], [0, 0, 1, 1], [1, 0, 0, 1]], dtype=float)
+    p["h.0.attn.c_attn.w"][8:12] = wv
+    p["h.0.attn.c_proj.w"][:] = np.eye(4)
+    bo = np.array([0.5, -0.25, 0.0, 0.125])
+    p["h.0.attn.c_proj.b"][:] = bo
+    a = np.array(_hand_ln(list(x0), list(g1), [0.0] * 4))
+    want = x0 + _torch_bf16(wv @ _torch_bf16(a)) + bo
+    assert not np.array_equal(want, x0 + _torch_bf16(wv @ a) + bo)  # the case can tell
+    if not np.allclose(np.asarray(res(p, tok, 1, 1))[0, 0], want, rtol=0, atol=1e-15):
+        fails.append("B: LayerNorm output not rounded before the projection")
+    return fails
+
+
+def test_bf16_activation_forward_pins():
+    res = lambda p, t, h, L: O.residual(p, t, h, L, act=O.round_bf16)
+    assert check_bf16_activation_residual(res) == []
+    # with every activation kept exact it is the forward; with bf16 storage it differs from it by
+    # a few bf16 units at most (GPT-2 small width, two layers, perturbed weights)
+    s = synth.ModelShape(n_vocab=500, n_ctx=16, d_model=768, n_head=12, n_layer=2, d_mlp=3072)
+    w = synth.make_weights(s, bf16=True, perturbed=True)
+    tok = synth.make_tokens(2, 9, s.n_vocab)
+    ref = O.forward(w, tok, 12, 2)
+    assert np.array_equal(O.forward(w, tok, 12, 2, act=O.exact), ref)
+    b = O.forward_bf16_activations(w, tok, 12, 2)
+    d = np.abs(b - ref)
+    assert 0 < d.max() < 8 * 2.0 ** -8 * np.abs(ref).max()
+
+
 @pytest.mark.slow
 def test_activation_sizes_b4_t1024(small_f32):
     # 从零手写GPT-2 §2.3: at batch 4, seq 1024 in fp32 the embedding output is ~12MB, the QKV
@@ -881,6 +1088,90 @@ def _wpe_all_rows_grads(p, tok, lab, n_head, n_layer):
     return loss, g
 
 
+def _post_ln_residual(p, tok, n_head, n_layers, eps=1e-5):
+    """Post-LN (the original Transformer order): x <- ln_1(x + attn(x)), x <- ln_2(x + mlp(x))."""
+    x = O.embed(p["wte"], p["wpe"], tok)
+    for l in range(n_layers):
+        pre = f"h.{l}."
+        x = O.layer_norm(x + O.attention_block(x, p, l, n_head), p[pre + "ln_1.w"], p[pre + "ln_1.b"], eps)
+        x = O.layer_norm(x + O.mlp_block(x, p, l), p[pre + "ln_2.w"], p[pre + "ln_2.b"], eps)
+    return x
+
+
+def _normalised_residual(p, tok, n_head, n_layers, eps=1e-5):
+    """The residual taken from the normalised stream: x <- ln(x) + sublayer(ln(x))."""
+    x = O.embed(p["wte"], p["wpe"], tok)
+    for l in range(n_layers):
+        pre = f"h.{l}."
+        a = O.layer_norm(x, p[pre + "ln_1.w"], p[pre + "ln_1.b"], eps)
+        x = a + O.attention_block(a, p, l, n_head)
+        a = O.layer_norm(x, p[pre + "ln_2.w"], p[pre + "ln_2.b"], eps)
+        x = a + O.mlp_block(a, p, l)
+    return x
+
+
+def _swapped_ln_residual(p, tok, n_head, n_layers, eps=1e-5):
+    """ln_2's parameters used before the attention and ln_1's before the MLP."""
+    x = O.embed(p["wte"], p["wpe"], tok)
+    for l in range(n_layers):
+        pre = f"h.{l}."
+        x = x + O.attention_block(O.layer_norm(x, p[pre + "ln_2.w"], p[pre + "ln_2.b"], eps), p, l, n_head)
+        x = x + O.mlp_block(O.layer_norm(x, p[pre + "ln_1.w"], p[pre + "ln_1.b"], eps), p, l)
+    return x
+
+
+def _parallel_block_residual(p, tok, n_head, n_layers, eps=1e-5):
+    """Both sub-layers read the block input: x <- x + attn(ln_1(x)) + mlp(ln_2(x))."""
+    x = O.embed(p["wte"], p["wpe"], tok)
+    for l in range(n_layers):
+        pre = f"h.{l}."
+        x = (x + O.attention_block(O.layer_norm(x, p[pre + "ln_1.w"], p[pre + "ln_1.b"], eps), p, l, n_head)
+             + O.mlp_block(O.layer_norm(x, p[pre + "ln_2.w"], p[pre + "ln_2.b"], eps), p, l))
+    return x
+
+
+def _no_ln_f_forward(p, tok, n_head, n_layer, eps=1e-5):
+    return O.lm_head(O.residual(p, tok, n_head, n_layer, eps), p["wte"])
+
+
+def _truncating_bf16(a):
+    a = np.asarray(a, dtype=np.float64)
+    _, e = np.frexp(a)
+    step = np.ldexp(1.0, e - 8)
+    return np.trunc(a / step) * step
+
+
+def _ties_away_bf16(a):
+    a = np.asarray(a, dtype=np.float64)
+    _, e = np.frexp(a)
+    step = np.ldexp(1.0, e - 8)
+    return np.sign(a) * np.floor(np.abs(a) / step + 0.5) * step
+
+
+def _seven_bit_bf16(a):
+    a = np.asarray(a, dtype=np.float64)
+    _, e = np.frexp(a)
+    step = np.ldexp(1.0, e - 7)
+    return np.round(a / step) * step
+
+
+def _rounded_residual_stream(p, tok, n_head, n_layers):
+    x = O.round_bf16(O.embed(p["wte"], p["wpe"], tok))
+    for l in range(n_layers):
+        x = O.round_bf16(O.block(x, p, l, n_head, act=O.round_bf16))
+    return x
+
+
+def _unrounded_ln_residual(p, tok, n_head, n_layers, eps=1e-5):
+    x = O.embed(p["wte"], p["wpe"], tok)
+    for l in range(n_layers):
+        pre = f"h.{l}."
+        x = x + O.attention_block(O.layer_norm(x, p[pre + "ln_1.w"], p[pre + "ln_1.b"], eps), p, l, n_head,
+                                  O.round_bf16)
+        x = x + O.mlp_block(O.layer_norm(x, p[pre + "ln_2.w"], p[pre + "ln_2.b"], eps), p, l, act=O.round_bf16)
+    return x
+
+
 @pytest.mark.parametrize("check,mutant", [
     (check_layer_norm, _unbiased_ln), (check_layer_norm, _eps_outside_ln), (check_layer_norm, _no_beta_ln),
     (check_gelu, _cubic_sign_gelu), (check_gelu, _no_half_gelu), (check_gelu, O.gelu_erf),
@@ -899,6 +1190,12 @@ def _wpe_all_rows_grads(p, tok, lab, n_head, n_layer):
     (check_linear_backward, _transposed_dw_linear_back), (check_attention_backward, _no_rowsum_attn_back),
     (check_xent_backward, _unnormalised_xent_back), (check_model_grads, _wte_head_only_grads),
     (check_model_grads, _wte_embedding_only_grads), (check_model_grads, _wpe_all_rows_grads),
+    (check_block_composition, _post_ln_residual), (check_block_composition, _normalised_residual),
+    (check_block_composition, _swapped_ln_residual), (check_block_composition, _parallel_block_residual),
+    (check_head_composition, _no_ln_f_forward),
+    (check_round_bf16, _truncating_bf16), (check_round_bf16, _ties_away_bf16), (check_round_bf16, _seven_bit_bf16),
+    (check_bf16_activation_residual, _rounded_residual_stream),
+    (check_bf16_activation_residual, _unrounded_ln_residual),
 ])
 def test_pins_catch_planted_mistakes(check, mutant):
     try:
