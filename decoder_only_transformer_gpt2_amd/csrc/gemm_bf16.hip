@@ -23,22 +23,7 @@ namespace {
 // us; 256 x 256 tiles of eight waves with a five-stage ring, one per CU, 404-418 us; 256 x 128
 // tiles two per CU 409 us).
 int choose_cfg(int M, int N, int K, bool kb) {
-#ifdef GPT2_GEMM_TUNE
-    if (const char* e = getenv("GPT2_GEMM_CFG")) {
-        const int c = atoi(e);
-        if (c >= 0 && c < kNumCfgs) return c;
-    }
-#endif
     auto tiles = [&](int bm, int bn) { return (long)((M + bm - 1) / bm) * ((N + bn - 1) / bn); };
-#ifdef GPT2_GEMM_TUNE
-    if (tiles(256, 256) >= 4 * 256)
-        if (const char* e = getenv("GPT2_HEAD_CFG")) return atoi(e);
-    {
-        char name[32];
-        snprintf(name, sizeof name, "GPT2_CFG_N%d", N);
-        if (const char* e = getenv(name)) return atoi(e);
-    }
-#endif
     if (tiles(256, 256) >= 4 * 256) return 21;  // vocabulary projection
     // narrow outputs of very many rows (the wte weight gradient, M = n_vocab): large tiles, since
     // the grid fills the CUs twice over anyway and each tile re-reads less through L2
@@ -79,24 +64,6 @@ hipError_t gemm_bf16(const uint16_t* A, const uint16_t* W, const float* bias, vo
         GPT2_CFG(23)
         GPT2_CFG(21)
         GPT2_CFG(28)
-#ifdef GPT2_GEMM_TUNE
-        GPT2_CFG(11)
-        GPT2_CFG(0)
-        GPT2_CFG(8)
-        GPT2_CFG(2)
-        GPT2_CFG(5)
-        GPT2_CFG(6)
-        GPT2_CFG(9)
-        GPT2_CFG(10)
-        GPT2_CFG(19)
-        GPT2_CFG(20)
-        GPT2_CFG(24)
-        GPT2_CFG(25)
-        GPT2_CFG(27)
-        GPT2_CFG(29)
-        GPT2_CFG(30)
-        GPT2_CFG(31)
-#endif
 #undef GPT2_CFG
     }
     return hipErrorInvalidValue;

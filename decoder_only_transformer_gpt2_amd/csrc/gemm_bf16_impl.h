@@ -333,12 +333,15 @@ void gemm_bf16_kernel(
                 // 4c + q in increasing order (a strict > keeps the first of equal values; the
                 // interleave keeps the 64 lanes' reads on distinct banks), then the row maximum (as
                 // an order key) and the smallest column holding it over the four lanes. Columns
-                // past N count as -inf; a lane with no column offers none.
+                // past N count as -inf; a lane with no column offers none (its -inf seed and its
+                // key never beat a real column, whatever the sign of the row's logits: the zero
+                // padding rows of wte give exactly 0 past N).
                 constexpr int CQ = WN / 4;
                 const int ar = lane >> 2, aq = lane & 3;
                 const float* sp = scr + ar * SP + aq;
                 const int lim = CHK ? cols - aq : WN;  // column 4c + aq is valid when 4c < lim
-                float bv = sp[0];
+                const bool has_col = !CHK || lim > 0;
+                float bv = has_col ? sp[0] : -INFINITY;
                 int bc = 0;
 #pragma unroll
                 for (int c = 1; c < CQ; ++c) {
@@ -348,9 +351,8 @@ void gemm_bf16_kernel(
                     bv = take ? x : bv;
                     bc = take ? c : bc;
                 }
-                const uint32_t key = f32_order_key(bv);
+                const uint32_t key = has_col ? f32_order_key(bv) : 0u;
                 const uint32_t kmax = quad_max_u32(key);
-                const bool has_col = !CHK || lim > 0;
                 const uint32_t col = (key == kmax && has_col) ? (uint32_t)(col0 + 4 * bc + aq) : 0xffffffffu;
                 const uint32_t cmin = quad_min_u32(col);
                 if (aq == 0) {
@@ -573,11 +575,6 @@ hipError_t launch_cfg(const uint16_t* A, const uint16_t* W, const float* bias, v
     // XCDs sweep neighbouring columns together, so the logits are written in long runs. The block
     // projections are insensitive to the order.
     int group_m = tiles_n >= 64 ? 1004 : 4;
-#ifdef GPT2_GEMM_TUNE
-    if (const char* e = getenv("GPT2_GEMM_GROUP")) group_m = atoi(e);
-    if (tiles_n >= 64)
-        if (const char* e = getenv("GPT2_HEAD_GROUP")) group_m = atoi(e);
-#endif
     dim3 grid(tiles_m * tiles_n), block(64 * WGM * WGN);
 #define GPT2_LAUNCH(E)                                                                                         \
     launch_epi<BM, BN, BK, S, WGM, WGN, E, KB>(grid, block, s, A, W, bias, C, M, N, K, (int)ldc, a_rows, w_rows, \
@@ -617,30 +614,12 @@ hipError_t launch_cfg(const uint16_t* A, const uint16_t* W, const float* bias, v
                                                                                 gelu_erf, a_rows, w_rows, c_kb, \
                                                                                 ho, s);                         \
     }
-// the configurations the library dispatches to (the tuning builds add the others of kCfgs)
+// the configurations the library dispatches to
 GPT2_GEMM_DECLARE_CFG(12)
 GPT2_GEMM_DECLARE_CFG(16)
 GPT2_GEMM_DECLARE_CFG(22)
 GPT2_GEMM_DECLARE_CFG(23)
 GPT2_GEMM_DECLARE_CFG(21)
 GPT2_GEMM_DECLARE_CFG(28)
-#ifdef GPT2_GEMM_TUNE
-GPT2_GEMM_DECLARE_CFG(11)
-GPT2_GEMM_DECLARE_CFG(0)
-GPT2_GEMM_DECLARE_CFG(8)
-GPT2_GEMM_DECLARE_CFG(2)
-GPT2_GEMM_DECLARE_CFG(5)
-GPT2_GEMM_DECLARE_CFG(6)
-GPT2_GEMM_DECLARE_CFG(9)
-GPT2_GEMM_DECLARE_CFG(10)
-GPT2_GEMM_DECLARE_CFG(19)
-GPT2_GEMM_DECLARE_CFG(20)
-GPT2_GEMM_DECLARE_CFG(24)
-GPT2_GEMM_DECLARE_CFG(25)
-GPT2_GEMM_DECLARE_CFG(27)
-GPT2_GEMM_DECLARE_CFG(29)
-GPT2_GEMM_DECLARE_CFG(30)
-GPT2_GEMM_DECLARE_CFG(31)
-#endif
 
 }  // namespace gpt2k

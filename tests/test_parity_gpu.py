@@ -7,7 +7,9 @@ Tolerances (written here, derived in the design notes):
   * argmax: bit-exact against the first maximum of the GPU's own fp32 logits;
   * single ops (LayerNorm, linear, attention): bounds from the roundings each op performs.
 """
+import json
 import math
+import os
 
 import numpy as np
 import pytest
@@ -32,6 +34,19 @@ def g():
 
 def log(msg):
     print(msg, flush=True)
+
+
+_REPORT = {}
+
+
+def record(key, **vals):
+    """Keep a measured parity figure; written as JSON to $GPT2_PARITY_REPORT (if set) after each
+    update, so a run that stops early still leaves what it measured."""
+    _REPORT[key] = vals
+    path = os.environ.get("GPT2_PARITY_REPORT")
+    if path:
+        with open(path, "w") as f:
+            json.dump(_REPORT, f, indent=1, sort_keys=True)
 
 
 def model(g, shape, dtype, perturbed=False, gelu="tanh"):
@@ -281,6 +296,14 @@ def bf16_report(got, ref, label):
     return err.max(), agree
 
 
+def near_tie_only(got, ref, e):
+    """Every top-1 disagreement sits where the oracle's own gap between its maximum and the GPU's
+    pick is at most 2e: with every logit within e of the oracle, no other position can flip."""
+    pick = first_argmax(got)
+    gap = ref.max(axis=-1) - np.take_along_axis(ref, pick[..., None], axis=-1)[..., 0]
+    return bool(np.all(gap <= 2 * e)), int(np.sum(pick != first_argmax(ref)))
+
+
 def test_forward_bf16_config1(g, small_bf16):
     """GPT-2 small, B=4, T=1024, bf16: the headline workload, oracle on every row."""
     m, w = small_bf16
@@ -290,43 +313,59 @@ def test_forward_bf16_config1(g, small_bf16):
     assert m.check(4, 1024) == g.OK
     got = logits.cpu().numpy()
     assert np.array_equal(am.cpu().numpy(), first_argmax(got))
-    worst, agree_all = 0.0, []
+    worst, agree_all, flips = 0.0, [], 0
     for b in range(4):
         ref = O.forward(w, tok[b:b + 1], 12, 12)
         e, a = bf16_report(got[b:b + 1], ref, f"row {b}")
+        ok, nf = near_tie_only(got[b:b + 1], ref, e)
+        assert ok, b
         worst = max(worst, e)
         agree_all.append(a)
+        flips += nf
+    record("gpt2_small_b4_t1024", positions=4096, max_abs_err=worst, top1=float(np.mean(agree_all)),
+           flips=flips, flips_all_near_ties=True)
     assert worst <= 5e-2
-    assert np.mean(agree_all) >= 0.99
+    assert np.mean(agree_all) >= 0.99, np.mean(agree_all)
 
 
-def _sampled_large(g, shape, B, samples, label):
+def _sampled_large(g, shape, B, samples, label, floor):
     """Full B x 1024 forward of a larger model on the GPU (the launch configuration the bench times);
-    the oracle runs on prefixes of a few batch rows. Causality makes the logits of positions
-    [0, t) depend on tokens [0, t) only, so a prefix run of the oracle gives exactly those rows."""
+    the oracle runs on whole batch rows and prefixes of others (at least 1024 positions in all).
+    Causality makes the logits of positions [0, t) depend on tokens [0, t) only, so a prefix run of
+    the oracle gives exactly those rows.
+
+    Bounds: max |logit error| <= 5e-2 on every sampled position; every top-1 disagreement sits at
+    an oracle near-tie (gap <= 2 max|err|), so each position the error bound can decide agrees. The
+    raw top-1 rate is measured, recorded and held to `floor`: 99% where it holds (GPT-2 medium:
+    99.3% over 1280 positions), 97% for GPT-2 XL (98.8% over 1152 positions). With bf16 activations
+    these random-init models have many near-ties, and rounding the activations the bf16
+    configuration stores, with everything else exact, already flips about 1.3% of GPT-2 medium's
+    positions (a float32 CPU model of exactly those roundings over 768 positions), so a rate near
+    99% is the most a kernel computing in that precision can give."""
     m, w = model(g, shape, "bf16")
     tok = synth.make_tokens(B, 1024)
     log(f"forward bf16 {label} B={B} T=1024")
     logits, am = m.forward(dev_tokens(tok))
     assert m.check(B, 1024) == g.OK
     am = am.cpu().numpy()
-    n_pos, n_agree = 0, 0
+    n_pos, n_agree, n_flip, worst = 0, 0, 0, 0.0
     for b, t in samples:
         got = logits[b, :t].cpu().numpy()
         assert np.array_equal(am[b, :t], first_argmax(got))
         ref = O.forward(w, tok[b:b + 1, :t], shape.n_head, shape.n_layer)[0]
         e, a = bf16_report(got, ref, f"{label} row {b} prefix {t}")
         assert e <= 5e-2
-        # Top-1: with every logit within e of the oracle, a position can change its top-1 only
-        # where the oracle's own gap between its maximum and the GPU's pick is at most 2e. The
-        # random-init models have many such near-ties, so the agreement rate is reported and
-        # held to a floor, and each disagreement is checked to be one of them.
-        pick = first_argmax(got)
-        gap = ref.max(axis=-1) - np.take_along_axis(ref, pick[:, None], axis=-1)[:, 0]
-        assert np.all(gap <= 2 * e)
+        ok, nf = near_tie_only(got, ref, e)
+        assert ok, (b, t)
+        worst = max(worst, e)
         n_pos += t
-        n_agree += int(round(a * t))
-    assert n_agree / n_pos >= 0.95
+        n_flip += nf
+        n_agree += t - nf
+    assert n_pos >= 1024
+    rate = n_agree / n_pos
+    record(label, positions=n_pos, max_abs_err=worst, top1=rate, flips=n_flip, flips_all_near_ties=True)
+    log(f"  {label}: top1 {rate:.5f} over {n_pos} positions, {n_flip} flips, all at near-ties")
+    assert rate >= floor, rate
     # argmax of every row against the GPU's own logits, one batch row at a time
     for b in range(B):
         assert np.array_equal(am[b], first_argmax(logits[b].cpu().numpy()))
@@ -334,13 +373,42 @@ def _sampled_large(g, shape, B, samples, label):
 
 
 def test_forward_bf16_medium_sampled(g):
-    """GPT-2 medium (24 layers, d=1024, 16 heads), B=8, T=1024."""
-    _sampled_large(g, synth.GPT2_MEDIUM, 8, [(0, 384), (7, 96)], "medium")
+    """GPT-2 medium (24 layers, d=1024, 16 heads), B=8, T=1024: oracle on all of row 0 and on a
+    256-position prefix of row 7 (1280 positions)."""
+    _sampled_large(g, synth.GPT2_MEDIUM, 8, [(0, 1024), (7, 256)], "gpt2_medium_b8_t1024", 0.99)
 
 
 def test_forward_bf16_xl_sampled(g):
-    """GPT-2 XL (48 layers, d=1600, 25 heads), B=4, T=1024."""
-    _sampled_large(g, synth.GPT2_XL, 4, [(0, 160), (3, 48)], "xl")
+    """GPT-2 XL (48 layers, d=1600, 25 heads), B=4, T=1024: oracle on all of row 0 and on a
+    128-position prefix of row 3 (1152 positions)."""
+    _sampled_large(g, synth.GPT2_XL, 4, [(0, 1024), (3, 128)], "gpt2_xl_b4_t1024", 0.97)
+
+
+def test_argmax_all_negative_logits(g):
+    """Rows whose logits are all negative: the tiled vocabulary projection's last column tile has
+    wavefronts with no column below n_vocab (the zero padding rows of wte give exactly 0 there),
+    which must never win the argmax. ln_f with gamma 0 and beta 1 gives every row xf = 1, and wte
+    shifted by -0.05 makes every logit sum_d wte[v, d] about -38 (N(-38.4, 0.55^2))."""
+    s = synth.GPT2_SMALL
+    w = synth.make_weights(s, bf16=True)
+    w["wte"] = synth.round_bf16(w["wte"] - np.float32(0.05))
+    w["ln_f.w"] = np.zeros_like(w["ln_f.w"])
+    w["ln_f.b"] = np.ones_like(w["ln_f.b"])
+    m = g.GPT2(g.ModelConfig(dtype="bf16"))
+    m.load_numpy(w)
+    want = int(np.argmax(w["wte"].astype(np.float64).sum(axis=1)))
+    tok = synth.make_tokens(2, 64)
+    logits, am = m.forward(dev_tokens(tok))
+    got = logits.cpu().numpy()
+    assert got.max() < 0
+    assert np.array_equal(am.cpu().numpy(), first_argmax(got))
+    assert np.all(am.cpu().numpy() == want)
+    # the next-token projection of more than 16 rows runs tiled as well
+    cache = m.kv_cache(20)
+    lg, nxt = m.prefill(dev_tokens(synth.make_tokens(20, 3)), cache, logits=True, nxt=True)
+    assert lg.max().item() < 0
+    assert torch.equal(nxt, lg.argmax(dim=-1).int())
+    assert np.all(nxt.cpu().numpy() == want)
 
 
 def test_forward_bf16_perturbed(g):
@@ -517,6 +585,35 @@ def test_decode_bf16_vs_forward_and_oracle(g, small_bf16):
     ref = O.forward(w, tok[:1], 12, 12)[:, 40:]
     e, a = bf16_report(got[:1], ref, "decode bf16 row 0")
     assert e <= 5e-2
+
+
+def test_decode_bf16_long_prefix_vs_oracle(g, small_bf16):
+    """GPT-2 small bf16 with a 512-token prompt, then 64 teacher-forced decode steps (positions
+    512..575, 513..576 keys per step) against the oracle's forward over the whole sequence: the
+    logit bound of the bf16 configuration, and every top-1 disagreement at an oracle near-tie."""
+    m, w = small_bf16
+    tok = synth.make_tokens(1, 576, seed=7)
+    got = _teacher_forced(m, tok, 512, m.kv_cache(1))
+    ref = O.forward(w, tok, 12, 12)[:, 512:]
+    e, a = bf16_report(got, ref, "decode bf16 positions 512..575")
+    ok, nf = near_tie_only(got, ref, e)
+    record("decode_bf16_small_pos512_575", positions=64, max_abs_err=e, top1=a, flips=nf)
+    assert e <= 5e-2
+    assert ok
+
+
+def test_decode_bf16_multi_chunk_context(g):
+    """bf16 decode attention past one 1024-key chunk (1501 keys: two chunks, the second partial),
+    against the oracle: per-row relative L2 of the logits within 8 bf16 units (2^-5), the scale of
+    a few roundings of the stored activations."""
+    s = synth.ModelShape(n_vocab=1000, n_ctx=2048, d_model=128, n_head=2, n_layer=2, d_mlp=512)
+    m, w = model(g, s, "bf16")
+    tok = synth.make_tokens(1, 1504, n_vocab=1000)
+    got = _teacher_forced(m, tok, 1500, m.kv_cache(1))
+    ref = O.forward(w, tok, 2, 2)[:, 1500:]
+    e = row_rel_l2(got, ref).max()
+    log(f"  bf16 decode at positions 1500..1503: max row rel L2 = {e:.3e}")
+    assert e <= 8 * BF16_U
 
 
 @pytest.mark.parametrize("n_ctx,pos", [(2048, 1500), (4096, 3000)])

@@ -1,16 +1,24 @@
 """GPU parity of the backward pass (gpt2_backward) against the oracle's loss_and_grads.
 
 Both sides get the same seeded weights (perturbed variant: non-zero biases, gains and shifts, so
-every gradient path carries signal) and token ids. Each gradient tensor is compared by its
-relative L2 error ||g_gpu - g_oracle|| / ||g_oracle||:
-  * fp32 mode: <= 1e-3. Every product is an fp32 dot product over at most K = 50304 terms (the
-    vocabulary); its rounding error is at most K u ~ 3e-3 relative in the worst case and ~sqrt(K) u
-    ~ 1e-5 typically (u = 2^-24), and the bound sits between the two;
-  * bf16 mode: <= 5e-2. Every product takes bf16 operands (u = 2^-8 = 3.9e-3 per rounding; each
-    gradient passes through the rounded forward activations, the rounded output gradient and the
-    rounded transposed copies, a handful of independent roundings per term) while the oracle keeps
-    every activation exact.
-Rows of the wpe gradient past T must be exactly zero on both sides.
+every gradient path carries signal) and token ids. Every element of every gradient tensor is
+compared, in the form of the gradient check of [手写] §5.2 (|g - o| <= atol + rtol |o|). Gradients
+have no natural unit and their rows differ in scale (the wte rows of tokens that occur carry the
+embedding gradient, the others only the head's), so the absolute term is taken per row of a matrix
+(the row's RMS over the oracle, rms_row(o)) and per tensor for a vector:
+  * fp32 mode: atol = 1e-4 rms_row(o), rtol = 1e-3 (the constants of that gradient check). Every
+    product is an fp32 dot product over at most K = 50304 terms; its rounding error is about
+    sqrt(K) u ~ 1e-5 of the term scale (u = 2^-24), inside the bound;
+  * bf16 mode: atol = rtol = 32 u_bf16 = 0.125 (u_bf16 = 2^-8, the unit roundoff of the 8-bit
+    significand). A gradient element is a sum of many terms, each carrying a few independent bf16
+    roundings against the exact oracle (the saved forward activation, the output gradient and,
+    inside attention, P and dS) plus what the layers above rounded: its error is close to normal
+    with a standard deviation of c u rms_row(o), c the number of roundings that compound (about
+    1.4 measured per tensor at T=64). The largest of up to 4e7 such errors is about 6 standard
+    deviations, so 32 u covers c up to 5.
+Each tensor's relative L2 error ||g - o|| / ||o|| is held as well: <= 1e-4 in fp32 (sqrt(K) u) and
+<= 8 u_bf16 in bf16 (c well under 8). Rows of the wpe gradient past T must be exactly zero on
+both sides.
 """
 import numpy as np
 import pytest
@@ -21,7 +29,9 @@ from decoder_only_transformer_gpt2_amd import synth
 
 pytestmark = pytest.mark.gpu
 
-TOL = {"f32": 1e-3, "bf16": 5e-2}
+U_BF16 = 2.0 ** -8
+# (atol in units of rms_row(o), rtol, bound on the per-tensor relative L2 error)
+TOL = {"f32": (1e-4, 1e-3, 1e-4), "bf16": (32 * U_BF16, 32 * U_BF16, 8 * U_BF16)}
 TINY = synth.ModelShape(n_vocab=1000, n_ctx=256, d_model=128, n_head=2, n_layer=2, d_mlp=512)
 
 
@@ -57,7 +67,10 @@ def gpu_grads(g, m, shape, tok, lab=None):
 
 
 def compare(got, ref, tol, T):
-    worst = ("", 0.0)
+    """Element-wise |g - o| <= atol * rms_row(o) + rtol * |o| and per-tensor relative L2 for every
+    tensor; every tensor's figures are logged before anything is asserted."""
+    atol, rtol, l2tol = tol
+    rows, bad = [], []
     for name, r in ref.items():
         x = got[name]
         assert x.shape == r.shape, name
@@ -65,12 +78,22 @@ def compare(got, ref, tol, T):
         if name == "wpe":
             assert not x[T:].any() and not r[T:].any(), "wpe rows past T must be zero"
             x, r = x[:T], r[:T]
-        err = np.linalg.norm(x - r) / max(np.linalg.norm(r), 1e-30)
-        if err > worst[1]:
-            worst = (name, err)
-        assert err <= tol, (name, err)
-    log(f"    worst relative L2 error: {worst[1]:.3e} ({worst[0]})")
-    return worst
+        if r.ndim == 2:
+            scale = np.sqrt(np.mean(r * r, axis=1, keepdims=True))
+        else:
+            scale = np.sqrt(np.mean(r * r))
+        bound = atol * np.maximum(scale, 1e-30) + rtol * np.abs(r)
+        ratio = np.abs(x - r) / bound
+        k = int(np.argmax(ratio))
+        l2 = float(np.linalg.norm(x - r) / max(np.linalg.norm(r), 1e-30))
+        rows.append((name, float(ratio.flat[k]), l2))
+        if ratio.flat[k] > 1.0 or l2 > l2tol:
+            bad.append((name, np.unravel_index(k, r.shape), float(x.flat[k]), float(r.flat[k]), float(ratio.flat[k]), l2))
+    we = max(rows, key=lambda t: t[1])
+    wl = max(rows, key=lambda t: t[2])
+    log(f"    worst element |g-o|/bound: {we[1]:.3f} ({we[0]}); worst relative L2: {wl[2]:.3e} ({wl[0]})")
+    assert not bad, bad[:5]
+    return we, wl
 
 
 def run_case(g, shape, dtype, B, T, ignore=()):
@@ -102,6 +125,18 @@ def test_backward_bf16_tiny(g):
 
 def test_backward_bf16_gpt2_small(g):
     run_case(g, synth.GPT2_SMALL, "bf16", 2, 64)
+
+
+def test_backward_bf16_gpt2_small_t1024(g):
+    """One full-length sequence of GPT-2 small, B=1 T=1024: the attention backward walks 16 key
+    tiles, the weight gradients reduce over 1024 rows, and the transposes move full tiles."""
+    run_case(g, synth.GPT2_SMALL, "bf16", 1, 1024, ignore=[(0, 100), (0, 1023)])
+
+
+def test_backward_f32_t1024(g):
+    """fp32 mode at T=1024 on a two-layer model of GPT-2 small width."""
+    s = synth.ModelShape(n_vocab=50257, n_ctx=1024, d_model=768, n_head=12, n_layer=2, d_mlp=3072)
+    run_case(g, s, "f32", 1, 1024)
 
 
 def test_backward_full_size_bf16(g):
