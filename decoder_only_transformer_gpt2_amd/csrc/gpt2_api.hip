@@ -3,6 +3,7 @@
 // the caller; nothing here allocates device memory.
 #include <algorithm>
 #include <cstring>
+#include <mutex>
 #include <new>
 #include <vector>
 
@@ -643,6 +644,41 @@ gpt2_status enqueue_backward(const gpt2_model* m, const int32_t* tokens, int B, 
 
 }  // namespace
 
+// ------------------------------------------------------------------ fixed scratch (no allocation)
+// Workspace of gpt2_forward_noalloc: a file-scope device array, one copy per GPU the library runs
+// on, held until the process ends. Host code never passes the array's name to a kernel or a copy
+// (on the host it is only a stand-in for the symbol): its device address is looked up once per
+// device with hipGetSymbolAddress and kept in scratch_addr.
+constexpr size_t kScratchBytes = (size_t)80 << 20;  // 80 MiB: GPT-2 small up to B*T = 4096 rows
+static __device__ __align__(256) char scratch[kScratchBytes];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex scratch_mu;
+void* scratch_addr[kMaxDevices] = {};
+
+// Device address of this device's scratch array for work enqueued on stream s (looked up on the
+// first call for that device, with the device current).
+gpt2_status scratch_for(hipStream_t s, char** out) {
+    int cur = 0, dev = 0;
+    if (hipGetDevice(&cur) != hipSuccess) return GPT2_EHIP;
+    dev = cur;
+    if (s && hipStreamGetDevice(s, &dev) != hipSuccess) return GPT2_EHIP;
+    if (dev < 0 || dev >= kMaxDevices) return GPT2_EHIP;
+    std::lock_guard<std::mutex> lock(scratch_mu);
+    if (!scratch_addr[dev]) {
+        if (dev != cur && hipSetDevice(dev) != hipSuccess) return GPT2_EHIP;
+        void* p = nullptr;
+        const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (dev != cur && hipSetDevice(cur) != hipSuccess) return GPT2_EHIP;
+        if (e != hipSuccess || !p) return GPT2_EHIP;
+        scratch_addr[dev] = p;
+    }
+    *out = static_cast<char*>(scratch_addr[dev]);
+    return GPT2_OK;
+}
+}  // namespace
+
 extern "C" {
 
 gpt2_status gpt2_config(const gpt2_config_t* cfg, gpt2_model** out) {
@@ -724,6 +760,21 @@ gpt2_status gpt2_forward(const gpt2_model* m, const int32_t* tokens, int32_t B, 
     if (st != GPT2_OK) return st;
     Sequencer q{s};
     return enqueue_forward(m, tokens, B, T, logits, argmax, static_cast<char*>(ws_dev), q);
+}
+
+gpt2_status gpt2_forward_noalloc(const gpt2_model* m, const int32_t* tokens, int32_t B, int32_t T, float* logits,
+                                 int32_t* argmax, hipStream_t s) {
+    if (!m || !tokens || !logits) return GPT2_EINVAL;
+    if (!m->loaded) return GPT2_ESTATE;
+    if (B < 1 || T < 1 || T > m->cfg.n_ctx) return GPT2_ESHAPE;
+    if ((int64_t)B * T > (int64_t)1 << 24 || ws_layout(m, B, T).total > kScratchBytes) return GPT2_EWORKSPACE;
+    char* ws = nullptr;
+    const gpt2_status st = scratch_for(s, &ws);
+    if (st != GPT2_OK) return st;
+    // every workspace buffer of the forward is written before it is read (the residual by the
+    // embedding, the head partials and token flags by their producers), so nothing is cleared
+    Sequencer q{s};
+    return enqueue_forward(m, tokens, B, T, logits, argmax, ws, q);
 }
 
 gpt2_status gpt2_forward_loss(const gpt2_model* m, const int32_t* tokens, const int32_t* labels, int32_t B, int32_t T,

@@ -41,6 +41,7 @@ SIGNATURES = {
     "gpt2_workspace_bytes": (_SZ, [_P, _I32, _I32]),
     "gpt2_load_weights": (_I32, [_P, ctypes.POINTER(_P), _I32, _I32, _P, _SZ, _P]),
     "gpt2_forward": (_I32, [_P, _P, _I32, _I32, _P, _P, _P, _SZ, _P]),
+    "gpt2_forward_noalloc": (_I32, [_P, _P, _I32, _I32, _P, _P, _P]),
     "gpt2_forward_loss": (_I32, [_P, _P, _P, _I32, _I32, _P, _P, _P, _SZ, _P]),
     "gpt2_kv_cache_bytes": (_SZ, [_P, _I32]),
     "gpt2_prefill": (_I32, [_P, _P, _I32, _I32, _P, _SZ, _P, _P, _P, _SZ, _P]),
@@ -234,6 +235,18 @@ class GPT2:
         _require_cuda(logits, argmax, ws)
         _check(lib().gpt2_forward(self._h, _ptr(tokens), B, T, _ptr(logits), _ptr(argmax), _ptr(ws), ws.numel(),
                                   _stream(stream)), "gpt2_forward")
+        return logits, argmax
+
+    def forward_noalloc(self, tokens: torch.Tensor, logits: torch.Tensor, argmax: torch.Tensor | None = None,
+                        stream=None):
+        """gpt2_forward_noalloc: the forward with the library's fixed scratch as workspace; the
+        caller passes every output (nothing is allocated here either)."""
+        _require_cuda(tokens, logits, argmax)
+        if tokens.dtype != torch.int32 or tokens.dim() != 2 or not tokens.is_contiguous():
+            raise ValueError("tokens must be a contiguous int32 [B, T] device tensor")
+        B, T = tokens.shape
+        _check(lib().gpt2_forward_noalloc(self._h, _ptr(tokens), B, T, _ptr(logits), _ptr(argmax), _stream(stream)),
+               "gpt2_forward_noalloc")
         return logits, argmax
 
     def forward_loss(self, tokens: torch.Tensor, labels: torch.Tensor | None = None, nll: torch.Tensor | None = None,

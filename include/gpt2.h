@@ -15,7 +15,8 @@
  * Conventions shared by every entry point
  *   - Every pointer named *_dev is a device pointer on the current HIP device. The caller owns
  *     every buffer (tokens, logits, packed weights, workspace); the library never calls
- *     hipMalloc or hipFree and keeps no device memory of its own.
+ *     hipMalloc or hipFree. Its only device memory of its own is the fixed scratch array of
+ *     gpt2_forward_noalloc (80 MiB per device, present from module load).
  *   - Every call that takes a hipStream_t only enqueues work on that stream (NULL = the null
  *     stream) and returns without synchronising, except gpt2_check, which synchronises it.
  *   - Arguments are validated on the host before anything is launched; on any error nothing is
@@ -122,6 +123,21 @@ gpt2_status gpt2_load_weights(gpt2_model* m, const void* const* src, int32_t n_s
 gpt2_status gpt2_forward(const gpt2_model* m, const int32_t* tokens_dev, int32_t B, int32_t T,
                          float* logits_dev, int32_t* argmax_dev, void* ws_dev, size_t ws_bytes,
                          hipStream_t stream);
+
+/* gpt2_forward for callers that cannot allocate device memory (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc): the same launches and results as gpt2_forward,
+ * with the workspace taken from a fixed array inside the library instead of a caller's buffer.
+ *   - The array holds 80 MiB per GPU the library runs on (GPT-2 small up to B*T = 4096 rows) and
+ *     lives until the process ends; its address on each device is looked up once, on the first call
+ *     for that device. The call itself allocates nothing and calls no allocating routine.
+ *   - GPT2_EWORKSPACE when gpt2_workspace_bytes(m, B, T) exceeds 80 MiB; the other argument rules
+ *     and errors are gpt2_forward's (logits_dev required, argmax_dev optional).
+ *   - Every call on one GPU shares that GPU's array: calls that overlap on one GPU (other streams,
+ *     other threads) race and must be serialised by the caller. Nothing in it needs clearing.
+ *   - Out-of-range token ids are clamped as in gpt2_forward but cannot be reported: gpt2_check
+ *     needs the caller's workspace. */
+gpt2_status gpt2_forward_noalloc(const gpt2_model* m, const int32_t* tokens_dev, int32_t B, int32_t T,
+                                 float* logits_dev, int32_t* argmax_dev, hipStream_t stream);
 
 /* The forward pass followed by the shifted next-token cross-entropy of [手写] §4.1, without
  * writing the logits: the vocabulary projection reduces each row to its log-sum-exp and the
