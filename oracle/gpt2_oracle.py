@@ -391,6 +391,28 @@ def causal_attention_backward(q: np.ndarray, k: np.ndarray, v: np.ndarray, do: n
     return (ds @ k) * scale, (np.swapaxes(ds, -1, -2) @ q) * scale, dv
 
 
+def causal_attention_backward_terms(q: np.ndarray, k: np.ndarray, v: np.ndarray, do: np.ndarray):
+    """Magnitudes of the terms that causal_attention_backward sums, for bounding the rounding error
+    of an implementation (the sum of |terms| of a dot product bounds what relative errors in its
+    operands can move it). With P the masked softmax, |dP| taken as |dO| |V|^T and the row-sum term
+    as rowsum(P |dP|): |dS| <= P (|dP| + rowsum(P |dP|)); then
+    dq_terms = |dS| |K| / sqrt(dh), dk_terms = |dS|^T |Q| / sqrt(dh), dv_terms = P^T |dO|.
+    (dQ is a sum of dS-weighted keys whose weights sum to zero, so it can be far smaller than
+    these terms when the keys share a common part.) Returns (dq_terms, dk_terms, dv_terms)."""
+    q = np.asarray(q, dtype=F64)
+    k = np.asarray(k, dtype=F64)
+    v = np.asarray(v, dtype=F64)
+    do = np.abs(np.asarray(do, dtype=F64))
+    T, dh = q.shape[-2], q.shape[-1]
+    scale = 1.0 / math.sqrt(dh)
+    s = (q @ np.swapaxes(k, -1, -2)) * scale
+    s = np.where(np.triu(np.ones((T, T), dtype=bool), k=1), -np.inf, s)
+    prob = softmax(s, axis=-1)
+    dp = do @ np.swapaxes(np.abs(v), -1, -2)
+    ds = prob * (dp + (prob * dp).sum(axis=-1, keepdims=True))
+    return (ds @ np.abs(k)) * scale, (np.swapaxes(ds, -1, -2) @ np.abs(q)) * scale, np.swapaxes(prob, -1, -2) @ do
+
+
 def shifted_cross_entropy_backward(logits: np.ndarray, labels: np.ndarray) -> np.ndarray:
     """Gradient of shifted_cross_entropy with respect to logits [B, T, V]: for every counted
     position (b, t < T-1), (softmax(logits[b, t]) - onehot(labels[b, t+1])) / n_counted; zero at
@@ -410,10 +432,14 @@ def shifted_cross_entropy_backward(logits: np.ndarray, labels: np.ndarray) -> np
 
 
 def loss_and_grads(p: dict, tokens: np.ndarray, labels: np.ndarray | None, n_head: int, n_layer: int,
-                   eps: float = 1e-5) -> tuple[float, dict]:
+                   eps: float = 1e-5, term_scales: bool = False):
     """Mean shifted cross-entropy of the forward (labels None: the tokens themselves) and its
     gradient with respect to every weight of p (same keys). The forward is the one above, step by
-    step, keeping what the backward needs; the backward visits the steps in reverse."""
+    step, keeping what the backward needs; the backward visits the steps in reverse.
+
+    term_scales: also return, per weight, the magnitude its gradient is built from: the backward
+    run on magnitudes (_gradient_magnitudes), the scale against which an implementation's rounding
+    error in that gradient is measured. Returns (loss, grads) or (loss, grads, scales)."""
     tokens = np.asarray(tokens)
     labels = tokens if labels is None else np.asarray(labels)
     B, T = tokens.shape
@@ -463,7 +489,89 @@ def loss_and_grads(p: dict, tokens: np.ndarray, labels: np.ndarray | None, n_hea
     dwpe = np.zeros_like(np.asarray(p["wpe"], F64))
     dwpe[:T] = dx.sum(axis=0)
     g["wpe"] = dwpe
-    return loss, g
+    if not term_scales:
+        return loss, g
+    return loss, g, _gradient_magnitudes(p, tokens, labels, logits, xf, x, saved, n_head, n_layer, eps)
+
+
+def _layer_norm_backward_terms(x, gamma, mdy, eps):
+    """Magnitudes of the terms of layer_norm_backward for output-gradient magnitudes mdy: with
+    |g| = mdy |gamma| and xhat's magnitude taken as |xhat| + 1 (its row RMS),
+    |dx| <= rstd (|g| + mean|g| + |xhat| mean|g xhat|); the gain and shift gradients sum
+    mdy |xhat| and mdy. Returns (dx, dgamma, dbeta) magnitudes."""
+    x = np.asarray(x, dtype=F64)
+    mean = x.mean(axis=-1, keepdims=True)
+    rstd = 1.0 / np.sqrt(((x - mean) ** 2).mean(axis=-1, keepdims=True) + eps)
+    xhat = np.abs((x - mean) * rstd) + 1.0  # |xhat| plus its row RMS (1)
+    gm = mdy * np.abs(np.asarray(gamma, F64))
+    dx = rstd * (gm + gm.mean(axis=-1, keepdims=True) + xhat * (gm * xhat).mean(axis=-1, keepdims=True))
+    d = x.shape[-1]
+    return dx, (mdy * xhat).reshape(-1, d).sum(axis=0), mdy.reshape(-1, d).sum(axis=0)
+
+
+def _gradient_magnitudes(p, tokens, labels, logits, xf, x_last, saved, n_head, n_layer, eps):
+    """The backward of loss_and_grads run on magnitudes: every step takes the magnitudes of its
+    inputs and returns the sum of the magnitudes of the terms it adds up (|dY| |W| for an input
+    gradient, |dY|^T |X| for a weight, sums of |dY| for biases and shifts, and the bounds of
+    _layer_norm_backward_terms, |gelu'| mdy and causal_attention_backward_terms), starting from
+    the magnitude (softmax + onehot) / n of the loss gradient. A forward activation X enters as
+    |X| plus its row's RMS: an implementation computes it with an error on the scale of its row,
+    so a small element can be off by far more than its own size. A relative error of e in every
+    term of every step moves each gradient by at most about e times its magnitude per step it went
+    through (a running error bound). Returns name -> magnitude, shaped like the gradients."""
+    B, T = np.asarray(tokens).shape
+    labels = np.asarray(tokens if labels is None else labels)
+    sc = {}
+    ab = lambda a: np.abs(np.asarray(a, dtype=F64))
+
+    def act(a):  # a forward activation's magnitude: |a| plus its row's RMS, since an implementation's
+        a = np.asarray(a, dtype=F64)  # error in an element scales with its row, not with the element
+        return np.abs(a) + np.sqrt((a * a).mean(axis=-1, keepdims=True))
+    # the loss gradient (softmax - onehot) / n: its two parts' magnitudes added
+    z = np.asarray(logits, dtype=F64)
+    _, counted = shifted_nll(z, labels)
+    n = max(int(counted.sum()), 1)
+    sm = softmax(z[:, :-1, :], axis=-1)
+    mlog = np.zeros_like(z)
+    mlog[:, :-1, :] = np.where(counted[..., None], sm, 0.0) / n
+    b_idx, t_idx = np.nonzero(counted)
+    mlog[b_idx, t_idx, labels[:, 1:][b_idx, t_idx]] += 1.0 / n
+
+    def lin(name, xin, mdy):
+        w = ab(p[name + ".w"])
+        n_out, n_in = w.shape
+        sc[name + ".w"] = mdy.reshape(-1, n_out).T @ act(xin).reshape(-1, n_in)
+        sc[name + ".b"] = mdy.reshape(-1, n_out).sum(axis=0)
+        return mdy @ w
+
+    mxf = mlog @ ab(p["wte"])
+    swte = mlog.reshape(-1, z.shape[-1]).T @ act(xf).reshape(-1, xf.shape[-1])
+    mdx, sc["ln_f.w"], sc["ln_f.b"] = _layer_norm_backward_terms(x_last, p["ln_f.w"], mxf, eps)
+    c = math.sqrt(2.0 / math.pi)
+    for l in reversed(range(n_layer)):
+        pre = f"h.{l}."
+        x_in, a1, q, k, v, o, x_mid, a2, u, h = saved[l]
+        mdh = lin(pre + "mlp.c_proj", h, mdx)
+        uu = np.asarray(u, F64)
+        t = np.tanh(c * (uu + 0.044715 * uu ** 3))
+        mdu = mdh * np.abs(0.5 * (1.0 + t) + 0.5 * uu * (1.0 - t * t) * c * (1.0 + 3.0 * 0.044715 * uu * uu))
+        mda2 = lin(pre + "mlp.c_fc", a2, mdu)
+        mln2, sc[pre + "ln_2.w"], sc[pre + "ln_2.b"] = _layer_norm_backward_terms(x_mid, p[pre + "ln_2.w"], mda2, eps)
+        mdx_mid = mdx + mln2
+        mdo = lin(pre + "attn.c_proj", o, mdx_mid)
+        dh_ = mdo.shape[-1] // n_head
+        mdo_h = mdo.reshape(B, T, n_head, dh_).transpose(0, 2, 1, 3)
+        tq, tk, tv = causal_attention_backward_terms(act(q), act(k), act(v), mdo_h)
+        mda1 = lin(pre + "attn.c_attn", a1, np.concatenate([merge_heads(tq), merge_heads(tk), merge_heads(tv)], -1))
+        mln1, sc[pre + "ln_1.w"], sc[pre + "ln_1.b"] = _layer_norm_backward_terms(x_in, p[pre + "ln_1.w"], mda1, eps)
+        mdx = mdx_mid + mln1
+    d = mdx.shape[-1]
+    np.add.at(swte, tokens.reshape(-1), mdx.reshape(-1, d))
+    sc["wte"] = swte
+    swpe = np.zeros(np.asarray(p["wpe"]).shape)
+    swpe[:T] = mdx.sum(axis=0)
+    sc["wpe"] = swpe
+    return sc
 
 
 def param_count(n_vocab: int, n_ctx: int, d: int, n_layer: int, d_mlp: int) -> int:

@@ -842,6 +842,32 @@ def check_model_grads(lg):
     return fails
 
 
+def check_gradient_term_scales(lg):
+    """lg(p, tok, lab, n_head, n_layer) -> (loss, grads, scales). Every scale is a sum of term
+    magnitudes, so it bounds its gradient (|g| <= S, the triangle inequality) and is never
+    negative; where every term of a sum is non-negative the two are equal: the value-gradient terms
+    of attention with a non-negative output gradient (dv = P^T dO, dv_terms = P^T |dO|)."""
+    s, p = tiny_model()
+    r = rng(37)
+    tok = r.integers(0, s.n_vocab, size=(2, 5))
+    _, g, sc = lg(p, tok, None, s.n_head, s.n_layer)
+    fails = [n for n in g if sc[n].shape != g[n].shape or np.any(sc[n] < np.abs(g[n]) - 1e-12)]
+    q, k, v = (r.standard_normal((1, 2, 6, 4)) for _ in range(3))
+    do = np.abs(r.standard_normal((1, 2, 6, 4)))
+    _, _, dv = O.causal_attention_backward(q, k, v, do)
+    tq, tk, tv = O.causal_attention_backward_terms(q, k, v, do)
+    if not np.allclose(tv, dv, rtol=1e-12, atol=0):
+        fails.append("dv terms")
+    dq, dk, _ = O.causal_attention_backward(q, k, v, do)
+    if np.any(tq < np.abs(dq) - 1e-12) or np.any(tk < np.abs(dk) - 1e-12):
+        fails.append("dq/dk terms")
+    return fails
+
+
+def test_gradient_term_scales_pins():
+    assert check_gradient_term_scales(lambda *a: O.loss_and_grads(*a, term_scales=True)) == []
+
+
 def test_layer_norm_backward_pins():
     assert check_layer_norm_backward(O.layer_norm_backward) == []
 
@@ -1172,6 +1198,21 @@ def _unrounded_ln_residual(p, tok, n_head, n_layers, eps=1e-5):
     return x
 
 
+def _signed_term_scales(p, tok, lab, n_head, n_layer):
+    """Scales summed without taking magnitudes: the gradients themselves."""
+    loss, g = O.loss_and_grads(p, tok, lab, n_head, n_layer)
+    return loss, g, {k: v.copy() for k, v in g.items()}
+
+
+def _head_only_wte_scales(p, tok, lab, n_head, n_layer):
+    """The wte scale without its embedding part."""
+    loss, g, sc = O.loss_and_grads(p, tok, lab, n_head, n_layer, term_scales=True)
+    xf = O.final_hidden(p, tok, n_head, n_layer)
+    dlog = O.shifted_cross_entropy_backward(O.lm_head(xf, p["wte"]), tok if lab is None else lab)
+    sc["wte"] = np.abs(dlog).reshape(-1, dlog.shape[-1]).T @ np.abs(xf).reshape(-1, xf.shape[-1])
+    return loss, g, sc
+
+
 @pytest.mark.parametrize("check,mutant", [
     (check_layer_norm, _unbiased_ln), (check_layer_norm, _eps_outside_ln), (check_layer_norm, _no_beta_ln),
     (check_gelu, _cubic_sign_gelu), (check_gelu, _no_half_gelu), (check_gelu, O.gelu_erf),
@@ -1196,6 +1237,7 @@ def _unrounded_ln_residual(p, tok, n_head, n_layers, eps=1e-5):
     (check_round_bf16, _truncating_bf16), (check_round_bf16, _ties_away_bf16), (check_round_bf16, _seven_bit_bf16),
     (check_bf16_activation_residual, _rounded_residual_stream),
     (check_bf16_activation_residual, _unrounded_ln_residual),
+    (check_gradient_term_scales, _signed_term_scales), (check_gradient_term_scales, _head_only_wte_scales),
 ])
 def test_pins_catch_planted_mistakes(check, mutant):
     try:
