@@ -101,7 +101,7 @@ def gemm_source_sha() -> str:
 def traffic_record():
     """HBM bytes per lm_head launch from the stored rocprofv3 counter summary, or None when the
     summary is missing or was taken on a different version of the GEMM sources."""
-    path = os.path.join(ROOT, "profiles", "lm_head_traffic.txt")
+    path = os.path.join(ROOT, "profiles", "forward_traffic_gpt2_small_b4_t1024.txt")
     if not os.path.exists(path):
         return None
     kv = {}
@@ -109,27 +109,80 @@ def traffic_record():
         if "=" in line and not line.startswith("#"):
             k, v = line.split("=", 1)
             kv[k.strip()] = v.strip()
-    if kv.get("kernel_source_sha") != gemm_source_sha() or "traffic_bytes_per_launch" not in kv:
+    if kv.get("kernel_source_sha") != gemm_source_sha() or "lm_head_traffic_bytes" not in kv:
         return None
-    return float(kv["traffic_bytes_per_launch"])
+    return float(kv["lm_head_traffic_bytes"])
+
+
+def host_info():
+    """CPU model (from /proc/cpuinfo) and the BLAS library numpy calls (threadpoolctl)."""
+    model = "unknown"
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    blas, threads = "unknown", os.cpu_count() or 1
+    try:
+        from threadpoolctl import threadpool_info
+        for p in threadpool_info():
+            if p.get("user_api") == "blas":
+                blas = f"{p.get('internal_api')} {p.get('version')}"
+                threads = p.get("num_threads", threads)
+                break
+    except Exception:  # pragma: no cover
+        pass
+    return model, blas, int(threads)
 
 
 def cpu_baseline(weights: dict, tokens: np.ndarray, s: synth.ModelShape):
     """Oracle (fp64 numpy) forward of one full sequence of the workload on the host cores."""
     from oracle import gpt2_oracle as O
-    try:
-        from threadpoolctl import threadpool_info
-        cores = max((p.get("num_threads", 1) for p in threadpool_info()), default=1)
-    except Exception:  # pragma: no cover
-        cores = os.cpu_count() or 1
+    model, blas, cores = host_info()
     sample = tokens[:1]
     O.forward(weights, tokens[:1, :4], s.n_head, s.n_layer)  # warm-up on a tiny input
     t0 = time.perf_counter()
     O.forward(weights, sample, s.n_head, s.n_layer)
     dt = time.perf_counter() - t0
-    return {"value": sample.size / dt, "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
+    return {"value": sample.size / dt, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "cpu_model": model, "blas": blas,
             "sample": f"one sequence (B=1, T={sample.shape[1]}) of the workload, full forward incl. logits, "
                       f"fp64 numpy, {dt:.1f} s"}
+
+
+def decode_step_bytes(s: synth.ModelShape, B: int, keys: float) -> float:
+    """HBM bytes one cached decode step reads at least: every block matrix and wte (the tied head)
+    once in bf16, row-major and unpadded (the few-row products stream them; the k-blocked and
+    transposed copies are not touched), the fp32 vectors, one wpe row, and the cached K and V of
+    `keys` positions for every layer and sequence (bf16)."""
+    d, f, L = s.d_model, s.d_mlp, s.n_layer
+    mats = L * (3 * d * d + d * d + f * d + d * f) + s.n_vocab * d
+    vecs = L * (2 * d + 3 * d + d + 2 * d + f + d) + 2 * d
+    return mats * 2.0 + vecs * 4.0 + d * 2.0 + 2.0 * L * B * d * keys * 2.0
+
+
+def random_model(gpt2, shape: synth.ModelShape, seed: int):
+    """A bf16 model of the given shape with weights of the synthetic init's distribution drawn on the
+    GPU (throughput only: the larger models' parity tests use the seeded host generator)."""
+    import torch
+    m = gpt2.GPT2(gpt2.ModelConfig(n_vocab=shape.n_vocab, n_ctx=shape.n_ctx, d_model=shape.d_model,
+                                   n_head=shape.n_head, n_layer=shape.n_layer, d_mlp=shape.d_mlp, dtype="bf16"))
+    gen = torch.Generator(device="cuda").manual_seed(seed)
+    ts = []
+    for _, shp, kind in synth.tensor_specs(shape):
+        if kind in ("emb", "w", "w_res"):
+            std = 0.02 if kind != "w_res" else 0.02 / (2.0 * shape.n_layer) ** 0.5
+            t = torch.randn(shp, generator=gen, device="cuda") * std
+        elif kind == "gamma":
+            t = torch.ones(shp, device="cuda")
+        else:
+            t = torch.zeros(shp, device="cuda")
+        ts.append(t.to(torch.bfloat16))
+    m.load_weights(ts)
+    del ts
+    return m
 
 
 def main():
@@ -142,7 +195,10 @@ def main():
     ap.add_argument("--no-loss", action="store_true", help="skip the fused forward+loss measurement")
     ap.add_argument("--no-decode", action="store_true", help="skip the cached decode measurement")
     ap.add_argument("--no-train", action="store_true", help="skip the forward+backward (gradients) measurement")
-    ap.add_argument("--no-kernels", action="store_true", help="skip the per-kernel breakdown (five extra forwards)")
+    ap.add_argument("--no-kernels", action="store_true",
+                    help="skip the per-kernel breakdown and the cold-cache LayerNorm / embedding figures")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip the isolated-attention, GPT-2 medium and GPT-2 XL measurements")
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="after the timed region, run a plain device-to-device copy of this many bytes three "
                          "times (a known-size reference for hardware traffic counters)")
@@ -251,13 +307,12 @@ def main():
             cur, nxt = nxt, cur
         torch.cuda.synchronize()
         dms = (time.perf_counter() - t3) * 1e3 / n_dec
-        wbytes = m.weight_bytes()
-        kv_row = 2 * shape.n_layer * B * shape.d_model * 2  # bytes of one cached position (K and V, bf16)
-        step_bytes = wbytes + kv_row * (T0 + n_dec / 2)
+        step_bytes = decode_step_bytes(shape, B, T0 + (n_dec + 1) / 2)  # mean keys over the steps
         out["decode"] = {"ms_per_step": dms, "tokens_per_s": B / (dms * 1e-3), "batch": B, "prefill_len": T0,
                          "steps": n_dec, "hbm_bytes_per_step": step_bytes,
                          "hbm_frac": step_bytes / (dms * 1e-3) / 1e9 / PEAK_HBM_GBS,
-                         "what": "greedy cached decode step (next-token argmax), weights + cache read per step"}
+                         "what": "greedy cached decode step (next-token argmax); hbm_bytes_per_step = the row-major bf16 "
+                                 "weights (block matrices and wte), vectors and the cached K/V one step reads"}
 
         # Sampled decoding with the knobs of the pages' generation example (temperature 0.7, top-k 50,
         # top-p 0.95, repetition penalty 1.2 over the whole sequence so far): each step writes the
@@ -330,35 +385,121 @@ def main():
         torch.cuda.synchronize()
         out["copy_bytes"] = args.copy_bytes
 
-    # Every launch kind of the forward, timed with HIP events around each launch of a few extra
-    # forwards (after the timed region): mean duration, algorithmic work and its roofline.
-    reps = 0 if args.no_kernels else 5
-    tot = {}
-    for _ in range(reps):
-        evs = [(raw_event(), raw_event()) for _ in kinds]
-        torch.cuda.synchronize()
-        m.forward_timed(tokens, logits, am, [a.cuda_event for a, _ in evs], [b.cuda_event for _, b in evs], ws)
-        torch.cuda.synchronize()
-        for k, (a, b) in zip(kinds, evs):
-            tot[k] = tot.get(k, 0.0) + a.elapsed_time(b)
+    # Every launch kind of the forward: one launch of each kind (its first in the forward) enqueued
+    # REPS times back to back inside an otherwise ordinary forward, with HIP events around the
+    # group only, so the mean per launch carries no event gaps. Algorithmic work and its roofline
+    # per launch; share = launches x mean / sum over kinds.
+    REPS = 100
     kernels = {}
-    all_ms = sum(tot.values()) / reps if reps else 0.0
-    for k in dict.fromkeys(kinds) if reps else []:
-        n = kinds.count(k)
-        us = tot[k] / reps / n * 1e3
-        bound, work = kernel_work(k, shape, B, T)
-        e = {"launches": n, "avg_us": us, "share": tot[k] / reps / all_ms}
-        if bound == "mfma":
-            e.update(bound="mfma", unit="TFLOP/s", work_per_launch=work, achieved=work / (us * 1e-6) / 1e12,
-                     peak=PEAK_BF16_TFLOPS)
-        elif bound == "hbm":
-            e.update(bound="hbm", unit="GB/s", work_per_launch=work, achieved=work / (us * 1e-6) / 1e9,
-                     peak=PEAK_HBM_GBS)
-        if bound:
-            e["frac"] = e["achieved"] / e["peak"]
-        kernels[k] = e
-    if reps:
+    if not args.no_kernels:
+        first = {}
+        for i, k in enumerate(kinds):
+            first.setdefault(k, i)
+        per = {}
+        for k, i in first.items():
+            e0, e1 = raw_event(), raw_event()  # recorded once so that their handles exist
+            m.forward_repeat(tokens, logits, am, i, REPS, e0.cuda_event, e1.cuda_event, ws)
+            torch.cuda.synchronize()
+            per[k] = e0.elapsed_time(e1) * 1e3 / REPS
+        all_us = sum(per[k] * kinds.count(k) for k in per)
+        for k, us in per.items():
+            n = kinds.count(k)
+            bound, work = kernel_work(k, shape, B, T)
+            e = {"launches": n, "avg_us": us, "share": us * n / all_us, "timing": f"{REPS} back-to-back launches"}
+            if bound == "mfma":
+                e.update(bound="mfma", unit="TFLOP/s", work_per_launch=work, achieved=work / (us * 1e-6) / 1e12,
+                         peak=PEAK_BF16_TFLOPS)
+            elif bound == "hbm":
+                e.update(bound="hbm", unit="GB/s", work_per_launch=work, achieved=work / (us * 1e-6) / 1e9,
+                         peak=PEAK_HBM_GBS)
+            if bound:
+                e["frac"] = e["achieved"] / e["peak"]
+            kernels[k] = e
         out["kernels"] = kernels
+
+        # Cold caches: the LayerNorm (gpt2_layernorm, [B*T, d] fp32 -> bf16) and the embedding (the
+        # forward's first launch) each right after a 512 MiB write that evicts the 256 MB memory-side
+        # cache and the L2s; median of 10.
+        flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+        xs = torch.randn((M, shape.d_model), device="cuda")
+        gam, bet = torch.ones(shape.d_model, device="cuda"), torch.zeros(shape.d_model, device="cuda")
+        yb = torch.empty((M, shape.d_model), dtype=torch.bfloat16, device="cuda")
+        cold = {"ln": [], "embed": []}
+        for _ in range(10):
+            flush.fill_(1)
+            e0, e1 = raw_event(), raw_event()
+            e0.record()
+            gpt2.layernorm(xs, gam, bet, 1e-5, torch.bfloat16, out=yb)
+            e1.record()
+            torch.cuda.synchronize()
+            cold["ln"].append(e0.elapsed_time(e1) * 1e3)
+            flush.fill_(2)
+            e0, e1 = raw_event(), raw_event()
+            m.forward_repeat(tokens, logits, am, 0, 1, e0.cuda_event, e1.cuda_event, ws)
+            torch.cuda.synchronize()
+            cold["embed"].append(e0.elapsed_time(e1) * 1e3)
+        out["cold_cache"] = {}
+        for k, what in (("ln", "gpt2_layernorm on [B*T, d] fp32 -> bf16 (row-major output)"),
+                        ("embed", "the forward's embedding launch")):
+            us = float(np.median(cold[k]))
+            work = kernel_work(k, shape, B, T)[1]
+            out["cold_cache"][k] = {"avg_us": us, "achieved": work / (us * 1e-6) / 1e9, "unit": "GB/s",
+                                    "frac": work / (us * 1e-6) / 1e9 / PEAK_HBM_GBS, "work_per_launch": work,
+                                    "what": what + ", after a 512 MiB write; median of 10 (one launch between events)"}
+        del flush, xs, yb
+
+    if not args.no_configs:
+        # The isolated-attention workload (B=8, H=12, T=1024, dh=64, bf16 Q/K/V ~ N(0,1)): 100
+        # back-to-back gpt2_attention calls between two events.
+        Bq, Hq, Tq = 8, 12, 1024
+        q, k_, v = (torch.randn((Bq, Hq, Tq, 64), device="cuda").to(torch.bfloat16) for _ in range(3))
+        o = torch.empty_like(q)
+        for _ in range(5):
+            gpt2.attention(q, k_, v, o)
+        e0, e1 = raw_event(), raw_event()
+        e0.record()
+        for _ in range(REPS):
+            gpt2.attention(q, k_, v, o)
+        e1.record()
+        torch.cuda.synchronize()
+        aus = e0.elapsed_time(e1) * 1e3 / REPS
+        afl = 2.0 * 2.0 * Bq * Hq * 64 * Tq * (Tq + 1) / 2.0
+        out["attention_config"] = {
+            "workload": "causal MHA alone, B=8 H=12 T=1024 dh=64, bf16", "avg_us": aus,
+            "tokens_per_s": Bq * Tq / (aus * 1e-6),
+            "roofline": {"bound": "mfma", "achieved": afl / (aus * 1e-6) / 1e12, "peak": PEAK_BF16_TFLOPS,
+                         "unit": "TFLOP/s", "frac": afl / (aus * 1e-6) / 1e12 / PEAK_BF16_TFLOPS,
+                         "flops_per_launch": afl},
+            "timing": f"{REPS} back-to-back calls"}
+        del q, k_, v, o
+        # GPT-2 medium (B=8) and XL (B=4) forwards at T=1024
+        for name in ("medium", "xl"):
+            if name == args.workload:
+                continue
+            sh, Bm, Tm = WORKLOADS[name]
+            mm = random_model(gpt2, sh, 11)
+            tk = torch.from_numpy(synth.make_tokens(Bm, Tm, sh.n_vocab)).cuda()
+            lg = torch.empty((Bm, Tm, sh.n_vocab), dtype=torch.float32, device="cuda")
+            amx = torch.empty((Bm, Tm), dtype=torch.int32, device="cuda")
+            wsm = mm.workspace(Bm, Tm)
+            for _ in range(3):
+                mm.forward(tk, lg, amx, wsm)
+            n_m = 10
+            torch.cuda.synchronize()
+            t6 = time.perf_counter()
+            for _ in range(n_m):
+                mm.forward(tk, lg, amx, wsm)
+            torch.cuda.synchronize()
+            mms = (time.perf_counter() - t6) * 1e3 / n_m
+            fl = forward_flops(sh, Bm, Tm)
+            out[f"forward_{name}"] = {
+                "workload": f"GPT-2 {name} forward, B={Bm} T={Tm}, bf16 operands / fp32 accumulation, fp32 logits",
+                "ms_per_step": mms, "tokens_per_s": Bm * Tm / (mms * 1e-3), "steps": n_m,
+                "roofline": {"bound": "mfma", "achieved": fl / (mms * 1e-3) / 1e12, "peak": PEAK_BF16_TFLOPS,
+                             "unit": "TFLOP/s", "frac": fl / (mms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+                             "flops_per_step": fl, "what": "whole forward"}}
+            del mm, lg, amx, wsm
+            torch.cuda.empty_cache()
 
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, tok_np, shape)

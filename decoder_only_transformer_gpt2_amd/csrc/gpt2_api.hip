@@ -199,6 +199,10 @@ struct Sequencer {
     int cap = 0;
     bool dry = false;
     int idx = 0;
+    // launch rep_idx is enqueued rep_n times back to back, with rep_before / rep_after around the
+    // group (for timing one kernel without per-launch event gaps)
+    int rep_idx = -1, rep_n = 1;
+    hipEvent_t rep_before = nullptr, rep_after = nullptr;
 
     template <class F>
     hipError_t run(int kind, F&& launch) {
@@ -209,7 +213,14 @@ struct Sequencer {
         }
         const bool slot = idx < n_slots;
         if (slot && before && before[idx] && hipEventRecord(before[idx], s) != hipSuccess) return hipErrorUnknown;
-        hipError_t e = launch();
+        hipError_t e = hipSuccess;
+        if (idx == rep_idx) {
+            if (rep_before && hipEventRecord(rep_before, s) != hipSuccess) return hipErrorUnknown;
+            for (int r = 0; r < rep_n && e == hipSuccess; ++r) e = launch();
+            if (e == hipSuccess && rep_after) e = hipEventRecord(rep_after, s);
+        } else {
+            e = launch();
+        }
         if (e == hipSuccess && slot && after && after[idx]) e = hipEventRecord(after[idx], s);
         ++idx;
         return e;
@@ -840,6 +851,21 @@ gpt2_status gpt2_forward_timed(const gpt2_model* m, const int32_t* tokens, int32
     q.before = ev_before;
     q.after = ev_after;
     q.n_slots = n_slots;
+    return enqueue_forward(m, tokens, B, T, logits, argmax, static_cast<char*>(ws_dev), q);
+}
+
+gpt2_status gpt2_forward_repeat(const gpt2_model* m, const int32_t* tokens, int32_t B, int32_t T, float* logits,
+                                int32_t* argmax, void* ws_dev, size_t ws_bytes, hipStream_t s, int32_t launch,
+                                int32_t repeats, hipEvent_t ev_before, hipEvent_t ev_after) {
+    const gpt2_status st = check_run_args(m, tokens, B, T, logits, ws_dev, ws_bytes);
+    if (st != GPT2_OK) return st;
+    if (launch < 0 || launch >= gpt2_forward_launches(m, argmax != nullptr, nullptr, 0) || repeats < 1)
+        return GPT2_EINVAL;
+    Sequencer q{s};
+    q.rep_idx = launch;
+    q.rep_n = repeats;
+    q.rep_before = ev_before;
+    q.rep_after = ev_after;
     return enqueue_forward(m, tokens, B, T, logits, argmax, static_cast<char*>(ws_dev), q);
 }
 

@@ -49,6 +49,7 @@ SIGNATURES = {
     "gpt2_forward_debug": (_I32, [_P, _P, _I32, _I32, _I32, _P, _P, _SZ, _P]),
     "gpt2_check": (_I32, [_P, _P, _I32, _I32, _P]),
     "gpt2_forward_launches": (_I32, [_P, _I32, ctypes.POINTER(_I32), _I32]),
+    "gpt2_forward_repeat": (_I32, [_P, _P, _I32, _I32, _P, _P, _P, _SZ, _P, _I32, _I32, _P, _P]),
     "gpt2_forward_timed": (_I32, [_P, _P, _I32, _I32, _P, _P, _P, _SZ, _P, ctypes.POINTER(_P), ctypes.POINTER(_P), _I32]),
     "gpt2_attention": (_I32, [_P, _I64P, _P, _I64P, _P, _I64P, _P, _I64P, _I32, _I32, _I32, _I32, _I32, _P]),
     "gpt2_layernorm": (_I32, [_P, _P, _P, _P, _I32, _I32, _F, _I32, _P]),
@@ -412,6 +413,16 @@ class GPT2:
                                         _stream(stream), eb, ea, n), "gpt2_forward_timed")
         return logits, argmax
 
+    def forward_repeat(self, tokens: torch.Tensor, logits: torch.Tensor, argmax: torch.Tensor | None, launch: int,
+                       repeats: int, before=None, after=None, ws: torch.Tensor | None = None, stream=None):
+        """forward() with launch number `launch` enqueued `repeats` times back to back and raw
+        hipEvent_t handles (ints or None) recorded around that group."""
+        B, T = tokens.shape
+        ws = self.workspace(B, T) if ws is None else ws
+        _check(lib().gpt2_forward_repeat(self._h, _ptr(tokens), B, T, _ptr(logits), _ptr(argmax), _ptr(ws), ws.numel(),
+                                         _stream(stream), launch, repeats, before, after), "gpt2_forward_repeat")
+        return logits, argmax
+
     def forward_debug(self, tokens: torch.Tensor, n_layers: int, ws: torch.Tensor | None = None, stream=None):
         _require_cuda(tokens)
         B, T = tokens.shape
@@ -487,10 +498,14 @@ def attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor
 
 
 def layernorm(x: torch.Tensor, gamma: torch.Tensor, beta: torch.Tensor, eps: float = 1e-5,
-              out_dtype: torch.dtype = torch.bfloat16, stream=None):
-    _require_cuda(x, gamma, beta)
+              out_dtype: torch.dtype = torch.bfloat16, stream=None, out: torch.Tensor | None = None):
+    """LayerNorm of the rows of fp32 x [M, n]; out (if given) must be a contiguous [M, n] tensor of
+    out_dtype."""
+    _require_cuda(x, gamma, beta, out)
     M, n = x.shape
-    y = torch.empty((M, n), dtype=out_dtype, device=x.device)
+    y = torch.empty((M, n), dtype=out_dtype, device=x.device) if out is None else out
+    if y.dtype != out_dtype or tuple(y.shape) != (M, n) or not y.is_contiguous():
+        raise ValueError("out must be a contiguous [M, n] tensor of out_dtype")
     _check(lib().gpt2_layernorm(_ptr(x), _ptr(gamma), _ptr(beta), _ptr(y), M, n, eps,
                                 BF16 if out_dtype == torch.bfloat16 else F32, _stream(stream)), "gpt2_layernorm")
     return y

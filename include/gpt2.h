@@ -212,6 +212,17 @@ gpt2_status gpt2_forward_timed(const gpt2_model* m, const int32_t* tokens_dev, i
                                hipStream_t stream, hipEvent_t* ev_before, hipEvent_t* ev_after,
                                int32_t n_slots);
 
+/* gpt2_forward with launch number `launch` (0-based, in the order of gpt2_forward_launches)
+ * enqueued `repeats` times back to back, with the caller's events ev_before / ev_after (either may
+ * be NULL) recorded around that group: for timing one kernel of the forward in the forward's own
+ * data layout, with no event between its launches. A repeated launch that accumulates into its
+ * output (the residual projections) leaves results that are not the forward's; GPT2_EINVAL for a
+ * launch number outside the forward or repeats < 1. Otherwise as gpt2_forward. */
+gpt2_status gpt2_forward_repeat(const gpt2_model* m, const int32_t* tokens_dev, int32_t B, int32_t T,
+                                float* logits_dev, int32_t* argmax_dev, void* ws_dev, size_t ws_bytes,
+                                hipStream_t stream, int32_t launch, int32_t repeats, hipEvent_t ev_before,
+                                hipEvent_t ev_after);
+
 /* Synchronise stream, then report GPT2_ETOKEN if the last forward that used ws_dev saw a token
  * id (or, for gpt2_forward_loss, a label other than -100) outside [0, n_vocab), else GPT2_OK.
  * B and T must be those of that forward. */
