@@ -15,8 +15,9 @@
 // the probabilities are already in the operand layout of the second product O^T += V^T P^T.
 // Online softmax in fp32 on the raw scores: exp2(s*c - m*c) is one FMA and one v_exp_f32 per score
 // (c = scale * log2 e); the reference maximum moves only when a query's maximum grows by more than
-// 2^8, so the accumulators are rarely rescaled. The row sums come from the matrix unit as
-// ones x P^T, over the same bf16 probabilities that weight V. Tiles wholly above a wavefront's
+// 2^8, so the accumulators are rarely rescaled. Each lane sums its own probabilities (fp32) into a
+// partial denominator; the four partials of a query are added once, after the key loop (a matrix-
+// unit sum as ones x P^T took eight more registers, and the kernel spilled). Tiles wholly above a wavefront's
 // diagonal are skipped; only tiles that cross it are masked (selects). Workgroups are issued
 // longest-first (last query tiles first) to even out the causal imbalance. When the grid is small,
 // a workgroup runs two groups of wavefronts over the same queries, each taking every other key
@@ -29,8 +30,14 @@ namespace {
 
 constexpr int KT = 64;        // keys per LDS tile
 constexpr int DH = 64;        // head size
-constexpr int VTS = KT + 4;   // row stride (elements) of the transposed V tile: 34 words, so the
-                              // 8-byte fragment reads of 16 rows fall on distinct banks
+constexpr int VTS = KT + 8;   // row stride (elements) of the transposed V tile: 36 words
+// Element offset of the key-pair word `w` (keys 2w, 2w+1) of row d of the transposed V tile: the
+// word index is XOR-ed with 8 * (d / 16), which with the 36-word stride puts both the transposing
+// 4-byte writes (eight d rows x eight key pairs per instruction) and the 8-byte fragment reads
+// (sixteen d rows x four key quads per half-wave) on 64 distinct banks. (A 34-word stride without
+// the XOR conflicted two-way on every write: a third of the kernel's LDS cycles.) The XOR moves
+// whole groups of eight words, so the four keys of a fragment read stay adjacent.
+__device__ __forceinline__ int vtw(int d, int w) { return d * VTS + 2 * (w ^ ((d >> 4) << 3)); }
 // Maximum over the four lanes L, L^16, L^32, L^48 (the four 16-lane rows). Only the rare
 // rescale path needs it. (The gfx950 row-swap builtins would avoid the LDS crossbar, but this
 // toolchain miscompiles them when both operands are the same value.)
@@ -91,10 +98,8 @@ __global__ __launch_bounds__(64 * WAVES * G, 4) void attn_bf16_kernel(
             qf[qb][kk] = __builtin_bit_cast(bf16x8_t, u);
         }
 
-    const u32x4_t ones_u = {0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};  // bf16 1.0 x 8
-    const bf16x8_t ones = __builtin_bit_cast(bf16x8_t, ones_u);
     f32x4_t oacc[NQ][4];  // [query block][d fragment]; rows d = df*16 + 4*g4 + e, column = query
-    f32x4_t lacc[NQ];     // every row: the running denominator of the column's query
+    float lsum[NQ];       // this lane's part of the running denominator (its keys 4*g4 .. of each block)
     float mrow[NQ];       // reference maximum of the raw scores of this lane's queries
     float mthr[NQ];       // mrow + 8 / scale_log2: scores above it move the reference
     float mbias[NQ];      // mrow * scale_log2 (0 while mrow is -inf)
@@ -102,7 +107,7 @@ __global__ __launch_bounds__(64 * WAVES * G, 4) void attn_bf16_kernel(
     for (int qb = 0; qb < NQ; ++qb) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) oacc[qb][i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-        lacc[qb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        lsum[qb] = 0.f;
         mrow[qb] = -INFINITY;
         mthr[qb] = -INFINITY;
         mbias[qb] = 0.f;
@@ -147,8 +152,8 @@ __global__ __launch_bounds__(64 * WAVES * G, 4) void attn_bf16_kernel(
 #pragma unroll
             for (int w = 0; w < 4; ++w) {
                 const uint32_t a = vr[2 * i][w], bb = vr[2 * i + 1][w];  // d = vdc*8 + 2w, +1 of keys 2kp, 2kp+1
-                *reinterpret_cast<uint32_t*>(&tV[(vdc * 8 + 2 * w) * VTS + 2 * kp]) = (a & 0xffffu) | (bb << 16);
-                *reinterpret_cast<uint32_t*>(&tV[(vdc * 8 + 2 * w + 1) * VTS + 2 * kp]) = (a >> 16) | (bb & 0xffff0000u);
+                *reinterpret_cast<uint32_t*>(&tV[vtw(vdc * 8 + 2 * w, kp)]) = (a & 0xffffu) | (bb << 16);
+                *reinterpret_cast<uint32_t*>(&tV[vtw(vdc * 8 + 2 * w + 1, kp)]) = (a >> 16) | (bb & 0xffff0000u);
             }
         }
     };
@@ -228,7 +233,7 @@ __global__ __launch_bounds__(64 * WAVES * G, 4) void attn_bf16_kernel(
                         mbias[qb] = mnew == -INFINITY ? 0.f : mnew * scale_log2;
 #pragma unroll
                         for (int df = 0; df < 4; ++df) oacc[qb][df] *= alpha;
-                        lacc[qb] *= alpha;
+                        lsum[qb] *= alpha;
                     }
                 }
                 // P^T in the B-operand layout: slot j of a lane holds key 32*hh + 4*g4 + j (j < 4) or
@@ -249,14 +254,14 @@ __global__ __launch_bounds__(64 * WAVES * G, 4) void attn_bf16_kernel(
                     pu[2] = pack_bf16x2(p[1][0], p[1][1]);
                     pu[3] = pack_bf16x2(p[1][2], p[1][3]);
                     pf[qb] = __builtin_bit_cast(bf16x8_t, pu);
-                    lacc[qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pf[qb], lacc[qb], 0, 0, 0);
+                    lsum[qb] += ((p[0][0] + p[0][1]) + (p[0][2] + p[0][3])) + ((p[1][0] + p[1][1]) + (p[1][2] + p[1][3]));
                 }
                 // O^T[d, query] += V^T[d, key] P^T[key, query], 32 keys per MFMA
 #pragma unroll
                 for (int df = 0; df < 4; ++df) {
-                    const uint16_t* vrow = &tV[(df * 16 + r16) * VTS + 32 * hh + 4 * g4];
-                    const u32x2_t lo = *reinterpret_cast<const u32x2_t*>(vrow);
-                    const u32x2_t hi = *reinterpret_cast<const u32x2_t*>(vrow + 16);
+                    const int vd = df * 16 + r16;
+                    const u32x2_t lo = *reinterpret_cast<const u32x2_t*>(&tV[vtw(vd, 16 * hh + 2 * g4)]);
+                    const u32x2_t hi = *reinterpret_cast<const u32x2_t*>(&tV[vtw(vd, 16 * hh + 8 + 2 * g4)]);
                     const bf16x8_t vf = __builtin_bit_cast(bf16x8_t, u32x4_t{lo[0], lo[1], hi[0], hi[1]});
 #pragma unroll
                     for (int qb = 0; qb < NQ; ++qb)
@@ -271,6 +276,12 @@ __global__ __launch_bounds__(64 * WAVES * G, 4) void attn_bf16_kernel(
         __syncthreads();
     }
 
+    // the denominator of query column r16: the four 16-lane rows hold its four key quarters
+#pragma unroll
+    for (int qb = 0; qb < NQ; ++qb) {
+        lsum[qb] += __shfl_xor(lsum[qb], 16, GPT2_WAVE);
+        lsum[qb] += __shfl_xor(lsum[qb], 32, GPT2_WAVE);
+    }
     if constexpr (G > 1) {
         // groups 1..G-1 hand their (accumulators, denominator, reference maximum) to group 0,
         // which rescales every part to the common maximum and adds them in group order. Merge
@@ -286,7 +297,7 @@ __global__ __launch_bounds__(64 * WAVES * G, 4) void attn_bf16_kernel(
                 for (int df = 0; df < 4; ++df)
 #pragma unroll
                     for (int e = 0; e < 4; ++e) at(grp, qb * 18 + df * 4 + e) = oacc[qb][df][e];
-                at(grp, qb * 18 + 16) = lacc[qb][0];
+                at(grp, qb * 18 + 16) = lsum[qb];
                 at(grp, qb * 18 + 17) = mrow[qb];
             }
         }
@@ -300,7 +311,7 @@ __global__ __launch_bounds__(64 * WAVES * G, 4) void attn_bf16_kernel(
             const float a0 = mrow[qb] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((mrow[qb] - mn) * scale_log2);
 #pragma unroll
             for (int df = 0; df < 4; ++df) oacc[qb][df] *= a0;
-            lacc[qb][0] *= a0;
+            lsum[qb] *= a0;
 #pragma unroll
             for (int g = 1; g < G; ++g) {
                 const float mg = at(g, qb * 18 + 17);
@@ -309,7 +320,7 @@ __global__ __launch_bounds__(64 * WAVES * G, 4) void attn_bf16_kernel(
                 for (int df = 0; df < 4; ++df)
 #pragma unroll
                     for (int e = 0; e < 4; ++e) oacc[qb][df][e] += at(g, qb * 18 + df * 4 + e) * ag;
-                lacc[qb][0] += at(g, qb * 18 + 16) * ag;
+                lsum[qb] += at(g, qb * 18 + 16) * ag;
             }
         }
     }
@@ -318,7 +329,7 @@ __global__ __launch_bounds__(64 * WAVES * G, 4) void attn_bf16_kernel(
     for (int qb = 0; qb < NQ; ++qb) {
         const int qi = qw + 16 * qb + r16;
         if (qi < T) {
-            const float inv = 1.0f / lacc[qb][0];
+            const float inv = 1.0f / lsum[qb];
             uint16_t* Ob = O + b * osb + h * osh + qi * ost;
 #pragma unroll
             for (int df = 0; df < 4; ++df) {
