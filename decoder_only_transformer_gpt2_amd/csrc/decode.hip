@@ -1,4 +1,4 @@
-// Incremental decoding with a key/value cache ([手写] §6.3 and [实战] §4.2: generation feeds one new
+// Incremental decoding with a key/value cache ([手写] §6.3 and [解析] §4.2: generation feeds one new
 // token per step; the keys and values of the earlier positions do not change, so they are kept
 // instead of recomputed). Per layer the cache holds K and V as [B][H][n_ctx][64] in the compute
 // dtype. A decode step's query attends to keys 0 .. pos: causality makes this the last row of the

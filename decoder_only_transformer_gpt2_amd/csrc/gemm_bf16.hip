@@ -24,19 +24,19 @@ namespace {
 // tiles two per CU 409 us).
 int choose_cfg(int M, int N, int K, bool kb) {
     auto tiles = [&](int bm, int bn) { return (long)((M + bm - 1) / bm) * ((N + bn - 1) / bn); };
-    if (tiles(256, 256) >= 4 * 256) return 21;  // vocabulary projection
+    if (tiles(256, 256) >= 4 * 256) return 2;  // vocabulary projection
     // narrow outputs of very many rows (the wte weight gradient, M = n_vocab): large tiles, since
     // the grid fills the CUs twice over anyway and each tile re-reads less through L2
-    if (N <= 1024 && tiles(256, 192) >= 512) return 16;
+    if (N <= 1024 && tiles(256, 192) >= 512) return 1;
     // narrow outputs on k-blocked operands (attn.c_proj, mlp.c_proj): 128 x 96 tiles of eight
     // wavefronts (two per SIMD, 32 x 48 each), one wave of 256 workgroups
-    if (N <= 1024 && kb && tiles(128, 96) >= 192) return 28;
-    if (N <= 1024) return 12;
-    if (tiles(192, 256) < 128) return 12;  // few rows (weight gradients, short prompts): fill the CUs
-    if (tiles(192, 256) <= 256) return 22;
+    if (N <= 1024 && kb && tiles(128, 96) >= 192) return 5;
+    if (N <= 1024) return 0;
+    if (tiles(192, 256) < 128) return 0;  // few rows (weight gradients, short prompts): fill the CUs
+    if (tiles(192, 256) <= 256) return 3;
     // k-blocked operands stream at full cache-line width, which favours the deeper 32-wide ring
-    if (kb && tiles(256, 192) <= 256) return 23;
-    return 16;
+    if (kb && tiles(256, 192) <= 256) return 4;
+    return 1;
 }
 
 }  // namespace
@@ -58,12 +58,12 @@ hipError_t gemm_bf16(const uint16_t* A, const uint16_t* W, const float* bias, vo
     switch (choose_cfg(M, N, K, kb)) {
 #define GPT2_CFG(i) \
     case i: return gemm_bf16_cfg_##i(A, W, bias, C, M, N, K, ldc, epi, gelu_erf, a_rows, w_rows, c_kb_rows, ho, s, kb);
-        GPT2_CFG(12)
-        GPT2_CFG(16)
-        GPT2_CFG(22)
-        GPT2_CFG(23)
-        GPT2_CFG(21)
-        GPT2_CFG(28)
+        GPT2_CFG(0)
+        GPT2_CFG(1)
+        GPT2_CFG(2)
+        GPT2_CFG(3)
+        GPT2_CFG(4)
+        GPT2_CFG(5)
 #undef GPT2_CFG
     }
     return hipErrorInvalidValue;

@@ -484,42 +484,15 @@ struct TileCfg {
     int bm, bn, bk, stages, wgm, wgn;
 };
 
-// Instantiated tile shapes.
+// Instantiated tile shapes (the ones the dispatcher in gemm_bf16.hip chooses).
 constexpr TileCfg kCfgs[] = {
-    {256, 256, 32, 4, 2, 4},  // 0: 8 waves, 128 KB ring
-    {256, 256, 64, 2, 2, 4},  // 1
-    {256, 192, 32, 4, 2, 2},  // 2: 4 waves
-    {128, 128, 32, 4, 2, 2},  // 3: 64 KB ring, 2 workgroups per CU
-    {128, 128, 64, 2, 2, 2},  // 4
-    {128, 64, 32, 4, 2, 2},   // 5: 48 KB ring, 3 per CU
-    {256, 128, 32, 4, 2, 4},  // 6
-    {128, 96, 64, 2, 2, 2},   // 7
-    {256, 256, 32, 5, 2, 4},  // 8: 160 KB ring
-    {192, 256, 32, 4, 2, 2},  // 9: 4 waves
-    {128, 96, 64, 3, 2, 2},   // 10
-    {128, 96, 64, 4, 2, 2},   // 11
-    {64, 96, 64, 4, 2, 2},    // 12
-    {128, 64, 64, 4, 2, 2},   // 13
-    {256, 256, 32, 4, 2, 2},  // 14: 4 waves, 128 x 128 each
-    {128, 128, 64, 4, 2, 2},  // 15
-    {256, 192, 64, 2, 2, 4},  // 16: 8 waves, 128 x 48 each
-    {128, 288, 64, 2, 2, 2},  // 17
-    {256, 128, 64, 2, 2, 4},  // 18
-    {192, 256, 64, 2, 2, 4},  // 19: 8 waves, 96 x 64 each
-    {256, 128, 32, 3, 2, 2},  // 20: 4 waves, 128 x 64 each, 72 KB ring: 2 workgroups per CU
-    {128, 256, 32, 3, 2, 2},  // 21: 4 waves, 64 x 128 each, 72 KB ring: 2 workgroups per CU
-    {192, 256, 32, 5, 2, 4},  // 22: 8 waves, 140 KB ring
-    {256, 192, 32, 5, 2, 4},  // 23: 8 waves, 140 KB ring
-    {64, 96, 32, 6, 2, 2},    // 24: 4 waves, 60 KB ring
-    {128, 96, 32, 5, 2, 2},   // 25: 4 waves, 70 KB ring
-    {128, 128, 32, 5, 2, 2},  // 26: 4 waves, 80 KB ring
-    {256, 128, 32, 5, 2, 4},  // 27: 8 waves, 120 KB ring
-    {128, 96, 64, 4, 4, 2},   // 28: 8 waves (4 x 2), 32 x 48 each, 112 KB ring
-    {64, 192, 64, 4, 2, 4},   // 29: 8 waves, 32 x 48 each, 128 KB ring
-    {256, 192, 32, 5, 4, 4},  // 30: 16 waves, 64 x 48 each, 140 KB ring
-    {192, 256, 32, 5, 4, 4},  // 31: 16 waves, 48 x 64 each, 140 KB ring
+    {64, 96, 64, 4, 2, 2},    // 0: 4 waves (32 x 48 each), 2 workgroups per CU: narrow row-major products
+    {256, 192, 64, 2, 2, 4},  // 1: 8 waves (128 x 48): narrow outputs of very many rows (wte gradient)
+    {128, 256, 32, 3, 2, 2},  // 2: 4 waves (64 x 128), 72 KB ring, 2 per CU: vocabulary projection
+    {192, 256, 32, 5, 2, 4},  // 3: 8 waves (96 x 64), 140 KB ring: N = 2304 (c_attn)
+    {256, 192, 32, 5, 2, 4},  // 4: 8 waves (128 x 48), 140 KB ring: N = 3072 on k-blocked operands (c_fc)
+    {128, 96, 64, 4, 4, 2},   // 5: 8 waves (4 x 2, 32 x 48 each), 112 KB ring: narrow k-blocked (c_proj)
 };
-[[maybe_unused]] constexpr int kNumCfgs = sizeof(kCfgs) / sizeof(kCfgs[0]);
 
 // One epilogue's launch, with the K loop fully unrolled for the step counts that occur: the
 // forward's k-blocked projections (K = 768 and 3072; for GPT-2 medium and XL the vocabulary
@@ -615,11 +588,11 @@ hipError_t launch_cfg(const uint16_t* A, const uint16_t* W, const float* bias, v
                                                                                 ho, s);                         \
     }
 // the configurations the library dispatches to
-GPT2_GEMM_DECLARE_CFG(12)
-GPT2_GEMM_DECLARE_CFG(16)
-GPT2_GEMM_DECLARE_CFG(22)
-GPT2_GEMM_DECLARE_CFG(23)
-GPT2_GEMM_DECLARE_CFG(21)
-GPT2_GEMM_DECLARE_CFG(28)
+GPT2_GEMM_DECLARE_CFG(0)
+GPT2_GEMM_DECLARE_CFG(1)
+GPT2_GEMM_DECLARE_CFG(2)
+GPT2_GEMM_DECLARE_CFG(3)
+GPT2_GEMM_DECLARE_CFG(4)
+GPT2_GEMM_DECLARE_CFG(5)
 
 }  // namespace gpt2k

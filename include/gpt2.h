@@ -8,6 +8,7 @@
  *
  * Pages the operations are defined on (titles as printed on the pages):
  *   [手写] "从零手写GPT-2：PyTorch实现Transformer解码器核心模块"
+ *   [实战] "GPT2模型开发实战：从原理到部署全解析"
  *   [解析] "GPT-2模型架构解析与实现指南"
  *   [复现] "复现GPT-2 124M"
  *   [指南] "从零实现 GPT-2：PyTorch 版大语言模型构建指南"
@@ -158,7 +159,7 @@ gpt2_status gpt2_forward_loss(const gpt2_model* m, const int32_t* tokens_dev, co
                               int32_t B, int32_t T, float* nll_dev, float* loss_dev, void* ws_dev,
                               size_t ws_bytes, hipStream_t stream);
 
-/* Cached incremental decoding ([手写] §6.3 greedy generation; [实战] §4.2): the keys and values of
+/* Cached incremental decoding ([手写] §6.3 greedy generation; [解析] §4.2 KV cache): the keys and values of
  * every layer are kept in a caller-owned cache so that each new token costs one position of the
  * forward. Layout: for each layer l, K then V, each [B][n_head][n_ctx][64] in the compute dtype
  * (bf16 or fp32). Positions are shared by the batch: every sequence has the same length.
