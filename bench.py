@@ -1,6 +1,6 @@
 """Forward-pass throughput of the HIP GPT-2 library on one MI355X.
 
-python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload small|medium|xl] [--no-cpu-baseline] [--no-loss] [--no-decode] [--no-train] [--no-kernels]
+python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload small|medium|xl] [--no-cpu-baseline] [--no-loss] [--no-decode] [--no-train] [--no-kernels] [--configs all|attention|none]
 
 One step = one gpt2_forward over a batch of synthetic token ids already resident in HBM:
 embedding, every block, ln_f, the tied lm_head (fp32 logits) and the fused argmax. Weights are the
@@ -197,8 +197,9 @@ def main():
     ap.add_argument("--no-train", action="store_true", help="skip the forward+backward (gradients) measurement")
     ap.add_argument("--no-kernels", action="store_true",
                     help="skip the per-kernel breakdown and the cold-cache LayerNorm / embedding figures")
-    ap.add_argument("--no-configs", action="store_true",
-                    help="skip the isolated-attention, GPT-2 medium and GPT-2 XL measurements")
+    ap.add_argument("--configs", choices=("all", "attention", "none"), default="all",
+                    help="the other workloads measured after the headline: the isolated attention (B=8 H=12 "
+                         "T=1024) and the GPT-2 medium / XL forwards (all), the attention alone, or none")
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="after the timed region, run a plain device-to-device copy of this many bytes three "
                          "times (a known-size reference for hardware traffic counters)")
@@ -448,7 +449,7 @@ def main():
                                     "what": what + ", after a 512 MiB write; median of 10 (one launch between events)"}
         del flush, xs, yb
 
-    if not args.no_configs:
+    if args.configs != "none":
         # The isolated-attention workload (B=8, H=12, T=1024, dh=64, bf16 Q/K/V ~ N(0,1)): 100
         # back-to-back gpt2_attention calls between two events.
         Bq, Hq, Tq = 8, 12, 1024
@@ -473,7 +474,7 @@ def main():
             "timing": f"{REPS} back-to-back calls"}
         del q, k_, v, o
         # GPT-2 medium (B=8) and XL (B=4) forwards at T=1024
-        for name in ("medium", "xl"):
+        for name in (("medium", "xl") if args.configs == "all" else ()):
             if name == args.workload:
                 continue
             sh, Bm, Tm = WORKLOADS[name]

@@ -273,6 +273,23 @@ int colsum_blocks(int R);
 hipError_t transpose_colsum(const float* src, long lds, int R, int C, uint16_t* dst, long ldd, int Rp, float* part,
                             float* out, hipStream_t s);
 hipError_t colsum(const float* src, long ld, int R, int C, float* part, float* out, hipStream_t s);
+// transpose_colsum without the final reduction: the partial column sums (ceil(Rp / 64) rows of C)
+// are left in part for a later colsum_reduce_multi; requires 16-byte strides and pointers.
+hipError_t transpose_colsum_partials(const float* src, long lds, int R, int C, uint16_t* dst, long ldd, int Rp,
+                                     float* part, hipStream_t s);
+// out[c] = sum over b < nb of part[b * C + c] for up to kColsumSegs independent (part, nb, C, out)
+// segments in one launch, each in the fixed order of colsum.
+struct ColsumSeg {
+    const float* part;
+    float* out;
+    int nb, C;
+};
+constexpr int kColsumSegs = 64;
+struct ColsumSegs {
+    ColsumSeg seg[kColsumSegs];
+    int n = 0;
+};
+hipError_t colsum_reduce_multi(const ColsumSegs& segs, hipStream_t s);
 // LayerNorm backward on rows of x with output gradient dy (fp32 [M, d]): dx += the input gradient,
 // dgamma / dbeta = column sums (pg, pb hold ln_backward_blocks(M) * d floats each: partial rows).
 int ln_backward_blocks(int M);

@@ -434,7 +434,8 @@ struct TrainLayout {
     WorkspaceLayout fw;
     size_t layer0, per_layer;
     size_t l_xin, l_xmid, l_a1, l_qkv, l_o, l_a2, l_u, l_h;  // inside one layer's block
-    size_t xfin, xf, logits, dx, dbuf, dbuf2, dact, dT, xT, wT, wteT, dlog, dlogT, part, lnpg, lnpb, lse, dvec, nll, cnt;
+    size_t xfin, xf, logits, dx, dbuf, dbuf2, dact, dT, xT, wT, wteT, dlog, dlogT, part, bpart, lnpg, lnpb, lse, dvec, nll,
+        cnt;
     size_t total;
     int64_t M, Mp, Mk, Vp, Vr, wide, rows_w, rows_dT, rows_x;
 };
@@ -484,6 +485,8 @@ TrainLayout train_layout(const gpt2_model* m, int B, int T) {
     L.dlog = take(L.Mp * L.Vp * as);
     L.dlogT = take(L.Vr * L.Mk * as);
     L.part = take((size_t)std::max<int64_t>(gpt2k::colsum_blocks((int)L.M), (L.Mk + 63) / 64) * L.wide * 4);
+    // bf16: the bias gradients' partial column sums of every layer, reduced in one launch at the end
+    L.bpart = take(is_bf16(m) ? (size_t)((L.Mk + 63) / 64) * (3 * d + d + f + d) * c.n_layer * 4 : 0);
     L.lnpg = take((size_t)gpt2k::ln_backward_blocks((int)L.M) * d * 4);
     L.lnpb = take((size_t)gpt2k::ln_backward_blocks((int)L.M) * d * 4);
     L.lse = take((size_t)B * c.n_head * T * 4);
@@ -596,12 +599,18 @@ gpt2_status enqueue_backward(const gpt2_model* m, const int32_t* tokens, int B, 
         return gpt2k::convert(src, false, dst, bf, (long)M * Cc, (long)Mp * Cc, s);
     };
     // the weight gradient and the input gradient of y = x W^T + b for output gradient dy (fp32 [M, n_out])
+    // bf16: the bias gradients' partial column sums, one region per bias, reduced together at the end
+    std::vector<gpt2k::ColsumSeg> bsegs;
+    float* bpart = reinterpret_cast<float*>(ws + L.bpart);
+    const int nbp = (int)((Mk + 63) / 64);
     auto linear_back = [&](const float* dy, int n_out, const void* x_act, int n_in, int widx, float* dx_out) -> hipError_t {
         hipError_t e;
-        if (bf) {  // bias gradient (column sums of dy) from the same pass as the transpose of dy
-            if ((e = gpt2k::transpose_colsum(dy, n_out, M, n_out, reinterpret_cast<uint16_t*>(dT), Mk, Mk, part,
-                                             G(widx + 1), s)) != hipSuccess)
+        if (bf) {  // bias gradient partials (column sums of dy) from the same pass as the transpose of dy
+            if ((e = gpt2k::transpose_colsum_partials(dy, n_out, M, n_out, reinterpret_cast<uint16_t*>(dT), Mk, Mk,
+                                                      bpart, s)) != hipSuccess)
                 return e;
+            bsegs.push_back({bpart, G(widx + 1), nbp, n_out});
+            bpart += (size_t)nbp * n_out;
         } else {
             if ((e = gpt2k::colsum(dy, n_out, M, n_out, part, G(widx + 1), s)) != hipSuccess) return e;
             if ((e = tr(dy, false, n_out, M, n_out, dT, Mk, Mk)) != hipSuccess) return e;
@@ -648,6 +657,12 @@ gpt2_status enqueue_backward(const gpt2_model* m, const int32_t* tokens, int B, 
         GPT2_HIP(linear_back(dbuf2, 3 * d, lay(l, L.l_a1), d, I(ATTN_W), dbuf));
         GPT2_HIP(gpt2k::ln_backward(reinterpret_cast<const float*>(lay(l, L.l_xin)), vecp(LN1_W), dbuf, dx, M, d,
                                     c.ln_eps, lnpg, lnpb, G(I(LN1_W)), G(I(LN1_B)), s));
+    }
+    // every bias gradient, kColsumSegs segments per launch
+    for (size_t i0 = 0; i0 < bsegs.size(); i0 += gpt2k::kColsumSegs) {
+        gpt2k::ColsumSegs part_segs;
+        for (size_t i = i0; i < std::min(bsegs.size(), i0 + gpt2k::kColsumSegs); ++i) part_segs.seg[part_segs.n++] = bsegs[i];
+        GPT2_HIP(gpt2k::colsum_reduce_multi(part_segs, s));
     }
     GPT2_HIP(gpt2k::embed_backward(tokens, dx, B, T, c.n_ctx, d, V, G(0), G(1), s));
     return GPT2_OK;

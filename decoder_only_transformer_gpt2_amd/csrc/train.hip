@@ -160,6 +160,33 @@ __global__ void __launch_bounds__(256) colsum_reduce_kernel(const float* __restr
     }
 }
 
+// colsum_reduce_kernel over several independent segments: blockIdx.y picks the segment, the column
+// blocks past its C return at once. Same per-column order as colsum_reduce_kernel.
+__global__ void __launch_bounds__(256) colsum_reduce_multi_kernel(const ColsumSegs segs) {
+    __shared__ float accg[kRedGroups][kRedCols];
+    const ColsumSeg sg = segs.seg[blockIdx.y];
+    if ((int)blockIdx.x * kRedCols >= sg.C) return;
+    const int cl = threadIdx.x % kRedCols, grp = threadIdx.x / kRedCols, c = blockIdx.x * kRedCols + cl;
+    const int per = (sg.nb + kRedGroups - 1) / kRedGroups, b0 = grp * per, b1 = min(sg.nb, b0 + per);
+    float a[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    if (c < sg.C) {
+        int b = b0;
+        for (; b + 8 <= b1; b += 8) {
+#pragma unroll
+            for (int u = 0; u < 8; ++u) a[u] += sg.part[(long)(b + u) * sg.C + c];
+        }
+        for (; b < b1; ++b) a[0] += sg.part[(long)b * sg.C + c];
+    }
+    accg[grp][cl] = ((a[0] + a[1]) + (a[2] + a[3])) + ((a[4] + a[5]) + (a[6] + a[7]));
+    __syncthreads();
+    if (grp == 0 && c < sg.C) {
+        float sum = 0.f;
+#pragma unroll
+        for (int g = 0; g < kRedGroups; ++g) sum += accg[g][cl];
+        sg.out[c] = sum;
+    }
+}
+
 // ------------------------------------------------------------------------------ LayerNorm backward
 // Four wavefronts per block of kLnRows rows, one row at a time per wavefront. For each row:
 // xhat = (x - mean) * rstd, g = dy * gamma, dx += rstd * (g - mean(g) - xhat * mean(g * xhat)). Each
@@ -723,6 +750,24 @@ hipError_t transpose_colsum(const float* src, long lds, int R, int C, uint16_t* 
     return hipGetLastError();
 }
 
+hipError_t transpose_colsum_partials(const float* src, long lds, int R, int C, uint16_t* dst, long ldd, int Rp,
+                                     float* part, hipStream_t s) {
+    const bool vec = lds % 8 == 0 && ldd % 8 == 0 && reinterpret_cast<uintptr_t>(src) % 16 == 0 &&
+                     reinterpret_cast<uintptr_t>(dst) % 16 == 0 && Rp >= R;
+    if (!vec) return hipErrorInvalidValue;
+    transpose_vec_kernel<false><<<dim3((C + 63) / 64, (Rp + 63) / 64), dim3(256), 0, s>>>(src, lds, R, C, dst, ldd, Rp,
+                                                                                          part);
+    return hipGetLastError();
+}
+
+hipError_t colsum_reduce_multi(const ColsumSegs& segs, hipStream_t s) {
+    if (segs.n < 1 || segs.n > kColsumSegs) return hipErrorInvalidValue;
+    int cmax = 0;
+    for (int i = 0; i < segs.n; ++i) cmax = max(cmax, segs.seg[i].C);
+    colsum_reduce_multi_kernel<<<dim3((cmax + kRedCols - 1) / kRedCols, segs.n), dim3(256), 0, s>>>(segs);
+    return hipGetLastError();
+}
+
 hipError_t colsum(const float* src, long ld, int R, int C, float* part, float* out, hipStream_t s) {
     const int nb = colsum_blocks(R);
     colsum_partial_kernel<<<dim3((C + 63) / 64, nb), dim3(256), 0, s>>>(src, ld, R, C, part);
@@ -742,9 +787,12 @@ hipError_t ln_backward(const float* x, const float* gamma, const float* dy, floa
         case 1600: ln_backward_kernel<25><<<grid, block, 0, s>>>(x, gamma, dy, dx, M, d, eps, pg, pb); break;
         default: ln_backward_kernel<0><<<grid, block, 0, s>>>(x, gamma, dy, dx, M, d, eps, pg, pb); break;
     }
-    colsum_reduce_kernel<<<dim3((d + kRedCols - 1) / kRedCols), dim3(256), 0, s>>>(pg, np, d, dgamma);
-    colsum_reduce_kernel<<<dim3((d + kRedCols - 1) / kRedCols), dim3(256), 0, s>>>(pb, np, d, dbeta);
-    return hipGetLastError();
+    if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
+    ColsumSegs segs;  // the gain and shift gradients in one launch
+    segs.seg[0] = {pg, dgamma, np, d};
+    segs.seg[1] = {pb, dbeta, np, d};
+    segs.n = 2;
+    return colsum_reduce_multi(segs, s);
 }
 
 hipError_t gelu_forward(const float* u, void* h, long n, bool bf16, int erf_form, hipStream_t s) {
