@@ -15,9 +15,8 @@
 // the probabilities are already in the operand layout of the second product O^T += V^T P^T.
 // Online softmax in fp32 on the raw scores: exp2(s*c - m*c) is one FMA and one v_exp_f32 per score
 // (c = scale * log2 e); the reference maximum moves only when a query's maximum grows by more than
-// 2^8, so the accumulators are rarely rescaled. Each lane sums its own probabilities (fp32) into a
-// partial denominator; the four partials of a query are added once, after the key loop (a matrix-
-// unit sum as ones x P^T took eight more registers, and the kernel spilled). Tiles wholly above a wavefront's
+// 2^8, so the accumulators are rarely rescaled. The row sums come from the matrix unit as
+// ones x P^T, over the same bf16 probabilities that weight V. Tiles wholly above a wavefront's
 // diagonal are skipped; only tiles that cross it are masked (selects). Workgroups are issued
 // longest-first (last query tiles first) to even out the causal imbalance. When the grid is small,
 // a workgroup runs two groups of wavefronts over the same queries, each taking every other key
@@ -99,7 +98,7 @@ __global__ __launch_bounds__(64 * WAVES * G, 4) void attn_bf16_kernel(
         }
 
     f32x4_t oacc[NQ][4];  // [query block][d fragment]; rows d = df*16 + 4*g4 + e, column = query
-    float lsum[NQ];       // this lane's part of the running denominator (its keys 4*g4 .. of each block)
+    f32x4_t lacc[NQ];     // every row: the running denominator of the column's query
     float mrow[NQ];       // reference maximum of the raw scores of this lane's queries
     float mthr[NQ];       // mrow + 8 / scale_log2: scores above it move the reference
     float mbias[NQ];      // mrow * scale_log2 (0 while mrow is -inf)
@@ -107,11 +106,14 @@ __global__ __launch_bounds__(64 * WAVES * G, 4) void attn_bf16_kernel(
     for (int qb = 0; qb < NQ; ++qb) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) oacc[qb][i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-        lsum[qb] = 0.f;
+        lacc[qb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
         mrow[qb] = -INFINITY;
         mthr[qb] = -INFINITY;
         mbias[qb] = 0.f;
     }
+
+    const u32x4_t ones_u = {0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};  // bf16 1.0 x 8
+    const bf16x8_t ones = __builtin_bit_cast(bf16x8_t, ones_u);
 
     // V item c of a group: key pair kp = c / 8 and d chunk vdc = c % 8, so that eight consecutive
     // lanes read one whole 128-byte key row per load
@@ -233,7 +235,7 @@ __global__ __launch_bounds__(64 * WAVES * G, 4) void attn_bf16_kernel(
                         mbias[qb] = mnew == -INFINITY ? 0.f : mnew * scale_log2;
 #pragma unroll
                         for (int df = 0; df < 4; ++df) oacc[qb][df] *= alpha;
-                        lsum[qb] *= alpha;
+                        lacc[qb] *= alpha;
                     }
                 }
                 // P^T in the B-operand layout: slot j of a lane holds key 32*hh + 4*g4 + j (j < 4) or
@@ -254,7 +256,7 @@ __global__ __launch_bounds__(64 * WAVES * G, 4) void attn_bf16_kernel(
                     pu[2] = pack_bf16x2(p[1][0], p[1][1]);
                     pu[3] = pack_bf16x2(p[1][2], p[1][3]);
                     pf[qb] = __builtin_bit_cast(bf16x8_t, pu);
-                    lsum[qb] += ((p[0][0] + p[0][1]) + (p[0][2] + p[0][3])) + ((p[1][0] + p[1][1]) + (p[1][2] + p[1][3]));
+                    lacc[qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pf[qb], lacc[qb], 0, 0, 0);
                 }
                 // O^T[d, query] += V^T[d, key] P^T[key, query], 32 keys per MFMA
 #pragma unroll
@@ -276,12 +278,6 @@ __global__ __launch_bounds__(64 * WAVES * G, 4) void attn_bf16_kernel(
         __syncthreads();
     }
 
-    // the denominator of query column r16: the four 16-lane rows hold its four key quarters
-#pragma unroll
-    for (int qb = 0; qb < NQ; ++qb) {
-        lsum[qb] += __shfl_xor(lsum[qb], 16, GPT2_WAVE);
-        lsum[qb] += __shfl_xor(lsum[qb], 32, GPT2_WAVE);
-    }
     if constexpr (G > 1) {
         // groups 1..G-1 hand their (accumulators, denominator, reference maximum) to group 0,
         // which rescales every part to the common maximum and adds them in group order. Merge
@@ -297,7 +293,7 @@ __global__ __launch_bounds__(64 * WAVES * G, 4) void attn_bf16_kernel(
                 for (int df = 0; df < 4; ++df)
 #pragma unroll
                     for (int e = 0; e < 4; ++e) at(grp, qb * 18 + df * 4 + e) = oacc[qb][df][e];
-                at(grp, qb * 18 + 16) = lsum[qb];
+                at(grp, qb * 18 + 16) = lacc[qb][0];
                 at(grp, qb * 18 + 17) = mrow[qb];
             }
         }
@@ -311,7 +307,7 @@ __global__ __launch_bounds__(64 * WAVES * G, 4) void attn_bf16_kernel(
             const float a0 = mrow[qb] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((mrow[qb] - mn) * scale_log2);
 #pragma unroll
             for (int df = 0; df < 4; ++df) oacc[qb][df] *= a0;
-            lsum[qb] *= a0;
+            lacc[qb][0] *= a0;
 #pragma unroll
             for (int g = 1; g < G; ++g) {
                 const float mg = at(g, qb * 18 + 17);
@@ -320,7 +316,7 @@ __global__ __launch_bounds__(64 * WAVES * G, 4) void attn_bf16_kernel(
                 for (int df = 0; df < 4; ++df)
 #pragma unroll
                     for (int e = 0; e < 4; ++e) oacc[qb][df][e] += at(g, qb * 18 + df * 4 + e) * ag;
-                lsum[qb] += at(g, qb * 18 + 16) * ag;
+                lacc[qb][0] += at(g, qb * 18 + 16) * ag;
             }
         }
     }
@@ -329,7 +325,7 @@ __global__ __launch_bounds__(64 * WAVES * G, 4) void attn_bf16_kernel(
     for (int qb = 0; qb < NQ; ++qb) {
         const int qi = qw + 16 * qb + r16;
         if (qi < T) {
-            const float inv = 1.0f / lsum[qb];
+            const float inv = 1.0f / lacc[qb][0];
             uint16_t* Ob = O + b * osb + h * osh + qi * ost;
 #pragma unroll
             for (int df = 0; df < 4; ++df) {
