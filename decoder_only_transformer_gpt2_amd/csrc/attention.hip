@@ -29,14 +29,14 @@ namespace {
 
 constexpr int KT = 64;        // keys per LDS tile
 constexpr int DH = 64;        // head size
-constexpr int VTS = KT + 8;   // row stride (elements) of the transposed V tile: 36 words
-// Element offset of the key-pair word `w` (keys 2w, 2w+1) of row d of the transposed V tile: the
-// word index is XOR-ed with 8 * (d / 16), which with the 36-word stride puts both the transposing
-// 4-byte writes (eight d rows x eight key pairs per instruction) and the 8-byte fragment reads
-// (sixteen d rows x four key quads per half-wave) on 64 distinct banks. (A 34-word stride without
-// the XOR conflicted two-way on every write: a third of the kernel's LDS cycles.) The XOR moves
-// whole groups of eight words, so the four keys of a fragment read stay adjacent.
-__device__ __forceinline__ int vtw(int d, int w) { return d * VTS + 2 * (w ^ ((d >> 4) << 3)); }
+constexpr int VTS = KT + 16;  // row stride (elements) of the transposed V tile: 40 words
+// Element offset of the key-pair word `w` (keys 2w, 2w+1) of row d of the transposed V tile. The
+// word index is XOR-ed with 4 * (d / 8); with the 40-word stride this puts both the transposing
+// 4-byte writes (eight d rows x four key pairs per 32 lanes: 4-byte accesses are served 32 lanes
+// at a time over 32 banks) and the 8-byte fragment reads (sixteen d rows x two key quads per 32
+// lanes, over 64 banks) on distinct banks. The XOR moves whole groups of four words, so the four
+// keys of a fragment read stay adjacent.
+__device__ __forceinline__ int vtw(int d, int w) { return d * VTS + 2 * (w ^ ((d >> 3) << 2)); }
 // Maximum over the four lanes L, L^16, L^32, L^48 (the four 16-lane rows). Only the rare
 // rescale path needs it. (The gfx950 row-swap builtins would avoid the LDS crossbar, but this
 // toolchain miscompiles them when both operands are the same value.)
@@ -45,12 +45,12 @@ __device__ __forceinline__ float max_over_rows(float m) {
     return fmaxf(m, __shfl_xor(m, 32, GPT2_WAVE));
 }
 
-// K tile element offset of (key, 16-byte chunk): chunks are permuted within a key row by
-// (key & 7) ^ ((key >> 3) & 1), which spreads the 16-byte reads of 16 consecutive keys over all
-// banks whether a read pass covers 8 or 16 lanes.
-__device__ __forceinline__ int kswz(int key, int chunk) {
-    return key * DH + ((chunk ^ (key & 7) ^ ((key >> 3) & 1)) << 3);
-}
+// K tile element offset of (key, 16-byte chunk): chunks are permuted within a key row by key & 7.
+// 16-byte accesses are served sixteen lanes at a time over 64 banks, and the sixteen lanes are not
+// a plain run: lanes 0-7 go with lanes 24-31 and lanes 8-15 with lanes 16-23 (likewise in the upper
+// half-wave). Under that pairing both the fragment reads (sixteen consecutive keys, one chunk per
+// lane) and the tile writes (eight chunks of two keys per eight lanes) fall on distinct banks.
+__device__ __forceinline__ int kswz(int key, int chunk) { return key * DH + ((chunk ^ (key & 7)) << 3); }
 
 template <int WAVES, int G>  // 32 queries per wavefront; G groups of WAVES wavefronts share the queries
 __global__ __launch_bounds__(64 * WAVES * G, 4) void attn_bf16_kernel(
@@ -80,6 +80,12 @@ __global__ __launch_bounds__(64 * WAVES * G, 4) void attn_bf16_kernel(
     const int grp = wave / WAVES, wv = wave % WAVES, tg = t % NG;  // group, wavefront and thread in the group
     const int r16 = lane & 15, g4 = lane >> 4;
     const int qw = q0 + QW * wv;  // this wavefront's first query; lane's queries: qw + 16*qb + r16
+    // lane part of the V^T fragment reads (low and high key quads). The high quad's base is made
+    // opaque to the compiler: with one base it fuses the two 8-byte reads into ds_read2_b64, which
+    // runs as two passes at half the LDS rate of ds_read_b64 and conflicts two-way on this layout.
+    const int vlane = r16 * VTS + 2 * ((2 * g4) ^ (4 * (r16 >> 3)));
+    int vlane_hi = vlane + 16;
+    asm volatile("" : "+v"(vlane_hi));
 
     const uint16_t* Qb = Q + b * qsb + h * qsh;
     const uint16_t* Kb = K + b * ksb + h * ksh;
@@ -261,9 +267,12 @@ __global__ __launch_bounds__(64 * WAVES * G, 4) void attn_bf16_kernel(
                 // O^T[d, query] += V^T[d, key] P^T[key, query], 32 keys per MFMA
 #pragma unroll
                 for (int df = 0; df < 4; ++df) {
-                    const int vd = df * 16 + r16;
-                    const u32x2_t lo = *reinterpret_cast<const u32x2_t*>(&tV[vtw(vd, 16 * hh + 2 * g4)]);
-                    const u32x2_t hi = *reinterpret_cast<const u32x2_t*>(&tV[vtw(vd, 16 * hh + 8 + 2 * g4)]);
+                    // vtw(df*16 + r16, 16*hh + 8*half + 2*g4), split into this lane's part (word
+                    // bits 1-2) and a part fixed per (df, hh, half) (word bits 3-4), which
+                    // becomes an immediate offset
+                    const int fixed = df * 16 * VTS + 2 * ((16 * hh) ^ (8 * df));
+                    const u32x2_t lo = *reinterpret_cast<const u32x2_t*>(tV + vlane + fixed);
+                    const u32x2_t hi = *reinterpret_cast<const u32x2_t*>(tV + vlane_hi + fixed + (df & 1 ? -32 : 0));
                     const bf16x8_t vf = __builtin_bit_cast(bf16x8_t, u32x4_t{lo[0], lo[1], hi[0], hi[1]});
 #pragma unroll
                     for (int qb = 0; qb < NQ; ++qb)
