@@ -14,9 +14,12 @@ the backward pass) under "train".
 
 The roofline object is for the lm_head GEMM, the largest single launch: its duration is taken
 from HIP events the library records on its own stream around that launch in every timed step.
-"kernels" gives the same for every launch kind of the forward (mean duration per launch from
-events around each launch of five extra forwards, algorithmic work, roofline fraction, share of
-the forward's kernel time).
+"kernels" gives the same for every launch kind of the forward (mean duration per launch from one
+launch of that kind repeated 100 times back to back inside a forward, between two events;
+algorithmic work, roofline fraction, share of the forward's kernel time), and "cold_cache" the
+LayerNorm and the embedding right after a write that evicts the caches. With --configs all it
+also times the isolated attention (B=8 H=12 T=1024) and the GPT-2 medium (B=8) and XL (B=4)
+forwards.
 The CPU baseline times the fp64 oracle on a bounded sample (one full sequence) on the host.
 """
 from __future__ import annotations
