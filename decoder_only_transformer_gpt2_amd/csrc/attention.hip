@@ -27,16 +27,23 @@
 namespace gpt2k {
 namespace {
 
-constexpr int KT = 64;        // keys per LDS tile
-constexpr int DH = 64;        // head size
-constexpr int VTS = KT + 16;  // row stride (elements) of the transposed V tile: 40 words
-// Element offset of the key-pair word `w` (keys 2w, 2w+1) of row d of the transposed V tile. The
-// word index is XOR-ed with 4 * (d / 8); with the 40-word stride this puts both the transposing
-// 4-byte writes (eight d rows x four key pairs per 32 lanes: 4-byte accesses are served 32 lanes
-// at a time over 32 banks) and the 8-byte fragment reads (sixteen d rows x two key quads per 32
-// lanes, over 64 banks) on distinct banks. The XOR moves whole groups of four words, so the four
-// keys of a fragment read stay adjacent.
-__device__ __forceinline__ int vtw(int d, int w) { return d * VTS + 2 * (w ^ ((d >> 3) << 2)); }
+constexpr int KT = 64;         // keys per LDS tile
+constexpr int DH = 64;         // head size
+constexpr int TSZ = KT * DH;   // elements of one K or V tile (8 KB)
+
+// K and V tiles are both [key][64 dims] in LDS, the eight 16-byte chunks of each key row permuted
+// by key & 7. The tiles arrive by LDS DMA (global_load_lds, 16 bytes per lane, a 1 KB block of
+// eight key rows per instruction); lane L of a block writes the LDS slot L, i.e. key row L / 8,
+// stored chunk L % 8, so it fetches source chunk (L % 8) ^ (L / 8). Reads:
+//  * K fragments (16 bytes per lane, sixteen consecutive keys x one chunk): 16-byte reads are
+//    served sixteen lanes at a time over 64 banks, the sixteen being lanes 0-7 with 24-31 and 8-15
+//    with 16-23; the key & 7 permutation puts each sixteen on distinct banks;
+//  * V^T fragments by ds_read_b64_tr_b16: in each group of sixteen lanes, lane 4r + q reads the
+//    four dims 4q .. 4q+3 of key row r of a four-key group and receives, transposed, four
+//    consecutive keys of one dimension (lane i: dim i of the sixteen) -- the A operand of
+//    O^T += V^T P^T. Thirty-two lanes read eight key rows x 32 bytes; under the permutation they
+//    fall on distinct banks (8-byte accesses are served 32 lanes at a time over 64 banks).
+__device__ __forceinline__ int kvswz(int key, int chunk) { return key * DH + ((chunk ^ (key & 7)) << 3); }
 // Maximum over the four lanes L, L^16, L^32, L^48 (the four 16-lane rows). Only the rare
 // rescale path needs it. (The gfx950 row-swap builtins would avoid the LDS crossbar, but this
 // toolchain miscompiles them when both operands are the same value.)
@@ -45,12 +52,17 @@ __device__ __forceinline__ float max_over_rows(float m) {
     return fmaxf(m, __shfl_xor(m, 32, GPT2_WAVE));
 }
 
-// K tile element offset of (key, 16-byte chunk): chunks are permuted within a key row by key & 7.
-// 16-byte accesses are served sixteen lanes at a time over 64 banks, and the sixteen lanes are not
-// a plain run: lanes 0-7 go with lanes 24-31 and lanes 8-15 with lanes 16-23 (likewise in the upper
-// half-wave). Under that pairing both the fragment reads (sixteen consecutive keys, one chunk per
-// lane) and the tile writes (eight chunks of two keys per eight lanes) fall on distinct banks.
-__device__ __forceinline__ int kswz(int key, int chunk) { return key * DH + ((chunk ^ (key & 7)) << 3); }
+// s_waitcnt vmcnt(0) expcnt(7) lgkmcnt(0): every vector memory access of this wavefront (the LDS
+// DMA included) and every LDS access has completed
+constexpr int kWaitAllMem = 0x0070;
+typedef short short4_t __attribute__((vector_size(8)));
+__device__ __forceinline__ u32x2_t lds_read_tr16(const uint16_t* p) {
+    const short4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) short4_t*)(p));
+    return __builtin_bit_cast(u32x2_t, v);
+}
+__device__ __forceinline__ void lds_dma16(const uint16_t* src, uint16_t* lds_block) {
+    __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)(lds_block), 16, 0, 0);
+}
 
 template <int WAVES, int G>  // 32 queries per wavefront; G groups of WAVES wavefronts share the queries
 __global__ __launch_bounds__(64 * WAVES * G, 4) void attn_bf16_kernel(
@@ -58,18 +70,16 @@ __global__ __launch_bounds__(64 * WAVES * G, 4) void attn_bf16_kernel(
     int64_t ksh, int64_t kst, const uint16_t* __restrict__ V, int64_t vsb, int64_t vsh, int64_t vst,
     uint16_t* __restrict__ O, int64_t osb, int64_t osh, int64_t ost, int64_t osx, int B, int H, int T,
     float scale_log2) {
-    constexpr int NQ = 2, QW = 16 * NQ;          // 16-query column blocks and queries per wavefront
+    static_assert(WAVES == 4, "each wavefront of a group moves two of the eight 1 KB blocks of a K or V tile");
+    constexpr int NQ = 2, QW = 16 * NQ;  // 16-query column blocks and queries per wavefront
     constexpr int QT = QW * WAVES, NG = 64 * WAVES;
-    constexpr int KCPT = KT * 8 / NG;            // 16-byte K chunks per thread per tile
-    constexpr int VPPT = KT * 4 / NG;            // (key pair, 16-byte d chunk) V items per thread per tile
-    static_assert(KCPT >= 1 && VPPT >= 1 && KT * 4 % NG == 0, "tile loader");
-    constexpr int KSZ = KT * DH, VSZ = DH * VTS;  // elements of one K tile and one transposed V tile
-    constexpr int RING = 2 * G * (KSZ + VSZ);
-    constexpr int MERGE = (G - 1) * WAVES * 64 * (NQ * 18) * 2;  // groups 1.. partial states (floats)
-    // [buffer][group] K tiles, then [buffer][group] V tiles; after the loop the merge area
-    __shared__ __attribute__((aligned(16))) uint16_t smem[RING > MERGE ? RING : MERGE];
-    auto tile_k = [&](int buf, int g) { return smem + (buf * G + g) * KSZ; };
-    auto tile_v = [&](int buf, int g) { return smem + 2 * G * KSZ + (buf * G + g) * VSZ; };
+    constexpr int BUF = G * 2 * TSZ;     // one ring slot: [group][K, V]
+    constexpr int NV = NQ * 18;          // merge values per lane (accumulators, denominator, maximum)
+    static_assert((G - 1) * 18 * NG * 4 <= BUF * 2, "merge area of one query block fits one ring slot");
+    // two ring slots as two objects, so that the compiler can tell the slot being read from the slot
+    // the DMA is filling
+    __shared__ __attribute__((aligned(1024))) uint16_t lds0[BUF];
+    __shared__ __attribute__((aligned(1024))) uint16_t lds1[BUF];
 
     const int nqt = (T + QT - 1) / QT;
     const int bh = blockIdx.x % (B * H);
@@ -77,15 +87,9 @@ __global__ __launch_bounds__(64 * WAVES * G, 4) void attn_bf16_kernel(
     const int b = bh / H, h = bh % H;
     const int q0 = qt * QT;
     const int t = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(t / GPT2_WAVE), lane = t % GPT2_WAVE;
-    const int grp = wave / WAVES, wv = wave % WAVES, tg = t % NG;  // group, wavefront and thread in the group
+    const int grp = wave / WAVES, wv = wave % WAVES;  // group and wavefront in the group
     const int r16 = lane & 15, g4 = lane >> 4;
     const int qw = q0 + QW * wv;  // this wavefront's first query; lane's queries: qw + 16*qb + r16
-    // lane part of the V^T fragment reads (low and high key quads). The high quad's base is made
-    // opaque to the compiler: with one base it fuses the two 8-byte reads into ds_read2_b64, which
-    // runs as two passes at half the LDS rate of ds_read_b64 and conflicts two-way on this layout.
-    const int vlane = r16 * VTS + 2 * ((2 * g4) ^ (4 * (r16 >> 3)));
-    int vlane_hi = vlane + 16;
-    asm volatile("" : "+v"(vlane_hi));
 
     const uint16_t* Qb = Q + b * qsb + h * qsh;
     const uint16_t* Kb = K + b * ksb + h * ksh;
@@ -121,189 +125,186 @@ __global__ __launch_bounds__(64 * WAVES * G, 4) void attn_bf16_kernel(
     const u32x4_t ones_u = {0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};  // bf16 1.0 x 8
     const bf16x8_t ones = __builtin_bit_cast(bf16x8_t, ones_u);
 
-    // V item c of a group: key pair kp = c / 8 and d chunk vdc = c % 8, so that eight consecutive
-    // lanes read one whole 128-byte key row per load
-    auto v_item = [](int c, int& kp, int& vdc) {
-        kp = c >> 3;
-        vdc = c & 7;
-    };
-    // tile loader: thread tg of a group moves KCPT 16-byte K chunks (key c/8, chunk c%8) and, for
-    // VPPT V items, the 16-byte d chunks of both keys of the pair. Keys past T read row T-1 (finite
-    // data): their scores are masked to -inf, so they weigh nothing.
-    auto load_tile = [&](int k0, u32x4_t (&kr)[KCPT], u32x4_t (&vr)[2 * VPPT]) {
+    // DMA: wavefront wv of a group moves blocks 2wv and 2wv+1 (key rows 16wv .. 16wv+15) of the K
+    // and the V tile. Keys past T read row T-1 (finite data): their scores are masked to -inf, so
+    // they weigh nothing.
+    const int drow = 16 * wv + (lane >> 3);
+    const int dch8 = ((lane & 7) ^ (lane >> 3)) * 8;
+    const int64_t koff = (int64_t)drow * kst + dch8, voff = (int64_t)drow * vst + dch8;
+    auto issue = [&](uint16_t* slot, int k0) __attribute__((always_inline)) {
+        uint16_t* tK = slot + grp * 2 * TSZ + 2 * wv * 512;
+        uint16_t* tV = tK + TSZ;
+        if (k0 + KT <= T) {
+            const uint16_t* ks = Kb + (int64_t)k0 * kst + koff;
+            const uint16_t* vs = Vb + (int64_t)k0 * vst + voff;
+            lds_dma16(ks, tK);
+            lds_dma16(ks + 8 * kst, tK + 512);
+            lds_dma16(vs, tV);
+            lds_dma16(vs + 8 * vst, tV + 512);
+        } else {
 #pragma unroll
-        for (int i = 0; i < KCPT; ++i) {
-            const int c = tg + i * NG, kkey = c / 8, kch = c % 8;
-            kr[i] = *reinterpret_cast<const u32x4_t*>(Kb + min(k0 + kkey, T - 1) * kst + kch * 8);
-        }
-#pragma unroll
-        for (int i = 0; i < VPPT; ++i) {
-            int kp, vdc;
-            v_item(tg + i * NG, kp, vdc);
-            const int key = k0 + 2 * kp;
-            vr[2 * i] = *reinterpret_cast<const u32x4_t*>(Vb + min(key, T - 1) * vst + vdc * 8);
-            vr[2 * i + 1] = *reinterpret_cast<const u32x4_t*>(Vb + min(key + 1, T - 1) * vst + vdc * 8);
-        }
-    };
-    auto store_tile = [&](int buf, const u32x4_t (&kr)[KCPT], const u32x4_t (&vr)[2 * VPPT]) {
-        uint16_t* tK = tile_k(buf, grp);
-        uint16_t* tV = tile_v(buf, grp);
-#pragma unroll
-        for (int i = 0; i < KCPT; ++i) {
-            const int c = tg + i * NG, kkey = c / 8, kch = c % 8;
-            *reinterpret_cast<u32x4_t*>(&tK[kswz(kkey, kch)]) = kr[i];
-        }
-#pragma unroll
-        for (int i = 0; i < VPPT; ++i) {
-            int kp, vdc;
-            v_item(tg + i * NG, kp, vdc);
-#pragma unroll
-            for (int w = 0; w < 4; ++w) {
-                const uint32_t a = vr[2 * i][w], bb = vr[2 * i + 1][w];  // d = vdc*8 + 2w, +1 of keys 2kp, 2kp+1
-                *reinterpret_cast<uint32_t*>(&tV[vtw(vdc * 8 + 2 * w, kp)]) = (a & 0xffffu) | (bb << 16);
-                *reinterpret_cast<uint32_t*>(&tV[vtw(vdc * 8 + 2 * w + 1, kp)]) = (a >> 16) | (bb & 0xffff0000u);
+            for (int i = 0; i < 2; ++i) {
+                const int key = min(k0 + drow + 8 * i, T - 1);
+                lds_dma16(Kb + (int64_t)key * kst + dch8, tK + i * 512);
+                lds_dma16(Vb + (int64_t)key * vst + dch8, tV + i * 512);
             }
         }
     };
+
+    // V^T fragment reads: lane 4r + q of each sixteen reads dims 4q..4q+3 of key 4*g4 + r of a
+    // 16-key group; per d fragment df the chunk is (2df + q/2) ^ (key & 7) (key & 7 does not depend
+    // on which 16-key group), so the four per-lane offsets are fixed and the group moves them by
+    // whole 16-key strides (immediate offsets)
+    int vtr[4];
+    {
+        const int r = r16 >> 2, q = r16 & 3, key = 4 * g4 + r;
+#pragma unroll
+        for (int df = 0; df < 4; ++df) vtr[df] = key * DH + (((2 * df + (q >> 1)) ^ (key & 7)) << 3) + 4 * (q & 1);
+    }
 
     // step s: group g runs key tile s*G + g
     const int kend = min(T, q0 + QT);
     const int n_kt = (kend + KT - 1) / KT;
     const int n_st = (n_kt + G - 1) / G;
-    u32x4_t kr[KCPT], vr[2 * VPPT];
-    load_tile(grp * KT, kr, vr);
-    store_tile(0, kr, vr);
-    if (n_st > 1) load_tile((G + grp) * KT, kr, vr);
-    __syncthreads();
 
-    for (int st = 0; st < n_st; ++st) {
-        const int kt = st * G + grp, k0 = kt * KT, buf = st & 1;
-        const uint16_t* tK = tile_k(buf, grp);
-        const uint16_t* tV = tile_v(buf, grp);
-        if (kt < n_kt && k0 <= qw + QW - 1) {  // some key of this tile is visible to some query of this wavefront
-            const bool edge = k0 + KT - 1 > qw || k0 + KT > T;  // the tile crosses the diagonal or T
-            // The tile runs as two halves of 32 keys, each with its own softmax update (fewer
-            // scores live at once). hh = 1 is skipped when all its keys lie above the diagonal.
+    auto compute = [&](const uint16_t* slot, int st) __attribute__((always_inline)) {
+        const int kt = st * G + grp, k0 = kt * KT;
+        const uint16_t* tK = slot + grp * 2 * TSZ;
+        const uint16_t* tV = tK + TSZ;
+        if (!(kt < n_kt && k0 <= qw + QW - 1)) return;  // no key of this tile is visible to this wavefront
+        const bool edge = k0 + KT - 1 > qw || k0 + KT > T;  // the tile crosses the diagonal or T
+        // The tile runs as two halves of 32 keys, each with its own softmax update (fewer scores
+        // live at once). hh = 1 is skipped when all its keys lie above the diagonal.
 #pragma unroll
-            for (int hh = 0; hh < 2; ++hh) {
-                if (hh == 1 && k0 + 32 > qw + QW - 1) break;
-                // S^T[key, query] for keys k0 + 32*hh .. +31 x 32 queries
-                f32x4_t s[NQ][2];
+        for (int hh = 0; hh < 2; ++hh) {
+            if (hh == 1 && k0 + 32 > qw + QW - 1) break;
+            // S^T[key, query] for keys k0 + 32*hh .. +31 x 32 queries
+            f32x4_t s[NQ][2];
 #pragma unroll
-                for (int m2 = 0; m2 < 2; ++m2) {
-                    const int mf = 2 * hh + m2;
-                    bf16x8_t kf[2];
+            for (int m2 = 0; m2 < 2; ++m2) {
+                const int mf = 2 * hh + m2;
+                bf16x8_t kf[2];
+#pragma unroll
+                for (int kk = 0; kk < 2; ++kk)
+                    kf[kk] = *reinterpret_cast<const bf16x8_t*>(&tK[kvswz(mf * 16 + r16, kk * 4 + g4)]);
+#pragma unroll
+                for (int qb = 0; qb < NQ; ++qb) {
+                    s[qb][m2] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                     for (int kk = 0; kk < 2; ++kk)
-                        kf[kk] = *reinterpret_cast<const bf16x8_t*>(&tK[kswz(mf * 16 + r16, kk * 4 + g4)]);
-#pragma unroll
-                    for (int qb = 0; qb < NQ; ++qb) {
-                        s[qb][m2] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                        for (int kk = 0; kk < 2; ++kk)
-                            s[qb][m2] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[kk], qf[qb][kk], s[qb][m2], 0, 0, 0);
-                    }
+                        s[qb][m2] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[kk], qf[qb][kk], s[qb][m2], 0, 0, 0);
                 }
-                if (edge) {
-                    // key k0 + 16*mf + 4*g4 + e is visible to query qi when it is <= min(qi, T-1)
-#pragma unroll
-                    for (int qb = 0; qb < NQ; ++qb) {
-                        const int lim = min(qw + 16 * qb + r16, T - 1) - k0 - 32 * hh - 4 * g4;
-#pragma unroll
-                        for (int m2 = 0; m2 < 2; ++m2)
-#pragma unroll
-                            for (int e = 0; e < 4; ++e) s[qb][m2][e] = 16 * m2 + e <= lim ? s[qb][m2][e] : -INFINITY;
-                    }
-                }
-                // The reference maximum mrow of a query moves only when one of its scores exceeds
-                // it by more than 8 in log2 units (the softmax does not depend on the constant
-                // subtracted, and unscaled probabilities up to 2^8 are exact enough in fp32 and
-                // bf16). Each lane tests its own scores against the threshold; only when some lane
-                // of the wavefront crosses it (the first tiles, then rarely) are the four lanes of
-                // each query combined, the reference moved and the accumulators rescaled.
-                float mloc[NQ];
-                bool grow = false;
+            }
+            if (edge) {
+                // key k0 + 16*mf + 4*g4 + e is visible to query qi when it is <= min(qi, T-1)
 #pragma unroll
                 for (int qb = 0; qb < NQ; ++qb) {
-                    mloc[qb] = fmaxf(fmaxf(fmaxf(s[qb][0][0], s[qb][0][1]), fmaxf(s[qb][0][2], s[qb][0][3])),
-                                     fmaxf(fmaxf(s[qb][1][0], s[qb][1][1]), fmaxf(s[qb][1][2], s[qb][1][3])));
-                    grow |= mloc[qb] > mthr[qb];
-                }
-                if (__builtin_amdgcn_ballot_w64(grow)) {
-#pragma unroll
-                    for (int qb = 0; qb < NQ; ++qb) {
-                        const float mnew = fmaxf(mrow[qb], max_over_rows(mloc[qb]));
-                        // a query with every key so far masked (only past T) keeps a zero state
-                        const float alpha =
-                            mnew == -INFINITY ? 1.f : __builtin_amdgcn_exp2f((mrow[qb] - mnew) * scale_log2);
-                        mrow[qb] = mnew;
-                        mthr[qb] = mnew + 8.f / scale_log2;
-                        mbias[qb] = mnew == -INFINITY ? 0.f : mnew * scale_log2;
-#pragma unroll
-                        for (int df = 0; df < 4; ++df) oacc[qb][df] *= alpha;
-                        lacc[qb] *= alpha;
-                    }
-                }
-                // P^T in the B-operand layout: slot j of a lane holds key 32*hh + 4*g4 + j (j < 4) or
-                // 32*hh + 16 + 4*g4 + (j - 4); V^T fragments use the same key order
-                bf16x8_t pf[NQ];
-#pragma unroll
-                for (int qb = 0; qb < NQ; ++qb) {
-                    const float mb = mbias[qb];
-                    float p[2][4];
+                    const int lim = min(qw + 16 * qb + r16, T - 1) - k0 - 32 * hh - 4 * g4;
 #pragma unroll
                     for (int m2 = 0; m2 < 2; ++m2)
 #pragma unroll
-                        for (int e = 0; e < 4; ++e)
-                            p[m2][e] = __builtin_amdgcn_exp2f(fmaf(s[qb][m2][e], scale_log2, -mb));
-                    u32x4_t pu;
-                    pu[0] = pack_bf16x2(p[0][0], p[0][1]);
-                    pu[1] = pack_bf16x2(p[0][2], p[0][3]);
-                    pu[2] = pack_bf16x2(p[1][0], p[1][1]);
-                    pu[3] = pack_bf16x2(p[1][2], p[1][3]);
-                    pf[qb] = __builtin_bit_cast(bf16x8_t, pu);
-                    lacc[qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pf[qb], lacc[qb], 0, 0, 0);
-                }
-                // O^T[d, query] += V^T[d, key] P^T[key, query], 32 keys per MFMA
-#pragma unroll
-                for (int df = 0; df < 4; ++df) {
-                    // vtw(df*16 + r16, 16*hh + 8*half + 2*g4), split into this lane's part (word
-                    // bits 1-2) and a part fixed per (df, hh, half) (word bits 3-4), which
-                    // becomes an immediate offset
-                    const int fixed = df * 16 * VTS + 2 * ((16 * hh) ^ (8 * df));
-                    const u32x2_t lo = *reinterpret_cast<const u32x2_t*>(tV + vlane + fixed);
-                    const u32x2_t hi = *reinterpret_cast<const u32x2_t*>(tV + vlane_hi + fixed + (df & 1 ? -32 : 0));
-                    const bf16x8_t vf = __builtin_bit_cast(bf16x8_t, u32x4_t{lo[0], lo[1], hi[0], hi[1]});
-#pragma unroll
-                    for (int qb = 0; qb < NQ; ++qb)
-                        oacc[qb][df] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pf[qb], oacc[qb][df], 0, 0, 0);
+                        for (int e = 0; e < 4; ++e) s[qb][m2][e] = 16 * m2 + e <= lim ? s[qb][m2][e] : -INFINITY;
                 }
             }
+            // The reference maximum mrow of a query moves only when one of its scores exceeds it
+            // by more than 8 in log2 units (the softmax does not depend on the constant
+            // subtracted, and unscaled probabilities up to 2^8 are exact enough in fp32 and bf16).
+            // Each lane tests its own scores against the threshold; only when some lane of the
+            // wavefront crosses it (the first tiles, then rarely) are the four lanes of each query
+            // combined, the reference moved and the accumulators rescaled.
+            float mloc[NQ];
+            bool grow = false;
+#pragma unroll
+            for (int qb = 0; qb < NQ; ++qb) {
+                mloc[qb] = fmaxf(fmaxf(fmaxf(s[qb][0][0], s[qb][0][1]), fmaxf(s[qb][0][2], s[qb][0][3])),
+                                 fmaxf(fmaxf(s[qb][1][0], s[qb][1][1]), fmaxf(s[qb][1][2], s[qb][1][3])));
+                grow |= mloc[qb] > mthr[qb];
+            }
+            if (__builtin_amdgcn_ballot_w64(grow)) {
+#pragma unroll
+                for (int qb = 0; qb < NQ; ++qb) {
+                    const float mnew = fmaxf(mrow[qb], max_over_rows(mloc[qb]));
+                    // a query with every key so far masked (only past T) keeps a zero state
+                    const float alpha = mnew == -INFINITY ? 1.f : __builtin_amdgcn_exp2f((mrow[qb] - mnew) * scale_log2);
+                    mrow[qb] = mnew;
+                    mthr[qb] = mnew + 8.f / scale_log2;
+                    mbias[qb] = mnew == -INFINITY ? 0.f : mnew * scale_log2;
+#pragma unroll
+                    for (int df = 0; df < 4; ++df) oacc[qb][df] *= alpha;
+                    lacc[qb] *= alpha;
+                }
+            }
+            // P^T in the B-operand layout: slot j of a lane holds key 32*hh + 4*g4 + j (j < 4) or
+            // 32*hh + 16 + 4*g4 + (j - 4); the V^T fragments use the same key order
+            bf16x8_t pf[NQ];
+#pragma unroll
+            for (int qb = 0; qb < NQ; ++qb) {
+                const float mb = mbias[qb];
+                float p[2][4];
+#pragma unroll
+                for (int m2 = 0; m2 < 2; ++m2)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) p[m2][e] = __builtin_amdgcn_exp2f(fmaf(s[qb][m2][e], scale_log2, -mb));
+                u32x4_t pu;
+                pu[0] = pack_bf16x2(p[0][0], p[0][1]);
+                pu[1] = pack_bf16x2(p[0][2], p[0][3]);
+                pu[2] = pack_bf16x2(p[1][0], p[1][1]);
+                pu[3] = pack_bf16x2(p[1][2], p[1][3]);
+                pf[qb] = __builtin_bit_cast(bf16x8_t, pu);
+                lacc[qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pf[qb], lacc[qb], 0, 0, 0);
+            }
+            // O^T[d, query] += V^T[d, key] P^T[key, query], 32 keys per MFMA; the transposing
+            // reads take keys 32hh + 4*g4 + 0..3 (low) and 32hh + 16 + 4*g4 + 0..3 (high)
+#pragma unroll
+            for (int df = 0; df < 4; ++df) {
+                const u32x2_t lo = lds_read_tr16(tV + vtr[df] + (32 * hh) * DH);
+                const u32x2_t hi = lds_read_tr16(tV + vtr[df] + (32 * hh + 16) * DH);
+                const bf16x8_t vf = __builtin_bit_cast(bf16x8_t, u32x4_t{lo[0], lo[1], hi[0], hi[1]});
+#pragma unroll
+                for (int qb = 0; qb < NQ; ++qb)
+                    oacc[qb][df] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pf[qb], oacc[qb][df], 0, 0, 0);
+            }
         }
-        if (st + 1 < n_st) {
-            store_tile(buf ^ 1, kr, vr);  // step st+1 (its loads were issued during step st)
-            if (st + 2 < n_st) load_tile(((st + 2) * G + grp) * KT, kr, vr);
-        }
-        __syncthreads();
+    };
+
+    // Step st reads ring slot st & 1. It waits for its own DMAs of that slot and meets the other
+    // wavefronts (their DMAs have landed too, and nobody still reads the other slot, which step
+    // st-1 used), starts the DMA of step st+1 into the other slot, then computes.
+    issue(lds0, grp * KT);
+    auto step = [&](auto slot_c, int st) __attribute__((always_inline)) {
+        constexpr int SL = decltype(slot_c)::value;
+        uint16_t* cur = SL == 0 ? lds0 : lds1;
+        uint16_t* nxt = SL == 0 ? lds1 : lds0;
+        __builtin_amdgcn_s_waitcnt(kWaitAllMem);
+        __builtin_amdgcn_s_barrier();
+        if (st + 1 < n_st) issue(nxt, ((st + 1) * G + grp) * KT);
+        compute(cur, st);
+    };
+    for (int st = 0; st < n_st; st += 2) {
+        step(std::integral_constant<int, 0>{}, st);
+        if (st + 1 < n_st) step(std::integral_constant<int, 1>{}, st + 1);
     }
 
     if constexpr (G > 1) {
         // groups 1..G-1 hand their (accumulators, denominator, reference maximum) to group 0,
         // which rescales every part to the common maximum and adds them in group order. Merge
-        // area: value j of a lane at [(group-1) * NQ*18 + j][wave][lane], so that consecutive
-        // lanes write consecutive words.
-        constexpr int NV = NQ * 18;
-        float* part = reinterpret_cast<float*>(smem);
-        auto at = [&](int g, int j) -> float& { return part[((g - 1) * NV + j) * NG + wv * 64 + lane]; };
+        // area: value j of query block qb of a lane at [(group-1) * 18 + j][wave][lane] of ring
+        // slot qb, so that consecutive lanes write consecutive words.
+        __builtin_amdgcn_s_waitcnt(kWaitAllMem);
+        __syncthreads();  // every wavefront is done with the ring
+        auto at = [&](int qb, int g, int j) -> float& {
+            float* part = reinterpret_cast<float*>(qb == 0 ? lds0 : lds1);
+            return part[((g - 1) * 18 + j) * NG + wv * 64 + lane];
+        };
         if (grp > 0) {
 #pragma unroll
             for (int qb = 0; qb < NQ; ++qb) {
 #pragma unroll
                 for (int df = 0; df < 4; ++df)
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) at(grp, qb * 18 + df * 4 + e) = oacc[qb][df][e];
-                at(grp, qb * 18 + 16) = lacc[qb][0];
-                at(grp, qb * 18 + 17) = mrow[qb];
+                    for (int e = 0; e < 4; ++e) at(qb, grp, df * 4 + e) = oacc[qb][df][e];
+                at(qb, grp, 16) = lacc[qb][0];
+                at(qb, grp, 17) = mrow[qb];
             }
         }
         __syncthreads();
@@ -312,20 +313,20 @@ __global__ __launch_bounds__(64 * WAVES * G, 4) void attn_bf16_kernel(
         for (int qb = 0; qb < NQ; ++qb) {
             float mn = mrow[qb];
 #pragma unroll
-            for (int g = 1; g < G; ++g) mn = fmaxf(mn, at(g, qb * 18 + 17));
+            for (int g = 1; g < G; ++g) mn = fmaxf(mn, at(qb, g, 17));
             const float a0 = mrow[qb] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((mrow[qb] - mn) * scale_log2);
 #pragma unroll
             for (int df = 0; df < 4; ++df) oacc[qb][df] *= a0;
             lacc[qb][0] *= a0;
 #pragma unroll
             for (int g = 1; g < G; ++g) {
-                const float mg = at(g, qb * 18 + 17);
+                const float mg = at(qb, g, 17);
                 const float ag = mg == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((mg - mn) * scale_log2);
 #pragma unroll
                 for (int df = 0; df < 4; ++df)
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) oacc[qb][df][e] += at(g, qb * 18 + df * 4 + e) * ag;
-                lacc[qb][0] += at(g, qb * 18 + 16) * ag;
+                    for (int e = 0; e < 4; ++e) oacc[qb][df][e] += at(qb, g, df * 4 + e) * ag;
+                lacc[qb][0] += at(qb, g, 16) * ag;
             }
         }
     }
