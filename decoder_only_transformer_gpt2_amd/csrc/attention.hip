@@ -64,8 +64,12 @@ __device__ __forceinline__ void lds_dma16(const uint16_t* src, uint16_t* lds_blo
     __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)(lds_block), 16, 0, 0);
 }
 
+// Register budget: with two groups (eight wavefronts, 64 KB of LDS) two workgroups share a CU only
+// at 128 VGPRs (four waves per SIMD); with one group, three 4-wave workgroups per CU (three waves per
+// SIMD) fill the CUs at B*H = 96, and the 168 VGPRs this allows remove the spills (B=8 H=12 T=1024:
+// 25.3 -> 23.6 us).
 template <int WAVES, int G>  // 32 queries per wavefront; G groups of WAVES wavefronts share the queries
-__global__ __launch_bounds__(64 * WAVES * G, 4) void attn_bf16_kernel(
+__global__ __launch_bounds__(64 * WAVES * G, G == 1 ? 3 : 4) void attn_bf16_kernel(
     const uint16_t* __restrict__ Q, int64_t qsb, int64_t qsh, int64_t qst, const uint16_t* __restrict__ K, int64_t ksb,
     int64_t ksh, int64_t kst, const uint16_t* __restrict__ V, int64_t vsb, int64_t vsh, int64_t vst,
     uint16_t* __restrict__ O, int64_t osb, int64_t osh, int64_t ost, int64_t osx, int B, int H, int T,
@@ -416,10 +420,11 @@ hipError_t attention_bf16(const uint16_t* q, const int64_t* qs, const uint16_t* 
     const int nqt = (T + 32 * WAVES - 1) / (32 * WAVES);
     // The causal grid is uneven (the last query tile attends to all keys). With at most two
     // workgroups per CU, two wavefront groups per workgroup split the key tiles, which halves the
-    // longest workgroups; with more workgroups, one group each. Measured at T=1024, H=12: B=4
-    // (384 workgroups) 22.4 us with two groups, 26.4 with one, 27.4 with four (one 16-wave
-    // workgroup per CU: its wavefronts run in lock step, so MFMA and VALU work no longer overlap
-    // across them); B=8 32.4 us with one group, 33.9 with two.
+    // longest workgroups; with more workgroups, one group each. Measured at T=1024, H=12 (with the
+    // register-staged tiles this kernel had before): B=4 (384 workgroups) 22.4 us with two groups,
+    // 26.4 with one, 27.4 with four (one 16-wave workgroup per CU: its wavefronts run in lock step,
+    // so MFMA and VALU work no longer overlap across them); B=8 32.4 us with one group, 33.9 with
+    // two. Now: B=4 18.3 us, B=8 23.6 us.
     const int nwg = nqt * B * H;
     const dim3 grid(nwg);
 #define GPT2_ATT_LAUNCH(G)                                                                                         \
