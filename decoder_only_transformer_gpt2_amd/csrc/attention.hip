@@ -73,7 +73,7 @@ __global__ __launch_bounds__(64 * WAVES * G, G == 1 ? 3 : 4) void attn_bf16_kern
     const uint16_t* __restrict__ Q, int64_t qsb, int64_t qsh, int64_t qst, const uint16_t* __restrict__ K, int64_t ksb,
     int64_t ksh, int64_t kst, const uint16_t* __restrict__ V, int64_t vsb, int64_t vsh, int64_t vst,
     uint16_t* __restrict__ O, int64_t osb, int64_t osh, int64_t ost, int64_t osx, int B, int H, int T,
-    float scale_log2) {
+    float scale_log2, int n_lone) {
     static_assert(WAVES == 4, "each wavefront of a group moves two of the eight 1 KB blocks of a K or V tile");
     constexpr int NQ = 2, QW = 16 * NQ;  // 16-query column blocks and queries per wavefront
     constexpr int QT = QW * WAVES, NG = 64 * WAVES;
@@ -86,8 +86,19 @@ __global__ __launch_bounds__(64 * WAVES * G, G == 1 ? 3 : 4) void attn_bf16_kern
     __shared__ __attribute__((aligned(1024))) uint16_t lds1[BUF];
 
     const int nqt = (T + QT - 1) / QT;
-    const int bh = blockIdx.x % (B * H);
-    const int qt = nqt - 1 - blockIdx.x / (B * H);
+    // Work unit u: query tiles longest first (u / (B*H) counts down from the last query tile).
+    // Workgroups are dispatched one per CU before any CU gets a second, and workgroup n_cu + i shares
+    // CU i with workgroup i. With n_lone CUs holding one workgroup (and n_pair = nwg - n_cu CUs two),
+    // the longest units go alone (ids n_pair .. n_cu-1) and the pairs match the next longest with
+    // the shortest (ids i and n_cu + i). n_lone = 0: plain longest-first order.
+    int u = blockIdx.x;
+    if (n_lone > 0) {
+        const int nwg = (int)gridDim.x, n_pair = nwg - (n_lone + (nwg - n_lone) / 2), n_cu = n_lone + n_pair;
+        const int bid = blockIdx.x;
+        u = bid >= n_cu ? nwg - 1 - (bid - n_cu) : bid >= n_pair ? bid - n_pair : n_lone + bid;
+    }
+    const int bh = u % (B * H);
+    const int qt = nqt - 1 - u / (B * H);
     const int b = bh / H, h = bh % H;
     const int q0 = qt * QT;
     const int t = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(t / GPT2_WAVE), lane = t % GPT2_WAVE;
@@ -412,6 +423,19 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(const float* __restrict__ 
 
 }  // namespace
 
+// Compute units of the current device (cached per device; 0 when the query fails).
+int cu_count() {
+    static int cached[64] = {};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    if (!cached[dev]) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+        cached[dev] = n;
+    }
+    return cached[dev];
+}
+
 hipError_t attention_bf16(const uint16_t* q, const int64_t* qs, const uint16_t* k, const int64_t* ks, const uint16_t* v,
                           const int64_t* vs, uint16_t* o, const int64_t* os, int B, int H, int T, hipStream_t s,
                           int64_t os_half) {
@@ -426,15 +450,18 @@ hipError_t attention_bf16(const uint16_t* q, const int64_t* qs, const uint16_t* 
     // so MFMA and VALU work no longer overlap across them); B=8 32.4 us with one group, 33.9 with
     // two. Now: B=4 18.3 us, B=8 23.6 us.
     const int nwg = nqt * B * H;
+    const int n_cu = cu_count();
     const dim3 grid(nwg);
-#define GPT2_ATT_LAUNCH(G)                                                                                         \
+#define GPT2_ATT_LAUNCH(G, LONE)                                                                                   \
     attn_bf16_kernel<WAVES, G><<<grid, dim3(64 * WAVES * G), 0, s>>>(q, qs[0], qs[1], qs[2], k, ks[0], ks[1], ks[2], \
                                                                      v, vs[0], vs[1], vs[2], o, os[0], os[1], os[2],  \
-                                                                     os_half, B, H, T, scale_log2)
-    if (nwg <= 512)
-        GPT2_ATT_LAUNCH(2);
-    else
-        GPT2_ATT_LAUNCH(1);
+                                                                     os_half, B, H, T, scale_log2, LONE)
+    if (nwg <= 2 * n_cu) {
+        // two workgroups fit a CU: n_cu - (nwg - n_cu) CUs get one
+        GPT2_ATT_LAUNCH(2, nwg > n_cu ? 2 * n_cu - nwg : 0);
+    } else {
+        GPT2_ATT_LAUNCH(1, 0);
+    }
 #undef GPT2_ATT_LAUNCH
     return hipGetLastError();
 }
