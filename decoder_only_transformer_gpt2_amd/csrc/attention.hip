@@ -68,18 +68,21 @@ __device__ __forceinline__ void lds_dma16(const uint16_t* src, uint16_t* lds_blo
 // at 128 VGPRs (four waves per SIMD); with one group, three 4-wave workgroups per CU (three waves per
 // SIMD) fill the CUs at B*H = 96, and the 168 VGPRs this allows remove the spills (B=8 H=12 T=1024:
 // 25.3 -> 23.6 us).
-template <int WAVES, int G>  // 32 queries per wavefront; G groups of WAVES wavefronts share the queries
+// LSE: also write each query's base-2 log-sum-exp of the scaled scores, log2 sum_j 2^(c s_j), summed
+// in fp32 over the unrounded probabilities (what the backward pass needs to form P again).
+template <int WAVES, int G, bool LSE>  // 32 queries per wavefront; G groups of WAVES wavefronts share the queries
 __global__ __launch_bounds__(64 * WAVES * G, G == 1 ? 3 : 4) void attn_bf16_kernel(
     const uint16_t* __restrict__ Q, int64_t qsb, int64_t qsh, int64_t qst, const uint16_t* __restrict__ K, int64_t ksb,
     int64_t ksh, int64_t kst, const uint16_t* __restrict__ V, int64_t vsb, int64_t vsh, int64_t vst,
     uint16_t* __restrict__ O, int64_t osb, int64_t osh, int64_t ost, int64_t osx, int B, int H, int T,
-    float scale_log2, int n_lone) {
+    float scale_log2, int n_lone, float* __restrict__ lse_out) {
     static_assert(WAVES == 4, "each wavefront of a group moves two of the eight 1 KB blocks of a K or V tile");
     constexpr int NQ = 2, QW = 16 * NQ;  // 16-query column blocks and queries per wavefront
     constexpr int QT = QW * WAVES, NG = 64 * WAVES;
     constexpr int BUF = G * 2 * TSZ;     // one ring slot: [group][K, V]
-    constexpr int NV = NQ * 18;          // merge values per lane (accumulators, denominator, maximum)
-    static_assert((G - 1) * 18 * NG * 4 <= BUF * 2, "merge area of one query block fits one ring slot");
+    constexpr int NVQ = LSE ? 19 : 18;   // merge values per lane and query block (accumulators, denominator,
+                                         // maximum, fp32 sum)
+    static_assert((G - 1) * NVQ * NG * 4 <= BUF * 2, "merge area of one query block fits one ring slot");
     // two ring slots as two objects, so that the compiler can tell the slot being read from the slot
     // the DMA is filling
     __shared__ __attribute__((aligned(1024))) uint16_t lds0[BUF];
@@ -127,8 +130,10 @@ __global__ __launch_bounds__(64 * WAVES * G, G == 1 ? 3 : 4) void attn_bf16_kern
     float mrow[NQ];       // reference maximum of the raw scores of this lane's queries
     float mthr[NQ];       // mrow + 8 / scale_log2: scores above it move the reference
     float mbias[NQ];      // mrow * scale_log2 (0 while mrow is -inf)
+    float lsum[NQ];       // (LSE) fp32 sum of this lane's unrounded probabilities, relative to mrow
 #pragma unroll
     for (int qb = 0; qb < NQ; ++qb) {
+        lsum[qb] = 0.f;
 #pragma unroll
         for (int i = 0; i < 4; ++i) oacc[qb][i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
         lacc[qb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
@@ -247,6 +252,7 @@ __global__ __launch_bounds__(64 * WAVES * G, G == 1 ? 3 : 4) void attn_bf16_kern
 #pragma unroll
                     for (int df = 0; df < 4; ++df) oacc[qb][df] *= alpha;
                     lacc[qb] *= alpha;
+                    if (LSE) lsum[qb] *= alpha;
                 }
             }
             // P^T in the B-operand layout: slot j of a lane holds key 32*hh + 4*g4 + j (j < 4) or
@@ -260,6 +266,8 @@ __global__ __launch_bounds__(64 * WAVES * G, G == 1 ? 3 : 4) void attn_bf16_kern
                 for (int m2 = 0; m2 < 2; ++m2)
 #pragma unroll
                     for (int e = 0; e < 4; ++e) p[m2][e] = __builtin_amdgcn_exp2f(fmaf(s[qb][m2][e], scale_log2, -mb));
+                if (LSE)
+                    lsum[qb] += ((p[0][0] + p[0][1]) + (p[0][2] + p[0][3])) + ((p[1][0] + p[1][1]) + (p[1][2] + p[1][3]));
                 u32x4_t pu;
                 pu[0] = pack_bf16x2(p[0][0], p[0][1]);
                 pu[1] = pack_bf16x2(p[0][2], p[0][3]);
@@ -301,15 +309,15 @@ __global__ __launch_bounds__(64 * WAVES * G, G == 1 ? 3 : 4) void attn_bf16_kern
     }
 
     if constexpr (G > 1) {
-        // groups 1..G-1 hand their (accumulators, denominator, reference maximum) to group 0,
-        // which rescales every part to the common maximum and adds them in group order. Merge
-        // area: value j of query block qb of a lane at [(group-1) * 18 + j][wave][lane] of ring
-        // slot qb, so that consecutive lanes write consecutive words.
+        // groups 1..G-1 hand their (accumulators, denominator, reference maximum, fp32 sum) to
+        // group 0, which rescales every part to the common maximum and adds them in group order.
+        // Merge area: value j of query block qb of a lane at [(group-1) * NVQ + j][wave][lane] of
+        // ring slot qb, so that consecutive lanes write consecutive words.
         __builtin_amdgcn_s_waitcnt(kWaitAllMem);
         __syncthreads();  // every wavefront is done with the ring
         auto at = [&](int qb, int g, int j) -> float& {
             float* part = reinterpret_cast<float*>(qb == 0 ? lds0 : lds1);
-            return part[((g - 1) * 18 + j) * NG + wv * 64 + lane];
+            return part[((g - 1) * NVQ + j) * NG + wv * 64 + lane];
         };
         if (grp > 0) {
 #pragma unroll
@@ -320,6 +328,7 @@ __global__ __launch_bounds__(64 * WAVES * G, G == 1 ? 3 : 4) void attn_bf16_kern
                     for (int e = 0; e < 4; ++e) at(qb, grp, df * 4 + e) = oacc[qb][df][e];
                 at(qb, grp, 16) = lacc[qb][0];
                 at(qb, grp, 17) = mrow[qb];
+                if (LSE) at(qb, grp, 18) = lsum[qb];
             }
         }
         __syncthreads();
@@ -333,6 +342,7 @@ __global__ __launch_bounds__(64 * WAVES * G, G == 1 ? 3 : 4) void attn_bf16_kern
 #pragma unroll
             for (int df = 0; df < 4; ++df) oacc[qb][df] *= a0;
             lacc[qb][0] *= a0;
+            if (LSE) lsum[qb] *= a0;
 #pragma unroll
             for (int g = 1; g < G; ++g) {
                 const float mg = at(qb, g, 17);
@@ -342,10 +352,23 @@ __global__ __launch_bounds__(64 * WAVES * G, G == 1 ? 3 : 4) void attn_bf16_kern
 #pragma unroll
                     for (int e = 0; e < 4; ++e) oacc[qb][df][e] += at(qb, g, df * 4 + e) * ag;
                 lacc[qb][0] += at(qb, g, 16) * ag;
+                if (LSE) lsum[qb] += at(qb, g, 18) * ag;
             }
+            mrow[qb] = mn;  // the reference of the merged state
         }
     }
 
+    if constexpr (LSE) {
+        // the four lanes of a query (g4 = 0..3) hold disjoint keys: add their sums
+#pragma unroll
+        for (int qb = 0; qb < NQ; ++qb) {
+            float tot = lsum[qb];
+            tot += __shfl_xor(tot, 16, GPT2_WAVE);
+            tot += __shfl_xor(tot, 32, GPT2_WAVE);
+            const int qi = qw + 16 * qb + r16;
+            if (g4 == 0 && qi < T) lse_out[(int64_t)bh * T + qi] = mrow[qb] * scale_log2 + __log2f(tot);
+        }
+    }
 #pragma unroll
     for (int qb = 0; qb < NQ; ++qb) {
         const int qi = qw + 16 * qb + r16;
@@ -438,7 +461,7 @@ int cu_count() {
 
 hipError_t attention_bf16(const uint16_t* q, const int64_t* qs, const uint16_t* k, const int64_t* ks, const uint16_t* v,
                           const int64_t* vs, uint16_t* o, const int64_t* os, int B, int H, int T, hipStream_t s,
-                          int64_t os_half) {
+                          int64_t os_half, float* lse_out) {
     const float scale_log2 = 0.125f * 1.4426950408889634f;  // (1/sqrt(64)) * log2(e)
     constexpr int WAVES = 4;  // 128 queries per workgroup
     const int nqt = (T + 32 * WAVES - 1) / (32 * WAVES);
@@ -452,10 +475,17 @@ hipError_t attention_bf16(const uint16_t* q, const int64_t* qs, const uint16_t* 
     const int nwg = nqt * B * H;
     const int n_cu = cu_count();
     const dim3 grid(nwg);
-#define GPT2_ATT_LAUNCH(G, LONE)                                                                                   \
-    attn_bf16_kernel<WAVES, G><<<grid, dim3(64 * WAVES * G), 0, s>>>(q, qs[0], qs[1], qs[2], k, ks[0], ks[1], ks[2], \
-                                                                     v, vs[0], vs[1], vs[2], o, os[0], os[1], os[2],  \
-                                                                     os_half, B, H, T, scale_log2, LONE)
+#define GPT2_ATT_LAUNCH1(G, LSE, LONE)                                                                             \
+    attn_bf16_kernel<WAVES, G, LSE><<<grid, dim3(64 * WAVES * G), 0, s>>>(                                         \
+        q, qs[0], qs[1], qs[2], k, ks[0], ks[1], ks[2], v, vs[0], vs[1], vs[2], o, os[0], os[1], os[2], os_half, B, H, \
+        T, scale_log2, LONE, lse_out)
+#define GPT2_ATT_LAUNCH(G, LONE)          \
+    do {                                  \
+        if (lse_out)                      \
+            GPT2_ATT_LAUNCH1(G, true, LONE);  \
+        else                              \
+            GPT2_ATT_LAUNCH1(G, false, LONE); \
+    } while (0)
     if (nwg <= 2 * n_cu) {
         // two workgroups fit a CU: n_cu - (nwg - n_cu) CUs get one
         GPT2_ATT_LAUNCH(2, nwg > n_cu ? 2 * n_cu - nwg : 0);
@@ -463,6 +493,7 @@ hipError_t attention_bf16(const uint16_t* q, const int64_t* qs, const uint16_t* 
         GPT2_ATT_LAUNCH(1, 0);
     }
 #undef GPT2_ATT_LAUNCH
+#undef GPT2_ATT_LAUNCH1
     return hipGetLastError();
 }
 

@@ -3,17 +3,17 @@
 //   §2.1-§2.2); given dO: dV = P^T dO, dP = dO V^T, dS = P * (dP - D) with D_i = dO_i . o_i,
 //   dQ = dS K / 8, dK = dS^T Q / 8.
 // Two kernels, each exact in its own accumulation order (no atomics):
-//   attn_bwd_dq_mfma: a workgroup owns 64 queries of one (b, h), a wavefront 16 of them. Pass 1
-//     over the key tiles finds each query's log-sum-exp (base 2); pass 2 forms S^T = K Q^T,
-//     P^T, dP^T = V dO^T and dS^T, and accumulates dQ^T += K^T dS^T. It also writes lse and D.
+//   attn_bwd_dq_mfma: a workgroup owns 64 queries of one (b, h), a wavefront 16 of them. With each
+//     query's log-sum-exp (base 2) from the forward pass, it forms S^T = K Q^T, P^T, dP^T = V dO^T
+//     and dS^T over the key tiles, and accumulates dQ^T += K^T dS^T. It also writes D.
 //   attn_bwd_dkv_mfma: a workgroup owns 64 keys, a wavefront 16 of them; over the query tiles on
 //     and after the diagonal it forms S = Q K^T, P, dP = dO V^T, dS and accumulates
 //     dV^T += dO^T P and dK^T += Q^T dS.
 // With v_mfma_f32_16x16x32_bf16 a lane's accumulator holds one column (lane % 16) and rows
 // 4 (lane / 16) + e; the four accumulators of a 64-row product therefore give every lane the 8
 // values of its column at rows {32 h + 4 g + j, 32 h + 16 + 4 g + j} (j < 4), which is directly
-// the B operand of the next product over those 32 rows; the A operand is read from a transposed
-// LDS tile with the same row order.
+// the B operand of the next product over those 32 rows; the A operand (the transposed tile) is read
+// from the same [row][d] LDS tile by ds_read_b64_tr_b16 with the same row order.
 #include "common.h"
 
 namespace gpt2k {
@@ -21,52 +21,13 @@ namespace {
 
 constexpr int BT = 64;        // rows (queries or keys) per tile
 constexpr int DHB = 64;       // head size
-constexpr int TSB = BT + 8;   // row stride of a transposed [d][row] tile (spreads rows over banks)
 
 __device__ __forceinline__ int swz(int row, int chunk) { return row * DHB + ((chunk ^ (row & 7)) << 3); }
 
-// Stage 64 rows x 64 dims of a bf16 matrix (row r at src + r * ld, rows >= n zero) into LDS as a
-// swizzled [row][d] tile and, when tr is set, also as a transposed [d][row] tile.
-__device__ __forceinline__ void stage_bf16(const uint16_t* __restrict__ src, long ld, int n, uint16_t* tile,
-                                           uint16_t* tr) {
-    for (int c = threadIdx.x; c < BT * 8; c += 256) {
-        const int r = c >> 3, ch = c & 7;
-        u32x4_t u = {0u, 0u, 0u, 0u};
-        if (r < n) u = *reinterpret_cast<const u32x4_t*>(src + (long)r * ld + ch * 8);
-        *reinterpret_cast<u32x4_t*>(&tile[swz(r, ch)]) = u;
-        if (tr) {
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                tr[(ch * 8 + 2 * j) * TSB + r] = (uint16_t)(u[j] & 0xffffu);
-                tr[(ch * 8 + 2 * j + 1) * TSB + r] = (uint16_t)(u[j] >> 16);
-            }
-        }
-    }
-}
-// The same for fp32 rows, rounded to bf16.
-__device__ __forceinline__ void stage_f32(const float* __restrict__ src, long ld, int n, uint16_t* tile, uint16_t* tr) {
-    for (int c = threadIdx.x; c < BT * 8; c += 256) {
-        const int r = c >> 3, ch = c & 7;
-        u32x4_t u = {0u, 0u, 0u, 0u};
-        if (r < n) {
-            const f32x4_t a = *reinterpret_cast<const f32x4_t*>(src + (long)r * ld + ch * 8);
-            const f32x4_t b = *reinterpret_cast<const f32x4_t*>(src + (long)r * ld + ch * 8 + 4);
-            u = u32x4_t{pack_bf16x2(a[0], a[1]), pack_bf16x2(a[2], a[3]), pack_bf16x2(b[0], b[1]), pack_bf16x2(b[2], b[3])};
-        }
-        *reinterpret_cast<u32x4_t*>(&tile[swz(r, ch)]) = u;
-        if (tr) {
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                tr[(ch * 8 + 2 * j) * TSB + r] = (uint16_t)(u[j] & 0xffffu);
-                tr[(ch * 8 + 2 * j + 1) * TSB + r] = (uint16_t)(u[j] >> 16);
-            }
-        }
-    }
-}
-
-// The same staging split in two, so that the next tile's global loads are in flight while the
-// current tile is computed: fetch_* loads this thread's two 16-byte chunks (rows >= n zero; fp32
-// rows kept as loaded), put_* rounds and writes them like stage_bf16 / stage_f32.
+// Staging of 64 rows x 64 dims into a swizzled [row][d] LDS tile, split in two so that the next
+// tile's global loads are in flight while the current tile is computed: fetch_* loads this
+// thread's two 16-byte chunks (rows >= n zero; fp32 rows kept as loaded), put_* rounds fp32 to
+// bf16 and writes them.
 struct Bf16Chunks {
     u32x4_t u[2];
 };
@@ -92,38 +53,42 @@ __device__ __forceinline__ void fetch_f32(const float* __restrict__ src, long ld
         }
     }
 }
-__device__ __forceinline__ void put_chunk(const u32x4_t& u, int c, uint16_t* tile, uint16_t* tr) {
+__device__ __forceinline__ void put_chunk(const u32x4_t& u, int c, uint16_t* tile) {
     const int r = c >> 3, ch = c & 7;
     *reinterpret_cast<u32x4_t*>(&tile[swz(r, ch)]) = u;
-    if (tr) {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            tr[(ch * 8 + 2 * j) * TSB + r] = (uint16_t)(u[j] & 0xffffu);
-            tr[(ch * 8 + 2 * j + 1) * TSB + r] = (uint16_t)(u[j] >> 16);
-        }
-    }
 }
-__device__ __forceinline__ void put_bf16(const Bf16Chunks& f, uint16_t* tile, uint16_t* tr) {
+__device__ __forceinline__ void put_bf16(const Bf16Chunks& f, uint16_t* tile) {
 #pragma unroll
-    for (int i = 0; i < 2; ++i) put_chunk(f.u[i], threadIdx.x + 256 * i, tile, tr);
+    for (int i = 0; i < 2; ++i) put_chunk(f.u[i], threadIdx.x + 256 * i, tile);
 }
-__device__ __forceinline__ void put_f32(const F32Chunks& f, uint16_t* tile, uint16_t* tr) {
+__device__ __forceinline__ void put_f32(const F32Chunks& f, uint16_t* tile) {
 #pragma unroll
     for (int i = 0; i < 2; ++i)
         put_chunk(u32x4_t{pack_bf16x2(f.a[i][0], f.a[i][1]), pack_bf16x2(f.a[i][2], f.a[i][3]),
                           pack_bf16x2(f.b[i][0], f.b[i][1]), pack_bf16x2(f.b[i][2], f.b[i][3])},
-                  threadIdx.x + 256 * i, tile, tr);
+                  threadIdx.x + 256 * i, tile);
 }
 
 // A operand from a swizzled [row][d] tile: row, dims kk * 32 + 8 g .. + 7
 __device__ __forceinline__ bf16x8_t a_rows(const uint16_t* tile, int row, int kk, int g) {
     return *reinterpret_cast<const bf16x8_t*>(&tile[swz(row, kk * 4 + g)]);
 }
-// A operand from a transposed [d][row] tile: row d, k-slots = rows {32 h + 4 g + j, 32 h + 16 + 4 g + j}
-__device__ __forceinline__ bf16x8_t a_trans(const uint16_t* tr, int d, int h, int g) {
-    const uint16_t* p = &tr[d * TSB + 32 * h + 4 * g];
-    const u32x2_t lo = *reinterpret_cast<const u32x2_t*>(p);
-    const u32x2_t hi = *reinterpret_cast<const u32x2_t*>(p + 16);
+// A operand of the transposed tile, A[d][k] = tile[k][d], read from the swizzled [row][d] tile by
+// ds_read_b64_tr_b16: lane (d = df*16 + lane%16, g = lane/16), k-slots = rows {32 h + 4 g + j, 32 h +
+// 16 + 4 g + j} (j < 4). In each sixteen lanes, lane 4r + q reads dims df*16 + 4q .. +3 of row
+// 32 h + 4 g + r (and of the row 16 further) and receives, transposed, dim df*16 + lane%16 of the
+// four rows. The rows' chunk permutation (row & 7) is the same for both row groups.
+typedef short short4_t __attribute__((vector_size(8)));
+__device__ __forceinline__ u32x2_t lds_read_tr16(const uint16_t* p) {
+    const short4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) short4_t*)(p));
+    return __builtin_bit_cast(u32x2_t, v);
+}
+__device__ __forceinline__ bf16x8_t a_trans(const uint16_t* tile, int df, int h, int lane) {
+    const int j = lane & 15, g = lane >> 4, r = j >> 2, q = j & 3;
+    const int row = 32 * h + 4 * g + r;
+    const int off = row * DHB + (((2 * df + (q >> 1)) ^ (row & 7)) << 3) + 4 * (q & 1);
+    const u32x2_t lo = lds_read_tr16(tile + off);
+    const u32x2_t hi = lds_read_tr16(tile + off + 16 * DHB);
     return __builtin_bit_cast(bf16x8_t, u32x4_t{lo[0], lo[1], hi[0], hi[1]});
 }
 // B operand over 32 rows from two accumulators (rows 4 g + e of fragments 2 h and 2 h + 1)
@@ -145,11 +110,10 @@ constexpr float kC2 = 0.125f * 1.4426950408889634f;  // (1 / sqrt(64)) * log2(e)
 
 __global__ __launch_bounds__(256) void attn_bwd_dq_mfma(const uint16_t* __restrict__ qkv, const uint16_t* __restrict__ o,
                                                         const float* __restrict__ dout, float* __restrict__ dqkv,
-                                                        float* __restrict__ lse_out, float* __restrict__ d_out, int B,
+                                                        const float* __restrict__ lse_in, float* __restrict__ d_out, int B,
                                                         int H, int T) {
     __shared__ __attribute__((aligned(16))) uint16_t sK[BT * DHB];
     __shared__ __attribute__((aligned(16))) uint16_t sV[BT * DHB];
-    __shared__ __attribute__((aligned(16))) uint16_t sKt[DHB * TSB];
     const int nqb = (T + BT - 1) / BT;
     const int bh = blockIdx.x % (B * H), qb = nqb - 1 - blockIdx.x / (B * H);  // longest first
     const int b = bh / H, h = bh % H, d = H * DHB;
@@ -184,45 +148,11 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_mfma(const uint16_t* __restri
     }
     dd += __shfl_xor(dd, 16);
     dd += __shfl_xor(dd, 32);
+    // this query's log-sum-exp (base 2, of the scores times c2), written by the forward pass
+    const float lse2 = qv ? lse_in[(long)bh * T + qi] : 0.f;
 
     const int n_kt = qb + 1;  // key tiles up to the diagonal
-    // pass 1: log-sum-exp of this lane's query (base 2, scores times c2)
-    float mx = -INFINITY, sm = 0.f;
-    for (int kt = 0; kt < n_kt; ++kt) {
-        const int k0 = kt * BT;
-        __syncthreads();
-        stage_bf16(base + d + (long)k0 * 3 * d, 3 * d, min(BT, T - k0), sK, nullptr);
-        __syncthreads();
-        if (k0 > qb * BT + 16 * w + 15) continue;  // wave-uniform: every key of the tile is after every query
-        f32x4_t s[4];
-#pragma unroll
-        for (int mf = 0; mf < 4; ++mf) {
-            s[mf] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int kk = 0; kk < 2; ++kk)
-                s[mf] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a_rows(sK, mf * 16 + r16, kk, g4), qf[kk], s[mf], 0, 0, 0);
-        }
-#pragma unroll
-        for (int mf = 0; mf < 4; ++mf)
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int key = k0 + mf * 16 + 4 * g4 + e;
-                if (key <= qi && key < T) {
-                    const float a = s[mf][e] * kC2;
-                    if (a > mx) {
-                        sm = sm * __builtin_amdgcn_exp2f(mx - a) + 1.f;
-                        mx = a;
-                    } else {
-                        sm += __builtin_amdgcn_exp2f(a - mx);
-                    }
-                }
-            }
-    }
-    lse_merge(mx, sm, __shfl_xor(mx, 16), __shfl_xor(sm, 16));
-    lse_merge(mx, sm, __shfl_xor(mx, 32), __shfl_xor(sm, 32));
-    const float lse2 = mx + __log2f(sm);
-
-    // pass 2: dQ^T += K^T dS^T over the key tiles
+    // dQ^T += K^T dS^T over the key tiles
     f32x4_t dq[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) dq[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
@@ -232,8 +162,8 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_mfma(const uint16_t* __restri
     for (int kt = 0; kt < n_kt; ++kt) {
         const int k0 = kt * BT;
         __syncthreads();
-        put_bf16(fk, sK, sKt);
-        put_bf16(fv, sV, nullptr);
+        put_bf16(fk, sK);
+        put_bf16(fv, sV);
         if (kt + 1 < n_kt) {
             const int k1 = k0 + BT, nk1 = min(BT, T - k1);
             fetch_bf16(base + d + (long)k1 * 3 * d, 3 * d, nk1, fk);
@@ -266,7 +196,7 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_mfma(const uint16_t* __restri
             const bf16x8_t dsf = b_pack(s[2 * hh], s[2 * hh + 1]);
 #pragma unroll
             for (int df = 0; df < 4; ++df)
-                dq[df] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a_trans(sKt, df * 16 + r16, hh, g4), dsf, dq[df], 0, 0, 0);
+                dq[df] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a_trans(sK, df, hh, lane), dsf, dq[df], 0, 0, 0);
         }
     }
     if (qv) {
@@ -274,10 +204,7 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_mfma(const uint16_t* __restri
 #pragma unroll
         for (int df = 0; df < 4; ++df)
             *reinterpret_cast<f32x4_t*>(out + df * 16 + 4 * g4) = dq[df] * 0.125f;
-        if (g4 == 0) {
-            lse_out[(long)bh * T + qi] = lse2;
-            d_out[(long)bh * T + qi] = dd;
-        }
+        if (g4 == 0) d_out[(long)bh * T + qi] = dd;
     }
 }
 
@@ -285,9 +212,7 @@ __global__ __launch_bounds__(256) void attn_bwd_dkv_mfma(const uint16_t* __restr
                                                          const float* __restrict__ lse, const float* __restrict__ dvec,
                                                          float* __restrict__ dqkv, int B, int H, int T) {
     __shared__ __attribute__((aligned(16))) uint16_t sQ[BT * DHB];
-    __shared__ __attribute__((aligned(16))) uint16_t sQt[DHB * TSB];
     __shared__ __attribute__((aligned(16))) uint16_t sG[BT * DHB];
-    __shared__ __attribute__((aligned(16))) uint16_t sGt[DHB * TSB];
     __shared__ float sL[BT], sD[BT];
     const int nkb = (T + BT - 1) / BT;
     const int bh = blockIdx.x % (B * H), kb = blockIdx.x / (B * H);  // most query tiles first
@@ -323,8 +248,8 @@ __global__ __launch_bounds__(256) void attn_bwd_dkv_mfma(const uint16_t* __restr
     for (int qt = kb; qt < nkb; ++qt) {
         const int q0 = qt * BT, nq = min(BT, T - q0);
         __syncthreads();
-        put_bf16(fq, sQ, sQt);
-        put_f32(fg, sG, sGt);
+        put_bf16(fq, sQ);
+        put_f32(fg, sG);
         if (t < BT) {
             sL[t] = fl;
             sD[t] = fd;
@@ -359,8 +284,8 @@ __global__ __launch_bounds__(256) void attn_bwd_dkv_mfma(const uint16_t* __restr
             const bf16x8_t dsf = b_pack(dp[2 * hh], dp[2 * hh + 1]);
 #pragma unroll
             for (int df = 0; df < 4; ++df) {
-                dv[df] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a_trans(sGt, df * 16 + r16, hh, g4), pf, dv[df], 0, 0, 0);
-                dk[df] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a_trans(sQt, df * 16 + r16, hh, g4), dsf, dk[df], 0, 0, 0);
+                dv[df] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a_trans(sG, df, hh, lane), pf, dv[df], 0, 0, 0);
+                dk[df] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a_trans(sQ, df, hh, lane), dsf, dk[df], 0, 0, 0);
             }
         }
     }

@@ -233,9 +233,10 @@ hipError_t xent_mean(const float* nll, const int32_t* tgt, int M, float* loss, h
 
 // o element (b, h, t, e) at o + b*os[0] + h*os[1] + t*os[2] + (e / 32) * os_half + e % 32 (os_half = 32
 // for a plain row; the k-blocked layout of [B*T, H*64] has os = {T*32, 2*rows*32, 32}, os_half = rows*32).
+// lse_out (optional, [B*H*T] fp32): each query's base-2 log-sum-exp of its scaled scores, for the backward.
 hipError_t attention_bf16(const uint16_t* q, const int64_t* qs, const uint16_t* k, const int64_t* ks,
                           const uint16_t* v, const int64_t* vs, uint16_t* o, const int64_t* os, int B, int H,
-                          int T, hipStream_t s, int64_t os_half = 32);
+                          int T, hipStream_t s, int64_t os_half = 32, float* lse_out = nullptr);
 hipError_t attention_f32(const float* q, const int64_t* qs, const float* k, const int64_t* ks, const float* v,
                          const int64_t* vs, float* o, const int64_t* os, int B, int H, int T, hipStream_t s);
 
@@ -303,7 +304,8 @@ hipError_t gelu_backward(const float* u, float* g, long n, int erf_form, hipStre
 hipError_t xent_grad(const float* logits, long ld, int M, int V, int Vp, const int32_t* tgt, int32_t* cnt, float* nll,
                      void* dlogits, bool bf16, hipStream_t s);
 // Causal attention backward on qkv [B, T, 3, H, 64] and o [B, T, H, 64] (compute dtype) with the
-// output gradient dout fp32 [B, T, H * 64]: dqkv fp32 [B, T, 3 * H * 64]; lse, dvec: [B * H * T] scratch.
+// output gradient dout fp32 [B, T, H * 64]: dqkv fp32 [B, T, 3 * H * 64]; lse, dvec: [B * H * T]. In
+// bf16 mode lse is an input (the forward's attention_bf16 lse_out); in fp32 mode both are scratch.
 hipError_t attention_backward(const void* qkv, const void* o, const float* dout, float* dqkv, float* lse, float* dvec,
                               int B, int H, int T, bool bf16, hipStream_t s);
 hipError_t attention_backward_bf16(const uint16_t* qkv, const uint16_t* o, const float* dout, float* dqkv, float* lse,

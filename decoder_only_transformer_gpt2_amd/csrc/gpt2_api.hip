@@ -433,7 +433,7 @@ size_t grad_offset(const gpt2_model* m, int i) {
 struct TrainLayout {
     WorkspaceLayout fw;
     size_t layer0, per_layer;
-    size_t l_xin, l_xmid, l_a1, l_qkv, l_o, l_a2, l_u, l_h;  // inside one layer's block
+    size_t l_xin, l_xmid, l_a1, l_qkv, l_o, l_a2, l_u, l_h, l_lse;  // inside one layer's block
     size_t xfin, xf, logits, dx, dbuf, dbuf2, dact, dT, xT, wT, wteT, dlog, dlogT, part, bpart, lnpg, lnpb, lse, dvec, nll,
         cnt;
     size_t total;
@@ -467,6 +467,8 @@ TrainLayout train_layout(const gpt2_model* m, int B, int T) {
     L.l_a2 = ltake(L.Mp * d * as);
     L.l_u = ltake(L.M * f * 4);
     L.l_h = ltake(L.Mp * f * as);
+    // bf16: each query's log-sum-exp from the forward attention, read by the attention backward
+    L.l_lse = ltake(is_bf16(m) ? (size_t)B * c.n_head * T * 4 : 0);
     L.per_layer = lo;
     L.layer0 = take(L.per_layer * c.n_layer);
     L.xfin = take(L.M * d * 4);
@@ -489,7 +491,7 @@ TrainLayout train_layout(const gpt2_model* m, int B, int T) {
     L.bpart = take(is_bf16(m) ? (size_t)((L.Mk + 63) / 64) * (3 * d + d + f + d) * c.n_layer * 4 : 0);
     L.lnpg = take((size_t)gpt2k::ln_backward_blocks((int)L.M) * d * 4);
     L.lnpb = take((size_t)gpt2k::ln_backward_blocks((int)L.M) * d * 4);
-    L.lse = take((size_t)B * c.n_head * T * 4);
+    L.lse = take(is_bf16(m) ? 0 : (size_t)B * c.n_head * T * 4);  // fp32 mode: the backward finds it
     L.dvec = take((size_t)B * c.n_head * T * 4);
     L.nll = take(L.M * 4);
     L.cnt = take(4);
@@ -529,7 +531,8 @@ gpt2_status enqueue_train_forward(const gpt2_model* m, const int32_t* tokens, co
             GPT2_HIP(gpt2k::attention_bf16(reinterpret_cast<const uint16_t*>(qkv), qs,
                                            reinterpret_cast<const uint16_t*>(qkv + d * as), qs,
                                            reinterpret_cast<const uint16_t*>(qkv + 2 * d * as), qs,
-                                           reinterpret_cast<uint16_t*>(o), os, B, H, T, s));
+                                           reinterpret_cast<uint16_t*>(o), os, B, H, T, s, 32,
+                                           reinterpret_cast<float*>(lay(l, L.l_lse))));
         else
             GPT2_HIP(gpt2k::attention_f32(reinterpret_cast<const float*>(qkv), qs,
                                           reinterpret_cast<const float*>(qkv + d * as), qs,
@@ -651,9 +654,9 @@ gpt2_status enqueue_backward(const gpt2_model* m, const int32_t* tokens, int B, 
                                     c.ln_eps, lnpg, lnpb, G(I(LN2_W)), G(I(LN2_B)), s));
         // attention projection, attention, c_attn, ln_1
         GPT2_HIP(linear_back(dx, d, lay(l, L.l_o), d, I(APROJ_W), dbuf));
-        GPT2_HIP(gpt2k::attention_backward(lay(l, L.l_qkv), lay(l, L.l_o), dbuf, dbuf2,
-                                           reinterpret_cast<float*>(ws + L.lse), reinterpret_cast<float*>(ws + L.dvec), B,
-                                           H, T, bf, s));
+        float* lse = reinterpret_cast<float*>(bf ? lay(l, L.l_lse) : ws + L.lse);  // bf16: written by the forward
+        GPT2_HIP(gpt2k::attention_backward(lay(l, L.l_qkv), lay(l, L.l_o), dbuf, dbuf2, lse,
+                                           reinterpret_cast<float*>(ws + L.dvec), B, H, T, bf, s));
         GPT2_HIP(linear_back(dbuf2, 3 * d, lay(l, L.l_a1), d, I(ATTN_W), dbuf));
         GPT2_HIP(gpt2k::ln_backward(reinterpret_cast<const float*>(lay(l, L.l_xin)), vecp(LN1_W), dbuf, dx, M, d,
                                     c.ln_eps, lnpg, lnpb, G(I(LN1_W)), G(I(LN1_B)), s));
