@@ -157,8 +157,8 @@ def cpu_baseline(weights: dict, tokens: np.ndarray, s: synth.ModelShape):
 
 def decode_step_bytes(s: synth.ModelShape, B: int, keys: float) -> float:
     """HBM bytes one cached decode step reads at least: every block matrix and wte (the tied head)
-    once in bf16, row-major and unpadded (the few-row products stream them; the k-blocked and
-    transposed copies are not touched), the fp32 vectors, one wpe row, and the cached K and V of
+    once in bf16, row-major and unpadded (the few-row products stream them; the k-blocked copies
+    are not touched), the fp32 vectors, one wpe row, and the cached K and V of
     `keys` positions for every layer and sequence (bf16)."""
     d, f, L = s.d_model, s.d_mlp, s.n_layer
     mats = L * (3 * d * d + d * d + f * d + d * f) + s.n_vocab * d

@@ -278,6 +278,10 @@ hipError_t colsum(const float* src, long ld, int R, int C, float* part, float* o
 // are left in part for a later colsum_reduce_multi; requires 16-byte strides and pointers.
 hipError_t transpose_colsum_partials(const float* src, long lds, int R, int C, uint16_t* dst, long ldd, int Rp,
                                      float* part, hipStream_t s);
+// fp32 [R, C] (row stride lds) -> bf16 [Rp, C] (row stride ldd; rows R..Rp-1 zero, Rp a multiple of 64),
+// with the column sums of every 64-row block left in part ([Rp / 64][C]) like transpose_colsum_partials.
+hipError_t convert_colsum_partials(const float* src, long lds, int R, int C, uint16_t* dst, long ldd, int Rp,
+                                   float* part, hipStream_t s);
 // out[c] = sum over b < nb of part[b * C + c] for up to kColsumSegs independent (part, nb, C, out)
 // segments in one launch, each in the fixed order of colsum.
 struct ColsumSeg {

@@ -1,0 +1,15 @@
+// bf16 products with operands stored reduction-dimension-outermost (gemm_bf16_tn.hip).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <cstdint>
+
+namespace gpt2k {
+// C[m][n] (fp32, row stride ldc) = sum_k A(k, m) B(k, n) for m < M, n < N, k < K (K a multiple of
+// 64). A(k, m) is A[k * lda + m] when a_mmajor, else A[m * lda + k]; likewise B (b_mmajor must be
+// set). a_lim / b_lim bound what is read: the row count of a K-major operand, the row width of an
+// M-major one (a multiple of 8); tiles reaching past it read duplicates of valid data, and only
+// C[m < M][n < N] is written. Rows k < K of an M-major operand must exist and hold finite values;
+// where the other operand's row k is zero they contribute nothing.
+hipError_t gemm_bf16_tn(const uint16_t* A, bool a_mmajor, long lda, int a_lim, const uint16_t* B, bool b_mmajor,
+                        long ldb, int b_lim, float* C, long ldc, int M, int N, int K, hipStream_t s);
+}  // namespace gpt2k

@@ -9,6 +9,7 @@
 
 #include "../../include/gpt2.h"
 #include "common.h"
+#include "gemm_tn.h"
 
 namespace {
 
@@ -52,7 +53,6 @@ struct gpt2_model {
     // bf16: byte offset of the k-blocked copy of each GEMM weight (wte and the four projections of
     // every layer), read by the tiled GEMMs of the forward; 0 for other tensors
     std::vector<size_t> kb_offset;
-    std::vector<size_t> t_offset;  // transposed copy per matrix (0: none), for the backward
     size_t weight_bytes = 0;
     void* weights = nullptr;  // borrowed device pointer, set by gpt2_load_weights
     bool loaded = false;
@@ -95,31 +95,13 @@ void build_layout(gpt2_model* m) {
         for (int l = 0; l < c.n_layer; ++l)
             for (int t : {ATTN_W, APROJ_W, FC_W, MPROJ_W}) kb(2 + l * PER_LAYER + t);
     }
-    // bf16: transposed copies for the backward's input-gradient products (dX = dY W reads W^T
-    // [in][out] as its K-contiguous operand), packed once at load instead of on every backward:
-    // rows padded to 256 (zero), wte^T with its columns padded to a multiple of 64 (zero).
-    m->t_offset.assign(m->slots.size(), 0);
-    if (c.dtype == GPT2_BF16) {
-        auto tcopy = [&](int i, int64_t ld) {
-            m->t_offset[i] = off;
-            off = align_up(off + (size_t)round_up(m->slots[i].cols, kRowPad) * ld * 2, kAlign);
-        };
-        tcopy(0, round_up(c.n_vocab, 64));
-        for (int l = 0; l < c.n_layer; ++l)
-            for (int t : {ATTN_W, APROJ_W, FC_W, MPROJ_W}) tcopy(2 + l * PER_LAYER + t, m->slots[2 + l * PER_LAYER + t].rows);
-    }
     m->weight_bytes = off;
 }
-
-// Row stride (elements) of the transposed copy of matrix idx: its source row count, padded to a
-// multiple of 64 for wte (the reduction length of the lm_head input gradient).
-int64_t t_ld(const gpt2_model* m, int idx) { return idx == 0 ? round_up(m->cfg.n_vocab, 64) : m->slots[idx].rows; }
 
 const void* wptr(const gpt2_model* m, int idx) { return static_cast<const char*>(m->weights) + m->slots[idx].offset; }
 const void* wptr_kb(const gpt2_model* m, int idx) {
     return static_cast<const char*>(m->weights) + m->kb_offset[idx];
 }
-const void* wptr_t(const gpt2_model* m, int idx) { return static_cast<const char*>(m->weights) + m->t_offset[idx]; }
 int layer_idx(int l, int t) { return 2 + l * PER_LAYER + t; }
 
 WorkspaceLayout ws_layout(const gpt2_model* m, int B, int T) {
@@ -478,14 +460,14 @@ TrainLayout train_layout(const gpt2_model* m, int B, int T) {
     L.dbuf = take(L.M * L.wide * 4);
     L.dbuf2 = take(L.M * L.wide * 4);
     L.dact = take(L.Mp * L.wide * as);
-    L.dT = take(L.rows_dT * L.Mk * as);
-    L.xT = take(L.rows_x * L.Mk * as);
-    // transposed weights: packed with the weights in bf16 mode, transposed per backward in fp32 mode
-    const bool wt_packed = is_bf16(m);
-    L.wT = take(wt_packed ? 0 : L.rows_w * L.wide * as);
-    L.wteT = take(wt_packed ? 0 : round_up(d, kRowPad) * L.Vp * as);
+    // transposed operands (fp32 mode only: the bf16 products read M-major operands directly)
+    const bool tr_ops = !is_bf16(m);
+    L.dT = take(tr_ops ? L.rows_dT * L.Mk * as : 0);
+    L.xT = take(tr_ops ? L.rows_x * L.Mk * as : 0);
+    L.wT = take(tr_ops ? L.rows_w * L.wide * as : 0);
+    L.wteT = take(tr_ops ? round_up(d, kRowPad) * L.Vp * as : 0);
     L.dlog = take(L.Mp * L.Vp * as);
-    L.dlogT = take(L.Vr * L.Mk * as);
+    L.dlogT = take(tr_ops ? L.Vr * L.Mk * as : 0);
     L.part = take((size_t)std::max<int64_t>(gpt2k::colsum_blocks((int)L.M), (L.Mk + 63) / 64) * L.wide * 4);
     // bf16: the bias gradients' partial column sums of every layer, reduced in one launch at the end
     L.bpart = take(is_bf16(m) ? (size_t)((L.Mk + 63) / 64) * (3 * d + d + f + d) * c.n_layer * 4 : 0);
@@ -563,8 +545,9 @@ gpt2_status enqueue_train_forward(const gpt2_model* m, const int32_t* tokens, co
 }
 
 // The backward pass: every gradient into grads (fp32, grad_offset layout), the layers in reverse.
-// Each weight gradient dW = dY^T X and input gradient dX = dY W is a GEMM C = A B^T on copies
-// transposed here (A and B both K-contiguous, K padded with zeros).
+// bf16: each weight gradient dW = dY^T X reduces over the rows of dY and X, read as M-major operands
+// (gemm_bf16_tn), and each input gradient dX = dY W reads W [out][in] with the reduction over its
+// rows; fp32: both are C = A B^T GEMMs on copies transposed here (K padded with zeros).
 gpt2_status enqueue_backward(const gpt2_model* m, const int32_t* tokens, int B, int T, float* grads, char* ws,
                              const TrainLayout& L, hipStream_t s) {
     const gpt2_config_t& c = m->cfg;
@@ -608,12 +591,20 @@ gpt2_status enqueue_backward(const gpt2_model* m, const int32_t* tokens, int B, 
     const int nbp = (int)((Mk + 63) / 64);
     auto linear_back = [&](const float* dy, int n_out, const void* x_act, int n_in, int widx, float* dx_out) -> hipError_t {
         hipError_t e;
-        if (bf) {  // bias gradient partials (column sums of dy) from the same pass as the transpose of dy
-            if ((e = gpt2k::transpose_colsum_partials(dy, n_out, M, n_out, reinterpret_cast<uint16_t*>(dT), Mk, Mk,
-                                                      bpart, s)) != hipSuccess)
+        if (bf) {
+            // dy -> bf16 rows (zero from M to Mk) with the bias gradient's column-sum partials
+            uint16_t* dy16 = reinterpret_cast<uint16_t*>(dact);
+            if ((e = gpt2k::convert_colsum_partials(dy, n_out, M, n_out, dy16, n_out, Mk, bpart, s)) != hipSuccess)
                 return e;
             bsegs.push_back({bpart, G(widx + 1), nbp, n_out});
             bpart += (size_t)nbp * n_out;
+            // dW [n_out, n_in] = sum over rows m < Mk of dy[m]^T x[m]
+            if ((e = gpt2k::gemm_bf16_tn(dy16, true, n_out, n_out, static_cast<const uint16_t*>(x_act), true, n_in, n_in,
+                                         G(widx), n_in, n_out, n_in, Mk, s)) != hipSuccess)
+                return e;
+            // dX [M, n_in] = dy W, W [n_out][n_in] reduced over its rows
+            return gpt2k::gemm_bf16_tn(dy16, false, n_out, Mk, static_cast<const uint16_t*>(wptr(m, widx)), true, n_in,
+                                       n_in, dx_out, n_in, M, n_in, n_out, s);
         } else {
             if ((e = gpt2k::colsum(dy, n_out, M, n_out, part, G(widx + 1), s)) != hipSuccess) return e;
             if ((e = tr(dy, false, n_out, M, n_out, dT, Mk, Mk)) != hipSuccess) return e;
@@ -621,23 +612,36 @@ gpt2_status enqueue_backward(const gpt2_model* m, const int32_t* tokens, int B, 
         if ((e = tr(x_act, true, n_in, M, n_in, xT, Mk, Mk)) != hipSuccess) return e;
         if ((e = gemm_nt(dT, pad(n_out), xT, pad(n_in), G(widx), n_out, n_in, Mk, n_in)) != hipSuccess) return e;
         if ((e = to_act(dy, n_out, dact)) != hipSuccess) return e;
-        const void* wt = wT;  // W^T: packed at load (bf16), else transposed here
-        if (m->t_offset[widx])
-            wt = wptr_t(m, widx);
-        else if ((e = tr(wptr(m, widx), true, n_in, n_out, n_in, wT, n_out, n_out)) != hipSuccess)
-            return e;
-        return gemm_nt(dact, Mp, wt, pad(n_in), dx_out, M, n_in, n_out, n_in);
+        if ((e = tr(wptr(m, widx), true, n_in, n_out, n_in, wT, n_out, n_out)) != hipSuccess) return e;
+        return gemm_nt(dact, Mp, wT, pad(n_in), dx_out, M, n_in, n_out, n_in);
     };
+    if (bf && Mk > M) {
+        // rows M .. Mk-1 of the M-major operands: zero (the reductions run over Mk rows)
+        const size_t pr = (size_t)(Mk - M);
+        for (int l = 0; l < c.n_layer; ++l) {
+            GPT2_HIP(hipMemsetAsync(lay(l, L.l_a1) + (size_t)M * d * 2, 0, pr * d * 2, s));
+            GPT2_HIP(hipMemsetAsync(lay(l, L.l_o) + (size_t)M * d * 2, 0, pr * d * 2, s));
+            GPT2_HIP(hipMemsetAsync(lay(l, L.l_a2) + (size_t)M * d * 2, 0, pr * d * 2, s));
+            GPT2_HIP(hipMemsetAsync(lay(l, L.l_h) + (size_t)M * f * 2, 0, pr * f * 2, s));
+        }
+        GPT2_HIP(hipMemsetAsync(ws + L.xf + (size_t)M * d * 2, 0, pr * d * 2, s));
+        GPT2_HIP(hipMemsetAsync(ws + L.dlog + (size_t)M * Vp * 2, 0, pr * Vp * 2, s));
+    }
     // lm_head: dxf = dlogits wte, dwte (head part) = dlogits^T xf
-    const void* wteT = ws + L.wteT;
-    if (m->t_offset[0])
-        wteT = wptr_t(m, 0);
-    else
+    if (bf) {
+        const uint16_t* dl16 = reinterpret_cast<const uint16_t*>(ws + L.dlog);
+        // wte [V rows, zero-padded past V][d], reduced over its rows (Vp of them)
+        GPT2_HIP(gpt2k::gemm_bf16_tn(dl16, false, Vp, Mp, static_cast<const uint16_t*>(wptr(m, 0)), true, d, d, dbuf, d,
+                                     M, d, Vp, s));
+        GPT2_HIP(gpt2k::gemm_bf16_tn(dl16, true, Vp, Vp, reinterpret_cast<const uint16_t*>(ws + L.xf), true, d, d, G(0),
+                                     d, V, d, Mk, s));
+    } else {
         GPT2_HIP(tr(wptr(m, 0), true, d, V, d, ws + L.wteT, Vp, Vp));
-    GPT2_HIP(gemm_nt(ws + L.dlog, Mp, wteT, pad(d), dbuf, M, d, Vp, d));
-    GPT2_HIP(tr(ws + L.dlog, true, Vp, M, Vp, ws + L.dlogT, Mk, Mk));
-    GPT2_HIP(tr(ws + L.xf, true, d, M, d, xT, Mk, Mk));
-    GPT2_HIP(gemm_nt(ws + L.dlogT, (int)L.Vr, xT, pad(d), G(0), V, d, Mk, d));
+        GPT2_HIP(gemm_nt(ws + L.dlog, Mp, ws + L.wteT, pad(d), dbuf, M, d, Vp, d));
+        GPT2_HIP(tr(ws + L.dlog, true, Vp, M, Vp, ws + L.dlogT, Mk, Mk));
+        GPT2_HIP(tr(ws + L.xf, true, d, M, d, xT, Mk, Mk));
+        GPT2_HIP(gemm_nt(ws + L.dlogT, (int)L.Vr, xT, pad(d), G(0), V, d, Mk, d));
+    }
     GPT2_HIP(hipMemsetAsync(dx, 0, (size_t)M * d * 4, s));
     const int ln_f = 2 + c.n_layer * PER_LAYER;
     GPT2_HIP(gpt2k::ln_backward(reinterpret_cast<float*>(ws + L.xfin), static_cast<const float*>(wptr(m, ln_f)), dbuf, dx,
@@ -768,12 +772,6 @@ gpt2_status gpt2_load_weights(gpt2_model* m, const void* const* src, int32_t n_s
                 GPT2_HIP(gpt2k::kblock_bf16(reinterpret_cast<const uint16_t*>(d),
                                             reinterpret_cast<uint16_t*>(static_cast<char*>(dst) + m->kb_offset[i]),
                                             s.rows_padded, (int)s.cols, stream));
-            if (m->t_offset[i]) {
-                char* t = static_cast<char*>(dst) + m->t_offset[i];
-                const int64_t ld = t_ld(m, i);
-                GPT2_HIP(hipMemsetAsync(t, 0, (size_t)round_up(s.cols, kRowPad) * ld * 2, stream));
-                GPT2_HIP(gpt2k::transpose(d, true, s.cols, (int)s.rows, (int)s.cols, t, true, ld, (int)ld, stream));
-            }
         } else {
             GPT2_HIP(gpt2k::convert(src[i], sb, d, false, s.rows, s.rows, stream));
         }

@@ -110,6 +110,47 @@ __global__ void __launch_bounds__(256) transpose_vec_kernel(const void* __restri
     }
 }
 
+// fp32 [R rows, C] (row stride lds) -> bf16 [Rp rows, C] (row stride ldd, rows R..Rp-1 zero), 16-byte
+// accesses on both sides, and the sums of each 64-row block's columns to colpart[blockIdx.y][c] in
+// the order of transpose_vec_kernel's (four 16-row quarters, each in row order, added in order).
+__global__ void __launch_bounds__(256) convert_colsum_kernel(const float* __restrict__ src, long lds, int R, int C,
+                                                             uint16_t* __restrict__ dst, long ldd, float* __restrict__ colpart) {
+    __shared__ float tile[64][65];
+    __shared__ float qsum[4][64];
+    const int c0 = blockIdx.x * 64, r0 = blockIdx.y * 64, t = threadIdx.x;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const int e = t + i * 256, rr = e >> 3, ck = (e & 7) * 8, r = r0 + rr, c = c0 + ck;
+        float v[8];
+        if (r < R && c + 8 <= C) {
+            const float4* p = reinterpret_cast<const float4*>(src + (long)r * lds + c);
+            const float4 a = p[0], b = p[1];
+            v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w; v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+        } else {
+#pragma unroll
+            for (int j = 0; j < 8; ++j) v[j] = (r < R && c + j < C) ? src[(long)r * lds + c + j] : 0.f;
+        }
+#pragma unroll
+        for (int j = 0; j < 8; ++j) tile[rr][ck + j] = v[j];
+        uint16_t* dp = dst + (long)r * ldd + c;
+        if (c + 8 <= C) {
+            *reinterpret_cast<u32x4_t*>(dp) = u32x4_t{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]),
+                                                      pack_bf16x2(v[4], v[5]), pack_bf16x2(v[6], v[7])};
+        } else {
+            for (int j = 0; j < 8 && c + j < C; ++j) dp[j] = f32_to_bf16_bits(v[j]);
+        }
+    }
+    __syncthreads();
+    const int cc = t & 63, q = t >> 6;
+    float a = 0.f;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) a += tile[q * 16 + j][cc];
+    qsum[q][cc] = a;
+    __syncthreads();
+    if (q == 0 && c0 + cc < C)
+        colpart[(long)blockIdx.y * C + c0 + cc] = ((qsum[0][cc] + qsum[1][cc]) + qsum[2][cc]) + qsum[3][cc];
+}
+
 // ------------------------------------------------------------------------------ column sums
 // part[b][c] = sum of src[r][c] over the 256 rows r of block b: four row groups of 64 rows per
 // column (eight loads in flight per thread), combined in group order.
@@ -757,6 +798,15 @@ hipError_t transpose_colsum_partials(const float* src, long lds, int R, int C, u
     if (!vec) return hipErrorInvalidValue;
     transpose_vec_kernel<false><<<dim3((C + 63) / 64, (Rp + 63) / 64), dim3(256), 0, s>>>(src, lds, R, C, dst, ldd, Rp,
                                                                                           part);
+    return hipGetLastError();
+}
+
+hipError_t convert_colsum_partials(const float* src, long lds, int R, int C, uint16_t* dst, long ldd, int Rp,
+                                   float* part, hipStream_t s) {
+    const bool vec = lds % 8 == 0 && ldd % 8 == 0 && reinterpret_cast<uintptr_t>(src) % 16 == 0 &&
+                     reinterpret_cast<uintptr_t>(dst) % 16 == 0 && Rp >= R && Rp % 64 == 0;
+    if (!vec) return hipErrorInvalidValue;
+    convert_colsum_kernel<<<dim3((C + 63) / 64, Rp / 64), dim3(256), 0, s>>>(src, lds, R, C, dst, ldd, part);
     return hipGetLastError();
 }
 
