@@ -246,7 +246,7 @@ __global__ __launch_bounds__(256) void attn_bwd_dkv_mfma(const uint16_t* __restr
     };
     fetch_q(kb * BT);
     for (int qt = kb; qt < nkb; ++qt) {
-        const int q0 = qt * BT, nq = min(BT, T - q0);
+        const int q0 = qt * BT;
         __syncthreads();
         put_bf16(fq, sQ);
         put_f32(fg, sG);

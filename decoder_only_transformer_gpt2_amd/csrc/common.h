@@ -106,16 +106,19 @@ __device__ __forceinline__ void row_ln_stats(const float* __restrict__ xr, int n
 }
 
 // row_ln_stats with the row read once into registers (n <= 4096): the same order, the same bits.
-__device__ __forceinline__ void row_ln_stats_reg(const float* __restrict__ xr, int n, float eps, float& mean,
-                                                 float& rstd) {
+// row_ln_load reads the row (float4 c = i*64 + lane into v[i], zeros past the end);
+// row_ln_stats_v reduces it.
+__device__ __forceinline__ void row_ln_load(const float* __restrict__ xr, int n, f32x4_t (&v)[16]) {
     const int lane = threadIdx.x % GPT2_WAVE, nq = n / 4;
     const f32x4_t* x4 = reinterpret_cast<const f32x4_t*>(xr);
-    f32x4_t v[16];
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
         const int c = lane + GPT2_WAVE * i;
         v[i] = c < nq ? x4[c] : f32x4_t{0.f, 0.f, 0.f, 0.f};
     }
+}
+__device__ __forceinline__ void row_ln_stats_v(const f32x4_t (&v)[16], int n, float eps, float& mean, float& rstd) {
+    const int lane = threadIdx.x % GPT2_WAVE, nq = n / 4;
     float s = 0.f;
 #pragma unroll
     for (int i = 0; i < 16; ++i)
@@ -196,11 +199,12 @@ hipError_t gemm_f32(const float* A, const float* W, const float* bias, void* C, 
                     int epi, int gelu_erf, const HeadOut& ho, hipStream_t s);
 // The same for M <= kSkinnyM rows (gemm_bf16 dispatches to it): 16 output columns per workgroup,
 // so the head partial count per row is ceil(N / 16). Needs a_rows >= 16 and w_rows >= N rounded
-// up to 16 readable rows.
+// up to 16 readable rows. w_kb: W is k-blocked ([K/32][w_rows][32]) instead of row-major.
 constexpr int kSkinnyM = 16;
 // Fusions of the few-row GEMM used by cached decoding:
 //   ln_x set: A is LayerNorm(ln_x rows; ln_g, ln_b, ln_eps) (fp32 [M, K] in; normalised and rounded
-//             to bf16 on the fly, the same bits the LayerNorm kernel writes); the A argument is unused;
+//             to bf16 into LDS, the same bits the LayerNorm kernel writes; K < 2048); the A
+//             argument is unused;
 //   kc set:   (bias epilogue of the fused QKV projection, N = 3d) columns [d, 2d) and [2d, 3d) of row m
 //             are also written as K and V of sequence m, position kv_pos, into the layer's cache
 //             ([B][H][kv_n_ctx][64] bf16 each).
@@ -216,7 +220,7 @@ struct SkinnyExtra {
 };
 hipError_t gemm_bf16_skinny(const uint16_t* A, const uint16_t* W, const float* bias, void* C, int M, int N, int K,
                             int ldc, int epi, int gelu_erf, int a_rows, int w_rows, const HeadOut& ho,
-                            const SkinnyExtra& ex, hipStream_t s);
+                            const SkinnyExtra& ex, hipStream_t s, bool w_kb = false);
 
 hipError_t argmax_reduce(const float* pv, const int32_t* pi, int M, int n_part, int32_t* out, hipStream_t s);
 

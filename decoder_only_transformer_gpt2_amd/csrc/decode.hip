@@ -5,23 +5,22 @@
 // full forward over the extended sequence.
 //
 // Decode attention is bound by reading the cache (HBM), not by arithmetic: one 1024-thread
-// workgroup per (b, h); scores are computed with one key per thread (its 128-byte row against q in LDS), the
-// softmax is online over chunks of 1024 keys (fp32, exp2 with the scale folded in), and the
-// weighted sum of V is split over 128 key groups x 8 chunks of 8 dimensions, each thread reading
-// 16-byte pieces of V rows with four rows in flight; the key groups are summed through LDS.
+// workgroup per (b, h), split into 128 groups of eight lanes. Group g takes keys g, g + 128, ...;
+// lane i of a group holds dimensions 8i .. 8i+7 of the query, of each of its keys and of its value
+// rows, so a wavefront's load covers eight whole rows. The K and V rows of up to eight keys per
+// group (four in fp32) are loaded together, one round trip per batch (1024 keys in bf16); a key's
+// score is the sum of the eight lanes' partial dot products (three butterfly steps). Each group
+// keeps its own running maximum, sum and weighted sum of V (online softmax in fp32, exp2 with the
+// scale folded in); at the end the groups are rescaled to the workgroup's maximum and summed
+// through LDS. (Splitting the keys of a (b, h) over several workgroups shortens this kernel, but
+// the projection that reads o then has to combine every split's state in each of its workgroups,
+// which costs as much as it saves.)
 #include "common.h"
 
 namespace gpt2k {
 namespace {
 
 constexpr int DHD = 64;      // head size
-constexpr int CHUNK = 1024;  // keys per softmax chunk
-
-template <bool BF16>
-__device__ __forceinline__ float load_elem(const void* p, size_t i) {
-    if (BF16) return bf16_bits_to_f32(static_cast<const uint16_t*>(p)[i]);
-    return static_cast<const float*>(p)[i];
-}
 
 template <bool BF16>
 __global__ __launch_bounds__(256) void kv_append_kernel(const void* __restrict__ qkv, int B, int T, int H, int pos0,
@@ -45,7 +44,7 @@ __global__ __launch_bounds__(256) void kv_append_kernel(const void* __restrict__
         *reinterpret_cast<const u32x4_t*>(src + 2 * d * esz);
 }
 
-// Eight consecutive elements of a cache row as fp32.
+// Eight consecutive elements (bf16 or fp32, 16-byte aligned) as fp32.
 template <bool BF16>
 __device__ __forceinline__ void load8(const void* base, size_t i, float (&v)[8]) {
     if (BF16) {
@@ -66,89 +65,103 @@ __device__ __forceinline__ void load8(const void* base, size_t i, float (&v)[8])
     }
 }
 
+// 16-byte (bf16) or 32-byte (fp32) piece of a cache row, kept raw until it is used.
+template <bool BF16>
+struct RowPiece {
+    u32x4_t u[BF16 ? 1 : 2];
+};
+template <bool BF16>
+__device__ __forceinline__ RowPiece<BF16> load_piece(const void* base, size_t i) {
+    RowPiece<BF16> r;
+    if constexpr (BF16) {
+        r.u[0] = *reinterpret_cast<const u32x4_t*>(static_cast<const uint16_t*>(base) + i);
+    } else {
+        r.u[0] = *reinterpret_cast<const u32x4_t*>(static_cast<const float*>(base) + i);
+        r.u[1] = *reinterpret_cast<const u32x4_t*>(static_cast<const float*>(base) + i + 4);
+    }
+    return r;
+}
+template <bool BF16>
+__device__ __forceinline__ float piece_elem(const RowPiece<BF16>& r, int e) {
+    if constexpr (BF16)
+        return bf16_bits_to_f32(e & 1 ? r.u[0][e >> 1] >> 16 : r.u[0][e >> 1] & 0xffffu);
+    else  // (not __builtin_bit_cast on the vector element: hipcc then read element 0 for every e)
+        return __uint_as_float(r.u[e >> 2][e & 3]);
+}
+
 constexpr int DT = 1024;  // threads of a decode-attention workgroup
 
 template <bool BF16>
 __global__ __launch_bounds__(DT) void decode_attn_kernel(const void* __restrict__ qkv, const void* __restrict__ kc,
                                                           const void* __restrict__ vc, void* __restrict__ o, int H,
                                                           int n_ctx, int n_keys, float scale_log2) {
-    constexpr int KG = DT / 8;  // key groups of the weighted sum (x 8 dimension chunks)
+    constexpr int KG = DT / 8;  // key groups of eight lanes
     constexpr int NWV = DT / GPT2_WAVE;
-    __shared__ float sq[DHD];
-    __shared__ float sp[CHUNK];
+    constexpr int KPB = BF16 ? 8 : 4;  // keys per group and batch
     __shared__ float red[NWV];
     __shared__ float so[KG][DHD + 1];
     __shared__ float sl[KG];
     const int bh = blockIdx.x, b = bh / H, h = bh % H;
     const int t = threadIdx.x, wave = t / GPT2_WAVE, lane = t % GPT2_WAVE;
-    const int kg = t / 8, dc = t % 8;  // this thread's key group and 8-dimension chunk
+    const int kg = t / 8, dc = t % 8;  // key group, 8-dimension piece
     const int d = H * DHD;
-    if (t < DHD) sq[t] = load_elem<BF16>(qkv, (size_t)b * 3 * d + h * DHD + t);
-    const size_t base = (size_t)bh * n_ctx * DHD;  // this (b, h)'s cache rows
-    float m_run = -INFINITY;                       // running maximum (base 2), the same in every thread
-    float oacc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    float lacc = 0.f;
-    __syncthreads();
-    for (int c0 = 0; c0 < n_keys; c0 += CHUNK) {
-        const int nk = min(CHUNK, n_keys - c0);
-        // scores, one key (a whole 64-element row) per thread
-        float lmax = -INFINITY;
-        for (int j = t; j < nk; j += DT) {
-            const size_t kr = base + (size_t)(c0 + j) * DHD;
+    float q[8];
+    load8<BF16>(qkv, (size_t)b * 3 * d + h * DHD + dc * 8, q);
+    const size_t base = (size_t)bh * n_ctx * DHD + dc * 8;  // this lane's piece of row 0 of (b, h)
+    float m_run = -INFINITY;  // the group's running maximum (base 2)
+    float lacc = 0.f, oacc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    for (int j0 = kg; j0 < n_keys; j0 += KG * KPB) {
+        RowPiece<BF16> kp[KPB], vp[KPB];
+#pragma unroll
+        for (int u = 0; u < KPB; ++u) {
+            const int j = j0 + u * KG;
+            if (j < n_keys) {
+                kp[u] = load_piece<BF16>(kc, base + (size_t)j * DHD);
+                vp[u] = load_piece<BF16>(vc, base + (size_t)j * DHD);
+            }
+        }
+        float sc[KPB];
+        float mb = -INFINITY;
+#pragma unroll
+        for (int u = 0; u < KPB; ++u) {
             float acc = 0.f;
 #pragma unroll
-            for (int c = 0; c < DHD / 8; ++c) {
-                float kv8[8];
-                load8<BF16>(kc, kr + c * 8, kv8);
-#pragma unroll
-                for (int e = 0; e < 8; ++e) acc = fmaf(sq[c * 8 + e], kv8[e], acc);
-            }
-            const float sv = acc * scale_log2;
-            sp[j] = sv;
-            lmax = fmaxf(lmax, sv);
+            for (int e = 0; e < 8; ++e) acc = fmaf(q[e], piece_elem<BF16>(kp[u], e), acc);
+            acc += __shfl_xor(acc, 1, 8);
+            acc += __shfl_xor(acc, 2, 8);
+            acc += __shfl_xor(acc, 4, 8);
+            sc[u] = j0 + u * KG < n_keys ? acc * scale_log2 : -INFINITY;
+            mb = fmaxf(mb, sc[u]);
         }
-#pragma unroll
-        for (int off = 32; off >= 1; off >>= 1) lmax = fmaxf(lmax, __shfl_xor(lmax, off, GPT2_WAVE));
-        if (lane == 0) red[wave] = lmax;
-        __syncthreads();
-        float cmax = red[0];
-#pragma unroll
-        for (int w = 1; w < NWV; ++w) cmax = fmaxf(cmax, red[w]);
-        const float m_new = fmaxf(m_run, cmax);  // finite: every chunk holds at least one key
+        const float m_new = fmaxf(m_run, mb);  // finite: key j0 is valid
         const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-        for (int j = t; j < nk; j += DT) sp[j] = __builtin_amdgcn_exp2f(sp[j] - m_new);
-        __syncthreads();
+        lacc *= alpha;
 #pragma unroll
         for (int e = 0; e < 8; ++e) oacc[e] *= alpha;
-        lacc *= alpha;
-        // weighted sum of V: 16-byte pieces of 32 rows per pass, four passes' loads in flight
-        int j = kg;
-        for (; j + 3 * KG < nk; j += 4 * KG) {
-            float v[4][8];
 #pragma unroll
-            for (int u = 0; u < 4; ++u) load8<BF16>(vc, base + (size_t)(c0 + j + u * KG) * DHD + dc * 8, v[u]);
+        for (int u = 0; u < KPB; ++u) {
+            if (j0 + u * KG < n_keys) {
+                const float p = __builtin_amdgcn_exp2f(sc[u] - m_new);
+                lacc += p;
 #pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                const float pj = sp[j + u * KG];
-#pragma unroll
-                for (int e = 0; e < 8; ++e) oacc[e] = fmaf(pj, v[u][e], oacc[e]);
-                lacc += pj;
+                for (int e = 0; e < 8; ++e) oacc[e] = fmaf(p, piece_elem<BF16>(vp[u], e), oacc[e]);
             }
         }
-        for (; j < nk; j += KG) {
-            float v[8];
-            load8<BF16>(vc, base + (size_t)(c0 + j) * DHD + dc * 8, v);
-            const float pj = sp[j];
-#pragma unroll
-            for (int e = 0; e < 8; ++e) oacc[e] = fmaf(pj, v[e], oacc[e]);
-            lacc += pj;
-        }
         m_run = m_new;
-        __syncthreads();  // sp and red are rewritten by the next chunk
     }
+    // the workgroup's maximum, then every group rescaled to it and summed through LDS
+    float wm = m_run;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) so[kg][dc * 8 + e] = oacc[e];
-    if (dc == 0) sl[kg] = lacc;
+    for (int off = 32; off >= 8; off >>= 1) wm = fmaxf(wm, __shfl_xor(wm, off, GPT2_WAVE));
+    if (lane == 0) red[wave] = wm;
+    __syncthreads();
+    float mx = red[0];
+#pragma unroll
+    for (int w = 1; w < NWV; ++w) mx = fmaxf(mx, red[w]);
+    const float sw = m_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run - mx);  // a group without keys: 0
+#pragma unroll
+    for (int e = 0; e < 8; ++e) so[kg][dc * 8 + e] = oacc[e] * sw;
+    if (dc == 0) sl[kg] = lacc * sw;
     __syncthreads();
     if (t < DHD) {
         float num = 0.f, den = 0.f;

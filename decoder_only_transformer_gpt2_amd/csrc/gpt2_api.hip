@@ -161,6 +161,11 @@ hipError_t linear(const gpt2_model* m, const void* A, int widx, int bidx, void* 
                   int epi, const gpt2k::HeadOut& ho, hipStream_t s, bool kb = false, bool c_kb = false) {
     const float* bias = bidx >= 0 ? static_cast<const float*>(wptr(m, bidx)) : nullptr;
     const int ge = m->cfg.gelu == GPT2_GELU_ERF;
+    // a few rows: the W-streaming kernel over the weight's k-blocked copy (whole cache lines)
+    if (is_bf16(m) && M <= gpt2k::kSkinnyM && !kb && !c_kb && m->kb_offset[widx])
+        return gpt2k::gemm_bf16_skinny(static_cast<const uint16_t*>(A), static_cast<const uint16_t*>(wptr_kb(m, widx)),
+                                       bias, C, M, N, K, (int)ldc, epi, ge, (int)round_up(M, kRowPad),
+                                       (int)m->slots[widx].rows_padded, ho, {}, s, true);
     if (is_bf16(m))
         return gpt2k::gemm_bf16(static_cast<const uint16_t*>(A),
                                 static_cast<const uint16_t*>(kb ? wptr_kb(m, widx) : wptr(m, widx)), bias, C, M, N, K,
@@ -233,11 +238,12 @@ gpt2_status enqueue_trunk(const gpt2_model* m, const int32_t* tokens, int B, int
     // q, k, v views of qkv [B, T, 3, H, 64]: strides (batch, head, token) in elements
     // cached decoding in bf16 with few rows: LayerNorms and the cache append fused into the
     // projections (fewer, larger launches)
-    const bool fuse = kv.from_cache && bf && M <= gpt2k::kSkinnyM;
+    const bool fuse = kv.from_cache && bf && M <= gpt2k::kSkinnyM && d < 2048;
     auto skinny = [&](int widx, int bidx, void* C, int N, int K, int epi, const gpt2k::SkinnyExtra& ex) {
-        return gpt2k::gemm_bf16_skinny(static_cast<const uint16_t*>(a), static_cast<const uint16_t*>(wptr(m, widx)),
+        return gpt2k::gemm_bf16_skinny(static_cast<const uint16_t*>(a), static_cast<const uint16_t*>(wptr_kb(m, widx)),
                                        static_cast<const float*>(wptr(m, bidx)), C, M, N, K, N, epi,
-                                       c.gelu == GPT2_GELU_ERF, (int)w.Mp, (int)m->slots[widx].rows_padded, {}, ex, s);
+                                       c.gelu == GPT2_GELU_ERF, (int)w.Mp, (int)m->slots[widx].rows_padded, {}, ex, s,
+                                       true);
     };
     const int64_t qs[3] = {(int64_t)T * 3 * d, 64, 3 * d};
     // bf16 with tiled GEMMs: the operands the GEMMs read (the LayerNorm outputs, the attention
