@@ -178,6 +178,12 @@ constexpr int kGemmF32BN = 64;
 hipError_t embed(const int32_t* tok, const void* wte, const void* wpe, float* x, int M, int T, int pos0, int d,
                  int n_vocab, bool bf16, int32_t* flags, hipStream_t s);
 int embed_flag_count(int M);
+// The embedding fused with the first LayerNorm (bf16 tables, k-blocked bf16 output y with kb_rows >= M
+// rows per block): writes x as embed() does and y as layernorm(x, g, b, y, ..., kb_rows) would, with
+// the same bits; the same token flags as embed().
+hipError_t embed_ln(const int32_t* tok, const uint16_t* wte, const uint16_t* wpe, float* x, const float* g,
+                    const float* b, uint16_t* y, int M, int T, int pos0, int n, int n_vocab, float eps, int kb_rows,
+                    int32_t* flags, hipStream_t s);
 
 // k-blocked layout of a bf16 matrix with `rows` rows and K columns (K a multiple of 32): the
 // 32-column blocks one after another, each holding all rows, [K/32][rows][32]. Element (r, k) sits

@@ -233,8 +233,22 @@ gpt2_status enqueue_trunk(const gpt2_model* m, const int32_t* tokens, int B, int
     void* qkv = ws + w.qkv;
     void* o = ws + w.o;
     void* hid = ws + w.hid;
-    GPT2_RUN(GPT2_K_EMBED, gpt2k::embed(tokens, wptr(m, 0), wptr(m, 1), x, M, T, kv.pos0, d, c.n_vocab, bf,
-                                        reinterpret_cast<int32_t*>(ws + w.flags), s));
+    // bf16 with tiled GEMMs: the operands the GEMMs read (the LayerNorm outputs, the attention
+    // output and the GELU output) are written k-blocked, Mp rows per 32-column block
+    const bool kbl = bf && M > gpt2k::kSkinnyM && !kv.from_cache;
+    const int Mp = kbl ? (int)w.Mp : 0;
+    // with k-blocked operands the first block's ln_1 is computed by the embedding launch
+    const bool embed_ln1 = kbl && n_layers > 0;
+    if (embed_ln1)
+        GPT2_RUN(GPT2_K_EMBED, gpt2k::embed_ln(tokens, static_cast<const uint16_t*>(wptr(m, 0)),
+                                               static_cast<const uint16_t*>(wptr(m, 1)), x,
+                                               static_cast<const float*>(wptr(m, layer_idx(0, LN1_W))),
+                                               static_cast<const float*>(wptr(m, layer_idx(0, LN1_B))),
+                                               static_cast<uint16_t*>(a), M, T, kv.pos0, d, c.n_vocab, c.ln_eps, Mp,
+                                               reinterpret_cast<int32_t*>(ws + w.flags), s));
+    else
+        GPT2_RUN(GPT2_K_EMBED, gpt2k::embed(tokens, wptr(m, 0), wptr(m, 1), x, M, T, kv.pos0, d, c.n_vocab, bf,
+                                            reinterpret_cast<int32_t*>(ws + w.flags), s));
     // q, k, v views of qkv [B, T, 3, H, 64]: strides (batch, head, token) in elements
     // cached decoding in bf16 with few rows: LayerNorms and the cache append fused into the
     // projections (fewer, larger launches)
@@ -246,10 +260,6 @@ gpt2_status enqueue_trunk(const gpt2_model* m, const int32_t* tokens, int B, int
                                        true);
     };
     const int64_t qs[3] = {(int64_t)T * 3 * d, 64, 3 * d};
-    // bf16 with tiled GEMMs: the operands the GEMMs read (the LayerNorm outputs, the attention
-    // output and the GELU output) are written k-blocked, Mp rows per 32-column block
-    const bool kbl = bf && M > gpt2k::kSkinnyM && !kv.from_cache;
-    const int Mp = kbl ? (int)w.Mp : 0;
     const int64_t os[3] = {kbl ? (int64_t)T * 32 : (int64_t)T * d, kbl ? (int64_t)2 * Mp * 32 : 64, kbl ? 32 : d};
     const int64_t os_half = kbl ? (int64_t)Mp * 32 : 32;
     const size_t as = act_size(m);
@@ -276,7 +286,8 @@ gpt2_status enqueue_trunk(const gpt2_model* m, const int32_t* tokens, int B, int
             ex.kv_pos = kv.pos0;
             GPT2_RUN(GPT2_K_QKV, skinny(L(ATTN_W), L(ATTN_B), qkv, 3 * d, d, gpt2k::EPI_BIAS, ex));
         } else {
-            GPT2_RUN(GPT2_K_LN, gpt2k::layernorm(x, vecp(LN1_W), vecp(LN1_B), a, M, d, c.ln_eps, bf, s, Mp));
+            if (!(embed_ln1 && l == 0))
+                GPT2_RUN(GPT2_K_LN, gpt2k::layernorm(x, vecp(LN1_W), vecp(LN1_B), a, M, d, c.ln_eps, bf, s, Mp));
             GPT2_RUN(GPT2_K_QKV,
                      linear(m, a, L(ATTN_W), L(ATTN_B), qkv, M, 3 * d, d, 3 * d, gpt2k::EPI_BIAS, {}, s, kbl));
             if (kv.cache) GPT2_RUN(GPT2_K_KV, gpt2k::kv_append(qkv, B, T, H, kv.pos0, kc, vc, c.n_ctx, bf, s));
@@ -881,7 +892,7 @@ gpt2_status gpt2_forward_repeat(const gpt2_model* m, const int32_t* tokens, int3
                                 int32_t repeats, hipEvent_t ev_before, hipEvent_t ev_after) {
     const gpt2_status st = check_run_args(m, tokens, B, T, logits, ws_dev, ws_bytes);
     if (st != GPT2_OK) return st;
-    if (launch < 0 || launch >= gpt2_forward_launches(m, argmax != nullptr, nullptr, 0) || repeats < 1)
+    if (launch < 0 || launch >= gpt2_forward_launches(m, B, T, argmax != nullptr, nullptr, 0) || repeats < 1)
         return GPT2_EINVAL;
     Sequencer q{s};
     q.rep_idx = launch;
@@ -891,15 +902,16 @@ gpt2_status gpt2_forward_repeat(const gpt2_model* m, const int32_t* tokens, int3
     return enqueue_forward(m, tokens, B, T, logits, argmax, static_cast<char*>(ws_dev), q);
 }
 
-int32_t gpt2_forward_launches(const gpt2_model* m, int32_t with_argmax, int32_t* kinds, int32_t cap) {
-    if (!m) return 0;
+int32_t gpt2_forward_launches(const gpt2_model* m, int32_t B, int32_t T, int32_t with_argmax, int32_t* kinds,
+                              int32_t cap) {
+    if (!m || B < 1 || T < 1 || T > m->cfg.n_ctx) return 0;
     Sequencer q{nullptr};
     q.dry = true;
     q.kinds = kinds;
     q.cap = kinds ? cap : 0;
     // a dry run touches no memory: the pointers only need to be non-null where the path branches
     int32_t dummy = 0;
-    if (enqueue_forward(m, &dummy, 1, 1, nullptr, with_argmax ? &dummy : nullptr, nullptr, q) != GPT2_OK) return 0;
+    if (enqueue_forward(m, &dummy, B, T, nullptr, with_argmax ? &dummy : nullptr, nullptr, q) != GPT2_OK) return 0;
     return q.idx;
 }
 

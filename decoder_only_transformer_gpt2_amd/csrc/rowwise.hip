@@ -328,6 +328,85 @@ __global__ __launch_bounds__(64 * WAVES) void layernorm_kb_kernel(const float* _
     }
 }
 
+// The embedding gather-add fused with the first block's ln_1, for bf16 tables and a k-blocked bf16
+// LayerNorm output: each wavefront forms its row of x in registers with the adds of embed_kernel,
+// stores it (the residual stream), and normalises it with the arithmetic of layernorm_kb_kernel
+// (the same sums in the same order), so x and the LayerNorm output carry exactly the bits of the two
+// launches this one replaces, and x is not read back from memory. Four rows per workgroup, the token
+// flags as in embed_kernel.
+template <int NV>
+__global__ __launch_bounds__(256) void embed_ln_kb_kernel(const int32_t* __restrict__ tok,
+                                                          const uint16_t* __restrict__ wte,
+                                                          const uint16_t* __restrict__ wpe, float* __restrict__ x,
+                                                          const float* __restrict__ g, const float* __restrict__ b,
+                                                          uint16_t* __restrict__ y, int M, int T, int pos0, int n,
+                                                          int n_vocab, float eps, int kb_rows,
+                                                          int32_t* __restrict__ flags) {
+    extern __shared__ __attribute__((aligned(16))) uint16_t sy[];  // [kRowsPerBlock][n + 8]
+    const int wave = threadIdx.x / GPT2_WAVE, lane = threadIdx.x % GPT2_WAVE;
+    const int r0 = blockIdx.x * kRowsPerBlock, row = r0 + wave, nq = n / 4, sp = n + 8;
+    const int rr = min(row, M - 1);  // rows past M compute on a valid row and store nothing
+    int t = tok[rr];
+    const int bad = row < M && (t < 0 || t >= n_vocab);
+    t = t < 0 ? 0 : t >= n_vocab ? n_vocab - 1 : t;
+    const int pos = pos0 + rr % T;
+    const uint2* er = reinterpret_cast<const uint2*>(wte + (size_t)t * n);
+    const uint2* pr = reinterpret_cast<const uint2*>(wpe + (size_t)pos * n);
+    float4* xr = reinterpret_cast<float4*>(x + (size_t)rr * n);
+    float4 v[NV];
+    float s = 0.f;
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+        const int c = i * GPT2_WAVE + lane;
+        v[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (c < nq) {
+            const uint2 e = er[c], p = pr[c];
+            v[i].x = bf16_bits_to_f32(e.x & 0xffffu) + bf16_bits_to_f32(p.x & 0xffffu);
+            v[i].y = bf16_bits_to_f32(e.x >> 16) + bf16_bits_to_f32(p.x >> 16);
+            v[i].z = bf16_bits_to_f32(e.y & 0xffffu) + bf16_bits_to_f32(p.y & 0xffffu);
+            v[i].w = bf16_bits_to_f32(e.y >> 16) + bf16_bits_to_f32(p.y >> 16);
+            if (row < M) xr[c] = v[i];
+        }
+        s += (v[i].x + v[i].y) + (v[i].z + v[i].w);
+    }
+    const float mean = wave_sum(s) / (float)n;
+    float q = 0.f;
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+        const int c = i * GPT2_WAVE + lane;
+        if (c < nq) {
+            const float a0 = v[i].x - mean, a1 = v[i].y - mean, a2 = v[i].z - mean, a3 = v[i].w - mean;
+            q += (a0 * a0 + a1 * a1) + (a2 * a2 + a3 * a3);
+        }
+    }
+    const float var = wave_sum(q) / (float)n;
+    const float rstd = 1.0f / sqrtf(var + eps);
+    const float4* g4 = reinterpret_cast<const float4*>(g);
+    const float4* b4 = reinterpret_cast<const float4*>(b);
+    uint16_t* srow = sy + wave * sp;
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+        const int c = i * GPT2_WAVE + lane;
+        if (c < nq) {
+            const float4 gg = g4[c], bb = b4[c];
+            uint2 p;
+            p.x = pack_bf16x2((v[i].x - mean) * rstd * gg.x + bb.x, (v[i].y - mean) * rstd * gg.y + bb.y);
+            p.y = pack_bf16x2((v[i].z - mean) * rstd * gg.z + bb.z, (v[i].w - mean) * rstd * gg.w + bb.w);
+            *reinterpret_cast<uint2*>(srow + 4 * c) = p;
+        }
+    }
+    const int any_bad = __syncthreads_or(bad);  // also the barrier before the staged rows are read
+    if (threadIdx.x == 0) flags[blockIdx.x] = any_bad;
+    const int n_chunks = (n / 32) * kRowsPerBlock * 4;  // 16-byte chunks: per block, four rows of four
+    for (int ci = threadIdx.x; ci < n_chunks; ci += blockDim.x) {
+        const int blk = ci / (kRowsPerBlock * 4), rl = (ci / 4) % kRowsPerBlock, part = ci % 4;
+        const int r = r0 + rl;
+        if (r < M)
+            *reinterpret_cast<u32x4_t*>(y + ((size_t)blk * kb_rows + r) * 32 + part * 8) =
+                *reinterpret_cast<const u32x4_t*>(sy + rl * sp + blk * 32 + part * 8);
+    }
+}
+
 // One 16-byte chunk (8 columns) per thread: chunk j of row r goes to block j/4 of the k-blocked copy.
 __global__ __launch_bounds__(256) void kblock_kernel(const uint16_t* __restrict__ src, uint16_t* __restrict__ dst,
                                                      long rows, int K) {
@@ -371,6 +450,25 @@ hipError_t embed(const int32_t* tok, const void* wte, const void* wpe, float* x,
         embed_kernel<true><<<grid, block, 0, s>>>(tok, wte, wpe, x, M, T, pos0, d, n_vocab, flags);
     else
         embed_kernel<false><<<grid, block, 0, s>>>(tok, wte, wpe, x, M, T, pos0, d, n_vocab, flags);
+    return hipGetLastError();
+}
+
+hipError_t embed_ln(const int32_t* tok, const uint16_t* wte, const uint16_t* wpe, float* x, const float* g,
+                    const float* b, uint16_t* y, int M, int T, int pos0, int n, int n_vocab, float eps, int kb_rows,
+                    int32_t* flags, hipStream_t s) {
+    if (M < 1 || kb_rows < M || n % 32 || n > 4096) return hipErrorInvalidValue;
+    const dim3 grid(embed_flag_count(M)), block(256);
+    const size_t lds = (size_t)kRowsPerBlock * (n + 8) * 2;
+    const int nq = n / 4;
+#define GPT2_EMBED_LN(NV) \
+    embed_ln_kb_kernel<NV><<<grid, block, lds, s>>>(tok, wte, wpe, x, g, b, y, M, T, pos0, n, n_vocab, eps, kb_rows, flags)
+    if (nq <= 4 * GPT2_WAVE)
+        GPT2_EMBED_LN(4);
+    else if (nq <= 8 * GPT2_WAVE)
+        GPT2_EMBED_LN(8);
+    else
+        GPT2_EMBED_LN(16);
+#undef GPT2_EMBED_LN
     return hipGetLastError();
 }
 

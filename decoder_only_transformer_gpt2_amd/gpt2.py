@@ -48,7 +48,7 @@ SIGNATURES = {
     "gpt2_decode_step": (_I32, [_P, _P, _I32, _I32, _P, _SZ, _P, _P, _P, _SZ, _P]),
     "gpt2_forward_debug": (_I32, [_P, _P, _I32, _I32, _I32, _P, _P, _SZ, _P]),
     "gpt2_check": (_I32, [_P, _P, _I32, _I32, _P]),
-    "gpt2_forward_launches": (_I32, [_P, _I32, ctypes.POINTER(_I32), _I32]),
+    "gpt2_forward_launches": (_I32, [_P, _I32, _I32, _I32, ctypes.POINTER(_I32), _I32]),
     "gpt2_forward_repeat": (_I32, [_P, _P, _I32, _I32, _P, _P, _P, _SZ, _P, _I32, _I32, _P, _P]),
     "gpt2_forward_timed": (_I32, [_P, _P, _I32, _I32, _P, _P, _P, _SZ, _P, ctypes.POINTER(_P), ctypes.POINTER(_P), _I32]),
     "gpt2_attention": (_I32, [_P, _I64P, _P, _I64P, _P, _I64P, _P, _I64P, _I32, _I32, _I32, _I32, _I32, _P]),
@@ -394,11 +394,13 @@ class GPT2:
                                    _ptr(ws), ws.numel(), _stream(stream)), "gpt2_backward")
         return loss, grads
 
-    def launches(self, with_argmax: bool = True) -> list[str]:
-        """Kinds of the kernel launches one forward enqueues, in order."""
-        n = lib().gpt2_forward_launches(self._h, int(with_argmax), None, 0)
+    def launches(self, B: int, T: int, with_argmax: bool = True) -> list[str]:
+        """Kinds of the kernel launches one forward over B x T tokens enqueues, in order."""
+        n = lib().gpt2_forward_launches(self._h, B, T, int(with_argmax), None, 0)
+        if n == 0:
+            raise ValueError(f"no forward for B={B}, T={T}")
         kinds = (ctypes.c_int32 * n)()
-        lib().gpt2_forward_launches(self._h, int(with_argmax), kinds, n)
+        lib().gpt2_forward_launches(self._h, B, T, int(with_argmax), kinds, n)
         return [KERNEL_KINDS[k] for k in kinds]
 
     def forward_timed(self, tokens: torch.Tensor, logits: torch.Tensor, argmax: torch.Tensor | None,

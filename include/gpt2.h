@@ -200,9 +200,12 @@ typedef enum {
     GPT2_K_KV = 11
 } gpt2_kernel_kind;
 
-/* Number of kernel launches one gpt2_forward enqueues (with_argmax: argmax_dev != NULL); when
- * kinds != NULL, also writes the gpt2_kernel_kind of the first min(cap, count) launches. */
-int32_t gpt2_forward_launches(const gpt2_model* m, int32_t with_argmax, int32_t* kinds, int32_t cap);
+/* Number of kernel launches one gpt2_forward over B x T tokens enqueues (with_argmax: argmax_dev !=
+ * NULL); when kinds != NULL, also writes the gpt2_kernel_kind of the first min(cap, count)
+ * launches. The sequence depends on the shape (in bf16 with more than 16 rows the embedding launch
+ * also computes the first block's ln_1). 0 for a NULL handle or B < 1, T < 1, T > n_ctx. Host only. */
+int32_t gpt2_forward_launches(const gpt2_model* m, int32_t B, int32_t T, int32_t with_argmax, int32_t* kinds,
+                              int32_t cap);
 
 /* gpt2_forward that also records caller-created HIP events (hipEventCreate) on stream around its
  * launches: for launch i < n_slots, ev_before[i] (if not NULL) is recorded right before it and

@@ -160,14 +160,26 @@ def test_grad_layout_and_train_workspace(g):
 def test_forward_launch_sequence(g):
     st, h = make(g)
     L = g.lib()
-    n = L.gpt2_forward_launches(h, 1, None, 0)
+    # a few rows (M <= 16): every LayerNorm is a launch of its own
+    n = L.gpt2_forward_launches(h, 1, 1, 1, None, 0)
     assert n == 1 + 7 * 12 + 3
     kinds = (ctypes.c_int32 * n)()
-    L.gpt2_forward_launches(h, 1, kinds, n)
+    L.gpt2_forward_launches(h, 1, 1, 1, kinds, n)
     names = [g.KERNEL_KINDS[k] for k in kinds]
     assert names[0] == "embed" and names[-3:] == ["ln_f", "lm_head", "argmax"]
     assert names[1:8] == ["ln", "qkv", "attn", "attn_proj", "ln", "fc", "mlp_proj"]
-    assert L.gpt2_forward_launches(h, 0, None, 0) == n - 1
+    assert L.gpt2_forward_launches(h, 1, 1, 0, None, 0) == n - 1
+    # bf16 on tiled GEMMs (B*T > 16): the embedding launch also computes the first block's ln_1
+    n = L.gpt2_forward_launches(h, 4, 1024, 1, None, 0)
+    assert n == 1 + 7 * 12 + 3 - 1
+    kinds = (ctypes.c_int32 * n)()
+    L.gpt2_forward_launches(h, 4, 1024, 1, kinds, n)
+    names = [g.KERNEL_KINDS[k] for k in kinds]
+    assert names[:8] == ["embed", "qkv", "attn", "attn_proj", "ln", "fc", "mlp_proj", "ln"]
+    assert names[-3:] == ["ln_f", "lm_head", "argmax"] and names.count("ln") == 2 * 12 - 1
+    # invalid shapes give no sequence
+    assert L.gpt2_forward_launches(h, 0, 4, 1, None, 0) == 0
+    assert L.gpt2_forward_launches(h, 1, 1025, 1, None, 0) == 0
     L.gpt2_destroy(h)
 
 
