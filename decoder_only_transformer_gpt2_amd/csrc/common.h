@@ -156,7 +156,10 @@ __device__ __forceinline__ void lse_quad_merge(float& m, float& s) {
 namespace gpt2k {
 
 // 0-3 as in the C ABI; 4 and 5 are internal: the erf GELU and the log-sum-exp head (no logits).
-enum Epi { EPI_BIAS = 0, EPI_BIAS_GELU = 1, EPI_BIAS_RESIDUAL = 2, EPI_LOGITS = 3, EPI_BIAS_GELU_ERF = 4, EPI_LSE = 5 };
+enum Epi {
+    EPI_BIAS = 0, EPI_BIAS_GELU = 1, EPI_BIAS_RESIDUAL = 2, EPI_LOGITS = 3, EPI_BIAS_GELU_ERF = 4, EPI_LSE = 5,
+    EPI_BIAS_GELU_U = 6, EPI_BIAS_GELU_U_ERF = 7
+};
 
 // Per-row, per-column-tile outputs of the vocabulary projection's epilogue ([M, n_part] arrays).
 //   EPI_LOGITS: pv/pi = (max logit, first column holding it) when pv is set.
@@ -168,6 +171,13 @@ struct HeadOut {
     int32_t* pi = nullptr;
     const int32_t* tgt = nullptr;
     float* tgt_logit = nullptr;
+    // Tiled bf16 GEMM only (more than kSkinnyM rows, row-major output):
+    //   EPI_BIAS_RESIDUAL with res set: C = res + (A W^T + b), res an fp32 matrix with C's row stride
+    //     (the residual read from one buffer and written to another, instead of C += ...);
+    //   EPI_BIAS_GELU_U: u = A W^T + b (fp32, row stride ldc) and C = gelu(u) in bf16 (tanh form;
+    //     the erf form with gelu_erf), the values the plain GELU epilogue stores.
+    const float* res = nullptr;
+    float* u = nullptr;
 };
 
 // Tile width along N the GEMMs use for a shape: the argmax partial count per row is ceil(N / BN).

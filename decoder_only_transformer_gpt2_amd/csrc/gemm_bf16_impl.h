@@ -105,6 +105,7 @@ void gemm_bf16_kernel(
     int group_m, int c_kb, HeadOut ho) {
     constexpr int NT = 64 * WGM * WGN, NW = WGM * WGN;
     constexpr bool HEAD = EPI == EPI_LOGITS || EPI == EPI_LSE;  // vocabulary projection: no bias
+    constexpr bool GU = EPI == EPI_BIAS_GELU_U || EPI == EPI_BIAS_GELU_U_ERF;  // u in fp32 and gelu(u) in bf16
     constexpr int WM = BM / WGM, WN = BN / WGN, FM = WM / 16, FN = WN / 16;
     constexpr int CPR = BK / 8;                  // 16-byte chunks per slab row
     constexpr int RPI = 64 / CPR;                // slab rows one 64-lane DMA instruction fills
@@ -375,8 +376,9 @@ void gemm_bf16_kernel(
                 if (!CHK || (r < rows && c < cols)) __builtin_nontemporal_store(scr[r * SP + c], Cs + r * ldc + c);
             }
         } else if (EPI == EPI_BIAS_RESIDUAL) {
-            // C += staged, four floats per lane
+            // C += staged (or C = res + staged), four floats per lane
             float* Cs = static_cast<float*>(Cv) + (size_t)rs * ldc + col0;
+            const float* Rs = ho.res ? ho.res + (size_t)rs * ldc + col0 : Cs;
             const bool vec = (ldc & 3) == 0;
 #pragma unroll
             for (int it = 0; it < (16 * (WN / 4) + GPT2_WAVE - 1) / GPT2_WAVE; ++it) {
@@ -386,12 +388,13 @@ void gemm_bf16_kernel(
                 if (CHK && r >= rows) continue;
                 const float* sv = &scr[r * SP + c];
                 float* cp = Cs + r * ldc + c;
+                const float* rp = Rs + r * ldc + c;
                 if ((!CHK || c + 4 <= cols) && vec) {
-                    f32x4_t cv = *reinterpret_cast<const f32x4_t*>(cp);
+                    f32x4_t cv = *reinterpret_cast<const f32x4_t*>(rp);
                     cv[0] += sv[0]; cv[1] += sv[1]; cv[2] += sv[2]; cv[3] += sv[3];
                     *reinterpret_cast<f32x4_t*>(cp) = cv;
                 } else {
-                    for (int t = 0; t < 4 && c + t < cols; ++t) cp[t] += sv[t];
+                    for (int t = 0; t < 4 && c + t < cols; ++t) cp[t] = rp[t] + sv[t];
                 }
             }
         } else {
@@ -411,15 +414,27 @@ void gemm_bf16_kernel(
                     const int col = col0 + c;
                     cp = static_cast<uint16_t*>(Cv) + ((size_t)(col >> 5) * c_kb + rs + r) * 32 + (col & 31);
                 }
+                // GU: sv holds u; u is stored as is and gelu(u) rounded to bf16
+                auto act = [](float v) {
+                    return EPI == EPI_BIAS_GELU_U ? gelu_tanh_fast(v) : EPI == EPI_BIAS_GELU_U_ERF ? gelu_erf_f32(v) : v;
+                };
+                float* up = GU ? ho.u + (size_t)(rs + r) * ldc + col0 + c : nullptr;
                 if ((!CHK || c + 8 <= cols) && vec) {
                     u32x4_t pk;
-                    pk[0] = pack_bf16x2(sv[0], sv[1]);
-                    pk[1] = pack_bf16x2(sv[2], sv[3]);
-                    pk[2] = pack_bf16x2(sv[4], sv[5]);
-                    pk[3] = pack_bf16x2(sv[6], sv[7]);
+                    pk[0] = pack_bf16x2(act(sv[0]), act(sv[1]));
+                    pk[1] = pack_bf16x2(act(sv[2]), act(sv[3]));
+                    pk[2] = pack_bf16x2(act(sv[4]), act(sv[5]));
+                    pk[3] = pack_bf16x2(act(sv[6]), act(sv[7]));
                     *reinterpret_cast<u32x4_t*>(cp) = pk;
+                    if (GU) {
+                        *reinterpret_cast<f32x4_t*>(up) = f32x4_t{sv[0], sv[1], sv[2], sv[3]};
+                        *reinterpret_cast<f32x4_t*>(up + 4) = f32x4_t{sv[4], sv[5], sv[6], sv[7]};
+                    }
                 } else {
-                    for (int t = 0; t < 8 && c + t < cols; ++t) cp[t] = f32_to_bf16_bits(sv[t]);
+                    for (int t = 0; t < 8 && c + t < cols; ++t) {
+                        cp[t] = f32_to_bf16_bits(act(sv[t]));
+                        if (GU) up[t] = sv[t];
+                    }
                 }
             }
         }
@@ -561,6 +576,16 @@ hipError_t launch_cfg(const uint16_t* A, const uint16_t* W, const float* bias, v
                 GPT2_LAUNCH(EPI_BIAS_GELU);
             break;
         case EPI_BIAS_RESIDUAL: GPT2_LAUNCH(EPI_BIAS_RESIDUAL); break;
+        case EPI_BIAS_GELU_U:  // row-major operands only (the training forward)
+            if constexpr (KB) {
+                return hipErrorInvalidValue;
+            } else {
+                if (gelu_erf)
+                    GPT2_LAUNCH(EPI_BIAS_GELU_U_ERF);
+                else
+                    GPT2_LAUNCH(EPI_BIAS_GELU_U);
+            }
+            break;
         case EPI_LSE: GPT2_LAUNCH(EPI_LSE); break;
         default: GPT2_LAUNCH(EPI_LOGITS); break;
     }

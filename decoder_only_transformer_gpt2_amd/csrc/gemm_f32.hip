@@ -134,6 +134,7 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(const float* __restrict__
 hipError_t gemm_f32(const float* A, const float* W, const float* bias, void* C, int M, int N, int K, long ldc, int epi,
                     int gelu_erf, const HeadOut& ho, hipStream_t s) {
     static_assert(kGemmF32BN == TN, "head partial count assumes BN = 64");
+    if (ho.res || ho.u) return hipErrorInvalidValue;  // the tiled bf16 kernel's epilogue options only
     const int tiles_m = (M + TM - 1) / TM, tiles_n = (N + TN - 1) / TN;
     dim3 grid(tiles_m * tiles_n), block(256);
 #define GPT2_LAUNCH(E) gemm_f32_kernel<E><<<grid, block, 0, s>>>(A, W, bias, C, M, N, K, ldc, gelu_erf, tiles_m, ho)

@@ -202,6 +202,7 @@ hipError_t gemm_bf16_skinny(const uint16_t* A, const uint16_t* W, const float* b
     // the LayerNorm in front: k-blocked W, K < 2048 (four wavefronts)
     if (lna && (!w_kb || K >= 2048 || K % 8)) return hipErrorInvalidValue;
     if (ex.kc && (epi != EPI_BIAS || N % 3 || (N / 3) % 64)) return hipErrorInvalidValue;
+    if (ho.res || ho.u) return hipErrorInvalidValue;  // the tiled kernel's epilogue options only
     const size_t lds = lna ? (size_t)M * (K + 8) * 2 : 0;
     // long K over few columns: sixteen wavefronts per workgroup keep enough of W in flight
     const bool wide = K >= 2048;

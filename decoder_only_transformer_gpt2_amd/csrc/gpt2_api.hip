@@ -499,8 +499,8 @@ TrainLayout train_layout(const gpt2_model* m, int B, int T) {
 }
 
 // Forward keeping what the backward needs, then the mean shifted cross-entropy and the loss
-// gradient with respect to the logits (the fused GELU epilogue is split: u = a W^T + b is kept in
-// fp32 and h = gelu(u) rounded to the compute dtype, the values the fused epilogue produces).
+// gradient with respect to the logits (the GELU input u = a W^T + b is kept in fp32 beside
+// h = gelu(u) rounded to the compute dtype, the values the inference epilogue produces).
 gpt2_status enqueue_train_forward(const gpt2_model* m, const int32_t* tokens, const int32_t* labels, int B, int T,
                                   float* loss, char* ws, const TrainLayout& L, hipStream_t s) {
     const gpt2_config_t& c = m->cfg;
@@ -510,6 +510,9 @@ gpt2_status enqueue_train_forward(const gpt2_model* m, const int32_t* tokens, co
     const int64_t qs[3] = {(int64_t)T * 3 * d, 64, 3 * d};
     const int64_t os[3] = {(int64_t)T * d, 64, d};
     auto lay = [&](int l, size_t o) { return ws + L.layer0 + (size_t)l * L.per_layer + o; };
+    // bf16 on the tiled GEMM (more than kSkinnyM rows): residual sums and the GELU input come from
+    // the projections' epilogues
+    const bool tiled = bf && M > gpt2k::kSkinnyM;
     GPT2_HIP(gpt2k::embed(tokens, wptr(m, 0), wptr(m, 1), reinterpret_cast<float*>(lay(0, L.l_xin)), M, T, 0, d,
                           c.n_vocab, bf, reinterpret_cast<int32_t*>(ws + L.fw.flags), s));
     for (int l = 0; l < c.n_layer; ++l) {
@@ -537,14 +540,34 @@ gpt2_status enqueue_train_forward(const gpt2_model* m, const int32_t* tokens, co
                                           reinterpret_cast<const float*>(qkv + d * as), qs,
                                           reinterpret_cast<const float*>(qkv + 2 * d * as), qs,
                                           reinterpret_cast<float*>(o), os, B, H, T, s));
-        GPT2_HIP(hipMemcpyAsync(xmid, xin, (size_t)M * d * 4, hipMemcpyDeviceToDevice, s));
-        GPT2_HIP(linear(m, o, I(APROJ_W), I(APROJ_B), xmid, M, d, d, d, gpt2k::EPI_BIAS_RESIDUAL, {}, s));
+        // each block keeps both residual states: the tiled bf16 GEMM reads the residual from one
+        // buffer and writes the sum to the next; otherwise the state is copied and added to in place
+        if (tiled) {
+            gpt2k::HeadOut hr;
+            hr.res = xin;
+            GPT2_HIP(linear(m, o, I(APROJ_W), I(APROJ_B), xmid, M, d, d, d, gpt2k::EPI_BIAS_RESIDUAL, hr, s));
+        } else {
+            GPT2_HIP(hipMemcpyAsync(xmid, xin, (size_t)M * d * 4, hipMemcpyDeviceToDevice, s));
+            GPT2_HIP(linear(m, o, I(APROJ_W), I(APROJ_B), xmid, M, d, d, d, gpt2k::EPI_BIAS_RESIDUAL, {}, s));
+        }
         GPT2_HIP(gpt2k::layernorm(xmid, vecp(LN2_W), vecp(LN2_B), a2, M, d, c.ln_eps, bf, s));
-        GPT2_HIP(hipMemsetAsync(u, 0, (size_t)M * f * 4, s));
-        GPT2_HIP(linear(m, a2, I(FC_W), I(FC_B), u, M, f, d, f, gpt2k::EPI_BIAS_RESIDUAL, {}, s));
-        GPT2_HIP(gpt2k::gelu_forward(u, h, (long)M * f, bf, c.gelu == GPT2_GELU_ERF, s));
-        GPT2_HIP(hipMemcpyAsync(xout, xmid, (size_t)M * d * 4, hipMemcpyDeviceToDevice, s));
-        GPT2_HIP(linear(m, h, I(MPROJ_W), I(MPROJ_B), xout, M, d, f, d, gpt2k::EPI_BIAS_RESIDUAL, {}, s));
+        if (tiled) {  // u and h = gelu(u) from one epilogue
+            gpt2k::HeadOut hu;
+            hu.u = u;
+            GPT2_HIP(linear(m, a2, I(FC_W), I(FC_B), h, M, f, d, f, gpt2k::EPI_BIAS_GELU_U, hu, s));
+        } else {
+            GPT2_HIP(hipMemsetAsync(u, 0, (size_t)M * f * 4, s));
+            GPT2_HIP(linear(m, a2, I(FC_W), I(FC_B), u, M, f, d, f, gpt2k::EPI_BIAS_RESIDUAL, {}, s));
+            GPT2_HIP(gpt2k::gelu_forward(u, h, (long)M * f, bf, c.gelu == GPT2_GELU_ERF, s));
+        }
+        if (tiled) {
+            gpt2k::HeadOut hr;
+            hr.res = xmid;
+            GPT2_HIP(linear(m, h, I(MPROJ_W), I(MPROJ_B), xout, M, d, f, d, gpt2k::EPI_BIAS_RESIDUAL, hr, s));
+        } else {
+            GPT2_HIP(hipMemcpyAsync(xout, xmid, (size_t)M * d * 4, hipMemcpyDeviceToDevice, s));
+            GPT2_HIP(linear(m, h, I(MPROJ_W), I(MPROJ_B), xout, M, d, f, d, gpt2k::EPI_BIAS_RESIDUAL, {}, s));
+        }
     }
     const int ln_f = 2 + c.n_layer * PER_LAYER;
     GPT2_HIP(gpt2k::layernorm(reinterpret_cast<float*>(ws + L.xfin), static_cast<const float*>(wptr(m, ln_f)),

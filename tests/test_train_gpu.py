@@ -124,6 +124,12 @@ def test_backward_bf16_gpt2_small(g):
     run_case(g, synth.GPT2_SMALL, "bf16", 2, 64)
 
 
+def test_backward_bf16_few_rows(g):
+    """B*T = 16 rows: the forward runs on the few-row GEMM, so the residual states are copied and
+    added to in place and the GELU runs as a kernel of its own (the tiled path fuses both)."""
+    run_case(g, synth.GPT2_SMALL, "bf16", 2, 8)
+
+
 def test_backward_bf16_gpt2_small_t1024(g):
     """One full-length sequence of GPT-2 small, B=1 T=1024: the attention backward walks 16 key
     tiles, the weight gradients reduce over 1024 rows, and the transposes move full tiles."""
