@@ -45,7 +45,7 @@ __device__ __forceinline__ u32x2_t lds_tr16(const uint16_t* p) {
 template <int BM, int BN, int S, int WGM, int WGN, bool AMM, bool BMM, int NKT>
 __global__ __launch_bounds__(64 * WGM * WGN, S * (BM + BN) * TBK * 2 <= 80 * 1024 ? 2 : 1) void gemm_tn_kernel(
     const uint16_t* __restrict__ A, long lda, int a_lim, const uint16_t* __restrict__ B, long ldb, int b_lim,
-    float* __restrict__ C, long ldc, int M, int N, int K, int tiles_m) {
+    float* __restrict__ C, long ldc, int M, int N, int K, int tiles_m, int ntiles) {
     constexpr int NW = WGM * WGN;
     constexpr int WM = BM / WGM, WN = BN / WGN, FM = WM / 16, FN = WN / 16;
     constexpr int SA = BM * TBK, SB = BN * TBK, STAGE = SA + SB;  // bf16 elements
@@ -61,7 +61,11 @@ __global__ __launch_bounds__(64 * WGM * WGN, S * (BM + BN) * TBK * 2 <= 80 * 102
     __shared__ __attribute__((aligned(S > 3 ? 1024 : 2))) uint16_t lds3[S > 3 ? STAGE : 1];
     auto slot = [&](int i) -> uint16_t* { return i == 0 ? lds0 : i == 1 ? lds1 : i == 2 ? lds2 : lds3; };
 
-    const TileCoord tc = tile_of(blockIdx.x, gridDim.x, tiles_m, 4, true);
+    // split along K: workgroup z * ntiles + b computes tile b over K steps [z nk, (z+1) nk) into
+    // the z-th M x ldc partial product
+    const int z = blockIdx.x / ntiles;
+    C += (long)z * M * ldc;
+    const TileCoord tc = tile_of(blockIdx.x % ntiles, ntiles, tiles_m, 4, true);
     const int m0 = tc.tm * BM, n0 = tc.tn * BN;
     const int wave = threadIdx.x / GPT2_WAVE, lane = threadIdx.x % GPT2_WAVE;
     const int wm = wave / WGN, wn = wave % WGN;
@@ -94,6 +98,7 @@ __global__ __launch_bounds__(64 * WGM * WGN, S * (BM + BN) * TBK * 2 <= 80 * 102
             kstep[p] = TBK;
         }
         dst[p] = (is_a ? 0 : SA) + qb * 512;
+        src[p] += (long)z * (K / TBK) * kstep[p];  // this split's first K step
     }
     auto issue = [&](int st, int kt) __attribute__((always_inline)) {
         uint16_t* b = slot(st);
@@ -206,21 +211,67 @@ __global__ __launch_bounds__(64 * WGM * WGN, S * (BM + BN) * TBK * 2 <= 80 * 102
         }
 }
 
+// C[m][n] = sum over z < nsplit of P[z][m][n] (P: nsplit partial products of M x N, row stride N),
+// added in increasing z, so the result does not depend on scheduling. Four columns per thread.
+__global__ __launch_bounds__(256) void splitk_sum_kernel(const float4* __restrict__ P, int nsplit, int M, int N4,
+                                                         float* __restrict__ C, long ldc) {
+    const long n = (long)M * N4;
+    for (long i = (long)blockIdx.x * 256 + threadIdx.x; i < n; i += (long)gridDim.x * 256) {
+        float4 a = P[i];
+        for (int z = 1; z < nsplit; ++z) {
+            const float4 b = P[(long)z * n + i];
+            a.x += b.x; a.y += b.y; a.z += b.z; a.w += b.w;
+        }
+        const long m = i / N4;
+        *reinterpret_cast<float4*>(C + m * ldc + 4 * (i % N4)) = a;
+    }
+}
+
+// nsplit > 1: the K range is split into nsplit parts of K / nsplit (a multiple of TBK); their
+// partial products go to part (nsplit x M x N floats) and are then summed into C.
 template <int BM, int BN, int S, int WGM, int WGN, bool AMM, bool BMM, int NKT>
 hipError_t launch_tn(const uint16_t* A, long lda, int a_lim, const uint16_t* B, long ldb, int b_lim, float* C, long ldc,
-                     int M, int N, int K, hipStream_t s) {
-    const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
-    gemm_tn_kernel<BM, BN, S, WGM, WGN, AMM, BMM, NKT><<<dim3(tiles_m * tiles_n), dim3(64 * WGM * WGN), 0, s>>>(
-        A, lda, a_lim, B, ldb, b_lim, C, ldc, M, N, K, tiles_m);
+                     int M, int N, int K, hipStream_t s, int nsplit = 1, float* part = nullptr) {
+    const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN, ntiles = tiles_m * tiles_n;
+    if (nsplit > 1) {
+        gemm_tn_kernel<BM, BN, S, WGM, WGN, AMM, BMM, NKT><<<dim3(ntiles * nsplit), dim3(64 * WGM * WGN), 0, s>>>(
+            A, lda, a_lim, B, ldb, b_lim, part, N, M, N, K / nsplit, tiles_m, ntiles);
+        const long n4 = (long)M * (N / 4);
+        splitk_sum_kernel<<<dim3((unsigned)std::min<long>((n4 + 255) / 256, 4096)), dim3(256), 0, s>>>(
+            reinterpret_cast<const float4*>(part), nsplit, M, N / 4, C, ldc);
+        return hipGetLastError();
+    }
+    gemm_tn_kernel<BM, BN, S, WGM, WGN, AMM, BMM, NKT><<<dim3(ntiles), dim3(64 * WGM * WGN), 0, s>>>(
+        A, lda, a_lim, B, ldb, b_lim, C, ldc, M, N, K, tiles_m, ntiles);
     return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t gemm_bf16_tn(const uint16_t* A, bool a_mmajor, long lda, int a_lim, const uint16_t* B, bool b_mmajor,
-                        long ldb, int b_lim, float* C, long ldc, int M, int N, int K, hipStream_t s) {
+                        long ldb, int b_lim, float* C, long ldc, int M, int N, int K, hipStream_t s, float* part,
+                        size_t part_elems) {
     if (M < 1 || N < 1 || K < TBK || K % TBK || !b_mmajor) return hipErrorInvalidValue;
     const int nk = K / TBK;
+    // Split along K where one pass would leave most CUs idle or run very long chains: a weight
+    // gradient with fewer than 128 tiles of 64 x 128 (attn.c_proj of GPT-2 small: 72) in four
+    // parts; a reduction over the vocabulary (nk in the hundreds) in three or two parts.
+    auto fits = [&](int ns) {
+        return part && N % 4 == 0 && ldc % 4 == 0 && reinterpret_cast<uintptr_t>(C) % 16 == 0 &&
+               (size_t)ns * M * N <= part_elems;
+    };
+    const long tiles64 = (long)((M + 63) / 64) * ((N + 127) / 128);
+    if (a_mmajor && M < 16384 && tiles64 < 128 && nk % 4 == 0 && nk >= 16 && fits(4)) {
+        if (nk == 64)
+            return launch_tn<64, 128, 3, 2, 2, true, true, 16>(A, lda, a_lim, B, ldb, b_lim, C, ldc, M, N, K, s, 4, part);
+        return launch_tn<64, 128, 3, 2, 2, true, true, 0>(A, lda, a_lim, B, ldb, b_lim, C, ldc, M, N, K, s, 4, part);
+    }
+    if (!a_mmajor && nk >= 256) {
+        if (nk % 3 == 0 && fits(3))
+            return launch_tn<64, 128, 3, 2, 2, false, true, 0>(A, lda, a_lim, B, ldb, b_lim, C, ldc, M, N, K, s, 3, part);
+        if (nk % 2 == 0 && fits(2))
+            return launch_tn<64, 128, 3, 2, 2, false, true, 0>(A, lda, a_lim, B, ldb, b_lim, C, ldc, M, N, K, s, 2, part);
+    }
     if (a_mmajor) {
         // weight gradients: 64 x 128 tiles of four wavefronts (32 x 64 each), two workgroups per
         // CU; for very many rows (the tied wte gradient, M = n_vocab) 128 x 128 tiles

@@ -10,6 +10,10 @@ namespace gpt2k {
 // M-major one (a multiple of 8); tiles reaching past it read duplicates of valid data, and only
 // C[m < M][n < N] is written. Rows k < K of an M-major operand must exist and hold finite values;
 // where the other operand's row k is zero they contribute nothing.
+// part: optional fp32 scratch of part_elems floats. With room for a few M x N partial products, a
+// product with few output tiles or a reduction over thousands of rows is split along K and its
+// partial products summed in a fixed order (the result repeats bit for bit from run to run).
 hipError_t gemm_bf16_tn(const uint16_t* A, bool a_mmajor, long lda, int a_lim, const uint16_t* B, bool b_mmajor,
-                        long ldb, int b_lim, float* C, long ldc, int M, int N, int K, hipStream_t s);
+                        long ldb, int b_lim, float* C, long ldc, int M, int N, int K, hipStream_t s,
+                        float* part = nullptr, size_t part_elems = 0);
 }  // namespace gpt2k

@@ -433,6 +433,7 @@ struct TrainLayout {
     WorkspaceLayout fw;
     size_t layer0, per_layer;
     size_t l_xin, l_xmid, l_a1, l_qkv, l_o, l_a2, l_u, l_h, l_lse;  // inside one layer's block
+    size_t splitk, splitk_elems;
     size_t xfin, xf, logits, dx, dbuf, dbuf2, dact, dT, xT, wT, wteT, dlog, dlogT, part, bpart, lnpg, lnpb, lse, dvec, nll,
         cnt;
     size_t total;
@@ -492,6 +493,10 @@ TrainLayout train_layout(const gpt2_model* m, int B, int T) {
     L.lnpb = take((size_t)gpt2k::ln_backward_blocks((int)L.M) * d * 4);
     L.lse = take(is_bf16(m) ? 0 : (size_t)B * c.n_head * T * 4);  // fp32 mode: the backward finds it
     L.dvec = take((size_t)B * c.n_head * T * 4);
+    // partial products of the products split along K (the vocabulary reduction of dxf in three
+    // parts, a narrow weight gradient in four)
+    L.splitk_elems = is_bf16(m) ? std::max<size_t>((size_t)3 * L.M * d, (size_t)4 * d * d) : 0;
+    L.splitk = take(L.splitk_elems * 4);
     L.nll = take(L.M * 4);
     L.cnt = take(4);
     L.total = off;
@@ -605,6 +610,7 @@ gpt2_status enqueue_backward(const gpt2_model* m, const int32_t* tokens, int B, 
     char* xT = ws + L.xT;
     char* wT = ws + L.wT;
     float* part = reinterpret_cast<float*>(ws + L.part);
+    float* splitk = reinterpret_cast<float*>(ws + L.splitk);
     float* lnpg = reinterpret_cast<float*>(ws + L.lnpg);
     float* lnpb = reinterpret_cast<float*>(ws + L.lnpb);
     // C[Mg, Ng] (fp32, row stride ldc) = A[Mg, Kg] B[Ng, Kg]^T in the compute dtype
@@ -640,7 +646,7 @@ gpt2_status enqueue_backward(const gpt2_model* m, const int32_t* tokens, int B, 
             bpart += (size_t)nbp * n_out;
             // dW [n_out, n_in] = sum over rows m < Mk of dy[m]^T x[m]
             if ((e = gpt2k::gemm_bf16_tn(dy16, true, n_out, n_out, static_cast<const uint16_t*>(x_act), true, n_in, n_in,
-                                         G(widx), n_in, n_out, n_in, Mk, s)) != hipSuccess)
+                                         G(widx), n_in, n_out, n_in, Mk, s, splitk, L.splitk_elems)) != hipSuccess)
                 return e;
             // dX [M, n_in] = dy W, W [n_out][n_in] reduced over its rows
             return gpt2k::gemm_bf16_tn(dy16, false, n_out, Mk, static_cast<const uint16_t*>(wptr(m, widx)), true, n_in,
@@ -672,7 +678,7 @@ gpt2_status enqueue_backward(const gpt2_model* m, const int32_t* tokens, int B, 
         const uint16_t* dl16 = reinterpret_cast<const uint16_t*>(ws + L.dlog);
         // wte [V rows, zero-padded past V][d], reduced over its rows (Vp of them)
         GPT2_HIP(gpt2k::gemm_bf16_tn(dl16, false, Vp, Mp, static_cast<const uint16_t*>(wptr(m, 0)), true, d, d, dbuf, d,
-                                     M, d, Vp, s));
+                                     M, d, Vp, s, splitk, L.splitk_elems));
         GPT2_HIP(gpt2k::gemm_bf16_tn(dl16, true, Vp, Vp, reinterpret_cast<const uint16_t*>(ws + L.xf), true, d, d, G(0),
                                      d, V, d, Mk, s));
     } else {
