@@ -180,6 +180,36 @@ void gemm_bf16_kernel(
 #pragma unroll
         for (int j = 0; j < FN; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
+    // Epilogue operands are loaded before the K loop, so their memory latency hides behind it: the
+    // bias of this lane's column in each 16-column block (0 past N) and, for the residual epilogue
+    // with narrow wave tiles, the residual values this lane adds to in the store loop below (four
+    // floats per lane and 16-row strip pass, the same order).
+    const int row0 = m0 + wm * WM, col0 = n0 + wn * WN;
+    // Interior tiles (the common case) take the store and argmax paths without bounds checks.
+    const bool interior = m0 + BM <= M && n0 + BN <= N;
+    float bcol[FN];
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+        const int n = col0 + j * 16 + r16;
+        bcol[j] = (!HEAD && n < N) ? bias[n] : 0.f;
+    }
+    constexpr int RIT = 16 * (WN / 4) / GPT2_WAVE;  // residual store passes per strip
+    constexpr bool RPRE = EPI == EPI_BIAS_RESIDUAL && (16 * (WN / 4)) % GPT2_WAVE == 0 && FM * RIT * 4 <= 32;
+    const bool rpre = RPRE && interior && (ldc & 3) == 0;
+    f32x4_t xres[RPRE ? FM : 1][RPRE ? RIT : 1];
+    if constexpr (RPRE) {
+        if (rpre) {
+            const float* Rb = (ho.res ? ho.res : static_cast<const float*>(Cv)) + (size_t)row0 * ldc + col0;
+#pragma unroll
+            for (int i = 0; i < FM; ++i)
+#pragma unroll
+                for (int it = 0; it < RIT; ++it) {
+                    const int idx = it * GPT2_WAVE + lane, r = idx / (WN / 4), c = (idx % (WN / 4)) * 4;
+                    xres[i][it] = *reinterpret_cast<const f32x4_t*>(Rb + (size_t)(i * 16 + r) * ldc + c);
+                }
+        }
+    }
+
     auto compute = [&](int st) {
         const uint16_t* sa = slot(st);
         const uint16_t* sw = sa + BM * BK;
@@ -278,15 +308,6 @@ void gemm_bf16_kernel(
     float* red_m = reinterpret_cast<float*>(red_v);                // (EPI_LSE) [WGN][BM] base-2 maximum
     float* red_s = reinterpret_cast<float*>(red_i);                // (EPI_LSE) [WGN][BM] sum below it
 
-    const int row0 = m0 + wm * WM, col0 = n0 + wn * WN;
-    // Interior tiles (the common case) take the store and argmax paths without bounds checks.
-    const bool interior = m0 + BM <= M && n0 + BN <= N;
-    float bcol[FN];  // bias of this lane's column in each 16-column block (0 past N)
-#pragma unroll
-    for (int j = 0; j < FN; ++j) {
-        const int n = col0 + j * 16 + r16;
-        bcol[j] = (!HEAD && n < N) ? bias[n] : 0.f;
-    }
 
     // One strip: 16 rows x WN columns staged in scr, then written out (a wavefront's LDS
     // operations complete in order, so its own staged values are visible to its later reads).
@@ -390,7 +411,11 @@ void gemm_bf16_kernel(
                 float* cp = Cs + r * ldc + c;
                 const float* rp = Rs + r * ldc + c;
                 if ((!CHK || c + 4 <= cols) && vec) {
-                    f32x4_t cv = *reinterpret_cast<const f32x4_t*>(rp);
+                    f32x4_t cv;
+                    if constexpr (RPRE && !CHK)
+                        cv = rpre ? xres[i][it] : *reinterpret_cast<const f32x4_t*>(rp);
+                    else
+                        cv = *reinterpret_cast<const f32x4_t*>(rp);
                     cv[0] += sv[0]; cv[1] += sv[1]; cv[2] += sv[2]; cv[3] += sv[3];
                     *reinterpret_cast<f32x4_t*>(cp) = cv;
                 } else {
