@@ -136,6 +136,14 @@ def test_backward_bf16_gpt2_small_t1024(g):
     run_case(g, synth.GPT2_SMALL, "bf16", 1, 1024, ignore=[(0, 100), (0, 1023)])
 
 
+def test_backward_bf16_b4_t1024_one_layer(g):
+    """B=4 T=1024 on one block of GPT-2 small width (vocabulary 1000): the weight gradients reduce
+    over 4096 rows, where the attn.c_proj weight gradient (72 tiles) runs in four K parts whose
+    partial products are summed afterwards."""
+    s = synth.ModelShape(n_vocab=1000, n_ctx=1024, d_model=768, n_head=12, n_layer=1, d_mlp=3072)
+    run_case(g, s, "bf16", 4, 1024, ignore=[(1, 500), (3, 1023)])
+
+
 def test_backward_f32_t1024(g):
     """fp32 mode at T=1024 on a two-layer model of GPT-2 small width."""
     s = synth.ModelShape(n_vocab=50257, n_ctx=1024, d_model=768, n_head=12, n_layer=2, d_mlp=3072)
