@@ -29,13 +29,17 @@ int choose_cfg(int M, int N, int K, bool kb) {
     // the grid fills the CUs twice over anyway and each tile re-reads less through L2
     if (N <= 1024 && tiles(256, 192) >= 512) return 1;
     // narrow outputs on k-blocked operands (attn.c_proj, mlp.c_proj): 128 x 96 tiles of eight
-    // wavefronts (two per SIMD, 32 x 48 each), one wave of 256 workgroups
+    // wavefronts (two per SIMD, 32 x 48 each), one wave of 256 workgroups at GPT-2 small B*T = 4096
+    // (128 x 128 tiles, fewer waves of workgroups for GPT-2 medium and XL, measured slower: medium
+    // B=8 forward 8.58 -> 8.87 ms)
     if (N <= 1024 && kb && tiles(128, 96) >= 192) return 5;
     if (N <= 1024) return 0;
     if (tiles(192, 256) < 128) return 0;  // few rows (weight gradients, short prompts): fill the CUs
     if (tiles(192, 256) <= 256) return 3;
-    // k-blocked operands stream at full cache-line width, which favours the deeper 32-wide ring
-    if (kb && tiles(256, 192) <= 256) return 4;
+    // k-blocked operands stream at full cache-line width, which favours the deeper 32-wide ring, also
+    // when the grid takes several waves (GPT-2 medium B=8 forward 9.06 -> 8.52 ms, XL B=4 20.04 ->
+    // 18.41 ms against the two-stage 64-wide ring, with bit-identical logits)
+    if (kb) return 4;
     return 1;
 }
 

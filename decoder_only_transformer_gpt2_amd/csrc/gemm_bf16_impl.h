@@ -536,8 +536,9 @@ constexpr TileCfg kCfgs[] = {
 
 // One epilogue's launch, with the K loop fully unrolled for the step counts that occur: the
 // forward's k-blocked projections (K = 768 and 3072; for GPT-2 medium and XL the vocabulary
-// projection and the residual projections, K = d and 4d for d = 1024 and 1600) and the plain fp32
-// products of the backward (K = 768, 2304, 3072 and B*T = 4096 at the benchmark shape).
+// projection, c_attn and c_fc, K = d, and the residual projections, K = d and 4d, for d = 1024 and
+// 1600) and the plain fp32 products of the backward (K = 768, 2304, 3072 and B*T = 4096 at the
+// benchmark shape).
 template <int BM, int BN, int BK, int S, int WGM, int WGN, int EPI, bool KB>
 void launch_epi(dim3 grid, dim3 block, hipStream_t s, const uint16_t* A, const uint16_t* W, const float* bias,
                 void* C, int M, int N, int K, int ldc, int a_rows, int w_rows, int tiles_m, int group_m, int c_kb,
@@ -550,9 +551,14 @@ void launch_epi(dim3 grid, dim3 block, hipStream_t s, const uint16_t* A, const u
     if constexpr (KB || EPI == EPI_LOGITS) {
         if constexpr (BK == 32) {
             if (nk == 24) return (void)GPT2_LAUNCH_NK(24);
-            // the vocabulary projection of GPT-2 medium and XL (K = d = 1024, 1600)
-            if constexpr (HEAD) {
+            // the vocabulary projection of GPT-2 medium and XL (K = d = 1024, 1600), and their c_attn
+            // and c_fc on the 256 x 192 tiles
+            if constexpr (HEAD || (KB && BM == 256 && BN == 192 && (EPI == EPI_BIAS || EPI == EPI_BIAS_GELU))) {
                 if (nk == 32) return (void)GPT2_LAUNCH_NK(32);
+                if (nk == 50) return (void)GPT2_LAUNCH_NK(50);
+            }
+            // attn.c_proj of GPT-2 XL (N = K = 1600) on the 192 x 256 tiles
+            if constexpr (KB && BM == 192 && BN == 256 && EPI == EPI_BIAS_RESIDUAL) {
                 if (nk == 50) return (void)GPT2_LAUNCH_NK(50);
             }
         } else {
