@@ -44,6 +44,15 @@ __device__ __forceinline__ float gelu_tanh_fast(float x) {
     return x * __builtin_amdgcn_rcpf(1.0f + e);
 }
 __device__ __forceinline__ float gelu_erf_f32(float x) { return 0.5f * x * (1.0f + erff(x * 0.7071067811865476f)); }
+// Their derivatives (the backward pass multiplies the output gradient by them).
+__device__ __forceinline__ float gelu_tanh_grad(float x) {
+    const float c = 0.7978845608028654f;  // sqrt(2/pi)
+    const float t = tanhf(c * (x + 0.044715f * x * x * x));
+    return 0.5f * (1.0f + t) + 0.5f * x * (1.0f - t * t) * c * (1.0f + 3.0f * 0.044715f * x * x);
+}
+__device__ __forceinline__ float gelu_erf_grad(float x) {
+    return 0.5f * (1.0f + erff(x * 0.7071067811865476f)) + x * 0.3989422804014327f * expf(-0.5f * x * x);
+}
 
 // (value, index) maximum with ties broken toward the smaller index (selects, no branches).
 __device__ __forceinline__ void argmax_merge(float& v, int& i, float v2, int i2) {

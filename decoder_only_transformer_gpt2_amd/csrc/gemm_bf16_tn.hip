@@ -42,10 +42,10 @@ __device__ __forceinline__ u32x2_t lds_tr16(const uint16_t* p) {
     return __builtin_bit_cast(u32x2_t, v);
 }
 
-template <int BM, int BN, int S, int WGM, int WGN, bool AMM, bool BMM, int NKT>
+template <int BM, int BN, int S, int WGM, int WGN, bool AMM, bool BMM, int NKT, bool GB = false>
 __global__ __launch_bounds__(64 * WGM * WGN, S * (BM + BN) * TBK * 2 <= 80 * 1024 ? 2 : 1) void gemm_tn_kernel(
     const uint16_t* __restrict__ A, long lda, int a_lim, const uint16_t* __restrict__ B, long ldb, int b_lim,
-    float* __restrict__ C, long ldc, int M, int N, int K, int tiles_m, int ntiles) {
+    float* __restrict__ C, long ldc, int M, int N, int K, int tiles_m, int ntiles, TnGeluBack gb) {
     constexpr int NW = WGM * WGN;
     constexpr int WM = BM / WGM, WN = BN / WGN, FM = WM / 16, FN = WN / 16;
     constexpr int SA = BM * TBK, SB = BN * TBK, STAGE = SA + SB;  // bf16 elements
@@ -196,6 +196,64 @@ __global__ __launch_bounds__(64 * WGM * WGN, S * (BM + BN) * TBK * 2 <= 80 * 102
 #undef GPT2_TN_WAIT_BARRIER
 
     // C rows m0 + wm*WM + i*16 + 4*g4 + e, columns n0 + wn*WN + j*16 + r16
+    if constexpr (GB) {
+        // g = C * gelu'(u) in bf16 (0 on rows past M) and each column's sum of g over the tile's 64
+        // rows. The tile goes through LDS ([64][BN + 4] fp32, rows 0-31 in ring slot 0, 32-63 in slot 1)
+        // so that u is read and g written in whole 16- and 32-byte pieces per lane.
+        static_assert(BM == 64 && BN == 128 && WGM * WGN == 4 && 32 * (BN + 4) * 4 <= STAGE * 2, "tile layout");
+        constexpr int TS = BN + 4;
+        auto trow = [&](int r) -> float* { return reinterpret_cast<float*>(r < 32 ? lds0 : lds1) + (r & 31) * TS; };
+        __syncthreads();  // the ring is idle
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+#pragma unroll
+                for (int j = 0; j < FN; ++j) trow(wm * WM + i * 16 + 4 * g4 + e)[wn * WN + j * 16 + r16] = acc[i][j][e];
+        __syncthreads();
+        const int t = threadIdx.x;
+        for (int idx = t; idx < BM * (BN / 8); idx += 64 * WGM * WGN) {
+            const int r = idx / (BN / 8), c8 = (idx % (BN / 8)) * 8, m = m0 + r, n = n0 + c8;
+            float* tp = trow(r) + c8;
+            float g[8];
+#pragma unroll
+            for (int k = 0; k < 8; ++k) g[k] = 0.f;
+            if (m < M) {
+                const float* up = gb.u + (long)m * gb.ldu + n;
+                if (n + 8 <= N) {
+                    const f32x4_t u0 = *reinterpret_cast<const f32x4_t*>(up);
+                    const f32x4_t u1 = *reinterpret_cast<const f32x4_t*>(up + 4);
+#pragma unroll
+                    for (int k = 0; k < 4; ++k) {
+                        g[k] = tp[k] * (gb.erf ? gelu_erf_grad(u0[k]) : gelu_tanh_grad(u0[k]));
+                        g[k + 4] = tp[k + 4] * (gb.erf ? gelu_erf_grad(u1[k]) : gelu_tanh_grad(u1[k]));
+                    }
+                } else {
+                    for (int k = 0; k < 8 && n + k < N; ++k)
+                        g[k] = tp[k] * (gb.erf ? gelu_erf_grad(up[k]) : gelu_tanh_grad(up[k]));
+                }
+            }
+#pragma unroll
+            for (int k = 0; k < 8; ++k) tp[k] = g[k];
+            uint16_t* yp = gb.y + (long)m * gb.ldy + n;
+            if (n + 8 <= N) {
+                u32x4_t pk;
+                pk[0] = pack_bf16x2(g[0], g[1]);
+                pk[1] = pack_bf16x2(g[2], g[3]);
+                pk[2] = pack_bf16x2(g[4], g[5]);
+                pk[3] = pack_bf16x2(g[6], g[7]);
+                *reinterpret_cast<u32x4_t*>(yp) = pk;
+            } else {
+                for (int k = 0; k < 8 && n + k < N; ++k) yp[k] = f32_to_bf16_bits(g[k]);
+            }
+        }
+        __syncthreads();
+        if (t < BN && n0 + t < N) {
+            float cs = 0.f;
+            for (int r = 0; r < BM; ++r) cs += trow(r)[t];
+            gb.part[(long)tc.tm * N + n0 + t] = cs;
+        }
+    } else {
 #pragma unroll
     for (int i = 0; i < FM; ++i)
 #pragma unroll
@@ -209,6 +267,7 @@ __global__ __launch_bounds__(64 * WGM * WGN, S * (BM + BN) * TBK * 2 <= 80 * 102
                 if (n < N) crow[n] = acc[i][j][e];
             }
         }
+    }
 }
 
 // C[m][n] = sum over z < nsplit of P[z][m][n] (P: nsplit partial products of M x N, row stride N),
@@ -229,20 +288,21 @@ __global__ __launch_bounds__(256) void splitk_sum_kernel(const float4* __restric
 
 // nsplit > 1: the K range is split into nsplit parts of K / nsplit (a multiple of TBK); their
 // partial products go to part (nsplit x M x N floats) and are then summed into C.
-template <int BM, int BN, int S, int WGM, int WGN, bool AMM, bool BMM, int NKT>
+template <int BM, int BN, int S, int WGM, int WGN, bool AMM, bool BMM, int NKT, bool GB = false>
 hipError_t launch_tn(const uint16_t* A, long lda, int a_lim, const uint16_t* B, long ldb, int b_lim, float* C, long ldc,
-                     int M, int N, int K, hipStream_t s, int nsplit = 1, float* part = nullptr) {
+                     int M, int N, int K, hipStream_t s, int nsplit = 1, float* part = nullptr,
+                     const TnGeluBack& gb = TnGeluBack()) {
     const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN, ntiles = tiles_m * tiles_n;
     if (nsplit > 1) {
         gemm_tn_kernel<BM, BN, S, WGM, WGN, AMM, BMM, NKT><<<dim3(ntiles * nsplit), dim3(64 * WGM * WGN), 0, s>>>(
-            A, lda, a_lim, B, ldb, b_lim, part, N, M, N, K / nsplit, tiles_m, ntiles);
+            A, lda, a_lim, B, ldb, b_lim, part, N, M, N, K / nsplit, tiles_m, ntiles, gb);
         const long n4 = (long)M * (N / 4);
         splitk_sum_kernel<<<dim3((unsigned)std::min<long>((n4 + 255) / 256, 4096)), dim3(256), 0, s>>>(
             reinterpret_cast<const float4*>(part), nsplit, M, N / 4, C, ldc);
         return hipGetLastError();
     }
-    gemm_tn_kernel<BM, BN, S, WGM, WGN, AMM, BMM, NKT><<<dim3(ntiles), dim3(64 * WGM * WGN), 0, s>>>(
-        A, lda, a_lim, B, ldb, b_lim, C, ldc, M, N, K, tiles_m, ntiles);
+    gemm_tn_kernel<BM, BN, S, WGM, WGN, AMM, BMM, NKT, GB><<<dim3(ntiles), dim3(64 * WGM * WGN), 0, s>>>(
+        A, lda, a_lim, B, ldb, b_lim, C, ldc, M, N, K, tiles_m, ntiles, gb);
     return hipGetLastError();
 }
 
@@ -250,9 +310,19 @@ hipError_t launch_tn(const uint16_t* A, long lda, int a_lim, const uint16_t* B, 
 
 hipError_t gemm_bf16_tn(const uint16_t* A, bool a_mmajor, long lda, int a_lim, const uint16_t* B, bool b_mmajor,
                         long ldb, int b_lim, float* C, long ldc, int M, int N, int K, hipStream_t s, float* part,
-                        size_t part_elems) {
+                        size_t part_elems, const TnGeluBack* gb) {
     if (M < 1 || N < 1 || K < TBK || K % TBK || !b_mmajor) return hipErrorInvalidValue;
     const int nk = K / TBK;
+    if (gb) {  // input gradient of c_fc's output through the GELU: 64 x 128 tiles, no split
+        if (a_mmajor || !gb->u || !gb->y || !gb->part || gb->ldu < N || gb->ldy < N || gb->ldu % 4 || gb->ldy % 8 ||
+            reinterpret_cast<uintptr_t>(gb->u) % 16 || reinterpret_cast<uintptr_t>(gb->y) % 16)
+            return hipErrorInvalidValue;
+        if (nk == 12)
+            return launch_tn<64, 128, 3, 2, 2, false, true, 12, true>(A, lda, a_lim, B, ldb, b_lim, nullptr, 0, M, N, K,
+                                                                      s, 1, nullptr, *gb);
+        return launch_tn<64, 128, 3, 2, 2, false, true, 0, true>(A, lda, a_lim, B, ldb, b_lim, nullptr, 0, M, N, K, s,
+                                                                 1, nullptr, *gb);
+    }
     // Split along K where one pass would leave most CUs idle or run very long chains: a weight
     // gradient with fewer than 128 tiles of 64 x 128 (attn.c_proj of GPT-2 small: 72) in four
     // parts; a reduction over the vocabulary (nk in the hundreds) in three or two parts.

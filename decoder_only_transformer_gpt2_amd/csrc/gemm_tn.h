@@ -13,7 +13,19 @@ namespace gpt2k {
 // part: optional fp32 scratch of part_elems floats. With room for a few M x N partial products, a
 // product with few output tiles or a reduction over thousands of rows is split along K and its
 // partial products summed in a fixed order (the result repeats bit for bit from run to run).
+// The GELU backward step fused into an input-gradient product (A K-major, B M-major, BM = 64 tiles):
+// instead of C, g = C * gelu'(u) (u fp32 [M][ldu], the GELU input; erf selects the erf form) is
+// written in bf16 to y [rows][ldy] (rows M .. ceil(M/64)*64 - 1 get 0), and the sums of g over each
+// 64-row block to part[block][N] (the bias gradient's partial column sums).
+struct TnGeluBack {
+    const float* u = nullptr;
+    long ldu = 0;
+    uint16_t* y = nullptr;
+    long ldy = 0;
+    float* part = nullptr;
+    int erf = 0;
+};
 hipError_t gemm_bf16_tn(const uint16_t* A, bool a_mmajor, long lda, int a_lim, const uint16_t* B, bool b_mmajor,
                         long ldb, int b_lim, float* C, long ldc, int M, int N, int K, hipStream_t s,
-                        float* part = nullptr, size_t part_elems = 0);
+                        float* part = nullptr, size_t part_elems = 0, const TnGeluBack* gb = nullptr);
 }  // namespace gpt2k

@@ -433,7 +433,7 @@ struct TrainLayout {
     WorkspaceLayout fw;
     size_t layer0, per_layer;
     size_t l_xin, l_xmid, l_a1, l_qkv, l_o, l_a2, l_u, l_h, l_lse;  // inside one layer's block
-    size_t splitk, splitk_elems;
+    size_t splitk, splitk_elems, dact2;
     size_t xfin, xf, logits, dx, dbuf, dbuf2, dact, dT, xT, wT, wteT, dlog, dlogT, part, bpart, lnpg, lnpb, lse, dvec, nll,
         cnt;
     size_t total;
@@ -478,6 +478,8 @@ TrainLayout train_layout(const gpt2_model* m, int B, int T) {
     L.dbuf = take(L.M * L.wide * 4);
     L.dbuf2 = take(L.M * L.wide * 4);
     L.dact = take(L.Mp * L.wide * as);
+    // bf16: c_fc's output gradient, written by the GELU-backward epilogue of mlp.c_proj's input gradient
+    L.dact2 = take(is_bf16(m) ? L.Mp * c.d_mlp * 2 : 0);
     // transposed operands (fp32 mode only: the bf16 products read M-major operands directly)
     const bool tr_ops = !is_bf16(m);
     L.dT = take(tr_ops ? L.rows_dT * L.Mk * as : 0);
@@ -635,6 +637,21 @@ gpt2_status enqueue_backward(const gpt2_model* m, const int32_t* tokens, int B, 
     std::vector<gpt2k::ColsumSeg> bsegs;
     float* bpart = reinterpret_cast<float*>(ws + L.bpart);
     const int nbp = (int)((Mk + 63) / 64);
+    // bf16: the weight gradient and the input gradient from the bf16 output gradient dy16 (rows M .. Mk-1
+    // zero) whose bias partial sums are at bp; gb: the input gradient goes through the GELU backward
+    // into c_fc's output gradient instead (dx_out unused)
+    auto linear_back16 = [&](const uint16_t* dy16, float* bp, int n_out, const void* x_act, int n_in, int widx,
+                             float* dx_out, const gpt2k::TnGeluBack* gb) -> hipError_t {
+        hipError_t e;
+        bsegs.push_back({bp, G(widx + 1), nbp, n_out});
+        // dW [n_out, n_in] = sum over rows m < Mk of dy[m]^T x[m]
+        if ((e = gpt2k::gemm_bf16_tn(dy16, true, n_out, n_out, static_cast<const uint16_t*>(x_act), true, n_in, n_in,
+                                     G(widx), n_in, n_out, n_in, Mk, s, splitk, L.splitk_elems)) != hipSuccess)
+            return e;
+        // dX [M, n_in] = dy W, W [n_out][n_in] reduced over its rows
+        return gpt2k::gemm_bf16_tn(dy16, false, n_out, Mk, static_cast<const uint16_t*>(wptr(m, widx)), true, n_in,
+                                   n_in, dx_out, n_in, M, n_in, n_out, s, nullptr, 0, gb);
+    };
     auto linear_back = [&](const float* dy, int n_out, const void* x_act, int n_in, int widx, float* dx_out) -> hipError_t {
         hipError_t e;
         if (bf) {
@@ -642,15 +659,9 @@ gpt2_status enqueue_backward(const gpt2_model* m, const int32_t* tokens, int B, 
             uint16_t* dy16 = reinterpret_cast<uint16_t*>(dact);
             if ((e = gpt2k::convert_colsum_partials(dy, n_out, M, n_out, dy16, n_out, Mk, bpart, s)) != hipSuccess)
                 return e;
-            bsegs.push_back({bpart, G(widx + 1), nbp, n_out});
+            float* bp = bpart;
             bpart += (size_t)nbp * n_out;
-            // dW [n_out, n_in] = sum over rows m < Mk of dy[m]^T x[m]
-            if ((e = gpt2k::gemm_bf16_tn(dy16, true, n_out, n_out, static_cast<const uint16_t*>(x_act), true, n_in, n_in,
-                                         G(widx), n_in, n_out, n_in, Mk, s, splitk, L.splitk_elems)) != hipSuccess)
-                return e;
-            // dX [M, n_in] = dy W, W [n_out][n_in] reduced over its rows
-            return gpt2k::gemm_bf16_tn(dy16, false, n_out, Mk, static_cast<const uint16_t*>(wptr(m, widx)), true, n_in,
-                                       n_in, dx_out, n_in, M, n_in, n_out, s);
+            return linear_back16(dy16, bp, n_out, x_act, n_in, widx, dx_out, nullptr);
         } else {
             if ((e = gpt2k::colsum(dy, n_out, M, n_out, part, G(widx + 1), s)) != hipSuccess) return e;
             if ((e = tr(dy, false, n_out, M, n_out, dT, Mk, Mk)) != hipSuccess) return e;
@@ -696,10 +707,30 @@ gpt2_status enqueue_backward(const gpt2_model* m, const int32_t* tokens, int B, 
         auto I = [&](int t) { return layer_idx(l, t); };
         auto vecp = [&](int t) { return static_cast<const float*>(wptr(m, I(t))); };
         // MLP projection, GELU, c_fc, ln_2
-        GPT2_HIP(linear_back(dx, d, lay(l, L.l_h), f, I(MPROJ_W), dbuf));
         const float* u = reinterpret_cast<const float*>(lay(l, L.l_u));
-        GPT2_HIP(gpt2k::gelu_backward(u, dbuf, (long)M * f, c.gelu == GPT2_GELU_ERF, s));
-        GPT2_HIP(linear_back(dbuf, f, lay(l, L.l_a2), d, I(FC_W), dbuf2));
+        if (bf) {
+            // mlp.c_proj's input gradient goes through the GELU backward in its epilogue, which writes
+            // c_fc's bf16 output gradient and its bias partial sums
+            uint16_t* dy16 = reinterpret_cast<uint16_t*>(dact);
+            GPT2_HIP(gpt2k::convert_colsum_partials(dx, d, M, d, dy16, d, Mk, bpart, s));
+            float* bp_proj = bpart;
+            bpart += (size_t)nbp * d;
+            float* bp_fc = bpart;
+            bpart += (size_t)nbp * f;
+            gpt2k::TnGeluBack gb;
+            gb.u = u;
+            gb.ldu = f;
+            gb.y = reinterpret_cast<uint16_t*>(ws + L.dact2);
+            gb.ldy = f;
+            gb.part = bp_fc;
+            gb.erf = c.gelu == GPT2_GELU_ERF;
+            GPT2_HIP(linear_back16(dy16, bp_proj, d, lay(l, L.l_h), f, I(MPROJ_W), nullptr, &gb));
+            GPT2_HIP(linear_back16(gb.y, bp_fc, f, lay(l, L.l_a2), d, I(FC_W), dbuf2, nullptr));
+        } else {
+            GPT2_HIP(linear_back(dx, d, lay(l, L.l_h), f, I(MPROJ_W), dbuf));
+            GPT2_HIP(gpt2k::gelu_backward(u, dbuf, (long)M * f, c.gelu == GPT2_GELU_ERF, s));
+            GPT2_HIP(linear_back(dbuf, f, lay(l, L.l_a2), d, I(FC_W), dbuf2));
+        }
         GPT2_HIP(gpt2k::ln_backward(reinterpret_cast<const float*>(lay(l, L.l_xmid)), vecp(LN2_W), dbuf2, dx, M, d,
                                     c.ln_eps, lnpg, lnpb, G(I(LN2_W)), G(I(LN2_B)), s));
         // attention projection, attention, c_attn, ln_1

@@ -342,14 +342,7 @@ __global__ void __launch_bounds__(64 * kLnWaves) ln_backward_kernel(const float*
 }
 
 // ------------------------------------------------------------------------------ GELU
-__device__ __forceinline__ float gelu_tanh_grad(float x) {
-    const float c = 0.7978845608028654f;  // sqrt(2/pi)
-    const float t = tanhf(c * (x + 0.044715f * x * x * x));
-    return 0.5f * (1.0f + t) + 0.5f * x * (1.0f - t * t) * c * (1.0f + 3.0f * 0.044715f * x * x);
-}
-__device__ __forceinline__ float gelu_erf_grad(float x) {
-    return 0.5f * (1.0f + erff(x * 0.7071067811865476f)) + x * 0.3989422804014327f * expf(-0.5f * x * x);
-}
+// (gelu_tanh_grad / gelu_erf_grad: common.h)
 // h = gelu(u) in the compute dtype (the values the fused forward epilogue produces from the same u)
 template <bool BF>
 __global__ void gelu_forward_kernel(const float* __restrict__ u, void* __restrict__ h, long n, int erf_form) {
