@@ -183,8 +183,9 @@ struct HeadOut {
     // Tiled bf16 GEMM only (more than kSkinnyM rows, row-major output):
     //   EPI_BIAS_RESIDUAL with res set: C = res + (A W^T + b), res an fp32 matrix with C's row stride
     //     (the residual read from one buffer and written to another, instead of C += ...);
-    //   EPI_BIAS_GELU_U: u = A W^T + b (fp32, row stride ldc) and C = gelu(u) in bf16 (tanh form;
-    //     the erf form with gelu_erf), the values the plain GELU epilogue stores.
+    //   EPI_BIAS_GELU_U: u = A W^T + b (fp32, row-major with row stride ldc) and C = gelu(u) in bf16
+    //     (row-major or k-blocked; tanh form, the erf form with gelu_erf), the values the plain GELU
+    //     epilogue stores.
     const float* res = nullptr;
     float* u = nullptr;
 };

@@ -54,7 +54,7 @@ hipError_t gemm_bf16(const uint16_t* A, const uint16_t* W, const float* bias, vo
     if (ldc < N || ldc > (1 << 26)) return hipErrorInvalidValue;  // in-strip offsets are 32-bit
     // a separate residual source and the saved GELU input: tiled kernel, row-major output only
     if (ho.res && (epi != EPI_BIAS_RESIDUAL || M <= kSkinnyM)) return hipErrorInvalidValue;
-    if (epi == EPI_BIAS_GELU_U && (!ho.u || M <= kSkinnyM || kb || c_kb_rows || (ldc & 3))) return hipErrorInvalidValue;
+    if (epi == EPI_BIAS_GELU_U && (!ho.u || M <= kSkinnyM || (ldc & 3))) return hipErrorInvalidValue;
     if (M <= kSkinnyM) {  // a few rows: a stream over W (row-major operands and output only)
         if (kb || c_kb_rows) return hipErrorInvalidValue;
         return gemm_bf16_skinny(A, W, bias, C, M, N, K, (int)ldc, epi, gelu_erf, a_rows, w_rows, ho, SkinnyExtra(), s);

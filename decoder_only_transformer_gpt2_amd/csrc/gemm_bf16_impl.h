@@ -607,15 +607,11 @@ hipError_t launch_cfg(const uint16_t* A, const uint16_t* W, const float* bias, v
                 GPT2_LAUNCH(EPI_BIAS_GELU);
             break;
         case EPI_BIAS_RESIDUAL: GPT2_LAUNCH(EPI_BIAS_RESIDUAL); break;
-        case EPI_BIAS_GELU_U:  // row-major operands only (the training forward)
-            if constexpr (KB) {
-                return hipErrorInvalidValue;
-            } else {
-                if (gelu_erf)
-                    GPT2_LAUNCH(EPI_BIAS_GELU_U_ERF);
-                else
-                    GPT2_LAUNCH(EPI_BIAS_GELU_U);
-            }
+        case EPI_BIAS_GELU_U:  // (the training forward)
+            if (gelu_erf)
+                GPT2_LAUNCH(EPI_BIAS_GELU_U_ERF);
+            else
+                GPT2_LAUNCH(EPI_BIAS_GELU_U);
             break;
         case EPI_LSE: GPT2_LAUNCH(EPI_LSE); break;
         default: GPT2_LAUNCH(EPI_LOGITS); break;

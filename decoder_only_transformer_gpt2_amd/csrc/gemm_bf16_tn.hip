@@ -42,7 +42,8 @@ __device__ __forceinline__ u32x2_t lds_tr16(const uint16_t* p) {
     return __builtin_bit_cast(u32x2_t, v);
 }
 
-template <int BM, int BN, int S, int WGM, int WGN, bool AMM, bool BMM, int NKT, bool GB = false>
+// BKB: the M-major B operand is k-blocked ([N/32][ldb][32]: element (k, n) at ((n / 32) * ldb + k) * 32 + n % 32).
+template <int BM, int BN, int S, int WGM, int WGN, bool AMM, bool BMM, int NKT, bool GB = false, bool BKB = false>
 __global__ __launch_bounds__(64 * WGM * WGN, S * (BM + BN) * TBK * 2 <= 80 * 1024 ? 2 : 1) void gemm_tn_kernel(
     const uint16_t* __restrict__ A, long lda, int a_lim, const uint16_t* __restrict__ B, long ldb, int b_lim,
     float* __restrict__ C, long ldc, int M, int N, int K, int tiles_m, int ntiles, TnGeluBack gb) {
@@ -89,8 +90,13 @@ __global__ __launch_bounds__(64 * WGM * WGN, S * (BM + BN) * TBK * 2 <= 80 * 102
             const int e = qb * 512 + 8 * lane, kr = e / width, sch = (e % width) / 8;
             const int sw = is_a ? (AMM ? mswz<BM>(kr) : 0) : (BMM ? mswz<BN>(kr) : 0);
             const int col = min(base + 8 * (sch ^ sw), lim - 8);  // columns past the operand: any finite data
-            src[p] = X + (long)kr * ld + col;
-            kstep[p] = TBK * ld;
+            if (BKB && !is_a) {
+                src[p] = X + ((long)(col >> 5) * ld + kr) * 32 + (col & 31);
+                kstep[p] = TBK * 32;
+            } else {
+                src[p] = X + (long)kr * ld + col;
+                kstep[p] = TBK * ld;
+            }
         } else {
             const int row = qb * 8 + (lane >> 3), sch = lane & 7;
             const int g = min(base + row, lim - 1);
@@ -288,20 +294,20 @@ __global__ __launch_bounds__(256) void splitk_sum_kernel(const float4* __restric
 
 // nsplit > 1: the K range is split into nsplit parts of K / nsplit (a multiple of TBK); their
 // partial products go to part (nsplit x M x N floats) and are then summed into C.
-template <int BM, int BN, int S, int WGM, int WGN, bool AMM, bool BMM, int NKT, bool GB = false>
+template <int BM, int BN, int S, int WGM, int WGN, bool AMM, bool BMM, int NKT, bool GB = false, bool BKB = false>
 hipError_t launch_tn(const uint16_t* A, long lda, int a_lim, const uint16_t* B, long ldb, int b_lim, float* C, long ldc,
                      int M, int N, int K, hipStream_t s, int nsplit = 1, float* part = nullptr,
                      const TnGeluBack& gb = TnGeluBack()) {
     const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN, ntiles = tiles_m * tiles_n;
     if (nsplit > 1) {
-        gemm_tn_kernel<BM, BN, S, WGM, WGN, AMM, BMM, NKT><<<dim3(ntiles * nsplit), dim3(64 * WGM * WGN), 0, s>>>(
+        gemm_tn_kernel<BM, BN, S, WGM, WGN, AMM, BMM, NKT, GB, BKB><<<dim3(ntiles * nsplit), dim3(64 * WGM * WGN), 0, s>>>(
             A, lda, a_lim, B, ldb, b_lim, part, N, M, N, K / nsplit, tiles_m, ntiles, gb);
         const long n4 = (long)M * (N / 4);
         splitk_sum_kernel<<<dim3((unsigned)std::min<long>((n4 + 255) / 256, 4096)), dim3(256), 0, s>>>(
             reinterpret_cast<const float4*>(part), nsplit, M, N / 4, C, ldc);
         return hipGetLastError();
     }
-    gemm_tn_kernel<BM, BN, S, WGM, WGN, AMM, BMM, NKT, GB><<<dim3(ntiles), dim3(64 * WGM * WGN), 0, s>>>(
+    gemm_tn_kernel<BM, BN, S, WGM, WGN, AMM, BMM, NKT, GB, BKB><<<dim3(ntiles), dim3(64 * WGM * WGN), 0, s>>>(
         A, lda, a_lim, B, ldb, b_lim, C, ldc, M, N, K, tiles_m, ntiles, gb);
     return hipGetLastError();
 }
@@ -310,9 +316,31 @@ hipError_t launch_tn(const uint16_t* A, long lda, int a_lim, const uint16_t* B, 
 
 hipError_t gemm_bf16_tn(const uint16_t* A, bool a_mmajor, long lda, int a_lim, const uint16_t* B, bool b_mmajor,
                         long ldb, int b_lim, float* C, long ldc, int M, int N, int K, hipStream_t s, float* part,
-                        size_t part_elems, const TnGeluBack* gb) {
+                        size_t part_elems, const TnGeluBack* gb, bool b_kb) {
     if (M < 1 || N < 1 || K < TBK || K % TBK || !b_mmajor) return hipErrorInvalidValue;
     const int nk = K / TBK;
+    if (b_kb) {
+        // weight gradients on a k-blocked activation (ldb = its rows per block, >= K; b_lim a
+        // multiple of 32): 64 x 128 tiles, the narrow ones split along K as below
+        if (!a_mmajor || gb || ldb < K || b_lim % 32 || M >= 16384) return hipErrorInvalidValue;
+        auto fits4 = [&]() {
+            return part && N % 4 == 0 && ldc % 4 == 0 && reinterpret_cast<uintptr_t>(C) % 16 == 0 &&
+                   (size_t)4 * M * N <= part_elems;
+        };
+        const long t64 = (long)((M + 63) / 64) * ((N + 127) / 128);
+        if (t64 < 128 && nk % 4 == 0 && nk >= 16 && fits4()) {
+            if (nk == 64)
+                return launch_tn<64, 128, 3, 2, 2, true, true, 16, false, true>(A, lda, a_lim, B, ldb, b_lim, C, ldc, M,
+                                                                                N, K, s, 4, part);
+            return launch_tn<64, 128, 3, 2, 2, true, true, 0, false, true>(A, lda, a_lim, B, ldb, b_lim, C, ldc, M, N,
+                                                                           K, s, 4, part);
+        }
+        if (nk == 64)
+            return launch_tn<64, 128, 3, 2, 2, true, true, 64, false, true>(A, lda, a_lim, B, ldb, b_lim, C, ldc, M, N,
+                                                                            K, s);
+        return launch_tn<64, 128, 3, 2, 2, true, true, 0, false, true>(A, lda, a_lim, B, ldb, b_lim, C, ldc, M, N, K,
+                                                                       s);
+    }
     if (gb) {  // input gradient of c_fc's output through the GELU: 64 x 128 tiles, no split
         if (a_mmajor || !gb->u || !gb->y || !gb->part || gb->ldu < N || gb->ldy < N || gb->ldu % 4 || gb->ldy % 8 ||
             reinterpret_cast<uintptr_t>(gb->u) % 16 || reinterpret_cast<uintptr_t>(gb->y) % 16)

@@ -27,5 +27,7 @@ struct TnGeluBack {
 };
 hipError_t gemm_bf16_tn(const uint16_t* A, bool a_mmajor, long lda, int a_lim, const uint16_t* B, bool b_mmajor,
                         long ldb, int b_lim, float* C, long ldc, int M, int N, int K, hipStream_t s,
-                        float* part = nullptr, size_t part_elems = 0, const TnGeluBack* gb = nullptr);
+                        float* part = nullptr, size_t part_elems = 0, const TnGeluBack* gb = nullptr,
+                        bool b_kb = false);
+// (b_kb: B is M-major and k-blocked, [N/32][ldb][32] with ldb >= K rows per block; weight gradients only)
 }  // namespace gpt2k

@@ -520,6 +520,7 @@ gpt2_status enqueue_train_forward(const gpt2_model* m, const int32_t* tokens, co
     // bf16 on the tiled GEMM (more than kSkinnyM rows): residual sums and the GELU input come from
     // the projections' epilogues
     const bool tiled = bf && M > gpt2k::kSkinnyM;
+    const int Mp = (int)L.Mp;
     GPT2_HIP(gpt2k::embed(tokens, wptr(m, 0), wptr(m, 1), reinterpret_cast<float*>(lay(0, L.l_xin)), M, T, 0, d,
                           c.n_vocab, bf, reinterpret_cast<int32_t*>(ws + L.fw.flags), s));
     for (int l = 0; l < c.n_layer; ++l) {
@@ -534,8 +535,10 @@ gpt2_status enqueue_train_forward(const gpt2_model* m, const int32_t* tokens, co
         char* a2 = lay(l, L.l_a2);
         float* u = reinterpret_cast<float*>(lay(l, L.l_u));
         char* h = lay(l, L.l_h);
-        GPT2_HIP(gpt2k::layernorm(xin, vecp(LN1_W), vecp(LN1_B), a1, M, d, c.ln_eps, bf, s));
-        GPT2_HIP(linear(m, a1, I(ATTN_W), I(ATTN_B), qkv, M, 3 * d, d, 3 * d, gpt2k::EPI_BIAS, {}, s));
+        // tiled bf16: the LayerNorm outputs and the GELU output are k-blocked (the layout the
+        // projections stream best; the backward's weight gradients read them that way too)
+        GPT2_HIP(gpt2k::layernorm(xin, vecp(LN1_W), vecp(LN1_B), a1, M, d, c.ln_eps, bf, s, tiled ? Mp : 0));
+        GPT2_HIP(linear(m, a1, I(ATTN_W), I(ATTN_B), qkv, M, 3 * d, d, 3 * d, gpt2k::EPI_BIAS, {}, s, tiled));
         if (bf)
             GPT2_HIP(gpt2k::attention_bf16(reinterpret_cast<const uint16_t*>(qkv), qs,
                                            reinterpret_cast<const uint16_t*>(qkv + d * as), qs,
@@ -557,11 +560,11 @@ gpt2_status enqueue_train_forward(const gpt2_model* m, const int32_t* tokens, co
             GPT2_HIP(hipMemcpyAsync(xmid, xin, (size_t)M * d * 4, hipMemcpyDeviceToDevice, s));
             GPT2_HIP(linear(m, o, I(APROJ_W), I(APROJ_B), xmid, M, d, d, d, gpt2k::EPI_BIAS_RESIDUAL, {}, s));
         }
-        GPT2_HIP(gpt2k::layernorm(xmid, vecp(LN2_W), vecp(LN2_B), a2, M, d, c.ln_eps, bf, s));
+        GPT2_HIP(gpt2k::layernorm(xmid, vecp(LN2_W), vecp(LN2_B), a2, M, d, c.ln_eps, bf, s, tiled ? Mp : 0));
         if (tiled) {  // u and h = gelu(u) from one epilogue
             gpt2k::HeadOut hu;
             hu.u = u;
-            GPT2_HIP(linear(m, a2, I(FC_W), I(FC_B), h, M, f, d, f, gpt2k::EPI_BIAS_GELU_U, hu, s));
+            GPT2_HIP(linear(m, a2, I(FC_W), I(FC_B), h, M, f, d, f, gpt2k::EPI_BIAS_GELU_U, hu, s, true, true));
         } else {
             GPT2_HIP(hipMemsetAsync(u, 0, (size_t)M * f * 4, s));
             GPT2_HIP(linear(m, a2, I(FC_W), I(FC_B), u, M, f, d, f, gpt2k::EPI_BIAS_RESIDUAL, {}, s));
@@ -570,7 +573,7 @@ gpt2_status enqueue_train_forward(const gpt2_model* m, const int32_t* tokens, co
         if (tiled) {
             gpt2k::HeadOut hr;
             hr.res = xmid;
-            GPT2_HIP(linear(m, h, I(MPROJ_W), I(MPROJ_B), xout, M, d, f, d, gpt2k::EPI_BIAS_RESIDUAL, hr, s));
+            GPT2_HIP(linear(m, h, I(MPROJ_W), I(MPROJ_B), xout, M, d, f, d, gpt2k::EPI_BIAS_RESIDUAL, hr, s, true));
         } else {
             GPT2_HIP(hipMemcpyAsync(xout, xmid, (size_t)M * d * 4, hipMemcpyDeviceToDevice, s));
             GPT2_HIP(linear(m, h, I(MPROJ_W), I(MPROJ_B), xout, M, d, f, d, gpt2k::EPI_BIAS_RESIDUAL, {}, s));
@@ -601,6 +604,8 @@ gpt2_status enqueue_backward(const gpt2_model* m, const int32_t* tokens, int B, 
     const bool bf = is_bf16(m);
     const int M = B * T, d = c.d_model, f = c.d_mlp, H = c.n_head, V = c.n_vocab;
     const int Mp = (int)L.Mp, Mk = (int)L.Mk, Vp = (int)L.Vp;
+    // the tiled bf16 forward left the LayerNorm and GELU outputs k-blocked (Mp rows per 32-column block)
+    const bool x_kb = bf && M > gpt2k::kSkinnyM;
     auto lay = [&](int l, size_t o) { return ws + L.layer0 + (size_t)l * L.per_layer + o; };
     auto G = [&](int i) { return grads + grad_offset(m, i) / 4; };
     auto pad = [&](int64_t r) { return (int)round_up(r, kRowPad); };
@@ -640,19 +645,22 @@ gpt2_status enqueue_backward(const gpt2_model* m, const int32_t* tokens, int B, 
     // bf16: the weight gradient and the input gradient from the bf16 output gradient dy16 (rows M .. Mk-1
     // zero) whose bias partial sums are at bp; gb: the input gradient goes through the GELU backward
     // into c_fc's output gradient instead (dx_out unused)
-    auto linear_back16 = [&](const uint16_t* dy16, float* bp, int n_out, const void* x_act, int n_in, int widx,
-                             float* dx_out, const gpt2k::TnGeluBack* gb) -> hipError_t {
+    // (x_kb: the activation x is k-blocked with Mp rows per block, as the tiled forward writes it)
+    auto linear_back16 = [&](const uint16_t* dy16, float* bp, int n_out, const void* x_act, int n_in, bool x_kb,
+                             int widx, float* dx_out, const gpt2k::TnGeluBack* gb) -> hipError_t {
         hipError_t e;
         bsegs.push_back({bp, G(widx + 1), nbp, n_out});
         // dW [n_out, n_in] = sum over rows m < Mk of dy[m]^T x[m]
-        if ((e = gpt2k::gemm_bf16_tn(dy16, true, n_out, n_out, static_cast<const uint16_t*>(x_act), true, n_in, n_in,
-                                     G(widx), n_in, n_out, n_in, Mk, s, splitk, L.splitk_elems)) != hipSuccess)
+        if ((e = gpt2k::gemm_bf16_tn(dy16, true, n_out, n_out, static_cast<const uint16_t*>(x_act), true,
+                                     x_kb ? Mp : n_in, n_in, G(widx), n_in, n_out, n_in, Mk, s, splitk,
+                                     L.splitk_elems, nullptr, x_kb)) != hipSuccess)
             return e;
         // dX [M, n_in] = dy W, W [n_out][n_in] reduced over its rows
         return gpt2k::gemm_bf16_tn(dy16, false, n_out, Mk, static_cast<const uint16_t*>(wptr(m, widx)), true, n_in,
                                    n_in, dx_out, n_in, M, n_in, n_out, s, nullptr, 0, gb);
     };
-    auto linear_back = [&](const float* dy, int n_out, const void* x_act, int n_in, int widx, float* dx_out) -> hipError_t {
+    auto linear_back = [&](const float* dy, int n_out, const void* x_act, int n_in, bool x_kb, int widx,
+                           float* dx_out) -> hipError_t {
         hipError_t e;
         if (bf) {
             // dy -> bf16 rows (zero from M to Mk) with the bias gradient's column-sum partials
@@ -661,7 +669,7 @@ gpt2_status enqueue_backward(const gpt2_model* m, const int32_t* tokens, int B, 
                 return e;
             float* bp = bpart;
             bpart += (size_t)nbp * n_out;
-            return linear_back16(dy16, bp, n_out, x_act, n_in, widx, dx_out, nullptr);
+            return linear_back16(dy16, bp, n_out, x_act, n_in, x_kb, widx, dx_out, nullptr);
         } else {
             if ((e = gpt2k::colsum(dy, n_out, M, n_out, part, G(widx + 1), s)) != hipSuccess) return e;
             if ((e = tr(dy, false, n_out, M, n_out, dT, Mk, Mk)) != hipSuccess) return e;
@@ -675,11 +683,17 @@ gpt2_status enqueue_backward(const gpt2_model* m, const int32_t* tokens, int B, 
     if (bf && Mk > M) {
         // rows M .. Mk-1 of the M-major operands: zero (the reductions run over Mk rows)
         const size_t pr = (size_t)(Mk - M);
+        // (k-blocked: those rows of every 32-column block)
+        auto zero_rows = [&](char* p, int n) {
+            if (x_kb)
+                return hipMemset2DAsync(p + (size_t)M * 64, (size_t)Mp * 64, 0, pr * 64, (size_t)n / 32, s);
+            return hipMemsetAsync(p + (size_t)M * n * 2, 0, pr * n * 2, s);
+        };
         for (int l = 0; l < c.n_layer; ++l) {
-            GPT2_HIP(hipMemsetAsync(lay(l, L.l_a1) + (size_t)M * d * 2, 0, pr * d * 2, s));
+            GPT2_HIP(zero_rows(lay(l, L.l_a1), d));
             GPT2_HIP(hipMemsetAsync(lay(l, L.l_o) + (size_t)M * d * 2, 0, pr * d * 2, s));
-            GPT2_HIP(hipMemsetAsync(lay(l, L.l_a2) + (size_t)M * d * 2, 0, pr * d * 2, s));
-            GPT2_HIP(hipMemsetAsync(lay(l, L.l_h) + (size_t)M * f * 2, 0, pr * f * 2, s));
+            GPT2_HIP(zero_rows(lay(l, L.l_a2), d));
+            GPT2_HIP(zero_rows(lay(l, L.l_h), f));
         }
         GPT2_HIP(hipMemsetAsync(ws + L.xf + (size_t)M * d * 2, 0, pr * d * 2, s));
         GPT2_HIP(hipMemsetAsync(ws + L.dlog + (size_t)M * Vp * 2, 0, pr * Vp * 2, s));
@@ -724,21 +738,21 @@ gpt2_status enqueue_backward(const gpt2_model* m, const int32_t* tokens, int B, 
             gb.ldy = f;
             gb.part = bp_fc;
             gb.erf = c.gelu == GPT2_GELU_ERF;
-            GPT2_HIP(linear_back16(dy16, bp_proj, d, lay(l, L.l_h), f, I(MPROJ_W), nullptr, &gb));
-            GPT2_HIP(linear_back16(gb.y, bp_fc, f, lay(l, L.l_a2), d, I(FC_W), dbuf2, nullptr));
+            GPT2_HIP(linear_back16(dy16, bp_proj, d, lay(l, L.l_h), f, x_kb, I(MPROJ_W), nullptr, &gb));
+            GPT2_HIP(linear_back16(gb.y, bp_fc, f, lay(l, L.l_a2), d, x_kb, I(FC_W), dbuf2, nullptr));
         } else {
-            GPT2_HIP(linear_back(dx, d, lay(l, L.l_h), f, I(MPROJ_W), dbuf));
+            GPT2_HIP(linear_back(dx, d, lay(l, L.l_h), f, false, I(MPROJ_W), dbuf));
             GPT2_HIP(gpt2k::gelu_backward(u, dbuf, (long)M * f, c.gelu == GPT2_GELU_ERF, s));
-            GPT2_HIP(linear_back(dbuf, f, lay(l, L.l_a2), d, I(FC_W), dbuf2));
+            GPT2_HIP(linear_back(dbuf, f, lay(l, L.l_a2), d, false, I(FC_W), dbuf2));
         }
         GPT2_HIP(gpt2k::ln_backward(reinterpret_cast<const float*>(lay(l, L.l_xmid)), vecp(LN2_W), dbuf2, dx, M, d,
                                     c.ln_eps, lnpg, lnpb, G(I(LN2_W)), G(I(LN2_B)), s));
         // attention projection, attention, c_attn, ln_1
-        GPT2_HIP(linear_back(dx, d, lay(l, L.l_o), d, I(APROJ_W), dbuf));
+        GPT2_HIP(linear_back(dx, d, lay(l, L.l_o), d, false, I(APROJ_W), dbuf));
         float* lse = reinterpret_cast<float*>(bf ? lay(l, L.l_lse) : ws + L.lse);  // bf16: written by the forward
         GPT2_HIP(gpt2k::attention_backward(lay(l, L.l_qkv), lay(l, L.l_o), dbuf, dbuf2, lse,
                                            reinterpret_cast<float*>(ws + L.dvec), B, H, T, bf, s));
-        GPT2_HIP(linear_back(dbuf2, 3 * d, lay(l, L.l_a1), d, I(ATTN_W), dbuf));
+        GPT2_HIP(linear_back(dbuf2, 3 * d, lay(l, L.l_a1), d, x_kb, I(ATTN_W), dbuf));
         GPT2_HIP(gpt2k::ln_backward(reinterpret_cast<const float*>(lay(l, L.l_xin)), vecp(LN1_W), dbuf, dx, M, d,
                                     c.ln_eps, lnpg, lnpb, G(I(LN1_W)), G(I(LN1_B)), s));
     }
