@@ -327,9 +327,12 @@ struct ColsumSegs {
 hipError_t colsum_reduce_multi(const ColsumSegs& segs, hipStream_t s);
 // LayerNorm backward on rows of x with output gradient dy (fp32 [M, d]): dx += the input gradient,
 // dgamma / dbeta = column sums (pg, pb hold ln_backward_blocks(M) * d floats each: partial rows).
+// With y16 (and pd, ln_backward_blocks(M) * d floats): the updated dx rows also in bf16 (row stride
+// d, rows 0..M-1 only) and their column sums' partial rows in pd, for a later colsum_reduce_multi.
 int ln_backward_blocks(int M);
 hipError_t ln_backward(const float* x, const float* gamma, const float* dy, float* dx, int M, int d, float eps, float* pg,
-                       float* pb, float* dgamma, float* dbeta, hipStream_t s);
+                       float* pb, float* dgamma, float* dbeta, hipStream_t s, uint16_t* y16 = nullptr,
+                       float* pd = nullptr);
 // h = gelu(u) in the compute dtype; g *= gelu'(u) in place (fp32).
 hipError_t gelu_forward(const float* u, void* h, long n, bool bf16, int erf_form, hipStream_t s);
 hipError_t gelu_backward(const float* u, float* g, long n, int erf_form, hipStream_t s);

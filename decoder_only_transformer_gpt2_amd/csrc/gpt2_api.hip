@@ -490,7 +490,10 @@ TrainLayout train_layout(const gpt2_model* m, int B, int T) {
     L.dlogT = take(tr_ops ? L.Vr * L.Mk * as : 0);
     L.part = take((size_t)std::max<int64_t>(gpt2k::colsum_blocks((int)L.M), (L.Mk + 63) / 64) * L.wide * 4);
     // bf16: the bias gradients' partial column sums of every layer, reduced in one launch at the end
-    L.bpart = take(is_bf16(m) ? (size_t)((L.Mk + 63) / 64) * (3 * d + d + f + d) * c.n_layer * 4 : 0);
+    // (c_attn, c_fc: one row per 64-row block; attn.c_proj, mlp.c_proj: one per LayerNorm-backward block)
+    L.bpart = take(is_bf16(m) ? ((size_t)((L.Mk + 63) / 64) * (3 * d + f) +
+                                 (size_t)gpt2k::ln_backward_blocks((int)L.M) * 2 * d) * c.n_layer * 4
+                              : 0);
     L.lnpg = take((size_t)gpt2k::ln_backward_blocks((int)L.M) * d * 4);
     L.lnpb = take((size_t)gpt2k::ln_backward_blocks((int)L.M) * d * 4);
     L.lse = take(is_bf16(m) ? 0 : (size_t)B * c.n_head * T * 4);  // fp32 mode: the backward finds it
@@ -646,10 +649,11 @@ gpt2_status enqueue_backward(const gpt2_model* m, const int32_t* tokens, int B, 
     // zero) whose bias partial sums are at bp; gb: the input gradient goes through the GELU backward
     // into c_fc's output gradient instead (dx_out unused)
     // (x_kb: the activation x is k-blocked with Mp rows per block, as the tiled forward writes it)
-    auto linear_back16 = [&](const uint16_t* dy16, float* bp, int n_out, const void* x_act, int n_in, bool x_kb,
-                             int widx, float* dx_out, const gpt2k::TnGeluBack* gb) -> hipError_t {
+    // (nb: the partial rows at bp)
+    auto linear_back16 = [&](const uint16_t* dy16, float* bp, int nb, int n_out, const void* x_act, int n_in,
+                             bool x_kb, int widx, float* dx_out, const gpt2k::TnGeluBack* gb) -> hipError_t {
         hipError_t e;
-        bsegs.push_back({bp, G(widx + 1), nbp, n_out});
+        bsegs.push_back({bp, G(widx + 1), nb, n_out});
         // dW [n_out, n_in] = sum over rows m < Mk of dy[m]^T x[m]
         if ((e = gpt2k::gemm_bf16_tn(dy16, true, n_out, n_out, static_cast<const uint16_t*>(x_act), true,
                                      x_kb ? Mp : n_in, n_in, G(widx), n_in, n_out, n_in, Mk, s, splitk,
@@ -669,7 +673,7 @@ gpt2_status enqueue_backward(const gpt2_model* m, const int32_t* tokens, int B, 
                 return e;
             float* bp = bpart;
             bpart += (size_t)nbp * n_out;
-            return linear_back16(dy16, bp, n_out, x_act, n_in, x_kb, widx, dx_out, nullptr);
+            return linear_back16(dy16, bp, nbp, n_out, x_act, n_in, x_kb, widx, dx_out, nullptr);
         } else {
             if ((e = gpt2k::colsum(dy, n_out, M, n_out, part, G(widx + 1), s)) != hipSuccess) return e;
             if ((e = tr(dy, false, n_out, M, n_out, dT, Mk, Mk)) != hipSuccess) return e;
@@ -714,21 +718,34 @@ gpt2_status enqueue_backward(const gpt2_model* m, const int32_t* tokens, int B, 
         GPT2_HIP(gemm_nt(ws + L.dlogT, (int)L.Vr, xT, pad(d), G(0), V, d, Mk, d));
     }
     GPT2_HIP(hipMemsetAsync(dx, 0, (size_t)M * d * 4, s));
+    // bf16: each LayerNorm backward also writes the next projection's bf16 output gradient (dact, row
+    // stride d) and that projection's bias partial sums (nbl rows at bp_ln); rows M .. Mk-1 stay zero
+    // (the weight gradients reduce over Mk rows)
+    uint16_t* dact16 = reinterpret_cast<uint16_t*>(dact);
+    const int nbl = gpt2k::ln_backward_blocks(M);
+    float* bp_ln = nullptr;
+    auto take_ln_part = [&]() {
+        bp_ln = bpart;
+        bpart += (size_t)nbl * d;
+        return bp_ln;
+    };
+    auto zero_dact_tail = [&]() {
+        return Mk > M ? hipMemsetAsync(dact16 + (size_t)M * d, 0, (size_t)(Mk - M) * d * 2, s) : hipSuccess;
+    };
     const int ln_f = 2 + c.n_layer * PER_LAYER;
+    if (bf) GPT2_HIP(zero_dact_tail());
     GPT2_HIP(gpt2k::ln_backward(reinterpret_cast<float*>(ws + L.xfin), static_cast<const float*>(wptr(m, ln_f)), dbuf, dx,
-                                M, d, c.ln_eps, lnpg, lnpb, G(ln_f), G(ln_f + 1), s));
+                                M, d, c.ln_eps, lnpg, lnpb, G(ln_f), G(ln_f + 1), s, bf ? dact16 : nullptr,
+                                bf ? take_ln_part() : nullptr));
     for (int l = c.n_layer - 1; l >= 0; --l) {
         auto I = [&](int t) { return layer_idx(l, t); };
         auto vecp = [&](int t) { return static_cast<const float*>(wptr(m, I(t))); };
         // MLP projection, GELU, c_fc, ln_2
         const float* u = reinterpret_cast<const float*>(lay(l, L.l_u));
         if (bf) {
-            // mlp.c_proj's input gradient goes through the GELU backward in its epilogue, which writes
-            // c_fc's bf16 output gradient and its bias partial sums
-            uint16_t* dy16 = reinterpret_cast<uint16_t*>(dact);
-            GPT2_HIP(gpt2k::convert_colsum_partials(dx, d, M, d, dy16, d, Mk, bpart, s));
-            float* bp_proj = bpart;
-            bpart += (size_t)nbp * d;
+            // mlp.c_proj's output gradient: dact from the LayerNorm backward above; its input gradient
+            // goes through the GELU backward in its epilogue, which writes c_fc's bf16 output gradient
+            // and its bias partial sums
             float* bp_fc = bpart;
             bpart += (size_t)nbp * f;
             gpt2k::TnGeluBack gb;
@@ -738,23 +755,32 @@ gpt2_status enqueue_backward(const gpt2_model* m, const int32_t* tokens, int B, 
             gb.ldy = f;
             gb.part = bp_fc;
             gb.erf = c.gelu == GPT2_GELU_ERF;
-            GPT2_HIP(linear_back16(dy16, bp_proj, d, lay(l, L.l_h), f, x_kb, I(MPROJ_W), nullptr, &gb));
-            GPT2_HIP(linear_back16(gb.y, bp_fc, f, lay(l, L.l_a2), d, x_kb, I(FC_W), dbuf2, nullptr));
+            GPT2_HIP(linear_back16(dact16, bp_ln, nbl, d, lay(l, L.l_h), f, x_kb, I(MPROJ_W), nullptr, &gb));
+            GPT2_HIP(linear_back16(gb.y, bp_fc, nbp, f, lay(l, L.l_a2), d, x_kb, I(FC_W), dbuf2, nullptr));
         } else {
             GPT2_HIP(linear_back(dx, d, lay(l, L.l_h), f, false, I(MPROJ_W), dbuf));
             GPT2_HIP(gpt2k::gelu_backward(u, dbuf, (long)M * f, c.gelu == GPT2_GELU_ERF, s));
             GPT2_HIP(linear_back(dbuf, f, lay(l, L.l_a2), d, false, I(FC_W), dbuf2));
         }
+        if (bf) GPT2_HIP(zero_dact_tail());
         GPT2_HIP(gpt2k::ln_backward(reinterpret_cast<const float*>(lay(l, L.l_xmid)), vecp(LN2_W), dbuf2, dx, M, d,
-                                    c.ln_eps, lnpg, lnpb, G(I(LN2_W)), G(I(LN2_B)), s));
+                                    c.ln_eps, lnpg, lnpb, G(I(LN2_W)), G(I(LN2_B)), s, bf ? dact16 : nullptr,
+                                    bf ? take_ln_part() : nullptr));
         // attention projection, attention, c_attn, ln_1
-        GPT2_HIP(linear_back(dx, d, lay(l, L.l_o), d, false, I(APROJ_W), dbuf));
+        if (bf)
+            GPT2_HIP(linear_back16(dact16, bp_ln, nbl, d, lay(l, L.l_o), d, false, I(APROJ_W), dbuf, nullptr));
+        else
+            GPT2_HIP(linear_back(dx, d, lay(l, L.l_o), d, false, I(APROJ_W), dbuf));
         float* lse = reinterpret_cast<float*>(bf ? lay(l, L.l_lse) : ws + L.lse);  // bf16: written by the forward
         GPT2_HIP(gpt2k::attention_backward(lay(l, L.l_qkv), lay(l, L.l_o), dbuf, dbuf2, lse,
                                            reinterpret_cast<float*>(ws + L.dvec), B, H, T, bf, s));
         GPT2_HIP(linear_back(dbuf2, 3 * d, lay(l, L.l_a1), d, x_kb, I(ATTN_W), dbuf));
+        // (the layer below's mlp.c_proj output gradient; none below the first layer)
+        const bool next16 = bf && l > 0;
+        if (next16) GPT2_HIP(zero_dact_tail());
         GPT2_HIP(gpt2k::ln_backward(reinterpret_cast<const float*>(lay(l, L.l_xin)), vecp(LN1_W), dbuf, dx, M, d,
-                                    c.ln_eps, lnpg, lnpb, G(I(LN1_W)), G(I(LN1_B)), s));
+                                    c.ln_eps, lnpg, lnpb, G(I(LN1_W)), G(I(LN1_B)), s, next16 ? dact16 : nullptr,
+                                    next16 ? take_ln_part() : nullptr));
     }
     // every bias gradient, kColsumSegs segments per launch
     for (size_t i0 = 0; i0 < bsegs.size(); i0 += gpt2k::kColsumSegs) {

@@ -229,51 +229,49 @@ __global__ void __launch_bounds__(256) colsum_reduce_multi_kernel(const ColsumSe
 }
 
 // ------------------------------------------------------------------------------ LayerNorm backward
-// Four wavefronts per block of kLnRows rows, one row at a time per wavefront. For each row:
-// xhat = (x - mean) * rstd, g = dy * gamma, dx += rstd * (g - mean(g) - xhat * mean(g * xhat)). Each
-// wavefront sums dy * xhat and dy per column over its rows (lane l owns columns l + 64 j) and writes
-// them as partial row (block * kLnWaves + wave) of pg / pb [partials][d].
+// One block per kLnRows rows. For each row: xhat = (x - mean) * rstd, g = dy * gamma,
+// dx += rstd * (g - mean(g) - xhat * mean(g * xhat)). The block sums dy * xhat and dy per column over
+// its rows and writes them as partial row blockIdx.x of pg / pb [blocks][d]. With y16 the new dx is
+// also written in bf16 (row stride d) and its per-column sums as partial row blockIdx.x of pd: the
+// output gradient of the projection before this LayerNorm, with its bias gradient's partials.
 constexpr int kLnRows = 16, kLnWaves = 4;
 
-// CPL > 0: the row and the column sums held in registers (d = 64 * CPL); CPL = 0: any d (multiple
-// of 64), the row re-read and the sums kept in the wave's own partial rows.
+// CPL > 0 (d = 64 * CPL): kLnWaves wavefronts, one row at a time each, the row and the column sums held
+// in registers (lane l owns columns l + 64 j), the waves' sums added in wave order through LDS.
+// CPL = 0 (any d, a multiple of 64): one wavefront takes the block's rows in order, re-reading the row
+// and accumulating in its partial rows.
 template <int CPL>
 __global__ void __launch_bounds__(64 * kLnWaves) ln_backward_kernel(const float* __restrict__ x,
                                                                     const float* __restrict__ gamma,
                                                                     const float* __restrict__ dy, float* __restrict__ dx,
                                                                     int M, int d, float eps, float* __restrict__ pg,
-                                                                    float* __restrict__ pb) {
+                                                                    float* __restrict__ pb, uint16_t* __restrict__ y16,
+                                                                    float* __restrict__ pd) {
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, blk = blockIdx.x;
-    float* og = pg + (long)(blk * kLnWaves + w) * d;
-    float* ob = pb + (long)(blk * kLnWaves + w) * d;
+    float* og = pg + (long)blk * d;
+    float* ob = pb + (long)blk * d;
+    float* od = y16 ? pd + (long)blk * d : nullptr;
     const float inv_d = 1.0f / (float)d;
-    float ag[CPL > 0 ? CPL : 1], ab[CPL > 0 ? CPL : 1];
     if constexpr (CPL > 0) {
+        float ag[CPL], ab[CPL], ad[CPL];
 #pragma unroll
-        for (int j = 0; j < CPL; ++j) ag[j] = ab[j] = 0.f;
-    } else {
-        for (int c = lane; c < d; c += 64) og[c] = ob[c] = 0.f;
-    }
-    // CPL > 0: the next row's x, dy and dx are loaded while this row is processed
-    [[maybe_unused]] float xv[CPL > 0 ? CPL : 1], gv[CPL > 0 ? CPL : 1], dv[CPL > 0 ? CPL : 1];
-    auto load_row = [&](int m, float* xa, float* ga, float* da) {
+        for (int j = 0; j < CPL; ++j) ag[j] = ab[j] = ad[j] = 0.f;
+        // the next row's x, dy and dx are loaded while this row is processed
+        float xv[CPL], gv[CPL], dv[CPL];
+        auto load_row = [&](int m, float* xa, float* ga, float* da) {
 #pragma unroll
-        for (int j = 0; j < (CPL > 0 ? CPL : 1); ++j) {
-            xa[j] = x[(long)m * d + lane + 64 * j];
-            ga[j] = dy[(long)m * d + lane + 64 * j];
-            da[j] = dx[(long)m * d + lane + 64 * j];
-        }
-    };
-    if constexpr (CPL > 0)
+            for (int j = 0; j < CPL; ++j) {
+                xa[j] = x[(long)m * d + lane + 64 * j];
+                ga[j] = dy[(long)m * d + lane + 64 * j];
+                da[j] = dx[(long)m * d + lane + 64 * j];
+            }
+        };
         if (blk * kLnRows + w < M) load_row(blk * kLnRows + w, xv, gv, dv);
 #pragma unroll
-    for (int rr = w; rr < kLnRows; rr += kLnWaves) {
-        const int m = blk * kLnRows + rr;
-        if (m >= M) break;
-        const float* xr = x + (long)m * d;
-        const float* gr = dy + (long)m * d;
-        float* dr = dx + (long)m * d;
-        if constexpr (CPL > 0) {
+        for (int rr = w; rr < kLnRows; rr += kLnWaves) {
+            const int m = blk * kLnRows + rr;
+            if (m >= M) break;
+            float* dr = dx + (long)m * d;
             float xn[CPL], gn[CPL], dn[CPL];
             const bool has_next = rr + kLnWaves < kLnRows && m + kLnWaves < M;
             if (has_next) load_row(m + kLnWaves, xn, gn, dn);
@@ -298,7 +296,12 @@ __global__ void __launch_bounds__(64 * kLnWaves) ln_backward_kernel(const float*
             for (int j = 0; j < CPL; ++j) {
                 const int c = lane + 64 * j;
                 const float g = gv[j] * gamma[c];
-                dr[c] = dv[j] + rstd * (g - mg - xv[j] * mgx);
+                const float nv = dv[j] + rstd * (g - mg - xv[j] * mgx);
+                dr[c] = nv;
+                if (y16) {
+                    y16[(long)m * d + c] = f32_to_bf16_bits(nv);
+                    ad[j] += nv;
+                }
                 ag[j] += gv[j] * xv[j];
                 ab[j] += gv[j];
             }
@@ -310,7 +313,38 @@ __global__ void __launch_bounds__(64 * kLnWaves) ln_backward_kernel(const float*
                     dv[j] = dn[j];
                 }
             }
-        } else {
+        }
+        __shared__ float red[3][kLnWaves][CPL * 64];
+#pragma unroll
+        for (int j = 0; j < CPL; ++j) {
+            red[0][w][lane + 64 * j] = ag[j];
+            red[1][w][lane + 64 * j] = ab[j];
+            red[2][w][lane + 64 * j] = ad[j];
+        }
+        __syncthreads();
+        for (int c = threadIdx.x; c < d; c += 64 * kLnWaves) {
+            float sa = red[0][0][c], sb = red[1][0][c], sd = red[2][0][c];
+#pragma unroll
+            for (int v = 1; v < kLnWaves; ++v) {
+                sa += red[0][v][c];
+                sb += red[1][v][c];
+                sd += red[2][v][c];
+            }
+            og[c] = sa;
+            ob[c] = sb;
+            if (od) od[c] = sd;
+        }
+    } else {
+        for (int c = lane; c < d; c += 64) {
+            og[c] = ob[c] = 0.f;
+            if (od) od[c] = 0.f;
+        }
+        for (int rr = 0; rr < kLnRows; ++rr) {
+            const int m = blk * kLnRows + rr;
+            if (m >= M) break;
+            const float* xr = x + (long)m * d;
+            const float* gr = dy + (long)m * d;
+            float* dr = dx + (long)m * d;
             float s = 0.f;
             for (int c = lane; c < d; c += 64) s += xr[c];
             const float mean = wave_sum(s) * inv_d;
@@ -326,17 +360,15 @@ __global__ void __launch_bounds__(64 * kLnWaves) ln_backward_kernel(const float*
             const float mg = wave_sum(sg) * inv_d, mgx = wave_sum(sgx) * inv_d;
             for (int c = lane; c < d; c += 64) {
                 const float xh = (xr[c] - mean) * rstd, g = gr[c] * gamma[c];
-                dr[c] += rstd * (g - mg - xh * mgx);
+                const float nv = dr[c] + rstd * (g - mg - xh * mgx);
+                dr[c] = nv;
+                if (y16) {
+                    y16[(long)m * d + c] = f32_to_bf16_bits(nv);
+                    od[c] += nv;
+                }
                 og[c] += gr[c] * xh;
                 ob[c] += gr[c];
             }
-        }
-    }
-    if constexpr (CPL > 0) {
-#pragma unroll
-        for (int j = 0; j < CPL; ++j) {
-            og[lane + 64 * j] = ag[j];
-            ob[lane + 64 * j] = ab[j];
         }
     }
 }
@@ -818,22 +850,24 @@ hipError_t colsum(const float* src, long ld, int R, int C, float* part, float* o
     return hipGetLastError();
 }
 
-int ln_backward_blocks(int M) { return (M + kLnRows - 1) / kLnRows * kLnWaves; }
+int ln_backward_blocks(int M) { return (M + kLnRows - 1) / kLnRows; }
 
 hipError_t ln_backward(const float* x, const float* gamma, const float* dy, float* dx, int M, int d, float eps, float* pg,
-                       float* pb, float* dgamma, float* dbeta, hipStream_t s) {
-    const int nb = (M + kLnRows - 1) / kLnRows, np = ln_backward_blocks(M);
+                       float* pb, float* dgamma, float* dbeta, hipStream_t s, uint16_t* y16, float* pd) {
+    if (y16 && !pd) return hipErrorInvalidValue;
+    const int nb = ln_backward_blocks(M);
     const dim3 grid(nb), block(64 * kLnWaves);
     switch (d) {
-        case 768: ln_backward_kernel<12><<<grid, block, 0, s>>>(x, gamma, dy, dx, M, d, eps, pg, pb); break;
-        case 1024: ln_backward_kernel<16><<<grid, block, 0, s>>>(x, gamma, dy, dx, M, d, eps, pg, pb); break;
-        case 1600: ln_backward_kernel<25><<<grid, block, 0, s>>>(x, gamma, dy, dx, M, d, eps, pg, pb); break;
-        default: ln_backward_kernel<0><<<grid, block, 0, s>>>(x, gamma, dy, dx, M, d, eps, pg, pb); break;
+        case 768: ln_backward_kernel<12><<<grid, block, 0, s>>>(x, gamma, dy, dx, M, d, eps, pg, pb, y16, pd); break;
+        case 1024: ln_backward_kernel<16><<<grid, block, 0, s>>>(x, gamma, dy, dx, M, d, eps, pg, pb, y16, pd); break;
+        case 1280: ln_backward_kernel<20><<<grid, block, 0, s>>>(x, gamma, dy, dx, M, d, eps, pg, pb, y16, pd); break;
+        case 1600: ln_backward_kernel<25><<<grid, block, 0, s>>>(x, gamma, dy, dx, M, d, eps, pg, pb, y16, pd); break;
+        default: ln_backward_kernel<0><<<grid, dim3(64), 0, s>>>(x, gamma, dy, dx, M, d, eps, pg, pb, y16, pd); break;
     }
     if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
     ColsumSegs segs;  // the gain and shift gradients in one launch
-    segs.seg[0] = {pg, dgamma, np, d};
-    segs.seg[1] = {pb, dbeta, np, d};
+    segs.seg[0] = {pg, dgamma, nb, d};
+    segs.seg[1] = {pb, dbeta, nb, d};
     segs.n = 2;
     return colsum_reduce_multi(segs, s);
 }
