@@ -234,10 +234,11 @@ __global__ void __launch_bounds__(256) colsum_reduce_multi_kernel(const ColsumSe
 // its rows and writes them as partial row blockIdx.x of pg / pb [blocks][d]. With y16 the new dx is
 // also written in bf16 (row stride d) and its per-column sums as partial row blockIdx.x of pd: the
 // output gradient of the projection before this LayerNorm, with its bias gradient's partials.
-constexpr int kLnRows = 16, kLnWaves = 4;
+constexpr int kLnRows = 16, kLnWaves = 8;
 
-// CPL > 0 (d = 64 * CPL): kLnWaves wavefronts, one row at a time each, the row and the column sums held
-// in registers (lane l owns columns l + 64 j), the waves' sums added in wave order through LDS.
+// CPL > 0 (d = 64 * CPL): kLnWaves wavefronts, one row at a time each (eight waves for two rows each:
+// with four waves per CU the loads in flight did not cover the memory latency), the row and the column
+// sums held in registers (lane l owns columns l + 64 j), the waves' sums added in wave order through LDS.
 // CPL = 0 (any d, a multiple of 64): one wavefront takes the block's rows in order, re-reading the row
 // and accumulating in its partial rows.
 template <int CPL>
@@ -314,26 +315,23 @@ __global__ void __launch_bounds__(64 * kLnWaves) ln_backward_kernel(const float*
                 }
             }
         }
-        __shared__ float red[3][kLnWaves][CPL * 64];
+        // one sum at a time through a [waves][d] buffer, added in wave order
+        __shared__ float red[kLnWaves][CPL * 64];
+        auto block_sum = [&](const float* a, float* out) {
 #pragma unroll
-        for (int j = 0; j < CPL; ++j) {
-            red[0][w][lane + 64 * j] = ag[j];
-            red[1][w][lane + 64 * j] = ab[j];
-            red[2][w][lane + 64 * j] = ad[j];
-        }
-        __syncthreads();
-        for (int c = threadIdx.x; c < d; c += 64 * kLnWaves) {
-            float sa = red[0][0][c], sb = red[1][0][c], sd = red[2][0][c];
+            for (int j = 0; j < CPL; ++j) red[w][lane + 64 * j] = a[j];
+            __syncthreads();
+            for (int c = threadIdx.x; c < d; c += 64 * kLnWaves) {
+                float t = red[0][c];
 #pragma unroll
-            for (int v = 1; v < kLnWaves; ++v) {
-                sa += red[0][v][c];
-                sb += red[1][v][c];
-                sd += red[2][v][c];
+                for (int v = 1; v < kLnWaves; ++v) t += red[v][c];
+                out[c] = t;
             }
-            og[c] = sa;
-            ob[c] = sb;
-            if (od) od[c] = sd;
-        }
+            __syncthreads();
+        };
+        block_sum(ag, og);
+        block_sum(ab, ob);
+        if (od) block_sum(ad, od);
     } else {
         for (int c = lane; c < d; c += 64) {
             og[c] = ob[c] = 0.f;
