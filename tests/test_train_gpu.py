@@ -144,6 +144,14 @@ def test_backward_bf16_b4_t1024_one_layer(g):
     run_case(g, s, "bf16", 4, 1024, ignore=[(1, 500), (3, 1023)])
 
 
+@pytest.mark.parametrize("d", [1024, 1280, 1600])
+def test_backward_bf16_wide(g, d):
+    """One block at the widths of GPT-2 medium, large and XL (64-wide heads, MLP 4d, vocabulary 1000),
+    B=1 T=48: the LayerNorm backward's register-held rows of 16, 20 and 25 columns per lane."""
+    s = synth.ModelShape(n_vocab=1000, n_ctx=64, d_model=d, n_head=d // 64, n_layer=1, d_mlp=4 * d)
+    run_case(g, s, "bf16", 1, 48, ignore=[(0, 7)])
+
+
 def test_backward_f32_t1024(g):
     """fp32 mode at T=1024 on a two-layer model of GPT-2 small width."""
     s = synth.ModelShape(n_vocab=50257, n_ctx=1024, d_model=768, n_head=12, n_layer=2, d_mlp=3072)
