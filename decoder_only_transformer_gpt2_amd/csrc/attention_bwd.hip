@@ -9,6 +9,9 @@
 //   attn_bwd_dkv_mfma: a workgroup owns 64 keys, a wavefront 16 of them; over the query tiles on
 //     and after the diagonal it forms S = Q K^T, P, dP = dO V^T, dS and accumulates
 //     dV^T += dO^T P and dK^T += Q^T dS.
+// Both write their gradient rows in bf16 into dqkv [B*T, 3 * H * 64] (the output gradient of the
+// QKV projection, whose weight and input gradients read it) and the sums of each 64-row tile's
+// columns into part [B * ceil(T / 64)][3 * H * 64] (partials of that projection's bias gradient).
 // With v_mfma_f32_16x16x32_bf16 a lane's accumulator holds one column (lane % 16) and rows
 // 4 (lane / 16) + e; the four accumulators of a 64-row product therefore give every lane the 8
 // values of its column at rows {32 h + 4 g + j, 32 h + 16 + 4 g + j} (j < 4), which is directly
@@ -108,8 +111,38 @@ __device__ __forceinline__ void row_operand(const uint16_t* row, int g, bf16x8_t
 
 constexpr float kC2 = 0.125f * 1.4426950408889634f;  // (1 / sqrt(64)) * log2(e)
 
+// One 64-row tile's gradient columns (lane: four dims 4 g4 .. 4 g4 + 3 of each 16-dim group df, for
+// its row; invalid rows hold zeros) to bf16 row-major out (row stride 3d), and their sums over the
+// tile's rows to part (64 floats): over the 16 rows of a wavefront by lane exchange, then over the
+// four wavefronts in wave order through red.
+__device__ __forceinline__ void tile_grad_out(const f32x4_t (&v)[4], bool valid, uint16_t* out, float* part,
+                                              float (*red)[DHB], int w, int lane) {
+    const int r16 = lane & 15, g4 = lane >> 4;
+    if (valid) {
+#pragma unroll
+        for (int df = 0; df < 4; ++df)
+            *reinterpret_cast<u32x2_t*>(out + df * 16 + 4 * g4) =
+                u32x2_t{pack_bf16x2(v[df][0], v[df][1]), pack_bf16x2(v[df][2], v[df][3])};
+    }
+#pragma unroll
+    for (int df = 0; df < 4; ++df)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            float x = v[df][e];
+            x += __shfl_xor(x, 1);
+            x += __shfl_xor(x, 2);
+            x += __shfl_xor(x, 4);
+            x += __shfl_xor(x, 8);
+            if (r16 == 0) red[w][df * 16 + 4 * g4 + e] = x;
+        }
+    __syncthreads();
+    if (threadIdx.x < DHB) part[threadIdx.x] = (red[0][threadIdx.x] + red[1][threadIdx.x]) + (red[2][threadIdx.x] + red[3][threadIdx.x]);
+    __syncthreads();
+}
+
 __global__ __launch_bounds__(256) void attn_bwd_dq_mfma(const uint16_t* __restrict__ qkv, const uint16_t* __restrict__ o,
-                                                        const float* __restrict__ dout, float* __restrict__ dqkv,
+                                                        const float* __restrict__ dout, uint16_t* __restrict__ dqkv,
+                                                        float* __restrict__ part,
                                                         const float* __restrict__ lse_in, float* __restrict__ d_out, int B,
                                                         int H, int T) {
     __shared__ __attribute__((aligned(16))) uint16_t sK[BT * DHB];
@@ -199,18 +232,18 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_mfma(const uint16_t* __restri
                 dq[df] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a_trans(sK, df, hh, lane), dsf, dq[df], 0, 0, 0);
         }
     }
-    if (qv) {
-        float* out = dqkv + qrow * 3 * d + h * DHB;
+    if (qv && g4 == 0) d_out[(long)bh * T + qi] = dd;
+    __shared__ float red[4][DHB];
+    f32x4_t v[4];
 #pragma unroll
-        for (int df = 0; df < 4; ++df)
-            *reinterpret_cast<f32x4_t*>(out + df * 16 + 4 * g4) = dq[df] * 0.125f;
-        if (g4 == 0) d_out[(long)bh * T + qi] = dd;
-    }
+    for (int df = 0; df < 4; ++df) v[df] = qv ? dq[df] * 0.125f : f32x4_t{0.f, 0.f, 0.f, 0.f};
+    tile_grad_out(v, qv, dqkv + qrow * 3 * d + h * DHB, part + ((long)b * nqb + qb) * 3 * d + h * DHB, red, w, lane);
 }
 
 __global__ __launch_bounds__(256) void attn_bwd_dkv_mfma(const uint16_t* __restrict__ qkv, const float* __restrict__ dout,
                                                          const float* __restrict__ lse, const float* __restrict__ dvec,
-                                                         float* __restrict__ dqkv, int B, int H, int T) {
+                                                         uint16_t* __restrict__ dqkv, float* __restrict__ part, int B,
+                                                         int H, int T) {
     __shared__ __attribute__((aligned(16))) uint16_t sQ[BT * DHB];
     __shared__ __attribute__((aligned(16))) uint16_t sG[BT * DHB];
     __shared__ float sL[BT], sD[BT];
@@ -289,23 +322,27 @@ __global__ __launch_bounds__(256) void attn_bwd_dkv_mfma(const uint16_t* __restr
             }
         }
     }
-    if (kv) {
-        float* out = dqkv + krow * 3 * d + h * DHB;
+    __shared__ float red[4][DHB];
+    f32x4_t v[4];
+    uint16_t* out = dqkv + krow * 3 * d + h * DHB;
+    float* pp = part + ((long)b * nkb + kb) * 3 * d + h * DHB;
 #pragma unroll
-        for (int df = 0; df < 4; ++df) {
-            *reinterpret_cast<f32x4_t*>(out + d + df * 16 + 4 * g4) = dk[df] * 0.125f;
-            *reinterpret_cast<f32x4_t*>(out + 2 * d + df * 16 + 4 * g4) = dv[df];
-        }
-    }
+    for (int df = 0; df < 4; ++df) v[df] = kv ? dk[df] * 0.125f : f32x4_t{0.f, 0.f, 0.f, 0.f};
+    tile_grad_out(v, kv, out + d, pp + d, red, w, lane);
+#pragma unroll
+    for (int df = 0; df < 4; ++df) v[df] = kv ? dv[df] : f32x4_t{0.f, 0.f, 0.f, 0.f};
+    tile_grad_out(v, kv, out + 2 * d, pp + 2 * d, red, w, lane);
 }
 
 }  // namespace
 
-hipError_t attention_backward_bf16(const uint16_t* qkv, const uint16_t* o, const float* dout, float* dqkv, float* lse,
-                                   float* dvec, int B, int H, int T, hipStream_t s) {
+int attention_backward_parts(int B, int T) { return B * ((T + BT - 1) / BT); }
+
+hipError_t attention_backward_bf16(const uint16_t* qkv, const uint16_t* o, const float* dout, uint16_t* dqkv,
+                                   float* part, float* lse, float* dvec, int B, int H, int T, hipStream_t s) {
     const dim3 grid((unsigned)(((T + BT - 1) / BT) * B * H)), block(256);
-    attn_bwd_dq_mfma<<<grid, block, 0, s>>>(qkv, o, dout, dqkv, lse, dvec, B, H, T);
-    attn_bwd_dkv_mfma<<<grid, block, 0, s>>>(qkv, dout, lse, dvec, dqkv, B, H, T);
+    attn_bwd_dq_mfma<<<grid, block, 0, s>>>(qkv, o, dout, dqkv, part, lse, dvec, B, H, T);
+    attn_bwd_dkv_mfma<<<grid, block, 0, s>>>(qkv, dout, lse, dvec, dqkv, part, B, H, T);
     return hipGetLastError();
 }
 

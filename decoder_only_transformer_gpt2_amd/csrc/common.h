@@ -298,20 +298,7 @@ hipError_t transpose(const void* src, bool src_bf16, long lds, int R, int C, voi
                      hipStream_t s);
 // out[c] = sum over rows of src[r * ld + c] (deterministic order); part holds colsum_blocks(R) * C floats.
 int colsum_blocks(int R);
-// transpose (fp32 src -> bf16 dst, as transpose) and out[c] = sum over rows of src[r][c], in one pass
-// over src when strides and pointers allow 16-byte accesses; part holds ceil(Rp / 64) * C floats
-// (and colsum_blocks(R) * C for the fallback).
-hipError_t transpose_colsum(const float* src, long lds, int R, int C, uint16_t* dst, long ldd, int Rp, float* part,
-                            float* out, hipStream_t s);
 hipError_t colsum(const float* src, long ld, int R, int C, float* part, float* out, hipStream_t s);
-// transpose_colsum without the final reduction: the partial column sums (ceil(Rp / 64) rows of C)
-// are left in part for a later colsum_reduce_multi; requires 16-byte strides and pointers.
-hipError_t transpose_colsum_partials(const float* src, long lds, int R, int C, uint16_t* dst, long ldd, int Rp,
-                                     float* part, hipStream_t s);
-// fp32 [R, C] (row stride lds) -> bf16 [Rp, C] (row stride ldd; rows R..Rp-1 zero, Rp a multiple of 64),
-// with the column sums of every 64-row block left in part ([Rp / 64][C]) like transpose_colsum_partials.
-hipError_t convert_colsum_partials(const float* src, long lds, int R, int C, uint16_t* dst, long ldd, int Rp,
-                                   float* part, hipStream_t s);
 // out[c] = sum over b < nb of part[b * C + c] for up to kColsumSegs independent (part, nb, C, out)
 // segments in one launch, each in the fixed order of colsum.
 struct ColsumSeg {
@@ -340,13 +327,16 @@ hipError_t gelu_backward(const float* u, float* g, long n, int erf_form, hipStre
 // gradient [M, Vp] (compute dtype; zero past V and on rows without target).
 hipError_t xent_grad(const float* logits, long ld, int M, int V, int Vp, const int32_t* tgt, int32_t* cnt, float* nll,
                      void* dlogits, bool bf16, hipStream_t s);
-// Causal attention backward on qkv [B, T, 3, H, 64] and o [B, T, H, 64] (compute dtype) with the
-// output gradient dout fp32 [B, T, H * 64]: dqkv fp32 [B, T, 3 * H * 64]; lse, dvec: [B * H * T]. In
-// bf16 mode lse is an input (the forward's attention_bf16 lse_out); in fp32 mode both are scratch.
+// Causal attention backward, fp32 mode: qkv [B, T, 3, H, 64] and o [B, T, H, 64] with the output
+// gradient dout [B, T, H * 64]: dqkv [B, T, 3 * H * 64]; lse, dvec [B * H * T] are scratch.
 hipError_t attention_backward(const void* qkv, const void* o, const float* dout, float* dqkv, float* lse, float* dvec,
                               int B, int H, int T, bool bf16, hipStream_t s);
-hipError_t attention_backward_bf16(const uint16_t* qkv, const uint16_t* o, const float* dout, float* dqkv, float* lse,
-                                   float* dvec, int B, int H, int T, hipStream_t s);
+// bf16 mode (matrix cores): dqkv in bf16 (rows 0 .. B*T-1) and the column sums of every 64-row tile
+// of each sequence in part ([attention_backward_parts(B, T)][3 * H * 64] floats); lse is the forward's
+// attention_bf16 lse_out, dvec [B * H * T] scratch.
+int attention_backward_parts(int B, int T);
+hipError_t attention_backward_bf16(const uint16_t* qkv, const uint16_t* o, const float* dout, uint16_t* dqkv,
+                                   float* part, float* lse, float* dvec, int B, int H, int T, hipStream_t s);
 // gwpe[t] = sum_b dx[b, t] (0 for t >= T, all n_ctx rows written); gwte[tok[m]] += dx[m].
 hipError_t embed_backward(const int32_t* tok, const float* dx, int B, int T, int n_ctx, int d, int V, float* gwte,
                           float* gwpe, hipStream_t s);

@@ -490,8 +490,9 @@ TrainLayout train_layout(const gpt2_model* m, int B, int T) {
     L.dlogT = take(tr_ops ? L.Vr * L.Mk * as : 0);
     L.part = take((size_t)std::max<int64_t>(gpt2k::colsum_blocks((int)L.M), (L.Mk + 63) / 64) * L.wide * 4);
     // bf16: the bias gradients' partial column sums of every layer, reduced in one launch at the end
-    // (c_attn, c_fc: one row per 64-row block; attn.c_proj, mlp.c_proj: one per LayerNorm-backward block)
-    L.bpart = take(is_bf16(m) ? ((size_t)((L.Mk + 63) / 64) * (3 * d + f) +
+    // (c_fc: one row per 64-row block; c_attn: one per 64-row tile of a sequence, from the attention
+    // backward; attn.c_proj, mlp.c_proj: one per LayerNorm-backward block)
+    L.bpart = take(is_bf16(m) ? ((size_t)((L.Mk + 63) / 64) * f + (size_t)gpt2k::attention_backward_parts(B, T) * 3 * d +
                                  (size_t)gpt2k::ln_backward_blocks((int)L.M) * 2 * d) * c.n_layer * 4
                               : 0);
     L.lnpg = take((size_t)gpt2k::ln_backward_blocks((int)L.M) * d * 4);
@@ -640,7 +641,6 @@ gpt2_status enqueue_backward(const gpt2_model* m, const int32_t* tokens, int B, 
     auto to_act = [&](const float* src, int Cc, void* dst) {
         return gpt2k::convert(src, false, dst, bf, (long)M * Cc, (long)Mp * Cc, s);
     };
-    // the weight gradient and the input gradient of y = x W^T + b for output gradient dy (fp32 [M, n_out])
     // bf16: the bias gradients' partial column sums, one region per bias, reduced together at the end
     std::vector<gpt2k::ColsumSeg> bsegs;
     float* bpart = reinterpret_cast<float*>(ws + L.bpart);
@@ -663,21 +663,12 @@ gpt2_status enqueue_backward(const gpt2_model* m, const int32_t* tokens, int B, 
         return gpt2k::gemm_bf16_tn(dy16, false, n_out, Mk, static_cast<const uint16_t*>(wptr(m, widx)), true, n_in,
                                    n_in, dx_out, n_in, M, n_in, n_out, s, nullptr, 0, gb);
     };
+    // fp32: the weight gradient and the input gradient of y = x W^T + b for output gradient dy ([M, n_out])
     auto linear_back = [&](const float* dy, int n_out, const void* x_act, int n_in, bool x_kb, int widx,
                            float* dx_out) -> hipError_t {
         hipError_t e;
-        if (bf) {
-            // dy -> bf16 rows (zero from M to Mk) with the bias gradient's column-sum partials
-            uint16_t* dy16 = reinterpret_cast<uint16_t*>(dact);
-            if ((e = gpt2k::convert_colsum_partials(dy, n_out, M, n_out, dy16, n_out, Mk, bpart, s)) != hipSuccess)
-                return e;
-            float* bp = bpart;
-            bpart += (size_t)nbp * n_out;
-            return linear_back16(dy16, bp, nbp, n_out, x_act, n_in, x_kb, widx, dx_out, nullptr);
-        } else {
-            if ((e = gpt2k::colsum(dy, n_out, M, n_out, part, G(widx + 1), s)) != hipSuccess) return e;
-            if ((e = tr(dy, false, n_out, M, n_out, dT, Mk, Mk)) != hipSuccess) return e;
-        }
+        if ((e = gpt2k::colsum(dy, n_out, M, n_out, part, G(widx + 1), s)) != hipSuccess) return e;
+        if ((e = tr(dy, false, n_out, M, n_out, dT, Mk, Mk)) != hipSuccess) return e;
         if ((e = tr(x_act, true, n_in, M, n_in, xT, Mk, Mk)) != hipSuccess) return e;
         if ((e = gemm_nt(dT, pad(n_out), xT, pad(n_in), G(widx), n_out, n_in, Mk, n_in)) != hipSuccess) return e;
         if ((e = to_act(dy, n_out, dact)) != hipSuccess) return e;
@@ -772,9 +763,21 @@ gpt2_status enqueue_backward(const gpt2_model* m, const int32_t* tokens, int B, 
         else
             GPT2_HIP(linear_back(dx, d, lay(l, L.l_o), d, false, I(APROJ_W), dbuf));
         float* lse = reinterpret_cast<float*>(bf ? lay(l, L.l_lse) : ws + L.lse);  // bf16: written by the forward
-        GPT2_HIP(gpt2k::attention_backward(lay(l, L.l_qkv), lay(l, L.l_o), dbuf, dbuf2, lse,
-                                           reinterpret_cast<float*>(ws + L.dvec), B, H, T, bf, s));
-        GPT2_HIP(linear_back(dbuf2, 3 * d, lay(l, L.l_a1), d, x_kb, I(ATTN_W), dbuf));
+        if (bf) {
+            // the attention backward writes c_attn's bf16 output gradient and its bias partial sums
+            const int nba = gpt2k::attention_backward_parts(B, T);
+            if (Mk > M) GPT2_HIP(hipMemsetAsync(dact16 + (size_t)M * 3 * d, 0, (size_t)(Mk - M) * 3 * d * 2, s));
+            float* bp_attn = bpart;
+            bpart += (size_t)nba * 3 * d;
+            GPT2_HIP(gpt2k::attention_backward_bf16(reinterpret_cast<const uint16_t*>(lay(l, L.l_qkv)),
+                                                    reinterpret_cast<const uint16_t*>(lay(l, L.l_o)), dbuf, dact16,
+                                                    bp_attn, lse, reinterpret_cast<float*>(ws + L.dvec), B, H, T, s));
+            GPT2_HIP(linear_back16(dact16, bp_attn, nba, 3 * d, lay(l, L.l_a1), d, x_kb, I(ATTN_W), dbuf, nullptr));
+        } else {
+            GPT2_HIP(gpt2k::attention_backward(lay(l, L.l_qkv), lay(l, L.l_o), dbuf, dbuf2, lse,
+                                               reinterpret_cast<float*>(ws + L.dvec), B, H, T, false, s));
+            GPT2_HIP(linear_back(dbuf2, 3 * d, lay(l, L.l_a1), d, x_kb, I(ATTN_W), dbuf));
+        }
         // (the layer below's mlp.c_proj output gradient; none below the first layer)
         const bool next16 = bf && l > 0;
         if (next16) GPT2_HIP(zero_dact_tail());

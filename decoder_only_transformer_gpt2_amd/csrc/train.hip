@@ -47,14 +47,10 @@ __global__ void __launch_bounds__(256) transpose_kernel(const void* __restrict__
 // of destination rows out of it; element by element only where a piece crosses R, C or Rp. The
 // 65-float tile rows keep both the row writes and the column reads of a wavefront on distinct
 // banks. The values are the same bits as transpose_kernel's (fp32 sources round to nearest even).
-// With colpart set (fp32 sources), the workgroup also writes the sums of its tile's columns over its
-// 64 rows to colpart[blockIdx.y][c] (four 16-row quarters added in order).
 template <bool SRC_BF>
 __global__ void __launch_bounds__(256) transpose_vec_kernel(const void* __restrict__ srcv, long lds, int R, int C,
-                                                            uint16_t* __restrict__ dst, long ldd, int Rp,
-                                                            float* __restrict__ colpart) {
+                                                            uint16_t* __restrict__ dst, long ldd, int Rp) {
     __shared__ float tile[64][65];
-    __shared__ float qsum[4][64];
     const int c0 = blockIdx.x * 64, r0 = blockIdx.y * 64, t = threadIdx.x;
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
@@ -84,16 +80,6 @@ __global__ void __launch_bounds__(256) transpose_vec_kernel(const void* __restri
         for (int j = 0; j < 8; ++j) tile[rr][ck + j] = v[j];
     }
     __syncthreads();
-    if (colpart) {
-        const int cc = t & 63, q = t >> 6;
-        float a = 0.f;
-#pragma unroll
-        for (int j = 0; j < 16; ++j) a += tile[q * 16 + j][cc];
-        qsum[q][cc] = a;
-        __syncthreads();
-        if (q == 0 && c0 + cc < C)
-            colpart[(long)blockIdx.y * C + c0 + cc] = ((qsum[0][cc] + qsum[1][cc]) + qsum[2][cc]) + qsum[3][cc];
-    }
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
         const int e = t + i * 256, cc = e >> 3, rk = (e & 7) * 8, c = c0 + cc, r = r0 + rk;
@@ -108,47 +94,6 @@ __global__ void __launch_bounds__(256) transpose_vec_kernel(const void* __restri
             for (int j = 0; j < 8 && r + j < Rp; ++j) dp[j] = f32_to_bf16_bits(tile[rk + j][cc]);
         }
     }
-}
-
-// fp32 [R rows, C] (row stride lds) -> bf16 [Rp rows, C] (row stride ldd, rows R..Rp-1 zero), 16-byte
-// accesses on both sides, and the sums of each 64-row block's columns to colpart[blockIdx.y][c] in
-// the order of transpose_vec_kernel's (four 16-row quarters, each in row order, added in order).
-__global__ void __launch_bounds__(256) convert_colsum_kernel(const float* __restrict__ src, long lds, int R, int C,
-                                                             uint16_t* __restrict__ dst, long ldd, float* __restrict__ colpart) {
-    __shared__ float tile[64][65];
-    __shared__ float qsum[4][64];
-    const int c0 = blockIdx.x * 64, r0 = blockIdx.y * 64, t = threadIdx.x;
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-        const int e = t + i * 256, rr = e >> 3, ck = (e & 7) * 8, r = r0 + rr, c = c0 + ck;
-        float v[8];
-        if (r < R && c + 8 <= C) {
-            const float4* p = reinterpret_cast<const float4*>(src + (long)r * lds + c);
-            const float4 a = p[0], b = p[1];
-            v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w; v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
-        } else {
-#pragma unroll
-            for (int j = 0; j < 8; ++j) v[j] = (r < R && c + j < C) ? src[(long)r * lds + c + j] : 0.f;
-        }
-#pragma unroll
-        for (int j = 0; j < 8; ++j) tile[rr][ck + j] = v[j];
-        uint16_t* dp = dst + (long)r * ldd + c;
-        if (c + 8 <= C) {
-            *reinterpret_cast<u32x4_t*>(dp) = u32x4_t{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]),
-                                                      pack_bf16x2(v[4], v[5]), pack_bf16x2(v[6], v[7])};
-        } else {
-            for (int j = 0; j < 8 && c + j < C; ++j) dp[j] = f32_to_bf16_bits(v[j]);
-        }
-    }
-    __syncthreads();
-    const int cc = t & 63, q = t >> 6;
-    float a = 0.f;
-#pragma unroll
-    for (int j = 0; j < 16; ++j) a += tile[q * 16 + j][cc];
-    qsum[q][cc] = a;
-    __syncthreads();
-    if (q == 0 && c0 + cc < C)
-        colpart[(long)blockIdx.y * C + c0 + cc] = ((qsum[0][cc] + qsum[1][cc]) + qsum[2][cc]) + qsum[3][cc];
 }
 
 // ------------------------------------------------------------------------------ column sums
@@ -784,9 +729,9 @@ hipError_t transpose(const void* src, bool src_bf16, long lds, int R, int C, voi
     const bool vec = lds % 8 == 0 && ldd % 8 == 0 && reinterpret_cast<uintptr_t>(src) % 16 == 0 &&
                      reinterpret_cast<uintptr_t>(dst) % 16 == 0;
     if (src_bf16 && dst_bf16 && vec)
-        transpose_vec_kernel<true><<<grid, block, 0, s>>>(src, lds, R, C, static_cast<uint16_t*>(dst), ldd, Rp, nullptr);
+        transpose_vec_kernel<true><<<grid, block, 0, s>>>(src, lds, R, C, static_cast<uint16_t*>(dst), ldd, Rp);
     else if (dst_bf16 && vec)
-        transpose_vec_kernel<false><<<grid, block, 0, s>>>(src, lds, R, C, static_cast<uint16_t*>(dst), ldd, Rp, nullptr);
+        transpose_vec_kernel<false><<<grid, block, 0, s>>>(src, lds, R, C, static_cast<uint16_t*>(dst), ldd, Rp);
     else if (src_bf16 && dst_bf16)
         transpose_kernel<true, true><<<grid, block, 0, s>>>(src, lds, R, C, dst, ldd, Rp);
     else if (src_bf16)
@@ -799,39 +744,6 @@ hipError_t transpose(const void* src, bool src_bf16, long lds, int R, int C, voi
 }
 
 int colsum_blocks(int R) { return (R + kColRows - 1) / kColRows; }
-
-hipError_t transpose_colsum(const float* src, long lds, int R, int C, uint16_t* dst, long ldd, int Rp, float* part,
-                            float* out, hipStream_t s) {
-    const bool vec = lds % 8 == 0 && ldd % 8 == 0 && reinterpret_cast<uintptr_t>(src) % 16 == 0 &&
-                     reinterpret_cast<uintptr_t>(dst) % 16 == 0 && Rp >= R;
-    if (!vec) {
-        const hipError_t e = colsum(src, lds, R, C, part, out, s);
-        return e != hipSuccess ? e : transpose(src, false, lds, R, C, dst, true, ldd, Rp, s);
-    }
-    const int nb = (Rp + 63) / 64;
-    transpose_vec_kernel<false><<<dim3((C + 63) / 64, nb), dim3(256), 0, s>>>(src, lds, R, C, dst, ldd, Rp, part);
-    colsum_reduce_kernel<<<dim3((C + kRedCols - 1) / kRedCols), dim3(256), 0, s>>>(part, nb, C, out);
-    return hipGetLastError();
-}
-
-hipError_t transpose_colsum_partials(const float* src, long lds, int R, int C, uint16_t* dst, long ldd, int Rp,
-                                     float* part, hipStream_t s) {
-    const bool vec = lds % 8 == 0 && ldd % 8 == 0 && reinterpret_cast<uintptr_t>(src) % 16 == 0 &&
-                     reinterpret_cast<uintptr_t>(dst) % 16 == 0 && Rp >= R;
-    if (!vec) return hipErrorInvalidValue;
-    transpose_vec_kernel<false><<<dim3((C + 63) / 64, (Rp + 63) / 64), dim3(256), 0, s>>>(src, lds, R, C, dst, ldd, Rp,
-                                                                                          part);
-    return hipGetLastError();
-}
-
-hipError_t convert_colsum_partials(const float* src, long lds, int R, int C, uint16_t* dst, long ldd, int Rp,
-                                   float* part, hipStream_t s) {
-    const bool vec = lds % 8 == 0 && ldd % 8 == 0 && reinterpret_cast<uintptr_t>(src) % 16 == 0 &&
-                     reinterpret_cast<uintptr_t>(dst) % 16 == 0 && Rp >= R && Rp % 64 == 0;
-    if (!vec) return hipErrorInvalidValue;
-    convert_colsum_kernel<<<dim3((C + 63) / 64, Rp / 64), dim3(256), 0, s>>>(src, lds, R, C, dst, ldd, part);
-    return hipGetLastError();
-}
 
 hipError_t colsum_reduce_multi(const ColsumSegs& segs, hipStream_t s) {
     if (segs.n < 1 || segs.n > kColsumSegs) return hipErrorInvalidValue;
@@ -928,9 +840,7 @@ hipError_t xent_grad(const float* logits, long ld, int M, int V, int Vp, const i
 
 hipError_t attention_backward(const void* qkv, const void* o, const float* dout, float* dqkv, float* lse, float* dvec,
                               int B, int H, int T, bool bf16, hipStream_t s) {
-    if (bf16)  // matrix-core kernels
-        return attention_backward_bf16(static_cast<const uint16_t*>(qkv), static_cast<const uint16_t*>(o), dout, dqkv,
-                                       lse, dvec, B, H, T, s);
+    if (bf16) return hipErrorInvalidValue;  // attention_backward_bf16
     const dim3 grid((T + AB_ROWS - 1) / AB_ROWS, B * H), block(AB_T);
     attn_bwd_q_kernel<false><<<grid, block, 0, s>>>(qkv, o, dout, dqkv, lse, dvec, H, T);
     attn_bwd_kv_kernel<false><<<grid, block, 0, s>>>(qkv, dout, lse, dvec, dqkv, H, T);
