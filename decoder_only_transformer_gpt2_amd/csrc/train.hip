@@ -430,7 +430,9 @@ __global__ void __launch_bounds__(256) xent_grad_kernel(const float* __restrict_
 // The same with the row held in registers: 512 threads per row, NF float4 per thread (row stride
 // ld a multiple of 4, columns V <= v of the row masked by index), so the logits are read once. The
 // row maximum and the sum of 2^((z - max) log2 e) are reduced over the wavefront and then over the
-// eight wavefronts in a fixed order.
+// eight wavefronts in a fixed order. Registers are capped at 128 (four waves per SIMD) so that two
+// rows share a CU, one loading while the other reduces and stores (at the 168 the compiler chose
+// otherwise, a CU held one row: 2.8% of a GPT-2 small training step, against a few spilled registers).
 constexpr int XG_T = 512;
 
 __device__ __forceinline__ float wave_max_xor(float v) {
@@ -445,7 +447,7 @@ __device__ __forceinline__ float wave_sum_xor(float v) {
 }
 
 template <bool BF, int NF>
-__global__ void __launch_bounds__(XG_T) xent_grad_reg_kernel(const float* __restrict__ logits, long ld, int V, int Vp,
+__global__ void __launch_bounds__(XG_T, 4) xent_grad_reg_kernel(const float* __restrict__ logits, long ld, int V, int Vp,
                                                             const int32_t* __restrict__ tgt,
                                                             const int32_t* __restrict__ cnt, float* __restrict__ nll,
                                                             void* __restrict__ dlogits) {
