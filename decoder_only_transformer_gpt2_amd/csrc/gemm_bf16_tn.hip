@@ -357,7 +357,9 @@ hipError_t gemm_bf16_tn(const uint16_t* A, bool a_mmajor, long lda, int a_lim, c
     }
     // Split along K where one pass would leave most CUs idle or run very long chains: a weight
     // gradient with fewer than 128 tiles of 64 x 128 (attn.c_proj of GPT-2 small: 72) in four
-    // parts; a reduction over the vocabulary (nk in the hundreds) in three or two parts.
+    // parts; a reduction over the vocabulary (nk in the hundreds) in six, three or two parts (six for
+    // GPT-2's 786 steps: 2304 workgroups fill the 512 slots of two per CU 4.5 times, where three parts
+    // filled them 2.25 times with twice the steps each; training step 7.75 -> 7.70 ms).
     auto fits = [&](int ns) {
         return part && N % 4 == 0 && ldc % 4 == 0 && reinterpret_cast<uintptr_t>(C) % 16 == 0 &&
                (size_t)ns * M * N <= part_elems;
@@ -369,6 +371,8 @@ hipError_t gemm_bf16_tn(const uint16_t* A, bool a_mmajor, long lda, int a_lim, c
         return launch_tn<64, 128, 3, 2, 2, true, true, 0>(A, lda, a_lim, B, ldb, b_lim, C, ldc, M, N, K, s, 4, part);
     }
     if (!a_mmajor && nk >= 256) {
+        if (nk % 6 == 0 && fits(6))
+            return launch_tn<64, 128, 3, 2, 2, false, true, 0>(A, lda, a_lim, B, ldb, b_lim, C, ldc, M, N, K, s, 6, part);
         if (nk % 3 == 0 && fits(3))
             return launch_tn<64, 128, 3, 2, 2, false, true, 0>(A, lda, a_lim, B, ldb, b_lim, C, ldc, M, N, K, s, 3, part);
         if (nk % 2 == 0 && fits(2))

@@ -499,9 +499,9 @@ TrainLayout train_layout(const gpt2_model* m, int B, int T) {
     L.lnpb = take((size_t)gpt2k::ln_backward_blocks((int)L.M) * d * 4);
     L.lse = take(is_bf16(m) ? 0 : (size_t)B * c.n_head * T * 4);  // fp32 mode: the backward finds it
     L.dvec = take((size_t)B * c.n_head * T * 4);
-    // partial products of the products split along K (the vocabulary reduction of dxf in three
+    // partial products of the products split along K (the vocabulary reduction of dxf in six
     // parts, a narrow weight gradient in four)
-    L.splitk_elems = is_bf16(m) ? std::max<size_t>((size_t)3 * L.M * d, (size_t)4 * d * d) : 0;
+    L.splitk_elems = is_bf16(m) ? std::max<size_t>((size_t)6 * L.M * d, (size_t)4 * d * d) : 0;
     L.splitk = take(L.splitk_elems * 4);
     L.nll = take(L.M * 4);
     L.cnt = take(4);
