@@ -111,33 +111,40 @@ __device__ __forceinline__ void row_operand(const uint16_t* row, int g, bf16x8_t
 
 constexpr float kC2 = 0.125f * 1.4426950408889634f;  // (1 / sqrt(64)) * log2(e)
 
-// One 64-row tile's gradient columns (lane: four dims 4 g4 .. 4 g4 + 3 of each 16-dim group df, for
-// its row; invalid rows hold zeros) to bf16 row-major out (row stride 3d), and their sums over the
-// tile's rows to part (64 floats): over the 16 rows of a wavefront by lane exchange, then over the
-// four wavefronts in wave order through red.
-__device__ __forceinline__ void tile_grad_out(const f32x4_t (&v)[4], bool valid, uint16_t* out, float* part,
-                                              float (*red)[DHB], int w, int lane) {
-    const int r16 = lane & 15, g4 = lane >> 4;
-    if (valid) {
+// NG gradients of one 64-row tile (lane: four dims 4 g4 .. 4 g4 + 3 of each 16-dim group df, for
+// row 16 w + lane % 16; invalid rows hold zeros) to bf16 row-major out[i] (row stride 3d), and their
+// column sums over the tile's rows to part[i] (64 floats each): the tile is staged in LDS (rows of
+// 68 floats, so the lanes' 16-byte writes of 16 rows meet distinct banks), each thread sums 16 rows
+// of one column, and the four quarter sums are added in order.
+constexpr int kStg = DHB + 4;
+template <int NG>
+__device__ __forceinline__ void tile_grad_out(const f32x4_t (&v)[NG][4], bool valid, uint16_t* const (&out)[NG],
+                                              float* const (&part)[NG], float (*stg)[64][kStg], float (*q4)[4][DHB],
+                                              int w, int lane) {
+    const int r16 = lane & 15, g4 = lane >> 4, row = 16 * w + r16;
 #pragma unroll
-        for (int df = 0; df < 4; ++df)
-            *reinterpret_cast<u32x2_t*>(out + df * 16 + 4 * g4) =
-                u32x2_t{pack_bf16x2(v[df][0], v[df][1]), pack_bf16x2(v[df][2], v[df][3])};
-    }
+    for (int i = 0; i < NG; ++i)
 #pragma unroll
-    for (int df = 0; df < 4; ++df)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            float x = v[df][e];
-            x += __shfl_xor(x, 1);
-            x += __shfl_xor(x, 2);
-            x += __shfl_xor(x, 4);
-            x += __shfl_xor(x, 8);
-            if (r16 == 0) red[w][df * 16 + 4 * g4 + e] = x;
+        for (int df = 0; df < 4; ++df) {
+            if (valid)
+                *reinterpret_cast<u32x2_t*>(out[i] + df * 16 + 4 * g4) =
+                    u32x2_t{pack_bf16x2(v[i][df][0], v[i][df][1]), pack_bf16x2(v[i][df][2], v[i][df][3])};
+            *reinterpret_cast<f32x4_t*>(&stg[i][row][df * 16 + 4 * g4]) = v[i][df];
         }
     __syncthreads();
-    if (threadIdx.x < DHB) part[threadIdx.x] = (red[0][threadIdx.x] + red[1][threadIdx.x]) + (red[2][threadIdx.x] + red[3][threadIdx.x]);
+    const int c = threadIdx.x & 63, qq = threadIdx.x >> 6;
+#pragma unroll
+    for (int i = 0; i < NG; ++i) {
+        float a = 0.f;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) a += stg[i][16 * qq + r][c];
+        q4[i][qq][c] = a;
+    }
     __syncthreads();
+    if (threadIdx.x < DHB) {
+#pragma unroll
+        for (int i = 0; i < NG; ++i) part[i][c] = ((q4[i][0][c] + q4[i][1][c]) + q4[i][2][c]) + q4[i][3][c];
+    }
 }
 
 __global__ __launch_bounds__(256) void attn_bwd_dq_mfma(const uint16_t* __restrict__ qkv, const uint16_t* __restrict__ o,
@@ -233,11 +240,14 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_mfma(const uint16_t* __restri
         }
     }
     if (qv && g4 == 0) d_out[(long)bh * T + qi] = dd;
-    __shared__ float red[4][DHB];
-    f32x4_t v[4];
+    __shared__ __attribute__((aligned(16))) float stg[1][64][kStg];
+    __shared__ float q4[1][4][DHB];
+    f32x4_t v[1][4];
 #pragma unroll
-    for (int df = 0; df < 4; ++df) v[df] = qv ? dq[df] * 0.125f : f32x4_t{0.f, 0.f, 0.f, 0.f};
-    tile_grad_out(v, qv, dqkv + qrow * 3 * d + h * DHB, part + ((long)b * nqb + qb) * 3 * d + h * DHB, red, w, lane);
+    for (int df = 0; df < 4; ++df) v[0][df] = qv ? dq[df] * 0.125f : f32x4_t{0.f, 0.f, 0.f, 0.f};
+    uint16_t* const outs[1] = {dqkv + qrow * 3 * d + h * DHB};
+    float* const parts[1] = {part + ((long)b * nqb + qb) * 3 * d + h * DHB};
+    tile_grad_out<1>(v, qv, outs, parts, stg, q4, w, lane);
 }
 
 __global__ __launch_bounds__(256) void attn_bwd_dkv_mfma(const uint16_t* __restrict__ qkv, const float* __restrict__ dout,
@@ -322,16 +332,19 @@ __global__ __launch_bounds__(256) void attn_bwd_dkv_mfma(const uint16_t* __restr
             }
         }
     }
-    __shared__ float red[4][DHB];
-    f32x4_t v[4];
+    __shared__ __attribute__((aligned(16))) float stg[2][64][kStg];
+    __shared__ float q4[2][4][DHB];
+    f32x4_t v[2][4];
     uint16_t* out = dqkv + krow * 3 * d + h * DHB;
     float* pp = part + ((long)b * nkb + kb) * 3 * d + h * DHB;
 #pragma unroll
-    for (int df = 0; df < 4; ++df) v[df] = kv ? dk[df] * 0.125f : f32x4_t{0.f, 0.f, 0.f, 0.f};
-    tile_grad_out(v, kv, out + d, pp + d, red, w, lane);
-#pragma unroll
-    for (int df = 0; df < 4; ++df) v[df] = kv ? dv[df] : f32x4_t{0.f, 0.f, 0.f, 0.f};
-    tile_grad_out(v, kv, out + 2 * d, pp + 2 * d, red, w, lane);
+    for (int df = 0; df < 4; ++df) {
+        v[0][df] = kv ? dk[df] * 0.125f : f32x4_t{0.f, 0.f, 0.f, 0.f};
+        v[1][df] = kv ? dv[df] : f32x4_t{0.f, 0.f, 0.f, 0.f};
+    }
+    uint16_t* const outs[2] = {out + d, out + 2 * d};
+    float* const parts[2] = {pp + d, pp + 2 * d};
+    tile_grad_out<2>(v, kv, outs, parts, stg, q4, w, lane);
 }
 
 }  // namespace
